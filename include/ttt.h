@@ -1,0 +1,177 @@
+/*
+ * ttt.h -- C ABI of the MI355X (gfx950) Test-Time-Training layer library.
+ *
+ * One call computes the forward pass of a TTT layer for every (batch, head)
+ * pair: the key/value pairs of the pair are a small training set for a
+ * fast-weight inner model F_W; the library instance-normalises the keys, runs
+ * F_W on them, back-propagates the reconstruction loss by hand to dW, takes one
+ * gradient step with learning rate eta and reads the result out on the queries:
+ *
+ *     V_hat = F_W(K_hat),   W* = W0 - eta * dL(V_hat, V)/dW,   O = F_W*(Q)
+ *
+ * (ViT3 summary page, section 02 "method essence", update equation; single
+ * full-batch step: section 03 guideline 2.)  With chunk > 0 the sequence is cut
+ * into causal chunks: each chunk first reads the weights left by the chunks
+ * before it, then takes its own step on its keys and values, with per-token
+ * learning rates and an optional L2 re-normalisation of the weights after each
+ * step (LaCT analysis page, sections "Nonlinear memory complements local
+ * attention" and "Order of operations excludes leaking the future").
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns a ttt_status; nothing throws across the ABI.
+ *     ttt_last_error() returns a human-readable message for the last failure.
+ *   - All tensor pointers are DEVICE pointers (memory of the current HIP
+ *     device), owned by the caller.  The library allocates no device memory:
+ *     scratch space is the caller's `workspace`.
+ *   - ttt_forward only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     default stream) and returns without synchronising, unless the flag
+ *     TTT_FLAG_CHECK_FINITE is set.  Arguments are validated on the host before
+ *     anything is enqueued; an invalid call enqueues nothing.
+ *   - A handle holds host state only.  One handle must not be used by two
+ *     threads at the same time; calls on one handle are ordered by the caller.
+ *   - Dense row-major layouts, no padding between rows:
+ *       q, k, v, o     [B, H, N, d]       dtype of the config (fp32 or bf16)
+ *       weights        [in, out] per matrix, fp32 (see ttt_weights)
+ *       per-token eta  [B, H, N]          fp32
+ */
+#ifndef TTT_H_
+#define TTT_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ABI_VERSION 1
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_ERR_INVALID = 1,      /* bad argument: null pointer, bad size, unknown enum */
+  TTT_ERR_UNSUPPORTED = 2,  /* valid request this library does not implement */
+  TTT_ERR_HIP = 3,          /* a HIP runtime call failed; see ttt_last_error */
+  TTT_ERR_NONFINITE = 4,    /* TTT_FLAG_CHECK_FINITE: O or the final weights hold NaN/Inf */
+  TTT_ERR_WORKSPACE = 5     /* workspace pointer null or smaller than ttt_workspace_bytes */
+} ttt_status;
+
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+/* Reconstruction loss (ViT3 page, section 03 guideline 1; LaCT page):
+ *   TTT_LOSS_MSE: L = sum_n eta_n/(n_b*d) * ||F(k_n) - v_n||^2   (mean over the
+ *                 n_b*d entries of the update batch, token-weighted by eta_n)
+ *   TTT_LOSS_DOT: L = -sum_n eta_n * <F(k_n), v_n>                (negative dot product) */
+typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_DOT = 1 } ttt_loss;
+
+/* Inner model F_W, row-vector convention, every matrix stored [in, out]:
+ *   TTT_INNER_LINEAR  : F(x) = x W                     w[0] = W  [d, d]
+ *   TTT_INNER_MLP_GELU: F(x) = gelu(x W1) W2           w[0] = W1 [d, h], w[1] = W2 [h, d]
+ *   TTT_INNER_SWIGLU  : F(x) = (silu(x W1) * (x W3)) W2
+ *                                  w[0] = W1 [d, h], w[1] = W2 [h, d], w[2] = W3 [d, h]
+ * gelu is the exact erf form.  (ViT3 page, guideline 4: two-layer MLP of width
+ * h = r*d; LaCT page: SwiGLU fast weights with three matrices.) */
+typedef enum { TTT_INNER_LINEAR = 0, TTT_INNER_MLP_GELU = 1, TTT_INNER_SWIGLU = 2 } ttt_inner;
+
+/* Flags (ttt_config.flags). */
+#define TTT_FLAG_CHECK_FINITE 0x1u   /* after the call, synchronise the stream and
+                                        return TTT_ERR_NONFINITE if O or the final
+                                        weights hold a NaN or Inf */
+#define TTT_FLAG_FORCE_GENERIC 0x2u  /* use the generic fp32-arithmetic kernels even
+                                        where a bf16 MFMA kernel exists */
+#define TTT_FLAG_LOG 0x4u            /* print the chosen kernels and launch shapes to stderr */
+
+typedef struct {
+  int B, H, N;      /* batch, heads, tokens per sequence (N >= 1) */
+  int d;            /* head dimension: 1..128 */
+  int hidden;       /* inner width h (MLP, SwiGLU): 1..512; ignored for LINEAR */
+  int dtype;        /* ttt_dtype of q, k, v, o */
+  int key_norm;     /* 1: instance-normalise the keys per (b, h, channel) over
+                       the N tokens, biased variance, no affine (Test-Time
+                       Training vs Sleep page, section "Side one") */
+  float eps;        /* added to the key variance inside the square root (>= 0) */
+  int renorm;       /* 1: after each update rescale every column of every
+                       matrix to the L2 norm that column has in W0 (LaCT page) */
+  unsigned flags;   /* TTT_FLAG_* */
+} ttt_config;
+
+/* Initial fast weights W0, fp32 device memory.  w[i] points at matrix i of
+ * the inner model (see ttt_inner; unused entries are ignored).  With
+ * batch_stride == 0 each matrix is [H, in, out] and shared by every batch
+ * element; otherwise matrix i of batch b starts at w[i] + b * batch_stride
+ * elements, e.g. batch_stride = H*in*out when each matrix is its own
+ * [B, H, in, out] buffer (all matrices of one model have in*out = d*h, or d*d
+ * for LINEAR, so one stride serves them all).  batch_stride must be 0 or
+ * >= H*in*out. */
+typedef struct {
+  const float* w[3];
+  long long batch_stride;
+} ttt_weights;
+
+/* Optional output of the final fast weights (after the last update), fp32
+ * [B, H, in, out] per matrix.  NULL entries (or a NULL struct) are skipped.
+ * Passing them back as W0 with batch_stride = H*in*out continues a chunked
+ * sequence: a split at a chunk boundary gives the same result as one call
+ * (when the re-norm targets are the same, e.g. unit-norm W0 columns). */
+typedef struct {
+  float* w[3];
+} ttt_weights_out;
+
+/* Inner learning rate (ViT3 page, guideline 3; per-token rates: LaCT page):
+ * eta_n = scale * (per_token ? per_token[b, h, n] : 1), per_token fp32
+ * [B, H, N] device memory or NULL. */
+typedef struct {
+  float scale;
+  const float* per_token;
+} ttt_eta;
+
+typedef struct ttt_handle ttt_handle;
+
+/* Version of this ABI (TTT_ABI_VERSION). */
+int ttt_version(void);
+
+/* Validate a configuration and create a handle (host memory only; makes no HIP
+ * call).  On error *out is set to NULL and the message is available from
+ * ttt_last_error(NULL). */
+int ttt_create(const ttt_config* cfg, ttt_handle** out);
+
+/* Bytes of device workspace ttt_forward needs for this handle and this
+ * (loss, inner, chunk) request; written to *bytes.  Host-only. */
+int ttt_workspace_bytes(const ttt_handle* h, int loss, int inner, int chunk, size_t* bytes);
+
+/* Enqueue the TTT-layer forward pass on `stream`.
+ *   q, k, v   [B, H, N, d] inputs (dtype of the config); o [B, H, N, d] output
+ *   W0        initial fast weights (fp32), eta learning rates
+ *   loss      ttt_loss; inner: ttt_inner
+ *   chunk     0: one full-batch step over all N tokens, then every query reads
+ *                the updated weights (write-then-query).
+ *             C > 0: causal chunks of C tokens (the last may be shorter); chunk c
+ *                reads the weights left by chunks 0..c-1, then updates them.
+ *                key_norm must be 0 (whole-sequence key statistics would leak
+ *                future keys): TTT_ERR_UNSUPPORTED otherwise.
+ *   W_out     optional final weights; workspace/ws_bytes: device scratch of at
+ *             least ttt_workspace_bytes(...) bytes, 256-byte aligned.
+ * q/k/v/o/W0 must not alias o or the workspace.  Returns TTT_OK once the work
+ * is enqueued (or, with TTT_FLAG_CHECK_FINITE, once it has finished). */
+int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v,
+                const ttt_weights* W0, const ttt_eta* eta, int loss, int inner, int chunk,
+                void* o, const ttt_weights_out* W_out, void* workspace, size_t ws_bytes,
+                void* stream);
+
+/* Name of the kernel family ttt_forward would use for this request, e.g.
+ * "mfma_full_mlp" or "generic"; NULL for an invalid request.  Host-only. */
+const char* ttt_path_name(const ttt_handle* h, int loss, int inner, int chunk);
+
+/* Release a handle (NULL is a no-op). */
+int ttt_destroy(ttt_handle* h);
+
+/* Message of the last failure on this handle (or of the last ttt_create when h
+ * is NULL); never NULL, "" when there was none. */
+const char* ttt_last_error(const ttt_handle* h);
+
+/* Static description of a status code. */
+const char* ttt_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H_ */

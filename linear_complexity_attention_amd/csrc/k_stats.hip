@@ -1,0 +1,182 @@
+// Key instance-normalisation statistics (Test-Time Training vs Sleep page,
+// section "Side one": keys carry a constant shift that must be removed before
+// the inner optimisation).  Per (batch, head, channel), over the N tokens:
+// mean and 1/sqrt(biased variance + eps).
+//
+// Two kernels: every workgroup reduces one token slice of one (b, h) pair to
+// (count, mean, M2) per channel with a two-pass sum over the slice (the second
+// pass hits L2), so the whole chip streams K once from HBM; a tiny second
+// kernel merges the slices with Chan's parallel-variance formula.
+#include "ttt_internal.h"
+
+namespace ttt {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* x);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float* x) {
+  bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* x) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// d % 8 == 0: each thread owns 8 consecutive channels of one token row; the
+// workgroup walks the slice R = 256/(d/8) rows at a time.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) k_stats_partial_v8(const T* __restrict__ k, int N, int d,
+                                                               int S, float* __restrict__ part) {
+  const int s = blockIdx.x, p = blockIdx.y;
+  const int L = (N + S - 1) / S;
+  const int n0 = s * L, n1 = min(N, n0 + L);
+  const int groups = d >> 3;
+  const int R = kThreads / groups;
+  const int cg = threadIdx.x % groups, r = threadIdx.x / groups;
+  const bool active = r < R;
+  const T* base = k + (size_t)p * N * d + cg * 8;
+  __shared__ float red[kThreads][8];
+  __shared__ float mean_s[128];
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (active)
+    for (int n = n0 + r; n < n1; n += R) {
+      float x[8];
+      load8<T>(base + (size_t)n * d, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += x[i];
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[threadIdx.x][i] = active ? acc[i] : 0.f;
+  __syncthreads();
+  const int cnt = max(n1 - n0, 0);
+  if (threadIdx.x < d) {
+    const int c = threadIdx.x, g = c >> 3, j = c & 7;
+    float sum = 0.f;
+    for (int rr = 0; rr < R; ++rr) sum += red[rr * groups + g][j];
+    mean_s[c] = cnt ? sum / (float)cnt : 0.f;
+  }
+  __syncthreads();
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { m[i] = mean_s[cg * 8 + i]; acc[i] = 0.f; }
+  if (active)
+    for (int n = n0 + r; n < n1; n += R) {
+      float x[8];
+      load8<T>(base + (size_t)n * d, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { float t = x[i] - m[i]; acc[i] += t * t; }
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[threadIdx.x][i] = active ? acc[i] : 0.f;
+  __syncthreads();
+  if (threadIdx.x < d) {
+    const int c = threadIdx.x, g = c >> 3, j = c & 7;
+    float m2 = 0.f;
+    for (int rr = 0; rr < R; ++rr) m2 += red[rr * groups + g][j];
+    float* o = part + ((size_t)p * S + s) * 3 * d;
+    o[c] = (float)cnt;
+    o[d + c] = mean_s[c];
+    o[2 * d + c] = m2;
+  }
+}
+
+// any d <= 256: thread = (channel, row lane)
+template <typename T>
+__global__ void __launch_bounds__(kThreads) k_stats_partial_scalar(const T* __restrict__ k, int N, int d,
+                                                                   int S, float* __restrict__ part) {
+  const int s = blockIdx.x, p = blockIdx.y;
+  const int L = (N + S - 1) / S;
+  const int n0 = s * L, n1 = min(N, n0 + L);
+  const int R = kThreads / d;
+  const int c = threadIdx.x % d, r = threadIdx.x / d;
+  const bool active = r < R;
+  const T* base = k + (size_t)p * N * d + c;
+  __shared__ float red[kThreads];
+  __shared__ float mean_s[256];
+  float acc = 0.f;
+  if (active)
+    for (int n = n0 + r; n < n1; n += R) acc += to_f32<T>(base[(size_t)n * d]);
+  red[threadIdx.x] = active ? acc : 0.f;
+  __syncthreads();
+  const int cnt = max(n1 - n0, 0);
+  if (threadIdx.x < d) {
+    float sum = 0.f;
+    for (int rr = 0; rr < R; ++rr) sum += red[rr * d + threadIdx.x];
+    mean_s[threadIdx.x] = cnt ? sum / (float)cnt : 0.f;
+  }
+  __syncthreads();
+  const float m = mean_s[c];
+  acc = 0.f;
+  if (active)
+    for (int n = n0 + r; n < n1; n += R) { float t = to_f32<T>(base[(size_t)n * d]) - m; acc += t * t; }
+  __syncthreads();
+  red[threadIdx.x] = active ? acc : 0.f;
+  __syncthreads();
+  if (threadIdx.x < d) {
+    float m2 = 0.f;
+    for (int rr = 0; rr < R; ++rr) m2 += red[rr * d + threadIdx.x];
+    float* o = part + ((size_t)p * S + s) * 3 * d;
+    o[threadIdx.x] = (float)cnt;
+    o[d + threadIdx.x] = mean_s[threadIdx.x];
+    o[2 * d + threadIdx.x] = m2;
+  }
+}
+
+// Chan et al.'s pairwise combination, applied slice by slice in a fixed order.
+__global__ void k_stats_final(const float* __restrict__ part, int P, int S, int d, float eps,
+                              float* __restrict__ stats) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P * d) return;
+  const int p = i / d, c = i % d;
+  double n = 0.0, mean = 0.0, m2 = 0.0;
+  for (int s = 0; s < S; ++s) {
+    const float* o = part + ((size_t)p * S + s) * 3 * d;
+    const double nb = o[c];
+    if (nb == 0.0) continue;
+    const double mb = o[d + c], m2b = o[2 * d + c];
+    const double nt = n + nb, delta = mb - mean;
+    mean += delta * nb / nt;
+    m2 += m2b + delta * delta * n * nb / nt;
+    n = nt;
+  }
+  const double var = n > 0.0 ? m2 / n : 0.0;
+  stats[(size_t)i * 2] = (float)mean;
+  stats[(size_t)i * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
+}
+
+}  // namespace
+
+void launch_stats_partial(const Problem& pb, int S, float* part, hipStream_t st) {
+  const int P = pb.B * pb.H;
+  dim3 grid(S, P);
+  if (pb.d % 8 == 0 && pb.d <= 128) {
+    if (pb.bf16)
+      hipLaunchKernelGGL(k_stats_partial_v8<bf16>, grid, dim3(kThreads), 0, st, (const bf16*)pb.k, pb.N, pb.d, S, part);
+    else
+      hipLaunchKernelGGL(k_stats_partial_v8<float>, grid, dim3(kThreads), 0, st, (const float*)pb.k, pb.N, pb.d, S, part);
+  } else {
+    if (pb.bf16)
+      hipLaunchKernelGGL(k_stats_partial_scalar<bf16>, grid, dim3(kThreads), 0, st, (const bf16*)pb.k, pb.N, pb.d, S, part);
+    else
+      hipLaunchKernelGGL(k_stats_partial_scalar<float>, grid, dim3(kThreads), 0, st, (const float*)pb.k, pb.N, pb.d, S, part);
+  }
+}
+
+void launch_stats_final(const Problem& pb, int S, const float* part, float eps, float* stats, hipStream_t st) {
+  const int P = pb.B * pb.H;
+  const int n = P * pb.d;
+  hipLaunchKernelGGL(k_stats_final, dim3((n + 255) / 256), dim3(256), 0, st, part, P, S, pb.d, eps, stats);
+}
+
+}  // namespace ttt

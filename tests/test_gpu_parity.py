@@ -1,0 +1,213 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 oracle
+on the same seeded inputs.  Pass bar: max|O_gpu - O_ref| / max|O_ref| <= 1e-2
+on the bf16 path and <= 1e-4 on the fp32 path, and the same bound on the
+update itself (dW = W_out - W0, dO = O - F_W0(Q)) so that a wrong backward
+cannot hide behind a small step."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ttt_oracle as orc
+from synth_inputs import WORKLOADS, Workload
+from tests.gpu_common import TOL, device_inputs, rel_err, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+GENERIC = 0x2   # TTT_FLAG_FORCE_GENERIC
+
+
+def _w0_pair(exact, b, h):
+    return [m[h] if m.ndim == 3 else m[b, h] for m in exact["W0"]]
+
+
+def _check_pairs(w, dev_in, exact, pairs, *, flags=0, tol=None, eta=None, chunk=None, tag=""):
+    tol = TOL[w.dtype] if tol is None else tol
+    O, W_out, path = run_gpu(w, dev_in, flags=flags, eta=eta, chunk=chunk)
+    O_ref, W_ref = run_oracle(w, exact, pairs=pairs, eta=eta, chunk=chunk)
+    Og = O.float().cpu().numpy()
+    Wg = [m.cpu().numpy() for m in W_out]
+    for i, (b, h) in enumerate(pairs):
+        e = rel_err(Og[b, h], O_ref[i])
+        assert e <= tol, f"{tag} O pair {(b, h)} rel err {e:.3e} > {tol} (path {path})"
+        w0 = _w0_pair(exact, b, h)
+        for m in range(len(w0)):
+            dW_ref = W_ref[i][m] - w0[m]
+            if np.max(np.abs(dW_ref)) == 0.0:
+                np.testing.assert_allclose(Wg[m][b, h], W_ref[i][m], atol=1e-6)
+                continue
+            e = rel_err(Wg[m][b, h] - w0[m], dW_ref)
+            assert e <= tol, f"{tag} dW{m} pair {(b, h)} rel err {e:.3e} > {tol} (path {path})"
+    return O, W_out, path
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+def test_c1_tiny_fp32_full():
+    w = WORKLOADS["c1_tiny_fp32"]
+    dev_in, exact = device_inputs(w)
+    O, W_out, path = _check_pairs(w, dev_in, exact, [(0, 0)], tag="c1")
+    # the output change caused by the update, against the oracle's
+    O0 = orc.oracle_readout(exact["q"], [m[None] for m in exact["W0"]], w.inner)
+    O_ref, _ = run_oracle(w, exact)
+    assert rel_err(O.double().cpu().numpy() - O0, O_ref - O0) <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["c2_vits_r1", "c2_vits_r4"])
+def test_c2_vit_small_all_pairs(name):
+    w = WORKLOADS[name]
+    dev_in, exact = device_inputs(w)
+    O, W_out, path = run_gpu(w, dev_in)
+    O_ref, W_ref = run_oracle(w, exact)
+    assert rel_err(O.float().cpu().numpy(), O_ref) <= 1e-2, path
+    for m in range(2):
+        dW = W_out[m].cpu().numpy() - exact["W0"][m][None]
+        assert rel_err(dW, W_ref[m] - exact["W0"][m][None]) <= 1e-2, (path, m)
+
+
+def test_c3_hires_sampled_pairs():
+    w = WORKLOADS["c3_hires_r4"]
+    dev_in, exact = device_inputs(w)
+    _check_pairs(w, dev_in, exact, [(0, 0), (3, 7), (7, 11)], tag="c3")
+
+
+def test_c4_dit_sampled_pairs():
+    w = WORKLOADS["c4_dit_h64"]
+    dev_in, exact = device_inputs(w)
+    _check_pairs(w, dev_in, exact, [(0, 0), (1, 23)], tag="c4")
+
+
+def test_c5_lact_sampled_pairs():
+    w = WORKLOADS["c5_lact_swiglu"]
+    dev_in, exact = device_inputs(w)
+    _check_pairs(w, dev_in, exact, [(0, 1), (0, 3)], tag="c5")
+
+
+# ---------------------------------------------------------------------------
+# Every inner model x loss x mode, several tiles with a ragged tail
+# ---------------------------------------------------------------------------
+COMBOS = [
+    ("mlp_gelu", "mse", 0, True, False),
+    ("mlp_gelu", "dot", 0, True, False),
+    ("swiglu", "dot", 0, True, True),
+    ("swiglu", "mse", 0, False, False),
+    ("linear", "mse", 0, True, False),
+    ("linear", "dot", 0, False, True),
+    ("swiglu", "dot", 96, False, True),
+    ("mlp_gelu", "mse", 100, False, False),
+    ("mlp_gelu", "dot", 64, False, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("inner,loss,chunk,key_norm,renorm", COMBOS)
+@pytest.mark.parametrize("generic", [False, True])
+def test_combos_ragged(inner, loss, chunk, key_norm, renorm, dtype, generic):
+    w = Workload("combo", B=2, H=3, N=333, d=64, hidden=128, dtype=dtype, inner=inner, loss=loss, chunk=chunk,
+                 key_norm=key_norm, renorm=renorm, per_token_eta=(loss == "dot"), seed=77,
+                 unit_columns=renorm, eta=1.0 if loss == "mse" else 0.5)
+    dev_in, exact = device_inputs(w)
+    _check_pairs(w, dev_in, exact, [(0, 0), (1, 2)], flags=GENERIC if generic else 0,
+                 tag=f"{inner}/{loss}/{chunk}/{dtype}/{'gen' if generic else 'auto'}")
+
+
+@pytest.mark.parametrize("d,hidden,N", [(32, 32, 256), (64, 64, 130), (64, 256, 517), (128, 256, 300),
+                                        (16, 48, 77), (64, 192, 250)])
+def test_shapes_mlp_mse(d, hidden, N):
+    w = Workload("shape", B=1, H=2, N=N, d=d, hidden=hidden, seed=5 + d + hidden + N)
+    dev_in, exact = device_inputs(w)
+    _check_pairs(w, dev_in, exact, [(0, 0), (0, 1)], tag=f"shape d={d} h={hidden} N={N}")
+
+
+def test_large_eta_exposes_backward():
+    """100x the step: the update dominates O, so an error in dW shows in O."""
+    w = Workload("eta100", B=2, H=2, N=1000, d=64, hidden=256, seed=31, eta=100.0)
+    dev_in, exact = device_inputs(w)
+    _check_pairs(w, dev_in, exact, [(0, 0), (1, 1)], tag="eta100")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+def test_single_token_with_key_norm_keeps_w0():
+    w = Workload("n1", B=2, H=2, N=1, d=64, hidden=64, seed=41)
+    dev_in, exact = device_inputs(w)
+    O, W_out, _ = run_gpu(w, dev_in)
+    for m, w0 in zip(W_out, dev_in[3]):
+        torch.testing.assert_close(m, w0[None].expand_as(m), rtol=0, atol=1e-7)
+    O_ref, _ = run_oracle(w, exact)
+    assert rel_err(O.float().cpu().numpy(), O_ref) <= 1e-2
+
+
+def test_eta_zero_reads_w0():
+    w = Workload("eta0", B=1, H=3, N=200, d=64, hidden=256, seed=42, eta=0.0)
+    dev_in, exact = device_inputs(w)
+    O, W_out, _ = run_gpu(w, dev_in)
+    O0 = orc.oracle_readout(exact["q"], [m[None] for m in exact["W0"]], w.inner)
+    assert rel_err(O.float().cpu().numpy(), O0) <= 1e-2
+
+
+# (chunk, N, eta): many sequential updates make the recurrence sensitive to
+# rounding (a relative perturbation of W0 grows with every chunk), so the step
+# sizes are chosen where the oracle's own amplification of a 1e-6 perturbation
+# stays below ~10x; the stress workload c5 is covered above.
+@pytest.mark.parametrize("chunk,N,eta", [(1, 40, 0.2), (7, 333, 0.1), (333, 333, 0.5), (5000, 333, 0.5)])
+def test_chunk_edges(chunk, N, eta):
+    w = Workload("chunks", B=1, H=2, N=N, d=64, hidden=128, inner="swiglu", loss="dot", chunk=chunk,
+                 key_norm=False, renorm=True, per_token_eta=True, unit_columns=True, seed=43, eta=eta)
+    dev_in, exact = device_inputs(w)
+    _check_pairs(w, dev_in, exact, [(0, 0), (0, 1)], tag=f"chunk={chunk}")
+
+
+def test_batch_specific_w0_and_continuation():
+    """W0 with a batch axis, and a sequence split at a chunk boundary into two
+    calls (the second seeded with W_out of the first) equals one call."""
+    w = Workload("cont", B=2, H=2, N=256, d=64, hidden=128, inner="swiglu", loss="dot", chunk=64,
+                 key_norm=False, renorm=True, per_token_eta=True, unit_columns=True, seed=44)
+    dev_in, exact = device_inputs(w, shared_w0=False)
+    _check_pairs(w, dev_in, exact, [(0, 1), (1, 0)], tag="bstride")
+    tq, tk, tv, tW, tet = dev_in
+    O_full, W_full, _ = run_gpu(w, dev_in)
+    half = lambda t: t[:, :, :128].contiguous()
+    rest = lambda t: t[:, :, 128:].contiguous()
+    w_half = Workload(**{**w.__dict__, "N": 128})
+    O1, W1, _ = run_gpu(w_half, (half(tq), half(tk), half(tv), tW, half(tet)))
+    O2, W2, _ = run_gpu(w_half, (rest(tq), rest(tk), rest(tv), W1, rest(tet)))
+    got = torch.cat([O1, O2], dim=2).float()
+    assert (got - O_full.float()).abs().max().item() <= 1e-2 * O_full.float().abs().max().item()
+    for a, b in zip(W2, W_full):
+        assert (a - b).abs().max().item() <= 1e-4 * b.abs().max().item()
+
+
+def test_deterministic_bitwise():
+    w = Workload("det", B=2, H=3, N=1500, d=64, hidden=256, seed=45)
+    dev_in, _ = device_inputs(w)
+    O1, W1, _ = run_gpu(w, dev_in)
+    O2, W2, _ = run_gpu(w, dev_in)
+    assert torch.equal(O1, O2)
+    for a, b in zip(W1, W2):
+        assert torch.equal(a, b)
+
+
+def test_check_finite_flag():
+    from linear_complexity_attention_amd import ttt
+
+    w = Workload("nan", B=1, H=2, N=100, d=64, hidden=64, seed=46)
+    dev_in, _ = device_inputs(w)
+    tq, tk, tv, tW, tet = dev_in
+    layer = ttt.TTTLayer(1, 2, 100, 64, 64, dtype="bf16", flags=ttt.TTT_FLAG_CHECK_FINITE)
+    layer.forward(tq, tk, tv, tW)            # clean inputs pass
+    tv2 = tv.clone()
+    tv2[0, 1, 17, 3] = float("nan")
+    with pytest.raises(ttt.TTTError) as ei:
+        layer.forward(tq, tk, tv2, tW)
+    assert ei.value.status == ttt.TTT_ERR_NONFINITE
+
+
+def test_generic_and_fast_paths_agree():
+    w = WORKLOADS["c2_vits_r4"]
+    dev_in, _ = device_inputs(w, B=4)
+    Oa, Wa, pa = run_gpu(w, dev_in)
+    Ob, Wb, pb = run_gpu(w, dev_in, flags=GENERIC)
+    assert pb == "generic"
+    assert rel_err(Oa.float().cpu().numpy(), Ob.float().cpu().numpy()) <= 1e-2
