@@ -160,6 +160,16 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v,
  * "mfma_full_mlp" or "generic"; NULL for an invalid request.  Host-only. */
 const char* ttt_path_name(const ttt_handle* h, int loss, int inner, int chunk);
 
+/* Measurement hook: with n_events == 8 and events[] holding hipEvent_t
+ * handles created by the caller, every later ttt_forward on this handle
+ * records events[2k] on its stream right before and events[2k+1] right after
+ * kernel family k: 0 key statistics, 1 gradient of the first update batch,
+ * 2 weight update of the first batch, 3 readout.  A family that does not run
+ * (no key norm) records both of its events back to back.  events == NULL or
+ * n_events == 0 switches the hook off.  The events are not owned by the
+ * library.  Host-only; returns TTT_ERR_INVALID for any other n_events. */
+int ttt_set_timing_events(ttt_handle* h, void* const* events, int n_events);
+
 /* Release a handle (NULL is a no-op). */
 int ttt_destroy(ttt_handle* h);
 

@@ -22,9 +22,26 @@ constexpr int kLanes = 4;
 // bf16 operand layouts:
 //   BF_ROWMAJOR   : [in][out] like the fp32 matrix
 //   BF_TRANSPOSED : [out][in]
+//   BF_MLP3       : GELU-MLP MFMA operands, per pair [W1^T (h x d) | W2 (h x d) | W2^T (d x h)]
 __device__ __forceinline__ long long bf16_index(int layout, int r, int c, int rows, int cols) {
   return layout == BF_TRANSPOSED ? (long long)c * rows + r : (long long)r * cols + c;
 }
+
+__device__ __forceinline__ void store_bf(bf16* pair_base, int layout, int i, long long msz, int r, int c,
+                                         int rows, int cols, float w) {
+  const bf16 v = (bf16)w;
+  if (layout == BF_MLP3) {
+    if (i == 0) pair_base[(long long)c * rows + r] = v;            // W1^T [h][d]
+    else {
+      pair_base[msz + (long long)r * cols + c] = v;                 // W2   [h][d]
+      pair_base[2 * msz + (long long)c * rows + r] = v;             // W2^T [d][h]
+    }
+    return;
+  }
+  pair_base[i * msz + bf16_index(layout, r, c, rows, cols)] = v;
+}
+
+__device__ __forceinline__ int bf_pair_mats(int layout, int nm) { return layout == BF_MLP3 ? 3 : nm; }
 
 __device__ __forceinline__ void mat_dims(const Problem& pb, int i, int& rows, int& cols) {
   if (pb.inner == INNER_LINEAR) { rows = pb.d; cols = pb.d; return; }
@@ -43,16 +60,33 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update(Problem pb, UpdateArg
   const bool live = j < cols;
   const float* cur = a.cur.mat(i, b, h);
   const float* w0 = a.w0.mat(i, b, h);
-  const float* part = a.part ? a.part + (size_t)p * pb.nm * pb.msz + (size_t)i * pb.msz : nullptr;
   float* nxt = a.next + ((size_t)p * pb.nm + i) * pb.msz;
+  // stream-K: workgroups [wg0, wg1] of the gradient kernel touched pair p
+  long long wg0 = 0, wg1 = -1, sk_total = 0;
+  if (a.part_mode == PART_STREAMK) {
+    sk_total = (long long)pb.B * pb.H * a.sk_tpp;
+    const long long xa = (long long)p * a.sk_tpp, xb = xa + a.sk_tpp - 1;
+    wg0 = ((xa + 1) * a.sk_G - 1) / sk_total;
+    wg1 = ((xb + 1) * a.sk_G - 1) / sk_total;
+  }
   __shared__ float red[2][kLanes][kCols];
   float nn = 0.f, nr = 0.f;
   if (live)
     for (int r = lane; r < rows; r += kLanes) {
       const size_t e = (size_t)r * cols + j;
       float w = cur[e];
-      if (part)
-        for (int s = 0; s < a.S; ++s) w -= part[s * a.part_pair_stride + e];
+      if (a.part) {
+        if (a.part_mode == PART_SPLITS) {
+          const float* pp = a.part + (size_t)p * pb.nm * pb.msz + (size_t)i * pb.msz;
+          for (int s = 0; s < a.S; ++s) w -= pp[s * a.part_pair_stride + e];
+        } else {
+          for (long long q = wg0; q <= wg1; ++q) {
+            const long long first = ((q * sk_total) / a.sk_G) / a.sk_tpp;
+            const float* pp = a.part + (q * a.sk_J + (p - first)) * pb.nm * pb.msz + (size_t)i * pb.msz;
+            w -= pp[e];
+          }
+        }
+      }
       nxt[e] = w;
       nn += w * w;
       const float w0v = w0[e];
@@ -69,13 +103,13 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update(Problem pb, UpdateArg
   }
   if (!live) return;
   float* out = a.out[i] ? a.out[i] + (size_t)p * pb.msz : nullptr;
-  bf16* bfo = a.bf ? a.bf + ((size_t)p * pb.nm + i) * pb.msz : nullptr;
+  bf16* bfo = a.bf ? a.bf + (size_t)p * bf_pair_mats(a.bf_layout, pb.nm) * pb.msz : nullptr;
   for (int r = lane; r < rows; r += kLanes) {
     const size_t e = (size_t)r * cols + j;
     float w = nxt[e];
     if (a.renorm) { w *= scale; nxt[e] = w; }
     if (out) out[e] = w;
-    if (bfo) bfo[bf16_index(a.bf_layout, r, j, rows, cols)] = (bf16)w;
+    if (bfo) store_bf(bfo, a.bf_layout, i, pb.msz, r, j, rows, cols, w);
   }
 }
 
@@ -85,10 +119,10 @@ __global__ void __launch_bounds__(256) k_convert_bf16(Problem pb, WRef W, bf16* 
   int rows, cols;
   mat_dims(pb, i, rows, cols);
   const float* src = W.mat(i, b, h);
-  bf16* o = dst + ((size_t)p * pb.nm + i) * pb.msz;
+  bf16* o = dst + (size_t)p * bf_pair_mats(layout, pb.nm) * pb.msz;
   for (long long e = blockIdx.x * 256 + threadIdx.x; e < (long long)rows * cols; e += (long long)gridDim.x * 256) {
     const int r = (int)(e / cols), c = (int)(e % cols);
-    o[bf16_index(layout, r, c, rows, cols)] = (bf16)src[e];
+    store_bf(o, layout, i, pb.msz, r, c, rows, cols, src[e]);
   }
 }
 

@@ -25,6 +25,8 @@ using namespace ttt;
 struct ttt_handle {
   ttt_config cfg;
   std::string err;
+  hipEvent_t events[8] = {};
+  bool timing = false;
 };
 
 namespace {
@@ -57,7 +59,9 @@ struct Plan {
   long long msz, wsz;                // elements per matrix / per pair
   // choices
   bool mfma_grad, mfma_query;
-  int S_stats, S_grad;
+  int S_stats, S_grad;               // S_grad: partial slots of the gradient kernel
+  int sk_G, sk_J;                    // stream-K geometry (MFMA gradient kernel)
+  int bf_layout, bf_mats;            // bf16 operand copies: layout and matrices per pair
   // byte offsets
   size_t off_stats_part, off_stats, off_states, off_part, off_gbuf, off_bf, off_flag, total;
   long long state_stride;            // floats between consecutive states
@@ -114,11 +118,16 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk) {
   pl.msz = pb.msz;
   pl.wsz = pb.msz * pb.nm;
   const bool generic_only = (c.flags & TTT_FLAG_FORCE_GENERIC) != 0;
-  pl.mfma_grad = !generic_only && mfma_full_supported(pb);
+  // A chain of several causal updates feeds each step's rounding into the next
+  // (the recurrence amplifies weight perturbations), so bf16 weight operands are
+  // used for a single update only; multi-chunk MLP gradients stay in fp32.
+  pl.mfma_grad = !generic_only && mfma_full_supported(pb) && pl.nb == 1;
   pl.mfma_query = !generic_only && mfma_query_supported(pb);
   pl.S_stats = c.key_norm ? choose_splits(pl.P, c.N, 64, 1024) : 0;
   if (pl.mfma_grad) {
-    pl.S_grad = mfma_full_splits(pb, pl.span);
+    int tpp_unused;
+    mfma_grad_geometry(pb, pl.span, &pl.sk_G, &pl.sk_J, &tpp_unused);
+    pl.S_grad = pl.sk_G * pl.sk_J;   // partial slots
   } else {
     const int outw = inner == TTT_INNER_LINEAR ? c.d : pb.hid;
     pl.S_grad = choose_splits((long long)pl.P * ((outw + 31) / 32), pl.span, 16, 1024);
@@ -132,11 +141,13 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk) {
   pl.state_stride = (long long)pl.P * pl.wsz;
   off = align256(off + sizeof(float) * (size_t)pl.nb * pl.state_stride);
   pl.off_part = off;
-  off = align256(off + sizeof(float) * (size_t)pl.S_grad * pl.P * pl.wsz);
+  off = align256(off + sizeof(float) * (size_t)pl.S_grad * (pl.mfma_grad ? 1 : pl.P) * pl.wsz);
   pl.off_gbuf = off;
   if (!pl.mfma_grad) off = align256(off + sizeof(float) * (size_t)pl.P * pl.span * c.d);
   pl.off_bf = off;
-  pl.bf_stride = (long long)pl.P * pl.wsz;
+  pl.bf_layout = pb.inner == INNER_MLP ? BF_MLP3 : BF_ROWMAJOR;
+  pl.bf_mats = pl.bf_layout == BF_MLP3 ? 3 : pl.nm;
+  pl.bf_stride = (long long)pl.P * pl.bf_mats * pl.msz;
   if (pl.mfma_grad || pl.mfma_query) off = align256(off + sizeof(uint16_t) * (size_t)(pl.nb + 1) * pl.bf_stride);
   pl.off_flag = off;
   off = align256(off + 64);
@@ -185,6 +196,18 @@ int ttt_create(const ttt_config* cfg, ttt_handle** out) {
   if (!h) return fail(nullptr, TTT_ERR_INVALID, "out of host memory");
   h->cfg = c;
   *out = h;
+  return TTT_OK;
+}
+
+int ttt_set_timing_events(ttt_handle* h, void* const* events, int n_events) {
+  if (!h) return fail(nullptr, TTT_ERR_INVALID, "handle is NULL");
+  if (!events || n_events == 0) { h->timing = false; return TTT_OK; }
+  if (n_events != 8) return fail(h, TTT_ERR_INVALID, "n_events must be 8 (got %d)", n_events);
+  for (int i = 0; i < 8; ++i) {
+    if (!events[i]) return fail(h, TTT_ERR_INVALID, "events[%d] is NULL", i);
+    h->events[i] = reinterpret_cast<hipEvent_t>(events[i]);
+  }
+  h->timing = true;
   return TTT_OK;
 }
 
@@ -275,44 +298,60 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
   // hipGetLastError is per thread and sticky: drop an error some earlier,
   // unrelated runtime call left behind so that only our launches are judged.
   (void)hipGetLastError();
+  auto mark = [&](int i) {
+    if (h->timing) (void)hipEventRecord(h->events[i], st);
+  };
+  mark(0);
   if (c.key_norm) {
     launch_stats_partial(pb, pl.S_stats, stats_part, st);
     launch_stats_final(pb, pl.S_stats, stats_part, c.eps, stats, st);
   }
+  mark(1);
   const bool need_bf = pl.mfma_grad || pl.mfma_query;
-  const int bf_layout = BF_ROWMAJOR;
+  const int bf_layout = pl.bf_layout;
   if (need_bf) launch_convert_bf16(pb, w0, bfs, bf_layout, st);   // bf16 state 0
 
   for (int b = 0; b < pl.nb; ++b) {
     const int t0 = chunk ? b * chunk : 0;
     const int nt = chunk ? std::min(chunk, c.N - t0) : c.N;
     const WRef cur = b == 0 ? w0 : state_ref(b);
+    if (b == 0) mark(2);
     if (pl.mfma_grad) {
-      launch_mfma_full_grad(pb, bfs + (long long)b * pl.bf_stride, t0, nt, pl.S_grad, part, st);
+      // the kernel accumulates eta_n-weighted (V_hat - V) or -eta_n V; the
+      // scalar eta and the MSE constant 2/(n_b d) are applied to its partials
+      const float scale = pb.loss == LOSS_MSE ? eta->scale * 2.0f / ((float)nt * (float)c.d) : eta->scale;
+      launch_mfma_full_grad(pb, bfs + (long long)b * pl.bf_stride, t0, nt, scale, part, st);
     } else {
       launch_gen_grad_out(pb, cur, t0, nt, gbuf, st);
       launch_gen_dW(pb, cur, t0, nt, gbuf, pl.S_grad, part, st);
     }
+    if (b == 0) mark(3);
     UpdateArgs ua{};
     ua.cur = cur;
     ua.w0 = w0;
     ua.part = part;
+    ua.part_mode = pl.mfma_grad ? PART_STREAMK : PART_SPLITS;
     ua.S = pl.S_grad;
     ua.part_pair_stride = (long long)pl.P * pl.wsz;
+    if (pl.mfma_grad) mfma_grad_geometry(pb, nt, &ua.sk_G, &ua.sk_J, &ua.sk_tpp);
     ua.next = states + (long long)b * pl.state_stride;
     const bool last = b == pl.nb - 1;
     for (int i = 0; i < 3; ++i) ua.out[i] = (last && W_out && i < nm) ? W_out->w[i] : nullptr;
     ua.bf = need_bf ? bfs + (long long)(b + 1) * pl.bf_stride : nullptr;
     ua.bf_layout = bf_layout;
     ua.renorm = c.renorm;
+    if (b == 0) mark(4);
     launch_update(pb, ua, st);
+    if (b == 0) mark(5);
   }
 
+  mark(6);
   if (pl.mfma_query) {
     launch_mfma_query(pb, bfs, pl.bf_stride, chunk ? pl.nb : 1, chunk, st);
   } else {
     launch_gen_query(pb, w0, states, pl.state_stride, chunk ? pl.nb : 1, chunk, st);
   }
+  mark(7);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
 

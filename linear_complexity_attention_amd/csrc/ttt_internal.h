@@ -8,7 +8,7 @@ namespace ttt {
 
 enum { INNER_LINEAR = 0, INNER_MLP = 1, INNER_SWIGLU = 2 };
 enum { LOSS_MSE = 0, LOSS_DOT = 1 };
-enum { BF_ROWMAJOR = 0, BF_TRANSPOSED = 1 };
+enum { BF_ROWMAJOR = 0, BF_TRANSPOSED = 1, BF_MLP3 = 2 };
 
 // Everything a kernel of one update batch (the whole sequence in full-batch
 // mode, one chunk in causal mode) needs to know.
@@ -48,28 +48,37 @@ void launch_gen_query(const Problem& pb, const WRef& w0, const float* states, lo
 // operand copy (layout chosen by `bf_layout`, see update.hip).
 struct UpdateArgs {
   WRef cur, w0;
-  const float* part; int S; long long part_pair_stride;  // part[s][p][nm][msz]
+  const float* part;            // gradient partials (already scaled by eta and the loss constant)
+  int part_mode;                // PART_SPLITS: part[s][p][nm][msz], s < S
+                                // PART_STREAMK: slot (i*J + p - first_pair(i)) of workgroup i
+  int S; long long part_pair_stride;
+  int sk_G, sk_J, sk_tpp;       // stream-K geometry of the gradient kernel
   float* next;                  // [P][nm][msz] fp32
   float* out[3];                // W_out matrices [B,H,in,out] or null
   bf16* bf;                     // bf16 operand copy or null
   int bf_layout;
   int renorm;
 };
+enum { PART_SPLITS = 0, PART_STREAMK = 1 };
 void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st);
 // bf16 operand copy of a weight state without an update (W0 for the first
 // gradient pass of the MFMA kernels)
 void launch_convert_bf16(const Problem& pb, const WRef& W, bf16* dst, int bf_layout, hipStream_t st);
 
 // ---- MFMA fast paths --------------------------------------------------------
-// full-h fused forward/backward of the GELU MLP on bf16 MFMA (d = 64, h in {64,128,256})
+// GELU-MLP, d = 64, h in {64,128,256}, bf16: fused forward/backward of one
+// update batch (tokens [t0, t0+nt)) on bf16 MFMA, stream-K over the pairs'
+// tiles; partials land in BF_MLP3-ordered slots (see mfma_grad_geometry).
 bool mfma_full_supported(const Problem& pb);
-int mfma_full_splits(const Problem& pb, int nt);
-void launch_mfma_full_grad(const Problem& pb, const bf16* Wbf, int t0, int nt, int S, float* part,
+void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_per_pair);
+void launch_mfma_full_grad(const Problem& pb, const bf16* wbf, int t0, int nt, float scale, float* part,
                            hipStream_t st);
-// query readout O = F_W(Q) on bf16 MFMA
+// readout O = F_W(Q) on bf16 MFMA; wstates: bf16 BF_MLP3 states, state s at
+// wstates + s*state_stride (state 0 = W0); full batch reads state 1, causal
+// chunk c reads state c.
 bool mfma_query_supported(const Problem& pb);
-void launch_mfma_query(const Problem& pb, const bf16* Wbf, long long state_stride, int nchunks,
-                       int chunk, hipStream_t st);
+void launch_mfma_query(const Problem& pb, const bf16* wstates, long long state_stride, int nchunks, int chunk,
+                       hipStream_t st);
 
 // ---- finiteness check ------------------------------------------------------
 void launch_zero_flag(int* flag, hipStream_t st);

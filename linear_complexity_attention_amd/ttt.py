@@ -71,6 +71,8 @@ _lib.ttt_forward.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(ttt
                              c_void_p]
 _lib.ttt_path_name.restype = c_char_p
 _lib.ttt_path_name.argtypes = [c_void_p, c_int, c_int, c_int]
+_lib.ttt_set_timing_events.restype = c_int
+_lib.ttt_set_timing_events.argtypes = [c_void_p, POINTER(c_void_p), c_int]
 _lib.ttt_destroy.restype = c_int
 _lib.ttt_destroy.argtypes = [c_void_p]
 _lib.ttt_last_error.restype = c_char_p
@@ -79,7 +81,7 @@ _lib.ttt_status_string.restype = c_char_p
 _lib.ttt_status_string.argtypes = [c_int]
 
 EXPORTED = ("ttt_version", "ttt_create", "ttt_workspace_bytes", "ttt_forward", "ttt_path_name",
-            "ttt_destroy", "ttt_last_error", "ttt_status_string")
+            "ttt_set_timing_events", "ttt_destroy", "ttt_last_error", "ttt_status_string")
 
 
 class TTTError(RuntimeError):
@@ -124,6 +126,17 @@ def ttt_workspace_bytes(handle, loss: int, inner: int, chunk: int) -> int:
 def ttt_path_name(handle, loss: int, inner: int, chunk: int):
     r = _lib.ttt_path_name(handle, loss, inner, chunk)
     return r.decode() if r is not None else None
+
+
+def ttt_set_timing_events(handle, events) -> None:
+    """events: sequence of 8 hipEvent_t handles (ints), or None to switch off."""
+    if events is None:
+        rc = _lib.ttt_set_timing_events(handle, None, 0)
+    else:
+        arr = (c_void_p * len(events))(*events)
+        rc = _lib.ttt_set_timing_events(handle, arr, len(events))
+    if rc != TTT_OK:
+        raise TTTError(rc, ttt_last_error(handle))
 
 
 def ttt_forward(handle, q, k, v, W0: ttt_weights, eta: ttt_eta, loss: int, inner: int, chunk: int, o,
