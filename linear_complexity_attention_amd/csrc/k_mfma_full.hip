@@ -5,18 +5,25 @@
 // 02), fused per 32-token tile:
 //     K_hat = (K - mu) * rstd                     key instance norm (TvS page)
 //     Z  = K_hat W1,  A = gelu(Z),  V_hat = A W2   forward on the keys
-//     G' = eta_n (V_hat - V)   [MSE]  |  -eta_n V  [dot]   (constant 2/(n_b d) and
-//                                                         the scalar eta folded at the end)
+//     G' = eta_n (V_hat - V) [MSE]  |  -eta_n V [dot]    (the MSE constant 2/(n_b d)
+//                                                       and the scalar eta are
+//                                                       applied to the partials)
 //     dW2 += A^T G',  dA = G' W2^T,  dZ = dA * gelu'(Z),  dW1 += K_hat^T dZ
-// Each of the 4 waves owns a quarter of the hidden units (its slice of Z, A,
-// dA, dZ, dW1, dW2); the two products that mix hidden units (V_hat = A W2 and
-// the K_hat^T / G'^T operands) go through LDS.  The token range of all (b, h)
-// pairs is cut evenly over the grid ("stream-K"): a workgroup that crosses a
-// pair boundary writes one fp32 partial per pair it touched, and the update
-// kernel adds them in a fixed order, so the result is run-to-run identical.
+// Each wave owns a slice of the hidden units (its slice of Z, A, dA, dZ, dW1,
+// dW2, with the weight fragments of that slice held in registers).  The tiles
+// shared by all waves sit in LDS in their natural layouts and are written with
+// wide stores only: K and V as [token][channel]; A and G' as
+// [unit][token], tokens of a row stored in the order the MFMA output packs them
+// (so one lane writes its 8 tokens with one store).  Operands that need the
+// other orientation are fetched with the transposing LDS read
+// ds_read_b64_tr_b16.  The token range of all (b, h) pairs is cut evenly over
+// the grid ("stream-K"): a workgroup that crosses a pair boundary writes one
+// fp32 partial per pair it touched; the update kernel adds them in a fixed
+// order, so results are run-to-run identical.
 //
 // k_mfma_query: step (iii), O = gelu(Q W1*) W2*, with tokens on the MFMA lane
-// axis so that both products chain through registers; W1*, W2* sit in LDS.
+// axis so that both products chain through registers; the fp32 weights of the
+// pair's state are converted to bf16 into LDS (natural layouts) per workgroup.
 //
 // GELU here is z * sigma(y(z)), y = z (a + b z^2 + c z^4), a logistic fit of
 // the normal CDF (max |error| 3.7e-5 on gelu, 9.3e-5 on gelu', far below the
@@ -29,14 +36,22 @@ namespace {
 
 constexpr int D = 64;
 constexpr int TT = 32;            // tokens per tile
-constexpr int NWAVE = 4;
-constexpr int NTHR = NWAVE * 64;
-// LDS row strides (bf16 elements), padded against bank conflicts
-constexpr int KRS = D + 8;        // [T][D] tiles
-constexpr int KCS = TT + 4;       // [D][T] tiles
+constexpr int LDK = 80;           // [token][channel] tile row stride (bf16)
+constexpr int LDT = 36;           // [unit][token] tile row stride (bf16)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: the 16 lanes of each quarter-wave each name an 8-byte
+// row piece; lane i receives element (i % 4) of the pieces of lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4 (in that order).
+__device__ __forceinline__ bf16x4 ld_tr(const bf16* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)((__attribute__((address_space(3))) char*)p));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 // logistic fit of Phi: y = z (A + B t + C t^2), t = z^2, pre-scaled by -log2(e)
@@ -67,7 +82,6 @@ __device__ __forceinline__ void gelu_fast2(float z, float& a, float& gp) {
 }
 
 __device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ bf16x4 ld4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ bf16x8 cat44(const bf16x4& x, const bf16x4& y) {
   bf16x8 r;
 #pragma unroll
@@ -80,41 +94,60 @@ __device__ __forceinline__ bf16x8 pack8(const f32x4& x, const f32x4& y) {
   for (int i = 0; i < 4; ++i) { r[i] = (bf16)x[i]; r[4 + i] = (bf16)y[i]; }
   return r;
 }
+__device__ __forceinline__ bf16x4 pack4(const f32x4& x) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
+  return r;
+}
+// storage column of token t inside a 32-token [unit][token] row: the 8 tokens
+// of MFMA lane group g (4g..4g+3 and 16+4g..16+4g+3) are contiguous at 8g.
+__device__ __forceinline__ int tok_col(int t) { return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3); }
 
-// bf16 copy of one pair's weights (layout BF_MLP3): [W1t (h x d) | W2 (h x d) | W2t (d x h)]
-struct Bf3 {
-  const bf16* w1t; const bf16* w2; const bf16* w2t;
-};
-__device__ __forceinline__ Bf3 bf3_of(const bf16* base, int p, int hid) {
-  const long long m = (long long)D * hid;
-  const bf16* b = base + (long long)p * 3 * m;
-  return {b, b + m, b + 2 * m};
+// Combined key statistics of pair p, channel c, from the per-slice partials
+// (count, mean, M2) with Chan's pairwise update.
+__device__ __forceinline__ void key_stat(const float* sp, int S, int c, float eps, float& mu, float& rstd) {
+  float n = 0.f, mean = 0.f, m2 = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* o = sp + (long long)s * 3 * D;
+    const float nb = o[c];
+    if (nb == 0.f) continue;
+    const float mb = o[D + c], m2b = o[2 * D + c];
+    const float nt = n + nb, delta = mb - mean;
+    mean += delta * (nb / nt);
+    m2 += m2b + delta * delta * (n * nb / nt);
+    n = nt;
+  }
+  mu = mean;
+  rstd = __builtin_amdgcn_rsqf(m2 / fmaxf(n, 1.f) + eps);
 }
 
 // ---------------------------------------------------------------------------
-template <int HID, int LOSS>
-__global__ void __launch_bounds__(NTHR, 1)
-k_mfma_grad(Problem pb, const bf16* __restrict__ wbf, int t0, int nt, int J, float scale,
-            float* __restrict__ part) {
+template <int HID, int LOSS, int NWAVE>
+__global__ void __launch_bounds__(NWAVE * 64, (NWAVE == 8 ? 2 : 1))
+k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float* __restrict__ spart, int S_stats,
+            float eps, float* __restrict__ part) {
+  constexpr int NTHR = NWAVE * 64;
   constexpr int HW = HID / NWAVE;      // hidden units per wave
   constexpr int NHB = HW / 16;         // 16-wide hidden blocks per wave
   constexpr int NKH = HID / 32;        // k-steps over the hidden width
-  constexpr int ATS = HID + 8;
-  __shared__ __attribute__((aligned(16))) bf16 Kr[TT * KRS];
-  __shared__ __attribute__((aligned(16))) bf16 Kc[D * KCS];
-  __shared__ __attribute__((aligned(16))) bf16 Vc[D * KCS];
-  __shared__ __attribute__((aligned(16))) bf16 Gr[TT * KRS];
-  __shared__ __attribute__((aligned(16))) bf16 Gc[D * KCS];
-  __shared__ __attribute__((aligned(16))) bf16 At[LOSS == LOSS_MSE ? TT * ATS : 8];
+  constexpr int NB2 = 8 / NWAVE;       // V_hat / G' output blocks (of 2 x 4) per wave
+  constexpr int SCH = D * TT / NTHR;   // channels staged per thread (8 or 4)
+  constexpr int SPR = D / SCH;         // staging threads per token row
+  __shared__ __attribute__((aligned(16))) bf16 Kr[TT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Vr[TT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Gc[D * LDT];
+  __shared__ __attribute__((aligned(16))) bf16 At[LOSS == LOSS_MSE ? HID * LDT : 8];
+  // W2^T of the pair ([c][h], bf16) for the V_hat = A W2 operand
+  constexpr int LW2 = HID + 8;
+  __shared__ __attribute__((aligned(16))) bf16 W2t[LOSS == LOSS_MSE ? D * LW2 : 8];
   __shared__ float eta_s[TT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int h0 = w * HW;
-  // staging role: token row st, channels 8*sc .. 8*sc+7
-  const int st = tid >> 3, sc = tid & 7;
-
+  const int st = tid / SPR, sc = (tid % SPR) * SCH;   // staging: token row, first channel
   const int P = pb.B * pb.H;
   const int tpp = (nt + TT - 1) / TT;
   const long long total = (long long)P * tpp;
@@ -122,38 +155,47 @@ k_mfma_grad(Problem pb, const bf16* __restrict__ wbf, int t0, int nt, int J, flo
   const long long begin = (long long)blockIdx.x * total / G;
   const long long end = (long long)(blockIdx.x + 1) * total / G;
   const int p_first = (int)(begin / tpp);
-
   const bf16* kin = (const bf16*)pb.k;
   const bf16* vin = (const bf16*)pb.v;
 
   long long x = begin;
   while (x < end) {
     const int p = (int)(x / tpp);
+    const int bb = p / pb.H, hh = p % pb.H;
     const int tile0 = (int)(x - (long long)p * tpp);
     const long long seg_end = end < (long long)(p + 1) * tpp ? end : (long long)(p + 1) * tpp;
     const int tile1 = (int)(seg_end - (long long)p * tpp);
 
-    // ---- per-pair constants: weight fragments (registers) and key statistics
-    const Bf3 wb = bf3_of(wbf, p, HID);
-    bf16x8 w1r[NHB][2], w2r[NHB][2], w2c[NKH];
+    // ---- weight fragments of this pair (fp32 state -> bf16 registers)
+    const float* W1 = W.mat(0, bb, hh);
+    const float* W2 = W.mat(1, bb, hh);
+    bf16x8 w1r[NHB][2], w2r[NHB][2];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        w1r[hb][ks] = ld8(wb.w1t + (long long)(h0 + 16 * hb + r) * D + 32 * ks + 8 * g);
-        w2r[hb][ks] = ld8(wb.w2 + (long long)(h0 + 16 * hb + r) * D + 32 * ks + 8 * g);
+        const int hcol = h0 + 16 * hb + r;
+        const float* p1 = W1 + (32 * ks + 8 * g) * HID + hcol;
+        const float4* p2 = reinterpret_cast<const float4*>(W2 + hcol * D + 32 * ks + 8 * g);
+        const float4 a = p2[0], b = p2[1];
+        w2r[hb][ks] = bf16x8{(bf16)a.x, (bf16)a.y, (bf16)a.z, (bf16)a.w, (bf16)b.x, (bf16)b.y, (bf16)b.z, (bf16)b.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w1r[hb][ks][j] = (bf16)p1[j * HID];      // W1[c][h]
+        // keep the fragment loads sequential: issuing them all at once would
+        // hold every 64-bit address live at the same time
+        __builtin_amdgcn_sched_barrier(0);
       }
     if (LOSS == LOSS_MSE) {
-#pragma unroll
-      for (int ks = 0; ks < NKH; ++ks) w2c[ks] = ld8(wb.w2t + (long long)(16 * w + r) * HID + 32 * ks + 8 * g);
+      __syncthreads();   // the previous segment's last tile may still read W2t
+      for (int e = tid; e < HID * D; e += NTHR) W2t[(e % D) * LW2 + e / D] = (bf16)W2[e];
     }
-    float mu[8], rs[8];
+    float mu[SCH], rs[SCH];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { mu[j] = 0.f; rs[j] = 1.f; }
-    if (pb.stats) {
-      const float* s = pb.stats + ((long long)p * D + 8 * sc) * 2;
+    for (int j = 0; j < SCH; ++j) { mu[j] = 0.f; rs[j] = 1.f; }
+    if (spart) {
+      const float* sp = spart + (long long)p * S_stats * 3 * D;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) { mu[j] = s[2 * j]; rs[j] = s[2 * j + 1]; }
+      for (int j = 0; j < SCH; ++j) key_stat(sp, S_stats, sc + j, eps, mu[j], rs[j]);
     }
     const bf16* kp = kin + ((long long)p * pb.N + t0) * D;
     const bf16* vp = vin + ((long long)p * pb.N + t0) * D;
@@ -165,35 +207,36 @@ k_mfma_grad(Problem pb, const bf16* __restrict__ wbf, int t0, int nt, int J, flo
 #pragma unroll
       for (int b = 0; b < NHB; ++b) { acc1[a][b] = f32x4{0, 0, 0, 0}; acc2[b][a] = f32x4{0, 0, 0, 0}; }
 
-    // prefetch of the first tile's rows
-    bf16x8 kreg = {}, vreg = {};
+    typedef __attribute__((__vector_size__(SCH * sizeof(__bf16)))) __bf16 stg_t;
+    stg_t kreg = {}, vreg = {};
     {
       const int n = tile0 * TT + st;
-      if (n < nt) { kreg = ld8(kp + (long long)n * D + 8 * sc); vreg = ld8(vp + (long long)n * D + 8 * sc); }
+      if (n < nt) {
+        kreg = *reinterpret_cast<const stg_t*>(kp + (long long)n * D + sc);
+        vreg = *reinterpret_cast<const stg_t*>(vp + (long long)n * D + sc);
+      }
     }
 
     for (int tile = tile0; tile < tile1; ++tile) {
       const int n = tile * TT + st;
       const bool live = n < nt;
-      // ---- stage K_hat (both layouts), V (channel-major), eta
+      // ---- stage K_hat, V ([token][channel]) and eta
       {
-        bf16x8 kh;
+        stg_t kh, vv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kh[j] = live ? (bf16)(((float)kreg[j] - mu[j]) * rs[j]) : (bf16)0.f;
-        *reinterpret_cast<bf16x8*>(&Kr[st * KRS + 8 * sc]) = kh;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          Kc[(8 * sc + j) * KCS + st] = kh[j];
-          Vc[(8 * sc + j) * KCS + st] = live ? vreg[j] : (bf16)0.f;
+        for (int j = 0; j < SCH; ++j) {
+          kh[j] = live ? (bf16)(((float)kreg[j] - mu[j]) * rs[j]) : (bf16)0.f;
+          vv[j] = live ? vreg[j] : (bf16)0.f;
         }
+        *reinterpret_cast<stg_t*>(&Kr[st * LDK + sc]) = kh;
+        *reinterpret_cast<stg_t*>(&Vr[st * LDK + sc]) = vv;
         if (sc == 0) eta_s[st] = live ? (ep ? ep[n] : 1.0f) : 0.0f;
       }
-      // prefetch the next tile (lands while this one computes)
       {
         const int nn = (tile + 1) * TT + st;
         if (tile + 1 < tile1 && nn < nt) {
-          kreg = ld8(kp + (long long)nn * D + 8 * sc);
-          vreg = ld8(vp + (long long)nn * D + 8 * sc);
+          kreg = *reinterpret_cast<const stg_t*>(kp + (long long)nn * D + sc);
+          vreg = *reinterpret_cast<const stg_t*>(vp + (long long)nn * D + sc);
         }
       }
       __syncthreads();
@@ -208,7 +251,7 @@ k_mfma_grad(Problem pb, const bf16* __restrict__ wbf, int t0, int nt, int J, flo
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          const bf16x8 a = ld8(&Kr[(16 * tb + r) * KRS + 32 * ks + 8 * g]);
+          const bf16x8 a = ld8(&Kr[(16 * tb + r) * LDK + 32 * ks + 8 * g]);
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) z[tb][hb] = mfma16(a, w1r[hb][ks], z[tb][hb]);
         }
@@ -227,59 +270,41 @@ k_mfma_grad(Problem pb, const bf16* __restrict__ wbf, int t0, int nt, int J, flo
             gp[tb][hb][i] = g_;
           }
         apk[hb] = pack8(av[0], av[1]);
+        if (LOSS == LOSS_MSE) *reinterpret_cast<bf16x8*>(&At[(h0 + 16 * hb + r) * LDT + 8 * g]) = apk[hb];
       }
-      if (LOSS == LOSS_MSE) {
-        // A^T -> LDS in token-major layout for V_hat = A W2
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int t = (j < 4) ? 4 * g + j : 16 + 4 * g + (j - 4);
-            At[t * ATS + h0 + 16 * hb + r] = apk[hb][j];
-          }
-      }
-      __syncthreads();
+      if (LOSS == LOSS_MSE) __syncthreads();
 
-      // ---- G' for (t = 16 tb + 4 g + i, c = 16 w + r)
-      {
-        f32x4 gv[2];
+      // ---- G' for the wave's (token block, channel block) pairs -> Gc
+#pragma unroll
+      for (int b2 = 0; b2 < NB2; ++b2) {
+        const int blk = w * NB2 + b2;
+        const int tb2 = blk >> 2, cb2 = blk & 3;
+        // V[t = 16 tb2 + 4 g + i][c = 16 cb2 + r]
+        const bf16x4 vq = ld_tr(&Vr[(16 * tb2 + 4 * g + (r >> 2)) * LDK + 16 * cb2 + 4 * (r & 3)]);
+        f32x4 gv;
         if (LOSS == LOSS_MSE) {
-          f32x4 vh[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-#pragma unroll
-          for (int ks = 0; ks < NKH; ++ks)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-              vh[tb] = mfma16(ld8(&At[(16 * tb + r) * ATS + 32 * ks + 8 * g]), w2c[ks], vh[tb]);
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            const bf16x4 vv = ld4(&Vc[(16 * w + r) * KCS + 16 * tb + 4 * g]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gv[tb][i] = eta_s[16 * tb + 4 * g + i] * (vh[tb][i] - (float)vv[i]);
+          f32x4 vh = f32x4{0, 0, 0, 0};
+#pragma unroll 2
+          for (int ks = 0; ks < NKH; ++ks) {
+            // A[t = 16 tb2 + r][h = 32 ks + 8 g + j]
+            const bf16x4 lo = ld_tr(&At[(32 * ks + 8 * g + (r >> 2)) * LDT + tok_col(16 * tb2 + 4 * (r & 3))]);
+            const bf16x4 hi = ld_tr(&At[(32 * ks + 8 * g + 4 + (r >> 2)) * LDT + tok_col(16 * tb2 + 4 * (r & 3))]);
+            vh = mfma16(cat44(lo, hi), ld8(&W2t[(16 * cb2 + r) * LW2 + 32 * ks + 8 * g]), vh);
           }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gv[i] = eta_s[16 * tb2 + 4 * g + i] * (vh[i] - (float)vq[i]);
         } else {
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            const bf16x4 vv = ld4(&Vc[(16 * w + r) * KCS + 16 * tb + 4 * g]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gv[tb][i] = -eta_s[16 * tb + 4 * g + i] * (float)vv[i];
-          }
+          for (int i = 0; i < 4; ++i) gv[i] = -eta_s[16 * tb2 + 4 * g + i] * (float)vq[i];
         }
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          bf16x4 gq;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gq[i] = (bf16)gv[tb][i];
-          *reinterpret_cast<bf16x4*>(&Gc[(16 * w + r) * KCS + 16 * tb + 4 * g]) = gq;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Gr[(16 * tb + 4 * g + i) * KRS + 16 * w + r] = gq[i];
-        }
+        *reinterpret_cast<bf16x4*>(&Gc[(16 * cb2 + r) * LDT + 8 * g + 4 * tb2]) = pack4(gv);
       }
       __syncthreads();
 
       // ---- dW2 += A^T G'
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const bf16x8 b = cat44(ld4(&Gc[(16 * cb + r) * KCS + 4 * g]), ld4(&Gc[(16 * cb + r) * KCS + 16 + 4 * g]));
+        const bf16x8 b = ld8(&Gc[(16 * cb + r) * LDT + 8 * g]);
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) acc2[hb][cb] = mfma16(apk[hb], b, acc2[hb][cb]);
       }
@@ -295,7 +320,10 @@ k_mfma_grad(Problem pb, const bf16* __restrict__ wbf, int t0, int nt, int J, flo
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
-            const bf16x8 a = ld8(&Gr[(16 * tb + r) * KRS + 32 * ks + 8 * g]);
+            // G'[t = 16 tb + r][c = 32 ks + 8 g + j]
+            const bf16x4 lo = ld_tr(&Gc[(32 * ks + 8 * g + (r >> 2)) * LDT + tok_col(16 * tb + 4 * (r & 3))]);
+            const bf16x4 hi = ld_tr(&Gc[(32 * ks + 8 * g + 4 + (r >> 2)) * LDT + tok_col(16 * tb + 4 * (r & 3))]);
+            const bf16x8 a = cat44(lo, hi);
 #pragma unroll
             for (int hb = 0; hb < NHB; ++hb) da[tb][hb] = mfma16(a, w2r[hb][ks], da[tb][hb]);
           }
@@ -307,17 +335,19 @@ k_mfma_grad(Problem pb, const bf16* __restrict__ wbf, int t0, int nt, int J, flo
           dzp[hb] = pack8(d0, d1);
         }
       }
-      // ---- dW1 += K_hat^T dZ
+      // ---- dW1 += K_hat^T dZ ; K_hat[t = tau(g, j)][c = 16 cb + r]
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const bf16x8 a = cat44(ld4(&Kc[(16 * cb + r) * KCS + 4 * g]), ld4(&Kc[(16 * cb + r) * KCS + 16 + 4 * g]));
+        const bf16x4 lo = ld_tr(&Kr[(4 * g + (r >> 2)) * LDK + 16 * cb + 4 * (r & 3)]);
+        const bf16x4 hi = ld_tr(&Kr[(16 + 4 * g + (r >> 2)) * LDK + 16 * cb + 4 * (r & 3)]);
+        const bf16x8 a = cat44(lo, hi);
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) acc1[cb][hb] = mfma16(a, dzp[hb], acc1[cb][hb]);
       }
       __syncthreads();
     }
 
-    // ---- partial of this (workgroup, pair) segment
+    // ---- partial of this (workgroup, pair) segment: [dW1 (d x h) | dW2 (h x d)]
     float* out = part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
@@ -339,20 +369,22 @@ k_mfma_grad(Problem pb, const bf16* __restrict__ wbf, int t0, int nt, int J, flo
 
 // ---------------------------------------------------------------------------
 // O = gelu(Q W1*) W2* with tokens on the MFMA n axis.  One workgroup = one
-// pair's token range; W1t and W2t of the pair's state are staged in LDS.
-constexpr int QTOK = 64;                 // tokens per wave iteration
+// pair's token range; the pair's fp32 W1, W2 are staged in LDS as bf16 in their
+// natural layouts ([c][h] and [h][c]) and read transposed.
+constexpr int QTOK = 64;                 // tokens per wave pass
+constexpr int QWAVE = 4;
 template <int HID>
-__global__ void __launch_bounds__(NTHR, 2)
-k_mfma_query(Problem pb, const bf16* __restrict__ wstates, long long state_stride, int chunk, int span,
+__global__ void __launch_bounds__(QWAVE * 64, 2)
+k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long state_stride, int chunk, int span,
              int groups, int tok_per_wg) {
-  constexpr int W1S = D + 8;             // W1t rows [HID][D]
-  constexpr int W2S = HID + 4;           // W2t rows [D][HID]
-  __shared__ __attribute__((aligned(16))) bf16 w1s[HID * W1S];
-  __shared__ __attribute__((aligned(16))) bf16 w2s[D * W2S];
+  constexpr int NTHR = QWAVE * 64;
+  constexpr int L1 = HID + 16;           // [c][h] row stride (16 mod 128: conflict-free transposed reads)
+  constexpr int L2 = 80;                 // [h][c] row stride
+  __shared__ __attribute__((aligned(16))) bf16 w1s[D * L1];
+  __shared__ __attribute__((aligned(16))) bf16 w2s[HID * L2];
   const int p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  // blockIdx.x = (batch of tokens c, group inside it); full batch: one batch of N
   const int c = blockIdx.x / groups, grp = blockIdx.x % groups;
   const int c0 = c * span;
   const int n0 = c0 + grp * tok_per_wg;
@@ -360,19 +392,25 @@ k_mfma_query(Problem pb, const bf16* __restrict__ wstates, long long state_strid
   if (n0 >= n1) return;
   // full batch reads state 1 (after the update); causal chunk c reads state c
   const int state = chunk ? c : 1;
-  const Bf3 wb = bf3_of(wstates + state * state_stride, p, HID);
-  for (int e = tid * 8; e < HID * D; e += NTHR * 8) {
-    const int hh = e / D, cc = e % D;
-    *reinterpret_cast<bf16x8*>(&w1s[hh * W1S + cc]) = ld8(wb.w1t + e);
+  const int bb = p / pb.H, hh = p % pb.H;
+  const float *W1, *W2;
+  if (state == 0) { W1 = w0.mat(0, bb, hh); W2 = w0.mat(1, bb, hh); }
+  else {
+    const float* base = states + (state - 1) * state_stride + (long long)p * 2 * D * HID;
+    W1 = base; W2 = base + (long long)D * HID;
   }
-  for (int e = tid * 8; e < HID * D; e += NTHR * 8) {
-    const int cc = e / HID, hh = e % HID;
-    *reinterpret_cast<bf16x8*>(&w2s[cc * W2S + hh]) = ld8(wb.w2t + e);
+  for (int e = tid * 4; e < HID * D; e += NTHR * 4) {
+    const float4 a = *reinterpret_cast<const float4*>(W1 + e);
+    const float4 b = *reinterpret_cast<const float4*>(W2 + e);
+    const int c1 = e / HID, h1 = e % HID;         // W1 [c][h]
+    const int h2 = e / D, c2 = e % D;              // W2 [h][c]
+    *reinterpret_cast<bf16x4*>(&w1s[c1 * L1 + h1]) = bf16x4{(bf16)a.x, (bf16)a.y, (bf16)a.z, (bf16)a.w};
+    *reinterpret_cast<bf16x4*>(&w2s[h2 * L2 + c2]) = bf16x4{(bf16)b.x, (bf16)b.y, (bf16)b.z, (bf16)b.w};
   }
   __syncthreads();
   const bf16* qp = (const bf16*)pb.q + (long long)p * pb.N * D;
   bf16* op = (bf16*)pb.o + (long long)p * pb.N * D;
-  for (int base = n0 + w * QTOK; base < n1; base += NWAVE * QTOK) {
+  for (int base = n0 + w * QTOK; base < n1; base += QWAVE * QTOK) {
     bf16x8 qb[4][2];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -397,7 +435,10 @@ k_mfma_query(Problem pb, const bf16* __restrict__ wstates, long long state_strid
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const bf16x8 a = ld8(&w1s[(32 * hc + 16 * u + r) * W1S + 32 * ks + 8 * g]);
+          // W1^T operand: W1[c = 32 ks + 8 g + j][h = 32 hc + 16 u + r]
+          const bf16x4 lo = ld_tr(&w1s[(32 * ks + 8 * g + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
+          const bf16x4 hi = ld_tr(&w1s[(32 * ks + 8 * g + 4 + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
+          const bf16x8 a = cat44(lo, hi);
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb) zt[u][tb] = mfma16(a, qb[tb][ks], zt[u][tb]);
         }
@@ -411,8 +452,10 @@ k_mfma_query(Problem pb, const bf16* __restrict__ wstates, long long state_strid
       }
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const bf16x8 a = cat44(ld4(&w2s[(16 * cb + r) * W2S + 32 * hc + 4 * g]),
-                               ld4(&w2s[(16 * cb + r) * W2S + 32 * hc + 16 + 4 * g]));
+        // W2^T operand: W2[h = 32 hc + tau(g, j)][c = 16 cb + r]
+        const bf16x4 lo = ld_tr(&w2s[(32 * hc + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
+        const bf16x4 hi = ld_tr(&w2s[(32 * hc + 16 + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
+        const bf16x8 a = cat44(lo, hi);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) o[cb][tb] = mfma16(a, ab[tb], o[cb][tb]);
       }
@@ -422,24 +465,22 @@ k_mfma_query(Problem pb, const bf16* __restrict__ wstates, long long state_strid
       const int n = base + 16 * tb + r;
       if (n < n1) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          bf16x4 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)o[cb][tb][i];
-          *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = v;
-        }
+        for (int cb = 0; cb < 4; ++cb)
+          *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = pack4(o[cb][tb]);
       }
     }
   }
 }
 
-template <int HID>
-void launch_grad_h(const Problem& pb, const bf16* wbf, int t0, int nt, int G, int J, float scale, float* part,
-                   hipStream_t st) {
+template <int HID, int NWAVE>
+void launch_grad_h(const Problem& pb, const WRef& W, int t0, int nt, int G, int J, float scale,
+                   const float* spart, int S_stats, float eps, float* part, hipStream_t st) {
   if (pb.loss == LOSS_MSE)
-    hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE>), dim3(G), dim3(NTHR), 0, st, pb, wbf, t0, nt, J, scale, part);
+    hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, NWAVE>), dim3(G), dim3(NWAVE * 64), 0, st, pb, W, t0, nt, J,
+                       scale, spart, S_stats, eps, part);
   else
-    hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT>), dim3(G), dim3(NTHR), 0, st, pb, wbf, t0, nt, J, scale, part);
+    hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, NWAVE>), dim3(G), dim3(NWAVE * 64), 0, st, pb, W, t0, nt, J,
+                       scale, spart, S_stats, eps, part);
 }
 
 }  // namespace
@@ -450,42 +491,41 @@ bool mfma_full_supported(const Problem& pb) {
 
 bool mfma_query_supported(const Problem& pb) { return mfma_full_supported(pb); }
 
-// grid of the stream-K gradient kernel: at most one workgroup per CU and
-// never more workgroups than tiles
+// grid of the stream-K gradient kernel: one workgroup per CU (two for the
+// 4-wave variant), never more workgroups than tiles
 void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_per_pair) {
   const int P = pb.B * pb.H;
   const int tpp = (nt + TT - 1) / TT;
   *tiles_per_pair = tpp;
   const long long total = (long long)P * tpp;
-  long long g = 256;
+  long long g = pb.hid == 64 ? 512 : 256;
   if (g > total) g = total;
   *G = (int)g;
-  // pairs a workgroup can touch: its tile count spans at most this many
   const long long per = (total + g - 1) / g;
   *J = (int)((per + tpp - 1) / tpp + 1);
 }
 
-void launch_mfma_full_grad(const Problem& pb, const bf16* wbf, int t0, int nt, float scale, float* part,
-                           hipStream_t st) {
+void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, float scale, const float* spart,
+                           int S_stats, float eps, float* part, hipStream_t st) {
   int G, J, tpp;
   mfma_grad_geometry(pb, nt, &G, &J, &tpp);
   switch (pb.hid) {
-    case 64: launch_grad_h<64>(pb, wbf, t0, nt, G, J, scale, part, st); break;
-    case 128: launch_grad_h<128>(pb, wbf, t0, nt, G, J, scale, part, st); break;
-    default: launch_grad_h<256>(pb, wbf, t0, nt, G, J, scale, part, st); break;
+    case 64: launch_grad_h<64, 4>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
+    case 128: launch_grad_h<128, 8>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
+    default: launch_grad_h<256, 8>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
   }
 }
 
-void launch_mfma_query(const Problem& pb, const bf16* wstates, long long state_stride, int nchunks, int chunk,
-                       hipStream_t st) {
+void launch_mfma_query(const Problem& pb, const WRef& w0, const float* states, long long state_stride, int nchunks,
+                       int chunk, hipStream_t st) {
   const int span = chunk ? (chunk < pb.N ? chunk : pb.N) : pb.N;
-  const int tpw = NWAVE * QTOK * 4;
+  const int tpw = QWAVE * QTOK * 4;
   const int groups = (span + tpw - 1) / tpw;
   dim3 grid(groups * nchunks, pb.B * pb.H);
   switch (pb.hid) {
-    case 64: hipLaunchKernelGGL((k_mfma_query<64>), grid, dim3(NTHR), 0, st, pb, wstates, state_stride, chunk, span, groups, tpw); break;
-    case 128: hipLaunchKernelGGL((k_mfma_query<128>), grid, dim3(NTHR), 0, st, pb, wstates, state_stride, chunk, span, groups, tpw); break;
-    default: hipLaunchKernelGGL((k_mfma_query<256>), grid, dim3(NTHR), 0, st, pb, wstates, state_stride, chunk, span, groups, tpw); break;
+    case 64: hipLaunchKernelGGL((k_mfma_query<64>), grid, dim3(QWAVE * 64), 0, st, pb, w0, states, state_stride, chunk, span, groups, tpw); break;
+    case 128: hipLaunchKernelGGL((k_mfma_query<128>), grid, dim3(QWAVE * 64), 0, st, pb, w0, states, state_stride, chunk, span, groups, tpw); break;
+    default: hipLaunchKernelGGL((k_mfma_query<256>), grid, dim3(QWAVE * 64), 0, st, pb, w0, states, state_stride, chunk, span, groups, tpw); break;
   }
 }
 

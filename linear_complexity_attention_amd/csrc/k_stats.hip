@@ -3,10 +3,10 @@
 // the inner optimisation).  Per (batch, head, channel), over the N tokens:
 // mean and 1/sqrt(biased variance + eps).
 //
-// Two kernels: every workgroup reduces one token slice of one (b, h) pair to
-// (count, mean, M2) per channel with a two-pass sum over the slice (the second
-// pass hits L2), so the whole chip streams K once from HBM; a tiny second
-// kernel merges the slices with Chan's parallel-variance formula.
+// Every workgroup reduces one token slice of one (b, h) pair to (count, mean,
+// M2) per channel, so the whole chip streams K once from HBM; the slices are
+// merged with Chan's parallel-variance formula, either by the gradient kernel
+// itself (MFMA path) or by a tiny second kernel (generic path).
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -31,7 +31,9 @@ __device__ __forceinline__ void load8<float>(const float* p, float* x) {
 }
 
 // d % 8 == 0: each thread owns 8 consecutive channels of one token row; the
-// workgroup walks the slice R = 256/(d/8) rows at a time.
+// workgroup walks the slice R = 256/(d/8) rows at a time, four rows in flight
+// per thread.  One pass: sums of (k - s) and (k - s)^2 around the pair's first
+// key row s (so the variance does not cancel), turned into (count, mean, M2).
 template <typename T>
 __global__ void __launch_bounds__(kThreads) k_stats_partial_v8(const T* __restrict__ k, int N, int d,
                                                                int S, float* __restrict__ part) {
@@ -43,51 +45,44 @@ __global__ void __launch_bounds__(kThreads) k_stats_partial_v8(const T* __restri
   const int cg = threadIdx.x % groups, r = threadIdx.x / groups;
   const bool active = r < R;
   const T* base = k + (size_t)p * N * d + cg * 8;
-  __shared__ float red[kThreads][8];
-  __shared__ float mean_s[128];
-  float acc[8];
+  __shared__ float red[2][kThreads][8];
+  float sh[8], s1[8], s2[8];
+  load8<T>(base, sh);                       // shift: the pair's first key row
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  if (active)
-    for (int n = n0 + r; n < n1; n += R) {
+  for (int i = 0; i < 8; ++i) { s1[i] = 0.f; s2[i] = 0.f; }
+  if (active) {
+    int n = n0 + r;
+    for (; n + 3 * R < n1; n += 4 * R) {
+      float x[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8<T>(base + (size_t)(n + u * R) * d, x[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { const float t = x[u][i] - sh[i]; s1[i] += t; s2[i] += t * t; }
+    }
+    for (; n < n1; n += R) {
       float x[8];
       load8<T>(base + (size_t)n * d, x);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += x[i];
+      for (int i = 0; i < 8; ++i) { const float t = x[i] - sh[i]; s1[i] += t; s2[i] += t * t; }
     }
+  }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red[threadIdx.x][i] = active ? acc[i] : 0.f;
+  for (int i = 0; i < 8; ++i) { red[0][threadIdx.x][i] = s1[i]; red[1][threadIdx.x][i] = s2[i]; }
   __syncthreads();
   const int cnt = max(n1 - n0, 0);
   if (threadIdx.x < d) {
     const int c = threadIdx.x, g = c >> 3, j = c & 7;
-    float sum = 0.f;
-    for (int rr = 0; rr < R; ++rr) sum += red[rr * groups + g][j];
-    mean_s[c] = cnt ? sum / (float)cnt : 0.f;
-  }
-  __syncthreads();
-  float m[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { m[i] = mean_s[cg * 8 + i]; acc[i] = 0.f; }
-  if (active)
-    for (int n = n0 + r; n < n1; n += R) {
-      float x[8];
-      load8<T>(base + (size_t)n * d, x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { float t = x[i] - m[i]; acc[i] += t * t; }
-    }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 8; ++i) red[threadIdx.x][i] = active ? acc[i] : 0.f;
-  __syncthreads();
-  if (threadIdx.x < d) {
-    const int c = threadIdx.x, g = c >> 3, j = c & 7;
-    float m2 = 0.f;
-    for (int rr = 0; rr < R; ++rr) m2 += red[rr * groups + g][j];
+    float a1 = 0.f, a2 = 0.f;
+    for (int rr = 0; rr < R; ++rr) { a1 += red[0][rr * groups + g][j]; a2 += red[1][rr * groups + g][j]; }
+    float shift[8];
+    load8<T>(k + (size_t)p * N * d + g * 8, shift);
+    const float m1 = cnt ? a1 / (float)cnt : 0.f;
     float* o = part + ((size_t)p * S + s) * 3 * d;
     o[c] = (float)cnt;
-    o[d + c] = mean_s[c];
-    o[2 * d + c] = m2;
+    o[d + c] = shift[j] + m1;
+    o[2 * d + c] = fmaxf(a2 - a1 * m1, 0.f);
   }
 }
 

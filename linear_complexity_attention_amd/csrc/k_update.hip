@@ -8,8 +8,7 @@
 //           memory complements local attention": L2 normalisation after the update)
 //
 // The partials are summed in a fixed order, so the result is bit-reproducible.
-// Besides the fp32 state the kernel can emit the caller's W_out and a bf16
-// copy laid out for the MFMA kernels (see bf16_index below).
+// Besides the fp32 state the kernel can emit the caller's W_out.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -17,31 +16,16 @@ namespace ttt {
 namespace {
 
 constexpr int kCols = 64;
-constexpr int kLanes = 4;
+constexpr int kLanes = 4;                        // row lanes per column (re-norm kernel)
 
-// bf16 operand layouts:
-//   BF_ROWMAJOR   : [in][out] like the fp32 matrix
-//   BF_TRANSPOSED : [out][in]
-//   BF_MLP3       : GELU-MLP MFMA operands, per pair [W1^T (h x d) | W2 (h x d) | W2^T (d x h)]
-__device__ __forceinline__ long long bf16_index(int layout, int r, int c, int rows, int cols) {
-  return layout == BF_TRANSPOSED ? (long long)c * rows + r : (long long)r * cols + c;
+// first and last workgroup of the stream-K gradient kernel that touched pair p
+__device__ __forceinline__ void sk_range(const UpdateArgs& a, int P, int p, long long& q0, long long& q1,
+                                         long long& total) {
+  total = (long long)P * a.sk_tpp;
+  const long long xa = (long long)p * a.sk_tpp, xb = xa + a.sk_tpp - 1;
+  q0 = ((xa + 1) * a.sk_G - 1) / total;
+  q1 = ((xb + 1) * a.sk_G - 1) / total;
 }
-
-__device__ __forceinline__ void store_bf(bf16* pair_base, int layout, int i, long long msz, int r, int c,
-                                         int rows, int cols, float w) {
-  const bf16 v = (bf16)w;
-  if (layout == BF_MLP3) {
-    if (i == 0) pair_base[(long long)c * rows + r] = v;            // W1^T [h][d]
-    else {
-      pair_base[msz + (long long)r * cols + c] = v;                 // W2   [h][d]
-      pair_base[2 * msz + (long long)c * rows + r] = v;             // W2^T [d][h]
-    }
-    return;
-  }
-  pair_base[i * msz + bf16_index(layout, r, c, rows, cols)] = v;
-}
-
-__device__ __forceinline__ int bf_pair_mats(int layout, int nm) { return layout == BF_MLP3 ? 3 : nm; }
 
 __device__ __forceinline__ void mat_dims(const Problem& pb, int i, int& rows, int& cols) {
   if (pb.inner == INNER_LINEAR) { rows = pb.d; cols = pb.d; return; }
@@ -49,8 +33,77 @@ __device__ __forceinline__ void mat_dims(const Problem& pb, int i, int& rows, in
   else { rows = pb.d; cols = pb.hid; }          // W1, W3 [d, h]
 }
 
-// grid = (column blocks, nm, P); thread = (column, row lane)
-__global__ void __launch_bounds__(kCols * kLanes) k_update(Problem pb, UpdateArgs a) {
+// No re-norm: every element is independent.  grid = (chunks of 1024 elements
+// of one pair's [nm][msz] block, P); each thread updates 4 consecutive floats.
+__global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
+  const int p = blockIdx.y;
+  const int b = p / pb.H, h = p % pb.H;
+  const long long wsz = (long long)pb.nm * pb.msz;
+  const long long e = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= wsz) return;
+  const int i = (int)(e / pb.msz);
+  const long long o = e - (long long)i * pb.msz;           // offset inside matrix i (msz % 4 == 0)
+  float4 w = *reinterpret_cast<const float4*>(a.cur.mat(i, b, h) + o);
+  auto sub = [&](const float* q) {
+    const float4 d = *reinterpret_cast<const float4*>(q + e);
+    w.x -= d.x; w.y -= d.y; w.z -= d.z; w.w -= d.w;
+  };
+  if (a.part_mode == PART_SPLITS) {
+    const float* pp = a.part + (size_t)p * wsz;
+    for (int s = 0; s < a.S; ++s) sub(pp + s * a.part_pair_stride);
+  } else {
+    long long q0, q1, total;
+    sk_range(a, pb.B * pb.H, p, q0, q1, total);
+    for (long long q = q0; q <= q1; ++q) {
+      const long long first = ((q * total) / a.sk_G) / a.sk_tpp;
+      sub(a.part + (q * a.sk_J + (p - first)) * wsz);
+    }
+  }
+  *reinterpret_cast<float4*>(a.next + (size_t)p * wsz + e) = w;
+  if (a.out[i]) *reinterpret_cast<float4*>(a.out[i] + (size_t)p * pb.msz + o) = w;
+}
+
+// Re-norm after the flat update: every output column of next is rescaled to
+// the L2 norm of the same column of W0.  grid = (column blocks, nm, P);
+// thread = (column, row lane), 16 row lanes per column.
+constexpr int kRLanes = 16;
+__global__ void __launch_bounds__(kCols * kRLanes) k_renorm(Problem pb, UpdateArgs a) {
+  const int i = blockIdx.y, p = blockIdx.z;
+  const int b = p / pb.H, h = p % pb.H;
+  int rows, cols;
+  mat_dims(pb, i, rows, cols);
+  const int j = blockIdx.x * kCols + threadIdx.x % kCols;
+  const int lane = threadIdx.x / kCols;
+  const bool live = j < cols;
+  const float* w0 = a.w0.mat(i, b, h);
+  float* nxt = a.next + ((size_t)p * pb.nm + i) * pb.msz;
+  __shared__ float red[2][kRLanes][kCols];
+  float nn = 0.f, nr = 0.f;
+  if (live)
+    for (int r = lane; r < rows; r += kRLanes) {
+      const float w = nxt[(size_t)r * cols + j], v = w0[(size_t)r * cols + j];
+      nn += w * w;
+      nr += v * v;
+    }
+  red[0][lane][threadIdx.x % kCols] = nn;
+  red[1][lane][threadIdx.x % kCols] = nr;
+  __syncthreads();
+  if (!live) return;
+  float sn = 0.f, sr = 0.f;
+  for (int l = 0; l < kRLanes; ++l) { sn += red[0][l][threadIdx.x % kCols]; sr += red[1][l][threadIdx.x % kCols]; }
+  const float scale = sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f);
+  float* out = a.out[i] ? a.out[i] + (size_t)p * pb.msz : nullptr;
+  for (int r = lane; r < rows; r += kRLanes) {
+    const size_t e = (size_t)r * cols + j;
+    const float w = nxt[e] * scale;
+    nxt[e] = w;
+    if (out) out[e] = w;
+  }
+}
+
+// Update and re-norm in one kernel for shapes the float4 path cannot take.
+// grid = (column blocks, nm, P); thread = (column, row lane).
+__global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, UpdateArgs a) {
   const int i = blockIdx.y, p = blockIdx.z;
   const int b = p / pb.H, h = p % pb.H;
   int rows, cols;
@@ -60,31 +113,23 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update(Problem pb, UpdateArg
   const bool live = j < cols;
   const float* cur = a.cur.mat(i, b, h);
   const float* w0 = a.w0.mat(i, b, h);
-  float* nxt = a.next + ((size_t)p * pb.nm + i) * pb.msz;
-  // stream-K: workgroups [wg0, wg1] of the gradient kernel touched pair p
-  long long wg0 = 0, wg1 = -1, sk_total = 0;
-  if (a.part_mode == PART_STREAMK) {
-    sk_total = (long long)pb.B * pb.H * a.sk_tpp;
-    const long long xa = (long long)p * a.sk_tpp, xb = xa + a.sk_tpp - 1;
-    wg0 = ((xa + 1) * a.sk_G - 1) / sk_total;
-    wg1 = ((xb + 1) * a.sk_G - 1) / sk_total;
-  }
+  const long long wsz = (long long)pb.nm * pb.msz;
+  float* nxt = a.next + (size_t)p * wsz + (size_t)i * pb.msz;
+  long long q0 = 0, q1 = -1, total = 0;
+  if (a.part_mode == PART_STREAMK) sk_range(a, pb.B * pb.H, p, q0, q1, total);
   __shared__ float red[2][kLanes][kCols];
   float nn = 0.f, nr = 0.f;
   if (live)
     for (int r = lane; r < rows; r += kLanes) {
       const size_t e = (size_t)r * cols + j;
       float w = cur[e];
-      if (a.part) {
-        if (a.part_mode == PART_SPLITS) {
-          const float* pp = a.part + (size_t)p * pb.nm * pb.msz + (size_t)i * pb.msz;
-          for (int s = 0; s < a.S; ++s) w -= pp[s * a.part_pair_stride + e];
-        } else {
-          for (long long q = wg0; q <= wg1; ++q) {
-            const long long first = ((q * sk_total) / a.sk_G) / a.sk_tpp;
-            const float* pp = a.part + (q * a.sk_J + (p - first)) * pb.nm * pb.msz + (size_t)i * pb.msz;
-            w -= pp[e];
-          }
+      if (a.part_mode == PART_SPLITS) {
+        const float* pp = a.part + (size_t)p * wsz + (size_t)i * pb.msz + e;
+        for (int s = 0; s < a.S; ++s) w -= pp[s * a.part_pair_stride];
+      } else {
+        for (long long q = q0; q <= q1; ++q) {
+          const long long first = ((q * total) / a.sk_G) / a.sk_tpp;
+          w -= a.part[(q * a.sk_J + (p - first)) * wsz + (size_t)i * pb.msz + e];
         }
       }
       nxt[e] = w;
@@ -92,51 +137,48 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update(Problem pb, UpdateArg
       const float w0v = w0[e];
       nr += w0v * w0v;
     }
-  float scale = 1.f;
-  if (a.renorm) {
-    red[0][lane][threadIdx.x % kCols] = nn;
-    red[1][lane][threadIdx.x % kCols] = nr;
-    __syncthreads();
-    float sn = 0.f, sr = 0.f;
-    for (int l = 0; l < kLanes; ++l) { sn += red[0][l][threadIdx.x % kCols]; sr += red[1][l][threadIdx.x % kCols]; }
-    scale = sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f);
-  }
+  red[0][lane][threadIdx.x % kCols] = nn;
+  red[1][lane][threadIdx.x % kCols] = nr;
+  __syncthreads();
+  float sn = 0.f, sr = 0.f;
+  for (int l = 0; l < kLanes; ++l) { sn += red[0][l][threadIdx.x % kCols]; sr += red[1][l][threadIdx.x % kCols]; }
+  const float scale = a.renorm ? sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f) : 1.f;
   if (!live) return;
   float* out = a.out[i] ? a.out[i] + (size_t)p * pb.msz : nullptr;
-  bf16* bfo = a.bf ? a.bf + (size_t)p * bf_pair_mats(a.bf_layout, pb.nm) * pb.msz : nullptr;
   for (int r = lane; r < rows; r += kLanes) {
     const size_t e = (size_t)r * cols + j;
-    float w = nxt[e];
-    if (a.renorm) { w *= scale; nxt[e] = w; }
+    const float w = nxt[e] * scale;
+    nxt[e] = w;
     if (out) out[e] = w;
-    if (bfo) store_bf(bfo, a.bf_layout, i, pb.msz, r, j, rows, cols, w);
-  }
-}
-
-__global__ void __launch_bounds__(256) k_convert_bf16(Problem pb, WRef W, bf16* dst, int layout) {
-  const int i = blockIdx.y, p = blockIdx.z;
-  const int b = p / pb.H, h = p % pb.H;
-  int rows, cols;
-  mat_dims(pb, i, rows, cols);
-  const float* src = W.mat(i, b, h);
-  bf16* o = dst + (size_t)p * bf_pair_mats(layout, pb.nm) * pb.msz;
-  for (long long e = blockIdx.x * 256 + threadIdx.x; e < (long long)rows * cols; e += (long long)gridDim.x * 256) {
-    const int r = (int)(e / cols), c = (int)(e % cols);
-    store_bf(o, layout, i, pb.msz, r, c, rows, cols, src[e]);
   }
 }
 
 }  // namespace
 
 void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st) {
+  const int P = pb.B * pb.H;
+  // the flat kernel moves float4s: every matrix base and stride must keep 16-byte alignment
+  bool aligned = pb.msz % 4 == 0 && a.cur.sb % 4 == 0 && a.cur.sh % 4 == 0;
+  for (int i = 0; i < pb.nm; ++i) aligned = aligned && (reinterpret_cast<uintptr_t>(a.cur.m[i]) % 16 == 0) &&
+                                          (!a.out[i] || reinterpret_cast<uintptr_t>(a.out[i]) % 16 == 0);
+  if (aligned) {
+    const long long wsz = (long long)pb.nm * pb.msz;
+    dim3 grid((unsigned)((wsz / 4 + 255) / 256), P);
+    if (!a.renorm) {
+      hipLaunchKernelGGL(k_update_flat, grid, dim3(256), 0, st, pb, a);
+      return;
+    }
+    UpdateArgs f = a;             // the re-norm pass writes W_out
+    for (int i = 0; i < 3; ++i) f.out[i] = nullptr;
+    hipLaunchKernelGGL(k_update_flat, grid, dim3(256), 0, st, pb, f);
+    const int maxcols = pb.inner == INNER_LINEAR ? pb.d : (pb.hid > pb.d ? pb.hid : pb.d);
+    dim3 g2((maxcols + kCols - 1) / kCols, pb.nm, P);
+    hipLaunchKernelGGL(k_renorm, g2, dim3(kCols * kRLanes), 0, st, pb, a);
+    return;
+  }
   const int maxcols = pb.inner == INNER_LINEAR ? pb.d : (pb.hid > pb.d ? pb.hid : pb.d);
-  dim3 grid((maxcols + kCols - 1) / kCols, pb.nm, pb.B * pb.H);
-  hipLaunchKernelGGL(k_update, grid, dim3(kCols * kLanes), 0, st, pb, a);
-}
-
-void launch_convert_bf16(const Problem& pb, const WRef& W, bf16* dst, int layout, hipStream_t st) {
-  dim3 grid(8, pb.nm, pb.B * pb.H);
-  hipLaunchKernelGGL(k_convert_bf16, grid, dim3(256), 0, st, pb, W, dst, layout);
+  dim3 grid((maxcols + kCols - 1) / kCols, pb.nm, P);
+  hipLaunchKernelGGL(k_update_renorm, grid, dim3(kCols * kLanes), 0, st, pb, a);
 }
 
 }  // namespace ttt

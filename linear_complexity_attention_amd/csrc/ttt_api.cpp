@@ -58,14 +58,13 @@ struct Plan {
   int P, nm, hid, nb, chunk, span;   // span: tokens of the longest update batch
   long long msz, wsz;                // elements per matrix / per pair
   // choices
-  bool mfma_grad, mfma_query;
+  bool mfma_grad, mfma_query;        // GELU-MLP MFMA kernels
+  bool lact_grad, lact_query;        // SwiGLU MFMA kernels
   int S_stats, S_grad;               // S_grad: partial slots of the gradient kernel
   int sk_G, sk_J;                    // stream-K geometry (MFMA gradient kernel)
-  int bf_layout, bf_mats;            // bf16 operand copies: layout and matrices per pair
   // byte offsets
-  size_t off_stats_part, off_stats, off_states, off_part, off_gbuf, off_bf, off_flag, total;
+  size_t off_stats_part, off_stats, off_states, off_part, off_gbuf, off_flag, total;
   long long state_stride;            // floats between consecutive states
-  long long bf_stride;               // bf16 elements between consecutive bf16 states
 };
 
 int choose_splits(long long other_blocks, int tokens, int per_block_min, int target) {
@@ -123,8 +122,12 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk) {
   // used for a single update only; multi-chunk MLP gradients stay in fp32.
   pl.mfma_grad = !generic_only && mfma_full_supported(pb) && pl.nb == 1;
   pl.mfma_query = !generic_only && mfma_query_supported(pb);
+  pl.lact_grad = !generic_only && !c.key_norm && lact_supported(pb);
+  pl.lact_query = !generic_only && lact_readout_supported(pb);
   pl.S_stats = c.key_norm ? choose_splits(pl.P, c.N, 64, 1024) : 0;
-  if (pl.mfma_grad) {
+  if (pl.lact_grad) {
+    pl.S_grad = lact_grad_splits(pb, pl.span);
+  } else if (pl.mfma_grad) {
     int tpp_unused;
     mfma_grad_geometry(pb, pl.span, &pl.sk_G, &pl.sk_J, &tpp_unused);
     pl.S_grad = pl.sk_G * pl.sk_J;   // partial slots
@@ -143,12 +146,7 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk) {
   pl.off_part = off;
   off = align256(off + sizeof(float) * (size_t)pl.S_grad * (pl.mfma_grad ? 1 : pl.P) * pl.wsz);
   pl.off_gbuf = off;
-  if (!pl.mfma_grad) off = align256(off + sizeof(float) * (size_t)pl.P * pl.span * c.d);
-  pl.off_bf = off;
-  pl.bf_layout = pb.inner == INNER_MLP ? BF_MLP3 : BF_ROWMAJOR;
-  pl.bf_mats = pl.bf_layout == BF_MLP3 ? 3 : pl.nm;
-  pl.bf_stride = (long long)pl.P * pl.bf_mats * pl.msz;
-  if (pl.mfma_grad || pl.mfma_query) off = align256(off + sizeof(uint16_t) * (size_t)(pl.nb + 1) * pl.bf_stride);
+  if (!pl.mfma_grad && !pl.lact_grad) off = align256(off + sizeof(float) * (size_t)pl.P * pl.span * c.d);
   pl.off_flag = off;
   off = align256(off + 64);
   pl.total = off;
@@ -234,6 +232,8 @@ const char* ttt_path_name(const ttt_handle* hc, int loss, int inner, int chunk) 
   Plan pl = make_plan(h, loss, inner, chunk);
   if (pl.mfma_grad && pl.mfma_query) return "mfma";
   if (pl.mfma_query) return "generic_grad+mfma_query";
+  if (pl.lact_grad && pl.lact_query) return "mfma_swiglu";
+  if (pl.lact_query) return "generic_grad+mfma_swiglu_query";
   return "generic";
 }
 
@@ -267,7 +267,6 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
   float* states = reinterpret_cast<float*>(ws + pl.off_states);
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
   float* gbuf = reinterpret_cast<float*>(ws + pl.off_gbuf);
-  bf16* bfs = reinterpret_cast<bf16*>(ws + pl.off_bf);
   int* flag = reinterpret_cast<int*>(ws + pl.off_flag);
 
   pb.q = q; pb.k = k; pb.v = v; pb.o = o;
@@ -279,7 +278,8 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
   if (log)
     std::fprintf(stderr, "[ttt] B=%d H=%d N=%d d=%d h=%d %s inner=%d loss=%d chunk=%d nb=%d grad=%s(S=%d) query=%s ws=%zu\n",
                  c.B, c.H, c.N, c.d, pb.hid, pb.bf16 ? "bf16" : "f32", inner, loss, chunk, pl.nb,
-                 pl.mfma_grad ? "mfma" : "generic", pl.S_grad, pl.mfma_query ? "mfma" : "generic", pl.total);
+                 pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu" : "generic", pl.S_grad,
+                 pl.mfma_query ? "mfma" : pl.lact_query ? "mfma_swiglu" : "generic", pl.total);
 
   WRef w0{};
   for (int i = 0; i < 3; ++i) w0.m[i] = i < nm ? W0->w[i] : W0->w[0];
@@ -304,23 +304,24 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
   mark(0);
   if (c.key_norm) {
     launch_stats_partial(pb, pl.S_stats, stats_part, st);
-    launch_stats_final(pb, pl.S_stats, stats_part, c.eps, stats, st);
+    // the MFMA gradient kernel merges the slices itself; the generic kernels
+    // read finished (mu, rstd) pairs
+    if (!pl.mfma_grad) launch_stats_final(pb, pl.S_stats, stats_part, c.eps, stats, st);
   }
   mark(1);
-  const bool need_bf = pl.mfma_grad || pl.mfma_query;
-  const int bf_layout = pl.bf_layout;
-  if (need_bf) launch_convert_bf16(pb, w0, bfs, bf_layout, st);   // bf16 state 0
 
   for (int b = 0; b < pl.nb; ++b) {
     const int t0 = chunk ? b * chunk : 0;
     const int nt = chunk ? std::min(chunk, c.N - t0) : c.N;
     const WRef cur = b == 0 ? w0 : state_ref(b);
     if (b == 0) mark(2);
-    if (pl.mfma_grad) {
+    if (pl.lact_grad) {
+      launch_lact_grad(pb, cur, t0, nt, pl.S_grad, eta->scale, part, st);
+    } else if (pl.mfma_grad) {
       // the kernel accumulates eta_n-weighted (V_hat - V) or -eta_n V; the
       // scalar eta and the MSE constant 2/(n_b d) are applied to its partials
       const float scale = pb.loss == LOSS_MSE ? eta->scale * 2.0f / ((float)nt * (float)c.d) : eta->scale;
-      launch_mfma_full_grad(pb, bfs + (long long)b * pl.bf_stride, t0, nt, scale, part, st);
+      launch_mfma_full_grad(pb, cur, t0, nt, scale, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part, st);
     } else {
       launch_gen_grad_out(pb, cur, t0, nt, gbuf, st);
       launch_gen_dW(pb, cur, t0, nt, gbuf, pl.S_grad, part, st);
@@ -337,8 +338,6 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
     ua.next = states + (long long)b * pl.state_stride;
     const bool last = b == pl.nb - 1;
     for (int i = 0; i < 3; ++i) ua.out[i] = (last && W_out && i < nm) ? W_out->w[i] : nullptr;
-    ua.bf = need_bf ? bfs + (long long)(b + 1) * pl.bf_stride : nullptr;
-    ua.bf_layout = bf_layout;
     ua.renorm = c.renorm;
     if (b == 0) mark(4);
     launch_update(pb, ua, st);
@@ -347,7 +346,9 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
 
   mark(6);
   if (pl.mfma_query) {
-    launch_mfma_query(pb, bfs, pl.bf_stride, chunk ? pl.nb : 1, chunk, st);
+    launch_mfma_query(pb, w0, states, pl.state_stride, chunk ? pl.nb : 1, chunk, st);
+  } else if (pl.lact_query) {
+    launch_lact_readout(pb, w0, states, pl.state_stride, chunk ? pl.nb : 1, chunk, st);
   } else {
     launch_gen_query(pb, w0, states, pl.state_stride, chunk ? pl.nb : 1, chunk, st);
   }

@@ -8,7 +8,6 @@ namespace ttt {
 
 enum { INNER_LINEAR = 0, INNER_MLP = 1, INNER_SWIGLU = 2 };
 enum { LOSS_MSE = 0, LOSS_DOT = 1 };
-enum { BF_ROWMAJOR = 0, BF_TRANSPOSED = 1, BF_MLP3 = 2 };
 
 // Everything a kernel of one update batch (the whole sequence in full-batch
 // mode, one chunk in causal mode) needs to know.
@@ -43,9 +42,8 @@ void launch_gen_query(const Problem& pb, const WRef& w0, const float* states, lo
                       int nchunks, int chunk, hipStream_t st);
 
 // ---- weight update (shared by every path) ----------------------------------
-// Wnew = Wcur - sum_s part[s]; optional column re-norm to W0's column norms;
-// writes the fp32 state (layout [P][nm][msz]), optionally W_out and a bf16
-// operand copy (layout chosen by `bf_layout`, see update.hip).
+// Wnew = Wcur - sum(partials); optional column re-norm to W0's column norms;
+// writes the fp32 state (layout [P][nm][msz]) and optionally W_out.
 struct UpdateArgs {
   WRef cur, w0;
   const float* part;            // gradient partials (already scaled by eta and the loss constant)
@@ -55,30 +53,39 @@ struct UpdateArgs {
   int sk_G, sk_J, sk_tpp;       // stream-K geometry of the gradient kernel
   float* next;                  // [P][nm][msz] fp32
   float* out[3];                // W_out matrices [B,H,in,out] or null
-  bf16* bf;                     // bf16 operand copy or null
-  int bf_layout;
   int renorm;
 };
 enum { PART_SPLITS = 0, PART_STREAMK = 1 };
 void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st);
-// bf16 operand copy of a weight state without an update (W0 for the first
-// gradient pass of the MFMA kernels)
-void launch_convert_bf16(const Problem& pb, const WRef& W, bf16* dst, int bf_layout, hipStream_t st);
 
 // ---- MFMA fast paths --------------------------------------------------------
-// GELU-MLP, d = 64, h in {64,128,256}, bf16: fused forward/backward of one
-// update batch (tokens [t0, t0+nt)) on bf16 MFMA, stream-K over the pairs'
-// tiles; partials land in BF_MLP3-ordered slots (see mfma_grad_geometry).
+// GELU-MLP, d = 64, h in {64,128,256}, bf16 tensors: fused forward/backward of
+// one update batch (tokens [t0, t0+nt)) at the fp32 weights W, stream-K over the
+// pairs' 32-token tiles; key statistics are combined from the per-slice
+// partials `spart` (S_stats slices, null: no key norm); partial slots as in
+// mfma_grad_geometry.
 bool mfma_full_supported(const Problem& pb);
 void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_per_pair);
-void launch_mfma_full_grad(const Problem& pb, const bf16* wbf, int t0, int nt, float scale, float* part,
-                           hipStream_t st);
-// readout O = F_W(Q) on bf16 MFMA; wstates: bf16 BF_MLP3 states, state s at
-// wstates + s*state_stride (state 0 = W0); full batch reads state 1, causal
-// chunk c reads state c.
+void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, float scale, const float* spart,
+                           int S_stats, float eps, float* part, hipStream_t st);
+// readout O = F_W(Q) on bf16 MFMA from fp32 states: full batch reads state 1,
+// causal chunk c reads state c (state 0 = w0, state s >= 1 at
+// states + (s-1)*state_stride, layout [P][nm][msz]).
 bool mfma_query_supported(const Problem& pb);
-void launch_mfma_query(const Problem& pb, const bf16* wstates, long long state_stride, int nchunks, int chunk,
-                       hipStream_t st);
+void launch_mfma_query(const Problem& pb, const WRef& w0, const float* states, long long state_stride, int nchunks,
+                       int chunk, hipStream_t st);
+
+// SwiGLU fast weights + negative dot loss (LaCT), bf16 tensors, d in {64,128},
+// h in {128,256}, no key norm: gradient of one update batch with hi/lo-split
+// bf16 MFMA operands (fp32-level accuracy), partials part[S][P][3][msz]
+bool lact_supported(const Problem& pb);
+int lact_grad_splits(const Problem& pb, int nt);
+void launch_lact_grad(const Problem& pb, const WRef& W, int t0, int nt, int S, float scale, float* part,
+                      hipStream_t st);
+// SwiGLU readout on bf16 MFMA (state addressing as launch_mfma_query)
+bool lact_readout_supported(const Problem& pb);
+void launch_lact_readout(const Problem& pb, const WRef& w0, const float* states, long long state_stride,
+                         int nchunks, int chunk, hipStream_t st);
 
 // ---- finiteness check ------------------------------------------------------
 void launch_zero_flag(int* flag, hipStream_t st);
