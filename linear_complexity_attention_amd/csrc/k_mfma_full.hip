@@ -37,7 +37,7 @@ namespace {
 constexpr int D = 64;
 constexpr int TT = 32;            // tokens per tile
 constexpr int LDK = 80;           // [token][channel] tile row stride (bf16)
-constexpr int LDT = 36;           // [unit][token] tile row stride (bf16)
+constexpr int LDT = 40;           // [unit][token] tile row stride (bf16; 80 B keeps 16-byte accesses aligned)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
@@ -123,6 +123,14 @@ __device__ __forceinline__ void key_stat(const float* sp, int S, int c, float ep
 }
 
 // ---------------------------------------------------------------------------
+// One tile's hidden activations as kept between pipeline stages: A (bf16, the
+// token order of the token-contracted MFMAs) and gelu'(Z) (bf16, same order).
+template <int NHB>
+struct Act {
+  bf16x8 a[NHB];
+  bf16x8 gp[NHB];
+};
+
 template <int HID, int LOSS, int NWAVE>
 __global__ void __launch_bounds__(NWAVE * 64, (NWAVE == 8 ? 2 : 1))
 k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float* __restrict__ spart, int S_stats,
@@ -134,14 +142,14 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
   constexpr int NB2 = 8 / NWAVE;       // V_hat / G' output blocks (of 2 x 4) per wave
   constexpr int SCH = D * TT / NTHR;   // channels staged per thread (8 or 4)
   constexpr int SPR = D / SCH;         // staging threads per token row
-  __shared__ __attribute__((aligned(16))) bf16 Kr[TT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 Vr[TT * LDK];
+  constexpr int LW2 = HID + 8;
+  // double-buffered token tiles; A and G' single-buffered (see the pipeline below)
+  __shared__ __attribute__((aligned(16))) bf16 Kr[2][TT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Vr[2][TT * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Gc[D * LDT];
   __shared__ __attribute__((aligned(16))) bf16 At[LOSS == LOSS_MSE ? HID * LDT : 8];
-  // W2^T of the pair ([c][h], bf16) for the V_hat = A W2 operand
-  constexpr int LW2 = HID + 8;
-  __shared__ __attribute__((aligned(16))) bf16 W2t[LOSS == LOSS_MSE ? D * LW2 : 8];
-  __shared__ float eta_s[TT];
+  __shared__ __attribute__((aligned(16))) bf16 W2t[LOSS == LOSS_MSE ? D * LW2 : 8];   // W2^T [c][h]
+  __shared__ float eta_s[2][TT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -155,8 +163,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
   const long long begin = (long long)blockIdx.x * total / G;
   const long long end = (long long)(blockIdx.x + 1) * total / G;
   const int p_first = (int)(begin / tpp);
-  const bf16* kin = (const bf16*)pb.k;
-  const bf16* vin = (const bf16*)pb.v;
+  typedef __attribute__((__vector_size__(SCH * sizeof(__bf16)))) __bf16 stg_t;
 
   long long x = begin;
   while (x < end) {
@@ -166,7 +173,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     const long long seg_end = end < (long long)(p + 1) * tpp ? end : (long long)(p + 1) * tpp;
     const int tile1 = (int)(seg_end - (long long)p * tpp);
 
-    // ---- weight fragments of this pair (fp32 state -> bf16 registers)
+    // ---- weight fragments of this pair (fp32 state -> bf16 registers / LDS)
     const float* W1 = W.mat(0, bb, hh);
     const float* W2 = W.mat(1, bb, hh);
     bf16x8 w1r[NHB][2], w2r[NHB][2];
@@ -185,10 +192,9 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         // hold every 64-bit address live at the same time
         __builtin_amdgcn_sched_barrier(0);
       }
-    if (LOSS == LOSS_MSE) {
-      __syncthreads();   // the previous segment's last tile may still read W2t
+    __syncthreads();   // the previous segment may still read W2t / the tiles
+    if (LOSS == LOSS_MSE)
       for (int e = tid; e < HID * D; e += NTHR) W2t[(e % D) * LW2 + e / D] = (bf16)W2[e];
-    }
     float mu[SCH], rs[SCH];
 #pragma unroll
     for (int j = 0; j < SCH; ++j) { mu[j] = 0.f; rs[j] = 1.f; }
@@ -197,8 +203,8 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
       for (int j = 0; j < SCH; ++j) key_stat(sp, S_stats, sc + j, eps, mu[j], rs[j]);
     }
-    const bf16* kp = kin + ((long long)p * pb.N + t0) * D;
-    const bf16* vp = vin + ((long long)p * pb.N + t0) * D;
+    const bf16* kp = (const bf16*)pb.k + ((long long)p * pb.N + t0) * D;
+    const bf16* vp = (const bf16*)pb.v + ((long long)p * pb.N + t0) * D;
     const float* ep = pb.eta_tok ? pb.eta_tok + (long long)p * pb.N + t0 : nullptr;
 
     f32x4 acc1[4][NHB], acc2[NHB][4];
@@ -207,42 +213,31 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
       for (int b = 0; b < NHB; ++b) { acc1[a][b] = f32x4{0, 0, 0, 0}; acc2[b][a] = f32x4{0, 0, 0, 0}; }
 
-    typedef __attribute__((__vector_size__(SCH * sizeof(__bf16)))) __bf16 stg_t;
+    // ---------------- pipeline stages ----------------
     stg_t kreg = {}, vreg = {};
-    {
-      const int n = tile0 * TT + st;
-      if (n < nt) {
+    auto prefetch = [&](int tile) {
+      const int n = tile * TT + st;
+      if (tile < tile1 && n < nt) {
         kreg = *reinterpret_cast<const stg_t*>(kp + (long long)n * D + sc);
         vreg = *reinterpret_cast<const stg_t*>(vp + (long long)n * D + sc);
       }
-    }
-
-    for (int tile = tile0; tile < tile1; ++tile) {
+    };
+    // normalised K, V ([token][channel]) and eta of `tile` into buffer buf
+    auto stage = [&](int tile, int buf) {
       const int n = tile * TT + st;
       const bool live = n < nt;
-      // ---- stage K_hat, V ([token][channel]) and eta
-      {
-        stg_t kh, vv;
+      stg_t kh, vv;
 #pragma unroll
-        for (int j = 0; j < SCH; ++j) {
-          kh[j] = live ? (bf16)(((float)kreg[j] - mu[j]) * rs[j]) : (bf16)0.f;
-          vv[j] = live ? vreg[j] : (bf16)0.f;
-        }
-        *reinterpret_cast<stg_t*>(&Kr[st * LDK + sc]) = kh;
-        *reinterpret_cast<stg_t*>(&Vr[st * LDK + sc]) = vv;
-        if (sc == 0) eta_s[st] = live ? (ep ? ep[n] : 1.0f) : 0.0f;
+      for (int j = 0; j < SCH; ++j) {
+        kh[j] = live ? (bf16)(((float)kreg[j] - mu[j]) * rs[j]) : (bf16)0.f;
+        vv[j] = live ? vreg[j] : (bf16)0.f;
       }
-      {
-        const int nn = (tile + 1) * TT + st;
-        if (tile + 1 < tile1 && nn < nt) {
-          kreg = *reinterpret_cast<const stg_t*>(kp + (long long)nn * D + sc);
-          vreg = *reinterpret_cast<const stg_t*>(vp + (long long)nn * D + sc);
-        }
-      }
-      __syncthreads();
-
-      // ---- Z = K_hat W1 (this wave's hidden slice), A = gelu(Z), gp = gelu'(Z)
-      f32x4 z[2][NHB];
+      *reinterpret_cast<stg_t*>(&Kr[buf][st * LDK + sc]) = kh;
+      *reinterpret_cast<stg_t*>(&Vr[buf][st * LDK + sc]) = vv;
+      if (sc == 0) eta_s[buf][st] = live ? (ep ? ep[n] : 1.0f) : 0.0f;
+    };
+    // Z = K_hat W1 for this wave's hidden slice
+    auto gemm1 = [&](int buf, f32x4 (&z)[2][NHB]) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -251,100 +246,140 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          const bf16x8 a = ld8(&Kr[(16 * tb + r) * LDK + 32 * ks + 8 * g]);
+          const bf16x8 a = ld8(&Kr[buf][(16 * tb + r) * LDK + 32 * ks + 8 * g]);
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) z[tb][hb] = mfma16(a, w1r[hb][ks], z[tb][hb]);
         }
-      f32x4 gp[2][NHB];
-      bf16x8 apk[NHB];
+    };
+    // A = gelu(Z), gp = gelu'(Z), packed in the (tb 0 | tb 1) token order
+    auto activate = [&](const f32x4 (&z)[2][NHB], Act<NHB>& act) {
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        f32x4 av[2];
+      for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float a_, g_;
             gelu_fast2(z[tb][hb][i], a_, g_);
-            av[tb][i] = a_;
-            gp[tb][hb][i] = g_;
+            act.a[hb][4 * tb + i] = (bf16)a_;
+            act.gp[hb][4 * tb + i] = (bf16)g_;
           }
-        apk[hb] = pack8(av[0], av[1]);
-        if (LOSS == LOSS_MSE) *reinterpret_cast<bf16x8*>(&At[(h0 + 16 * hb + r) * LDT + 8 * g]) = apk[hb];
+    };
+    auto write_at = [&](const Act<NHB>& act) {
+      if (LOSS == LOSS_MSE) {
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb)
+          *reinterpret_cast<bf16x8*>(&At[(h0 + 16 * hb + r) * LDT + 8 * g]) = act.a[hb];
       }
-      if (LOSS == LOSS_MSE) __syncthreads();
-
-      // ---- G' for the wave's (token block, channel block) pairs -> Gc
+    };
+    // G' of the wave's (token block, channel block) pairs -> Gc
+    auto gprime = [&](int buf) {
 #pragma unroll
       for (int b2 = 0; b2 < NB2; ++b2) {
         const int blk = w * NB2 + b2;
         const int tb2 = blk >> 2, cb2 = blk & 3;
         // V[t = 16 tb2 + 4 g + i][c = 16 cb2 + r]
-        const bf16x4 vq = ld_tr(&Vr[(16 * tb2 + 4 * g + (r >> 2)) * LDK + 16 * cb2 + 4 * (r & 3)]);
+        const bf16x4 vq = ld_tr(&Vr[buf][(16 * tb2 + 4 * g + (r >> 2)) * LDK + 16 * cb2 + 4 * (r & 3)]);
         f32x4 gv;
         if (LOSS == LOSS_MSE) {
-          f32x4 vh = f32x4{0, 0, 0, 0};
-#pragma unroll 2
+          // two independent accumulation chains halve the MFMA latency chain
+          f32x4 v0 = f32x4{0, 0, 0, 0}, v1 = f32x4{0, 0, 0, 0};
+#pragma unroll
           for (int ks = 0; ks < NKH; ++ks) {
             // A[t = 16 tb2 + r][h = 32 ks + 8 g + j]
             const bf16x4 lo = ld_tr(&At[(32 * ks + 8 * g + (r >> 2)) * LDT + tok_col(16 * tb2 + 4 * (r & 3))]);
             const bf16x4 hi = ld_tr(&At[(32 * ks + 8 * g + 4 + (r >> 2)) * LDT + tok_col(16 * tb2 + 4 * (r & 3))]);
-            vh = mfma16(cat44(lo, hi), ld8(&W2t[(16 * cb2 + r) * LW2 + 32 * ks + 8 * g]), vh);
+            const bf16x8 bw = ld8(&W2t[(16 * cb2 + r) * LW2 + 32 * ks + 8 * g]);
+            if (ks & 1) v1 = mfma16(cat44(lo, hi), bw, v1);
+            else v0 = mfma16(cat44(lo, hi), bw, v0);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i] = eta_s[16 * tb2 + 4 * g + i] * (vh[i] - (float)vq[i]);
+          for (int i = 0; i < 4; ++i) gv[i] = eta_s[buf][16 * tb2 + 4 * g + i] * ((v0[i] + v1[i]) - (float)vq[i]);
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i] = -eta_s[16 * tb2 + 4 * g + i] * (float)vq[i];
+          for (int i = 0; i < 4; ++i) gv[i] = -eta_s[buf][16 * tb2 + 4 * g + i] * (float)vq[i];
         }
         *reinterpret_cast<bf16x4*>(&Gc[(16 * cb2 + r) * LDT + 8 * g + 4 * tb2]) = pack4(gv);
       }
-      __syncthreads();
-
-      // ---- dW2 += A^T G'
+    };
+    // dW2 += A^T G';  dA = G' W2^T;  dZ = dA gelu'(Z);  dW1 += K_hat^T dZ
+    auto backward = [&](int buf, const Act<NHB>& act) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const bf16x8 b = ld8(&Gc[(16 * cb + r) * LDT + 8 * g]);
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) acc2[hb][cb] = mfma16(apk[hb], b, acc2[hb][cb]);
+        for (int hb = 0; hb < NHB; ++hb) acc2[hb][cb] = mfma16(act.a[hb], b, acc2[hb][cb]);
       }
-      // ---- dA = G' W2^T, dZ = dA * gelu'(Z)
+      f32x4 da[2][NHB];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) da[tb][hb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          // G'[t = 16 tb + r][c = 32 ks + 8 g + j]
+          const bf16x4 lo = ld_tr(&Gc[(32 * ks + 8 * g + (r >> 2)) * LDT + tok_col(16 * tb + 4 * (r & 3))]);
+          const bf16x4 hi = ld_tr(&Gc[(32 * ks + 8 * g + 4 + (r >> 2)) * LDT + tok_col(16 * tb + 4 * (r & 3))]);
+          const bf16x8 a = cat44(lo, hi);
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) da[tb][hb] = mfma16(a, w2r[hb][ks], da[tb][hb]);
+        }
       bf16x8 dzp[NHB];
-      {
-        f32x4 da[2][NHB];
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int hb = 0; hb < NHB; ++hb) da[tb][hb] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            // G'[t = 16 tb + r][c = 32 ks + 8 g + j]
-            const bf16x4 lo = ld_tr(&Gc[(32 * ks + 8 * g + (r >> 2)) * LDT + tok_col(16 * tb + 4 * (r & 3))]);
-            const bf16x4 hi = ld_tr(&Gc[(32 * ks + 8 * g + 4 + (r >> 2)) * LDT + tok_col(16 * tb + 4 * (r & 3))]);
-            const bf16x8 a = cat44(lo, hi);
-#pragma unroll
-            for (int hb = 0; hb < NHB; ++hb) da[tb][hb] = mfma16(a, w2r[hb][ks], da[tb][hb]);
-          }
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) {
-          f32x4 d0, d1;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { d0[i] = da[0][hb][i] * gp[0][hb][i]; d1[i] = da[1][hb][i] * gp[1][hb][i]; }
-          dzp[hb] = pack8(d0, d1);
-        }
-      }
-      // ---- dW1 += K_hat^T dZ ; K_hat[t = tau(g, j)][c = 16 cb + r]
+          for (int i = 0; i < 4; ++i) dzp[hb][4 * tb + i] = (bf16)(da[tb][hb][i] * (float)act.gp[hb][4 * tb + i]);
+      // K_hat[t = tau(g, j)][c = 16 cb + r]
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const bf16x4 lo = ld_tr(&Kr[(4 * g + (r >> 2)) * LDK + 16 * cb + 4 * (r & 3)]);
-        const bf16x4 hi = ld_tr(&Kr[(16 + 4 * g + (r >> 2)) * LDK + 16 * cb + 4 * (r & 3)]);
+        const bf16x4 lo = ld_tr(&Kr[buf][(4 * g + (r >> 2)) * LDK + 16 * cb + 4 * (r & 3)]);
+        const bf16x4 hi = ld_tr(&Kr[buf][(16 + 4 * g + (r >> 2)) * LDK + 16 * cb + 4 * (r & 3)]);
         const bf16x8 a = cat44(lo, hi);
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) acc1[cb][hb] = mfma16(a, dzp[hb], acc1[cb][hb]);
       }
+    };
+
+    // ---------------- prologue: tile0 through its G' ----------------
+    Act<NHB> cur;
+    prefetch(tile0);
+    stage(tile0, 0);
+    prefetch(tile0 + 1);
+    __syncthreads();
+    {
+      f32x4 z[2][NHB];
+      gemm1(0, z);
+      activate(z, cur);
+      write_at(cur);
+    }
+    if (LOSS == LOSS_MSE) __syncthreads();
+    gprime(0);
+    if (tile0 + 1 < tile1) { stage(tile0 + 1, 1); prefetch(tile0 + 2); }
+    __syncthreads();
+
+    // ---------------- steady state ----------------
+    // iteration i: forward of tile i+1 (GEMM1, GELU) overlapped with the
+    // backward of tile i; then V_hat / G' of tile i+1 and staging of tile i+2.
+    for (int tile = tile0; tile < tile1; ++tile) {
+      const int cb_ = (tile - tile0) & 1, nb_ = cb_ ^ 1;
+      const bool has_next = tile + 1 < tile1;
+      Act<NHB> nxt;
+      if (has_next) {
+        f32x4 z[2][NHB];
+        gemm1(nb_, z);
+        activate(z, nxt);
+      }
+      backward(cb_, cur);
+      if (has_next) write_at(nxt);
       __syncthreads();
+      if (has_next) gprime(nb_);
+      if (tile + 2 < tile1) { stage(tile + 2, cb_); prefetch(tile + 3); }
+      __syncthreads();
+      if (has_next) cur = nxt;
     }
 
     // ---- partial of this (workgroup, pair) segment: [dW1 (d x h) | dW2 (h x d)]
@@ -372,9 +407,9 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 // pair's token range; the pair's fp32 W1, W2 are staged in LDS as bf16 in their
 // natural layouts ([c][h] and [h][c]) and read transposed.
 constexpr int QTOK = 64;                 // tokens per wave pass
-constexpr int QWAVE = 4;
+constexpr int QWAVE = 8;
 template <int HID>
-__global__ void __launch_bounds__(QWAVE * 64, 2)
+__global__ void __launch_bounds__(QWAVE * 64, 1)
 k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long state_stride, int chunk, int span,
              int groups, int tok_per_wg) {
   constexpr int NTHR = QWAVE * 64;
@@ -424,9 +459,8 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) o[cb][tb] = f32x4{0, 0, 0, 0};
-#pragma unroll 2
-    for (int hc = 0; hc < HID / 32; ++hc) {
-      f32x4 zt[2][4];
+    // Z^T of hidden chunk hc (32 units) for the wave's 64 tokens
+    auto gemm1 = [&](int hc, f32x4 (&zt)[2][4]) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -442,12 +476,24 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb) zt[u][tb] = mfma16(a, qb[tb][ks], zt[u][tb]);
         }
+    };
+    // software pipeline: the first product of chunk hc+1 is issued before the
+    // GELU of chunk hc, so matrix and vector units work side by side
+    f32x4 zc[2][4], zn[2][4];
+    gemm1(0, zn);
+#pragma unroll
+    for (int hc = 0; hc < HID / 32; ++hc) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) zc[u][tb] = zn[u][tb];
+      if (hc + 1 < HID / 32) gemm1(hc + 1, zn);
       bf16x8 ab[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         f32x4 a0, a1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { a0[i] = gelu_fast(zt[0][tb][i]); a1[i] = gelu_fast(zt[1][tb][i]); }
+        for (int i = 0; i < 4; ++i) { a0[i] = gelu_fast(zc[0][tb][i]); a1[i] = gelu_fast(zc[1][tb][i]); }
         ab[tb] = pack8(a0, a1);
       }
 #pragma unroll
@@ -519,7 +565,7 @@ void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, flo
 void launch_mfma_query(const Problem& pb, const WRef& w0, const float* states, long long state_stride, int nchunks,
                        int chunk, hipStream_t st) {
   const int span = chunk ? (chunk < pb.N ? chunk : pb.N) : pb.N;
-  const int tpw = QWAVE * QTOK * 4;
+  const int tpw = QWAVE * QTOK * 2;
   const int groups = (span + tpw - 1) / tpw;
   dim3 grid(groups * nchunks, pb.B * pb.H);
   switch (pb.hid) {
