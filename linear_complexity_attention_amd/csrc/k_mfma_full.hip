@@ -25,9 +25,9 @@
 // axis so that both products chain through registers; the fp32 weights of the
 // pair's state are converted to bf16 into LDS (natural layouts) per workgroup.
 //
-// GELU here is z * sigma(y(z)), y = z (a + b z^2 + c z^4), a logistic fit of
-// the normal CDF (max |error| 3.7e-5 on gelu, 9.3e-5 on gelu', far below the
-// bf16 rounding of the MFMA operands); the fp32 kernels use the exact erf form.
+// GELU and gelu' are evaluated two elements at a time in packed f16 from a
+// polynomial fit of the normal CDF (see gelu_h2 below); the fp32 kernels use
+// the exact erf form.
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -54,31 +54,53 @@ __device__ __forceinline__ bf16x4 ld_tr(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// logistic fit of Phi: y = z (A + B t + C t^2), t = z^2, pre-scaled by -log2(e)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kGa = 1.59484567f, kGb = 7.40075326e-2f, kGc = -6.94974947e-4f;
-constexpr float kPa = -kGa * kLog2e, kPb = -kGb * kLog2e, kPc = -kGc * kLog2e;
-constexpr float kDa = kGa, kDb = 3.0f * kGb, kDc = 5.0f * kGc;
-
-__device__ __forceinline__ float sig_of(float zc, float t) {
-  const float p = __builtin_fmaf(t, __builtin_fmaf(t, kPc, kPb), kPa);
-  const float e = __builtin_amdgcn_exp2f(zc * p);
-  return __builtin_amdgcn_rcpf(1.0f + e);
+// Packed-f16 GELU.  With w = clamp(Z/c, -1, 1), u = w^2 and v = 2u - 1,
+//     c*Phi(Z) = c/2 + w P(v),     gelu'(Z) = 1/2 + w Q(v)
+// where P, Q are degree-6 fits in the shifted variable v (small coefficients,
+// so Horner in f16 loses little), c = 3.5.  gelu(Z) = (Z/c) * (c*Phi).  Two
+// elements per instruction and no transcendental; max |error| 3.3e-3 on gelu
+// (relative 5e-4 at large |Z|) and 2.9e-3 on gelu', inside the bf16 rounding
+// of the MFMA operands these values become.  The weights feeding Z are
+// pre-scaled by 1/c so the MFMA delivers Z/c directly.
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+constexpr float kClampC = 3.5f;
+__device__ __forceinline__ h2 hh(float x) { return h2{(_Float16)x, (_Float16)x}; }
+__device__ __forceinline__ h2 poly_p(h2 v) {
+  h2 p = hh(0.034846943f);
+  p = __builtin_elementwise_fma(p, v, hh(-0.1021939f));
+  p = __builtin_elementwise_fma(p, v, hh(0.186821488f));
+  p = __builtin_elementwise_fma(p, v, hh(-0.358320439f));
+  p = __builtin_elementwise_fma(p, v, hh(0.65378186f));
+  p = __builtin_elementwise_fma(p, v, hh(-1.10760263f));
+  return __builtin_elementwise_fma(p, v, hh(2.44194935f));
 }
-
-__device__ __forceinline__ float gelu_fast(float z) {
-  const float zc = __builtin_amdgcn_fmed3f(z, -9.0f, 9.0f);
-  return z * sig_of(zc, zc * zc);
+__device__ __forceinline__ h2 poly_q(h2 v) {
+  h2 q = hh(0.0954901068f);
+  q = __builtin_elementwise_fma(q, v, hh(-0.234467175f));
+  q = __builtin_elementwise_fma(q, v, hh(0.296631852f));
+  q = __builtin_elementwise_fma(q, v, hh(-0.388431366f));
+  q = __builtin_elementwise_fma(q, v, hh(0.49006813f));
+  q = __builtin_elementwise_fma(q, v, hh(-0.519321705f));
+  return __builtin_elementwise_fma(q, v, hh(0.763167748f));
 }
-
-__device__ __forceinline__ void gelu_fast2(float z, float& a, float& gp) {
-  const float zc = __builtin_amdgcn_fmed3f(z, -9.0f, 9.0f);
-  const float t = zc * zc;
-  const float s = sig_of(zc, t);
-  a = z * s;
-  const float yd = __builtin_fmaf(t, __builtin_fmaf(t, kDc, kDb), kDa);
-  const float ss = __builtin_fmaf(-s, s, s);
-  gp = __builtin_fmaf(zc * yd, ss, s);
+// (z0, z1) = Z/c of two elements -> gelu(Z) of both
+__device__ __forceinline__ void gelu_h2(float z0, float z1, float& a0, float& a1) {
+  h2 w = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(z0, z1));
+  w = __builtin_elementwise_min(__builtin_elementwise_max(w, hh(-1.0f)), hh(1.0f));
+  const h2 v = __builtin_elementwise_fma(w * w, hh(2.0f), hh(-1.0f));
+  const h2 cphi = __builtin_elementwise_fma(w, poly_p(v), hh(0.5f * kClampC));
+  a0 = z0 * (float)cphi.x;
+  a1 = z1 * (float)cphi.y;
+}
+// gelu and gelu' of two elements; gelu' stays packed f16
+__device__ __forceinline__ void gelu2_h2(float z0, float z1, float& a0, float& a1, h2& gp) {
+  h2 w = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(z0, z1));
+  w = __builtin_elementwise_min(__builtin_elementwise_max(w, hh(-1.0f)), hh(1.0f));
+  const h2 v = __builtin_elementwise_fma(w * w, hh(2.0f), hh(-1.0f));
+  const h2 cphi = __builtin_elementwise_fma(w, poly_p(v), hh(0.5f * kClampC));
+  gp = __builtin_elementwise_fma(w, poly_q(v), hh(0.5f));
+  a0 = z0 * (float)cphi.x;
+  a1 = z1 * (float)cphi.y;
 }
 
 __device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -128,7 +150,7 @@ __device__ __forceinline__ void key_stat(const float* sp, int S, int c, float ep
 template <int NHB>
 struct Act {
   bf16x8 a[NHB];
-  bf16x8 gp[NHB];
+  h2 gp[NHB][4];        // gelu'(Z), packed f16 pairs, same token order as a
 };
 
 template <int HID, int LOSS, int NWAVE>
@@ -187,7 +209,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         const float4 a = p2[0], b = p2[1];
         w2r[hb][ks] = bf16x8{(bf16)a.x, (bf16)a.y, (bf16)a.z, (bf16)a.w, (bf16)b.x, (bf16)b.y, (bf16)b.z, (bf16)b.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w1r[hb][ks][j] = (bf16)p1[j * HID];      // W1[c][h]
+        for (int j = 0; j < 8; ++j) w1r[hb][ks][j] = (bf16)(p1[j * HID] * (1.0f / kClampC));   // W1[c][h] / c
         // keep the fragment loads sequential: issuing them all at once would
         // hold every 64-bit address live at the same time
         __builtin_amdgcn_sched_barrier(0);
@@ -258,11 +280,11 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float a_, g_;
-            gelu_fast2(z[tb][hb][i], a_, g_);
-            act.a[hb][4 * tb + i] = (bf16)a_;
-            act.gp[hb][4 * tb + i] = (bf16)g_;
+          for (int i = 0; i < 4; i += 2) {
+            float a0, a1;
+            gelu2_h2(z[tb][hb][i], z[tb][hb][i + 1], a0, a1, act.gp[hb][2 * tb + i / 2]);
+            act.a[hb][4 * tb + i] = (bf16)a0;
+            act.a[hb][4 * tb + i + 1] = (bf16)a1;
           }
     };
     auto write_at = [&](const Act<NHB>& act) {
@@ -332,7 +354,10 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dzp[hb][4 * tb + i] = (bf16)(da[tb][hb][i] * (float)act.gp[hb][4 * tb + i]);
+          for (int i = 0; i < 4; ++i) {
+            const h2 gq = act.gp[hb][2 * tb + i / 2];
+            dzp[hb][4 * tb + i] = (bf16)(da[tb][hb][i] * (float)((i & 1) ? gq.y : gq.x));
+          }
       // K_hat[t = tau(g, j)][c = 16 cb + r]
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
@@ -437,9 +462,11 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
   for (int e = tid * 4; e < HID * D; e += NTHR * 4) {
     const float4 a = *reinterpret_cast<const float4*>(W1 + e);
     const float4 b = *reinterpret_cast<const float4*>(W2 + e);
-    const int c1 = e / HID, h1 = e % HID;         // W1 [c][h]
+    const int c1 = e / HID, h1 = e % HID;         // W1 [c][h], pre-scaled by 1/c for the packed GELU
     const int h2 = e / D, c2 = e % D;              // W2 [h][c]
-    *reinterpret_cast<bf16x4*>(&w1s[c1 * L1 + h1]) = bf16x4{(bf16)a.x, (bf16)a.y, (bf16)a.z, (bf16)a.w};
+    constexpr float ic = 1.0f / kClampC;
+    *reinterpret_cast<bf16x4*>(&w1s[c1 * L1 + h1]) =
+        bf16x4{(bf16)(a.x * ic), (bf16)(a.y * ic), (bf16)(a.z * ic), (bf16)(a.w * ic)};
     *reinterpret_cast<bf16x4*>(&w2s[h2 * L2 + c2]) = bf16x4{(bf16)b.x, (bf16)b.y, (bf16)b.z, (bf16)b.w};
   }
   __syncthreads();
@@ -493,7 +520,13 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
       for (int tb = 0; tb < 4; ++tb) {
         f32x4 a0, a1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { a0[i] = gelu_fast(zc[0][tb][i]); a1[i] = gelu_fast(zc[1][tb][i]); }
+        for (int i = 0; i < 4; i += 2) {
+          float x0, x1;
+          gelu_h2(zc[0][tb][i], zc[0][tb][i + 1], x0, x1);
+          a0[i] = x0; a0[i + 1] = x1;
+          gelu_h2(zc[1][tb][i], zc[1][tb][i + 1], x0, x1);
+          a1[i] = x0; a1[i + 1] = x1;
+        }
         ab[tb] = pack8(a0, a1);
       }
 #pragma unroll
