@@ -69,20 +69,22 @@ def stored_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(w, budget_s):
-    """The float64 oracle on whole (b, h) pairs of the same workload, one pair
-    after another until `budget_s` seconds have passed; scaled to tokens/s."""
+def cpu_baseline(w, budget_s, inputs):
+    """The float64 oracle on whole (b, h) pairs of the same workload and inputs,
+    pair after pair (wrapping round) until `budget_s` seconds have passed;
+    scaled to tokens/s of the whole layer."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import ttt_oracle as orc
-    from synth_inputs import make_inputs
 
-    q, k, v, W0, et = make_inputs(w, B=1)         # batch element 0: H pairs
+    q, k, v, W0, et = inputs
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     done, t_total = 0, 0.0
-    for h in range(w.H):
-        sl = (slice(0, 1), slice(h, h + 1))
+    while t_total < budget_s:
+        p = done % (w.B * w.H)
+        b, h = divmod(p, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
         args = [a[sl].astype(np.float64) for a in (q, k, v)]
         W = [m[h:h + 1].astype(np.float64) for m in W0]
         eta_tok = None if et is None else et[sl].astype(np.float64)
@@ -91,12 +93,11 @@ def cpu_baseline(w, budget_s):
                            chunk=w.chunk, key_norm=w.key_norm, renorm=w.renorm)
         t_total += time.perf_counter() - t
         done += 1
-        if t_total >= budget_s:
-            break
     pair_tokens_per_s = done * w.N / t_total
     return {"value": pair_tokens_per_s / w.H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.B * w.H} (b,h) pairs ({done * w.N} pair-tokens) of the same workload, "
-                      f"{t_total:.1f} s of float64 NumPy; tokens/s = pair-tokens/s / H"}
+            "sample": f"{done} (b,h) pair runs of the same workload's inputs ({done * w.N} pair-tokens, "
+                      f"{w.B * w.H} distinct pairs cycled), {t_total:.1f} s of float64 NumPy; "
+                      f"tokens/s = pair-tokens/s / H"}
 
 
 def main():
@@ -107,6 +108,9 @@ def main():
     ap.add_argument("--workload", default="c3_hires_r4")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (fp32 read + write) five times; its "
+                         "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -114,6 +118,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
+        return
 
     from linear_complexity_attention_amd import ttt
     from synth_inputs import WORKLOADS, make_inputs
@@ -125,7 +139,6 @@ def main():
     tq, tk, tv = (torch.from_numpy(a).to(dev).to(tdt).contiguous() for a in (q, k, v))
     tW = [torch.from_numpy(m).to(dev).contiguous() for m in W0]
     tet = torch.from_numpy(et).to(dev).contiguous() if et is not None else None
-    del q, k, v
     layer = ttt.TTTLayer(w.B, w.H, w.N, w.d, w.hidden, dtype=w.dtype, key_norm=w.key_norm, eps=1e-5,
                          renorm=w.renorm)
     out = torch.empty_like(tq)
@@ -191,13 +204,14 @@ def main():
         "layer_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
         "frac_of_bf16_peak": layer_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "kernel_ms": kern_ms,
-        "roofline": {"kernel": "fused forward/backward (k_mfma_grad)" if "mfma" in (path or "") else "grad",
+        "roofline": {"kernel": {"mfma": "fused forward/backward (k_mfma_grad)",
+                                "mfma_swiglu": "SwiGLU forward/backward (k_lact_grad), first chunk"}.get(path, "grad"),
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "algorithmic_flops_per_launch": grad_flops},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, (q, k, v, W0, et))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

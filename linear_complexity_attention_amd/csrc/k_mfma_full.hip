@@ -28,6 +28,8 @@
 // GELU and gelu' are evaluated two elements at a time in packed f16 from a
 // polynomial fit of the normal CDF (see gelu_h2 below); the fp32 kernels use
 // the exact erf form.
+#include <type_traits>
+
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -428,126 +430,186 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 }
 
 // ---------------------------------------------------------------------------
-// O = gelu(Q W1*) W2* with tokens on the MFMA n axis.  One workgroup = one
-// pair's token range; the pair's fp32 W1, W2 are staged in LDS as bf16 in their
-// natural layouts ([c][h] and [h][c]) and read transposed.
-constexpr int QTOK = 64;                 // tokens per wave pass
-constexpr int QWAVE = 8;
+// O = gelu(Q W1*) W2* with tokens on the MFMA n axis.
+//
+// One workgroup of 16 waves per CU.  The (pair, token) space is cut into equal
+// contiguous ranges, one per workgroup; a range covers one or two weight
+// states (pair, chunk).  For each state the workgroup stages the weights in
+// LDS in their natural layouts (read transposed by the MFMA operand loads) and
+// splits its tokens over the waves in 16-token units, so every wave gets the
+// same work to within 16 tokens.  A wave walks its tokens 32 at a time (16 for
+// the last piece) and prefetches the next piece's Q while computing.
+//
+// The first product runs on bf16 (Q is bf16); the second on f16, fed straight
+// from the packed-f16 GELU: W1 is staged scaled by sqrt(2)/c, so the MFMA
+// yields zh = sqrt(2) Z / c, and with w = clamp(zh, +-sqrt(2)), v = w^2 - 1
+//     c Phi(Z) = c/2 + w P(v) / sqrt(2),   zh * c Phi(Z) = sqrt(2) gelu(Z);
+// W2 is staged scaled by 1/sqrt(2) to compensate.
+// Workgroup -> range mapping is XCD-aware: consecutive ranges (which share a
+// pair's weights) are given to workgroups of the same XCD.
+constexpr int QW = 16;                  // waves per workgroup
+constexpr float kSqrt2 = 1.41421356237f;
+constexpr float kRSqrt2 = 0.70710678119f;
+
+__device__ __forceinline__ h2 poly_p_s(h2 v) {       // P(v) / sqrt(2)
+  h2 p = hh(0.034846943f * kRSqrt2);
+  p = __builtin_elementwise_fma(p, v, hh(-0.1021939f * kRSqrt2));
+  p = __builtin_elementwise_fma(p, v, hh(0.186821488f * kRSqrt2));
+  p = __builtin_elementwise_fma(p, v, hh(-0.358320439f * kRSqrt2));
+  p = __builtin_elementwise_fma(p, v, hh(0.65378186f * kRSqrt2));
+  p = __builtin_elementwise_fma(p, v, hh(-1.10760263f * kRSqrt2));
+  return __builtin_elementwise_fma(p, v, hh(2.44194935f * kRSqrt2));
+}
+typedef float f2 __attribute__((ext_vector_type(2)));
+// (z0, z1) = sqrt(2) Z / c of two elements -> sqrt(2) gelu(Z) of both, packed f16
+__device__ __forceinline__ h2 gelu_s2(float z0, float z1) {
+  const h2 zh = __builtin_convertvector(f2{z0, z1}, h2);
+  const h2 w = __builtin_elementwise_min(__builtin_elementwise_max(zh, hh(-kSqrt2)), hh(kSqrt2));
+  const h2 v = __builtin_elementwise_fma(w, w, hh(-1.0f));
+  const h2 cphi = __builtin_elementwise_fma(w, poly_p_s(v), hh(0.5f * kClampC));
+  return zh * cphi;
+}
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 ld_tr_h(const f16* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)((__attribute__((address_space(3))) char*)p));
+  return __builtin_bit_cast(f16x4, v);
+}
+
 template <int HID>
-__global__ void __launch_bounds__(QWAVE * 64, 1)
-k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long state_stride, int chunk, int span,
-             int groups, int tok_per_wg) {
-  constexpr int NTHR = QWAVE * 64;
+__global__ void __launch_bounds__(QW * 64, 1)
+k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long state_stride, int chunk, int span) {
+  constexpr int NTHR = QW * 64;
   constexpr int L1 = HID + 16;           // [c][h] row stride (16 mod 128: conflict-free transposed reads)
   constexpr int L2 = 80;                 // [h][c] row stride
   __shared__ __attribute__((aligned(16))) bf16 w1s[D * L1];
-  __shared__ __attribute__((aligned(16))) bf16 w2s[HID * L2];
-  const int p = blockIdx.y;
+  __shared__ __attribute__((aligned(16))) f16 w2s[HID * L2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int c = blockIdx.x / groups, grp = blockIdx.x % groups;
-  const int c0 = c * span;
-  const int n0 = c0 + grp * tok_per_wg;
-  const int n1 = min(min(pb.N, c0 + span), n0 + tok_per_wg);
-  if (n0 >= n1) return;
-  // full batch reads state 1 (after the update); causal chunk c reads state c
-  const int state = chunk ? c : 1;
-  const int bb = p / pb.H, hh = p % pb.H;
-  const float *W1, *W2;
-  if (state == 0) { W1 = w0.mat(0, bb, hh); W2 = w0.mat(1, bb, hh); }
-  else {
-    const float* base = states + (state - 1) * state_stride + (long long)p * 2 * D * HID;
-    W1 = base; W2 = base + (long long)D * HID;
-  }
-  for (int e = tid * 4; e < HID * D; e += NTHR * 4) {
-    const float4 a = *reinterpret_cast<const float4*>(W1 + e);
-    const float4 b = *reinterpret_cast<const float4*>(W2 + e);
-    const int c1 = e / HID, h1 = e % HID;         // W1 [c][h], pre-scaled by 1/c for the packed GELU
-    const int h2 = e / D, c2 = e % D;              // W2 [h][c]
-    constexpr float ic = 1.0f / kClampC;
-    *reinterpret_cast<bf16x4*>(&w1s[c1 * L1 + h1]) =
-        bf16x4{(bf16)(a.x * ic), (bf16)(a.y * ic), (bf16)(a.z * ic), (bf16)(a.w * ic)};
-    *reinterpret_cast<bf16x4*>(&w2s[h2 * L2 + c2]) = bf16x4{(bf16)b.x, (bf16)b.y, (bf16)b.z, (bf16)b.w};
-  }
-  __syncthreads();
-  const bf16* qp = (const bf16*)pb.q + (long long)p * pb.N * D;
-  bf16* op = (bf16*)pb.o + (long long)p * pb.N * D;
-  for (int base = n0 + w * QTOK; base < n1; base += QWAVE * QTOK) {
-    bf16x8 qb[4][2];
+  const int N = pb.N;
+  const long long T = (long long)pb.B * pb.H * N;
+  const int G = gridDim.x;
+  const int L = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  long long t = (long long)L * T / G;
+  const long long t_end = (long long)(L + 1) * T / G;
+
+  while (t < t_end) {
+    const int p = (int)(t / N);
+    const int n0 = (int)(t - (long long)p * N);
+    const int c = n0 / span;
+    const int n1 = (int)min((long long)min(N, (c + 1) * span), n0 + (t_end - t));
+    // full batch reads state 1 (after the update); causal chunk c reads state c
+    const int state = chunk ? c : 1;
+    const int bb = p / pb.H, hh_ = p % pb.H;
+    const float *W1, *W2;
+    if (state == 0) { W1 = w0.mat(0, bb, hh_); W2 = w0.mat(1, bb, hh_); }
+    else {
+      const float* base = states + (state - 1) * state_stride + (long long)p * 2 * D * HID;
+      W1 = base; W2 = base + (long long)D * HID;
+    }
+    __syncthreads();                     // the previous state's LDS reads are done
+    for (int e = tid * 4; e < HID * D; e += NTHR * 4) {
+      const float4 a = *reinterpret_cast<const float4*>(W1 + e);
+      const float4 b = *reinterpret_cast<const float4*>(W2 + e);
+      const int c1 = e / HID, h1 = e % HID;         // W1 [c][h]
+      const int h2_ = e / D, c2 = e % D;             // W2 [h][c]
+      constexpr float s1 = kSqrt2 / kClampC;
+      *reinterpret_cast<bf16x4*>(&w1s[c1 * L1 + h1]) =
+          bf16x4{(bf16)(a.x * s1), (bf16)(a.y * s1), (bf16)(a.z * s1), (bf16)(a.w * s1)};
+      *reinterpret_cast<f16x4*>(&w2s[h2_ * L2 + c2]) =
+          f16x4{(f16)(b.x * kRSqrt2), (f16)(b.y * kRSqrt2), (f16)(b.z * kRSqrt2), (f16)(b.w * kRSqrt2)};
+    }
+    __syncthreads();
+
+    const int units = (n1 - n0 + 15) >> 4;
+    const int a_ = n0 + 16 * (w * units / QW);
+    const int b_ = min(n1, n0 + 16 * ((w + 1) * units / QW));
+    const bf16* qp = (const bf16*)pb.q + (long long)p * N * D;
+    bf16* op = (bf16*)pb.o + (long long)p * N * D;
+    auto load_q = [&](int pos, bf16x8 (&q)[2][2]) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int n = base + 16 * tb + r;
-        qb[tb][ks] = n < n1 ? ld8(qp + (long long)n * D + 32 * ks + 8 * g) : bf16x8{};
-      }
-    f32x4 o[4][4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) o[cb][tb] = f32x4{0, 0, 0, 0};
-    // Z^T of hidden chunk hc (32 units) for the wave's 64 tokens
-    auto gemm1 = [&](int hc, f32x4 (&zt)[2][4]) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) zt[u][tb] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          // W1^T operand: W1[c = 32 ks + 8 g + j][h = 32 hc + 16 u + r]
-          const bf16x4 lo = ld_tr(&w1s[(32 * ks + 8 * g + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
-          const bf16x4 hi = ld_tr(&w1s[(32 * ks + 8 * g + 4 + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
-          const bf16x8 a = cat44(lo, hi);
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) zt[u][tb] = mfma16(a, qb[tb][ks], zt[u][tb]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int n = pos + 16 * tb + r;
+          q[tb][ks] = n < b_ ? ld8(qp + (long long)n * D + 32 * ks + 8 * g) : bf16x8{};
         }
     };
-    // software pipeline: the first product of chunk hc+1 is issued before the
-    // GELU of chunk hc, so matrix and vector units work side by side
-    f32x4 zc[2][4], zn[2][4];
-    gemm1(0, zn);
+    // one pass over NTB 16-token blocks starting at pos
+    auto pass = [&](auto ntb_c, int pos, const bf16x8 (&q)[2][2]) {
+      constexpr int NTB = decltype(ntb_c)::value;
+      f32x4 o[4][NTB];
 #pragma unroll
-    for (int hc = 0; hc < HID / 32; ++hc) {
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = f32x4{0, 0, 0, 0};
+#pragma unroll 2
+      for (int hc = 0; hc < HID / 32; ++hc) {
+        f32x4 z[2][NTB];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) zc[u][tb] = zn[u][tb];
-      if (hc + 1 < HID / 32) gemm1(hc + 1, zn);
-      bf16x8 ab[4];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        f32x4 a0, a1;
+          for (int tb = 0; tb < NTB; ++tb) z[u][tb] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          float x0, x1;
-          gelu_h2(zc[0][tb][i], zc[0][tb][i + 1], x0, x1);
-          a0[i] = x0; a0[i + 1] = x1;
-          gelu_h2(zc[1][tb][i], zc[1][tb][i + 1], x0, x1);
-          a1[i] = x0; a1[i + 1] = x1;
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            // W1^T operand: W1[c = 32 ks + 8 g + j][h = 32 hc + 16 u + r]
+            const bf16x4 lo = ld_tr(&w1s[(32 * ks + 8 * g + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
+            const bf16x4 hi = ld_tr(&w1s[(32 * ks + 8 * g + 4 + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
+            const bf16x8 a = cat44(lo, hi);
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) z[u][tb] = mfma16(a, q[tb][ks], z[u][tb]);
+          }
+        // activation operand: hidden k-slots j < 4 -> u = 0, i = j; j >= 4 -> u = 1, i = j - 4
+        f16x8 ab[NTB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+          const h2 x0 = gelu_s2(z[0][tb][0], z[0][tb][1]), x1 = gelu_s2(z[0][tb][2], z[0][tb][3]);
+          const h2 x2 = gelu_s2(z[1][tb][0], z[1][tb][1]), x3 = gelu_s2(z[1][tb][2], z[1][tb][3]);
+          ab[tb] = f16x8{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
         }
-        ab[tb] = pack8(a0, a1);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          // W2^T operand: W2[h = 32 hc + tau(g, j)][c = 16 cb + r]
+          const f16x4 lo = ld_tr_h(&w2s[(32 * hc + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
+          const f16x4 hi = ld_tr_h(&w2s[(32 * hc + 16 + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
+          const f16x8 a = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = mfma16h(a, ab[tb], o[cb][tb]);
+        }
       }
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        // W2^T operand: W2[h = 32 hc + tau(g, j)][c = 16 cb + r]
-        const bf16x4 lo = ld_tr(&w2s[(32 * hc + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
-        const bf16x4 hi = ld_tr(&w2s[(32 * hc + 16 + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
-        const bf16x8 a = cat44(lo, hi);
+      for (int tb = 0; tb < NTB; ++tb) {
+        const int n = pos + 16 * tb + r;
+        if (n < b_) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) o[cb][tb] = mfma16(a, ab[tb], o[cb][tb]);
+          for (int cb = 0; cb < 4; ++cb)
+            *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = pack4(o[cb][tb]);
+        }
       }
+    };
+    bf16x8 qc[2][2];
+    int pos = a_;
+    if (pos < b_) load_q(pos, qc);
+    while (pos < b_) {
+      const int take = b_ - pos > 16 ? 32 : 16;
+      const int nxt = pos + take;
+      bf16x8 qn[2][2];
+      if (nxt < b_) load_q(nxt, qn);     // prefetch the next piece
+      if (take == 32) pass(std::integral_constant<int, 2>{}, pos, qc);
+      else pass(std::integral_constant<int, 1>{}, pos, qc);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) qc[tb][ks] = qn[tb][ks];
+      pos = nxt;
     }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int n = base + 16 * tb + r;
-      if (n < n1) {
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = pack4(o[cb][tb]);
-      }
-    }
+    t += n1 - n0;
   }
 }
 
@@ -597,14 +659,17 @@ void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, flo
 
 void launch_mfma_query(const Problem& pb, const WRef& w0, const float* states, long long state_stride, int nchunks,
                        int chunk, hipStream_t st) {
+  (void)nchunks;
   const int span = chunk ? (chunk < pb.N ? chunk : pb.N) : pb.N;
-  const int tpw = QWAVE * QTOK * 2;
-  const int groups = (span + tpw - 1) / tpw;
-  dim3 grid(groups * nchunks, pb.B * pb.H);
+  // one workgroup per CU, fewer when there are not 512 tokens for each
+  const long long T = (long long)pb.B * pb.H * pb.N;
+  long long G = device_cu_count();
+  if (G > (T + 511) / 512) G = (T + 511) / 512;
+  if (G < 1) G = 1;
   switch (pb.hid) {
-    case 64: hipLaunchKernelGGL((k_mfma_query<64>), grid, dim3(QWAVE * 64), 0, st, pb, w0, states, state_stride, chunk, span, groups, tpw); break;
-    case 128: hipLaunchKernelGGL((k_mfma_query<128>), grid, dim3(QWAVE * 64), 0, st, pb, w0, states, state_stride, chunk, span, groups, tpw); break;
-    default: hipLaunchKernelGGL((k_mfma_query<256>), grid, dim3(QWAVE * 64), 0, st, pb, w0, states, state_stride, chunk, span, groups, tpw); break;
+    case 64: hipLaunchKernelGGL((k_mfma_query<64>), dim3((unsigned)G), dim3(QW * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
+    case 128: hipLaunchKernelGGL((k_mfma_query<128>), dim3((unsigned)G), dim3(QW * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
+    default: hipLaunchKernelGGL((k_mfma_query<256>), dim3((unsigned)G), dim3(QW * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
   }
 }
 

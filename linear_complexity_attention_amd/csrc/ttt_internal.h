@@ -87,6 +87,9 @@ bool lact_readout_supported(const Problem& pb);
 void launch_lact_readout(const Problem& pb, const WRef& w0, const float* states, long long state_stride,
                          int nchunks, int chunk, hipStream_t st);
 
+// compute units of the current device (cached per device; 256 if unknown)
+int device_cu_count();
+
 // ---- finiteness check ------------------------------------------------------
 void launch_zero_flag(int* flag, hipStream_t st);
 void launch_check_finite(const Problem& pb, float* const* wfinal, long long wcount, int* flag,
