@@ -38,8 +38,8 @@ namespace {
 
 constexpr int D = 64;
 constexpr int TT = 32;            // tokens per tile
-constexpr int LDK = 80;           // [token][channel] tile row stride (bf16)
-constexpr int LDT = 40;           // [unit][token] tile row stride (bf16; 80 B keeps 16-byte accesses aligned)
+constexpr int LDK = 64;           // [token][channel] tile row stride (bf16), swizzled by kswz
+constexpr int LDT = 32;           // [unit][token] tile row stride (bf16), swizzled by tswz
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
@@ -124,6 +124,18 @@ __device__ __forceinline__ bf16x4 pack4(const f32x4& x) {
   for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
   return r;
 }
+// XOR swizzles of the LDS tiles (column index in bf16 elements).  Row `row`
+// of a [token][channel] tile stores channel c at c ^ kswz(row); row `row` of a
+// [unit][token] tile stores token column t at t ^ tswz(row).  They make every
+// access pattern of the gradient kernel conflict-free on the 64 LDS banks:
+// 16-byte row reads and staging writes, and the transposing 8-byte reads
+// whose 32 lanes span rows {0..7} (token tiles) or {0..3, 8..11} (unit tiles).
+// kswz moves whole 8-element pieces, so 16-byte accesses stay contiguous;
+// tswz also moves 4-element halves, so 16-byte accesses to [unit][token]
+// tiles are split into two 8-byte ones.
+__device__ __forceinline__ int kswz(int row) { return ((row >> 3) & 1) * 8 + ((row >> 1) & 1) * 16 + ((row >> 2) & 1) * 32; }
+__device__ __forceinline__ int tswz(int row) { return ((row >> 3) & 1) * 4 + (row & 1) * 8 + ((row >> 2) & 1) * 16; }
+
 // storage column of token t inside a 32-token [unit][token] row: the 8 tokens
 // of MFMA lane group g (4g..4g+3 and 16+4g..16+4g+3) are contiguous at 8g.
 __device__ __forceinline__ int tok_col(int t) { return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3); }
@@ -256,8 +268,8 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         kh[j] = live ? (bf16)(((float)kreg[j] - mu[j]) * rs[j]) : (bf16)0.f;
         vv[j] = live ? vreg[j] : (bf16)0.f;
       }
-      *reinterpret_cast<stg_t*>(&Kr[buf][st * LDK + sc]) = kh;
-      *reinterpret_cast<stg_t*>(&Vr[buf][st * LDK + sc]) = vv;
+      *reinterpret_cast<stg_t*>(&Kr[buf][st * LDK + (sc ^ kswz(st))]) = kh;
+      *reinterpret_cast<stg_t*>(&Vr[buf][st * LDK + (sc ^ kswz(st))]) = vv;
       if (sc == 0) eta_s[buf][st] = live ? (ep ? ep[n] : 1.0f) : 0.0f;
     };
     // Z = K_hat W1 for this wave's hidden slice
@@ -270,7 +282,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          const bf16x8 a = ld8(&Kr[buf][(16 * tb + r) * LDK + 32 * ks + 8 * g]);
+          const bf16x8 a = ld8(&Kr[buf][(16 * tb + r) * LDK + ((32 * ks + 8 * g) ^ kswz(r))]);
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) z[tb][hb] = mfma16(a, w1r[hb][ks], z[tb][hb]);
         }
@@ -293,7 +305,12 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       if (LOSS == LOSS_MSE) {
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb)
-          *reinterpret_cast<bf16x8*>(&At[(h0 + 16 * hb + r) * LDT + 8 * g]) = act.a[hb];
+        {
+          bf16* row = &At[(h0 + 16 * hb + r) * LDT];
+          const bf16x8& v = act.a[hb];
+          *reinterpret_cast<bf16x4*>(row + ((8 * g) ^ tswz(r))) = bf16x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<bf16x4*>(row + ((8 * g + 4) ^ tswz(r))) = bf16x4{v[4], v[5], v[6], v[7]};
+        }
       }
     };
     // G' of the wave's (token block, channel block) pairs -> Gc
@@ -303,7 +320,8 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         const int blk = w * NB2 + b2;
         const int tb2 = blk >> 2, cb2 = blk & 3;
         // V[t = 16 tb2 + 4 g + i][c = 16 cb2 + r]
-        const bf16x4 vq = ld_tr(&Vr[buf][(16 * tb2 + 4 * g + (r >> 2)) * LDK + 16 * cb2 + 4 * (r & 3)]);
+        const int vrow = 16 * tb2 + 4 * g + (r >> 2);
+        const bf16x4 vq = ld_tr(&Vr[buf][vrow * LDK + ((16 * cb2 + 4 * (r & 3)) ^ kswz(vrow))]);
         f32x4 gv;
         if (LOSS == LOSS_MSE) {
           // two independent accumulation chains halve the MFMA latency chain
@@ -311,8 +329,9 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
           for (int ks = 0; ks < NKH; ++ks) {
             // A[t = 16 tb2 + r][h = 32 ks + 8 g + j]
-            const bf16x4 lo = ld_tr(&At[(32 * ks + 8 * g + (r >> 2)) * LDT + tok_col(16 * tb2 + 4 * (r & 3))]);
-            const bf16x4 hi = ld_tr(&At[(32 * ks + 8 * g + 4 + (r >> 2)) * LDT + tok_col(16 * tb2 + 4 * (r & 3))]);
+            const int ar = 32 * ks + 8 * g + (r >> 2);
+            const bf16x4 lo = ld_tr(&At[ar * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar))]);
+            const bf16x4 hi = ld_tr(&At[(ar + 4) * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar + 4))]);
             const bf16x8 bw = ld8(&W2t[(16 * cb2 + r) * LW2 + 32 * ks + 8 * g]);
             if (ks & 1) v1 = mfma16(cat44(lo, hi), bw, v1);
             else v0 = mfma16(cat44(lo, hi), bw, v0);
@@ -323,14 +342,16 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
           for (int i = 0; i < 4; ++i) gv[i] = -eta_s[buf][16 * tb2 + 4 * g + i] * (float)vq[i];
         }
-        *reinterpret_cast<bf16x4*>(&Gc[(16 * cb2 + r) * LDT + 8 * g + 4 * tb2]) = pack4(gv);
+        *reinterpret_cast<bf16x4*>(&Gc[(16 * cb2 + r) * LDT + ((8 * g + 4 * tb2) ^ tswz(r))]) = pack4(gv);
       }
     };
     // dW2 += A^T G';  dA = G' W2^T;  dZ = dA gelu'(Z);  dW1 += K_hat^T dZ
     auto backward = [&](int buf, const Act<NHB>& act) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const bf16x8 b = ld8(&Gc[(16 * cb + r) * LDT + 8 * g]);
+        const bf16* grow = &Gc[(16 * cb + r) * LDT];
+        const bf16x8 b = cat44(*reinterpret_cast<const bf16x4*>(grow + ((8 * g) ^ tswz(r))),
+                               *reinterpret_cast<const bf16x4*>(grow + ((8 * g + 4) ^ tswz(r))));
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) acc2[hb][cb] = mfma16(act.a[hb], b, acc2[hb][cb]);
       }
@@ -344,8 +365,9 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           // G'[t = 16 tb + r][c = 32 ks + 8 g + j]
-          const bf16x4 lo = ld_tr(&Gc[(32 * ks + 8 * g + (r >> 2)) * LDT + tok_col(16 * tb + 4 * (r & 3))]);
-          const bf16x4 hi = ld_tr(&Gc[(32 * ks + 8 * g + 4 + (r >> 2)) * LDT + tok_col(16 * tb + 4 * (r & 3))]);
+          const int gr = 32 * ks + 8 * g + (r >> 2);
+          const bf16x4 lo = ld_tr(&Gc[gr * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr))]);
+          const bf16x4 hi = ld_tr(&Gc[(gr + 4) * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr + 4))]);
           const bf16x8 a = cat44(lo, hi);
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) da[tb][hb] = mfma16(a, w2r[hb][ks], da[tb][hb]);
@@ -363,8 +385,9 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       // K_hat[t = tau(g, j)][c = 16 cb + r]
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const bf16x4 lo = ld_tr(&Kr[buf][(4 * g + (r >> 2)) * LDK + 16 * cb + 4 * (r & 3)]);
-        const bf16x4 hi = ld_tr(&Kr[buf][(16 + 4 * g + (r >> 2)) * LDK + 16 * cb + 4 * (r & 3)]);
+        const int kr0 = 4 * g + (r >> 2);
+        const bf16x4 lo = ld_tr(&Kr[buf][kr0 * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0))]);
+        const bf16x4 hi = ld_tr(&Kr[buf][(kr0 + 16) * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0 + 16))]);
         const bf16x8 a = cat44(lo, hi);
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) acc1[cb][hb] = mfma16(a, dzp[hb], acc1[cb][hb]);
