@@ -76,7 +76,14 @@ typedef enum { TTT_INNER_LINEAR = 0, TTT_INNER_MLP_GELU = 1, TTT_INNER_SWIGLU = 
                                         return TTT_ERR_NONFINITE if O or the final
                                         weights hold a NaN or Inf */
 #define TTT_FLAG_FORCE_GENERIC 0x2u  /* use the generic fp32-arithmetic kernels even
-                                        where a bf16 MFMA kernel exists */
+                                        where an MFMA kernel exists.  The GELU-MLP
+                                        MFMA kernels (bf16 tensors, d = 64) carry
+                                        the activations, the loss gradient and dZ
+                                        as f16, so they need |F(k) - v|, |v| and
+                                        the pre-activations below ~4e4; larger
+                                        values overflow to Inf (reported by
+                                        TTT_FLAG_CHECK_FINITE).  This flag lifts
+                                        that limit at fp32-kernel speed. */
 #define TTT_FLAG_LOG 0x4u            /* print the chosen kernels and launch shapes to stderr */
 
 typedef struct {

@@ -1,5 +1,5 @@
-// bf16 MFMA kernels of the GELU-MLP inner model, head dimension 64, hidden
-// width 64/128/256 (gfx950, wave64, v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// MFMA kernels of the GELU-MLP inner model, head dimension 64, hidden width
+// 64/128/256 (gfx950, wave64, v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulate).
 //
 // k_mfma_grad: steps (i)-(ii) of one inner update (ViT3 summary page, section
 // 02), fused per 32-token tile:
@@ -11,22 +11,23 @@
 //     dW2 += A^T G',  dA = G' W2^T,  dZ = dA * gelu'(Z),  dW1 += K_hat^T dZ
 // Each wave owns a slice of the hidden units (its slice of Z, A, dA, dZ, dW1,
 // dW2, with the weight fragments of that slice held in registers).  The tiles
-// shared by all waves sit in LDS in their natural layouts and are written with
-// wide stores only: K and V as [token][channel]; A and G' as
-// [unit][token], tokens of a row stored in the order the MFMA output packs them
-// (so one lane writes its 8 tokens with one store).  Operands that need the
-// other orientation are fetched with the transposing LDS read
-// ds_read_b64_tr_b16.  The token range of all (b, h) pairs is cut evenly over
-// the grid ("stream-K"): a workgroup that crosses a pair boundary writes one
-// fp32 partial per pair it touched; the update kernel adds them in a fixed
-// order, so results are run-to-run identical.
+// shared by all waves sit in LDS, XOR-swizzled so that every access is free
+// of bank conflicts: K and V as [token][channel]; A and G' as [unit][token],
+// tokens of a row stored in the order the MFMA output packs them (so one lane
+// writes its 8 tokens at once).  Operands that need the other orientation are
+// fetched with the transposing LDS read ds_read_b64_tr_b16.  A, G' and dZ are
+// f16 (A and dZ come out of the packed-f16 GELU), and so is the normalised key
+// tile (|K_hat| <= sqrt(N)); raw keys (no key norm) stay bf16.  The token range
+// of all (b, h) pairs is cut evenly over the grid ("stream-K"): a workgroup
+// that crosses a pair boundary writes one fp32 partial per pair it touched;
+// the update kernel adds them in a fixed order, so results are run-to-run
+// identical.
 //
 // k_mfma_query: step (iii), O = gelu(Q W1*) W2*, with tokens on the MFMA lane
-// axis so that both products chain through registers; the fp32 weights of the
-// pair's state are converted to bf16 into LDS (natural layouts) per workgroup.
+// axis so that both products chain through registers (details at the kernel).
 //
 // GELU and gelu' are evaluated two elements at a time in packed f16 from a
-// polynomial fit of the normal CDF (see gelu_h2 below); the fp32 kernels use
+// polynomial fit of the normal CDF (see gelu_chains below); the fp32 kernels use
 // the exact erf form.
 #include <type_traits>
 
@@ -56,73 +57,102 @@ __device__ __forceinline__ bf16x4 ld_tr(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// Packed-f16 GELU.  With w = clamp(Z/c, -1, 1), u = w^2 and v = 2u - 1,
-//     c*Phi(Z) = c/2 + w P(v),     gelu'(Z) = 1/2 + w Q(v)
-// where P, Q are degree-6 fits in the shifted variable v (small coefficients,
-// so Horner in f16 loses little), c = 3.5.  gelu(Z) = (Z/c) * (c*Phi).  Two
-// elements per instruction and no transcendental; max |error| 3.3e-3 on gelu
-// (relative 5e-4 at large |Z|) and 2.9e-3 on gelu', inside the bf16 rounding
-// of the MFMA operands these values become.  The weights feeding Z are
-// pre-scaled by 1/c so the MFMA delivers Z/c directly.
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+// Packed-f16 GELU.  With c = 3.5, zh = sqrt(2) Z / c, w = clamp(zh, -sqrt(2),
+// sqrt(2)) and v = w^2 - 1 (in [-1, 1]),
+//     c Phi(Z) = c/2 + w P(v) / sqrt(2),     gelu'(Z) = 1/2 + w Q(v) / sqrt(2)
+// where P, Q are degree-6 Lawson (minimax) fits in v, whose small coefficients
+// keep f16 Horner accurate; then zh * c Phi(Z) = sqrt(2) gelu(Z).  Two elements
+// per instruction and no transcendental; max |error| 3.3e-3 on gelu (relative
+// 1e-3 at large |Z|) and 3.0e-3 on gelu'.  The weights that produce Z are
+// staged pre-scaled by sqrt(2)/c, so the MFMA delivers zh; the activation
+// A' = sqrt(2) gelu(Z) is consumed by products whose other operand (or result)
+// carries the compensating 1/sqrt(2).
+typedef _Float16 f16;
+typedef f16 h2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 constexpr float kClampC = 3.5f;
-__device__ __forceinline__ h2 hh(float x) { return h2{(_Float16)x, (_Float16)x}; }
-__device__ __forceinline__ h2 poly_p(h2 v) {
-  h2 p = hh(0.034846943f);
-  p = __builtin_elementwise_fma(p, v, hh(-0.1021939f));
-  p = __builtin_elementwise_fma(p, v, hh(0.186821488f));
-  p = __builtin_elementwise_fma(p, v, hh(-0.358320439f));
-  p = __builtin_elementwise_fma(p, v, hh(0.65378186f));
-  p = __builtin_elementwise_fma(p, v, hh(-1.10760263f));
-  return __builtin_elementwise_fma(p, v, hh(2.44194935f));
-}
-__device__ __forceinline__ h2 poly_q(h2 v) {
-  h2 q = hh(0.0954901068f);
-  q = __builtin_elementwise_fma(q, v, hh(-0.234467175f));
-  q = __builtin_elementwise_fma(q, v, hh(0.296631852f));
-  q = __builtin_elementwise_fma(q, v, hh(-0.388431366f));
-  q = __builtin_elementwise_fma(q, v, hh(0.49006813f));
-  q = __builtin_elementwise_fma(q, v, hh(-0.519321705f));
-  return __builtin_elementwise_fma(q, v, hh(0.763167748f));
-}
-// (z0, z1) = Z/c of two elements -> gelu(Z) of both
-__device__ __forceinline__ void gelu_h2(float z0, float z1, float& a0, float& a1) {
-  h2 w = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(z0, z1));
-  w = __builtin_elementwise_min(__builtin_elementwise_max(w, hh(-1.0f)), hh(1.0f));
-  const h2 v = __builtin_elementwise_fma(w * w, hh(2.0f), hh(-1.0f));
-  const h2 cphi = __builtin_elementwise_fma(w, poly_p(v), hh(0.5f * kClampC));
-  a0 = z0 * (float)cphi.x;
-  a1 = z1 * (float)cphi.y;
-}
-// gelu and gelu' of two elements; gelu' stays packed f16
-__device__ __forceinline__ void gelu2_h2(float z0, float z1, float& a0, float& a1, h2& gp) {
-  h2 w = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(z0, z1));
-  w = __builtin_elementwise_min(__builtin_elementwise_max(w, hh(-1.0f)), hh(1.0f));
-  const h2 v = __builtin_elementwise_fma(w * w, hh(2.0f), hh(-1.0f));
-  const h2 cphi = __builtin_elementwise_fma(w, poly_p(v), hh(0.5f * kClampC));
-  gp = __builtin_elementwise_fma(w, poly_q(v), hh(0.5f));
-  a0 = z0 * (float)cphi.x;
-  a1 = z1 * (float)cphi.y;
+constexpr float kSqrt2 = 1.41421356237f;
+constexpr float kRSqrt2 = 0.70710678119f;
+constexpr float kZScale = kSqrt2 / kClampC;     // applied to W1 (and W3) when staged
+__device__ __forceinline__ h2 hh(float x) { return h2{(f16)x, (f16)x}; }
+__device__ __forceinline__ h2 cvt_h2(float x0, float x1) { return __builtin_convertvector(f2{x0, x1}, h2); }
+// Coefficients of P(v)/sqrt(2) and Q(v)/sqrt(2), highest degree first.
+constexpr float kP[7] = {0.034846943f * kRSqrt2, -0.1021939f * kRSqrt2, 0.186821488f * kRSqrt2,
+                         -0.358320439f * kRSqrt2, 0.65378186f * kRSqrt2, -1.10760263f * kRSqrt2,
+                         2.44194935f * kRSqrt2};
+constexpr float kQ[7] = {0.0954901068f * kRSqrt2, -0.234467175f * kRSqrt2, 0.296631852f * kRSqrt2,
+                         -0.388431366f * kRSqrt2, 0.49006813f * kRSqrt2, -0.519321705f * kRSqrt2,
+                         0.763167748f * kRSqrt2};
+// The Horner chains of NC element pairs are advanced together: a dependent
+// packed-f16 FMA must wait a cycle after its producer, independent ones need
+// not, so interleaving the chains keeps the VALU issuing every cycle.
+//   z[2c], z[2c+1] = zh of pair c  ->  a[c] = sqrt(2) gelu(Z)  (and gp[c] = gelu'(Z))
+template <int NC, bool GRAD>
+__device__ __forceinline__ void gelu_chains(const float* z, h2* a, h2* gp) {
+  h2 zh[NC], w[NC], v[NC], p[NC], q[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) zh[c] = cvt_h2(z[2 * c], z[2 * c + 1]);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) w[c] = __builtin_elementwise_max(zh[c], hh(-kSqrt2));
+#pragma unroll
+  for (int c = 0; c < NC; ++c) w[c] = __builtin_elementwise_min(w[c], hh(kSqrt2));
+#pragma unroll
+  for (int c = 0; c < NC; ++c) v[c] = __builtin_elementwise_fma(w[c], w[c], hh(-1.0f));
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    p[c] = __builtin_elementwise_fma(hh(kP[0]), v[c], hh(kP[1]));
+    if (GRAD) q[c] = __builtin_elementwise_fma(hh(kQ[0]), v[c], hh(kQ[1]));
+  }
+#pragma unroll
+  for (int k = 2; k < 7; ++k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      p[c] = __builtin_elementwise_fma(p[c], v[c], hh(kP[k]));
+      if (GRAD) q[c] = __builtin_elementwise_fma(q[c], v[c], hh(kQ[k]));
+    }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    a[c] = zh[c] * __builtin_elementwise_fma(w[c], p[c], hh(0.5f * kClampC));
+    if (GRAD) gp[c] = __builtin_elementwise_fma(w[c], q[c], hh(0.5f));
+  }
 }
 
-__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ bf16x8 cat44(const bf16x4& x, const bf16x4& y) {
-  bf16x8 r;
+// element-type generic helpers (bf16 or f16 MFMA operands)
+template <typename T> struct Vec;
+template <> struct Vec<bf16> { typedef bf16x8 v8; typedef bf16x4 v4; };
+template <> struct Vec<f16> { typedef f16x8 v8; typedef f16x4 v4; };
+__device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v4 ld_trt(const T* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)((__attribute__((address_space(3))) char*)p));
+  return __builtin_bit_cast(typename Vec<T>::v4, v);
+}
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::v8 ld8t(const T* p) { return *reinterpret_cast<const typename Vec<T>::v8*>(p); }
+template <typename V8, typename V4>
+__device__ __forceinline__ V8 cat44t(const V4& x, const V4& y) {
+  V8 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) { r[i] = x[i]; r[4 + i] = y[i]; }
   return r;
 }
-__device__ __forceinline__ bf16x8 pack8(const f32x4& x, const f32x4& y) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { r[i] = (bf16)x[i]; r[4 + i] = (bf16)y[i]; }
-  return r;
-}
+
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x8 cat44(const bf16x4& x, const bf16x4& y) { return cat44t<bf16x8>(x, y); }
+__device__ __forceinline__ f16x8 cat44(const f16x4& x, const f16x4& y) { return cat44t<f16x8>(x, y); }
 __device__ __forceinline__ bf16x4 pack4(const f32x4& x) {
   bf16x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
   return r;
+}
+__device__ __forceinline__ f16x4 pack4h(const f32x4& x) {
+  const h2 a = cvt_h2(x[0], x[1]), b = cvt_h2(x[2], x[3]);
+  return f16x4{a.x, a.y, b.x, b.y};
 }
 // XOR swizzles of the LDS tiles (column index in bf16 elements).  Row `row`
 // of a [token][channel] tile stores channel c at c ^ kswz(row); row `row` of a
@@ -159,18 +189,24 @@ __device__ __forceinline__ void key_stat(const float* sp, int S, int c, float ep
 }
 
 // ---------------------------------------------------------------------------
-// One tile's hidden activations as kept between pipeline stages: A (bf16, the
-// token order of the token-contracted MFMAs) and gelu'(Z) (bf16, same order).
+// One tile's hidden activations as kept between pipeline stages: A' =
+// sqrt(2) gelu(Z) and gelu'(Z), packed f16, in the token order of the
+// token-contracted MFMAs.
 template <int NHB>
 struct Act {
-  bf16x8 a[NHB];
-  h2 gp[NHB][4];        // gelu'(Z), packed f16 pairs, same token order as a
+  f16x8 a[NHB];
+  h2 gp[NHB][4];
 };
 
-template <int HID, int LOSS, int NWAVE>
-__global__ void __launch_bounds__(NWAVE * 64, (NWAVE == 8 ? 2 : 1))
+// KNORM: keys are instance-normalised (|K_hat| <= sqrt(N), so the key tile and
+// the products it enters use f16); without it the raw keys stay bf16.
+template <int HID, int LOSS, int NWAVE, bool KNORM>
+__global__ void __launch_bounds__(NWAVE * 64, 1)
 k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float* __restrict__ spart, int S_stats,
             float eps, float* __restrict__ part) {
+  typedef typename std::conditional<KNORM, f16, bf16>::type KT;
+  typedef typename Vec<KT>::v8 k8;
+  typedef typename Vec<KT>::v4 k4;
   constexpr int NTHR = NWAVE * 64;
   constexpr int HW = HID / NWAVE;      // hidden units per wave
   constexpr int NHB = HW / 16;         // 16-wide hidden blocks per wave
@@ -179,12 +215,12 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
   constexpr int SCH = D * TT / NTHR;   // channels staged per thread (8 or 4)
   constexpr int SPR = D / SCH;         // staging threads per token row
   constexpr int LW2 = HID + 8;
-  // double-buffered token tiles; A and G' single-buffered (see the pipeline below)
-  __shared__ __attribute__((aligned(16))) bf16 Kr[2][TT * LDK];
+  // double-buffered token tiles; A' and G' single-buffered (see the pipeline below)
+  __shared__ __attribute__((aligned(16))) KT Kr[2][TT * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Vr[2][TT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 Gc[D * LDT];
-  __shared__ __attribute__((aligned(16))) bf16 At[LOSS == LOSS_MSE ? HID * LDT : 8];
-  __shared__ __attribute__((aligned(16))) bf16 W2t[LOSS == LOSS_MSE ? D * LW2 : 8];   // W2^T [c][h]
+  __shared__ __attribute__((aligned(16))) f16 Gc[D * LDT];
+  __shared__ __attribute__((aligned(16))) f16 At[LOSS == LOSS_MSE ? HID * LDT : 8];
+  __shared__ __attribute__((aligned(16))) f16 W2t[LOSS == LOSS_MSE ? D * LW2 : 8];   // W2^T / sqrt(2), [c][h]
   __shared__ float eta_s[2][TT];
 
   const int tid = threadIdx.x;
@@ -200,19 +236,21 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
   const long long end = (long long)(blockIdx.x + 1) * total / G;
   const int p_first = (int)(begin / tpp);
   typedef __attribute__((__vector_size__(SCH * sizeof(__bf16)))) __bf16 stg_t;
+  typedef KT stgk_t __attribute__((ext_vector_type(SCH)));
 
   long long x = begin;
   while (x < end) {
     const int p = (int)(x / tpp);
-    const int bb = p / pb.H, hh = p % pb.H;
+    const int bb = p / pb.H, hh_ = p % pb.H;
     const int tile0 = (int)(x - (long long)p * tpp);
     const long long seg_end = end < (long long)(p + 1) * tpp ? end : (long long)(p + 1) * tpp;
     const int tile1 = (int)(seg_end - (long long)p * tpp);
 
-    // ---- weight fragments of this pair (fp32 state -> bf16 registers / LDS)
-    const float* W1 = W.mat(0, bb, hh);
-    const float* W2 = W.mat(1, bb, hh);
-    bf16x8 w1r[NHB][2], w2r[NHB][2];
+    // ---- weight fragments of this pair (fp32 state -> registers / LDS)
+    const float* W1 = W.mat(0, bb, hh_);
+    const float* W2 = W.mat(1, bb, hh_);
+    k8 w1r[NHB][2];
+    f16x8 w2r[NHB][2];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
@@ -221,20 +259,20 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         const float* p1 = W1 + (32 * ks + 8 * g) * HID + hcol;
         const float4* p2 = reinterpret_cast<const float4*>(W2 + hcol * D + 32 * ks + 8 * g);
         const float4 a = p2[0], b = p2[1];
-        w2r[hb][ks] = bf16x8{(bf16)a.x, (bf16)a.y, (bf16)a.z, (bf16)a.w, (bf16)b.x, (bf16)b.y, (bf16)b.z, (bf16)b.w};
+        w2r[hb][ks] = f16x8{(f16)a.x, (f16)a.y, (f16)a.z, (f16)a.w, (f16)b.x, (f16)b.y, (f16)b.z, (f16)b.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w1r[hb][ks][j] = (bf16)(p1[j * HID] * (1.0f / kClampC));   // W1[c][h] / c
+        for (int j = 0; j < 8; ++j) w1r[hb][ks][j] = (KT)(p1[j * HID] * kZScale);
         // keep the fragment loads sequential: issuing them all at once would
         // hold every 64-bit address live at the same time
         __builtin_amdgcn_sched_barrier(0);
       }
     __syncthreads();   // the previous segment may still read W2t / the tiles
     if (LOSS == LOSS_MSE)
-      for (int e = tid; e < HID * D; e += NTHR) W2t[(e % D) * LW2 + e / D] = (bf16)W2[e];
+      for (int e = tid; e < HID * D; e += NTHR) W2t[(e % D) * LW2 + e / D] = (f16)(W2[e] * kRSqrt2);
     float mu[SCH], rs[SCH];
 #pragma unroll
     for (int j = 0; j < SCH; ++j) { mu[j] = 0.f; rs[j] = 1.f; }
-    if (spart) {
+    if (KNORM) {
       const float* sp = spart + (long long)p * S_stats * 3 * D;
 #pragma unroll
       for (int j = 0; j < SCH; ++j) key_stat(sp, S_stats, sc + j, eps, mu[j], rs[j]);
@@ -262,17 +300,18 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     auto stage = [&](int tile, int buf) {
       const int n = tile * TT + st;
       const bool live = n < nt;
-      stg_t kh, vv;
+      stgk_t kh;
+      stg_t vv;
 #pragma unroll
       for (int j = 0; j < SCH; ++j) {
-        kh[j] = live ? (bf16)(((float)kreg[j] - mu[j]) * rs[j]) : (bf16)0.f;
+        kh[j] = live ? (KT)(((float)kreg[j] - mu[j]) * rs[j]) : (KT)0.f;
         vv[j] = live ? vreg[j] : (bf16)0.f;
       }
-      *reinterpret_cast<stg_t*>(&Kr[buf][st * LDK + (sc ^ kswz(st))]) = kh;
+      *reinterpret_cast<stgk_t*>(&Kr[buf][st * LDK + (sc ^ kswz(st))]) = kh;
       *reinterpret_cast<stg_t*>(&Vr[buf][st * LDK + (sc ^ kswz(st))]) = vv;
       if (sc == 0) eta_s[buf][st] = live ? (ep ? ep[n] : 1.0f) : 0.0f;
     };
-    // Z = K_hat W1 for this wave's hidden slice
+    // Z' = K_hat W1 sqrt(2)/c for this wave's hidden slice
     auto gemm1 = [&](int buf, f32x4 (&z)[2][NHB]) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
@@ -282,34 +321,30 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          const bf16x8 a = ld8(&Kr[buf][(16 * tb + r) * LDK + ((32 * ks + 8 * g) ^ kswz(r))]);
+          const k8 a = ld8t(&Kr[buf][(16 * tb + r) * LDK + ((32 * ks + 8 * g) ^ kswz(r))]);
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) z[tb][hb] = mfma16(a, w1r[hb][ks], z[tb][hb]);
         }
     };
-    // A = gelu(Z), gp = gelu'(Z), packed in the (tb 0 | tb 1) token order
+    // A' = sqrt(2) gelu(Z), gp = gelu'(Z), packed in the (tb 0 | tb 1) token order
     auto activate = [&](const f32x4 (&z)[2][NHB], Act<NHB>& act) {
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            float a0, a1;
-            gelu2_h2(z[tb][hb][i], z[tb][hb][i + 1], a0, a1, act.gp[hb][2 * tb + i / 2]);
-            act.a[hb][4 * tb + i] = (bf16)a0;
-            act.a[hb][4 * tb + i + 1] = (bf16)a1;
-          }
+      for (int hb = 0; hb < NHB; ++hb) {
+        const float zz[8] = {z[0][hb][0], z[0][hb][1], z[0][hb][2], z[0][hb][3],
+                             z[1][hb][0], z[1][hb][1], z[1][hb][2], z[1][hb][3]};
+        h2 av[4];
+        gelu_chains<4, true>(zz, av, act.gp[hb]);
+        act.a[hb] = f16x8{av[0].x, av[0].y, av[1].x, av[1].y, av[2].x, av[2].y, av[3].x, av[3].y};
+      }
     };
     auto write_at = [&](const Act<NHB>& act) {
       if (LOSS == LOSS_MSE) {
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb)
-        {
-          bf16* row = &At[(h0 + 16 * hb + r) * LDT];
-          const bf16x8& v = act.a[hb];
-          *reinterpret_cast<bf16x4*>(row + ((8 * g) ^ tswz(r))) = bf16x4{v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<bf16x4*>(row + ((8 * g + 4) ^ tswz(r))) = bf16x4{v[4], v[5], v[6], v[7]};
+        for (int hb = 0; hb < NHB; ++hb) {
+          f16* row = &At[(h0 + 16 * hb + r) * LDT];
+          const f16x8& v = act.a[hb];
+          *reinterpret_cast<f16x4*>(row + ((8 * g) ^ tswz(r))) = f16x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f16x4*>(row + ((8 * g + 4) ^ tswz(r))) = f16x4{v[4], v[5], v[6], v[7]};
         }
       }
     };
@@ -321,18 +356,18 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         const int tb2 = blk >> 2, cb2 = blk & 3;
         // V[t = 16 tb2 + 4 g + i][c = 16 cb2 + r]
         const int vrow = 16 * tb2 + 4 * g + (r >> 2);
-        const bf16x4 vq = ld_tr(&Vr[buf][vrow * LDK + ((16 * cb2 + 4 * (r & 3)) ^ kswz(vrow))]);
+        const bf16x4 vq = ld_trt(&Vr[buf][vrow * LDK + ((16 * cb2 + 4 * (r & 3)) ^ kswz(vrow))]);
         f32x4 gv;
         if (LOSS == LOSS_MSE) {
           // two independent accumulation chains halve the MFMA latency chain
           f32x4 v0 = f32x4{0, 0, 0, 0}, v1 = f32x4{0, 0, 0, 0};
 #pragma unroll
           for (int ks = 0; ks < NKH; ++ks) {
-            // A[t = 16 tb2 + r][h = 32 ks + 8 g + j]
+            // A'[t = 16 tb2 + r][h = 32 ks + 8 g + j]
             const int ar = 32 * ks + 8 * g + (r >> 2);
-            const bf16x4 lo = ld_tr(&At[ar * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar))]);
-            const bf16x4 hi = ld_tr(&At[(ar + 4) * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar + 4))]);
-            const bf16x8 bw = ld8(&W2t[(16 * cb2 + r) * LW2 + 32 * ks + 8 * g]);
+            const f16x4 lo = ld_trt(&At[ar * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar))]);
+            const f16x4 hi = ld_trt(&At[(ar + 4) * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar + 4))]);
+            const f16x8 bw = ld8t(&W2t[(16 * cb2 + r) * LW2 + 32 * ks + 8 * g]);
             if (ks & 1) v1 = mfma16(cat44(lo, hi), bw, v1);
             else v0 = mfma16(cat44(lo, hi), bw, v0);
           }
@@ -342,16 +377,16 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
           for (int i = 0; i < 4; ++i) gv[i] = -eta_s[buf][16 * tb2 + 4 * g + i] * (float)vq[i];
         }
-        *reinterpret_cast<bf16x4*>(&Gc[(16 * cb2 + r) * LDT + ((8 * g + 4 * tb2) ^ tswz(r))]) = pack4(gv);
+        *reinterpret_cast<f16x4*>(&Gc[(16 * cb2 + r) * LDT + ((8 * g + 4 * tb2) ^ tswz(r))]) = pack4h(gv);
       }
     };
-    // dW2 += A^T G';  dA = G' W2^T;  dZ = dA gelu'(Z);  dW1 += K_hat^T dZ
+    // dW2 += A'^T G';  dA = G' W2^T;  dZ = dA gelu'(Z);  dW1 += K_hat^T dZ
     auto backward = [&](int buf, const Act<NHB>& act) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const bf16* grow = &Gc[(16 * cb + r) * LDT];
-        const bf16x8 b = cat44(*reinterpret_cast<const bf16x4*>(grow + ((8 * g) ^ tswz(r))),
-                               *reinterpret_cast<const bf16x4*>(grow + ((8 * g + 4) ^ tswz(r))));
+        const f16* grow = &Gc[(16 * cb + r) * LDT];
+        const f16x8 b = cat44(*reinterpret_cast<const f16x4*>(grow + ((8 * g) ^ tswz(r))),
+                              *reinterpret_cast<const f16x4*>(grow + ((8 * g + 4) ^ tswz(r))));
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) acc2[hb][cb] = mfma16(act.a[hb], b, acc2[hb][cb]);
       }
@@ -366,29 +401,30 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         for (int tb = 0; tb < 2; ++tb) {
           // G'[t = 16 tb + r][c = 32 ks + 8 g + j]
           const int gr = 32 * ks + 8 * g + (r >> 2);
-          const bf16x4 lo = ld_tr(&Gc[gr * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr))]);
-          const bf16x4 hi = ld_tr(&Gc[(gr + 4) * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr + 4))]);
-          const bf16x8 a = cat44(lo, hi);
+          const f16x4 lo = ld_trt(&Gc[gr * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr))]);
+          const f16x4 hi = ld_trt(&Gc[(gr + 4) * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr + 4))]);
+          const f16x8 a = cat44(lo, hi);
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) da[tb][hb] = mfma16(a, w2r[hb][ks], da[tb][hb]);
         }
-      bf16x8 dzp[NHB];
+      k8 dzp[NHB];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const h2 gq = act.gp[hb][2 * tb + i / 2];
-            dzp[hb][4 * tb + i] = (bf16)(da[tb][hb][i] * (float)((i & 1) ? gq.y : gq.x));
+          for (int i = 0; i < 4; i += 2) {
+            const h2 dz = cvt_h2(da[tb][hb][i], da[tb][hb][i + 1]) * act.gp[hb][2 * tb + i / 2];
+            dzp[hb][4 * tb + i] = (KT)(float)dz.x;
+            dzp[hb][4 * tb + i + 1] = (KT)(float)dz.y;
           }
       // K_hat[t = tau(g, j)][c = 16 cb + r]
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const int kr0 = 4 * g + (r >> 2);
-        const bf16x4 lo = ld_tr(&Kr[buf][kr0 * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0))]);
-        const bf16x4 hi = ld_tr(&Kr[buf][(kr0 + 16) * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0 + 16))]);
-        const bf16x8 a = cat44(lo, hi);
+        const k4 lo = ld_trt(&Kr[buf][kr0 * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0))]);
+        const k4 hi = ld_trt(&Kr[buf][(kr0 + 16) * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0 + 16))]);
+        const k8 a = cat44(lo, hi);
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) acc1[cb][hb] = mfma16(a, dzp[hb], acc1[cb][hb]);
       }
@@ -433,7 +469,9 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     }
 
     // ---- partial of this (workgroup, pair) segment: [dW1 (d x h) | dW2 (h x d)]
+    // (acc2 holds A'^T G' = sqrt(2) A^T G')
     float* out = part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID);
+    const float scale2 = scale * kRSqrt2;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -447,7 +485,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          out[(long long)D * HID + (h0 + 16 * hb + 4 * g + i) * D + 16 * cb + r] = scale * acc2[hb][cb][i];
+          out[(long long)D * HID + (h0 + 16 * hb + 4 * g + i) * D + 16 * cb + r] = scale2 * acc2[hb][cb][i];
     x = seg_end;
   }
 }
@@ -471,38 +509,6 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 // Workgroup -> range mapping is XCD-aware: consecutive ranges (which share a
 // pair's weights) are given to workgroups of the same XCD.
 constexpr int QW = 16;                  // waves per workgroup
-constexpr float kSqrt2 = 1.41421356237f;
-constexpr float kRSqrt2 = 0.70710678119f;
-
-__device__ __forceinline__ h2 poly_p_s(h2 v) {       // P(v) / sqrt(2)
-  h2 p = hh(0.034846943f * kRSqrt2);
-  p = __builtin_elementwise_fma(p, v, hh(-0.1021939f * kRSqrt2));
-  p = __builtin_elementwise_fma(p, v, hh(0.186821488f * kRSqrt2));
-  p = __builtin_elementwise_fma(p, v, hh(-0.358320439f * kRSqrt2));
-  p = __builtin_elementwise_fma(p, v, hh(0.65378186f * kRSqrt2));
-  p = __builtin_elementwise_fma(p, v, hh(-1.10760263f * kRSqrt2));
-  return __builtin_elementwise_fma(p, v, hh(2.44194935f * kRSqrt2));
-}
-typedef float f2 __attribute__((ext_vector_type(2)));
-// (z0, z1) = sqrt(2) Z / c of two elements -> sqrt(2) gelu(Z) of both, packed f16
-__device__ __forceinline__ h2 gelu_s2(float z0, float z1) {
-  const h2 zh = __builtin_convertvector(f2{z0, z1}, h2);
-  const h2 w = __builtin_elementwise_min(__builtin_elementwise_max(zh, hh(-kSqrt2)), hh(kSqrt2));
-  const h2 v = __builtin_elementwise_fma(w, w, hh(-1.0f));
-  const h2 cphi = __builtin_elementwise_fma(w, poly_p_s(v), hh(0.5f * kClampC));
-  return zh * cphi;
-}
-typedef _Float16 f16;
-typedef f16 f16x8 __attribute__((ext_vector_type(8)));
-typedef f16 f16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f16x4 ld_tr_h(const f16* p) {
-  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)((__attribute__((address_space(3))) char*)p));
-  return __builtin_bit_cast(f16x4, v);
-}
-
 template <int HID>
 __global__ void __launch_bounds__(QW * 64, 1)
 k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long state_stride, int chunk, int span) {
@@ -540,9 +546,8 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
       const float4 b = *reinterpret_cast<const float4*>(W2 + e);
       const int c1 = e / HID, h1 = e % HID;         // W1 [c][h]
       const int h2_ = e / D, c2 = e % D;             // W2 [h][c]
-      constexpr float s1 = kSqrt2 / kClampC;
       *reinterpret_cast<bf16x4*>(&w1s[c1 * L1 + h1]) =
-          bf16x4{(bf16)(a.x * s1), (bf16)(a.y * s1), (bf16)(a.z * s1), (bf16)(a.w * s1)};
+          bf16x4{(bf16)(a.x * kZScale), (bf16)(a.y * kZScale), (bf16)(a.z * kZScale), (bf16)(a.w * kZScale)};
       *reinterpret_cast<f16x4*>(&w2s[h2_ * L2 + c2]) =
           f16x4{(f16)(b.x * kRSqrt2), (f16)(b.y * kRSqrt2), (f16)(b.z * kRSqrt2), (f16)(b.w * kRSqrt2)};
     }
@@ -592,18 +597,20 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
         f16x8 ab[NTB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-          const h2 x0 = gelu_s2(z[0][tb][0], z[0][tb][1]), x1 = gelu_s2(z[0][tb][2], z[0][tb][3]);
-          const h2 x2 = gelu_s2(z[1][tb][0], z[1][tb][1]), x3 = gelu_s2(z[1][tb][2], z[1][tb][3]);
-          ab[tb] = f16x8{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+          const float zz[8] = {z[0][tb][0], z[0][tb][1], z[0][tb][2], z[0][tb][3],
+                               z[1][tb][0], z[1][tb][1], z[1][tb][2], z[1][tb][3]};
+          h2 x[4];
+          gelu_chains<4, false>(zz, x, nullptr);
+          ab[tb] = f16x8{x[0].x, x[0].y, x[1].x, x[1].y, x[2].x, x[2].y, x[3].x, x[3].y};
         }
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           // W2^T operand: W2[h = 32 hc + tau(g, j)][c = 16 cb + r]
-          const f16x4 lo = ld_tr_h(&w2s[(32 * hc + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
-          const f16x4 hi = ld_tr_h(&w2s[(32 * hc + 16 + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
+          const f16x4 lo = ld_trt(&w2s[(32 * hc + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
+          const f16x4 hi = ld_trt(&w2s[(32 * hc + 16 + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
           const f16x8 a = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-          for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = mfma16h(a, ab[tb], o[cb][tb]);
+          for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = mfma16(a, ab[tb], o[cb][tb]);
         }
       }
 #pragma unroll
@@ -639,12 +646,22 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
 template <int HID, int NWAVE>
 void launch_grad_h(const Problem& pb, const WRef& W, int t0, int nt, int G, int J, float scale,
                    const float* spart, int S_stats, float eps, float* part, hipStream_t st) {
-  if (pb.loss == LOSS_MSE)
-    hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, NWAVE>), dim3(G), dim3(NWAVE * 64), 0, st, pb, W, t0, nt, J,
-                       scale, spart, S_stats, eps, part);
-  else
-    hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, NWAVE>), dim3(G), dim3(NWAVE * 64), 0, st, pb, W, t0, nt, J,
-                       scale, spart, S_stats, eps, part);
+  const dim3 grid(G), block(NWAVE * 64);
+  if (pb.loss == LOSS_MSE) {
+    if (spart)
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, NWAVE, true>), grid, block, 0, st, pb, W, t0, nt, J, scale,
+                         spart, S_stats, eps, part);
+    else
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, NWAVE, false>), grid, block, 0, st, pb, W, t0, nt, J, scale,
+                         spart, S_stats, eps, part);
+  } else {
+    if (spart)
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, NWAVE, true>), grid, block, 0, st, pb, W, t0, nt, J, scale,
+                         spart, S_stats, eps, part);
+    else
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, NWAVE, false>), grid, block, 0, st, pb, W, t0, nt, J, scale,
+                         spart, S_stats, eps, part);
+  }
 }
 
 }  // namespace

@@ -211,3 +211,27 @@ def test_generic_and_fast_paths_agree():
     Ob, Wb, pb = run_gpu(w, dev_in, flags=GENERIC)
     assert pb == "generic"
     assert rel_err(Oa.float().cpu().numpy(), Ob.float().cpu().numpy()) <= 1e-2
+
+
+def test_f16_range_of_the_mlp_fast_path():
+    """The GELU-MLP MFMA kernels carry the loss gradient in f16: values past its
+    range are reported as non-finite (TTT_FLAG_CHECK_FINITE), and the generic
+    fp32 kernels (TTT_FLAG_FORCE_GENERIC) still compute the layer."""
+    from linear_complexity_attention_amd import ttt
+
+    w = Workload("range", B=1, H=2, N=100, d=64, hidden=64, seed=47)
+    dev_in, exact = device_inputs(w)
+    tq, tk, tv, tW, tet = dev_in
+    big = (tv.float() * 1.0e5).to(torch.bfloat16)
+    fast = ttt.TTTLayer(1, 2, 100, 64, 64, dtype="bf16", flags=ttt.TTT_FLAG_CHECK_FINITE)
+    assert fast.path_name("mse", "mlp_gelu", 0) == "mfma"
+    with pytest.raises(ttt.TTTError) as ei:
+        fast.forward(tq, tk, big, tW)
+    assert ei.value.status == ttt.TTT_ERR_NONFINITE
+    slow = ttt.TTTLayer(1, 2, 100, 64, 64, dtype="bf16",
+                        flags=ttt.TTT_FLAG_CHECK_FINITE | ttt.TTT_FLAG_FORCE_GENERIC)
+    O = slow.forward(tq, tk, big, tW)
+    torch.cuda.synchronize()
+    O_ref, _ = orc.oracle_forward(exact["q"], exact["k"], big.double().cpu().numpy(), exact["W0"],
+                                  eta_scale=1.0, loss="mse", inner="mlp_gelu", chunk=0, key_norm=True, eps=1e-5)
+    assert rel_err(O.float().cpu().numpy(), O_ref) <= TOL["bf16"]
