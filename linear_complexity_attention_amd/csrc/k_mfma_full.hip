@@ -154,17 +154,17 @@ __device__ __forceinline__ f16x4 pack4h(const f32x4& x) {
   const h2 a = cvt_h2(x[0], x[1]), b = cvt_h2(x[2], x[3]);
   return f16x4{a.x, a.y, b.x, b.y};
 }
-// XOR swizzles of the LDS tiles (column index in bf16 elements).  Row `row`
+// XOR swizzles of the LDS tiles (column index in 2-byte elements).  Row `row`
 // of a [token][channel] tile stores channel c at c ^ kswz(row); row `row` of a
-// [unit][token] tile stores token column t at t ^ tswz(row).  They make every
-// access pattern of the gradient kernel conflict-free on the 64 LDS banks:
-// 16-byte row reads and staging writes, and the transposing 8-byte reads
-// whose 32 lanes span rows {0..7} (token tiles) or {0..3, 8..11} (unit tiles).
-// kswz moves whole 8-element pieces, so 16-byte accesses stay contiguous;
-// tswz also moves 4-element halves, so 16-byte accesses to [unit][token]
-// tiles are split into two 8-byte ones.
+// [unit][token] tile stores token column t at t ^ tswz(row).  Both were chosen
+// by measuring SQ_LDS_BANK_CONFLICT on every access pattern of the gradient
+// kernel (row reads and writes of 8 or 16 bytes per lane, and the transposing
+// reads); with them none of those patterns has a bank conflict.  kswz moves
+// whole 8-element pieces, so 16-byte accesses stay contiguous; tswz also moves
+// 4-element halves, so 16-byte accesses to [unit][token] tiles are split into
+// two 8-byte ones.
 __device__ __forceinline__ int kswz(int row) { return ((row >> 3) & 1) * 8 + ((row >> 1) & 1) * 16 + ((row >> 2) & 1) * 32; }
-__device__ __forceinline__ int tswz(int row) { return ((row >> 3) & 1) * 4 + (row & 1) * 8 + ((row >> 2) & 1) * 16; }
+__device__ __forceinline__ int tswz(int row) { return ((row >> 3) & 1) * 4 + ((row >> 1) & 1) * 8 + ((row >> 2) & 1) * 16; }
 
 // storage column of token t inside a 32-token [unit][token] row: the 8 tokens
 // of MFMA lane group g (4g..4g+3 and 16+4g..16+4g+3) are contiguous at 8g.
