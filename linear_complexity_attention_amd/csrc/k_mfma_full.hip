@@ -189,45 +189,47 @@ __device__ __forceinline__ void key_stat(const float* sp, int S, int c, float ep
 }
 
 // ---------------------------------------------------------------------------
-// One tile's hidden activations as kept between pipeline stages: A' =
-// sqrt(2) gelu(Z) and gelu'(Z), packed f16, in the token order of the
-// token-contracted MFMAs.
-template <int NHB>
-struct Act {
-  f16x8 a[NHB];
-  h2 gp[NHB][4];
-};
-
-// KNORM: keys are instance-normalised (|K_hat| <= sqrt(N), so the key tile and
-// the products it enters use f16); without it the raw keys stay bf16.
-template <int HID, int LOSS, int NWAVE, bool KNORM>
-__global__ void __launch_bounds__(NWAVE * 64, 1)
+// Fused forward/backward of one update batch, producer/consumer form.
+//
+// A workgroup has 8 waves: 4 producers and 4 consumers; producer q and
+// consumer q own the same quarter of the hidden units (HP = HID/4) and share
+// SIMD q, so the producer's VALU-heavy GELU and the consumer's MFMA-heavy
+// weight-gradient products overlap on that SIMD.  Tiles of 32 tokens flow
+// through a three-stage pipeline, one barrier per stage:
+//   phase k, producers: stage K_hat, V, eta of tile k+1 (prefetched a phase
+//            earlier); Z' = K_hat W1 sqrt(2)/c and the packed GELU of tile k
+//            -> A' (At[k%3]) and gelu' (Gp[k%3]); V_hat and G' of tile k-1
+//            (G' -> Gc[(k-1)%2]);
+//   phase k, consumers: backward of tile k-2: dW2 += A'^T G', dA = G' W2^T,
+//            dZ = dA gelu'(Z), dW1 += K_hat^T dZ.
+// Buffers: K tiles x4, V tiles x3, A' x3, gelu' x3, G' x2.
+template <int HID, int LOSS, bool KNORM>
+__global__ void __launch_bounds__(512, HID == 64 ? 2 : 1)
 k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float* __restrict__ spart, int S_stats,
             float eps, float* __restrict__ part) {
   typedef typename std::conditional<KNORM, f16, bf16>::type KT;
   typedef typename Vec<KT>::v8 k8;
   typedef typename Vec<KT>::v4 k4;
-  constexpr int NTHR = NWAVE * 64;
-  constexpr int HW = HID / NWAVE;      // hidden units per wave
-  constexpr int NHB = HW / 16;         // 16-wide hidden blocks per wave
+  constexpr int HP = HID / 4;          // hidden units per producer / consumer
+  constexpr int NHB = HP / 16;         // 16-wide hidden blocks per wave
   constexpr int NKH = HID / 32;        // k-steps over the hidden width
-  constexpr int NB2 = 8 / NWAVE;       // V_hat / G' output blocks (of 2 x 4) per wave
-  constexpr int SCH = D * TT / NTHR;   // channels staged per thread (8 or 4)
-  constexpr int SPR = D / SCH;         // staging threads per token row
-  constexpr int LW2 = HID + 8;
-  // double-buffered token tiles; A' and G' single-buffered (see the pipeline below)
-  __shared__ __attribute__((aligned(16))) KT Kr[2][TT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 Vr[2][TT * LDK];
-  __shared__ __attribute__((aligned(16))) f16 Gc[D * LDT];
-  __shared__ __attribute__((aligned(16))) f16 At[LOSS == LOSS_MSE ? HID * LDT : 8];
-  __shared__ __attribute__((aligned(16))) f16 W2t[LOSS == LOSS_MSE ? D * LW2 : 8];   // W2^T / sqrt(2), [c][h]
-  __shared__ float eta_s[2][TT];
+  constexpr int SCH = 8;               // channels staged per producer thread
+  constexpr int NK = 4, NV = 3, NA = 3, NG = 2;
+  __shared__ __attribute__((aligned(16))) KT Kr[NK][TT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Vr[NV][TT * LDK];
+  __shared__ __attribute__((aligned(16))) f16 At[NA][HID * LDT];
+  __shared__ __attribute__((aligned(16))) h2 Gp[NA][4 * NHB * 64 * 4];
+  __shared__ __attribute__((aligned(16))) f16 Gc[NG][D * LDT];
+  __shared__ float eta_s[NV][TT];
+  __shared__ float kst[KNORM ? D : 1][2];   // key mean, rstd per channel
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, provably uniform
+  const int q = w & 3;
+  const bool producer = w < 4;
   const int r = lane & 15, g = lane >> 4;
-  const int h0 = w * HW;
-  const int st = tid / SPR, sc = (tid % SPR) * SCH;   // staging: token row, first channel
+  const int h0 = q * HP;
   const int P = pb.B * pb.H;
   const int tpp = (nt + TT - 1) / TT;
   const long long total = (long long)P * tpp;
@@ -235,8 +237,6 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
   const long long begin = (long long)blockIdx.x * total / G;
   const long long end = (long long)(blockIdx.x + 1) * total / G;
   const int p_first = (int)(begin / tpp);
-  typedef __attribute__((__vector_size__(SCH * sizeof(__bf16)))) __bf16 stg_t;
-  typedef KT stgk_t __attribute__((ext_vector_type(SCH)));
 
   long long x = begin;
   while (x < end) {
@@ -244,248 +244,248 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     const int bb = p / pb.H, hh_ = p % pb.H;
     const int tile0 = (int)(x - (long long)p * tpp);
     const long long seg_end = end < (long long)(p + 1) * tpp ? end : (long long)(p + 1) * tpp;
-    const int tile1 = (int)(seg_end - (long long)p * tpp);
-
-    // ---- weight fragments of this pair (fp32 state -> registers / LDS)
+    const int n = (int)(seg_end - x);                 // tiles of this segment
     const float* W1 = W.mat(0, bb, hh_);
     const float* W2 = W.mat(1, bb, hh_);
-    k8 w1r[NHB][2];
-    f16x8 w2r[NHB][2];
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int hcol = h0 + 16 * hb + r;
-        const float* p1 = W1 + (32 * ks + 8 * g) * HID + hcol;
-        const float4* p2 = reinterpret_cast<const float4*>(W2 + hcol * D + 32 * ks + 8 * g);
-        const float4 a = p2[0], b = p2[1];
-        w2r[hb][ks] = f16x8{(f16)a.x, (f16)a.y, (f16)a.z, (f16)a.w, (f16)b.x, (f16)b.y, (f16)b.z, (f16)b.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w1r[hb][ks][j] = (KT)(p1[j * HID] * kZScale);
-        // keep the fragment loads sequential: issuing them all at once would
-        // hold every 64-bit address live at the same time
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    __syncthreads();   // the previous segment may still read W2t / the tiles
-    if (LOSS == LOSS_MSE)
-      for (int e = tid; e < HID * D; e += NTHR) W2t[(e % D) * LW2 + e / D] = (f16)(W2[e] * kRSqrt2);
-    float mu[SCH], rs[SCH];
-#pragma unroll
-    for (int j = 0; j < SCH; ++j) { mu[j] = 0.f; rs[j] = 1.f; }
-    if (KNORM) {
-      const float* sp = spart + (long long)p * S_stats * 3 * D;
-#pragma unroll
-      for (int j = 0; j < SCH; ++j) key_stat(sp, S_stats, sc + j, eps, mu[j], rs[j]);
-    }
-    const bf16* kp = (const bf16*)pb.k + ((long long)p * pb.N + t0) * D;
-    const bf16* vp = (const bf16*)pb.v + ((long long)p * pb.N + t0) * D;
-    const float* ep = pb.eta_tok ? pb.eta_tok + (long long)p * pb.N + t0 : nullptr;
 
-    f32x4 acc1[4][NHB], acc2[NHB][4];
+    if (producer) {
+      // ---------------- producer ----------------
+      const int st = tid / (D / SCH), sc = (tid % (D / SCH)) * SCH;   // staging: token row, first channel
+      k8 w1r[NHB][2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-      for (int b = 0; b < NHB; ++b) { acc1[a][b] = f32x4{0, 0, 0, 0}; acc2[b][a] = f32x4{0, 0, 0, 0}; }
-
-    // ---------------- pipeline stages ----------------
-    stg_t kreg = {}, vreg = {};
-    auto prefetch = [&](int tile) {
-      const int n = tile * TT + st;
-      if (tile < tile1 && n < nt) {
-        kreg = *reinterpret_cast<const stg_t*>(kp + (long long)n * D + sc);
-        vreg = *reinterpret_cast<const stg_t*>(vp + (long long)n * D + sc);
-      }
-    };
-    // normalised K, V ([token][channel]) and eta of `tile` into buffer buf
-    auto stage = [&](int tile, int buf) {
-      const int n = tile * TT + st;
-      const bool live = n < nt;
-      stgk_t kh;
-      stg_t vv;
+        for (int ks = 0; ks < 2; ++ks) {
+          const float* p1 = W1 + (32 * ks + 8 * g) * HID + h0 + 16 * hb + r;
 #pragma unroll
-      for (int j = 0; j < SCH; ++j) {
-        kh[j] = live ? (KT)(((float)kreg[j] - mu[j]) * rs[j]) : (KT)0.f;
-        vv[j] = live ? vreg[j] : (bf16)0.f;
-      }
-      *reinterpret_cast<stgk_t*>(&Kr[buf][st * LDK + (sc ^ kswz(st))]) = kh;
-      *reinterpret_cast<stg_t*>(&Vr[buf][st * LDK + (sc ^ kswz(st))]) = vv;
-      if (sc == 0) eta_s[buf][st] = live ? (ep ? ep[n] : 1.0f) : 0.0f;
-    };
-    // Z' = K_hat W1 sqrt(2)/c for this wave's hidden slice
-    auto gemm1 = [&](int buf, f32x4 (&z)[2][NHB]) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) z[tb][hb] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const k8 a = ld8t(&Kr[buf][(16 * tb + r) * LDK + ((32 * ks + 8 * g) ^ kswz(r))]);
-#pragma unroll
-          for (int hb = 0; hb < NHB; ++hb) z[tb][hb] = mfma16(a, w1r[hb][ks], z[tb][hb]);
+          for (int j = 0; j < 8; ++j) w1r[hb][ks][j] = (KT)(p1[j * HID] * kZScale);
+          __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    // A' = sqrt(2) gelu(Z), gp = gelu'(Z), packed in the (tb 0 | tb 1) token order
-    auto activate = [&](const f32x4 (&z)[2][NHB], Act<NHB>& act) {
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        const float zz[8] = {z[0][hb][0], z[0][hb][1], z[0][hb][2], z[0][hb][3],
-                             z[1][hb][0], z[1][hb][1], z[1][hb][2], z[1][hb][3]};
-        h2 av[4];
-        gelu_chains<4, true>(zz, av, act.gp[hb]);
-        act.a[hb] = f16x8{av[0].x, av[0].y, av[1].x, av[1].y, av[2].x, av[2].y, av[3].x, av[3].y};
-      }
-    };
-    auto write_at = [&](const Act<NHB>& act) {
+      // W2 / sqrt(2) as the B operand of V_hat = A' W2: column block q (16 channels)
+      f16x8 w2g[LOSS == LOSS_MSE ? NKH : 1];
       if (LOSS == LOSS_MSE) {
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) {
-          f16* row = &At[(h0 + 16 * hb + r) * LDT];
-          const f16x8& v = act.a[hb];
-          *reinterpret_cast<f16x4*>(row + ((8 * g) ^ tswz(r))) = f16x4{v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f16x4*>(row + ((8 * g + 4) ^ tswz(r))) = f16x4{v[4], v[5], v[6], v[7]};
+        for (int ks = 0; ks < NKH; ++ks) {
+          const float* p2 = W2 + (32 * ks + 8 * g) * D + 16 * q + r;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w2g[ks][j] = (f16)(p2[j * D] * kRSqrt2);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    };
-    // G' of the wave's (token block, channel block) pairs -> Gc
-    auto gprime = [&](int buf) {
+      // key statistics of the thread's 8 channels, parked in LDS to keep them
+      // out of the registers.  Every thread writes the entries it reads (the 32
+      // threads of a channel write identical values), so no barrier is needed.
+      if (KNORM) {
+        const float* sp = spart + (long long)p * S_stats * 3 * D;
+        float mu[SCH], rs[SCH];
 #pragma unroll
-      for (int b2 = 0; b2 < NB2; ++b2) {
-        const int blk = w * NB2 + b2;
-        const int tb2 = blk >> 2, cb2 = blk & 3;
-        // V[t = 16 tb2 + 4 g + i][c = 16 cb2 + r]
-        const int vrow = 16 * tb2 + 4 * g + (r >> 2);
-        const bf16x4 vq = ld_trt(&Vr[buf][vrow * LDK + ((16 * cb2 + 4 * (r & 3)) ^ kswz(vrow))]);
-        f32x4 gv;
-        if (LOSS == LOSS_MSE) {
-          // two independent accumulation chains halve the MFMA latency chain
-          f32x4 v0 = f32x4{0, 0, 0, 0}, v1 = f32x4{0, 0, 0, 0};
+        for (int j = 0; j < SCH; ++j) key_stat(sp, S_stats, sc + j, eps, mu[j], rs[j]);
 #pragma unroll
-          for (int ks = 0; ks < NKH; ++ks) {
-            // A'[t = 16 tb2 + r][h = 32 ks + 8 g + j]
-            const int ar = 32 * ks + 8 * g + (r >> 2);
-            const f16x4 lo = ld_trt(&At[ar * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar))]);
-            const f16x4 hi = ld_trt(&At[(ar + 4) * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar + 4))]);
-            const f16x8 bw = ld8t(&W2t[(16 * cb2 + r) * LW2 + 32 * ks + 8 * g]);
-            if (ks & 1) v1 = mfma16(cat44(lo, hi), bw, v1);
-            else v0 = mfma16(cat44(lo, hi), bw, v0);
+        for (int j = 0; j < SCH; ++j) { kst[sc + j][0] = mu[j]; kst[sc + j][1] = rs[j]; }
+      }
+      const bf16* kp = (const bf16*)pb.k + ((long long)p * pb.N + t0) * D;
+      const bf16* vp = (const bf16*)pb.v + ((long long)p * pb.N + t0) * D;
+      const float* ep = pb.eta_tok ? pb.eta_tok + (long long)p * pb.N + t0 : nullptr;
+      bf16x8 kreg = {}, vreg = {};
+      auto prefetch = [&](int i) {              // segment-relative tile i
+        const int nn = (tile0 + i) * TT + st;
+        if (i < n && nn < nt) {
+          kreg = *reinterpret_cast<const bf16x8*>(kp + (long long)nn * D + sc);
+          vreg = *reinterpret_cast<const bf16x8*>(vp + (long long)nn * D + sc);
+        }
+      };
+      auto stage = [&](int i) {
+        const int nn = (tile0 + i) * TT + st;
+        const bool live = nn < nt;
+        k8 kh;
+        bf16x8 vv;
+#pragma unroll
+        for (int j = 0; j < SCH; ++j) {
+          const float kv = KNORM ? ((float)kreg[j] - kst[sc + j][0]) * kst[sc + j][1] : (float)kreg[j];
+          kh[j] = live ? (KT)kv : (KT)0.f;
+          vv[j] = live ? vreg[j] : (bf16)0.f;
+        }
+        *reinterpret_cast<k8*>(&Kr[i % NK][st * LDK + (sc ^ kswz(st))]) = kh;
+        *reinterpret_cast<bf16x8*>(&Vr[i % NV][st * LDK + (sc ^ kswz(st))]) = vv;
+        if (sc == 0) eta_s[i % NV][st] = live ? (ep ? ep[nn] : 1.0f) : 0.0f;
+      };
+      // forward of tile i: Z', A' -> At, gelu' -> Gp, two hidden blocks at a time
+      auto forward = [&](int i) {
+        constexpr int HB2 = NHB < 2 ? NHB : 2;
+        const KT* kt = Kr[i % NK];
+        f16* at = At[i % NA];
+        h2* gpo = Gp[i % NA];
+#pragma unroll
+        for (int hc = 0; hc < NHB; hc += HB2) {
+          f32x4 z[2][HB2];
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int hb = 0; hb < HB2; ++hb) z[tb][hb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+              const k8 a = ld8t(&kt[(16 * tb + r) * LDK + ((32 * ks + 8 * g) ^ kswz(r))]);
+#pragma unroll
+              for (int hb = 0; hb < HB2; ++hb) z[tb][hb] = mfma16(a, w1r[hc + hb][ks], z[tb][hb]);
+            }
+#pragma unroll
+          for (int hb = 0; hb < HB2; ++hb) {
+            const float zz[8] = {z[0][hb][0], z[0][hb][1], z[0][hb][2], z[0][hb][3],
+                                 z[1][hb][0], z[1][hb][1], z[1][hb][2], z[1][hb][3]};
+            h2 av[4], gp[4];
+            gelu_chains<4, true>(zz, av, gp);
+            f16* row = &at[(h0 + 16 * (hc + hb) + r) * LDT];
+            *reinterpret_cast<f16x4*>(row + ((8 * g) ^ tswz(r))) = f16x4{av[0].x, av[0].y, av[1].x, av[1].y};
+            *reinterpret_cast<f16x4*>(row + ((8 * g + 4) ^ tswz(r))) = f16x4{av[2].x, av[2].y, av[3].x, av[3].y};
+            h2* gq = &gpo[((q * NHB + hc + hb) * 64 + lane) * 4];
+            *reinterpret_cast<f16x8*>(gq) =
+                f16x8{gp[0].x, gp[0].y, gp[1].x, gp[1].y, gp[2].x, gp[2].y, gp[3].x, gp[3].y};
           }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i] = eta_s[buf][16 * tb2 + 4 * g + i] * ((v0[i] + v1[i]) - (float)vq[i]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i] = -eta_s[buf][16 * tb2 + 4 * g + i] * (float)vq[i];
         }
-        *reinterpret_cast<f16x4*>(&Gc[(16 * cb2 + r) * LDT + ((8 * g + 4 * tb2) ^ tswz(r))]) = pack4h(gv);
-      }
-    };
-    // dW2 += A'^T G';  dA = G' W2^T;  dZ = dA gelu'(Z);  dW1 += K_hat^T dZ
-    auto backward = [&](int buf, const Act<NHB>& act) {
+      };
+      // V_hat and G' of tile i for channel block q, both 16-token halves -> Gc
+      auto gprime = [&](int i) {
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const f16* grow = &Gc[(16 * cb + r) * LDT];
-        const f16x8 b = cat44(*reinterpret_cast<const f16x4*>(grow + ((8 * g) ^ tswz(r))),
-                              *reinterpret_cast<const f16x4*>(grow + ((8 * g + 4) ^ tswz(r))));
+        for (int tb2 = 0; tb2 < 2; ++tb2) {
+          const int vrow = 16 * tb2 + 4 * g + (r >> 2);
+          const bf16x4 vq = ld_trt(&Vr[i % NV][vrow * LDK + ((16 * q + 4 * (r & 3)) ^ kswz(vrow))]);
+          f32x4 gv;
+          if (LOSS == LOSS_MSE) {
+            const f16* at = At[i % NA];
+            f32x4 v0 = f32x4{0, 0, 0, 0}, v1 = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) acc2[hb][cb] = mfma16(act.a[hb], b, acc2[hb][cb]);
-      }
-      f32x4 da[2][NHB];
+            for (int ks = 0; ks < NKH; ++ks) {
+              // A'[t = 16 tb2 + r][h = 32 ks + 8 g + j]
+              const int ar = 32 * ks + 8 * g + (r >> 2);
+              const f16x4 lo = ld_trt(&at[ar * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar))]);
+              const f16x4 hi = ld_trt(&at[(ar + 4) * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar + 4))]);
+              if (ks & 1) v1 = mfma16(cat44(lo, hi), w2g[ks], v1);
+              else v0 = mfma16(cat44(lo, hi), w2g[ks], v0);
+            }
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+            for (int j = 0; j < 4; ++j) gv[j] = eta_s[i % NV][16 * tb2 + 4 * g + j] * ((v0[j] + v1[j]) - (float)vq[j]);
+          } else {
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) da[tb][hb] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          // G'[t = 16 tb + r][c = 32 ks + 8 g + j]
-          const int gr = 32 * ks + 8 * g + (r >> 2);
-          const f16x4 lo = ld_trt(&Gc[gr * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr))]);
-          const f16x4 hi = ld_trt(&Gc[(gr + 4) * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr + 4))]);
-          const f16x8 a = cat44(lo, hi);
-#pragma unroll
-          for (int hb = 0; hb < NHB; ++hb) da[tb][hb] = mfma16(a, w2r[hb][ks], da[tb][hb]);
+            for (int j = 0; j < 4; ++j) gv[j] = -eta_s[i % NV][16 * tb2 + 4 * g + j] * (float)vq[j];
+          }
+          *reinterpret_cast<f16x4*>(&Gc[i % NG][(16 * q + r) * LDT + ((8 * g + 4 * tb2) ^ tswz(r))]) = pack4h(gv);
         }
-      k8 dzp[NHB];
+      };
+
+      prefetch(0);
+      stage(0);
+      prefetch(1);
+      __syncthreads();
+      for (int k = 0; k < n + 2; ++k) {
+        if (k + 1 < n) { stage(k + 1); prefetch(k + 2); }
+        if (k < n) forward(k);
+        if (k >= 1 && k <= n) gprime(k - 1);
+        __syncthreads();
+      }
+    } else {
+      // ---------------- consumer ----------------
+      f16x8 w2r[NHB][2];   // W2 as the B operand of dA = G' W2^T (k = channel, n = hidden)
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int ks = 0; ks < 2; ++ks) {
+          const float4* p2 = reinterpret_cast<const float4*>(W2 + (h0 + 16 * hb + r) * D + 32 * ks + 8 * g);
+          const float4 a = p2[0], b = p2[1];
+          w2r[hb][ks] = f16x8{(f16)a.x, (f16)a.y, (f16)a.z, (f16)a.w, (f16)b.x, (f16)b.y, (f16)b.z, (f16)b.w};
+        }
+      f32x4 acc1[4][NHB], acc2[NHB][4];
 #pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const h2 dz = cvt_h2(da[tb][hb][i], da[tb][hb][i + 1]) * act.gp[hb][2 * tb + i / 2];
-            dzp[hb][4 * tb + i] = (KT)(float)dz.x;
-            dzp[hb][4 * tb + i + 1] = (KT)(float)dz.y;
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < NHB; ++b) { acc1[a][b] = f32x4{0, 0, 0, 0}; acc2[b][a] = f32x4{0, 0, 0, 0}; }
+      auto backward = [&](int i) {
+        const f16* gc = Gc[i % NG];
+        const f16* at = At[i % NA];
+        const h2* gpi = Gp[i % NA];
+        const KT* kt = Kr[i % NK];
+        // pass 1: dW2 += A'^T G' (G' as the B operand: k = token, n = channel)
+        {
+          f16x8 gb[4];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const f16* grow = &gc[(16 * cb + r) * LDT];
+            gb[cb] = cat44(*reinterpret_cast<const f16x4*>(grow + ((8 * g) ^ tswz(r))),
+                           *reinterpret_cast<const f16x4*>(grow + ((8 * g + 4) ^ tswz(r))));
           }
-      // K_hat[t = tau(g, j)][c = 16 cb + r]
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int kr0 = 4 * g + (r >> 2);
-        const k4 lo = ld_trt(&Kr[buf][kr0 * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0))]);
-        const k4 hi = ld_trt(&Kr[buf][(kr0 + 16) * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0 + 16))]);
-        const k8 a = cat44(lo, hi);
+          for (int hb = 0; hb < NHB; ++hb) {
+            // A'^T (m = hidden, k = token) from the unit-major tile
+            const f16* arow = &at[(h0 + 16 * hb + r) * LDT];
+            const f16x8 aa = cat44(*reinterpret_cast<const f16x4*>(arow + ((8 * g) ^ tswz(r))),
+                                   *reinterpret_cast<const f16x4*>(arow + ((8 * g + 4) ^ tswz(r))));
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) acc1[cb][hb] = mfma16(a, dzp[hb], acc1[cb][hb]);
+            for (int cb = 0; cb < 4; ++cb) acc2[hb][cb] = mfma16(aa, gb[cb], acc2[hb][cb]);
+          }
+        }
+        // pass 2: dA = G' W2^T (G' as the A operand: m = token, k = channel), dZ = dA gelu'(Z)
+        k8 dz[NHB];
+        {
+          f16x8 ga[2][2];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+              const int gr = 32 * ks + 8 * g + (r >> 2);
+              ga[ks][tb] = cat44(ld_trt(&gc[gr * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr))]),
+                                 ld_trt(&gc[(gr + 4) * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr + 4))]));
+            }
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) {
+            f32x4 da[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+              for (int tb = 0; tb < 2; ++tb) da[tb] = mfma16(ga[ks][tb], w2r[hb][ks], da[tb]);
+            const f16x8 gpv = *reinterpret_cast<const f16x8*>(&gpi[((q * NHB + hb) * 64 + lane) * 4]);
+            const h2 g0{gpv[0], gpv[1]}, g1{gpv[2], gpv[3]}, g2{gpv[4], gpv[5]}, g3{gpv[6], gpv[7]};
+            const h2 d0 = cvt_h2(da[0][0], da[0][1]) * g0, d1 = cvt_h2(da[0][2], da[0][3]) * g1;
+            const h2 d2 = cvt_h2(da[1][0], da[1][1]) * g2, d3 = cvt_h2(da[1][2], da[1][3]) * g3;
+            dz[hb][0] = (KT)(float)d0.x; dz[hb][1] = (KT)(float)d0.y; dz[hb][2] = (KT)(float)d1.x;
+            dz[hb][3] = (KT)(float)d1.y; dz[hb][4] = (KT)(float)d2.x; dz[hb][5] = (KT)(float)d2.y;
+            dz[hb][6] = (KT)(float)d3.x; dz[hb][7] = (KT)(float)d3.y;
+          }
+        }
+        // pass 3: dW1 += K_hat^T dZ (K_hat^T as the A operand: m = channel, k = token)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const int kr0 = 4 * g + (r >> 2);
+          const k8 ka = cat44(ld_trt(&kt[kr0 * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0))]),
+                              ld_trt(&kt[(kr0 + 16) * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0 + 16))]));
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) acc1[cb][hb] = mfma16(ka, dz[hb], acc1[cb][hb]);
+        }
+      };
+      __syncthreads();                           // the producers' prologue
+      for (int k = 0; k < n + 2; ++k) {
+        if (k >= 2) backward(k - 2);
+        __syncthreads();
       }
-    };
-
-    // ---------------- prologue: tile0 through its G' ----------------
-    Act<NHB> cur;
-    prefetch(tile0);
-    stage(tile0, 0);
-    prefetch(tile0 + 1);
-    __syncthreads();
-    {
-      f32x4 z[2][NHB];
-      gemm1(0, z);
-      activate(z, cur);
-      write_at(cur);
-    }
-    if (LOSS == LOSS_MSE) __syncthreads();
-    gprime(0);
-    if (tile0 + 1 < tile1) { stage(tile0 + 1, 1); prefetch(tile0 + 2); }
-    __syncthreads();
-
-    // ---------------- steady state ----------------
-    // iteration i: forward of tile i+1 (GEMM1, GELU) overlapped with the
-    // backward of tile i; then V_hat / G' of tile i+1 and staging of tile i+2.
-    for (int tile = tile0; tile < tile1; ++tile) {
-      const int cb_ = (tile - tile0) & 1, nb_ = cb_ ^ 1;
-      const bool has_next = tile + 1 < tile1;
-      Act<NHB> nxt;
-      if (has_next) {
-        f32x4 z[2][NHB];
-        gemm1(nb_, z);
-        activate(z, nxt);
-      }
-      backward(cb_, cur);
-      if (has_next) write_at(nxt);
-      __syncthreads();
-      if (has_next) gprime(nb_);
-      if (tile + 2 < tile1) { stage(tile + 2, cb_); prefetch(tile + 3); }
-      __syncthreads();
-      if (has_next) cur = nxt;
-    }
-
-    // ---- partial of this (workgroup, pair) segment: [dW1 (d x h) | dW2 (h x d)]
-    // (acc2 holds A'^T G' = sqrt(2) A^T G')
-    float* out = part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID);
-    const float scale2 = scale * kRSqrt2;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          out[(16 * cb + 4 * g + i) * HID + h0 + 16 * hb + r] = scale * acc1[cb][hb][i];
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
+      // partial of this (workgroup, pair) segment: [dW1 (d x h) | dW2 (h x d)]
+      // (acc2 holds A'^T G' = sqrt(2) A^T G')
+      float* out = part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID);
+      const float scale2 = scale * kRSqrt2;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          out[(long long)D * HID + (h0 + 16 * hb + 4 * g + i) * D + 16 * cb + r] = scale2 * acc2[hb][cb][i];
+        for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            out[(16 * cb + 4 * g + i) * HID + h0 + 16 * hb + r] = scale * acc1[cb][hb][i];
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            out[(long long)D * HID + (h0 + 16 * hb + 4 * g + i) * D + 16 * cb + r] = scale2 * acc2[hb][cb][i];
+    }
     x = seg_end;
   }
 }
@@ -643,24 +643,24 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
   }
 }
 
-template <int HID, int NWAVE>
+template <int HID>
 void launch_grad_h(const Problem& pb, const WRef& W, int t0, int nt, int G, int J, float scale,
                    const float* spart, int S_stats, float eps, float* part, hipStream_t st) {
-  const dim3 grid(G), block(NWAVE * 64);
+  const dim3 grid(G), block(512);
   if (pb.loss == LOSS_MSE) {
     if (spart)
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, NWAVE, true>), grid, block, 0, st, pb, W, t0, nt, J, scale,
-                         spart, S_stats, eps, part);
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, true>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
+                         S_stats, eps, part);
     else
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, NWAVE, false>), grid, block, 0, st, pb, W, t0, nt, J, scale,
-                         spart, S_stats, eps, part);
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, false>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
+                         S_stats, eps, part);
   } else {
     if (spart)
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, NWAVE, true>), grid, block, 0, st, pb, W, t0, nt, J, scale,
-                         spart, S_stats, eps, part);
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, true>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
+                         S_stats, eps, part);
     else
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, NWAVE, false>), grid, block, 0, st, pb, W, t0, nt, J, scale,
-                         spart, S_stats, eps, part);
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, false>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
+                         S_stats, eps, part);
   }
 }
 
@@ -672,14 +672,14 @@ bool mfma_full_supported(const Problem& pb) {
 
 bool mfma_query_supported(const Problem& pb) { return mfma_full_supported(pb); }
 
-// grid of the stream-K gradient kernel: one workgroup per CU (two for the
-// 4-wave variant), never more workgroups than tiles
+// grid of the stream-K gradient kernel: one workgroup per CU (two for hidden
+// width 64, whose workgroups fit twice), never more workgroups than tiles
 void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_per_pair) {
   const int P = pb.B * pb.H;
   const int tpp = (nt + TT - 1) / TT;
   *tiles_per_pair = tpp;
   const long long total = (long long)P * tpp;
-  long long g = pb.hid == 64 ? 512 : 256;
+  long long g = (long long)device_cu_count() * (pb.hid == 64 ? 2 : 1);
   if (g > total) g = total;
   *G = (int)g;
   const long long per = (total + g - 1) / g;
@@ -691,9 +691,9 @@ void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, flo
   int G, J, tpp;
   mfma_grad_geometry(pb, nt, &G, &J, &tpp);
   switch (pb.hid) {
-    case 64: launch_grad_h<64, 4>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
-    case 128: launch_grad_h<128, 8>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
-    default: launch_grad_h<256, 8>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
+    case 64: launch_grad_h<64>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
+    case 128: launch_grad_h<128>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
+    default: launch_grad_h<256>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
   }
 }
 
