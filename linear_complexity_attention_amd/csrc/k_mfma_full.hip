@@ -170,23 +170,6 @@ __device__ __forceinline__ int tswz(int row) { return ((row >> 3) & 1) * 4 + ((r
 // of MFMA lane group g (4g..4g+3 and 16+4g..16+4g+3) are contiguous at 8g.
 __device__ __forceinline__ int tok_col(int t) { return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3); }
 
-// Combined key statistics of pair p, channel c, from the per-slice partials
-// (count, mean, M2) with Chan's pairwise update.
-__device__ __forceinline__ void key_stat(const float* sp, int S, int c, float eps, float& mu, float& rstd) {
-  float n = 0.f, mean = 0.f, m2 = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float* o = sp + (long long)s * 3 * D;
-    const float nb = o[c];
-    if (nb == 0.f) continue;
-    const float mb = o[D + c], m2b = o[2 * D + c];
-    const float nt = n + nb, delta = mb - mean;
-    mean += delta * (nb / nt);
-    m2 += m2b + delta * delta * (n * nb / nt);
-    n = nt;
-  }
-  mu = mean;
-  rstd = __builtin_amdgcn_rsqf(m2 / fmaxf(n, 1.f) + eps);
-}
 
 // ---------------------------------------------------------------------------
 // Fused forward/backward of one update batch, producer/consumer form.
@@ -221,7 +204,8 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
   __shared__ __attribute__((aligned(16))) h2 Gp[NA][4 * NHB * 64 * 4];
   __shared__ __attribute__((aligned(16))) f16 Gc[NG][D * LDT];
   __shared__ float eta_s[NV][TT];
-  __shared__ float kst[KNORM ? D : 1][2];   // key mean, rstd per channel
+  __shared__ __attribute__((aligned(16))) float kst[KNORM ? D : 1][2];   // key mean, rstd per channel
+  __shared__ float kpart[KNORM ? 8 : 1][3][KNORM ? D : 1];               // slice groups (count, mean, M2)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -248,6 +232,46 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     const float* W1 = W.mat(0, bb, hh_);
     const float* W2 = W.mat(1, bb, hh_);
 
+    // key statistics of the pair: the per-slice (count, mean, M2) partials are
+    // merged with Chan's formula, first by 8 groups of 64 threads (slices
+    // s = group, group + 8, ...), then by one thread per channel
+    if (KNORM) {
+      const int c = tid & 63, grp = tid >> 6;
+      const float* sp = spart + (long long)p * S_stats * 3 * D;
+      float cn = 0.f, mean = 0.f, m2 = 0.f;
+      for (int sl = grp; sl < S_stats; sl += 8) {
+        const float* o = sp + (long long)sl * 3 * D;
+        const float nb = o[c], mb = o[D + c], m2b = o[2 * D + c];
+        const float nt_ = cn + nb;
+        if (nb > 0.f) {
+          const float delta = mb - mean, f = nb / nt_;
+          mean += delta * f;
+          m2 += m2b + delta * delta * cn * f;
+          cn = nt_;
+        }
+      }
+      kpart[grp][0][c] = cn;
+      kpart[grp][1][c] = mean;
+      kpart[grp][2][c] = m2;
+      __syncthreads();
+      if (tid < D) {
+        float cn2 = 0.f, mean2 = 0.f, m22 = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < 8; ++gi) {
+          const float nb = kpart[gi][0][tid];
+          if (nb > 0.f) {
+            const float nt_ = cn2 + nb, delta = kpart[gi][1][tid] - mean2, f = nb / nt_;
+            mean2 += delta * f;
+            m22 += kpart[gi][2][tid] + delta * delta * cn2 * f;
+            cn2 = nt_;
+          }
+        }
+        kst[tid][0] = mean2;
+        kst[tid][1] = __builtin_amdgcn_rsqf(m22 / fmaxf(cn2, 1.f) + eps);
+      }
+      __syncthreads();
+    }
+
     if (producer) {
       // ---------------- producer ----------------
       const int st = tid / (D / SCH), sc = (tid % (D / SCH)) * SCH;   // staging: token row, first channel
@@ -271,17 +295,6 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           for (int j = 0; j < 8; ++j) w2g[ks][j] = (f16)(p2[j * D] * kRSqrt2);
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      // key statistics of the thread's 8 channels, parked in LDS to keep them
-      // out of the registers.  Every thread writes the entries it reads (the 32
-      // threads of a channel write identical values), so no barrier is needed.
-      if (KNORM) {
-        const float* sp = spart + (long long)p * S_stats * 3 * D;
-        float mu[SCH], rs[SCH];
-#pragma unroll
-        for (int j = 0; j < SCH; ++j) key_stat(sp, S_stats, sc + j, eps, mu[j], rs[j]);
-#pragma unroll
-        for (int j = 0; j < SCH; ++j) { kst[sc + j][0] = mu[j]; kst[sc + j][1] = rs[j]; }
       }
       const bf16* kp = (const bf16*)pb.k + ((long long)p * pb.N + t0) * D;
       const bf16* vp = (const bf16*)pb.v + ((long long)p * pb.N + t0) * D;

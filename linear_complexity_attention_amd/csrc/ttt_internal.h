@@ -61,7 +61,7 @@ void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st);
 // ---- MFMA fast paths --------------------------------------------------------
 // GELU-MLP, d = 64, h in {64,128,256}, bf16 tensors: fused forward/backward of
 // one update batch (tokens [t0, t0+nt)) at the fp32 weights W, stream-K over the
-// pairs' 32-token tiles; key statistics are combined from the per-slice
+// pairs' 32-token tiles; the key statistics are merged from the per-slice
 // partials `spart` (S_stats slices, null: no key norm); partial slots as in
 // mfma_grad_geometry.
 bool mfma_full_supported(const Problem& pb);
