@@ -171,6 +171,12 @@ __device__ __forceinline__ int tswz(int row) { return ((row >> 3) & 1) * 4 + ((r
 __device__ __forceinline__ int tok_col(int t) { return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3); }
 
 
+// Index of tile i's buffer in a ring of N.  Taken through readfirstlane so
+// that the compiler treats it as an opaque uniform value: otherwise loop
+// strength reduction turns every LDS address into its own induction variable.
+template <int N>
+__device__ __forceinline__ int ring(int i) { return __builtin_amdgcn_readfirstlane(i % N); }
+
 // ---------------------------------------------------------------------------
 // Fused forward/backward of one update batch, producer/consumer form.
 //
@@ -232,74 +238,123 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     const float* W1 = W.mat(0, bb, hh_);
     const float* W2 = W.mat(1, bb, hh_);
 
-    // key statistics of the pair: the per-slice (count, mean, M2) partials are
-    // merged with Chan's formula, first by 8 groups of 64 threads (slices
-    // s = group, group + 8, ...), then by one thread per channel
-    if (KNORM) {
-      const int c = tid & 63, grp = tid >> 6;
-      const float* sp = spart + (long long)p * S_stats * 3 * D;
-      float cn = 0.f, mean = 0.f, m2 = 0.f;
-      for (int sl = grp; sl < S_stats; sl += 8) {
-        const float* o = sp + (long long)sl * 3 * D;
-        const float nb = o[c], mb = o[D + c], m2b = o[2 * D + c];
-        const float nt_ = cn + nb;
-        if (nb > 0.f) {
-          const float delta = mb - mean, f = nb / nt_;
-          mean += delta * f;
-          m2 += m2b + delta * delta * cn * f;
-          cn = nt_;
-        }
-      }
-      kpart[grp][0][c] = cn;
-      kpart[grp][1][c] = mean;
-      kpart[grp][2][c] = m2;
-      __syncthreads();
-      if (tid < D) {
-        float cn2 = 0.f, mean2 = 0.f, m22 = 0.f;
+    // ---- segment prologue (all waves): the pair's weights and key statistics.
+    // W1 * sqrt(2)/c and W2 / sqrt(2) are staged in LDS, in their natural
+    // [in][out] layouts, over the A' / gelu' buffers (unused until phase 0),
+    // with coalesced 16-byte loads; the producers then take their MFMA
+    // fragments with transposing reads.  The key statistics are merged from
+    // the per-slice (count, mean, M2) partials with Chan's formula, first by 8
+    // groups of 64 threads (slices s = group, group + 8, ...), then by one
+    // thread per channel.
+    constexpr int L1 = HID + 16, L2 = 80;                // row strides of the staged W1, W2
+    KT* w1s = reinterpret_cast<KT*>(&At[0][0]);
+    f16* w2s = reinterpret_cast<f16*>(&Gp[0][0]);
+    static_assert(D * L1 <= NA * HID * LDT, "W1 staging exceeds the A' buffers");
+    static_assert(HID * L2 <= NA * 4 * NHB * 64 * 4 * 2, "W2 staging exceeds the gelu' buffers");
+    {
+      constexpr int NL = D * HID / (512 * 4);           // float4 loads per thread and matrix
+      float4 a1[NL], a2[NL];
 #pragma unroll
-        for (int gi = 0; gi < 8; ++gi) {
-          const float nb = kpart[gi][0][tid];
+      for (int j = 0; j < NL; ++j) {
+        a1[j] = reinterpret_cast<const float4*>(W1)[tid + 512 * j];
+        a2[j] = reinterpret_cast<const float4*>(W2)[tid + 512 * j];
+      }
+      float cn = 0.f, mean = 0.f, m2 = 0.f;
+      if (KNORM) {
+        const int c = tid & 63, grp = tid >> 6;
+        const float* sp = spart + (long long)p * S_stats * 3 * D;
+        for (int sl = grp; sl < S_stats; sl += 8) {
+          const float* o = sp + (long long)sl * 3 * D;
+          const float nb = o[c], mb = o[D + c], m2b = o[2 * D + c];
+          const float nt_ = cn + nb;
           if (nb > 0.f) {
-            const float nt_ = cn2 + nb, delta = kpart[gi][1][tid] - mean2, f = nb / nt_;
-            mean2 += delta * f;
-            m22 += kpart[gi][2][tid] + delta * delta * cn2 * f;
-            cn2 = nt_;
+            const float delta = mb - mean, f = nb / nt_;
+            mean += delta * f;
+            m2 += m2b + delta * delta * cn * f;
+            cn = nt_;
           }
         }
-        kst[tid][0] = mean2;
-        kst[tid][1] = __builtin_amdgcn_rsqf(m22 / fmaxf(cn2, 1.f) + eps);
+        kpart[grp][0][c] = cn;
+        kpart[grp][1][c] = mean;
+        kpart[grp][2][c] = m2;
       }
-      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int e = 4 * (tid + 512 * j);
+        const int c1 = e / HID, h1 = e % HID;            // W1 [c][h]
+        const int h2_ = e / D, c2 = e % D;                // W2 [h][c]
+        typedef typename Vec<KT>::v4 kt4;
+        *reinterpret_cast<kt4*>(&w1s[c1 * L1 + h1]) =
+            kt4{(KT)(a1[j].x * kZScale), (KT)(a1[j].y * kZScale), (KT)(a1[j].z * kZScale), (KT)(a1[j].w * kZScale)};
+        *reinterpret_cast<f16x4*>(&w2s[h2_ * L2 + c2]) =
+            f16x4{(f16)(a2[j].x * kRSqrt2), (f16)(a2[j].y * kRSqrt2), (f16)(a2[j].z * kRSqrt2), (f16)(a2[j].w * kRSqrt2)};
+      }
     }
+    __syncthreads();
+    if (KNORM && tid < D) {
+      float cn2 = 0.f, mean2 = 0.f, m22 = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < 8; ++gi) {
+        const float nb = kpart[gi][0][tid];
+        if (nb > 0.f) {
+          const float nt_ = cn2 + nb, delta = kpart[gi][1][tid] - mean2, f = nb / nt_;
+          mean2 += delta * f;
+          m22 += kpart[gi][2][tid] + delta * delta * cn2 * f;
+          cn2 = nt_;
+        }
+      }
+      kst[tid][0] = mean2;
+      kst[tid][1] = __builtin_amdgcn_rsqf(m22 / fmaxf(cn2, 1.f) + eps);
+    }
+    if (KNORM) __syncthreads();                        // kst is read by every staging thread
 
     if (producer) {
       // ---------------- producer ----------------
+      // issue priority over the consumer of the same SIMD: the producer's GELU
+      // waits on its own Z' MFMAs, which must not queue behind the consumer's
+      __builtin_amdgcn_s_setprio(2);
       const int st = tid / (D / SCH), sc = (tid % (D / SCH)) * SCH;   // staging: token row, first channel
+      // W1' as the B operand of Z' = K_hat W1' (k = channel, n = hidden)
       k8 w1r[NHB][2];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const float* p1 = W1 + (32 * ks + 8 * g) * HID + h0 + 16 * hb + r;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) w1r[hb][ks][j] = (KT)(p1[j * HID] * kZScale);
-          __builtin_amdgcn_sched_barrier(0);
+          const int row = 32 * ks + 8 * g + (r >> 2), col = h0 + 16 * hb + 4 * (r & 3);
+          w1r[hb][ks] = cat44(ld_trt(&w1s[row * L1 + col]), ld_trt(&w1s[(row + 4) * L1 + col]));
         }
-      // W2 / sqrt(2) as the B operand of V_hat = A' W2: column block q (16 channels)
+      // W2 / sqrt(2) as the B operand of V_hat = A' W2 (k = hidden, n = channel): column block q
       f16x8 w2g[LOSS == LOSS_MSE ? NKH : 1];
       if (LOSS == LOSS_MSE) {
 #pragma unroll
         for (int ks = 0; ks < NKH; ++ks) {
-          const float* p2 = W2 + (32 * ks + 8 * g) * D + 16 * q + r;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) w2g[ks][j] = (f16)(p2[j * D] * kRSqrt2);
-          __builtin_amdgcn_sched_barrier(0);
+          const int row = 32 * ks + 8 * g + (r >> 2), col = 16 * q + 4 * (r & 3);
+          w2g[ks] = cat44(ld_trt(&w2s[row * L2 + col]), ld_trt(&w2s[(row + 4) * L2 + col]));
         }
       }
       const bf16* kp = (const bf16*)pb.k + ((long long)p * pb.N + t0) * D;
       const bf16* vp = (const bf16*)pb.v + ((long long)p * pb.N + t0) * D;
       const float* ep = pb.eta_tok ? pb.eta_tok + (long long)p * pb.N + t0 : nullptr;
       bf16x8 kreg = {}, vreg = {};
+      // per-lane LDS offsets (elements), the same for every tile; what varies
+      // with the tile, the hidden block or the k-step is a uniform addend
+      const int r4 = r >> 2, r3 = r & 3;
+      const int offSt = st * LDK + (sc ^ kswz(st));                          // staging writes
+      const int offK0 = r * LDK + ((8 * g) ^ kswz(r));                        // Z' operand, ks = 0 (+16 tb LDK)
+      const int offK1 = r * LDK + ((32 + 8 * g) ^ kswz(r));                   // ks = 1
+      const int offAw0 = (h0 + r) * LDT + ((8 * g) ^ tswz(r));                // A' writes (+16 hb LDT)
+      const int offAw1 = (h0 + r) * LDT + ((8 * g + 4) ^ tswz(r));
+      int offTr[2][2];                                                        // A' transposed reads (+32 ks LDT)
+#pragma unroll
+      for (int tb2 = 0; tb2 < 2; ++tb2)
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          const int ar = 8 * g + r4 + 4 * o;
+          offTr[tb2][o] = ar * LDT + (tok_col(16 * tb2 + 4 * r3) ^ tswz(ar));
+        }
+      const int offV = (4 * g + r4) * LDK + ((16 * q + 4 * r3) ^ kswz(4 * g + r4));   // V reads (+16 tb2 LDK)
+      const int offGc0 = (16 * q + r) * LDT + ((8 * g) ^ tswz(r));            // G' writes, tb2 = 0
+      const int offGc1 = (16 * q + r) * LDT + ((8 * g + 4) ^ tswz(r));        // tb2 = 1
       auto prefetch = [&](int i) {              // segment-relative tile i
         const int nn = (tile0 + i) * TT + st;
         if (i < n && nn < nt) {
@@ -318,85 +373,115 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           kh[j] = live ? (KT)kv : (KT)0.f;
           vv[j] = live ? vreg[j] : (bf16)0.f;
         }
-        *reinterpret_cast<k8*>(&Kr[i % NK][st * LDK + (sc ^ kswz(st))]) = kh;
-        *reinterpret_cast<bf16x8*>(&Vr[i % NV][st * LDK + (sc ^ kswz(st))]) = vv;
-        if (sc == 0) eta_s[i % NV][st] = live ? (ep ? ep[nn] : 1.0f) : 0.0f;
+        *reinterpret_cast<k8*>(&Kr[ring<NK>(i)][offSt]) = kh;
+        *reinterpret_cast<bf16x8*>(&Vr[ring<NV>(i)][offSt]) = vv;
+        if (sc == 0) eta_s[ring<NV>(i)][st] = live ? (ep ? ep[nn] : 1.0f) : 0.0f;
       };
-      // forward of tile i: Z', A' -> At, gelu' -> Gp, two hidden blocks at a time
-      auto forward = [&](int i) {
-        constexpr int HB2 = NHB < 2 ? NHB : 2;
-        const KT* kt = Kr[i % NK];
-        f16* at = At[i % NA];
-        h2* gpo = Gp[i % NA];
+      // forward of tile i in chunks of two hidden blocks: Z' (MFMA) ...
+      constexpr int HB2 = NHB < 2 ? NHB : 2;
+      constexpr int NCH = NHB / HB2;
+      auto fwd_gemm = [&](int i, int hc, f32x4 (&z)[2][HB2]) {
+        const KT* kt0 = Kr[ring<NK>(i)] + offK0;
+        const KT* kt1 = Kr[ring<NK>(i)] + offK1;
 #pragma unroll
-        for (int hc = 0; hc < NHB; hc += HB2) {
-          f32x4 z[2][HB2];
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
+          for (int hb = 0; hb < HB2; ++hb) z[tb][hb] = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int hb = 0; hb < HB2; ++hb) z[tb][hb] = f32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
+          for (int tb = 0; tb < 2; ++tb) {
+            const k8 a = ld8t((ks ? kt1 : kt0) + 16 * tb * LDK);
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-              const k8 a = ld8t(&kt[(16 * tb + r) * LDK + ((32 * ks + 8 * g) ^ kswz(r))]);
+            for (int hb = 0; hb < HB2; ++hb) z[tb][hb] = mfma16(a, w1r[hc + hb][ks], z[tb][hb]);
+          }
+      };
+      // ... then GELU: A' -> At, gelu' -> Gp
+      auto fwd_act = [&](int i, int hc, const f32x4 (&z)[2][HB2]) {
+        f16* at0 = At[ring<NA>(i)] + offAw0;
+        f16* at1 = At[ring<NA>(i)] + offAw1;
+        h2* gpo = Gp[ring<NA>(i)] + lane * 4;
 #pragma unroll
-              for (int hb = 0; hb < HB2; ++hb) z[tb][hb] = mfma16(a, w1r[hc + hb][ks], z[tb][hb]);
-            }
+        for (int hb = 0; hb < HB2; ++hb) {
+          const float zz[8] = {z[0][hb][0], z[0][hb][1], z[0][hb][2], z[0][hb][3],
+                               z[1][hb][0], z[1][hb][1], z[1][hb][2], z[1][hb][3]};
+          h2 av[4], gp[4];
+          gelu_chains<4, true>(zz, av, gp);
+          *reinterpret_cast<f16x4*>(at0 + 16 * (hc + hb) * LDT) = f16x4{av[0].x, av[0].y, av[1].x, av[1].y};
+          *reinterpret_cast<f16x4*>(at1 + 16 * (hc + hb) * LDT) = f16x4{av[2].x, av[2].y, av[3].x, av[3].y};
+          h2* gq = gpo + (q * NHB + hc + hb) * 256;
+          *reinterpret_cast<f16x8*>(gq) =
+              f16x8{gp[0].x, gp[0].y, gp[1].x, gp[1].y, gp[2].x, gp[2].y, gp[3].x, gp[3].y};
+        }
+      };
+      // V_hat of tile i, token half tb2, channel block q: the MFMA chains ...
+      auto gp_issue = [&](int i, int tb2, f32x4& v0, f32x4& v1) {
+        v0 = f32x4{0, 0, 0, 0};
+        v1 = f32x4{0, 0, 0, 0};
+        if (LOSS == LOSS_MSE) {
+          // A'[t = 16 tb2 + r][h = 32 ks + 8 g + j]
+          const f16* alo = At[ring<NA>(i)] + offTr[tb2][0];
+          const f16* ahi = At[ring<NA>(i)] + offTr[tb2][1];
 #pragma unroll
-          for (int hb = 0; hb < HB2; ++hb) {
-            const float zz[8] = {z[0][hb][0], z[0][hb][1], z[0][hb][2], z[0][hb][3],
-                                 z[1][hb][0], z[1][hb][1], z[1][hb][2], z[1][hb][3]};
-            h2 av[4], gp[4];
-            gelu_chains<4, true>(zz, av, gp);
-            f16* row = &at[(h0 + 16 * (hc + hb) + r) * LDT];
-            *reinterpret_cast<f16x4*>(row + ((8 * g) ^ tswz(r))) = f16x4{av[0].x, av[0].y, av[1].x, av[1].y};
-            *reinterpret_cast<f16x4*>(row + ((8 * g + 4) ^ tswz(r))) = f16x4{av[2].x, av[2].y, av[3].x, av[3].y};
-            h2* gq = &gpo[((q * NHB + hc + hb) * 64 + lane) * 4];
-            *reinterpret_cast<f16x8*>(gq) =
-                f16x8{gp[0].x, gp[0].y, gp[1].x, gp[1].y, gp[2].x, gp[2].y, gp[3].x, gp[3].y};
+          for (int ks = 0; ks < NKH; ++ks) {
+            const f16x4 lo = ld_trt(alo + 32 * ks * LDT);
+            const f16x4 hi = ld_trt(ahi + 32 * ks * LDT);
+            if (ks & 1) v1 = mfma16(cat44(lo, hi), w2g[ks], v1);
+            else v0 = mfma16(cat44(lo, hi), w2g[ks], v0);
           }
         }
       };
-      // V_hat and G' of tile i for channel block q, both 16-token halves -> Gc
-      auto gprime = [&](int i) {
+      // ... and G' = eta (V_hat - V) [MSE] or -eta V [dot] -> Gc
+      auto gp_fin = [&](int i, int tb2, const f32x4& v0, const f32x4& v1) {
+        const bf16x4 vq = ld_trt(Vr[ring<NV>(i)] + offV + 16 * tb2 * LDK);
+        f32x4 gv;
 #pragma unroll
-        for (int tb2 = 0; tb2 < 2; ++tb2) {
-          const int vrow = 16 * tb2 + 4 * g + (r >> 2);
-          const bf16x4 vq = ld_trt(&Vr[i % NV][vrow * LDK + ((16 * q + 4 * (r & 3)) ^ kswz(vrow))]);
-          f32x4 gv;
-          if (LOSS == LOSS_MSE) {
-            const f16* at = At[i % NA];
-            f32x4 v0 = f32x4{0, 0, 0, 0}, v1 = f32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int ks = 0; ks < NKH; ++ks) {
-              // A'[t = 16 tb2 + r][h = 32 ks + 8 g + j]
-              const int ar = 32 * ks + 8 * g + (r >> 2);
-              const f16x4 lo = ld_trt(&at[ar * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar))]);
-              const f16x4 hi = ld_trt(&at[(ar + 4) * LDT + (tok_col(16 * tb2 + 4 * (r & 3)) ^ tswz(ar + 4))]);
-              if (ks & 1) v1 = mfma16(cat44(lo, hi), w2g[ks], v1);
-              else v0 = mfma16(cat44(lo, hi), w2g[ks], v0);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) gv[j] = eta_s[i % NV][16 * tb2 + 4 * g + j] * ((v0[j] + v1[j]) - (float)vq[j]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) gv[j] = -eta_s[i % NV][16 * tb2 + 4 * g + j] * (float)vq[j];
-          }
-          *reinterpret_cast<f16x4*>(&Gc[i % NG][(16 * q + r) * LDT + ((8 * g + 4 * tb2) ^ tswz(r))]) = pack4h(gv);
+        for (int j = 0; j < 4; ++j) {
+          const float e = eta_s[ring<NV>(i)][16 * tb2 + 4 * g + j];
+          gv[j] = LOSS == LOSS_MSE ? e * ((v0[j] + v1[j]) - (float)vq[j]) : -e * (float)vq[j];
         }
+        *reinterpret_cast<f16x4*>(Gc[ring<NG>(i)] + (tb2 ? offGc1 : offGc0)) = pack4h(gv);
       };
 
       prefetch(0);
       stage(0);
       prefetch(1);
       __syncthreads();
-      for (int k = 0; k < n + 2; ++k) {
+      // phase 0: forward of tile 0
+      if (1 < n) { stage(1); prefetch(2); }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        f32x4 z[2][HB2];
+        fwd_gemm(0, c * HB2, z);
+        fwd_act(0, c * HB2, z);
+      }
+      __syncthreads();
+      // phases 1 .. n-1: forward of tile k interleaved with V_hat / G' of tile k-1,
+      // so that the V_hat MFMA chains run under the GELU arithmetic
+      for (int k = 1; k < n; ++k) {
         if (k + 1 < n) { stage(k + 1); prefetch(k + 2); }
-        if (k < n) forward(k);
-        if (k >= 1 && k <= n) gprime(k - 1);
+        f32x4 va0, va1, vb0, vb1;
+        f32x4 z[2][HB2];
+        fwd_gemm(k, 0, z);
+        gp_issue(k - 1, 0, va0, va1);
+        fwd_act(k, 0, z);
+        if (NCH > 1) fwd_gemm(k, HB2, z);
+        gp_fin(k - 1, 0, va0, va1);
+        gp_issue(k - 1, 1, vb0, vb1);
+        if (NCH > 1) fwd_act(k, HB2, z);
+        gp_fin(k - 1, 1, vb0, vb1);
         __syncthreads();
       }
+      // phase n: V_hat / G' of the last tile; phase n+1: the consumers' last backward
+      {
+        f32x4 v0, v1;
+        gp_issue(n - 1, 0, v0, v1);
+        gp_fin(n - 1, 0, v0, v1);
+        gp_issue(n - 1, 1, v0, v1);
+        gp_fin(n - 1, 1, v0, v1);
+      }
+      __syncthreads();
+      __syncthreads();
     } else {
       // ---------------- consumer ----------------
       f16x8 w2r[NHB][2];   // W2 as the B operand of dA = G' W2^T (k = channel, n = hidden)
@@ -413,26 +498,38 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < NHB; ++b) { acc1[a][b] = f32x4{0, 0, 0, 0}; acc2[b][a] = f32x4{0, 0, 0, 0}; }
+      // per-lane LDS offsets (elements), as in the producer
+      const int r4 = r >> 2, r3 = r & 3;
+      const int offR0 = r * LDT + ((8 * g) ^ tswz(r));         // unit-major rows, token half 0 (+16 cb LDT)
+      const int offR1 = r * LDT + ((8 * g + 4) ^ tswz(r));     // token half 1
+      int offGt[2][2];                                          // G' transposed reads (+32 ks LDT)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          const int gr = 8 * g + r4 + 4 * o;
+          offGt[tb][o] = gr * LDT + (tok_col(16 * tb + 4 * r3) ^ tswz(gr));
+        }
+      int offKt[4];                                             // K_hat transposed reads (+16 LDK for hi)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) offKt[cb] = (4 * g + r4) * LDK + ((16 * cb + 4 * r3) ^ kswz(4 * g + r4));
       auto backward = [&](int i) {
-        const f16* gc = Gc[i % NG];
-        const f16* at = At[i % NA];
-        const h2* gpi = Gp[i % NA];
-        const KT* kt = Kr[i % NK];
+        const f16* gc = Gc[ring<NG>(i)];
+        const f16* at = At[ring<NA>(i)] + h0 * LDT;
+        const h2* gpi = Gp[ring<NA>(i)] + lane * 4;
+        const KT* kt = Kr[ring<NK>(i)];
         // pass 1: dW2 += A'^T G' (G' as the B operand: k = token, n = channel)
         {
           f16x8 gb[4];
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            const f16* grow = &gc[(16 * cb + r) * LDT];
-            gb[cb] = cat44(*reinterpret_cast<const f16x4*>(grow + ((8 * g) ^ tswz(r))),
-                           *reinterpret_cast<const f16x4*>(grow + ((8 * g + 4) ^ tswz(r))));
-          }
+          for (int cb = 0; cb < 4; ++cb)
+            gb[cb] = cat44(*reinterpret_cast<const f16x4*>(gc + offR0 + 16 * cb * LDT),
+                           *reinterpret_cast<const f16x4*>(gc + offR1 + 16 * cb * LDT));
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) {
             // A'^T (m = hidden, k = token) from the unit-major tile
-            const f16* arow = &at[(h0 + 16 * hb + r) * LDT];
-            const f16x8 aa = cat44(*reinterpret_cast<const f16x4*>(arow + ((8 * g) ^ tswz(r))),
-                                   *reinterpret_cast<const f16x4*>(arow + ((8 * g + 4) ^ tswz(r))));
+            const f16x8 aa = cat44(*reinterpret_cast<const f16x4*>(at + offR0 + 16 * hb * LDT),
+                                   *reinterpret_cast<const f16x4*>(at + offR1 + 16 * hb * LDT));
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) acc2[hb][cb] = mfma16(aa, gb[cb], acc2[hb][cb]);
           }
@@ -445,9 +542,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-              const int gr = 32 * ks + 8 * g + (r >> 2);
-              ga[ks][tb] = cat44(ld_trt(&gc[gr * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr))]),
-                                 ld_trt(&gc[(gr + 4) * LDT + (tok_col(16 * tb + 4 * (r & 3)) ^ tswz(gr + 4))]));
+              ga[ks][tb] = cat44(ld_trt(gc + offGt[tb][0] + 32 * ks * LDT), ld_trt(gc + offGt[tb][1] + 32 * ks * LDT));
             }
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) {
@@ -456,7 +551,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
               for (int tb = 0; tb < 2; ++tb) da[tb] = mfma16(ga[ks][tb], w2r[hb][ks], da[tb]);
-            const f16x8 gpv = *reinterpret_cast<const f16x8*>(&gpi[((q * NHB + hb) * 64 + lane) * 4]);
+            const f16x8 gpv = *reinterpret_cast<const f16x8*>(gpi + (q * NHB + hb) * 256);
             const h2 g0{gpv[0], gpv[1]}, g1{gpv[2], gpv[3]}, g2{gpv[4], gpv[5]}, g3{gpv[6], gpv[7]};
             const h2 d0 = cvt_h2(da[0][0], da[0][1]) * g0, d1 = cvt_h2(da[0][2], da[0][3]) * g1;
             const h2 d2 = cvt_h2(da[1][0], da[1][1]) * g2, d3 = cvt_h2(da[1][2], da[1][3]) * g3;
@@ -468,9 +563,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         // pass 3: dW1 += K_hat^T dZ (K_hat^T as the A operand: m = channel, k = token)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-          const int kr0 = 4 * g + (r >> 2);
-          const k8 ka = cat44(ld_trt(&kt[kr0 * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0))]),
-                              ld_trt(&kt[(kr0 + 16) * LDK + ((16 * cb + 4 * (r & 3)) ^ kswz(kr0 + 16))]));
+          const k8 ka = cat44(ld_trt(kt + offKt[cb]), ld_trt(kt + offKt[cb] + 16 * LDK));
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) acc1[cb][hb] = mfma16(ka, dz[hb], acc1[cb][hb]);
         }
