@@ -573,24 +573,21 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         if (k >= 2) backward(k - 2);
         __syncthreads();
       }
-      // partial of this (workgroup, pair) segment: [dW1 (d x h) | dW2 (h x d)]
-      // (acc2 holds A'^T G' = sqrt(2) A^T G')
-      float* out = part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID);
+      // partial of this (workgroup, pair) segment, [dW1 part | dW2 part], each
+      // stored in register order: float4 ((q*4 + cb)*NHB + hb)*64 + lane holds
+      // dW1[16cb + 4g + i][h0 + 16hb + r], float4 ((q*NHB + hb)*4 + cb)*64 + lane
+      // holds dW2[h0 + 16hb + 4g + i][16cb + r] (i = 0..3), so every store
+      // instruction writes 1 KB contiguously.  (acc2 holds A'^T G' = sqrt(2) A^T G'.)
+      f32x4* out = reinterpret_cast<f32x4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
       const float scale2 = scale * kRSqrt2;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            out[(16 * cb + 4 * g + i) * HID + h0 + 16 * hb + r] = scale * acc1[cb][hb][i];
+        for (int hb = 0; hb < NHB; ++hb) out[((q * 4 + cb) * NHB + hb) * 64 + lane] = scale * acc1[cb][hb];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            out[(long long)D * HID + (h0 + 16 * hb + 4 * g + i) * D + 16 * cb + r] = scale2 * acc2[hb][cb][i];
+        for (int cb = 0; cb < 4; ++cb) out[D * HID / 4 + ((q * NHB + hb) * 4 + cb) * 64 + lane] = scale2 * acc2[hb][cb];
     }
     x = seg_end;
   }

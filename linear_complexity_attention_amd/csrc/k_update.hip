@@ -63,6 +63,56 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
   if (a.out[i]) *reinterpret_cast<float4*>(a.out[i] + (size_t)p * pb.msz + o) = w;
 }
 
+// Update from the MFMA gradient kernel's stream-K partials, which are stored in
+// its register order (d = 64, GELU MLP, hidden width HID split in quarters of
+// HP = HID/4 units, NHB = HP/16 blocks of 16):
+//   dW1 part: float4 ((qq*4 + cb)*NHB + hb)*64 + l  ->  dW1[16cb + 4g + i][qq*HP + 16hb + r]
+//   dW2 part: float4 ((qq*NHB + hb)*4 + cb)*64 + l  ->  dW2[qq*HP + 16hb + 4g + i][16cb + r]
+// with l = 16g + r, i = 0..3.  Thread = one float4 of the partial: it sums that
+// float4 over the pair's slots (coalesced) and updates the 4 weights it maps to.
+// grid = (D*HID/2 / 256, P).
+template <int HID>
+__global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a) {
+  constexpr int D = 64, HP = HID / 4, NHB = HP / 16, HALF = D * HID / 4;   // float4s per matrix
+  const int p = blockIdx.y;
+  const int b = p / pb.H, h = p % pb.H;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= 2 * HALF) return;
+  const int mat = j >= HALF ? 1 : 0;
+  const int jj = j - mat * HALF;
+  const int l = jj & 63, blk = jj >> 6, g = l >> 4, r = l & 15;
+  int base, step;                 // element offset of i = 0 inside the matrix, stride over i
+  if (mat == 0) {
+    const int hb = blk % NHB, cb = (blk / NHB) & 3, qq = blk / (4 * NHB);
+    base = (16 * cb + 4 * g) * HID + qq * HP + 16 * hb + r;
+    step = HID;
+  } else {
+    const int cb = blk & 3, hb = (blk >> 2) % NHB, qq = blk / (4 * NHB);
+    base = (qq * HP + 16 * hb + 4 * g) * D + 16 * cb + r;
+    step = D;
+  }
+  const long long wsz = 2LL * D * HID;
+  long long q0, q1, total;
+  sk_range(a, pb.B * pb.H, p, q0, q1, total);
+  float4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (long long q = q0; q <= q1; ++q) {
+    const long long first = ((q * total) / a.sk_G) / a.sk_tpp;
+    const float4 d = reinterpret_cast<const float4*>(a.part + (q * a.sk_J + (p - first)) * wsz)[j];
+    sum.x += d.x; sum.y += d.y; sum.z += d.z; sum.w += d.w;
+  }
+  const float* cur = a.cur.mat(mat, b, h);
+  float* nxt = a.next + (size_t)p * wsz + (size_t)mat * D * HID;
+  float* out = a.out[mat] ? a.out[mat] + (size_t)p * D * HID : nullptr;
+  const float s4[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = base + i * step;
+    const float w = cur[e] - s4[i];
+    nxt[e] = w;
+    if (out) out[e] = w;
+  }
+}
+
 // Re-norm after the flat update: every output column of next is rescaled to
 // the L2 norm of the same column of W0.  grid = (column blocks, nm, P);
 // thread = (column, row lane), 16 row lanes per column.
@@ -157,6 +207,24 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, Up
 
 void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st) {
   const int P = pb.B * pb.H;
+  if (a.part_mode == PART_STREAMK) {
+    // partials of the MFMA gradient kernel (GELU MLP, d = 64)
+    UpdateArgs f = a;
+    if (a.renorm)
+      for (int i = 0; i < 3; ++i) f.out[i] = nullptr;   // the re-norm pass writes W_out
+    const dim3 grid((unsigned)((pb.d * pb.hid / 2 + 255) / 256), P);
+    switch (pb.hid) {
+      case 64: hipLaunchKernelGGL(k_update_streamk<64>, grid, dim3(256), 0, st, pb, f); break;
+      case 128: hipLaunchKernelGGL(k_update_streamk<128>, grid, dim3(256), 0, st, pb, f); break;
+      default: hipLaunchKernelGGL(k_update_streamk<256>, grid, dim3(256), 0, st, pb, f); break;
+    }
+    if (a.renorm) {
+      const int maxcols = pb.hid > pb.d ? pb.hid : pb.d;
+      dim3 g2((maxcols + kCols - 1) / kCols, pb.nm, P);
+      hipLaunchKernelGGL(k_renorm, g2, dim3(kCols * kRLanes), 0, st, pb, a);
+    }
+    return;
+  }
   // the flat kernel moves float4s: every matrix base and stride must keep 16-byte alignment
   bool aligned = pb.msz % 4 == 0 && a.cur.sb % 4 == 0 && a.cur.sh % 4 == 0;
   for (int i = 0; i < pb.nm; ++i) aligned = aligned && (reinterpret_cast<uintptr_t>(a.cur.m[i]) % 16 == 0) &&

@@ -48,7 +48,9 @@ struct UpdateArgs {
   WRef cur, w0;
   const float* part;            // gradient partials (already scaled by eta and the loss constant)
   int part_mode;                // PART_SPLITS: part[s][p][nm][msz], s < S
-                                // PART_STREAMK: slot (i*J + p - first_pair(i)) of workgroup i
+                                // PART_STREAMK: slot (i*J + p - first_pair(i)) of workgroup i,
+                                // laid out in the MFMA gradient kernel's register order
+                                // (see k_update_streamk)
   int S; long long part_pair_stride;
   int sk_G, sk_J, sk_tpp;       // stream-K geometry of the gradient kernel
   float* next;                  // [P][nm][msz] fp32
