@@ -171,6 +171,9 @@ __device__ __forceinline__ int tswz(int row) { return ((row >> 3) & 1) * 4 + ((r
 __device__ __forceinline__ int tok_col(int t) { return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3); }
 
 
+// producer (and consumer) waves of the gradient kernel for hidden width HID
+template <int HID> constexpr int kGradWaves = mfma_grad_waves(HID);
+
 // Index of tile i's buffer in a ring of N.  Taken through readfirstlane so
 // that the compiler treats it as an opaque uniform value: otherwise loop
 // strength reduction turns every LDS address into its own induction variable.
@@ -180,10 +183,10 @@ __device__ __forceinline__ int ring(int i) { return __builtin_amdgcn_readfirstla
 // ---------------------------------------------------------------------------
 // Fused forward/backward of one update batch, producer/consumer form.
 //
-// A workgroup has 8 waves: 4 producers and 4 consumers; producer q and
-// consumer q own the same quarter of the hidden units (HP = HID/4) and share
-// SIMD q, so the producer's VALU-heavy GELU and the consumer's MFMA-heavy
-// weight-gradient products overlap on that SIMD.  Tiles of 32 tokens flow
+// A workgroup has 2 NW waves: NW producers and NW consumers (NW = 4 or 8);
+// producer q and consumer q own the same HP = HID/NW hidden units and share a
+// SIMD (waves w and w + 4 land on the same SIMD), so the producer's VALU-heavy
+// GELU and the consumer's MFMA-heavy weight-gradient products overlap there.  Tiles of 32 tokens flow
 // through a three-stage pipeline, one barrier per stage:
 //   phase k, producers: stage K_hat, V, eta of tile k+1 (prefetched a phase
 //            earlier); Z' = K_hat W1 sqrt(2)/c and the packed GELU of tile k
@@ -192,32 +195,35 @@ __device__ __forceinline__ int ring(int i) { return __builtin_amdgcn_readfirstla
 //   phase k, consumers: backward of tile k-2: dW2 += A'^T G', dA = G' W2^T,
 //            dZ = dA gelu'(Z), dW1 += K_hat^T dZ.
 // Buffers: K tiles x4, V tiles x3, A' x3, gelu' x3, G' x2.
-template <int HID, int LOSS, bool KNORM>
-__global__ void __launch_bounds__(512, HID == 64 ? 2 : 1)
+template <int HID, int LOSS, bool KNORM, int NW>
+__global__ void __launch_bounds__(128 * NW, 1)
 k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float* __restrict__ spart, int S_stats,
             float eps, float* __restrict__ part) {
   typedef typename std::conditional<KNORM, f16, bf16>::type KT;
   typedef typename Vec<KT>::v8 k8;
   typedef typename Vec<KT>::v4 k4;
-  constexpr int HP = HID / 4;          // hidden units per producer / consumer
+  constexpr int NTH = 128 * NW;        // threads
+  constexpr int HP = HID / NW;         // hidden units per producer / consumer
   constexpr int NHB = HP / 16;         // 16-wide hidden blocks per wave
   constexpr int NKH = HID / 32;        // k-steps over the hidden width
-  constexpr int SCH = 8;               // channels staged per producer thread
+  constexpr int SCH = 32 / NW;         // channels staged per producer thread
+  constexpr int NB2 = 8 / NW;          // V_hat / G' blocks (16 tokens x 16 channels) per producer
+  static_assert(NHB >= 1, "at least one 16-wide hidden block per wave");
   constexpr int NK = 4, NV = 3, NA = 3, NG = 2;
   __shared__ __attribute__((aligned(16))) KT Kr[NK][TT * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Vr[NV][TT * LDK];
   __shared__ __attribute__((aligned(16))) f16 At[NA][HID * LDT];
-  __shared__ __attribute__((aligned(16))) h2 Gp[NA][4 * NHB * 64 * 4];
+  __shared__ __attribute__((aligned(16))) h2 Gp[NA][NW * NHB * 64 * 4];
   __shared__ __attribute__((aligned(16))) f16 Gc[NG][D * LDT];
   __shared__ float eta_s[NV][TT];
   __shared__ __attribute__((aligned(16))) float kst[KNORM ? D : 1][2];   // key mean, rstd per channel
-  __shared__ float kpart[KNORM ? 8 : 1][3][KNORM ? D : 1];               // slice groups (count, mean, M2)
+  __shared__ float kpart[KNORM ? 2 * NW : 1][3][KNORM ? D : 1];          // slice groups (count, mean, M2)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, provably uniform
-  const int q = w & 3;
-  const bool producer = w < 4;
+  const int q = w & (NW - 1);
+  const bool producer = w < NW;
   const int r = lane & 15, g = lane >> 4;
   const int h0 = q * HP;
   const int P = pb.B * pb.H;
@@ -243,27 +249,27 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     // [in][out] layouts, over the A' / gelu' buffers (unused until phase 0),
     // with coalesced 16-byte loads; the producers then take their MFMA
     // fragments with transposing reads.  The key statistics are merged from
-    // the per-slice (count, mean, M2) partials with Chan's formula, first by 8
-    // groups of 64 threads (slices s = group, group + 8, ...), then by one
-    // thread per channel.
+    // the per-slice (count, mean, M2) partials with Chan's formula, first by
+    // 2 NW groups of 64 threads (slices s = group, group + 2 NW, ...), then by
+    // one thread per channel.
     constexpr int L1 = HID + 16, L2 = 80;                // row strides of the staged W1, W2
     KT* w1s = reinterpret_cast<KT*>(&At[0][0]);
     f16* w2s = reinterpret_cast<f16*>(&Gp[0][0]);
     static_assert(D * L1 <= NA * HID * LDT, "W1 staging exceeds the A' buffers");
-    static_assert(HID * L2 <= NA * 4 * NHB * 64 * 4 * 2, "W2 staging exceeds the gelu' buffers");
+    static_assert(HID * L2 <= NA * NW * NHB * 64 * 4 * 2, "W2 staging exceeds the gelu' buffers");
     {
-      constexpr int NL = D * HID / (512 * 4);           // float4 loads per thread and matrix
+      constexpr int NL = D * HID / (NTH * 4);           // float4 loads per thread and matrix
       float4 a1[NL], a2[NL];
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        a1[j] = reinterpret_cast<const float4*>(W1)[tid + 512 * j];
-        a2[j] = reinterpret_cast<const float4*>(W2)[tid + 512 * j];
+        a1[j] = reinterpret_cast<const float4*>(W1)[tid + NTH * j];
+        a2[j] = reinterpret_cast<const float4*>(W2)[tid + NTH * j];
       }
       float cn = 0.f, mean = 0.f, m2 = 0.f;
       if (KNORM) {
         const int c = tid & 63, grp = tid >> 6;
         const float* sp = spart + (long long)p * S_stats * 3 * D;
-        for (int sl = grp; sl < S_stats; sl += 8) {
+        for (int sl = grp; sl < S_stats; sl += 2 * NW) {
           const float* o = sp + (long long)sl * 3 * D;
           const float nb = o[c], mb = o[D + c], m2b = o[2 * D + c];
           const float nt_ = cn + nb;
@@ -280,7 +286,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       }
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        const int e = 4 * (tid + 512 * j);
+        const int e = 4 * (tid + NTH * j);
         const int c1 = e / HID, h1 = e % HID;            // W1 [c][h]
         const int h2_ = e / D, c2 = e % D;                // W2 [h][c]
         typedef typename Vec<KT>::v4 kt4;
@@ -294,7 +300,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     if (KNORM && tid < D) {
       float cn2 = 0.f, mean2 = 0.f, m22 = 0.f;
 #pragma unroll
-      for (int gi = 0; gi < 8; ++gi) {
+      for (int gi = 0; gi < 2 * NW; ++gi) {
         const float nb = kpart[gi][0][tid];
         if (nb > 0.f) {
           const float nt_ = cn2 + nb, delta = kpart[gi][1][tid] - mean2, f = nb / nt_;
@@ -323,19 +329,25 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           const int row = 32 * ks + 8 * g + (r >> 2), col = h0 + 16 * hb + 4 * (r & 3);
           w1r[hb][ks] = cat44(ld_trt(&w1s[row * L1 + col]), ld_trt(&w1s[(row + 4) * L1 + col]));
         }
-      // W2 / sqrt(2) as the B operand of V_hat = A' W2 (k = hidden, n = channel): column block q
+      // V_hat / G' blocks of this producer: channel block cb2, token halves
+      // tb2 = 0, 1 (NW = 4) or tb2 = q / 4 (NW = 8)
+      const int cb2 = q & 3;
+      auto tbh = [&](int b) { return NB2 == 2 ? b : q >> 2; };
+      // W2 / sqrt(2) as the B operand of V_hat = A' W2 (k = hidden, n = channel): column block cb2
       f16x8 w2g[LOSS == LOSS_MSE ? NKH : 1];
       if (LOSS == LOSS_MSE) {
 #pragma unroll
         for (int ks = 0; ks < NKH; ++ks) {
-          const int row = 32 * ks + 8 * g + (r >> 2), col = 16 * q + 4 * (r & 3);
+          const int row = 32 * ks + 8 * g + (r >> 2), col = 16 * cb2 + 4 * (r & 3);
           w2g[ks] = cat44(ld_trt(&w2s[row * L2 + col]), ld_trt(&w2s[(row + 4) * L2 + col]));
         }
       }
       const bf16* kp = (const bf16*)pb.k + ((long long)p * pb.N + t0) * D;
       const bf16* vp = (const bf16*)pb.v + ((long long)p * pb.N + t0) * D;
       const float* ep = pb.eta_tok ? pb.eta_tok + (long long)p * pb.N + t0 : nullptr;
-      bf16x8 kreg = {}, vreg = {};
+      typedef __bf16 stg_t __attribute__((ext_vector_type(SCH)));
+      typedef KT stgk_t __attribute__((ext_vector_type(SCH)));
+      stg_t kreg = {}, vreg = {};
       // per-lane LDS offsets (elements), the same for every tile; what varies
       // with the tile, the hidden block or the k-step is a uniform addend
       const int r4 = r >> 2, r3 = r & 3;
@@ -352,29 +364,29 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           const int ar = 8 * g + r4 + 4 * o;
           offTr[tb2][o] = ar * LDT + (tok_col(16 * tb2 + 4 * r3) ^ tswz(ar));
         }
-      const int offV = (4 * g + r4) * LDK + ((16 * q + 4 * r3) ^ kswz(4 * g + r4));   // V reads (+16 tb2 LDK)
-      const int offGc0 = (16 * q + r) * LDT + ((8 * g) ^ tswz(r));            // G' writes, tb2 = 0
-      const int offGc1 = (16 * q + r) * LDT + ((8 * g + 4) ^ tswz(r));        // tb2 = 1
+      const int offV = (4 * g + r4) * LDK + ((16 * cb2 + 4 * r3) ^ kswz(4 * g + r4));   // V reads (+16 tb2 LDK)
+      const int offGc0 = (16 * cb2 + r) * LDT + ((8 * g) ^ tswz(r));          // G' writes, tb2 = 0
+      const int offGc1 = (16 * cb2 + r) * LDT + ((8 * g + 4) ^ tswz(r));      // tb2 = 1
       auto prefetch = [&](int i) {              // segment-relative tile i
         const int nn = (tile0 + i) * TT + st;
         if (i < n && nn < nt) {
-          kreg = *reinterpret_cast<const bf16x8*>(kp + (long long)nn * D + sc);
-          vreg = *reinterpret_cast<const bf16x8*>(vp + (long long)nn * D + sc);
+          kreg = *reinterpret_cast<const stg_t*>(kp + (long long)nn * D + sc);
+          vreg = *reinterpret_cast<const stg_t*>(vp + (long long)nn * D + sc);
         }
       };
       auto stage = [&](int i) {
         const int nn = (tile0 + i) * TT + st;
         const bool live = nn < nt;
-        k8 kh;
-        bf16x8 vv;
+        stgk_t kh;
+        stg_t vv;
 #pragma unroll
         for (int j = 0; j < SCH; ++j) {
           const float kv = KNORM ? ((float)kreg[j] - kst[sc + j][0]) * kst[sc + j][1] : (float)kreg[j];
           kh[j] = live ? (KT)kv : (KT)0.f;
           vv[j] = live ? vreg[j] : (bf16)0.f;
         }
-        *reinterpret_cast<k8*>(&Kr[ring<NK>(i)][offSt]) = kh;
-        *reinterpret_cast<bf16x8*>(&Vr[ring<NV>(i)][offSt]) = vv;
+        *reinterpret_cast<stgk_t*>(&Kr[ring<NK>(i)][offSt]) = kh;
+        *reinterpret_cast<stg_t*>(&Vr[ring<NV>(i)][offSt]) = vv;
         if (sc == 0) eta_s[ring<NV>(i)][st] = live ? (ep ? ep[nn] : 1.0f) : 0.0f;
       };
       // forward of tile i in chunks of two hidden blocks: Z' (MFMA) ...
@@ -414,7 +426,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
               f16x8{gp[0].x, gp[0].y, gp[1].x, gp[1].y, gp[2].x, gp[2].y, gp[3].x, gp[3].y};
         }
       };
-      // V_hat of tile i, token half tb2, channel block q: the MFMA chains ...
+      // V_hat of tile i, token half tb2, channel block cb2: the MFMA chains ...
       auto gp_issue = [&](int i, int tb2, f32x4& v0, f32x4& v1) {
         v0 = f32x4{0, 0, 0, 0};
         v1 = f32x4{0, 0, 0, 0};
@@ -463,22 +475,21 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         f32x4 va0, va1, vb0, vb1;
         f32x4 z[2][HB2];
         fwd_gemm(k, 0, z);
-        gp_issue(k - 1, 0, va0, va1);
+        gp_issue(k - 1, tbh(0), va0, va1);
         fwd_act(k, 0, z);
         if (NCH > 1) fwd_gemm(k, HB2, z);
-        gp_fin(k - 1, 0, va0, va1);
-        gp_issue(k - 1, 1, vb0, vb1);
+        gp_fin(k - 1, tbh(0), va0, va1);
+        if (NB2 > 1) gp_issue(k - 1, tbh(1), vb0, vb1);
         if (NCH > 1) fwd_act(k, HB2, z);
-        gp_fin(k - 1, 1, vb0, vb1);
+        if (NB2 > 1) gp_fin(k - 1, tbh(1), vb0, vb1);
         __syncthreads();
       }
       // phase n: V_hat / G' of the last tile; phase n+1: the consumers' last backward
-      {
+#pragma unroll
+      for (int b = 0; b < NB2; ++b) {
         f32x4 v0, v1;
-        gp_issue(n - 1, 0, v0, v1);
-        gp_fin(n - 1, 0, v0, v1);
-        gp_issue(n - 1, 1, v0, v1);
-        gp_fin(n - 1, 1, v0, v1);
+        gp_issue(n - 1, tbh(b), v0, v1);
+        gp_fin(n - 1, tbh(b), v0, v1);
       }
       __syncthreads();
       __syncthreads();
@@ -749,20 +760,21 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
 template <int HID>
 void launch_grad_h(const Problem& pb, const WRef& W, int t0, int nt, int G, int J, float scale,
                    const float* spart, int S_stats, float eps, float* part, hipStream_t st) {
-  const dim3 grid(G), block(512);
+  constexpr int NW = kGradWaves<HID>;
+  const dim3 grid(G), block(128 * NW);
   if (pb.loss == LOSS_MSE) {
     if (spart)
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, true>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, true, NW>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
                          S_stats, eps, part);
     else
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, false>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, false, NW>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
                          S_stats, eps, part);
   } else {
     if (spart)
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, true>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, true, NW>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
                          S_stats, eps, part);
     else
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, false>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, false, NW>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
                          S_stats, eps, part);
   }
 }
@@ -782,7 +794,7 @@ void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_pe
   const int tpp = (nt + TT - 1) / TT;
   *tiles_per_pair = tpp;
   const long long total = (long long)P * tpp;
-  long long g = (long long)device_cu_count() * (pb.hid == 64 ? 2 : 1);
+  long long g = (long long)device_cu_count() * (pb.hid == 64 ? 2 : 1);   // width 64 fits twice per CU
   if (g > total) g = total;
   *G = (int)g;
   const long long per = (total + g - 1) / g;

@@ -64,16 +64,16 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
 }
 
 // Update from the MFMA gradient kernel's stream-K partials, which are stored in
-// its register order (d = 64, GELU MLP, hidden width HID split in quarters of
-// HP = HID/4 units, NHB = HP/16 blocks of 16):
+// its register order (d = 64, GELU MLP, hidden width HID split over its waves
+// in slices of HP units, NHB = HP/16 blocks of 16):
 //   dW1 part: float4 ((qq*4 + cb)*NHB + hb)*64 + l  ->  dW1[16cb + 4g + i][qq*HP + 16hb + r]
 //   dW2 part: float4 ((qq*NHB + hb)*4 + cb)*64 + l  ->  dW2[qq*HP + 16hb + 4g + i][16cb + r]
 // with l = 16g + r, i = 0..3.  Thread = one float4 of the partial: it sums that
 // float4 over the pair's slots (coalesced) and updates the 4 weights it maps to.
 // grid = (D*HID/2 / 256, P).
-template <int HID>
+template <int HID, int HP>
 __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a) {
-  constexpr int D = 64, HP = HID / 4, NHB = HP / 16, HALF = D * HID / 4;   // float4s per matrix
+  constexpr int D = 64, NHB = HP / 16, HALF = D * HID / 4;   // float4s per matrix
   const int p = blockIdx.y;
   const int b = p / pb.H, h = p % pb.H;
   const int j = blockIdx.x * 256 + threadIdx.x;
@@ -214,9 +214,9 @@ void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st) {
       for (int i = 0; i < 3; ++i) f.out[i] = nullptr;   // the re-norm pass writes W_out
     const dim3 grid((unsigned)((pb.d * pb.hid / 2 + 255) / 256), P);
     switch (pb.hid) {
-      case 64: hipLaunchKernelGGL(k_update_streamk<64>, grid, dim3(256), 0, st, pb, f); break;
-      case 128: hipLaunchKernelGGL(k_update_streamk<128>, grid, dim3(256), 0, st, pb, f); break;
-      default: hipLaunchKernelGGL(k_update_streamk<256>, grid, dim3(256), 0, st, pb, f); break;
+      case 64: hipLaunchKernelGGL((k_update_streamk<64, 64 / mfma_grad_waves(64)>), grid, dim3(256), 0, st, pb, f); break;
+      case 128: hipLaunchKernelGGL((k_update_streamk<128, 128 / mfma_grad_waves(128)>), grid, dim3(256), 0, st, pb, f); break;
+      default: hipLaunchKernelGGL((k_update_streamk<256, 256 / mfma_grad_waves(256)>), grid, dim3(256), 0, st, pb, f); break;
     }
     if (a.renorm) {
       const int maxcols = pb.hid > pb.d ? pb.hid : pb.d;
