@@ -57,39 +57,48 @@ __device__ __forceinline__ bf16x4 ld_tr(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// Packed-f16 GELU.  With c = 3.5, zh = sqrt(2) Z / c, w = clamp(zh, -sqrt(2),
-// sqrt(2)) and v = w^2 - 1 (in [-1, 1]),
+// Packed-f16 GELU.  With a clamp point c, zh = sqrt(2) Z / c, w = clamp(zh,
+// -sqrt(2), sqrt(2)) and v = w^2 - 1 (in [-1, 1]),
 //     c Phi(Z) = c/2 + w P(v) / sqrt(2),     gelu'(Z) = 1/2 + w Q(v) / sqrt(2)
-// where P, Q are degree-6 Lawson (minimax) fits in v, whose small coefficients
-// keep f16 Horner accurate; then zh * c Phi(Z) = sqrt(2) gelu(Z).  Two elements
-// per instruction and no transcendental; max |error| 3.3e-3 on gelu (relative
-// 1e-3 at large |Z|) and 3.0e-3 on gelu'.  The weights that produce Z are
-// staged pre-scaled by sqrt(2)/c, so the MFMA delivers zh; the activation
+// where P, Q are Lawson (minimax) fits in v, whose small coefficients keep f16
+// Horner accurate; then zh * c Phi(Z) = sqrt(2) gelu(Z).  Two elements per
+// instruction and no transcendental.  The weights that produce Z are staged
+// pre-scaled by sqrt(2)/c, so the MFMA delivers zh; the activation
 // A' = sqrt(2) gelu(Z) is consumed by products whose other operand (or result)
-// carries the compensating 1/sqrt(2).
+// carries the compensating 1/sqrt(2).  Two fits (coefficients of v^0, v^1, ...):
+//   GeluFit5: c = 3.5, P and Q of degree 5, max |error| 4.5e-3 on gelu
+//             (|Z| < 4), 2.4e-3 on gelu'; for the gradient kernel;
+//   GeluFit4: c = 3.125, P of degree 4, max |error| 4.7e-3 on gelu (|Z| < 4);
+//             for the readout, which needs no gelu'.
+// Beyond |Z| = 4 the error is the f16 rounding of the result (relative 1e-3).
 typedef _Float16 f16;
 typedef f16 h2 __attribute__((ext_vector_type(2)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f2 __attribute__((ext_vector_type(2)));
-constexpr float kClampC = 3.5f;
 constexpr float kSqrt2 = 1.41421356237f;
 constexpr float kRSqrt2 = 0.70710678119f;
-constexpr float kZScale = kSqrt2 / kClampC;     // applied to W1 (and W3) when staged
+struct GeluFit5 {
+  static constexpr float c = 3.5f;
+  static constexpr int NP = 6, NQ = 6;
+  static constexpr float P[6] = {2.442589408f, -1.104925742f, 0.63956925f, -0.372622668f, 0.231905421f, -0.087876027f};
+  static constexpr float Q[6] = {0.764969678f, -0.512306439f, 0.450549349f, -0.42596567f, 0.42093503f, -0.196860224f};
+};
+struct GeluFit4 {
+  static constexpr float c = 3.125f;
+  static constexpr int NP = 5, NQ = 1;
+  static constexpr float P[5] = {2.14908049f, -0.897445747f, 0.478055487f, -0.263695363f, 0.094819101f};
+  static constexpr float Q[1] = {0.f};
+};
+constexpr float kZScale = kSqrt2 / GeluFit5::c;        // W1 staging scale of the gradient kernel
+constexpr float kZScaleQ = kSqrt2 / GeluFit4::c;       // ... and of the readout
 __device__ __forceinline__ h2 hh(float x) { return h2{(f16)x, (f16)x}; }
 __device__ __forceinline__ h2 cvt_h2(float x0, float x1) { return __builtin_convertvector(f2{x0, x1}, h2); }
-// Coefficients of P(v)/sqrt(2) and Q(v)/sqrt(2), highest degree first.
-constexpr float kP[7] = {0.034846943f * kRSqrt2, -0.1021939f * kRSqrt2, 0.186821488f * kRSqrt2,
-                         -0.358320439f * kRSqrt2, 0.65378186f * kRSqrt2, -1.10760263f * kRSqrt2,
-                         2.44194935f * kRSqrt2};
-constexpr float kQ[7] = {0.0954901068f * kRSqrt2, -0.234467175f * kRSqrt2, 0.296631852f * kRSqrt2,
-                         -0.388431366f * kRSqrt2, 0.49006813f * kRSqrt2, -0.519321705f * kRSqrt2,
-                         0.763167748f * kRSqrt2};
 // The Horner chains of NC element pairs are advanced together: a dependent
 // packed-f16 FMA must wait a cycle after its producer, independent ones need
 // not, so interleaving the chains keeps the VALU issuing every cycle.
 //   z[2c], z[2c+1] = zh of pair c  ->  a[c] = sqrt(2) gelu(Z)  (and gp[c] = gelu'(Z))
-template <int NC, bool GRAD>
+template <class F, int NC, bool GRAD>
 __device__ __forceinline__ void gelu_chains(const float* z, h2* a, h2* gp) {
   h2 zh[NC], w[NC], v[NC], p[NC], q[NC];
 #pragma unroll
@@ -102,20 +111,23 @@ __device__ __forceinline__ void gelu_chains(const float* z, h2* a, h2* gp) {
   for (int c = 0; c < NC; ++c) v[c] = __builtin_elementwise_fma(w[c], w[c], hh(-1.0f));
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    p[c] = __builtin_elementwise_fma(hh(kP[0]), v[c], hh(kP[1]));
-    if (GRAD) q[c] = __builtin_elementwise_fma(hh(kQ[0]), v[c], hh(kQ[1]));
+    p[c] = __builtin_elementwise_fma(hh(F::P[F::NP - 1] * kRSqrt2), v[c], hh(F::P[F::NP - 2] * kRSqrt2));
+    if constexpr (GRAD) q[c] = __builtin_elementwise_fma(hh(F::Q[F::NQ - 1] * kRSqrt2), v[c], hh(F::Q[F::NQ - 2] * kRSqrt2));
   }
 #pragma unroll
-  for (int k = 2; k < 7; ++k)
+  for (int k = F::NP - 3; k >= 0; --k)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      p[c] = __builtin_elementwise_fma(p[c], v[c], hh(kP[k]));
-      if (GRAD) q[c] = __builtin_elementwise_fma(q[c], v[c], hh(kQ[k]));
-    }
+    for (int c = 0; c < NC; ++c) p[c] = __builtin_elementwise_fma(p[c], v[c], hh(F::P[k] * kRSqrt2));
+  if constexpr (GRAD) {
+#pragma unroll
+    for (int k = F::NQ - 3; k >= 0; --k)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) q[c] = __builtin_elementwise_fma(q[c], v[c], hh(F::Q[k] * kRSqrt2));
+  }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    a[c] = zh[c] * __builtin_elementwise_fma(w[c], p[c], hh(0.5f * kClampC));
-    if (GRAD) gp[c] = __builtin_elementwise_fma(w[c], q[c], hh(0.5f));
+    a[c] = zh[c] * __builtin_elementwise_fma(w[c], p[c], hh(0.5f * F::c));
+    if constexpr (GRAD) gp[c] = __builtin_elementwise_fma(w[c], q[c], hh(0.5f));
   }
 }
 
@@ -418,7 +430,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           const float zz[8] = {z[0][hb][0], z[0][hb][1], z[0][hb][2], z[0][hb][3],
                                z[1][hb][0], z[1][hb][1], z[1][hb][2], z[1][hb][3]};
           h2 av[4], gp[4];
-          gelu_chains<4, true>(zz, av, gp);
+          gelu_chains<GeluFit5, 4, true>(zz, av, gp);
           *reinterpret_cast<f16x4*>(at0 + 16 * (hc + hb) * LDT) = f16x4{av[0].x, av[0].y, av[1].x, av[1].y};
           *reinterpret_cast<f16x4*>(at1 + 16 * (hc + hb) * LDT) = f16x4{av[2].x, av[2].y, av[3].x, av[3].y};
           h2* gq = gpo + (q * NHB + hc + hb) * 256;
@@ -661,7 +673,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
       const int c1 = e / HID, h1 = e % HID;         // W1 [c][h]
       const int h2_ = e / D, c2 = e % D;             // W2 [h][c]
       *reinterpret_cast<bf16x4*>(&w1s[c1 * L1 + h1]) =
-          bf16x4{(bf16)(a.x * kZScale), (bf16)(a.y * kZScale), (bf16)(a.z * kZScale), (bf16)(a.w * kZScale)};
+          bf16x4{(bf16)(a.x * kZScaleQ), (bf16)(a.y * kZScaleQ), (bf16)(a.z * kZScaleQ), (bf16)(a.w * kZScaleQ)};
       *reinterpret_cast<f16x4*>(&w2s[h2_ * L2 + c2]) =
           f16x4{(f16)(b.x * kRSqrt2), (f16)(b.y * kRSqrt2), (f16)(b.z * kRSqrt2), (f16)(b.w * kRSqrt2)};
     }
@@ -714,7 +726,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
           const float zz[8] = {z[0][tb][0], z[0][tb][1], z[0][tb][2], z[0][tb][3],
                                z[1][tb][0], z[1][tb][1], z[1][tb][2], z[1][tb][3]};
           h2 x[4];
-          gelu_chains<4, false>(zz, x, nullptr);
+          gelu_chains<GeluFit4, 4, false>(zz, x, nullptr);
           ab[tb] = f16x8{x[0].x, x[0].y, x[1].x, x[1].y, x[2].x, x[2].y, x[3].x, x[3].y};
         }
 #pragma unroll
