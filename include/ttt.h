@@ -172,7 +172,9 @@ const char* ttt_path_name(const ttt_handle* h, int loss, int inner, int chunk);
  * records events[2k] on its stream right before and events[2k+1] right after
  * kernel family k: 0 key statistics, 1 gradient of the first update batch,
  * 2 weight update of the first batch, 3 readout.  A family that does not run
- * (no key norm) records both of its events back to back.  events == NULL or
+ * (no key norm) records both of its events back to back.  A NULL entry is
+ * skipped (each recorded event adds a little time between kernels, so a
+ * caller timing one family passes only its two events).  events == NULL or
  * n_events == 0 switches the hook off.  The events are not owned by the
  * library.  Host-only; returns TTT_ERR_INVALID for any other n_events. */
 int ttt_set_timing_events(ttt_handle* h, void* const* events, int n_events);

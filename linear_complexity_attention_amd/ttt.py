@@ -129,11 +129,12 @@ def ttt_path_name(handle, loss: int, inner: int, chunk: int):
 
 
 def ttt_set_timing_events(handle, events) -> None:
-    """events: sequence of 8 hipEvent_t handles (ints), or None to switch off."""
+    """events: sequence of 8 hipEvent_t handles (ints; None entries are
+    skipped), or None to switch off."""
     if events is None:
         rc = _lib.ttt_set_timing_events(handle, None, 0)
     else:
-        arr = (c_void_p * len(events))(*events)
+        arr = (c_void_p * len(events))(*[e if e else None for e in events])
         rc = _lib.ttt_set_timing_events(handle, arr, len(events))
     if rc != TTT_OK:
         raise TTTError(rc, ttt_last_error(handle))
