@@ -114,41 +114,76 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
 }
 
 // Re-norm after the flat update: every output column of next is rescaled to
-// the L2 norm of the same column of W0.  grid = (column blocks, nm, P);
-// thread = (column, row lane), 16 row lanes per column.
-constexpr int kRLanes = 16;
-__global__ void __launch_bounds__(kCols * kRLanes) k_renorm(Problem pb, UpdateArgs a) {
+// the L2 norm of the same column of W0.  grid = (column blocks of 16, nm, P);
+// thread = (column, row lane), 64 row lanes per column, each holding its rows'
+// values in registers between the norm reduction and the rescale (rows past
+// RMAX * 64 are read again for the rescale).
+constexpr int kRCols = 16, kRLanes = 64;
+template <int RMAX>
+__global__ void __launch_bounds__(kRCols * kRLanes) k_renorm(Problem pb, UpdateArgs a) {
   const int i = blockIdx.y, p = blockIdx.z;
   const int b = p / pb.H, h = p % pb.H;
   int rows, cols;
   mat_dims(pb, i, rows, cols);
-  const int j = blockIdx.x * kCols + threadIdx.x % kCols;
-  const int lane = threadIdx.x / kCols;
+  const int cl = threadIdx.x % kRCols, lane = threadIdx.x / kRCols;
+  const int j = blockIdx.x * kRCols + cl;
   const bool live = j < cols;
   const float* w0 = a.w0.mat(i, b, h);
   float* nxt = a.next + ((size_t)p * pb.nm + i) * pb.msz;
-  __shared__ float red[2][kRLanes][kCols];
+  __shared__ float red[2][kRLanes][kRCols];
+  float v[RMAX];
   float nn = 0.f, nr = 0.f;
-  if (live)
-    for (int r = lane; r < rows; r += kRLanes) {
-      const float w = nxt[(size_t)r * cols + j], v = w0[(size_t)r * cols + j];
-      nn += w * w;
-      nr += v * v;
+#pragma unroll
+  for (int k = 0; k < RMAX; ++k) {
+    const int r = lane + kRLanes * k;
+    v[k] = 0.f;
+    if (live && r < rows) {
+      const size_t e = (size_t)r * cols + j;
+      v[k] = nxt[e];
+      const float w0v = w0[e];
+      nn += v[k] * v[k];
+      nr += w0v * w0v;
     }
-  red[0][lane][threadIdx.x % kCols] = nn;
-  red[1][lane][threadIdx.x % kCols] = nr;
+  }
+  if (live)                                  // rows beyond the register block: read twice
+    for (int r = lane + kRLanes * RMAX; r < rows; r += kRLanes) {
+      const size_t e = (size_t)r * cols + j;
+      const float x = nxt[e], w0v = w0[e];
+      nn += x * x;
+      nr += w0v * w0v;
+    }
+  red[0][lane][cl] = nn;
+  red[1][lane][cl] = nr;
   __syncthreads();
   if (!live) return;
   float sn = 0.f, sr = 0.f;
-  for (int l = 0; l < kRLanes; ++l) { sn += red[0][l][threadIdx.x % kCols]; sr += red[1][l][threadIdx.x % kCols]; }
+  for (int l = 0; l < kRLanes; ++l) { sn += red[0][l][cl]; sr += red[1][l][cl]; }
   const float scale = sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f);
   float* out = a.out[i] ? a.out[i] + (size_t)p * pb.msz : nullptr;
-  for (int r = lane; r < rows; r += kRLanes) {
-    const size_t e = (size_t)r * cols + j;
-    const float w = nxt[e] * scale;
-    nxt[e] = w;
-    if (out) out[e] = w;
+#pragma unroll
+  for (int k = 0; k < RMAX; ++k) {
+    const int r = lane + kRLanes * k;
+    if (r < rows) {
+      const size_t e = (size_t)r * cols + j;
+      nxt[e] = v[k] * scale;
+      if (out) out[e] = v[k] * scale;
+    }
   }
+  for (int r = lane + kRLanes * RMAX; r < rows; r += kRLanes) {
+    const size_t e = (size_t)r * cols + j;
+    const float x = nxt[e] * scale;
+    nxt[e] = x;
+    if (out) out[e] = x;
+  }
+}
+
+static void launch_renorm(const Problem& pb, const UpdateArgs& a, hipStream_t st) {
+  const int P = pb.B * pb.H;
+  const int side = pb.inner == INNER_LINEAR ? pb.d : (pb.hid > pb.d ? pb.hid : pb.d);   // max rows, max cols
+  dim3 g((side + kRCols - 1) / kRCols, pb.nm, P);
+  if (side <= 2 * kRLanes) hipLaunchKernelGGL(k_renorm<2>, g, dim3(kRCols * kRLanes), 0, st, pb, a);
+  else if (side <= 4 * kRLanes) hipLaunchKernelGGL(k_renorm<4>, g, dim3(kRCols * kRLanes), 0, st, pb, a);
+  else hipLaunchKernelGGL(k_renorm<8>, g, dim3(kRCols * kRLanes), 0, st, pb, a);
 }
 
 // Update and re-norm in one kernel for shapes the float4 path cannot take.
@@ -218,11 +253,7 @@ void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st) {
       case 128: hipLaunchKernelGGL((k_update_streamk<128, 128 / mfma_grad_waves(128)>), grid, dim3(256), 0, st, pb, f); break;
       default: hipLaunchKernelGGL((k_update_streamk<256, 256 / mfma_grad_waves(256)>), grid, dim3(256), 0, st, pb, f); break;
     }
-    if (a.renorm) {
-      const int maxcols = pb.hid > pb.d ? pb.hid : pb.d;
-      dim3 g2((maxcols + kCols - 1) / kCols, pb.nm, P);
-      hipLaunchKernelGGL(k_renorm, g2, dim3(kCols * kRLanes), 0, st, pb, a);
-    }
+    if (a.renorm) launch_renorm(pb, a, st);
     return;
   }
   // the flat kernel moves float4s: every matrix base and stride must keep 16-byte alignment
@@ -239,9 +270,7 @@ void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st) {
     UpdateArgs f = a;             // the re-norm pass writes W_out
     for (int i = 0; i < 3; ++i) f.out[i] = nullptr;
     hipLaunchKernelGGL(k_update_flat, grid, dim3(256), 0, st, pb, f);
-    const int maxcols = pb.inner == INNER_LINEAR ? pb.d : (pb.hid > pb.d ? pb.hid : pb.d);
-    dim3 g2((maxcols + kCols - 1) / kCols, pb.nm, P);
-    hipLaunchKernelGGL(k_renorm, g2, dim3(kCols * kRLanes), 0, st, pb, a);
+    launch_renorm(pb, a, st);
     return;
   }
   const int maxcols = pb.inner == INNER_LINEAR ? pb.d : (pb.hid > pb.d ? pb.hid : pb.d);
