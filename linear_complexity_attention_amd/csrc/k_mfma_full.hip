@@ -5,10 +5,12 @@
 // 02), fused per 32-token tile:
 //     K_hat = (K - mu) * rstd                     key instance norm (TvS page)
 //     Z  = K_hat W1,  A = gelu(Z),  V_hat = A W2   forward on the keys
-//     G' = eta_n (V_hat - V) [MSE]  |  -eta_n V [dot]    (the MSE constant 2/(n_b d)
-//                                                       and the scalar eta are
-//                                                       applied to the partials)
-//     dW2 += A^T G',  dA = G' W2^T,  dZ = dA * gelu'(Z),  dW1 += K_hat^T dZ
+//     G' = eta_n (V - V_hat) [MSE]  |  eta_n V [dot]     the negated loss gradient
+//                                                       per token (the sign, the
+//                                                       MSE constant 2/(n_b d) and
+//                                                       the scalar eta are applied
+//                                                       to the partials)
+//     dW2 -= A^T G',  dA = G' W2^T,  dZ = dA * gelu'(Z),  dW1 -= K_hat^T dZ
 // Each wave owns a slice of the hidden units (its slice of Z, A, dA, dZ, dW1,
 // dW2, with the weight fragments of that slice held in registers).  The tiles
 // shared by all waves sit in LDS, XOR-swizzled so that every access is free
@@ -66,8 +68,9 @@ __device__ __forceinline__ bf16x4 ld_tr(const bf16* p) {
 // pre-scaled by sqrt(2)/c, so the MFMA delivers zh; the activation
 // A' = sqrt(2) gelu(Z) is consumed by products whose other operand (or result)
 // carries the compensating 1/sqrt(2).  Two fits (coefficients of v^0, v^1, ...):
-//   GeluFit5: c = 3.5, P and Q of degree 5, max |error| 4.5e-3 on gelu
-//             (|Z| < 4), 2.4e-3 on gelu'; for the gradient kernel;
+//   GeluFitG: c = 3.5, P of degree 4, Q of degree 5, max |error| 5.7e-3 on
+//             gelu (|Z| < 4), 2.4e-3 on gelu'; for the gradient kernel (gelu'
+//             needs the wider clamp point: it approaches 1 only slowly);
 //   GeluFit4: c = 3.125, P of degree 4, max |error| 4.7e-3 on gelu (|Z| < 4);
 //             for the readout, which needs no gelu'.
 // Beyond |Z| = 4 the error is the f16 rounding of the result (relative 1e-3).
@@ -78,10 +81,10 @@ typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 constexpr float kSqrt2 = 1.41421356237f;
 constexpr float kRSqrt2 = 0.70710678119f;
-struct GeluFit5 {
+struct GeluFitG {
   static constexpr float c = 3.5f;
-  static constexpr int NP = 6, NQ = 6;
-  static constexpr float P[6] = {2.442589408f, -1.104925742f, 0.63956925f, -0.372622668f, 0.231905421f, -0.087876027f};
+  static constexpr int NP = 5, NQ = 6;
+  static constexpr float P[5] = {2.440403834f, -1.086301905f, 0.665899315f, -0.464786102f, 0.196728345f};
   static constexpr float Q[6] = {0.764969678f, -0.512306439f, 0.450549349f, -0.42596567f, 0.42093503f, -0.196860224f};
 };
 struct GeluFit4 {
@@ -90,17 +93,18 @@ struct GeluFit4 {
   static constexpr float P[5] = {2.14908049f, -0.897445747f, 0.478055487f, -0.263695363f, 0.094819101f};
   static constexpr float Q[1] = {0.f};
 };
-constexpr float kZScale = kSqrt2 / GeluFit5::c;        // W1 staging scale of the gradient kernel
+constexpr float kZScale = kSqrt2 / GeluFitG::c;         // W1 staging scale of the gradient kernel
 constexpr float kZScaleQ = kSqrt2 / GeluFit4::c;       // ... and of the readout
 __device__ __forceinline__ h2 hh(float x) { return h2{(f16)x, (f16)x}; }
 __device__ __forceinline__ h2 cvt_h2(float x0, float x1) { return __builtin_convertvector(f2{x0, x1}, h2); }
 // The Horner chains of NC element pairs are advanced together: a dependent
 // packed-f16 FMA must wait a cycle after its producer, independent ones need
 // not, so interleaving the chains keeps the VALU issuing every cycle.
-//   z[2c], z[2c+1] = zh of pair c  ->  a[c] = sqrt(2) gelu(Z)  (and gp[c] = gelu'(Z))
-template <class F, int NC, bool GRAD>
-__device__ __forceinline__ void gelu_chains(const float* z, h2* a, h2* gp) {
-  h2 zh[NC], w[NC], v[NC], p[NC], q[NC];
+//   z[2c], z[2c+1] = zh of pair c  ->  a[c] = sqrt(2) gelu(Z)  (and, if wout,
+//   wout[c] = w, from which gelu_deriv_chains gives gelu'(Z))
+template <class F, int NC>
+__device__ __forceinline__ void gelu_chains(const float* z, h2* a, h2* wout) {
+  h2 zh[NC], w[NC], v[NC], p[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) zh[c] = cvt_h2(z[2 * c], z[2 * c + 1]);
 #pragma unroll
@@ -110,25 +114,33 @@ __device__ __forceinline__ void gelu_chains(const float* z, h2* a, h2* gp) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) v[c] = __builtin_elementwise_fma(w[c], w[c], hh(-1.0f));
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
+  for (int c = 0; c < NC; ++c)
     p[c] = __builtin_elementwise_fma(hh(F::P[F::NP - 1] * kRSqrt2), v[c], hh(F::P[F::NP - 2] * kRSqrt2));
-    if constexpr (GRAD) q[c] = __builtin_elementwise_fma(hh(F::Q[F::NQ - 1] * kRSqrt2), v[c], hh(F::Q[F::NQ - 2] * kRSqrt2));
-  }
 #pragma unroll
   for (int k = F::NP - 3; k >= 0; --k)
 #pragma unroll
     for (int c = 0; c < NC; ++c) p[c] = __builtin_elementwise_fma(p[c], v[c], hh(F::P[k] * kRSqrt2));
-  if constexpr (GRAD) {
-#pragma unroll
-    for (int k = F::NQ - 3; k >= 0; --k)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) q[c] = __builtin_elementwise_fma(q[c], v[c], hh(F::Q[k] * kRSqrt2));
-  }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     a[c] = zh[c] * __builtin_elementwise_fma(w[c], p[c], hh(0.5f * F::c));
-    if constexpr (GRAD) gp[c] = __builtin_elementwise_fma(w[c], q[c], hh(0.5f));
+    if (wout) wout[c] = w[c];
   }
+}
+//   w[c] (clamped zh of pair c)  ->  gp[c] = gelu'(Z)
+template <class F, int NC>
+__device__ __forceinline__ void gelu_deriv_chains(const h2* w, h2* gp) {
+  h2 v[NC], q[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) v[c] = __builtin_elementwise_fma(w[c], w[c], hh(-1.0f));
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    q[c] = __builtin_elementwise_fma(hh(F::Q[F::NQ - 1] * kRSqrt2), v[c], hh(F::Q[F::NQ - 2] * kRSqrt2));
+#pragma unroll
+  for (int k = F::NQ - 3; k >= 0; --k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c] = __builtin_elementwise_fma(q[c], v[c], hh(F::Q[k] * kRSqrt2));
+#pragma unroll
+  for (int c = 0; c < NC; ++c) gp[c] = __builtin_elementwise_fma(w[c], q[c], hh(0.5f));
 }
 
 // element-type generic helpers (bf16 or f16 MFMA operands)
@@ -202,11 +214,13 @@ __device__ __forceinline__ int ring(int i) { return __builtin_amdgcn_readfirstla
 // through a three-stage pipeline, one barrier per stage:
 //   phase k, producers: stage K_hat, V, eta of tile k+1 (prefetched a phase
 //            earlier); Z' = K_hat W1 sqrt(2)/c and the packed GELU of tile k
-//            -> A' (At[k%3]) and gelu' (Gp[k%3]); V_hat and G' of tile k-1
+//            -> A' (At[k%3]) and the clamped w (Gp[k%3]); V_hat and G' of tile k-1
 //            (G' -> Gc[(k-1)%2]);
 //   phase k, consumers: backward of tile k-2: dW2 += A'^T G', dA = G' W2^T,
-//            dZ = dA gelu'(Z), dW1 += K_hat^T dZ.
-// Buffers: K tiles x4, V tiles x3, A' x3, gelu' x3, G' x2.
+//            dZ = dA gelu'(Z) (gelu' from w), dW1 += K_hat^T dZ.
+// The gelu' polynomial runs on the consumers: the producers' GELU arithmetic
+// is the critical path, the consumers have slack.
+// Buffers: K tiles x4, V tiles x3, A' x3, w x3, G' x2.
 template <int HID, int LOSS, bool KNORM, int NW>
 __global__ void __launch_bounds__(128 * NW, 1)
 k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float* __restrict__ spart, int S_stats,
@@ -228,7 +242,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
   __shared__ __attribute__((aligned(16))) h2 Gp[NA][NW * NHB * 64 * 4];
   __shared__ __attribute__((aligned(16))) f16 Gc[NG][D * LDT];
   __shared__ float eta_s[NV][TT];
-  __shared__ __attribute__((aligned(16))) float kst[KNORM ? D : 1][2];   // key mean, rstd per channel
+  __shared__ __attribute__((aligned(16))) float kst[KNORM ? D : 1][2];   // key rstd, -mean * rstd per channel
   __shared__ float kpart[KNORM ? 2 * NW : 1][3][KNORM ? D : 1];          // slice groups (count, mean, M2)
 
   const int tid = threadIdx.x;
@@ -258,7 +272,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 
     // ---- segment prologue (all waves): the pair's weights and key statistics.
     // W1 * sqrt(2)/c and W2 / sqrt(2) are staged in LDS, in their natural
-    // [in][out] layouts, over the A' / gelu' buffers (unused until phase 0),
+    // [in][out] layouts, over the A' / w buffers (unused until phase 0),
     // with coalesced 16-byte loads; the producers then take their MFMA
     // fragments with transposing reads.  The key statistics are merged from
     // the per-slice (count, mean, M2) partials with Chan's formula, first by
@@ -268,7 +282,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     KT* w1s = reinterpret_cast<KT*>(&At[0][0]);
     f16* w2s = reinterpret_cast<f16*>(&Gp[0][0]);
     static_assert(D * L1 <= NA * HID * LDT, "W1 staging exceeds the A' buffers");
-    static_assert(HID * L2 <= NA * NW * NHB * 64 * 4 * 2, "W2 staging exceeds the gelu' buffers");
+    static_assert(HID * L2 <= NA * NW * NHB * 64 * 4 * 2, "W2 staging exceeds the w buffers");
     {
       constexpr int NL = D * HID / (NTH * 4);           // float4 loads per thread and matrix
       float4 a1[NL], a2[NL];
@@ -305,7 +319,8 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         *reinterpret_cast<kt4*>(&w1s[c1 * L1 + h1]) =
             kt4{(KT)(a1[j].x * kZScale), (KT)(a1[j].y * kZScale), (KT)(a1[j].z * kZScale), (KT)(a1[j].w * kZScale)};
         *reinterpret_cast<f16x4*>(&w2s[h2_ * L2 + c2]) =
-            f16x4{(f16)(a2[j].x * kRSqrt2), (f16)(a2[j].y * kRSqrt2), (f16)(a2[j].z * kRSqrt2), (f16)(a2[j].w * kRSqrt2)};
+            f16x4{(f16)(a2[j].x * -kRSqrt2), (f16)(a2[j].y * -kRSqrt2), (f16)(a2[j].z * -kRSqrt2),
+                  (f16)(a2[j].w * -kRSqrt2)};
       }
     }
     __syncthreads();
@@ -321,8 +336,13 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           cn2 = nt_;
         }
       }
-      kst[tid][0] = mean2;
-      kst[tid][1] = __builtin_amdgcn_rsqf(m22 / fmaxf(cn2, 1.f) + eps);
+      // K_hat = fma(k, rstd, -mean * rstd) with rstd cut to 16 significant
+      // bits: the product of a bf16 key (8 bits) and rstd is then exact, so a
+      // key equal to a bf16-representable mean (a single token, a constant
+      // channel) normalises to exactly 0, as (k - mean) * rstd does.
+      const float rs = __uint_as_float(__float_as_uint(__builtin_amdgcn_rsqf(m22 / fmaxf(cn2, 1.f) + eps)) & 0xffffff00u);
+      kst[tid][0] = rs;
+      kst[tid][1] = -mean2 * rs;
     }
     if (KNORM) __syncthreads();                        // kst is read by every staging thread
 
@@ -345,7 +365,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       // tb2 = 0, 1 (NW = 4) or tb2 = q / 4 (NW = 8)
       const int cb2 = q & 3;
       auto tbh = [&](int b) { return NB2 == 2 ? b : q >> 2; };
-      // W2 / sqrt(2) as the B operand of V_hat = A' W2 (k = hidden, n = channel): column block cb2
+      // -W2 / sqrt(2) as the B operand of -V_hat = A' (-W2 / sqrt(2)) (k = hidden, n = channel): column block cb2
       f16x8 w2g[LOSS == LOSS_MSE ? NKH : 1];
       if (LOSS == LOSS_MSE) {
 #pragma unroll
@@ -386,20 +406,21 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           vreg = *reinterpret_cast<const stg_t*>(vp + (long long)nn * D + sc);
         }
       };
+      // Rows past the end of the batch keep whatever finite keys and values the
+      // registers hold (zeros, or an earlier tile's): their eta is 0, so their
+      // G' row is 0 and they add exactly nothing to dW1 and dW2.
       auto stage = [&](int i) {
         const int nn = (tile0 + i) * TT + st;
-        const bool live = nn < nt;
-        stgk_t kh;
-        stg_t vv;
+        if constexpr (KNORM) {
+          stgk_t kh;
 #pragma unroll
-        for (int j = 0; j < SCH; ++j) {
-          const float kv = KNORM ? ((float)kreg[j] - kst[sc + j][0]) * kst[sc + j][1] : (float)kreg[j];
-          kh[j] = live ? (KT)kv : (KT)0.f;
-          vv[j] = live ? vreg[j] : (bf16)0.f;
+          for (int j = 0; j < SCH; ++j) kh[j] = (KT)__builtin_fmaf((float)kreg[j], kst[sc + j][0], kst[sc + j][1]);
+          *reinterpret_cast<stgk_t*>(&Kr[ring<NK>(i)][offSt]) = kh;
+        } else {
+          *reinterpret_cast<stg_t*>(&Kr[ring<NK>(i)][offSt]) = kreg;
         }
-        *reinterpret_cast<stgk_t*>(&Kr[ring<NK>(i)][offSt]) = kh;
-        *reinterpret_cast<stg_t*>(&Vr[ring<NV>(i)][offSt]) = vv;
-        if (sc == 0) eta_s[ring<NV>(i)][st] = live ? (ep ? ep[nn] : 1.0f) : 0.0f;
+        *reinterpret_cast<stg_t*>(&Vr[ring<NV>(i)][offSt]) = vreg;
+        if (sc == 0) eta_s[ring<NV>(i)][st] = nn < nt ? (ep ? ep[nn] : 1.0f) : 0.0f;
       };
       // forward of tile i in chunks of two hidden blocks: Z' (MFMA) ...
       constexpr int HB2 = NHB < 2 ? NHB : 2;
@@ -420,7 +441,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
             for (int hb = 0; hb < HB2; ++hb) z[tb][hb] = mfma16(a, w1r[hc + hb][ks], z[tb][hb]);
           }
       };
-      // ... then GELU: A' -> At, gelu' -> Gp
+      // ... then GELU: A' -> At, w -> Gp
       auto fwd_act = [&](int i, int hc, const f32x4 (&z)[2][HB2]) {
         f16* at0 = At[ring<NA>(i)] + offAw0;
         f16* at1 = At[ring<NA>(i)] + offAw1;
@@ -430,7 +451,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           const float zz[8] = {z[0][hb][0], z[0][hb][1], z[0][hb][2], z[0][hb][3],
                                z[1][hb][0], z[1][hb][1], z[1][hb][2], z[1][hb][3]};
           h2 av[4], gp[4];
-          gelu_chains<GeluFit5, 4, true>(zz, av, gp);
+          gelu_chains<GeluFitG, 4>(zz, av, gp);
           *reinterpret_cast<f16x4*>(at0 + 16 * (hc + hb) * LDT) = f16x4{av[0].x, av[0].y, av[1].x, av[1].y};
           *reinterpret_cast<f16x4*>(at1 + 16 * (hc + hb) * LDT) = f16x4{av[2].x, av[2].y, av[3].x, av[3].y};
           h2* gq = gpo + (q * NHB + hc + hb) * 256;
@@ -438,10 +459,12 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
               f16x8{gp[0].x, gp[0].y, gp[1].x, gp[1].y, gp[2].x, gp[2].y, gp[3].x, gp[3].y};
         }
       };
-      // V_hat of tile i, token half tb2, channel block cb2: the MFMA chains ...
+      // V - V_hat of tile i, token half tb2, channel block cb2: two MFMA chains,
+      // one starting from V ...
       auto gp_issue = [&](int i, int tb2, f32x4& v0, f32x4& v1) {
+        const bf16x4 vq = ld_trt(Vr[ring<NV>(i)] + offV + 16 * tb2 * LDK);
         v0 = f32x4{0, 0, 0, 0};
-        v1 = f32x4{0, 0, 0, 0};
+        v1 = f32x4{(float)vq[0], (float)vq[1], (float)vq[2], (float)vq[3]};
         if (LOSS == LOSS_MSE) {
           // A'[t = 16 tb2 + r][h = 32 ks + 8 g + j]
           const f16* alo = At[ring<NA>(i)] + offTr[tb2][0];
@@ -455,14 +478,13 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           }
         }
       };
-      // ... and G' = eta (V_hat - V) [MSE] or -eta V [dot] -> Gc
+      // ... and G' = eta (V - V_hat) [MSE] or eta V [dot] -> Gc.  A full tile
+      // without per-token rates has eta = 1 on every row.
       auto gp_fin = [&](int i, int tb2, const f32x4& v0, const f32x4& v1) {
-        const bf16x4 vq = ld_trt(Vr[ring<NV>(i)] + offV + 16 * tb2 * LDK);
-        f32x4 gv;
+        f32x4 gv = v0 + v1;
+        if (ep || (tile0 + i + 1) * TT > nt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = eta_s[ring<NV>(i)][16 * tb2 + 4 * g + j];
-          gv[j] = LOSS == LOSS_MSE ? e * ((v0[j] + v1[j]) - (float)vq[j]) : -e * (float)vq[j];
+          for (int j = 0; j < 4; ++j) gv[j] *= eta_s[ring<NV>(i)][16 * tb2 + 4 * g + j];
         }
         *reinterpret_cast<f16x4*>(Gc[ring<NG>(i)] + (tb2 ? offGc1 : offGc0)) = pack4h(gv);
       };
@@ -574,10 +596,12 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
               for (int tb = 0; tb < 2; ++tb) da[tb] = mfma16(ga[ks][tb], w2r[hb][ks], da[tb]);
-            const f16x8 gpv = *reinterpret_cast<const f16x8*>(gpi + (q * NHB + hb) * 256);
-            const h2 g0{gpv[0], gpv[1]}, g1{gpv[2], gpv[3]}, g2{gpv[4], gpv[5]}, g3{gpv[6], gpv[7]};
-            const h2 d0 = cvt_h2(da[0][0], da[0][1]) * g0, d1 = cvt_h2(da[0][2], da[0][3]) * g1;
-            const h2 d2 = cvt_h2(da[1][0], da[1][1]) * g2, d3 = cvt_h2(da[1][2], da[1][3]) * g3;
+            const f16x8 wv = *reinterpret_cast<const f16x8*>(gpi + (q * NHB + hb) * 256);
+            const h2 wc[4] = {h2{wv[0], wv[1]}, h2{wv[2], wv[3]}, h2{wv[4], wv[5]}, h2{wv[6], wv[7]}};
+            h2 gd[4];
+            gelu_deriv_chains<GeluFitG, 4>(wc, gd);
+            const h2 d0 = cvt_h2(da[0][0], da[0][1]) * gd[0], d1 = cvt_h2(da[0][2], da[0][3]) * gd[1];
+            const h2 d2 = cvt_h2(da[1][0], da[1][1]) * gd[2], d3 = cvt_h2(da[1][2], da[1][3]) * gd[3];
             dz[hb][0] = (KT)(float)d0.x; dz[hb][1] = (KT)(float)d0.y; dz[hb][2] = (KT)(float)d1.x;
             dz[hb][3] = (KT)(float)d1.y; dz[hb][4] = (KT)(float)d2.x; dz[hb][5] = (KT)(float)d2.y;
             dz[hb][6] = (KT)(float)d3.x; dz[hb][7] = (KT)(float)d3.y;
@@ -600,13 +624,14 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       // stored in register order: float4 ((q*4 + cb)*NHB + hb)*64 + lane holds
       // dW1[16cb + 4g + i][h0 + 16hb + r], float4 ((q*NHB + hb)*4 + cb)*64 + lane
       // holds dW2[h0 + 16hb + 4g + i][16cb + r] (i = 0..3), so every store
-      // instruction writes 1 KB contiguously.  (acc2 holds A'^T G' = sqrt(2) A^T G'.)
+      // instruction writes 1 KB contiguously.  (acc2 holds A'^T G' = sqrt(2) A^T G';
+      // G' is the negated gradient, hence the negative scales.)
       f32x4* out = reinterpret_cast<f32x4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
-      const float scale2 = scale * kRSqrt2;
+      const float scale1 = -scale, scale2 = -scale * kRSqrt2;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) out[((q * 4 + cb) * NHB + hb) * 64 + lane] = scale * acc1[cb][hb];
+        for (int hb = 0; hb < NHB; ++hb) out[((q * 4 + cb) * NHB + hb) * 64 + lane] = scale1 * acc1[cb][hb];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
@@ -726,7 +751,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
           const float zz[8] = {z[0][tb][0], z[0][tb][1], z[0][tb][2], z[0][tb][3],
                                z[1][tb][0], z[1][tb][1], z[1][tb][2], z[1][tb][3]};
           h2 x[4];
-          gelu_chains<GeluFit4, 4, false>(zz, x, nullptr);
+          gelu_chains<GeluFit4, 4>(zz, x, nullptr);
           ab[tb] = f16x8{x[0].x, x[0].y, x[1].x, x[1].y, x[2].x, x[2].y, x[3].x, x[3].y};
         }
 #pragma unroll

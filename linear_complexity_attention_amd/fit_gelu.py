@@ -65,7 +65,7 @@ def fits(c, deg_p, deg_q=None):
 
 
 if __name__ == "__main__":
-    for name, c, dp, dq in (("GeluFit5 (gradient)", 3.5, 5, 5), ("GeluFit4 (readout)", 3.125, 4, None)):
+    for name, c, dp, dq in (("GeluFitG (gradient)", 3.5, 4, 5), ("GeluFit4 (readout)", 3.125, 4, None)):
         P, Q = fits(c, dp, dq)
         ea, eg = f16_errors(c, P, Q)
         print(f"{name}: c = {c}")
