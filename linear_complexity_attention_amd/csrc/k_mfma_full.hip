@@ -197,6 +197,9 @@ __device__ __forceinline__ int tok_col(int t) { return t < 16 ? 8 * (t >> 2) + (
 
 // producer (and consumer) waves of the gradient kernel for hidden width HID
 template <int HID> constexpr int kGradWaves = mfma_grad_waves(HID);
+// workgroups per CU: at width 64 the kernel fits twice (both its LDS and, under
+// this bound, its registers), at 128 and 256 once
+template <int HID> constexpr int kGradBlocksPerCU = HID == 64 ? 2 : 1;
 
 // Index of tile i's buffer in a ring of N.  Taken through readfirstlane so
 // that the compiler treats it as an opaque uniform value: otherwise loop
@@ -205,6 +208,17 @@ template <int N>
 __device__ __forceinline__ int ring(int i) { return __builtin_amdgcn_readfirstlane(i % N); }
 
 // ---------------------------------------------------------------------------
+// Chan et al.'s pairwise combination of (count, mean, M2) statistics: fold
+// (nb, mb, m2b) into (cn, mean, m2); empty parts are skipped.
+__device__ __forceinline__ void chan_merge(float& cn, float& mean, float& m2, float nb, float mb, float m2b) {
+  if (nb > 0.f) {
+    const float nt = cn + nb, delta = mb - mean, f = nb * __builtin_amdgcn_rcpf(nt);
+    mean += delta * f;
+    m2 += m2b + delta * delta * cn * f;
+    cn = nt;
+  }
+}
+
 // Fused forward/backward of one update batch, producer/consumer form.
 //
 // A workgroup has 2 NW waves: NW producers and NW consumers (NW = 4 or 8);
@@ -222,7 +236,7 @@ __device__ __forceinline__ int ring(int i) { return __builtin_amdgcn_readfirstla
 // is the critical path, the consumers have slack.
 // Buffers: K tiles x4, V tiles x3, A' x3, w x3, G' x2.
 template <int HID, int LOSS, bool KNORM, int NW>
-__global__ void __launch_bounds__(128 * NW, 1)
+__global__ void __launch_bounds__(128 * NW, kGradBlocksPerCU<HID> * NW / 2)   // threads, waves per SIMD
 k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float* __restrict__ spart, int S_stats,
             float eps, float* __restrict__ part) {
   typedef typename std::conditional<KNORM, f16, bf16>::type KT;
@@ -243,7 +257,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
   __shared__ __attribute__((aligned(16))) f16 Gc[NG][D * LDT];
   __shared__ float eta_s[NV][TT];
   __shared__ __attribute__((aligned(16))) float kst[KNORM ? D : 1][2];   // key rstd, -mean * rstd per channel
-  __shared__ float kpart[KNORM ? 2 * NW : 1][3][KNORM ? D : 1];          // slice groups (count, mean, M2)
+  __shared__ float kpart[KNORM ? NTH / 64 : 1][3][KNORM ? D : 1];       // slice groups (count, mean, M2)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -268,16 +282,32 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
     const long long seg_end = end < (long long)(p + 1) * tpp ? end : (long long)(p + 1) * tpp;
     const int n = (int)(seg_end - x);                 // tiles of this segment
     const float* W1 = W.mat(0, bb, hh_);
-    const float* W2 = W.mat(1, bb, hh_);
+
+    // producer staging: thread -> (token row st, channels sc .. sc + SCH - 1) of a
+    // tile; tile 0's keys and values are loaded first, under the prologue
+    typedef __bf16 stg_t __attribute__((ext_vector_type(SCH)));
+    const int st = tid / (D / SCH), sc = (tid % (D / SCH)) * SCH;
+    const bf16* kp = (const bf16*)pb.k + ((long long)p * pb.N + t0) * D;
+    const bf16* vp = (const bf16*)pb.v + ((long long)p * pb.N + t0) * D;
+    stg_t kreg = {}, vreg = {};
+    auto prefetch = [&](int i) {              // segment-relative tile i
+      const int nn = (tile0 + i) * TT + st;
+      if (i < n && nn < nt) {
+        kreg = *reinterpret_cast<const stg_t*>(kp + (long long)nn * D + sc);
+        vreg = *reinterpret_cast<const stg_t*>(vp + (long long)nn * D + sc);
+      }
+    };
+    if (producer) prefetch(0);
 
     // ---- segment prologue (all waves): the pair's weights and key statistics.
-    // W1 * sqrt(2)/c and W2 / sqrt(2) are staged in LDS, in their natural
+    // W1 * sqrt(2)/c and -W2 / sqrt(2) are staged in LDS, in their natural
     // [in][out] layouts, over the A' / w buffers (unused until phase 0),
     // with coalesced 16-byte loads; the producers then take their MFMA
-    // fragments with transposing reads.  The key statistics are merged from
-    // the per-slice (count, mean, M2) partials with Chan's formula, first by
-    // 2 NW groups of 64 threads (slices s = group, group + 2 NW, ...), then by
-    // one thread per channel.
+    // fragments with transposing reads, the consumers theirs with plain
+    // 16-byte reads.  The key statistics are merged from the per-slice
+    // (count, mean, M2) partials with Chan's formula, first by 2 NW groups of
+    // 64 threads (slices s = group, group + 2 NW, ...), then by one thread per
+    // channel.
     constexpr int L1 = HID + 16, L2 = 80;                // row strides of the staged W1, W2
     KT* w1s = reinterpret_cast<KT*>(&At[0][0]);
     f16* w2s = reinterpret_cast<f16*>(&Gp[0][0]);
@@ -289,22 +319,23 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         a1[j] = reinterpret_cast<const float4*>(W1)[tid + NTH * j];
-        a2[j] = reinterpret_cast<const float4*>(W2)[tid + NTH * j];
+        a2[j] = reinterpret_cast<const float4*>(W.mat(1, bb, hh_))[tid + NTH * j];
       }
-      float cn = 0.f, mean = 0.f, m2 = 0.f;
-      if (KNORM) {
+      if (KNORM) {                    // slices grp, grp + NG, ...: loads of 4 slices in flight at once
+        constexpr int NG = NTH / 64, U = 4;
         const int c = tid & 63, grp = tid >> 6;
-        const float* sp = spart + (long long)p * S_stats * 3 * D;
-        for (int sl = grp; sl < S_stats; sl += 2 * NW) {
-          const float* o = sp + (long long)sl * 3 * D;
-          const float nb = o[c], mb = o[D + c], m2b = o[2 * D + c];
-          const float nt_ = cn + nb;
-          if (nb > 0.f) {
-            const float delta = mb - mean, f = nb / nt_;
-            mean += delta * f;
-            m2 += m2b + delta * delta * cn * f;
-            cn = nt_;
+        const float* sp = spart + (long long)p * S_stats * 3 * D + c;
+        float cn = 0.f, mean = 0.f, m2 = 0.f;
+        for (int s0 = grp; s0 < S_stats; s0 += NG * U) {
+          float nb[U], mb[U], m2b[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int sl = s0 + NG * u;
+            nb[u] = 0.f; mb[u] = 0.f; m2b[u] = 0.f;
+            if (sl < S_stats) { nb[u] = sp[sl * 3 * D]; mb[u] = sp[sl * 3 * D + D]; m2b[u] = sp[sl * 3 * D + 2 * D]; }
           }
+#pragma unroll
+          for (int u = 0; u < U; ++u) chan_merge(cn, mean, m2, nb[u], mb[u], m2b[u]);
         }
         kpart[grp][0][c] = cn;
         kpart[grp][1][c] = mean;
@@ -323,26 +354,18 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
                   (f16)(a2[j].w * -kRSqrt2)};
       }
     }
-    __syncthreads();
+    __syncthreads();                                   // staged weights, slice-group statistics
     if (KNORM && tid < D) {
-      float cn2 = 0.f, mean2 = 0.f, m22 = 0.f;
+      float cn = 0.f, mean = 0.f, m2 = 0.f;
 #pragma unroll
-      for (int gi = 0; gi < 2 * NW; ++gi) {
-        const float nb = kpart[gi][0][tid];
-        if (nb > 0.f) {
-          const float nt_ = cn2 + nb, delta = kpart[gi][1][tid] - mean2, f = nb / nt_;
-          mean2 += delta * f;
-          m22 += kpart[gi][2][tid] + delta * delta * cn2 * f;
-          cn2 = nt_;
-        }
-      }
+      for (int gi = 0; gi < NTH / 64; ++gi) chan_merge(cn, mean, m2, kpart[gi][0][tid], kpart[gi][1][tid], kpart[gi][2][tid]);
       // K_hat = fma(k, rstd, -mean * rstd) with rstd cut to 16 significant
       // bits: the product of a bf16 key (8 bits) and rstd is then exact, so a
       // key equal to a bf16-representable mean (a single token, a constant
       // channel) normalises to exactly 0, as (k - mean) * rstd does.
-      const float rs = __uint_as_float(__float_as_uint(__builtin_amdgcn_rsqf(m22 / fmaxf(cn2, 1.f) + eps)) & 0xffffff00u);
+      const float rs = __uint_as_float(__float_as_uint(__builtin_amdgcn_rsqf(m2 / fmaxf(cn, 1.f) + eps)) & 0xffffff00u);
       kst[tid][0] = rs;
-      kst[tid][1] = -mean2 * rs;
+      kst[tid][1] = -mean * rs;
     }
     if (KNORM) __syncthreads();                        // kst is read by every staging thread
 
@@ -351,7 +374,6 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       // issue priority over the consumer of the same SIMD: the producer's GELU
       // waits on its own Z' MFMAs, which must not queue behind the consumer's
       __builtin_amdgcn_s_setprio(2);
-      const int st = tid / (D / SCH), sc = (tid % (D / SCH)) * SCH;   // staging: token row, first channel
       // W1' as the B operand of Z' = K_hat W1' (k = channel, n = hidden)
       k8 w1r[NHB][2];
 #pragma unroll
@@ -374,12 +396,8 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           w2g[ks] = cat44(ld_trt(&w2s[row * L2 + col]), ld_trt(&w2s[(row + 4) * L2 + col]));
         }
       }
-      const bf16* kp = (const bf16*)pb.k + ((long long)p * pb.N + t0) * D;
-      const bf16* vp = (const bf16*)pb.v + ((long long)p * pb.N + t0) * D;
       const float* ep = pb.eta_tok ? pb.eta_tok + (long long)p * pb.N + t0 : nullptr;
-      typedef __bf16 stg_t __attribute__((ext_vector_type(SCH)));
       typedef KT stgk_t __attribute__((ext_vector_type(SCH)));
-      stg_t kreg = {}, vreg = {};
       // per-lane LDS offsets (elements), the same for every tile; what varies
       // with the tile, the hidden block or the k-step is a uniform addend
       const int r4 = r >> 2, r3 = r & 3;
@@ -399,13 +417,6 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       const int offV = (4 * g + r4) * LDK + ((16 * cb2 + 4 * r3) ^ kswz(4 * g + r4));   // V reads (+16 tb2 LDK)
       const int offGc0 = (16 * cb2 + r) * LDT + ((8 * g) ^ tswz(r));          // G' writes, tb2 = 0
       const int offGc1 = (16 * cb2 + r) * LDT + ((8 * g + 4) ^ tswz(r));      // tb2 = 1
-      auto prefetch = [&](int i) {              // segment-relative tile i
-        const int nn = (tile0 + i) * TT + st;
-        if (i < n && nn < nt) {
-          kreg = *reinterpret_cast<const stg_t*>(kp + (long long)nn * D + sc);
-          vreg = *reinterpret_cast<const stg_t*>(vp + (long long)nn * D + sc);
-        }
-      };
       // Rows past the end of the batch keep whatever finite keys and values the
       // registers hold (zeros, or an earlier tile's): their eta is 0, so their
       // G' row is 0 and they add exactly nothing to dW1 and dW2.
@@ -489,7 +500,6 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         *reinterpret_cast<f16x4*>(Gc[ring<NG>(i)] + (tb2 ? offGc1 : offGc0)) = pack4h(gv);
       };
 
-      prefetch(0);
       stage(0);
       prefetch(1);
       __syncthreads();
@@ -529,15 +539,13 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       __syncthreads();
     } else {
       // ---------------- consumer ----------------
-      f16x8 w2r[NHB][2];   // W2 as the B operand of dA = G' W2^T (k = channel, n = hidden)
+      // -W2 / sqrt(2) as the B operand of dA' = G' (-W2 / sqrt(2))^T (k = channel, n = hidden),
+      // from the staged copy (overwritten from phase 0 on)
+      f16x8 w2r[NHB][2];
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const float4* p2 = reinterpret_cast<const float4*>(W2 + (h0 + 16 * hb + r) * D + 32 * ks + 8 * g);
-          const float4 a = p2[0], b = p2[1];
-          w2r[hb][ks] = f16x8{(f16)a.x, (f16)a.y, (f16)a.z, (f16)a.w, (f16)b.x, (f16)b.y, (f16)b.z, (f16)b.w};
-        }
+        for (int ks = 0; ks < 2; ++ks) w2r[hb][ks] = *reinterpret_cast<const f16x8*>(&w2s[(h0 + 16 * hb + r) * L2 + 32 * ks + 8 * g]);
       f32x4 acc1[4][NHB], acc2[NHB][4];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -579,7 +587,8 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
             for (int cb = 0; cb < 4; ++cb) acc2[hb][cb] = mfma16(aa, gb[cb], acc2[hb][cb]);
           }
         }
-        // pass 2: dA = G' W2^T (G' as the A operand: m = token, k = channel), dZ = dA gelu'(Z)
+        // pass 2: dA' = G' (-W2 / sqrt(2))^T (G' as the A operand: m = token, k = channel),
+        // dZ' = dA' gelu'(Z)
         k8 dz[NHB];
         {
           f16x8 ga[2][2];
@@ -624,10 +633,11 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       // stored in register order: float4 ((q*4 + cb)*NHB + hb)*64 + lane holds
       // dW1[16cb + 4g + i][h0 + 16hb + r], float4 ((q*NHB + hb)*4 + cb)*64 + lane
       // holds dW2[h0 + 16hb + 4g + i][16cb + r] (i = 0..3), so every store
-      // instruction writes 1 KB contiguously.  (acc2 holds A'^T G' = sqrt(2) A^T G';
-      // G' is the negated gradient, hence the negative scales.)
+      // instruction writes 1 KB contiguously.  With G' the negated gradient,
+      // acc2 holds A'^T G' = -sqrt(2) A^T G and acc1 holds K_hat^T dZ' =
+      // K_hat^T dZ / sqrt(2).
       f32x4* out = reinterpret_cast<f32x4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
-      const float scale1 = -scale, scale2 = -scale * kRSqrt2;
+      const float scale1 = scale * kSqrt2, scale2 = -scale * kRSqrt2;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -666,8 +676,8 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
   constexpr int NTHR = QW * 64;
   constexpr int L1 = HID + 16;           // [c][h] row stride (16 mod 128: conflict-free transposed reads)
   constexpr int L2 = 80;                 // [h][c] row stride
-  __shared__ __attribute__((aligned(16))) bf16 w1s[D * L1];
-  __shared__ __attribute__((aligned(16))) f16 w2s[HID * L2];
+  __shared__ __attribute__((aligned(16))) bf16 w1b[2][D * L1];
+  __shared__ __attribute__((aligned(16))) f16 w2b[2][HID * L2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int N = pb.N;
@@ -677,32 +687,74 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
   long long t = (long long)L * T / G;
   const long long t_end = (long long)(L + 1) * T / G;
 
-  while (t < t_end) {
-    const int p = (int)(t / N);
-    const int n0 = (int)(t - (long long)p * N);
-    const int c = n0 / span;
-    const int n1 = (int)min((long long)min(N, (c + 1) * span), n0 + (t_end - t));
-    // full batch reads state 1 (after the update); causal chunk c reads state c
-    const int state = chunk ? c : 1;
-    const int bb = p / pb.H, hh_ = p % pb.H;
-    const float *W1, *W2;
-    if (state == 0) { W1 = w0.mat(0, bb, hh_); W2 = w0.mat(1, bb, hh_); }
-    else {
-      const float* base = states + (state - 1) * state_stride + (long long)p * 2 * D * HID;
-      W1 = base; W2 = base + (long long)D * HID;
-    }
-    __syncthreads();                     // the previous state's LDS reads are done
-    for (int e = tid * 4; e < HID * D; e += NTHR * 4) {
-      const float4 a = *reinterpret_cast<const float4*>(W1 + e);
-      const float4 b = *reinterpret_cast<const float4*>(W2 + e);
+  // segment of the range starting at token tt: pair p, tokens [n0, n1) of it,
+  // all read from one state (full batch: state 1, after the update; causal
+  // chunk c: state c)
+  struct Seg { int p, n0, n1, state; };
+  auto seg_at = [&](long long tt) {
+    Seg sg;
+    sg.p = (int)(tt / N);
+    sg.n0 = (int)(tt - (long long)sg.p * N);
+    const int c = sg.n0 / span;
+    sg.n1 = (int)min((long long)min(N, (c + 1) * span), sg.n0 + (t_end - tt));
+    sg.state = chunk ? c : 1;
+    return sg;
+  };
+  auto wptr = [&](const Seg& sg, int m) -> const float* {
+    if (sg.state == 0) return w0.mat(m, sg.p / pb.H, sg.p % pb.H);
+    return states + (sg.state - 1) * state_stride + (long long)sg.p * 2 * D * HID + (long long)m * D * HID;
+  };
+  // the weights of up to two segments are staged in LDS (two buffers), their
+  // loads in flight together: a range that crosses a pair boundary pays one
+  // staging latency, not two
+  constexpr int NL = HID * D / (NTHR * 4);       // float4 loads per thread and matrix
+  static_assert(HID * D % (NTHR * 4) == 0, "weights split evenly over the threads");
+  auto stage_store = [&](int buf, const float4 (&a)[NL], const float4 (&b)[NL]) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int e = 4 * (tid + NTHR * j);
       const int c1 = e / HID, h1 = e % HID;         // W1 [c][h]
       const int h2_ = e / D, c2 = e % D;             // W2 [h][c]
-      *reinterpret_cast<bf16x4*>(&w1s[c1 * L1 + h1]) =
-          bf16x4{(bf16)(a.x * kZScaleQ), (bf16)(a.y * kZScaleQ), (bf16)(a.z * kZScaleQ), (bf16)(a.w * kZScaleQ)};
-      *reinterpret_cast<f16x4*>(&w2s[h2_ * L2 + c2]) =
-          f16x4{(f16)(b.x * kRSqrt2), (f16)(b.y * kRSqrt2), (f16)(b.z * kRSqrt2), (f16)(b.w * kRSqrt2)};
+      *reinterpret_cast<bf16x4*>(&w1b[buf][c1 * L1 + h1]) = bf16x4{
+          (bf16)(a[j].x * kZScaleQ), (bf16)(a[j].y * kZScaleQ), (bf16)(a[j].z * kZScaleQ), (bf16)(a[j].w * kZScaleQ)};
+      *reinterpret_cast<f16x4*>(&w2b[buf][h2_ * L2 + c2]) =
+          f16x4{(f16)(b[j].x * kRSqrt2), (f16)(b[j].y * kRSqrt2), (f16)(b[j].z * kRSqrt2), (f16)(b[j].w * kRSqrt2)};
     }
+  };
+  auto stage_load = [&](const Seg& sg, float4 (&a)[NL], float4 (&b)[NL]) {
+    const float4* W1 = reinterpret_cast<const float4*>(wptr(sg, 0));
+    const float4* W2 = reinterpret_cast<const float4*>(wptr(sg, 1));
+#pragma unroll
+    for (int j = 0; j < NL; ++j) { a[j] = W1[tid + NTHR * j]; b[j] = W2[tid + NTHR * j]; }
+  };
+  if (t < t_end) {
+    const Seg s0 = seg_at(t);
+    const long long t1 = t + (s0.n1 - s0.n0);
+    float4 a0[NL], b0[NL], a1[NL], b1[NL];
+    stage_load(s0, a0, b0);
+    if (t1 < t_end) stage_load(seg_at(t1), a1, b1);
+    stage_store(0, a0, b0);
+    if (t1 < t_end) stage_store(1, a1, b1);
     __syncthreads();
+  }
+
+  for (int si = 0; t < t_end; ++si) {
+    const Seg sg = seg_at(t);
+    const int p = sg.p, n0 = sg.n0, n1 = sg.n1;
+    const int buf = si & 1;
+    if (si >= 2) {                       // third and later segments: stage in place
+      float4 a[NL], b[NL];
+      stage_load(sg, a, b);
+      __syncthreads();                   // every wave is done with segment si - 2
+      stage_store(buf, a, b);
+      __syncthreads();
+    }
+    // the segment's work, with the buffer a compile-time constant (LDS
+    // addresses stay lane offset + immediate)
+    auto segment = [&](auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const bf16* w1s = w1b[BUF];
+    const f16* w2s = w2b[BUF];
 
     const int units = (n1 - n0 + 15) >> 4;
     const int a_ = n0 + 16 * (w * units / QW);
@@ -790,6 +842,9 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
         for (int ks = 0; ks < 2; ++ks) qc[tb][ks] = qn[tb][ks];
       pos = nxt;
     }
+    };
+    if (buf == 0) segment(std::integral_constant<int, 0>{});
+    else segment(std::integral_constant<int, 1>{});
     t += n1 - n0;
   }
 }
@@ -831,7 +886,7 @@ void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_pe
   const int tpp = (nt + TT - 1) / TT;
   *tiles_per_pair = tpp;
   const long long total = (long long)P * tpp;
-  long long g = (long long)device_cu_count() * (pb.hid == 64 ? 2 : 1);   // width 64 fits twice per CU
+  long long g = (long long)device_cu_count() * (pb.hid == 64 ? kGradBlocksPerCU<64> : 1);
   if (g > total) g = total;
   *G = (int)g;
   const long long per = (total + g - 1) / g;
