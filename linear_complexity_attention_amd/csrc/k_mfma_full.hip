@@ -778,7 +778,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = f32x4{0, 0, 0, 0};
-#pragma unroll 2
+#pragma unroll
       for (int hc = 0; hc < HID / 32; ++hc) {
         f32x4 z[2][NTB];
 #pragma unroll
