@@ -268,11 +268,10 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
   const int h0 = q * HP;
   const int P = pb.B * pb.H;
   const int tpp = (nt + TT - 1) / TT;
-  const long long total = (long long)P * tpp;
-  const long long G = gridDim.x;
-  const long long begin = (long long)blockIdx.x * total / G;
-  const long long end = (long long)(blockIdx.x + 1) * total / G;
-  const int p_first = (int)(begin / tpp);
+  const long long G = gridDim.x, C = (long long)P * (tpp + kSkAlpha);
+  const long long begin = sk_tile_at((long long)blockIdx.x * C / G, tpp);
+  const long long end = sk_tile_at((long long)(blockIdx.x + 1) * C / G, tpp);
+  const int p_first = (int)sk_first_pair(blockIdx.x, G, C, tpp);
 
   long long x = begin;
   while (x < end) {
@@ -889,8 +888,9 @@ void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_pe
   long long g = (long long)device_cu_count() * (pb.hid == 64 ? kGradBlocksPerCU<64> : 1);
   if (g > total) g = total;
   *G = (int)g;
-  const long long per = (total + g - 1) / g;
-  *J = (int)((per + tpp - 1) / tpp + 1);
+  // a range of ceil(C / G) line units touches at most this many pairs
+  const long long U = tpp + kSkAlpha, per = ((long long)P * U + g - 1) / g;
+  *J = (int)((per + U - 1) / U + 1);
 }
 
 void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, float scale, const float* spart,

@@ -19,12 +19,14 @@ constexpr int kCols = 64;
 constexpr int kLanes = 4;                        // row lanes per column (re-norm kernel)
 
 // first and last workgroup of the stream-K gradient kernel that touched pair p
+// (the workgroups holding its first and last tile on the cost line), and the
+// line length C
 __device__ __forceinline__ void sk_range(const UpdateArgs& a, int P, int p, long long& q0, long long& q1,
-                                         long long& total) {
-  total = (long long)P * a.sk_tpp;
-  const long long xa = (long long)p * a.sk_tpp, xb = xa + a.sk_tpp - 1;
-  q0 = ((xa + 1) * a.sk_G - 1) / total;
-  q1 = ((xb + 1) * a.sk_G - 1) / total;
+                                         long long& C) {
+  const long long U = a.sk_tpp + kSkAlpha;
+  C = (long long)P * U;
+  q0 = sk_group_of(p * U + kSkAlpha, a.sk_G, C);
+  q1 = sk_group_of(p * U + kSkAlpha + a.sk_tpp - 1, a.sk_G, C);
 }
 
 __device__ __forceinline__ void mat_dims(const Problem& pb, int i, int& rows, int& cols) {
@@ -52,10 +54,10 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
     const float* pp = a.part + (size_t)p * wsz;
     for (int s = 0; s < a.S; ++s) sub(pp + s * a.part_pair_stride);
   } else {
-    long long q0, q1, total;
-    sk_range(a, pb.B * pb.H, p, q0, q1, total);
+    long long q0, q1, C;
+    sk_range(a, pb.B * pb.H, p, q0, q1, C);
     for (long long q = q0; q <= q1; ++q) {
-      const long long first = ((q * total) / a.sk_G) / a.sk_tpp;
+      const long long first = sk_first_pair(q, a.sk_G, C, a.sk_tpp);
       sub(a.part + (q * a.sk_J + (p - first)) * wsz);
     }
   }
@@ -92,11 +94,11 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
     step = D;
   }
   const long long wsz = 2LL * D * HID;
-  long long q0, q1, total;
-  sk_range(a, pb.B * pb.H, p, q0, q1, total);
+  long long q0, q1, C;
+  sk_range(a, pb.B * pb.H, p, q0, q1, C);
   float4 sum = {0.f, 0.f, 0.f, 0.f};
   for (long long q = q0; q <= q1; ++q) {
-    const long long first = ((q * total) / a.sk_G) / a.sk_tpp;
+    const long long first = sk_first_pair(q, a.sk_G, C, a.sk_tpp);
     const float4 d = reinterpret_cast<const float4*>(a.part + (q * a.sk_J + (p - first)) * wsz)[j];
     sum.x += d.x; sum.y += d.y; sum.z += d.z; sum.w += d.w;
   }
@@ -200,8 +202,8 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, Up
   const float* w0 = a.w0.mat(i, b, h);
   const long long wsz = (long long)pb.nm * pb.msz;
   float* nxt = a.next + (size_t)p * wsz + (size_t)i * pb.msz;
-  long long q0 = 0, q1 = -1, total = 0;
-  if (a.part_mode == PART_STREAMK) sk_range(a, pb.B * pb.H, p, q0, q1, total);
+  long long q0 = 0, q1 = -1, C = 1;
+  if (a.part_mode == PART_STREAMK) sk_range(a, pb.B * pb.H, p, q0, q1, C);
   __shared__ float red[2][kLanes][kCols];
   float nn = 0.f, nr = 0.f;
   if (live)
@@ -213,7 +215,7 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, Up
         for (int s = 0; s < a.S; ++s) w -= pp[s * a.part_pair_stride];
       } else {
         for (long long q = q0; q <= q1; ++q) {
-          const long long first = ((q * total) / a.sk_G) / a.sk_tpp;
+          const long long first = sk_first_pair(q, a.sk_G, C, a.sk_tpp);
           w -= a.part[(q * a.sk_J + (p - first)) * wsz + (size_t)i * pb.msz + e];
         }
       }

@@ -58,6 +58,25 @@ struct UpdateArgs {
   int renorm;
 };
 enum { PART_SPLITS = 0, PART_STREAMK = 1 };
+
+// Stream-K split of the MFMA gradient kernel.  The (pair, 32-token tile) space
+// is laid on a cost line on which pair p occupies U = tpp + kSkAlpha units: a
+// prologue slot of kSkAlpha units (the cost of staging a pair's weights and
+// statistics, in tiles) followed by its tpp tiles.  Workgroup q of G takes the
+// line range [q C / G, (q + 1) C / G), C = P U, i.e. the tiles in it: ranges
+// that cross a pair boundary, and so pay a second prologue, get fewer tiles.
+constexpr int kSkAlpha = 6;
+// flattened tile index (pair * tpp + tile) of the first tile at or after line position u
+__host__ __device__ inline long long sk_tile_at(long long u, int tpp) {
+  const long long U = tpp + kSkAlpha, p = u / U, t = u % U - kSkAlpha;
+  return p * tpp + (t > 0 ? t : 0);
+}
+// workgroup whose line range holds position u
+__host__ __device__ inline long long sk_group_of(long long u, long long G, long long C) { return ((u + 1) * G - 1) / C; }
+// first pair of workgroup q's range (its partial slot j holds pair first + j)
+__host__ __device__ inline long long sk_first_pair(long long q, long long G, long long C, int tpp) {
+  return (q * C / G) / (tpp + kSkAlpha);
+}
 void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st);
 
 // ---- MFMA fast paths --------------------------------------------------------
