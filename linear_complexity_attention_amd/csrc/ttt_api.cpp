@@ -90,6 +90,14 @@ int choose_splits(long long other_blocks, int tokens, int per_block_min, int tar
   return (int)s;
 }
 
+int stats_splits(long long pairs, int tokens) {
+  long long s = 4LL * device_cu_count() / pairs;
+  const long long maxs = (tokens + 63) / 64;
+  if (s > maxs) s = maxs;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
 int check_request(ttt_handle* h, int loss, int inner, int chunk) {
   const ttt_config& c = h->cfg;
   if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT) return fail(h, TTT_ERR_INVALID, "unknown loss %d", loss);
@@ -139,7 +147,9 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk) {
   pl.mfma_query = !generic_only && mfma_query_supported(pb);
   pl.lact_grad = !generic_only && !c.key_norm && lact_supported(pb);
   pl.lact_query = !generic_only && lact_readout_supported(pb);
-  pl.S_stats = c.key_norm ? choose_splits(pl.P, c.N, 64, 1024) : 0;
+  // key-stat slices: at most 4 workgroups per CU in total, so that all of them
+  // run in one round (a partial second round would idle most of the chip)
+  pl.S_stats = c.key_norm ? stats_splits(pl.P, c.N) : 0;
   if (pl.lact_grad) {
     pl.S_grad = lact_grad_splits(pb, pl.span);
   } else if (pl.mfma_grad) {
