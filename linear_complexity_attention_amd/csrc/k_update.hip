@@ -29,6 +29,13 @@ __device__ __forceinline__ void sk_range(const UpdateArgs& a, int P, int p, long
   q1 = sk_group_of(p * U + kSkAlpha + a.sk_tpp - 1, a.sk_G, C);
 }
 
+// partial slot of pair p written by workgroup q (q0 <= q <= q1): a workgroup
+// after q0 starts inside p, so p is its first pair (slot q J); q0 may have
+// started in an earlier pair
+__device__ __forceinline__ long long sk_slot(const UpdateArgs& a, int p, long long q, long long q0, long long C) {
+  return q * a.sk_J + (q == q0 ? p - sk_first_pair(q0, a.sk_G, C, a.sk_tpp) : 0);
+}
+
 __device__ __forceinline__ void mat_dims(const Problem& pb, int i, int& rows, int& cols) {
   if (pb.inner == INNER_LINEAR) { rows = pb.d; cols = pb.d; return; }
   if (i == 1) { rows = pb.hid; cols = pb.d; }   // W2 [h, d]
@@ -56,10 +63,7 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
   } else {
     long long q0, q1, C;
     sk_range(a, pb.B * pb.H, p, q0, q1, C);
-    for (long long q = q0; q <= q1; ++q) {
-      const long long first = sk_first_pair(q, a.sk_G, C, a.sk_tpp);
-      sub(a.part + (q * a.sk_J + (p - first)) * wsz);
-    }
+    for (long long q = q0; q <= q1; ++q) sub(a.part + sk_slot(a, p, q, q0, C) * wsz);
   }
   *reinterpret_cast<float4*>(a.next + (size_t)p * wsz + e) = w;
   if (a.out[i]) *reinterpret_cast<float4*>(a.out[i] + (size_t)p * pb.msz + o) = w;
@@ -96,11 +100,16 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
   const long long wsz = 2LL * D * HID;
   long long q0, q1, C;
   sk_range(a, pb.B * pb.H, p, q0, q1, C);
+  // the pair's slots, four loads in flight at a time, added in workgroup order
   float4 sum = {0.f, 0.f, 0.f, 0.f};
-  for (long long q = q0; q <= q1; ++q) {
-    const long long first = sk_first_pair(q, a.sk_G, C, a.sk_tpp);
-    const float4 d = reinterpret_cast<const float4*>(a.part + (q * a.sk_J + (p - first)) * wsz)[j];
-    sum.x += d.x; sum.y += d.y; sum.z += d.z; sum.w += d.w;
+  for (long long q = q0; q <= q1; q += 4) {
+    float4 d[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q + u <= q1) d[u] = reinterpret_cast<const float4*>(a.part + sk_slot(a, p, q + u, q0, C) * wsz)[j];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q + u <= q1) { sum.x += d[u].x; sum.y += d[u].y; sum.z += d[u].z; sum.w += d[u].w; }
   }
   const float* cur = a.cur.mat(mat, b, h);
   float* nxt = a.next + (size_t)p * wsz + (size_t)mat * D * HID;
@@ -214,10 +223,7 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, Up
         const float* pp = a.part + (size_t)p * wsz + (size_t)i * pb.msz + e;
         for (int s = 0; s < a.S; ++s) w -= pp[s * a.part_pair_stride];
       } else {
-        for (long long q = q0; q <= q1; ++q) {
-          const long long first = sk_first_pair(q, a.sk_G, C, a.sk_tpp);
-          w -= a.part[(q * a.sk_J + (p - first)) * wsz + (size_t)i * pb.msz + e];
-        }
+        for (long long q = q0; q <= q1; ++q) w -= a.part[sk_slot(a, p, q, q0, C) * wsz + (size_t)i * pb.msz + e];
       }
       nxt[e] = w;
       nn += w * w;
