@@ -653,12 +653,13 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 // ---------------------------------------------------------------------------
 // O = gelu(Q W1*) W2* with tokens on the MFMA n axis.
 //
-// One workgroup of 16 waves per CU.  The (pair, token) space is cut into equal
-// contiguous ranges, one per workgroup; a range covers one or two weight
-// states (pair, chunk).  For each state the workgroup stages the weights in
-// LDS in their natural layouts (read transposed by the MFMA operand loads) and
-// splits its tokens over the waves in 16-token units, so every wave gets the
-// same work to within 16 tokens.  A wave walks its tokens 32 at a time (16 for
+// One workgroup per CU (16 waves; 8 at width 64).  The (pair, token) space is
+// cut into equal contiguous ranges, one per workgroup; a range covers one or
+// more weight states (pair, chunk).  The workgroup stages each state's weights
+// in LDS in their natural layouts (read transposed by the MFMA operand loads),
+// the first two at once into two buffers, and splits the state's tokens over
+// the waves in 16-token units, so every wave gets the same work to within 16
+// tokens.  A wave walks its tokens 32 at a time (64 at width 64; shorter for
 // the last piece) and prefetches the next piece's Q while computing.
 //
 // The first product runs on bf16 (Q is bf16); the second on f16, fed straight
@@ -668,10 +669,15 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 // W2 is staged scaled by 1/sqrt(2) to compensate.
 // Workgroup -> range mapping is XCD-aware: consecutive ranges (which share a
 // pair's weights) are given to workgroups of the same XCD.
-constexpr int QW = 16;                  // waves per workgroup
+// waves per workgroup and 16-token blocks per pass: 16 waves of 32-token passes
+// at widths 128 and 256; 8 waves of 64-token passes at width 64, where a pass
+// is short and the wider one keeps more Q loads in flight (measured)
+template <int HID> constexpr int kQW = HID == 64 ? 8 : 16;
+template <int HID> constexpr int kQTB = HID == 64 ? 4 : 2;
 template <int HID>
-__global__ void __launch_bounds__(QW * 64, 1)
+__global__ void __launch_bounds__(kQW<HID> * 64, 1)
 k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long state_stride, int chunk, int span) {
+  constexpr int QW = kQW<HID>, QTB = kQTB<HID>;
   constexpr int NTHR = QW * 64;
   constexpr int L1 = HID + 16;           // [c][h] row stride (16 mod 128: conflict-free transposed reads)
   constexpr int L2 = 80;                 // [h][c] row stride
@@ -760,9 +766,9 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
     const int b_ = min(n1, n0 + 16 * ((w + 1) * units / QW));
     const bf16* qp = (const bf16*)pb.q + (long long)p * N * D;
     bf16* op = (bf16*)pb.o + (long long)p * N * D;
-    auto load_q = [&](int pos, bf16x8 (&q)[2][2]) {
+    auto load_q = [&](int pos, bf16x8 (&q)[QTB][2]) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < QTB; ++tb)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int n = pos + 16 * tb + r;
@@ -770,7 +776,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
         }
     };
     // one pass over NTB 16-token blocks starting at pos
-    auto pass = [&](auto ntb_c, int pos, const bf16x8 (&q)[2][2]) {
+    auto pass = [&](auto ntb_c, int pos, const bf16x8 (&q)[QTB][2]) {
       constexpr int NTB = decltype(ntb_c)::value;
       f32x4 o[4][NTB];
 #pragma unroll
@@ -825,18 +831,25 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
         }
       }
     };
-    bf16x8 qc[2][2];
+    bf16x8 qc[QTB][2];
     int pos = a_;
     if (pos < b_) load_q(pos, qc);
     while (pos < b_) {
-      const int take = b_ - pos > 16 ? 32 : 16;
+      const int rem = b_ - pos;
+      const int take = rem > 16 * (QTB - 1) ? 16 * QTB : (rem > 16 ? 32 : 16);
       const int nxt = pos + take;
-      bf16x8 qn[2][2];
+      bf16x8 qn[QTB][2];
       if (nxt < b_) load_q(nxt, qn);     // prefetch the next piece
-      if (take == 32) pass(std::integral_constant<int, 2>{}, pos, qc);
-      else pass(std::integral_constant<int, 1>{}, pos, qc);
+      if constexpr (QTB == 4) {
+        if (take == 64) pass(std::integral_constant<int, 4>{}, pos, qc);
+        else if (take == 32) pass(std::integral_constant<int, 2>{}, pos, qc);
+        else pass(std::integral_constant<int, 1>{}, pos, qc);
+      } else {
+        if (take == 32) pass(std::integral_constant<int, 2>{}, pos, qc);
+        else pass(std::integral_constant<int, 1>{}, pos, qc);
+      }
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < QTB; ++tb)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) qc[tb][ks] = qn[tb][ks];
       pos = nxt;
@@ -914,9 +927,9 @@ void launch_mfma_query(const Problem& pb, const WRef& w0, const float* states, l
   if (G > (T + 511) / 512) G = (T + 511) / 512;
   if (G < 1) G = 1;
   switch (pb.hid) {
-    case 64: hipLaunchKernelGGL((k_mfma_query<64>), dim3((unsigned)G), dim3(QW * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
-    case 128: hipLaunchKernelGGL((k_mfma_query<128>), dim3((unsigned)G), dim3(QW * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
-    default: hipLaunchKernelGGL((k_mfma_query<256>), dim3((unsigned)G), dim3(QW * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
+    case 64: hipLaunchKernelGGL((k_mfma_query<64>), dim3((unsigned)G), dim3(kQW<64> * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
+    case 128: hipLaunchKernelGGL((k_mfma_query<128>), dim3((unsigned)G), dim3(kQW<128> * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
+    default: hipLaunchKernelGGL((k_mfma_query<256>), dim3((unsigned)G), dim3(kQW<256> * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
   }
 }
 
