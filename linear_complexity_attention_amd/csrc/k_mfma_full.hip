@@ -241,7 +241,6 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
             float eps, float* __restrict__ part) {
   typedef typename std::conditional<KNORM, f16, bf16>::type KT;
   typedef typename Vec<KT>::v8 k8;
-  typedef typename Vec<KT>::v4 k4;
   constexpr int NTH = 128 * NW;        // threads
   constexpr int HP = HID / NW;         // hidden units per producer / consumer
   constexpr int NHB = HP / 16;         // 16-wide hidden blocks per wave

@@ -88,9 +88,11 @@ void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st);
 bool mfma_full_supported(const Problem& pb);
 // producer (= consumer) waves of the gradient kernel for hidden width hid; the
 // hidden units are split over them in slices of hid / mfma_grad_waves(hid).
-// (8 + 8 waves at width 256 measured 5 % slower than 4 + 4: the extra reads of
-// the shared LDS tiles cost more than the added latency hiding.)
-constexpr int mfma_grad_waves(int hid) { return hid >= 64 ? 4 : 4; }
+// Measured alternatives at width 256: 8 + 8 waves ran 5 % slower (the extra
+// reads of the shared LDS tiles cost more than the added latency hiding), and
+// 4 producers + 8 consumers (the consumers also computing V_hat) 2.2x slower
+// (at three waves per SIMD the consumers spill registers).
+constexpr int mfma_grad_waves(int /*hid*/) { return 4; }
 void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_per_pair);
 void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, float scale, const float* spart,
                            int S_stats, float eps, float* part, hipStream_t st);
