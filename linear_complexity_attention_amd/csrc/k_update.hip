@@ -141,7 +141,8 @@ __global__ void __launch_bounds__(kRCols * kRLanes) k_renorm(Problem pb, UpdateA
   const bool live = j < cols;
   const float* w0 = a.w0.mat(i, b, h);
   float* nxt = a.next + ((size_t)p * pb.nm + i) * pb.msz;
-  __shared__ float red[2][kRLanes][kRCols];
+  constexpr int kWaves = kRCols * kRLanes / 64;   // each wave holds 4 row lanes of every column
+  __shared__ float red[2][kWaves][kRCols];
   float v[RMAX];
   float nn = 0.f, nr = 0.f;
 #pragma unroll
@@ -163,12 +164,16 @@ __global__ void __launch_bounds__(kRCols * kRLanes) k_renorm(Problem pb, UpdateA
       nn += x * x;
       nr += w0v * w0v;
     }
-  red[0][lane][cl] = nn;
-  red[1][lane][cl] = nr;
+  // column sums: the 4 row lanes of a column inside a wave (wave lanes cl,
+  // cl + 16, cl + 32, cl + 48), then the waves through LDS
+  nn += __shfl_xor(nn, 16); nr += __shfl_xor(nr, 16);
+  nn += __shfl_xor(nn, 32); nr += __shfl_xor(nr, 32);
+  if ((lane & 3) == 0) { red[0][lane >> 2][cl] = nn; red[1][lane >> 2][cl] = nr; }
   __syncthreads();
   if (!live) return;
   float sn = 0.f, sr = 0.f;
-  for (int l = 0; l < kRLanes; ++l) { sn += red[0][l][cl]; sr += red[1][l][cl]; }
+#pragma unroll
+  for (int l = 0; l < kWaves; ++l) { sn += red[0][l][cl]; sr += red[1][l][cl]; }
   const float scale = sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f);
   float* out = a.out[i] ? a.out[i] + (size_t)p * pb.msz : nullptr;
 #pragma unroll
