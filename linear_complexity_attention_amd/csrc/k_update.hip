@@ -57,9 +57,17 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
     const float4 d = *reinterpret_cast<const float4*>(q + e);
     w.x -= d.x; w.y -= d.y; w.z -= d.z; w.w -= d.w;
   };
-  if (a.part_mode == PART_SPLITS) {
+  if (a.part_mode == PART_SPLITS) {           // four splits' loads in flight, subtracted in split order
     const float* pp = a.part + (size_t)p * wsz;
-    for (int s = 0; s < a.S; ++s) sub(pp + s * a.part_pair_stride);
+    for (int s = 0; s < a.S; s += 4) {
+      float4 d[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (s + u < a.S) d[u] = *reinterpret_cast<const float4*>(pp + (s + u) * a.part_pair_stride + e);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (s + u < a.S) { w.x -= d[u].x; w.y -= d[u].y; w.z -= d[u].z; w.w -= d[u].w; }
+    }
   } else {
     long long q0, q1, C;
     sk_range(a, pb.B * pb.H, p, q0, q1, C);
