@@ -111,23 +111,30 @@ k_lact_grad(Problem pb, WRef W, int t0, int nt, int S, float scale, float* __res
   const bf16* vp = (const bf16*)pb.v + ((long long)p * pb.N + t0) * D;
   const float* ep = pb.eta_tok ? pb.eta_tok + (long long)p * pb.N + t0 : nullptr;
 
-  for (int tt = n0; tt < n1; tt += TT) {
-    // ---- stage K, V ([token][channel]) and the per-token rates
-    {
-      const int n = tt + st;
-      const bool live = n < n1;
+  // K, V and the per-token rate of this thread's staging row, one tile ahead
+  // (one wave per SIMD: nothing else would hide the load latency)
+  bf16x8 kv[SCH / 8], vv[SCH / 8];
+  float ev = 0.f;
+  auto fetch = [&](int tt) {
+    const int n = tt + st;
+    const bool live = tt < n1 && n < n1;
 #pragma unroll
-      for (int u = 0; u < SCH / 8; ++u) {
-        bf16x8 kv = {}, vv = {};
-        if (live) {
-          kv = ld8(kp + (long long)n * D + sc + 8 * u);
-          vv = ld8(vp + (long long)n * D + sc + 8 * u);
-        }
-        *reinterpret_cast<bf16x8*>(&Kr[st * LDK + sc + 8 * u]) = kv;
-        *reinterpret_cast<bf16x8*>(&Vr[st * LDK + sc + 8 * u]) = vv;
-      }
-      if (sc == 0) eta_s[st] = live ? (ep ? ep[n] : 1.0f) : 0.0f;
+    for (int u = 0; u < SCH / 8; ++u) {
+      kv[u] = live ? ld8(kp + (long long)n * D + sc + 8 * u) : bf16x8{};
+      vv[u] = live ? ld8(vp + (long long)n * D + sc + 8 * u) : bf16x8{};
     }
+    if (sc == 0) ev = live ? (ep ? ep[n] : 1.0f) : 0.0f;
+  };
+  fetch(n0);
+  for (int tt = n0; tt < n1; tt += TT) {
+    // ---- stage K, V ([token][channel]) and the per-token rates, fetch the next tile
+#pragma unroll
+    for (int u = 0; u < SCH / 8; ++u) {
+      *reinterpret_cast<bf16x8*>(&Kr[st * LDK + sc + 8 * u]) = kv[u];
+      *reinterpret_cast<bf16x8*>(&Vr[st * LDK + sc + 8 * u]) = vv[u];
+    }
+    if (sc == 0) eta_s[st] = ev;
+    fetch(tt + TT);
     __syncthreads();
 
     // ---- Z1 = K W1, Z3 = K W3, dHv = V W2^T (this wave's 16 hidden units)
