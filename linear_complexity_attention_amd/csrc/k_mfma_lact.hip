@@ -227,10 +227,15 @@ k_lact_readout(Problem pb, WRef w0, const float* __restrict__ states, long long 
   __shared__ __attribute__((aligned(16))) bf16 w1s[D * L1];
   __shared__ __attribute__((aligned(16))) bf16 w3s[D * L1];
   __shared__ __attribute__((aligned(16))) bf16 w2s[HH * L2];
-  const int p = blockIdx.y;
+  // XCD-aware work mapping: workgroups are dealt to the 8 XCDs round-robin, so
+  // the work index L gives consecutive L (the groups of one (pair, chunk),
+  // which read the same weight state) to workgroups of one XCD and its L2
+  const int nb = gridDim.x * gridDim.y, bid = blockIdx.y * gridDim.x + blockIdx.x;
+  const int L = nb % 8 == 0 ? (bid % 8) * (nb / 8) + bid / 8 : bid;
+  const int p = L / gridDim.x, bx = L % gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int c = blockIdx.x / groups, grp = blockIdx.x % groups;
+  const int c = bx / groups, grp = bx % groups;
   const int c0 = c * span;
   const int n0 = c0 + grp * (RW * RTOK);
   const int n1 = min(min(pb.N, c0 + span), n0 + RW * RTOK);
