@@ -789,6 +789,9 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int tb = 0; tb < NTB; ++tb) z[u][tb] = f32x4{0, 0, 0, 0};
+        // issue priority while this wave has MFMAs to issue, so that the MFMA
+        // pipe is fed ahead of the other waves' GELU arithmetic (measured: 2 %)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -801,6 +804,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
             for (int tb = 0; tb < NTB; ++tb) z[u][tb] = mfma16(a, q[tb][ks], z[u][tb]);
           }
         // activation operand: hidden k-slots j < 4 -> u = 0, i = j; j >= 4 -> u = 1, i = j - 4
+        __builtin_amdgcn_s_setprio(0);
         f16x8 ab[NTB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
@@ -810,6 +814,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
           gelu_chains<GeluFit4, 4>(zz, x, nullptr);
           ab[tb] = f16x8{x[0].x, x[0].y, x[1].x, x[1].y, x[2].x, x[2].y, x[3].x, x[3].y};
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           // W2^T operand: W2[h = 32 hc + tau(g, j)][c = 16 cb + r]
