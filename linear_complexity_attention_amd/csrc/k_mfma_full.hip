@@ -67,13 +67,25 @@ __device__ __forceinline__ bf16x4 ld_tr(const bf16* p) {
 // instruction and no transcendental.  The weights that produce Z are staged
 // pre-scaled by sqrt(2)/c, so the MFMA delivers zh; the activation
 // A' = sqrt(2) gelu(Z) is consumed by products whose other operand (or result)
-// carries the compensating 1/sqrt(2).  Two fits (coefficients of v^0, v^1, ...):
+// carries the compensating 1/sqrt(2).
+// Where no w is needed (the readout), the same P is evaluated on the
+// unclamped zh and the clamp moves to the output, where the last FMA's clamp
+// bit does it for free:
+//     Phi(Z) = clamp01(1/2 + zh P(zh^2 - 1) / (sqrt(2) c)),  zh Phi(Z) = (sqrt(2)/c) gelu(Z).
+// Beyond the fit interval the degree-9 odd polynomial leaves [0, 1] with the
+// sign of Z and never comes back (checked for every finite f16 zh; once v^k
+// overflows, the infinities carry that sign), so Phi is exactly 0 or 1 there.
+// Two fits (coefficients of v^0, v^1, ...):
 //   GeluFitG: c = 3.5, P of degree 4, Q of degree 5, max |error| 5.7e-3 on
-//             gelu (|Z| < 4), 2.4e-3 on gelu'; for the gradient kernel (gelu'
-//             needs the wider clamp point: it approaches 1 only slowly);
-//   GeluFit4: c = 3.125, P of degree 4, max |error| 4.7e-3 on gelu (|Z| < 4);
-//             for the readout, which needs no gelu'.
-// Beyond |Z| = 4 the error is the f16 rounding of the result (relative 1e-3).
+//             gelu (|Z| < 4; beyond, the result's relative error is 1e-3),
+//             2.4e-3 on gelu'; for the gradient kernel (gelu' needs the wider
+//             clamp point: it approaches 1 only slowly);
+//   GeluFit4: c = 3.125, P of degree 4, output clamp, max |error| 2.6e-3 on
+//             gelu beyond the f16 rounding of the result (relative 5e-4),
+//             over every finite f16 zh; for the readout, which needs no gelu'.
+// The gradient kernel keeps the input clamp: its w feeds gelu' as well, and
+// packed max and min issue slower than an FMA (measured), so moving the clamp
+// of w to the waves that evaluate gelu' cost more than it saved.
 typedef _Float16 f16;
 typedef f16 h2 __attribute__((ext_vector_type(2)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
@@ -95,6 +107,7 @@ struct GeluFit4 {
 };
 constexpr float kZScale = kSqrt2 / GeluFitG::c;         // W1 staging scale of the gradient kernel
 constexpr float kZScaleQ = kSqrt2 / GeluFit4::c;       // ... and of the readout
+constexpr float kW2ScaleQ = 1.f / kZScaleQ;            // W2 staging scale of the readout (c/sqrt(2))
 __device__ __forceinline__ h2 hh(float x) { return h2{(f16)x, (f16)x}; }
 __device__ __forceinline__ h2 cvt_h2(float x0, float x1) { return __builtin_convertvector(f2{x0, x1}, h2); }
 // The Horner chains of NC element pairs are advanced together: a dependent
@@ -124,6 +137,30 @@ __device__ __forceinline__ void gelu_chains(const float* z, h2* a, h2* wout) {
   for (int c = 0; c < NC; ++c) {
     a[c] = zh[c] * __builtin_elementwise_fma(w[c], p[c], hh(0.5f * F::c));
     if (wout) wout[c] = w[c];
+  }
+}
+//   z[2c], z[2c+1] = zh of pair c  ->  a[c] = (sqrt(2)/c) gelu(Z), output-clamped form
+template <class F, int NC>
+__device__ __forceinline__ void gelu_chains_oc(const float* z, h2* a) {
+  constexpr float s = kRSqrt2 / F::c;
+  h2 zh[NC], v[NC], p[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) zh[c] = cvt_h2(z[2 * c], z[2 * c + 1]);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) v[c] = __builtin_elementwise_fma(zh[c], zh[c], hh(-1.0f));
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    p[c] = __builtin_elementwise_fma(hh(F::P[F::NP - 1] * s), v[c], hh(F::P[F::NP - 2] * s));
+#pragma unroll
+  for (int k = F::NP - 3; k >= 0; --k)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) p[c] = __builtin_elementwise_fma(p[c], v[c], hh(F::P[k] * s));
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    // max-then-min against 0 and 1 becomes the FMA's clamp bit
+    const h2 phi = __builtin_elementwise_min(
+        __builtin_elementwise_max(__builtin_elementwise_fma(zh[c], p[c], hh(0.5f)), hh(0.f)), hh(1.f));
+    a[c] = zh[c] * phi;
   }
 }
 //   w[c] (clamped zh of pair c)  ->  gp[c] = gelu'(Z)
@@ -663,9 +700,8 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 //
 // The first product runs on bf16 (Q is bf16); the second on f16, fed straight
 // from the packed-f16 GELU: W1 is staged scaled by sqrt(2)/c, so the MFMA
-// yields zh = sqrt(2) Z / c, and with w = clamp(zh, +-sqrt(2)), v = w^2 - 1
-//     c Phi(Z) = c/2 + w P(v) / sqrt(2),   zh * c Phi(Z) = sqrt(2) gelu(Z);
-// W2 is staged scaled by 1/sqrt(2) to compensate.
+// yields zh = sqrt(2) Z / c, and the output-clamped GELU gives zh Phi(Z) =
+// (sqrt(2)/c) gelu(Z); W2 is staged scaled by c/sqrt(2) to compensate.
 // Workgroup -> range mapping is XCD-aware: consecutive ranges (which share a
 // pair's weights) are given to workgroups of the same XCD.
 // waves per workgroup and 16-token blocks per pass: 16 waves of 32-token passes
@@ -722,7 +758,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
       *reinterpret_cast<bf16x4*>(&w1b[buf][c1 * L1 + h1]) = bf16x4{
           (bf16)(a[j].x * kZScaleQ), (bf16)(a[j].y * kZScaleQ), (bf16)(a[j].z * kZScaleQ), (bf16)(a[j].w * kZScaleQ)};
       *reinterpret_cast<f16x4*>(&w2b[buf][h2_ * L2 + c2]) =
-          f16x4{(f16)(b[j].x * kRSqrt2), (f16)(b[j].y * kRSqrt2), (f16)(b[j].z * kRSqrt2), (f16)(b[j].w * kRSqrt2)};
+          f16x4{(f16)(b[j].x * kW2ScaleQ), (f16)(b[j].y * kW2ScaleQ), (f16)(b[j].z * kW2ScaleQ), (f16)(b[j].w * kW2ScaleQ)};
     }
   };
   auto stage_load = [&](const Seg& sg, float4 (&a)[NL], float4 (&b)[NL]) {
@@ -811,7 +847,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
           const float zz[8] = {z[0][tb][0], z[0][tb][1], z[0][tb][2], z[0][tb][3],
                                z[1][tb][0], z[1][tb][1], z[1][tb][2], z[1][tb][3]};
           h2 x[4];
-          gelu_chains<GeluFit4, 4>(zz, x, nullptr);
+          gelu_chains_oc<GeluFit4, 4>(zz, x);
           ab[tb] = f16x8{x[0].x, x[0].y, x[1].x, x[1].y, x[2].x, x[2].y, x[3].x, x[3].y};
         }
         __builtin_amdgcn_s_setprio(1);

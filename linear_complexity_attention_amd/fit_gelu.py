@@ -6,7 +6,12 @@ v = w^2 - 1, the kernels evaluate
 in f16 Horner form.  P and Q are Lawson (iteratively reweighted least squares,
 converging to minimax) fits on v in [-1, 1]; the errors printed here are those
 of the f16 evaluation the kernels perform (fma in one rounding, RNE
-conversions), over Z in [-4, 4].  Run: python fit_gelu.py
+conversions), over Z in [-4, 4].
+The readout evaluates the same P on the unclamped zh and clamps the output:
+    Phi(Z) = clamp01(1/2 + zh P(zh^2 - 1) / (sqrt(2) c)),   A = zh Phi(Z).
+For that form the error is taken over every finite f16 value of zh (the part
+beyond the f16 rounding of the result, relative 2^-11), and the values that
+do not clamp and the NaN results are counted.  Run: python fit_gelu.py
 """
 import numpy as np
 from scipy.special import erf
@@ -58,6 +63,27 @@ def f16_errors(c, P, Q=None):
     return err_a, err_g
 
 
+def f16_errors_out_clamp(c, P):
+    h = np.float16
+    fma = lambda a, b, cc: (a.astype(np.float64) * b.astype(np.float64) + np.float64(cc)).astype(h)
+    zh = np.arange(65536, dtype=np.uint16).view(h)
+    zh = zh[np.isfinite(zh)]                           # every finite f16 zh
+    z = zh.astype(np.float64) * c / np.sqrt(2.0)
+    s = np.sqrt(0.5) / c
+    with np.errstate(over="ignore", invalid="ignore"):
+        v = fma(zh, zh, h(-1.0))                       # +inf for |zh| > 256
+        acc = np.full_like(v, h(P[-1] * s))
+        for k in range(len(P) - 2, -1, -1):
+            acc = fma(acc, v, h(P[k] * s))
+        phi = fma(zh, acc, h(0.5)).astype(np.float64)
+    n_nan = int(np.isnan(phi).sum())
+    z_open = np.abs(z[(phi > 0.0) & (phi < 1.0)]).max()  # beyond it Phi is exactly 0 or 1
+    phi = np.clip(phi, 0.0, 1.0)
+    a = (zh.astype(np.float64) * phi).astype(h).astype(np.float64) * c / np.sqrt(2.0)
+    g = z * cdf(z)
+    return (np.abs(a - g) - np.abs(g) * 2.0 ** -11).max(), z_open, n_nan
+
+
 def fits(c, deg_p, deg_q=None):
     P = lawson(lambda w0: (c * cdf(c * w0) - c / 2.0) / w0, deg_p, c)
     Q = None if deg_q is None else lawson(lambda w0: (cdf(c * w0) + c * w0 * pdf(c * w0) - 0.5) / w0, deg_q, 1.0)
@@ -73,3 +99,7 @@ if __name__ == "__main__":
         if Q is not None:
             print("  Q =", np.array2string(Q, precision=9, separator=", "))
         print(f"  max |error| gelu {ea:.2e}" + ("" if eg is None else f", gelu' {eg:.2e}"))
+        if Q is None:
+            eo, zo, nn = f16_errors_out_clamp(c, P)
+            print(f"  output-clamped form: max |error| gelu {eo:.2e} beyond the result's rounding,"
+                  f" Phi exactly 0 or 1 for |Z| > {zo:.3f}, NaN results: {nn}")
