@@ -263,10 +263,10 @@ __device__ __forceinline__ void chan_merge(float& cn, float& mean, float& m2, fl
 // SIMD (waves w and w + 4 land on the same SIMD), so the producer's VALU-heavy
 // GELU and the consumer's MFMA-heavy weight-gradient products overlap there.  Tiles of 32 tokens flow
 // through a three-stage pipeline, one barrier per stage:
-//   phase k, producers: stage K_hat, V, eta of tile k+1 (prefetched a phase
-//            earlier); Z' = K_hat W1 sqrt(2)/c and the packed GELU of tile k
+//   phase k, producers: Z' = K_hat W1 sqrt(2)/c and the packed GELU of tile k
 //            -> A' (At[k%3]) and the clamped w (Gp[k%3]); V_hat and G' of tile k-1
-//            (G' -> Gc[(k-1)%2]);
+//            (G' -> Gc[(k-1)%2]); then stage K_hat, V, eta of tile k+1 (loaded
+//            from the end of the phase before) and request tile k+2;
 //   phase k, consumers: backward of tile k-2: dW2 += A'^T G', dA = G' W2^T,
 //            dZ = dA gelu'(Z) (gelu' from w), dW1 += K_hat^T dZ.
 // The gelu' polynomial runs on the consumers: the producers' GELU arithmetic
@@ -538,19 +538,19 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       stage(0);
       prefetch(1);
       __syncthreads();
-      // phase 0: forward of tile 0
-      if (1 < n) { stage(1); prefetch(2); }
+      // phase 0: forward of tile 0.  Each phase stages the next tile at its end,
+      // from loads issued at the end of the phase before (a whole phase earlier)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         f32x4 z[2][HB2];
         fwd_gemm(0, c * HB2, z);
         fwd_act(0, c * HB2, z);
       }
+      if (1 < n) { stage(1); prefetch(2); }
       __syncthreads();
       // phases 1 .. n-1: forward of tile k interleaved with V_hat / G' of tile k-1,
       // so that the V_hat MFMA chains run under the GELU arithmetic
       for (int k = 1; k < n; ++k) {
-        if (k + 1 < n) { stage(k + 1); prefetch(k + 2); }
         f32x4 va0, va1, vb0, vb1;
         f32x4 z[2][HB2];
         fwd_gemm(k, 0, z);
@@ -561,6 +561,7 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         if (NB2 > 1) gp_issue(k - 1, tbh(1), vb0, vb1);
         if (NCH > 1) fwd_act(k, HB2, z);
         if (NB2 > 1) gp_fin(k - 1, tbh(1), vb0, vb1);
+        if (k + 1 < n) { stage(k + 1); prefetch(k + 2); }
         __syncthreads();
       }
       // phase n: V_hat / G' of the last tile; phase n+1: the consumers' last backward
