@@ -144,6 +144,24 @@ def test_shapes_mlp_mse(d, hidden, N):
     _check_pairs(w, dev_in, exact, [(0, 0), (0, 1)], tag=f"shape d={d} h={hidden} N={N}")
 
 
+# the remaining kernel instances and the largest widths: SwiGLU at (d, h) =
+# (64, 256) and (128, 128) (the LaCT kernels' other two shapes), the generic
+# path at h = 512 (the widest supported) and the linear model at d = 128
+@pytest.mark.parametrize("inner,loss,d,hidden,chunk,renorm,path", [
+    ("swiglu", "dot", 64, 256, 100, True, "mfma_swiglu"),
+    ("swiglu", "dot", 128, 128, 128, True, "mfma_swiglu"),
+    ("mlp_gelu", "mse", 64, 512, 0, False, "generic"),
+    ("linear", "mse", 128, 128, 0, False, "generic"),
+])
+def test_shapes_other_kernels(inner, loss, d, hidden, chunk, renorm, path):
+    w = Workload("shape2", B=1, H=2, N=300, d=d, hidden=hidden, inner=inner, loss=loss, chunk=chunk,
+                 key_norm=(chunk == 0), renorm=renorm, per_token_eta=(loss == "dot"), unit_columns=renorm,
+                 seed=11 + d + hidden, eta=0.3 if loss == "dot" else 1.0)
+    dev_in, exact = device_inputs(w)
+    _, _, got = _check_pairs(w, dev_in, exact, [(0, 0), (0, 1)], tag=f"{inner} d={d} h={hidden} chunk={chunk}")
+    assert got == path
+
+
 def test_large_eta_exposes_backward():
     """100x the step: the update dominates O, so an error in dW shows in O."""
     w = Workload("eta100", B=2, H=2, N=1000, d=64, hidden=256, seed=31, eta=100.0)
