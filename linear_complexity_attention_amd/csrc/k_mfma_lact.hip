@@ -267,15 +267,31 @@ k_lact_readout(Problem pb, WRef w0, const float* __restrict__ states, long long 
   for (int half = 0; half < HID / HH; ++half) {
     const int hb0 = half * HH;
     if (half) __syncthreads();
-    for (int e = tid * 4; e < D * HH; e += NTHR * 4) {
-      const int cc = e / HH, hx = e % HH;                      // W1, W3 [c][h] rows
-      const float4 a = *reinterpret_cast<const float4*>(W1 + cc * HID + hb0 + hx);
-      const float4 b = *reinterpret_cast<const float4*>(W3 + cc * HID + hb0 + hx);
-      *reinterpret_cast<bf16x4*>(&w1s[cc * L1 + hx]) = bf16x4{(bf16)a.x, (bf16)a.y, (bf16)a.z, (bf16)a.w};
-      *reinterpret_cast<bf16x4*>(&w3s[cc * L1 + hx]) = bf16x4{(bf16)b.x, (bf16)b.y, (bf16)b.z, (bf16)b.w};
-      const int hy = e / D, cy = e % D;                        // W2 [h][c] rows
-      const float4 m = *reinterpret_cast<const float4*>(W2 + (long long)(hb0 + hy) * D + cy);
-      *reinterpret_cast<bf16x4*>(&w2s[hy * L2 + cy]) = bf16x4{(bf16)m.x, (bf16)m.y, (bf16)m.z, (bf16)m.w};
+    // the half's weights, in batches of SB float4 per matrix and thread: the
+    // loads of a batch are all in flight before the first conversion waits
+    constexpr int NIT = D * HH / (NTHR * 4), SB = NIT < 4 ? NIT : 4;
+    static_assert(D * HH % (NTHR * 4) == 0 && NIT % SB == 0, "staging splits evenly");
+#pragma unroll
+    for (int k0 = 0; k0 < NIT; k0 += SB) {
+      float4 a[SB], b[SB], m[SB];
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int e = tid * 4 + (k0 + k) * NTHR * 4;
+        const int cc = e / HH, hx = e % HH;                    // W1, W3 [c][h] rows
+        const int hy = e / D, cy = e % D;                      // W2 [h][c] rows
+        a[k] = *reinterpret_cast<const float4*>(W1 + cc * HID + hb0 + hx);
+        b[k] = *reinterpret_cast<const float4*>(W3 + cc * HID + hb0 + hx);
+        m[k] = *reinterpret_cast<const float4*>(W2 + (long long)(hb0 + hy) * D + cy);
+      }
+#pragma unroll
+      for (int k = 0; k < SB; ++k) {
+        const int e = tid * 4 + (k0 + k) * NTHR * 4;
+        const int cc = e / HH, hx = e % HH;
+        const int hy = e / D, cy = e % D;
+        *reinterpret_cast<bf16x4*>(&w1s[cc * L1 + hx]) = bf16x4{(bf16)a[k].x, (bf16)a[k].y, (bf16)a[k].z, (bf16)a[k].w};
+        *reinterpret_cast<bf16x4*>(&w3s[cc * L1 + hx]) = bf16x4{(bf16)b[k].x, (bf16)b[k].y, (bf16)b[k].z, (bf16)b[k].w};
+        *reinterpret_cast<bf16x4*>(&w2s[hy * L2 + cy]) = bf16x4{(bf16)m[k].x, (bf16)m[k].y, (bf16)m[k].z, (bf16)m[k].w};
+      }
     }
     __syncthreads();
     if (base < n1) {
