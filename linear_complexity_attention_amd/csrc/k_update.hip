@@ -106,6 +106,11 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
     step = D;
   }
   const long long wsz = 2LL * D * HID;
+  // W_cur's four values first, so that their loads overlap the partials'
+  const float* cur = a.cur.mat(mat, b, h);
+  float c4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c4[i] = cur[base + i * step];
   long long q0, q1, C;
   sk_range(a, pb.B * pb.H, p, q0, q1, C);
   // the pair's slots, four loads in flight at a time, added in workgroup order
@@ -119,14 +124,13 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
     for (int u = 0; u < 4; ++u)
       if (q + u <= q1) { sum.x += d[u].x; sum.y += d[u].y; sum.z += d[u].z; sum.w += d[u].w; }
   }
-  const float* cur = a.cur.mat(mat, b, h);
   float* nxt = a.next + (size_t)p * wsz + (size_t)mat * D * HID;
   float* out = a.out[mat] ? a.out[mat] + (size_t)p * D * HID : nullptr;
   const float s4[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = base + i * step;
-    const float w = cur[e] - s4[i];
+    const float w = c4[i] - s4[i];
     nxt[e] = w;
     if (out) out[e] = w;
   }
