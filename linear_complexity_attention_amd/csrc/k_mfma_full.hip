@@ -452,15 +452,19 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       const int offV = (4 * g + r4) * LDK + ((16 * cb2 + 4 * r3) ^ kswz(4 * g + r4));   // V reads (+16 tb2 LDK)
       const int offGc0 = (16 * cb2 + r) * LDT + ((8 * g) ^ tswz(r));          // G' writes, tb2 = 0
       const int offGc1 = (16 * cb2 + r) * LDT + ((8 * g + 4) ^ tswz(r));      // tb2 = 1
-      // Rows past the end of the batch keep whatever finite keys and values the
-      // registers hold (zeros, or an earlier tile's): their eta is 0, so their
-      // G' row is 0 and they add exactly nothing to dW1 and dW2.
+      // Rows past the end of the batch: their eta is 0, so their G' row is 0
+      // and they add exactly nothing to dW1 and dW2, provided their keys and
+      // values are finite.  Raw keys and values there are zeros or an earlier
+      // tile's; normalised keys are zeroed (-mean * rstd alone can exceed the
+      // f16 range when the variance is tiny).  Only a pair's last tile has such
+      // rows, so full tiles skip the test.
       auto stage = [&](int i) {
         const int nn = (tile0 + i) * TT + st;
         if constexpr (KNORM) {
           stgk_t kh;
 #pragma unroll
           for (int j = 0; j < SCH; ++j) kh[j] = (KT)__builtin_fmaf((float)kreg[j], kst[sc + j][0], kst[sc + j][1]);
+          if ((tile0 + i + 1) * TT > nt && nn >= nt) kh = stgk_t{};
           *reinterpret_cast<stgk_t*>(&Kr[ring<NK>(i)][offSt]) = kh;
         } else {
           *reinterpret_cast<stg_t*>(&Kr[ring<NK>(i)][offSt]) = kreg;
@@ -938,13 +942,7 @@ void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_pe
   const int P = pb.B * pb.H;
   const int tpp = (nt + TT - 1) / TT;
   *tiles_per_pair = tpp;
-  const long long total = (long long)P * tpp;
-  long long g = (long long)device_cu_count() * (pb.hid == 64 ? kGradBlocksPerCU<64> : 1);
-  if (g > total) g = total;
-  *G = (int)g;
-  // a range of ceil(C / G) line units touches at most this many pairs
-  const long long U = tpp + kSkAlpha, per = ((long long)P * U + g - 1) / g;
-  *J = (int)((per + U - 1) / U + 1);
+  sk_geometry(P, tpp, (long long)device_cu_count() * (pb.hid == 64 ? kGradBlocksPerCU<64> : 1), G, J);
 }
 
 void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, float scale, const float* spart,

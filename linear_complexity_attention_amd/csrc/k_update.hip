@@ -18,22 +18,16 @@ namespace {
 constexpr int kCols = 64;
 constexpr int kLanes = 4;                        // row lanes per column (re-norm kernel)
 
-// first and last workgroup of the stream-K gradient kernel that touched pair p
-// (the workgroups holding its first and last tile on the cost line), and the
-// line length C
+// first and last workgroup of the stream-K gradient kernel that touched pair
+// p, and the cost-line length C
 __device__ __forceinline__ void sk_range(const UpdateArgs& a, int P, int p, long long& q0, long long& q1,
                                          long long& C) {
-  const long long U = a.sk_tpp + kSkAlpha;
-  C = (long long)P * U;
-  q0 = sk_group_of(p * U + kSkAlpha, a.sk_G, C);
-  q1 = sk_group_of(p * U + kSkAlpha + a.sk_tpp - 1, a.sk_G, C);
+  C = (long long)P * (a.sk_tpp + kSkAlpha);
+  sk_pair_groups(p, a.sk_tpp, a.sk_G, C, &q0, &q1);
 }
 
-// partial slot of pair p written by workgroup q (q0 <= q <= q1): a workgroup
-// after q0 starts inside p, so p is its first pair (slot q J); q0 may have
-// started in an earlier pair
-__device__ __forceinline__ long long sk_slot(const UpdateArgs& a, int p, long long q, long long q0, long long C) {
-  return q * a.sk_J + (q == q0 ? p - sk_first_pair(q0, a.sk_G, C, a.sk_tpp) : 0);
+__device__ __forceinline__ long long slot_of(const UpdateArgs& a, int p, long long q, long long q0, long long C) {
+  return sk_slot(p, q, q0, a.sk_G, C, a.sk_tpp, a.sk_J);
 }
 
 __device__ __forceinline__ void mat_dims(const Problem& pb, int i, int& rows, int& cols) {
@@ -71,7 +65,7 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
   } else {
     long long q0, q1, C;
     sk_range(a, pb.B * pb.H, p, q0, q1, C);
-    for (long long q = q0; q <= q1; ++q) sub(a.part + sk_slot(a, p, q, q0, C) * wsz);
+    for (long long q = q0; q <= q1; ++q) sub(a.part + slot_of(a, p, q, q0, C) * wsz);
   }
   *reinterpret_cast<float4*>(a.next + (size_t)p * wsz + e) = w;
   if (a.out[i]) *reinterpret_cast<float4*>(a.out[i] + (size_t)p * pb.msz + o) = w;
@@ -119,7 +113,7 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
     float4 d[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (q + u <= q1) d[u] = reinterpret_cast<const float4*>(a.part + sk_slot(a, p, q + u, q0, C) * wsz)[j];
+      if (q + u <= q1) d[u] = reinterpret_cast<const float4*>(a.part + slot_of(a, p, q + u, q0, C) * wsz)[j];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (q + u <= q1) { sum.x += d[u].x; sum.y += d[u].y; sum.z += d[u].z; sum.w += d[u].w; }
@@ -240,7 +234,7 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, Up
         const float* pp = a.part + (size_t)p * wsz + (size_t)i * pb.msz + e;
         for (int s = 0; s < a.S; ++s) w -= pp[s * a.part_pair_stride];
       } else {
-        for (long long q = q0; q <= q1; ++q) w -= a.part[sk_slot(a, p, q, q0, C) * wsz + (size_t)i * pb.msz + e];
+        for (long long q = q0; q <= q1; ++q) w -= a.part[slot_of(a, p, q, q0, C) * wsz + (size_t)i * pb.msz + e];
       }
       nxt[e] = w;
       nn += w * w;

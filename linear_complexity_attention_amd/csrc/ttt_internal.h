@@ -77,6 +77,31 @@ __host__ __device__ inline long long sk_group_of(long long u, long long G, long 
 __host__ __device__ inline long long sk_first_pair(long long q, long long G, long long C, int tpp) {
   return (q * C / G) / (tpp + kSkAlpha);
 }
+// Grid of the stream-K split for P pairs of tpp tiles: G = min(target, P*tpp)
+// workgroups (never more workgroups than tiles) and J, the partial slots each
+// workgroup owns: a range of ceil(C / G) line units touches at most J pairs.
+__host__ __device__ inline void sk_geometry(long long P, int tpp, long long target, int* G, int* J) {
+  const long long total = P * tpp;
+  const long long g = target < total ? target : total;
+  const long long U = tpp + kSkAlpha, per = (P * U + g - 1) / g;
+  *G = (int)g;
+  *J = (int)((per + U - 1) / U + 1);
+}
+// first and last workgroup whose tile range holds a tile of pair p (the ones
+// holding its first and its last tile on the cost line)
+__host__ __device__ inline void sk_pair_groups(long long p, int tpp, long long G, long long C, long long* q0,
+                                               long long* q1) {
+  const long long U = tpp + kSkAlpha;
+  *q0 = sk_group_of(p * U + kSkAlpha, G, C);
+  *q1 = sk_group_of(p * U + kSkAlpha + tpp - 1, G, C);
+}
+// partial slot of pair p written by workgroup q (q0 <= q <= q1): a workgroup
+// after q0 starts inside p, so p is its first pair (slot q J); q0 may have
+// started in an earlier pair
+__host__ __device__ inline long long sk_slot(long long p, long long q, long long q0, long long G, long long C, int tpp,
+                                             int J) {
+  return q * J + (q == q0 ? p - sk_first_pair(q0, G, C, tpp) : 0);
+}
 void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st);
 
 // ---- MFMA fast paths --------------------------------------------------------

@@ -84,6 +84,17 @@ EXPORTED = ("ttt_version", "ttt_create", "ttt_workspace_bytes", "ttt_forward", "
             "ttt_set_timing_events", "ttt_destroy", "ttt_last_error", "ttt_status_string")
 
 
+def matrix_shapes(inner: int, d: int, hidden: int):
+    """[in, out] shape of every matrix of the inner model (include/ttt.h)."""
+    if inner == TTT_INNER_LINEAR:
+        return [(d, d)]
+    if inner == TTT_INNER_MLP_GELU:
+        return [(d, hidden), (hidden, d)]
+    if inner == TTT_INNER_SWIGLU:
+        return [(d, hidden), (hidden, d), (d, hidden)]
+    raise ValueError(f"unknown inner model {inner}")
+
+
 class TTTError(RuntimeError):
     def __init__(self, status: int, message: str):
         self.status = status
@@ -164,11 +175,18 @@ class TTTLayer:
         self.handle = ttt_create(self.cfg)
         self._ws = None
 
+    # bound at class creation: at interpreter shutdown the module globals may
+    # already be gone when __del__ runs
+    _destroy = staticmethod(_lib.ttt_destroy)
+
     def __del__(self):
         h = getattr(self, "handle", None)
         if h is not None:
-            ttt_destroy(h)
             self.handle = None
+            try:
+                self._destroy(h)
+            except Exception:   # interpreter teardown: nothing left to release into
+                pass
 
     def workspace_bytes(self, loss="mse", inner="mlp_gelu", chunk=0) -> int:
         return ttt_workspace_bytes(self.handle, LOSSES[loss], INNERS[inner], chunk)
@@ -183,20 +201,48 @@ class TTTLayer:
         c = self.cfg
         tdt = torch.bfloat16 if c.dtype == TTT_BF16 else torch.float32
         for name, t in (("q", q), ("k", k), ("v", v)):
-            if not t.is_cuda or t.dtype != tdt or not t.is_contiguous() or tuple(t.shape) != (c.B, c.H, c.N, c.d):
-                raise ValueError(f"{name} must be a contiguous cuda {tdt} tensor of shape {(c.B, c.H, c.N, c.d)}")
+            if (not t.is_cuda or t.device != q.device or t.dtype != tdt or not t.is_contiguous()
+                    or tuple(t.shape) != (c.B, c.H, c.N, c.d)):
+                raise ValueError(f"{name} must be a contiguous cuda {tdt} tensor on q's device of shape "
+                                 f"{(c.B, c.H, c.N, c.d)}")
         li, ii = LOSSES[loss], INNERS[inner]
         nm = N_MATRICES[ii]
+        shapes = matrix_shapes(ii, c.d, c.hidden)
         if len(W0) != nm:
             raise ValueError(f"{inner} needs {nm} weight matrices")
-        stride = 0
-        for w in W0:
-            if not w.is_cuda or w.dtype != torch.float32 or not w.is_contiguous():
-                raise ValueError("W0 matrices must be contiguous cuda float32 tensors")
-            if w.dim() == 4:
-                stride = w[0].numel()
+        lead = None
+        for i, (w, (fi, fo)) in enumerate(zip(W0, shapes)):
+            if not w.is_cuda or w.device != q.device or w.dtype != torch.float32 or not w.is_contiguous():
+                raise ValueError(f"W0[{i}] must be a contiguous float32 tensor on {q.device}")
+            if tuple(w.shape) not in ((c.H, fi, fo), (c.B, c.H, fi, fo)):
+                raise ValueError(f"W0[{i}] must have shape {(c.H, fi, fo)} or {(c.B, c.H, fi, fo)}, "
+                                 f"got {tuple(w.shape)}")
+            if lead is None:
+                lead = w.dim()
+            elif w.dim() != lead:
+                raise ValueError("all W0 matrices must share one layout ([H,in,out] or [B,H,in,out])")
+        # one batch stride serves every matrix (all have in*out elements per head)
+        stride = c.H * shapes[0][0] * shapes[0][1] if lead == 4 else 0
+        if eta_tok is not None:
+            if (not eta_tok.is_cuda or eta_tok.device != q.device or eta_tok.dtype != torch.float32
+                    or not eta_tok.is_contiguous() or tuple(eta_tok.shape) != (c.B, c.H, c.N)):
+                raise ValueError(f"eta_tok must be a contiguous float32 tensor on {q.device} of shape "
+                                 f"{(c.B, c.H, c.N)}")
         if out is None:
             out = torch.empty_like(q)
+        elif (out.device != q.device or out.dtype != tdt or not out.is_contiguous()
+              or tuple(out.shape) != (c.B, c.H, c.N, c.d)):
+            raise ValueError(f"out must be a contiguous {tdt} tensor on {q.device} of shape {(c.B, c.H, c.N, c.d)}")
+        if W_out is not None:
+            if len(W_out) != nm:
+                raise ValueError(f"W_out needs {nm} matrices")
+            for i, (w, (fi, fo)) in enumerate(zip(W_out, shapes)):
+                if w is None:
+                    continue
+                if (w.device != q.device or w.dtype != torch.float32 or not w.is_contiguous()
+                        or tuple(w.shape) != (c.B, c.H, fi, fo)):
+                    raise ValueError(f"W_out[{i}] must be a contiguous float32 tensor on {q.device} of shape "
+                                     f"{(c.B, c.H, fi, fo)}")
         nbytes = ttt_workspace_bytes(self.handle, li, ii, chunk)
         if self._ws is None or self._ws.numel() < nbytes or self._ws.device != q.device:
             self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
@@ -209,7 +255,7 @@ class TTTLayer:
         if W_out is not None:
             wo = ttt_weights_out()
             for i, w in enumerate(W_out):
-                wo.w[i] = w.data_ptr()
+                wo.w[i] = w.data_ptr() if w is not None else None
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = ttt_forward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), wts, e, li, ii, chunk,
                          out.data_ptr(), wo, self._ws.data_ptr(), self._ws.numel(), stream)

@@ -23,12 +23,12 @@ def device_inputs(w: Workload, *, B=None, H=None, N=None, seed=None, shared_w0=T
     return (tq, tk, tv, tW, tet), exact
 
 
-def run_gpu(w: Workload, dev_in, *, flags=0, eta=None, return_weights=True, chunk=None):
+def run_gpu(w: Workload, dev_in, *, flags=0, eta=None, return_weights=True, chunk=None, eps=1e-5):
     from linear_complexity_attention_amd import ttt
 
     tq, tk, tv, tW, tet = dev_in
     B, H, N, d = tq.shape
-    layer = ttt.TTTLayer(B, H, N, d, w.hidden, dtype=w.dtype, key_norm=w.key_norm, eps=1e-5,
+    layer = ttt.TTTLayer(B, H, N, d, w.hidden, dtype=w.dtype, key_norm=w.key_norm, eps=eps,
                          renorm=w.renorm, flags=flags)
     W_out = None
     if return_weights:
@@ -40,11 +40,11 @@ def run_gpu(w: Workload, dev_in, *, flags=0, eta=None, return_weights=True, chun
     return O, W_out, path
 
 
-def run_oracle(w: Workload, exact, *, pairs=None, eta=None, chunk=None):
+def run_oracle(w: Workload, exact, *, pairs=None, eta=None, chunk=None, eps=1e-5):
     """Oracle on all pairs, or on the listed (b, h) pairs only (each pair is
     independent, so a slice of the inputs gives that pair's exact result)."""
     kw = dict(eta_scale=w.eta if eta is None else eta, loss=w.loss, inner=w.inner,
-              chunk=w.chunk if chunk is None else chunk, key_norm=w.key_norm, eps=1e-5, renorm=w.renorm)
+              chunk=w.chunk if chunk is None else chunk, key_norm=w.key_norm, eps=eps, renorm=w.renorm)
     if pairs is None:
         return orc.oracle_forward(exact["q"], exact["k"], exact["v"], exact["W0"], eta_tok=exact["eta_tok"], **kw)
     Os, Ws = [], []

@@ -20,10 +20,17 @@ def _w0_pair(exact, b, h):
     return [m[h] if m.ndim == 3 else m[b, h] for m in exact["W0"]]
 
 
-def _check_pairs(w, dev_in, exact, pairs, *, flags=0, tol=None, eta=None, chunk=None, tag=""):
+def _all_pairs(w):
+    return [(b, h) for b in range(w.B) for h in range(w.H)]
+
+
+def _check_pairs(w, dev_in, exact, pairs, *, flags=0, tol=None, eta=None, chunk=None, tag="", eps=1e-5):
+    """O and dW = W_out - W0 of every listed pair, element by element, against
+    the oracle (pairs=None: all pairs)."""
     tol = TOL[w.dtype] if tol is None else tol
-    O, W_out, path = run_gpu(w, dev_in, flags=flags, eta=eta, chunk=chunk)
-    O_ref, W_ref = run_oracle(w, exact, pairs=pairs, eta=eta, chunk=chunk)
+    pairs = _all_pairs(w) if pairs is None else pairs
+    O, W_out, path = run_gpu(w, dev_in, flags=flags, eta=eta, chunk=chunk, eps=eps)
+    O_ref, W_ref = run_oracle(w, exact, pairs=pairs, eta=eta, chunk=chunk, eps=eps)
     Og = O.float().cpu().numpy()
     Wg = [m.cpu().numpy() for m in W_out]
     for i, (b, h) in enumerate(pairs):
@@ -86,26 +93,30 @@ def _check_output_change(w, dev_in, exact, O, pairs, tag):
         assert err <= tol, f"{tag} dO pair {(b, h)}: max err {err:.3e} > {tol:.3e}"
 
 
-def test_c3_hires_sampled_pairs():
+# c3, c4, c5 at full size, in the launch configuration the benchmark times:
+# O and dW of every (b, h) pair against the oracle (which computes each pair
+# alone; pairs are independent), plus the output change on a sample of pairs
+def test_c3_hires_all_pairs():
     w = WORKLOADS["c3_hires_r4"]
     dev_in, exact = device_inputs(w)
-    pairs = [(0, 0), (3, 7), (7, 11)]
-    O, _, _ = _check_pairs(w, dev_in, exact, pairs, tag="c3")
-    _check_output_change(w, dev_in, exact, O, pairs, "c3")
+    O, _, path = _check_pairs(w, dev_in, exact, None, tag="c3")
+    assert path == "mfma"
+    _check_output_change(w, dev_in, exact, O, [(0, 0), (3, 7), (7, 11)], "c3")
 
 
-def test_c4_dit_sampled_pairs():
+def test_c4_dit_all_pairs():
     w = WORKLOADS["c4_dit_h64"]
     dev_in, exact = device_inputs(w)
-    pairs = [(0, 0), (1, 23)]
-    O, _, _ = _check_pairs(w, dev_in, exact, pairs, tag="c4")
-    _check_output_change(w, dev_in, exact, O, pairs, "c4")
+    O, _, path = _check_pairs(w, dev_in, exact, None, tag="c4")
+    assert path == "mfma"
+    _check_output_change(w, dev_in, exact, O, [(0, 0), (1, 23)], "c4")
 
 
-def test_c5_lact_sampled_pairs():
+def test_c5_lact_all_pairs():
     w = WORKLOADS["c5_lact_swiglu"]
     dev_in, exact = device_inputs(w)
-    _check_pairs(w, dev_in, exact, [(0, 1), (0, 3)], tag="c5")
+    _, _, path = _check_pairs(w, dev_in, exact, None, tag="c5")
+    assert path == "mfma_swiglu"
 
 
 # ---------------------------------------------------------------------------
@@ -121,6 +132,11 @@ COMBOS = [
     ("swiglu", "dot", 96, False, True),
     ("mlp_gelu", "mse", 100, False, False),
     ("mlp_gelu", "dot", 64, False, True),
+    # raw (not normalised) keys on the GELU-MLP MFMA kernel, and its stream-K
+    # update followed by the column re-norm
+    ("mlp_gelu", "mse", 0, False, False),
+    ("mlp_gelu", "dot", 0, False, True),
+    ("mlp_gelu", "mse", 0, True, True),
 ]
 
 
@@ -134,6 +150,22 @@ def test_combos_ragged(inner, loss, chunk, key_norm, renorm, dtype, generic):
     dev_in, exact = device_inputs(w)
     _check_pairs(w, dev_in, exact, [(0, 0), (1, 2)], flags=GENERIC if generic else 0,
                  tag=f"{inner}/{loss}/{chunk}/{dtype}/{'gen' if generic else 'auto'}")
+
+
+# every instance of the GELU-MLP MFMA gradient kernel: hidden 64/128/256 x
+# MSE/dot x key norm on/off, full batch, ragged N that spans several stream-K
+# ranges (pairs x tiles > workgroups), with and without the column re-norm
+@pytest.mark.parametrize("hidden", [64, 128, 256])
+@pytest.mark.parametrize("loss", ["mse", "dot"])
+@pytest.mark.parametrize("key_norm", [False, True])
+def test_mfma_mlp_instances(hidden, loss, key_norm):
+    renorm = loss == "dot"
+    w = Workload("inst", B=3, H=5, N=1111, d=64, hidden=hidden, loss=loss, key_norm=key_norm, renorm=renorm,
+                 per_token_eta=(loss == "dot"), unit_columns=renorm, seed=900 + hidden + 2 * key_norm,
+                 eta=1.0 if loss == "mse" else 0.05)
+    dev_in, exact = device_inputs(w)
+    _, _, path = _check_pairs(w, dev_in, exact, None, tag=f"h={hidden} {loss} kn={key_norm}")
+    assert path == "mfma"
 
 
 @pytest.mark.parametrize("d,hidden,N", [(32, 32, 256), (64, 64, 130), (64, 256, 517), (128, 256, 300),
@@ -180,6 +212,53 @@ def test_single_token_with_key_norm_keeps_w0():
         torch.testing.assert_close(m, w0[None].expand_as(m), rtol=0, atol=1e-7)
     O_ref, _ = run_oracle(w, exact)
     assert rel_err(O.float().cpu().numpy(), O_ref) <= 1e-2
+
+
+def test_single_token_tiny_eps_padding_rows():
+    """N = 1 with a tiny eps: rstd is 1e5, so -mean * rstd of the 31 padding
+    rows of the only tile is beyond the f16 range; those rows must not poison
+    dW (W stays exactly W0, O is finite and equals the oracle)."""
+    w = Workload("n1eps", B=1, H=3, N=1, d=64, hidden=256, seed=48)
+    dev_in, exact = device_inputs(w)
+    O, W_out, path = run_gpu(w, dev_in, eps=1e-10)
+    assert path == "mfma"
+    for m, w0 in zip(W_out, dev_in[3]):
+        torch.testing.assert_close(m, w0[None].expand_as(m), rtol=0, atol=1e-7)
+    assert torch.isfinite(O.float()).all()
+    O_ref, _ = run_oracle(w, exact, eps=1e-10)
+    assert rel_err(O.float().cpu().numpy(), O_ref) <= 1e-2
+
+
+def test_binding_rejects_bad_tensors():
+    """The binding checks every tensor's device, dtype, layout and shape before
+    the C call, so a mismatch cannot reach the kernels."""
+    from linear_complexity_attention_amd import ttt
+
+    w = Workload("val", B=2, H=2, N=64, d=64, hidden=128, seed=49)
+    (tq, tk, tv, tW, _), _ = device_inputs(w)
+    layer = ttt.TTTLayer(2, 2, 64, 64, 128)
+    bad_w0 = [
+        [tW[0][:, :32].contiguous(), tW[1]],                     # wrong inner shape
+        [tW[0], tW[1].transpose(-1, -2).contiguous()],             # W2 stored [d, h]
+        [tW[0].double(), tW[1]],                                   # dtype
+        [tW[0][None].expand(2, -1, -1, -1).contiguous(), tW[1]],   # mixed layouts
+        [tW[0]],                                                   # too few matrices
+    ]
+    for W0 in bad_w0:
+        with pytest.raises(ValueError):
+            layer.forward(tq, tk, tv, W0)
+    with pytest.raises(ValueError):
+        layer.forward(tq, tk, tv, tW, eta_tok=torch.ones(2, 2, 63, device=tq.device))
+    with pytest.raises(ValueError):
+        layer.forward(tq, tk, tv, tW, out=torch.empty(2, 2, 64, 32, dtype=torch.bfloat16, device=tq.device))
+    with pytest.raises(ValueError):
+        layer.forward(tq, tk, tv, tW, W_out=[torch.empty(2, 2, 64, 128, device=tq.device),
+                                             torch.empty(2, 2, 64, 128, device=tq.device)])
+    with pytest.raises(ValueError):
+        layer.forward(tq[:, :, :, :32], tk, tv, tW)
+    O = layer.forward(tq, tk, tv, tW)          # the valid call still works
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all()
 
 
 def test_eta_zero_reads_w0():
