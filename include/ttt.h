@@ -163,6 +163,26 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v,
                 void* o, const ttt_weights_out* W_out, void* workspace, size_t ws_bytes,
                 void* stream);
 
+/* ttt_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments and results are those of ttt_forward, without the workspace: the
+ * scratch memory is a fixed array of TTT_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on, from the first call on that GPU until
+ * the process ends.  The call allocates and frees nothing.
+ *   - A request whose ttt_workspace_bytes exceeds TTT_NOALLOC_SCRATCH_BYTES is
+ *     rejected with TTT_ERR_WORKSPACE before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's array, and the array keeps the
+ *     last call's contents (nothing in it needs to start at zero).  Calls that
+ *     overlap on one GPU (two streams, two threads, or two handles without an
+ *     ordering between them) race on it: order them on one stream or
+ *     synchronise between them.
+ *   - The first call on a GPU makes one runtime call to look the array up
+ *     (hipGetSymbolAddress); TTT_ERR_HIP if that fails. */
+#define TTT_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+int ttt_forward_noalloc(ttt_handle* h, const void* q, const void* k, const void* v,
+                        const ttt_weights* W0, const ttt_eta* eta, int loss, int inner, int chunk,
+                        void* o, const ttt_weights_out* W_out, void* stream);
+
 /* Name of the kernel family ttt_forward would use for this request, e.g.
  * "mfma_full_mlp" or "generic"; NULL for an invalid request.  Host-only. */
 const char* ttt_path_name(const ttt_handle* h, int loss, int inner, int chunk);

@@ -48,14 +48,19 @@ namespace {
 
 thread_local std::string g_create_err;
 
-int fail(ttt_handle* h, int code, const char* fmt, ...) {
+int vfail(ttt_handle* h, int code, const char* fmt, va_list ap) {
   char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
   if (h) h->err = buf; else g_create_err = buf;
   return code;
+}
+
+int fail(ttt_handle* h, int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int r = vfail(h, code, fmt, ap);
+  va_end(ap);
+  return r;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -183,6 +188,16 @@ int hip_fail(ttt_handle* h, hipError_t e, const char* what) {
 }
 
 }  // namespace
+
+namespace ttt {
+int set_error(ttt_handle* h, int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int r = vfail(h, code, fmt, ap);
+  va_end(ap);
+  return r;
+}
+}  // namespace ttt
 
 extern "C" {
 

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include "common.h"
 
+struct ttt_handle;
+
 namespace ttt {
 
 enum { INNER_LINEAR = 0, INNER_MLP = 1, INNER_SWIGLU = 2 };
@@ -142,6 +144,13 @@ void launch_lact_readout(const Problem& pb, const WRef& w0, const float* states,
 
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cu_count();
+
+// scratch bytes per device behind ttt_forward_noalloc (every benchmarked
+// configuration fits; the largest, ViT-S at r = 4, needs 145 MiB)
+constexpr size_t kNoallocScratchBytes = size_t(192) << 20;
+// record a printf-style message as the handle's last error (h == NULL: the
+// thread's create error) and return code
+int set_error(ttt_handle* h, int code, const char* fmt, ...);
 
 // ---- finiteness check ------------------------------------------------------
 void launch_zero_flag(int* flag, hipStream_t st);

@@ -69,6 +69,11 @@ _lib.ttt_forward.restype = c_int
 _lib.ttt_forward.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(ttt_weights), POINTER(ttt_eta),
                              c_int, c_int, c_int, c_void_p, POINTER(ttt_weights_out), c_void_p, c_size_t,
                              c_void_p]
+_lib.ttt_forward_noalloc.restype = c_int
+_lib.ttt_forward_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(ttt_weights),
+                                     POINTER(ttt_eta), c_int, c_int, c_int, c_void_p, POINTER(ttt_weights_out),
+                                     c_void_p]
+TTT_NOALLOC_SCRATCH_BYTES = 192 << 20
 _lib.ttt_path_name.restype = c_char_p
 _lib.ttt_path_name.argtypes = [c_void_p, c_int, c_int, c_int]
 _lib.ttt_set_timing_events.restype = c_int
@@ -80,8 +85,8 @@ _lib.ttt_last_error.argtypes = [c_void_p]
 _lib.ttt_status_string.restype = c_char_p
 _lib.ttt_status_string.argtypes = [c_int]
 
-EXPORTED = ("ttt_version", "ttt_create", "ttt_workspace_bytes", "ttt_forward", "ttt_path_name",
-            "ttt_set_timing_events", "ttt_destroy", "ttt_last_error", "ttt_status_string")
+EXPORTED = ("ttt_version", "ttt_create", "ttt_workspace_bytes", "ttt_forward", "ttt_forward_noalloc",
+            "ttt_path_name", "ttt_set_timing_events", "ttt_destroy", "ttt_last_error", "ttt_status_string")
 
 
 def matrix_shapes(inner: int, d: int, hidden: int):
@@ -157,6 +162,14 @@ def ttt_forward(handle, q, k, v, W0: ttt_weights, eta: ttt_eta, loss: int, inner
     ctypes pointers); returns the status code without raising."""
     return _lib.ttt_forward(handle, q, k, v, byref(W0), byref(eta), loss, inner, chunk, o,
                             byref(W_out) if W_out is not None else None, workspace, ws_bytes, stream)
+
+
+def ttt_forward_noalloc(handle, q, k, v, W0: ttt_weights, eta: ttt_eta, loss: int, inner: int, chunk: int, o,
+                        W_out, stream) -> int:
+    """Raw call of the entry point that uses the library's own per-device
+    scratch array instead of a workspace; returns the status code."""
+    return _lib.ttt_forward_noalloc(handle, q, k, v, byref(W0), byref(eta), loss, inner, chunk, o,
+                                    byref(W_out) if W_out is not None else None, stream)
 
 
 # ---- torch convenience layer --------------------------------------------------

@@ -107,3 +107,21 @@ def test_forward_rejects_before_enqueue():
         assert rc == ttt.TTT_ERR_INVALID and "batch_stride" in ttt.ttt_last_error(h)
     finally:
         ttt.ttt_destroy(h)
+
+
+def test_noalloc_rejects_oversize_request_on_host():
+    """ttt_forward_noalloc checks the request against its fixed scratch size
+    before any HIP call."""
+    h = ttt.ttt_create(_cfg(B=64, H=16, N=8192, hidden=512))
+    try:
+        assert ttt.ttt_workspace_bytes(h, ttt.TTT_LOSS_MSE, ttt.TTT_INNER_MLP_GELU, 0) > ttt.TTT_NOALLOC_SCRATCH_BYTES
+        fake = 1 << 20
+        W = ttt.ttt_weights()
+        W.w[0] = W.w[1] = fake
+        rc = ttt.ttt_forward_noalloc(h, fake, fake, fake, W, ttt.ttt_eta(1.0, None), ttt.TTT_LOSS_MSE,
+                                     ttt.TTT_INNER_MLP_GELU, 0, fake, None, None)
+        assert rc == ttt.TTT_ERR_WORKSPACE and "ttt_forward_noalloc" in ttt.ttt_last_error(h)
+        assert ttt.ttt_forward_noalloc(None, fake, fake, fake, W, ttt.ttt_eta(1.0, None), 0, 1, 0, fake, None,
+                                       None) == ttt.TTT_ERR_INVALID
+    finally:
+        ttt.ttt_destroy(h)
