@@ -22,6 +22,16 @@ from SciPy).  Pages cited (full addresses in the design doc):
 * [TvS]   "Test-Time Training vs Sleep" compare page, section "Side one"
   (key instance normalisation removes the constant key shift; NaN without it).
 
+The update variants follow the same pages:
+* update rules [LaCT "Nonlinear memory..."]: plain gradient step, momentum,
+  and Muon (the momentum matrix orthogonalised by Newton-Schulz iterations);
+  L2 normalisation after every update;
+* several epochs over one update batch, and sequential mini-batches that all
+  write before any query reads [ViT3 §03 guideline 2];
+* only the first layer adjusted [TvS "Side one"];
+* chunks that only read while others write (video: clean chunks write, noisy
+  chunks read) [LaCT "Order of operations..."].
+
 Every pinned property of this file is exercised by ``tests/test_oracle.py``.
 Readings of points the pages leave open (MSE reduction constant, norm axis,
 epsilon, activation, re-norm axis, ...) are listed in the design doc; each function
@@ -173,6 +183,58 @@ def column_renorm(W, Wref):
     return W * (n_ref / np.maximum(n_new, 1e-12))
 
 
+# ---------------------------------------------------------------------------
+# Update rules [LaCT "Nonlinear memory complements local attention": plain
+# gradient descent, momentum, and Muon, which turns the matrix gradient into
+# an orthogonalised matrix by Newton-Schulz iterations; L2 normalisation after
+# the update].  The page names the rules only.  Readings:
+#   momentum: M <- beta M + G,   W <- W - M        (heavy ball, M starts at 0)
+#   Muon    : M <- beta M + G,   W <- W - s NS(M)   (beta = 0: no momentum)
+# where G is the eta-weighted chunk gradient and NS is the Newton-Schulz
+# orthogonalisation of the published Muon optimiser (Jordan et al., 2024):
+# X = M / (||M||_F + 1e-7); k times X <- a X + (b A + c A A) X with A = X X^T,
+# (a, b, c) = (3.4445, -4.7750, 2.0315), computed on the wide orientation
+# (rows <= cols; a tall matrix is transposed first and back after).  Each step
+# maps every singular value sigma of X to a sigma + b sigma^3 + c sigma^5 and
+# keeps the singular vectors.
+# ---------------------------------------------------------------------------
+RULE_GD = "gd"
+RULE_MOMENTUM = "momentum"
+RULE_MUON = "muon"
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+def newton_schulz(M, steps):
+    a, b, c = NS_COEFFS
+    tall = M.shape[0] > M.shape[1]
+    X = M.T if tall else M
+    X = X / (np.sqrt(np.sum(X * X)) + 1e-7)
+    for _ in range(steps):
+        A = X @ X.T
+        X = a * X + (b * A + c * (A @ A)) @ X
+    return X.T if tall else X
+
+
+def apply_rule(W, dW, M, rule, beta, muon_scale, ns_steps, update):
+    """One update of the matrices flagged in ``update`` (the others keep their
+    values and their momentum).  dW already carries eta.  Returns (W, M)."""
+    W, M = list(W), list(M)
+    for i, (w, g) in enumerate(zip(W, dW)):
+        if not update[i]:
+            continue
+        if rule == RULE_GD:
+            W[i] = w - g
+        elif rule == RULE_MOMENTUM:
+            M[i] = beta * M[i] + g
+            W[i] = w - M[i]
+        elif rule == RULE_MUON:
+            M[i] = beta * M[i] + g
+            W[i] = w - muon_scale * newton_schulz(M[i], ns_steps)
+        else:
+            raise ValueError(f"unknown update rule {rule!r}")
+    return W, M
+
+
 def inner_step(inner, loss, W, X, V, eta_n):
     """One gradient step of the inner model on the mini-dataset (X, V).
 
@@ -197,18 +259,35 @@ def _pair_weights(W0, b, h):
     return out
 
 
+ORDER_CAUSAL = "causal"
+ORDER_WRITE_THEN_QUERY = "write_then_query"
+
+
 def oracle_forward(q, k, v, W0, *, eta_scale=1.0, eta_tok=None, loss=LOSS_MSE,
                    inner=INNER_MLP, chunk=0, key_norm=True, eps=1e-5,
-                   renorm=False):
+                   renorm=False, epochs=1, update_mask=None, order=ORDER_CAUSAL,
+                   chunk_update=None, rule=RULE_GD, beta=0.0, muon_scale=1.0,
+                   ns_steps=5):
     """TTT-layer forward.  q, k, v: [B, H, N, d]; W0: list of matrices
     ([H, in, out] or [B, H, in, out]); eta_tok: None or [B, H, N].
 
-    chunk == 0 : full batch, one step over all N tokens, then every query reads
-                 the updated weights (write-then-query) [ViT3 §03 guideline 2;
-                 LaCT "Order of operations"].
-    chunk == C : causal large chunks of C tokens (the last may be shorter); each
-                 chunk first reads the weights left by the earlier chunks, then
-                 takes its own step [LaCT "Order of operations"].
+    chunk == 0 : full batch, one update batch of all N tokens, then every
+                 query reads the updated weights (write-then-query) [ViT3 §03
+                 guideline 2; LaCT "Order of operations"].
+    chunk == C : update batches of C tokens (the last may be shorter).
+                 order "causal": each chunk first reads the weights left by
+                 the earlier chunks, then takes its own step [LaCT "Order of
+                 operations"]; order "write_then_query": every chunk writes in
+                 turn (sequential mini-batches), then every query reads the
+                 final weights [ViT3 §03 guideline 2; LaCT, sets of images].
+    epochs     : gradient steps on each update batch [ViT3 §03 guideline 2].
+    update_mask: which matrices the steps change (None: all); e.g. [True,
+                 False] adjusts only the first layer [TvS "Side one"].
+    chunk_update: None or one flag per chunk; a chunk with a false flag only
+                 reads (video: clean chunks write, noisy chunks read) [LaCT].
+    rule, beta, muon_scale, ns_steps: the update rule (see apply_rule).
+    renorm     : after every update, each updated matrix's columns get their
+                 W0 norms back [LaCT].
     Returns (O [B, H, N, d], W_final list of [B, H, in, out]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -217,35 +296,51 @@ def oracle_forward(q, k, v, W0, *, eta_scale=1.0, eta_tok=None, loss=LOSS_MSE,
     B, H, N, d = q.shape
     if chunk < 0:
         raise ValueError("chunk must be >= 0")
-    if chunk > 0 and key_norm:
+    if order not in (ORDER_CAUSAL, ORDER_WRITE_THEN_QUERY):
+        raise ValueError(f"unknown order {order!r}")
+    causal = chunk > 0 and order == ORDER_CAUSAL
+    if causal and key_norm:
         raise ValueError("key instance norm over the whole sequence would read "
                          "future keys in causal chunked mode")
+    if epochs < 1:
+        raise ValueError("epochs must be >= 1")
     nm = n_matrices(inner)
     if len(W0) != nm:
         raise ValueError(f"{inner} needs {nm} matrices, got {len(W0)}")
+    update = [True] * nm if update_mask is None else [bool(x) for x in update_mask]
+    if len(update) != nm:
+        raise ValueError("update_mask needs one flag per matrix")
+    span = chunk if chunk > 0 else N
+    nb = (N + span - 1) // span
+    if chunk_update is not None and len(chunk_update) != nb:
+        raise ValueError(f"chunk_update needs {nb} flags")
     O = np.zeros_like(q)
     W_final = [np.zeros((B, H) + np.asarray(w).shape[-2:]) for w in W0]
     for b in range(B):
         for h in range(H):
             Wref = _pair_weights(W0, b, h)
             W = [w.copy() for w in Wref]
+            M = [np.zeros_like(w) for w in Wref]
             Q, K, V = q[b, h], k[b, h], v[b, h]
             eta = np.full(N, float(eta_scale))
             if eta_tok is not None:
                 eta = eta * np.asarray(eta_tok, dtype=np.float64)[b, h]
             Kh = key_instnorm(K, eps) if key_norm else K
-            if chunk == 0:
-                W, _ = inner_step(inner, loss, W, Kh, V, eta)
-                if renorm:
-                    W = [column_renorm(w, r) for w, r in zip(W, Wref)]
-                O[b, h] = inner_forward(inner, W, Q)[0]
-            else:
-                for s in range(0, N, chunk):
-                    e = min(s + chunk, N)
+            for c in range(nb):
+                s, e = c * span, min((c + 1) * span, N)
+                if causal:
                     O[b, h, s:e] = inner_forward(inner, W, Q[s:e])[0]   # read
-                    W, _ = inner_step(inner, loss, W, Kh[s:e], V[s:e], eta[s:e])
+                if chunk_update is not None and not chunk_update[c]:
+                    continue                                              # read-only chunk
+                for _ in range(epochs):
+                    Vhat, cache = inner_forward(inner, W, Kh[s:e])
+                    G = loss_grad(loss, Vhat, V[s:e], eta[s:e])
+                    dW = inner_backward(inner, W, Kh[s:e], G, cache)
+                    W, M = apply_rule(W, dW, M, rule, beta, muon_scale, ns_steps, update)
                     if renorm:
-                        W = [column_renorm(w, r) for w, r in zip(W, Wref)]
+                        W = [column_renorm(w, r) if u else w for w, r, u in zip(W, Wref, update)]
+            if not causal:
+                O[b, h] = inner_forward(inner, W, Q)[0]                   # write, then query
             for i in range(nm):
                 W_final[i][b, h] = W[i]
     return O, W_final

@@ -117,9 +117,12 @@ def test_backward_matches_finite_differences(inner, loss):
 # --------------------------------------------------------------------------
 # P2: an independent derivation with torch.autograd in float64
 # --------------------------------------------------------------------------
-def _torch_layer(q, k, v, W0, eta_scale, eta_tok, loss, inner, chunk, key_norm, eps, renorm):
+def _torch_layer(q, k, v, W0, eta_scale, eta_tok, loss, inner, chunk, key_norm, eps, renorm, *, epochs=1,
+                 update_mask=None, write_then_query=False, chunk_update=None, beta=None):
     """The layer written with library pieces: F.instance_norm for the key
-    statistics, F.gelu / F.silu, F.mse_loss, and autograd for dL/dW."""
+    statistics, F.gelu / F.silu, F.mse_loss, and autograd for dL/dW.  Options:
+    several epochs per batch, a per-matrix update mask, chunks that all write
+    before the queries read, read-only chunks, heavy-ball momentum (beta)."""
     F = torch.nn.functional
     q, k, v = (torch.tensor(a, dtype=torch.float64) for a in (q, k, v))
     B, H, N, d = q.shape
@@ -142,26 +145,41 @@ def _torch_layer(q, k, v, W0, eta_scale, eta_tok, loss, inner, chunk, key_norm, 
         for h in range(H):
             ref = [torch.tensor(np.asarray(w)[h], dtype=torch.float64) for w in W0]
             Ws = [w.clone() for w in ref]
+            mom = [torch.zeros_like(w) for w in ref]
+            upd = [True] * len(ref) if update_mask is None else list(update_mask)
             bounds = [(0, N)] if chunk == 0 else [(s, min(s + chunk, N)) for s in range(0, N, chunk)]
-            for (s, e) in bounds:
-                if chunk:
+            causal = chunk > 0 and not write_then_query
+            for ci, (s, e) in enumerate(bounds):
+                if causal:
                     O[b, h, s:e] = fwd(Ws, q[b, h, s:e])
-                Wg = [w.clone().requires_grad_(True) for w in Ws]
-                Vh = fwd(Wg, k[b, h, s:e])
-                et = eta[b, h, s:e]
-                if loss == orc.LOSS_MSE:
-                    if eta_tok is None:
-                        Lv = float(eta_scale) * F.mse_loss(Vh, v[b, h, s:e], reduction="mean")
+                if chunk_update is not None and not chunk_update[ci]:
+                    continue
+                for _ in range(epochs):
+                    Wg = [w.clone().requires_grad_(True) for w in Ws]
+                    Vh = fwd(Wg, k[b, h, s:e])
+                    et = eta[b, h, s:e]
+                    if loss == orc.LOSS_MSE:
+                        if eta_tok is None:
+                            Lv = float(eta_scale) * F.mse_loss(Vh, v[b, h, s:e], reduction="mean")
+                        else:
+                            Lv = (et[:, None] * (Vh - v[b, h, s:e]) ** 2).mean()
                     else:
-                        Lv = (et[:, None] * (Vh - v[b, h, s:e]) ** 2).mean()
-                else:
-                    Lv = -(et[:, None] * Vh * v[b, h, s:e]).sum()
-                grads = torch.autograd.grad(Lv, Wg)
-                Ws = [w - g for w, g in zip(Ws, grads)]
-                if renorm:
-                    Ws = [w * (r.norm(dim=0, keepdim=True) / w.norm(dim=0, keepdim=True).clamp_min(1e-12))
-                          for w, r in zip(Ws, ref)]
-            if not chunk:
+                        Lv = -(et[:, None] * Vh * v[b, h, s:e]).sum()
+                    grads = torch.autograd.grad(Lv, Wg)
+                    new = []
+                    for i, (w, g) in enumerate(zip(Ws, grads)):
+                        if not upd[i]:
+                            new.append(w)
+                            continue
+                        if beta is not None:
+                            mom[i] = beta * mom[i] + g
+                            g = mom[i]
+                        w = w - g
+                        if renorm:
+                            w = w * (ref[i].norm(dim=0, keepdim=True) / w.norm(dim=0, keepdim=True).clamp_min(1e-12))
+                        new.append(w)
+                    Ws = new
+            if not causal:
                 O[b, h] = fwd(Ws, q[b, h])
     return O.detach().numpy()
 
@@ -185,6 +203,195 @@ def test_oracle_matches_autograd_layer(inner, loss, chunk, key_norm, renorm, per
     O, _ = orc.oracle_forward(q, k, v, W0, eps=1e-5, **args)
     O_ref = _torch_layer(q, k, v, W0, args["eta_scale"], eta_tok, loss, inner, chunk, key_norm, 1e-5, renorm)
     np.testing.assert_allclose(O, O_ref, rtol=1e-10, atol=1e-12)
+
+
+# the update variants against the same independent derivation: epochs,
+# first-layer-only, sequential mini-batches read at the end, read-only chunks,
+# heavy-ball momentum (with re-norm where the pages pair it with the rule)
+@pytest.mark.parametrize("inner,loss,chunk,opts", [
+    (orc.INNER_MLP, orc.LOSS_MSE, 0, dict(epochs=3)),
+    (orc.INNER_SWIGLU, orc.LOSS_DOT, 0, dict(epochs=2, renorm=True)),
+    (orc.INNER_MLP, orc.LOSS_MSE, 0, dict(update_mask=[True, False])),
+    (orc.INNER_SWIGLU, orc.LOSS_DOT, 5, dict(update_mask=[True, False, True], renorm=True)),
+    (orc.INNER_MLP, orc.LOSS_MSE, 4, dict(write_then_query=True)),
+    (orc.INNER_SWIGLU, orc.LOSS_DOT, 5, dict(write_then_query=True, key_norm=True, epochs=2)),
+    (orc.INNER_SWIGLU, orc.LOSS_DOT, 4, dict(chunk_update=[1, 0, 0, 1, 1], renorm=True)),
+    (orc.INNER_MLP, orc.LOSS_DOT, 6, dict(chunk_update=[0, 1, 0], write_then_query=True)),
+    (orc.INNER_SWIGLU, orc.LOSS_DOT, 5, dict(beta=0.9, renorm=True)),
+    (orc.INNER_MLP, orc.LOSS_MSE, 0, dict(beta=0.5, epochs=3, update_mask=[False, True])),
+])
+def test_update_variants_match_autograd_layer(inner, loss, chunk, opts):
+    rng = np.random.default_rng(12)
+    q, k, v, W0 = _rand_case(rng, B=2, H=2, N=17, d=5, h=7, inner=inner)
+    eta_tok = 0.1 + rng.random((2, 2, 17))
+    opts = dict(opts)
+    key_norm = opts.pop("key_norm", False)
+    renorm = opts.pop("renorm", False)
+    beta = opts.pop("beta", None)
+    O, _ = orc.oracle_forward(q, k, v, W0, eta_scale=0.8, eta_tok=eta_tok, loss=loss, inner=inner, chunk=chunk,
+                              key_norm=key_norm, renorm=renorm,
+                              rule=orc.RULE_GD if beta is None else orc.RULE_MOMENTUM, beta=beta or 0.0,
+                              order=orc.ORDER_WRITE_THEN_QUERY if opts.get("write_then_query") else orc.ORDER_CAUSAL,
+                              epochs=opts.get("epochs", 1), update_mask=opts.get("update_mask"),
+                              chunk_update=opts.get("chunk_update"))
+    O_ref = _torch_layer(q, k, v, W0, 0.8, eta_tok, loss, inner, chunk, key_norm, 1e-5, renorm, beta=beta, **opts)
+    np.testing.assert_allclose(O, O_ref, rtol=1e-10, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Newton-Schulz orthogonalisation (Muon) and the update rules in closed form
+# --------------------------------------------------------------------------
+def _ns_by_svd(M, steps):
+    """What the published iteration does, through the SVD: every singular value
+    s of M / ||M||_F goes through p(s) = a s + b s^3 + c s^5 `steps` times; the
+    singular vectors stay."""
+    a, b, c = 3.4445, -4.7750, 2.0315
+    U, S, Vt = np.linalg.svd(M, full_matrices=False)
+    s = S / (np.linalg.norm(M) + 1e-7)
+    for _ in range(steps):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return (U * s) @ Vt
+
+
+@pytest.mark.parametrize("shape", [(5, 8), (8, 5), (6, 6), (16, 48)])
+@pytest.mark.parametrize("steps", [1, 5])
+def test_newton_schulz_acts_on_singular_values(shape, steps):
+    M = np.random.default_rng(21).standard_normal(shape)
+    np.testing.assert_allclose(orc.newton_schulz(M, steps), _ns_by_svd(M, steps), rtol=1e-9, atol=1e-11)
+
+
+def test_newton_schulz_five_steps_nearly_orthogonal():
+    """Muon's five steps bring every singular value of a well-conditioned
+    matrix into roughly [0.7, 1.2] (the quintic is tuned for fast, not exact,
+    convergence)."""
+    M = np.random.default_rng(22).standard_normal((32, 64))
+    s = np.linalg.svd(orc.newton_schulz(M, 5), compute_uv=False)
+    assert s.min() > 0.6 and s.max() < 1.25, s
+
+
+def _lin_dot_case(rng, N=24, d=4):
+    q = rng.standard_normal((1, 1, N, d))
+    k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    eta_tok = 0.2 + rng.random((1, 1, N))
+    return q, k, v, [np.zeros((1, d, d))], eta_tok
+
+
+def test_momentum_linear_dot_closed_form():
+    """Linear inner model, dot loss, W0 = 0: the chunk gradient g_j =
+    -K_j^T diag(eta_j) V_j does not depend on W, so heavy-ball momentum gives
+    W_c = sum_{j<c} (1 - beta^(c-j)) / (1 - beta) K_j^T diag(eta_j) V_j and
+    O_c = Q_c W_c (block-causal linear attention with geometric weights)."""
+    rng = np.random.default_rng(23)
+    q, k, v, W0, et = _lin_dot_case(rng)
+    C, beta = 6, 0.7
+    O, _ = orc.oracle_forward(q, k, v, W0, eta_tok=et, loss=orc.LOSS_DOT, inner=orc.INNER_LINEAR, chunk=C,
+                              key_norm=False, rule=orc.RULE_MOMENTUM, beta=beta)
+    Q, K, V, E = q[0, 0], k[0, 0], v[0, 0], et[0, 0]
+    for c in range(4):
+        W = np.zeros((4, 4))
+        for j in range(c):
+            sl = slice(j * C, (j + 1) * C)
+            W += (1 - beta ** (c - j)) / (1 - beta) * K[sl].T @ (E[sl, None] * V[sl])
+        np.testing.assert_allclose(O[0, 0, c * C:(c + 1) * C], Q[c * C:(c + 1) * C] @ W, rtol=1e-11, atol=1e-12)
+
+
+def test_muon_linear_dot_closed_form():
+    """Linear inner model, dot loss, W0 = 0, Muon without momentum: each chunk
+    adds s NS(K_j^T diag(eta_j) V_j) (NS is odd), with NS through the SVD."""
+    rng = np.random.default_rng(24)
+    q, k, v, W0, et = _lin_dot_case(rng, N=30, d=5)
+    C, scale = 10, 0.3
+    O, Wf = orc.oracle_forward(q, k, v, W0, eta_tok=et, loss=orc.LOSS_DOT, inner=orc.INNER_LINEAR, chunk=C,
+                               key_norm=False, rule=orc.RULE_MUON, beta=0.0, muon_scale=scale, ns_steps=5)
+    Q, K, V, E = q[0, 0], k[0, 0], v[0, 0], et[0, 0]
+    W = np.zeros((5, 5))
+    for c in range(3):
+        sl = slice(c * C, (c + 1) * C)
+        np.testing.assert_allclose(O[0, 0, sl], Q[sl] @ W, rtol=1e-9, atol=1e-11)
+        W = W + scale * _ns_by_svd(K[sl].T @ (E[sl, None] * V[sl]), 5)
+    np.testing.assert_allclose(Wf[0][0, 0], W, rtol=1e-9, atol=1e-11)
+
+
+def test_epochs_linear_mse_closed_form():
+    """E epochs of full-batch GD on the linear model with MSE:
+    W_E = (I - a S)^E W0 + sum_{j<E} (I - a S)^j a K^T V, S = K^T K,
+    a = eta 2 / (N d) (key norm off)."""
+    rng = np.random.default_rng(25)
+    N, d, E, eta = 20, 4, 4, 3.0
+    q = rng.standard_normal((1, 1, N, d))
+    k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    W0 = [rng.standard_normal((1, d, d)) * 0.5]
+    _, Wf = orc.oracle_forward(q, k, v, W0, eta_scale=eta, loss=orc.LOSS_MSE, inner=orc.INNER_LINEAR, chunk=0,
+                               key_norm=False, epochs=E)
+    K, V = k[0, 0], v[0, 0]
+    a = eta * 2.0 / (N * d)
+    T = np.eye(d) - a * K.T @ K
+    want = np.linalg.matrix_power(T, E) @ W0[0][0]
+    want += sum(np.linalg.matrix_power(T, j) @ (a * K.T @ V) for j in range(E))
+    np.testing.assert_allclose(Wf[0][0, 0], want, rtol=1e-11, atol=1e-12)
+
+
+def test_first_layer_only_keeps_second_layer():
+    """Only the first layer adjusted [TvS]: W2 stays W0's, W1 takes the same
+    step as in the full update (both gradients are taken at W0)."""
+    rng = np.random.default_rng(26)
+    q, k, v, W0 = _rand_case(rng, B=2, H=2, N=15, d=4, h=6)
+    O, Wf = orc.oracle_forward(q, k, v, W0, update_mask=[True, False])
+    _, Wfull = orc.oracle_forward(q, k, v, W0)
+    np.testing.assert_array_equal(Wf[1], np.broadcast_to(W0[1][None], Wf[1].shape))
+    np.testing.assert_allclose(Wf[0], Wfull[0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(O, orc.oracle_readout(q, Wf, orc.INNER_MLP), rtol=1e-13, atol=1e-14)
+
+
+def test_write_then_query_dot_linear_equals_full_batch():
+    """With the dot loss the linear model's gradient does not depend on W, so
+    sequential mini-batches that all write before the queries read give the
+    full-batch result: linear attention eta Q (K^T V) at W0 = 0."""
+    rng = np.random.default_rng(27)
+    q, k, v, W0, et = _lin_dot_case(rng, N=23)
+    args = dict(eta_tok=et, loss=orc.LOSS_DOT, inner=orc.INNER_LINEAR, key_norm=False)
+    O_seq, W_seq = orc.oracle_forward(q, k, v, W0, chunk=5, order=orc.ORDER_WRITE_THEN_QUERY, **args)
+    O_full, W_full = orc.oracle_forward(q, k, v, W0, chunk=0, **args)
+    np.testing.assert_allclose(O_seq, O_full, rtol=1e-12, atol=1e-13)
+    Q, K, V, E = q[0, 0], k[0, 0], v[0, 0], et[0, 0]
+    np.testing.assert_allclose(O_full[0, 0], Q @ (K.T @ (E[:, None] * V)), rtol=1e-12, atol=1e-13)
+
+
+def test_read_only_chunks_block_causal():
+    """Read-only chunks [LaCT, video]: O_c = Q_c sum_{j<c, j writes}
+    K_j^T diag(eta_j) V_j for the linear model with dot loss at W0 = 0; with
+    no writing chunk every query reads W0 and W0 is returned."""
+    rng = np.random.default_rng(28)
+    q, k, v, W0, et = _lin_dot_case(rng, N=25)
+    C, mask = 5, [1, 0, 1, 0, 1]
+    args = dict(eta_tok=et, loss=orc.LOSS_DOT, inner=orc.INNER_LINEAR, key_norm=False, chunk=C)
+    O, _ = orc.oracle_forward(q, k, v, W0, chunk_update=mask, **args)
+    Q, K, V, E = q[0, 0], k[0, 0], v[0, 0], et[0, 0]
+    for c in range(5):
+        W = sum((K[j * C:(j + 1) * C].T @ (E[j * C:(j + 1) * C, None] * V[j * C:(j + 1) * C])
+                 for j in range(c) if mask[j]), np.zeros((4, 4)))
+        np.testing.assert_allclose(O[0, 0, c * C:(c + 1) * C], Q[c * C:(c + 1) * C] @ W, rtol=1e-11, atol=1e-12)
+    rng2 = np.random.default_rng(29)
+    q2, k2, v2, W02 = _rand_case(rng2, N=12, d=4, h=6, inner=orc.INNER_SWIGLU)
+    O2, Wf2 = orc.oracle_forward(q2, k2, v2, W02, inner=orc.INNER_SWIGLU, loss=orc.LOSS_DOT, chunk=4,
+                                 key_norm=False, chunk_update=[0, 0, 0], renorm=True)
+    np.testing.assert_array_equal(O2, orc.oracle_readout(q2, [w[None] for w in W02], orc.INNER_SWIGLU))
+    for a, b in zip(Wf2, W02):
+        np.testing.assert_array_equal(a[0, 0], b[0])
+
+
+def test_renorm_applies_to_updated_matrices_only():
+    rng = np.random.default_rng(30)
+    q, k, v, W0 = _rand_case(rng, N=12, d=4, h=6, inner=orc.INNER_SWIGLU, wscale=1.0)
+    _, Wf = orc.oracle_forward(q, k, v, W0, inner=orc.INNER_SWIGLU, loss=orc.LOSS_DOT, chunk=4, key_norm=False,
+                               renorm=True, update_mask=[False, True, True], rule=orc.RULE_MOMENTUM, beta=0.5)
+    np.testing.assert_array_equal(Wf[0][0, 0], W0[0][0])
+    for i in (1, 2):
+        np.testing.assert_allclose(np.linalg.norm(Wf[i][0, 0], axis=0), np.linalg.norm(W0[i][0], axis=0),
+                                   rtol=1e-12)
+        assert np.max(np.abs(Wf[i][0, 0] - W0[i][0])) > 1e-3
 
 
 # --------------------------------------------------------------------------
