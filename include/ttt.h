@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 1
+#define TTT_ABI_VERSION 2
 
 typedef enum {
   TTT_OK = 0,
@@ -130,6 +130,56 @@ typedef struct {
   const float* per_token;
 } ttt_eta;
 
+/* Update rule applied to the eta-weighted gradient G of every update batch
+ * (LaCT page, "Nonlinear memory complements local attention": gradient
+ * descent, momentum and Muon, the last turning the matrix gradient into an
+ * orthogonalised matrix by Newton-Schulz iterations; L2 normalisation, when
+ * renorm is on, follows every update):
+ *   TTT_RULE_GD      : W <- W - G
+ *   TTT_RULE_MOMENTUM: M <- beta M + G,  W <- W - M          (M starts at 0)
+ *   TTT_RULE_MUON    : M <- beta M + G,  W <- W - muon_scale NS(M)
+ * NS is the quintic Newton-Schulz iteration of the published Muon optimiser:
+ * X = M / (||M||_F + 1e-7), then ns_steps times X <- a X + (b A + c A^2) X with
+ * A = X X^T and (a, b, c) = (3.4445, -4.7750, 2.0315), on the wide orientation
+ * of M (a tall matrix is transposed and back).  Computed in fp32.  The
+ * momentum of one call starts at zero (it is not carried across calls). */
+typedef enum { TTT_RULE_GD = 0, TTT_RULE_MOMENTUM = 1, TTT_RULE_MUON = 2 } ttt_rule;
+
+/* Order of reads and writes with chunk > 0 (LaCT page, "Order of operations
+ * excludes leaking the future"; ViT3 page, section 03 guideline 2):
+ *   TTT_ORDER_CAUSAL          : each chunk reads the weights left by the chunks
+ *                               before it, then updates them (language, video);
+ *                               key_norm is rejected (it would read the future).
+ *   TTT_ORDER_WRITE_THEN_QUERY: the chunks update in turn (sequential
+ *                               mini-batches), then every query reads the final
+ *                               weights (sets of images); key_norm allowed. */
+typedef enum { TTT_ORDER_CAUSAL = 0, TTT_ORDER_WRITE_THEN_QUERY = 1 } ttt_order;
+
+/* Per-call options of ttt_forward_ex.  A zero-initialised struct (or a NULL
+ * pointer) gives the plain layer: one epoch, every matrix updated, causal
+ * order, every chunk writes, gradient descent.
+ *   epochs       gradient steps on each update batch (0 or 1: one step; ViT3
+ *                page, section 03 guideline 2: several epochs)
+ *   update_mask  bit i set: matrix i of the inner model is updated; the others
+ *                keep W0 (0: every matrix).  0x1 adjusts only the first layer
+ *                (Test-Time Training vs Sleep page, "Side one").
+ *   order        ttt_order (used when chunk > 0)
+ *   chunk_update HOST array of ceil(N / chunk) flags, or NULL: a chunk whose
+ *                flag is 0 only reads (its keys and values are not trained on;
+ *                video: clean chunks write, noisy chunks read, LaCT page)
+ *   rule, beta, muon_scale, ns_steps: the update rule (ttt_rule); ns_steps 0
+ *                means 5; muon_scale must be finite (TTT_RULE_MUON) */
+typedef struct {
+  int epochs;
+  unsigned update_mask;
+  int order;
+  const unsigned char* chunk_update;
+  int rule;
+  float beta;
+  float muon_scale;
+  int ns_steps;
+} ttt_options;
+
 typedef struct ttt_handle ttt_handle;
 
 /* Version of this ABI (TTT_ABI_VERSION). */
@@ -162,6 +212,20 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v,
                 const ttt_weights* W0, const ttt_eta* eta, int loss, int inner, int chunk,
                 void* o, const ttt_weights_out* W_out, void* workspace, size_t ws_bytes,
                 void* stream);
+
+/* ttt_forward with per-call options (NULL: the plain layer; see ttt_options).
+ * The workspace must hold ttt_workspace_bytes_ex(..., opt, ...) bytes. */
+int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v,
+                   const ttt_weights* W0, const ttt_eta* eta, int loss, int inner, int chunk,
+                   const ttt_options* opt, void* o, const ttt_weights_out* W_out,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of a ttt_forward_ex request (opt NULL: the plain layer). */
+int ttt_workspace_bytes_ex(const ttt_handle* h, int loss, int inner, int chunk, const ttt_options* opt,
+                           size_t* bytes);
+
+/* Kernel family ttt_forward_ex would use; NULL for an invalid request. */
+const char* ttt_path_name_ex(const ttt_handle* h, int loss, int inner, int chunk, const ttt_options* opt);
 
 /* ttt_forward for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).

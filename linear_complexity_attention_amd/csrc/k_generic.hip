@@ -284,10 +284,21 @@ __global__ void k_check_finite(const void* o, int bf, long long n, const float* 
 
 __global__ void k_zero_flag(int* flag) { if (threadIdx.x == 0) *flag = 0; }
 
+__global__ void __launch_bounds__(256) k_fill_zero(float* p, long long n) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = 0.f;
+}
+
 }  // namespace
 
 void launch_zero_flag(int* flag, hipStream_t st) {
   hipLaunchKernelGGL(k_zero_flag, dim3(1), dim3(64), 0, st, flag);
+}
+
+void launch_fill_zero(float* p, long long n, hipStream_t st) {
+  long long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
 }
 
 void launch_gen_grad_out(const Problem& pb, const WRef& W, int t0, int nt, float* gbuf, hipStream_t st) {

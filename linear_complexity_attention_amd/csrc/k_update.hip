@@ -3,6 +3,11 @@
 //
 //   W_next = W_cur - sum_s partial_s        (eta is already inside the partials,
 //                                            ViT3 summary page, section 02 update)
+//   momentum (LaCT analysis page, update rules): M = beta M + sum_s partial_s,
+//           W_next = W_cur - M; Muon folds the partials into M the same way and
+//           leaves the step to the Newton-Schulz kernels (k_muon.hip)
+//   matrices outside the update mask keep W_cur (Test-Time Training vs Sleep
+//   page, "Side one": only the first layer adjusted)
 //   renorm: every output column of every [in, out] matrix is rescaled to the L2
 //           norm that column has in W0 (LaCT analysis page, section "Nonlinear
 //           memory complements local attention": L2 normalisation after the update)
@@ -46,12 +51,19 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
   if (e >= wsz) return;
   const int i = (int)(e / pb.msz);
   const long long o = e - (long long)i * pb.msz;           // offset inside matrix i (msz % 4 == 0)
-  float4 w = *reinterpret_cast<const float4*>(a.cur.mat(i, b, h) + o);
-  auto sub = [&](const float* q) {
-    const float4 d = *reinterpret_cast<const float4*>(q + e);
-    w.x -= d.x; w.y -= d.y; w.z -= d.z; w.w -= d.w;
+  const float4 wc = *reinterpret_cast<const float4*>(a.cur.mat(i, b, h) + o);
+  float4 w = wc;
+  const bool upd = (a.mask >> i) & 1u;
+  const bool gd = a.rule == RULE_GD;
+  // gradient descent subtracts the partials one by one; the momentum rules sum
+  // them first (same order) and fold the sum into M
+  float4 g = {0.f, 0.f, 0.f, 0.f};
+  auto take = [&](const float4& d) {
+    if (gd) { w.x -= d.x; w.y -= d.y; w.z -= d.z; w.w -= d.w; }
+    else { g.x += d.x; g.y += d.y; g.z += d.z; g.w += d.w; }
   };
-  if (a.part_mode == PART_SPLITS) {           // four splits' loads in flight, subtracted in split order
+  if (!upd) {
+  } else if (a.part_mode == PART_SPLITS) {    // four splits' loads in flight, taken in split order
     const float* pp = a.part + (size_t)p * wsz;
     for (int s = 0; s < a.S; s += 4) {
       float4 d[4];
@@ -60,12 +72,19 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
         if (s + u < a.S) d[u] = *reinterpret_cast<const float4*>(pp + (s + u) * a.part_pair_stride + e);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (s + u < a.S) { w.x -= d[u].x; w.y -= d[u].y; w.z -= d[u].z; w.w -= d[u].w; }
+        if (s + u < a.S) take(d[u]);
     }
   } else {
     long long q0, q1, C;
     sk_range(a, pb.B * pb.H, p, q0, q1, C);
-    for (long long q = q0; q <= q1; ++q) sub(a.part + slot_of(a, p, q, q0, C) * wsz);
+    for (long long q = q0; q <= q1; ++q) take(*reinterpret_cast<const float4*>(a.part + slot_of(a, p, q, q0, C) * wsz + e));
+  }
+  if (upd && !gd) {
+    float4* mp = reinterpret_cast<float4*>(a.mom + (size_t)p * wsz + e);
+    float4 m = *mp;
+    m.x = a.beta * m.x + g.x; m.y = a.beta * m.y + g.y; m.z = a.beta * m.z + g.z; m.w = a.beta * m.w + g.w;
+    *mp = m;
+    if (!a.mom_only) { w.x = wc.x - m.x; w.y = wc.y - m.y; w.z = wc.z - m.z; w.w = wc.w - m.w; }
   }
   *reinterpret_cast<float4*>(a.next + (size_t)p * wsz + e) = w;
   if (a.out[i]) *reinterpret_cast<float4*>(a.out[i] + (size_t)p * pb.msz + o) = w;
@@ -105,8 +124,10 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
   float c4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) c4[i] = cur[base + i * step];
+  const bool upd = (a.mask >> mat) & 1u;
   long long q0, q1, C;
   sk_range(a, pb.B * pb.H, p, q0, q1, C);
+  if (!upd) q1 = q0 - 1;          // a matrix outside the mask keeps W_cur
   // the pair's slots, four loads in flight at a time, added in workgroup order
   float4 sum = {0.f, 0.f, 0.f, 0.f};
   for (long long q = q0; q <= q1; q += 4) {
@@ -121,10 +142,16 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
   float* nxt = a.next + (size_t)p * wsz + (size_t)mat * D * HID;
   float* out = a.out[mat] ? a.out[mat] + (size_t)p * D * HID : nullptr;
   const float s4[4] = {sum.x, sum.y, sum.z, sum.w};
+  float* mom = (upd && a.rule != RULE_GD) ? a.mom + (size_t)p * wsz + (size_t)mat * D * HID : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = base + i * step;
-    const float w = c4[i] - s4[i];
+    float w = c4[i] - s4[i];
+    if (mom) {
+      const float m = a.beta * mom[e] + s4[i];
+      mom[e] = m;
+      w = a.mom_only ? c4[i] : c4[i] - m;
+    }
     nxt[e] = w;
     if (out) out[e] = w;
   }
@@ -180,7 +207,9 @@ __global__ void __launch_bounds__(kRCols * kRLanes) k_renorm(Problem pb, UpdateA
   float sn = 0.f, sr = 0.f;
 #pragma unroll
   for (int l = 0; l < kWaves; ++l) { sn += red[0][l][cl]; sr += red[1][l][cl]; }
-  const float scale = sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f);
+  // matrices outside the update mask kept W_cur, whose columns already have
+  // W0's norms: they are only copied to W_out
+  const float scale = ((a.mask >> i) & 1u) ? sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f) : 1.0f;
   float* out = a.out[i] ? a.out[i] + (size_t)p * pb.msz : nullptr;
 #pragma unroll
   for (int k = 0; k < RMAX; ++k) {
@@ -199,7 +228,9 @@ __global__ void __launch_bounds__(kRCols * kRLanes) k_renorm(Problem pb, UpdateA
   }
 }
 
-static void launch_renorm(const Problem& pb, const UpdateArgs& a, hipStream_t st) {
+}  // namespace
+
+void launch_renorm(const Problem& pb, const UpdateArgs& a, hipStream_t st) {
   const int P = pb.B * pb.H;
   const int side = pb.inner == INNER_LINEAR ? pb.d : (pb.hid > pb.d ? pb.hid : pb.d);   // max rows, max cols
   dim3 g((side + kRCols - 1) / kRCols, pb.nm, P);
@@ -207,6 +238,8 @@ static void launch_renorm(const Problem& pb, const UpdateArgs& a, hipStream_t st
   else if (side <= 4 * kRLanes) hipLaunchKernelGGL(k_renorm<4>, g, dim3(kRCols * kRLanes), 0, st, pb, a);
   else hipLaunchKernelGGL(k_renorm<8>, g, dim3(kRCols * kRLanes), 0, st, pb, a);
 }
+
+namespace {
 
 // Update and re-norm in one kernel for shapes the float4 path cannot take.
 // grid = (column blocks, nm, P); thread = (column, row lane).
@@ -225,16 +258,34 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, Up
   long long q0 = 0, q1 = -1, C = 1;
   if (a.part_mode == PART_STREAMK) sk_range(a, pb.B * pb.H, p, q0, q1, C);
   __shared__ float red[2][kLanes][kCols];
+  const bool upd = (a.mask >> i) & 1u;
+  const bool gd = a.rule == RULE_GD;
+  float* mom = (upd && !gd) ? a.mom + (size_t)p * wsz + (size_t)i * pb.msz : nullptr;
   float nn = 0.f, nr = 0.f;
   if (live)
     for (int r = lane; r < rows; r += kLanes) {
       const size_t e = (size_t)r * cols + j;
-      float w = cur[e];
-      if (a.part_mode == PART_SPLITS) {
-        const float* pp = a.part + (size_t)p * wsz + (size_t)i * pb.msz + e;
-        for (int s = 0; s < a.S; ++s) w -= pp[s * a.part_pair_stride];
-      } else {
-        for (long long q = q0; q <= q1; ++q) w -= a.part[slot_of(a, p, q, q0, C) * wsz + (size_t)i * pb.msz + e];
+      const float wc = cur[e];
+      float w = wc, g = 0.f;
+      if (upd) {
+        if (a.part_mode == PART_SPLITS) {
+          const float* pp = a.part + (size_t)p * wsz + (size_t)i * pb.msz + e;
+          for (int s = 0; s < a.S; ++s) {
+            if (gd) w -= pp[s * a.part_pair_stride];
+            else g += pp[s * a.part_pair_stride];
+          }
+        } else {
+          for (long long q = q0; q <= q1; ++q) {
+            const float d = a.part[slot_of(a, p, q, q0, C) * wsz + (size_t)i * pb.msz + e];
+            if (gd) w -= d;
+            else g += d;
+          }
+        }
+      }
+      if (mom) {
+        const float m = a.beta * mom[e] + g;
+        mom[e] = m;
+        if (!a.mom_only) w = wc - m;
       }
       nxt[e] = w;
       nn += w * w;
@@ -246,7 +297,7 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, Up
   __syncthreads();
   float sn = 0.f, sr = 0.f;
   for (int l = 0; l < kLanes; ++l) { sn += red[0][l][threadIdx.x % kCols]; sr += red[1][l][threadIdx.x % kCols]; }
-  const float scale = a.renorm ? sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f) : 1.f;
+  const float scale = (a.renorm && upd) ? sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f) : 1.f;
   if (!live) return;
   float* out = a.out[i] ? a.out[i] + (size_t)p * pb.msz : nullptr;
   for (int r = lane; r < rows; r += kLanes) {
@@ -259,8 +310,13 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, Up
 
 }  // namespace
 
-void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st) {
+void launch_update(const Problem& pb, const UpdateArgs& a_in, hipStream_t st) {
   const int P = pb.B * pb.H;
+  UpdateArgs a = a_in;
+  if (a.mom_only) {               // Muon: only M is updated here; the step, re-norm and W_out follow
+    a.renorm = 0;
+    for (int i = 0; i < 3; ++i) a.out[i] = nullptr;
+  }
   if (a.part_mode == PART_STREAMK) {
     // partials of the MFMA gradient kernel (GELU MLP, d = 64)
     UpdateArgs f = a;

@@ -83,7 +83,7 @@ struct Plan {
   int S_stats, S_grad;               // S_grad: partial slots of the gradient kernel
   int sk_G, sk_J;                    // stream-K geometry (MFMA gradient kernel)
   // byte offsets
-  size_t off_stats_part, off_stats, off_states, off_part, off_gbuf, off_flag, total;
+  size_t off_stats_part, off_stats, off_states, off_part, off_gbuf, off_mom, off_muon, off_flag, total;
   long long state_stride;            // floats between consecutive states
 };
 
@@ -103,19 +103,59 @@ int stats_splits(long long pairs, int tokens) {
   return (int)s;
 }
 
-int check_request(ttt_handle* h, int loss, int inner, int chunk) {
+// ttt_options with the defaults filled in
+struct Opts {
+  int epochs = 1;
+  unsigned mask = 0;
+  bool causal = false;              // chunk > 0 and TTT_ORDER_CAUSAL
+  const unsigned char* chunk_update = nullptr;
+  int rule = RULE_GD;
+  float beta = 0.f, muon_scale = 1.f;
+  int ns_steps = 5;
+};
+
+int check_request(ttt_handle* h, int loss, int inner, int chunk, const ttt_options* o, Opts* out) {
   const ttt_config& c = h->cfg;
   if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT) return fail(h, TTT_ERR_INVALID, "unknown loss %d", loss);
   if (inner != TTT_INNER_LINEAR && inner != TTT_INNER_MLP_GELU && inner != TTT_INNER_SWIGLU)
     return fail(h, TTT_ERR_INVALID, "unknown inner model %d", inner);
   if (chunk < 0) return fail(h, TTT_ERR_INVALID, "chunk must be >= 0 (got %d)", chunk);
-  if (chunk > 0 && c.key_norm)
+  Opts op;
+  const int nm = n_mats(inner);
+  op.mask = (1u << nm) - 1;
+  if (o) {
+    if (o->epochs < 0) return fail(h, TTT_ERR_INVALID, "epochs must be >= 0 (got %d)", o->epochs);
+    if (o->epochs > 1) op.epochs = o->epochs;
+    if (o->update_mask & ~op.mask)
+      return fail(h, TTT_ERR_INVALID, "update_mask 0x%x names matrices the inner model does not have (%d)",
+                  o->update_mask, nm);
+    if (o->update_mask) op.mask = o->update_mask;
+    if (o->order != TTT_ORDER_CAUSAL && o->order != TTT_ORDER_WRITE_THEN_QUERY)
+      return fail(h, TTT_ERR_INVALID, "unknown order %d", o->order);
+    op.causal = chunk > 0 && o->order == TTT_ORDER_CAUSAL;
+    op.chunk_update = o->chunk_update;
+    if (o->rule != TTT_RULE_GD && o->rule != TTT_RULE_MOMENTUM && o->rule != TTT_RULE_MUON)
+      return fail(h, TTT_ERR_INVALID, "unknown update rule %d", o->rule);
+    op.rule = o->rule == TTT_RULE_GD ? RULE_GD : o->rule == TTT_RULE_MOMENTUM ? RULE_MOMENTUM : RULE_MUON;
+    if (!std::isfinite(o->beta)) return fail(h, TTT_ERR_INVALID, "beta must be finite");
+    op.beta = o->beta;
+    if (op.rule == RULE_MUON && !std::isfinite(o->muon_scale))
+      return fail(h, TTT_ERR_INVALID, "muon_scale must be finite");
+    op.muon_scale = o->muon_scale;
+    if (o->ns_steps < 0 || o->ns_steps > 64) return fail(h, TTT_ERR_INVALID, "ns_steps must be in 0..64");
+    if (o->ns_steps) op.ns_steps = o->ns_steps;
+  } else {
+    op.causal = chunk > 0;
+  }
+  if (op.causal && c.key_norm)
     return fail(h, TTT_ERR_UNSUPPORTED,
-                "key_norm with chunk > 0: whole-sequence key statistics would read future keys");
+                "key_norm with causal chunks: whole-sequence key statistics would read future keys");
   if (inner != TTT_INNER_LINEAR && (c.hidden < 1 || c.hidden > 512))
     return fail(h, TTT_ERR_UNSUPPORTED, "hidden must be in 1..512 (got %d)", c.hidden);
   const long long nb = chunk ? (c.N + (long long)chunk - 1) / chunk : 1;
   if (nb > 65535) return fail(h, TTT_ERR_UNSUPPORTED, "too many chunks (%lld > 65535)", nb);
+  if (nb * op.epochs > (1LL << 20)) return fail(h, TTT_ERR_UNSUPPORTED, "too many updates (%lld)", nb * op.epochs);
+  if (out) *out = op;
   return TTT_OK;
 }
 
@@ -132,7 +172,7 @@ Problem make_problem(const ttt_handle* h, int loss, int inner) {
   return pb;
 }
 
-Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk) {
+Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk, const Opts& op) {
   const ttt_config& c = h->cfg;
   Problem pb = make_problem(h, loss, inner);
   Plan pl{};
@@ -148,7 +188,7 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk) {
   // A chain of several causal updates feeds each step's rounding into the next
   // (the recurrence amplifies weight perturbations), so bf16 weight operands are
   // used for a single update only; multi-chunk MLP gradients stay in fp32.
-  pl.mfma_grad = !generic_only && mfma_full_supported(pb) && pl.nb == 1;
+  pl.mfma_grad = !generic_only && mfma_full_supported(pb) && pl.nb == 1 && op.epochs == 1;
   pl.mfma_query = !generic_only && mfma_query_supported(pb);
   pl.lact_grad = !generic_only && !c.key_norm && lact_supported(pb);
   pl.lact_query = !generic_only && lact_readout_supported(pb);
@@ -177,6 +217,10 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk) {
   off = align256(off + sizeof(float) * (size_t)pl.S_grad * (pl.mfma_grad ? 1 : pl.P) * pl.wsz);
   pl.off_gbuf = off;
   if (!pl.mfma_grad && !pl.lact_grad) off = align256(off + sizeof(float) * (size_t)pl.P * pl.span * c.d);
+  pl.off_mom = off;
+  if (op.rule != RULE_GD) off = align256(off + sizeof(float) * (size_t)pl.P * pl.wsz);
+  pl.off_muon = off;
+  if (op.rule == RULE_MUON) off = align256(off + sizeof(float) * muon_scratch_floats(pb));
   pl.off_flag = off;
   off = align256(off + 64);
   pl.total = off;
@@ -253,20 +297,27 @@ int ttt_destroy(ttt_handle* h) {
 
 const char* ttt_last_error(const ttt_handle* h) { return h ? h->err.c_str() : g_create_err.c_str(); }
 
-int ttt_workspace_bytes(const ttt_handle* hc, int loss, int inner, int chunk, size_t* bytes) {
+int ttt_workspace_bytes_ex(const ttt_handle* hc, int loss, int inner, int chunk, const ttt_options* opt,
+                           size_t* bytes) {
   ttt_handle* h = const_cast<ttt_handle*>(hc);
   if (!h) return fail(nullptr, TTT_ERR_INVALID, "handle is NULL");
   if (!bytes) return fail(h, TTT_ERR_INVALID, "bytes is NULL");
-  int rc = check_request(h, loss, inner, chunk);
+  Opts op;
+  int rc = check_request(h, loss, inner, chunk, opt, &op);
   if (rc) return rc;
-  *bytes = make_plan(h, loss, inner, chunk).total;
+  *bytes = make_plan(h, loss, inner, chunk, op).total;
   return TTT_OK;
 }
 
-const char* ttt_path_name(const ttt_handle* hc, int loss, int inner, int chunk) {
+int ttt_workspace_bytes(const ttt_handle* h, int loss, int inner, int chunk, size_t* bytes) {
+  return ttt_workspace_bytes_ex(h, loss, inner, chunk, nullptr, bytes);
+}
+
+const char* ttt_path_name_ex(const ttt_handle* hc, int loss, int inner, int chunk, const ttt_options* opt) {
   ttt_handle* h = const_cast<ttt_handle*>(hc);
-  if (!h || check_request(h, loss, inner, chunk)) return nullptr;
-  Plan pl = make_plan(h, loss, inner, chunk);
+  Opts op;
+  if (!h || check_request(h, loss, inner, chunk, opt, &op)) return nullptr;
+  Plan pl = make_plan(h, loss, inner, chunk, op);
   if (pl.mfma_grad && pl.mfma_query) return "mfma";
   if (pl.mfma_query) return "generic_grad+mfma_query";
   if (pl.lact_grad && pl.lact_query) return "mfma_swiglu";
@@ -274,12 +325,17 @@ const char* ttt_path_name(const ttt_handle* hc, int loss, int inner, int chunk) 
   return "generic";
 }
 
-int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
-                const ttt_eta* eta, int loss, int inner, int chunk, void* o, const ttt_weights_out* W_out,
-                void* workspace, size_t ws_bytes, void* stream) {
+const char* ttt_path_name(const ttt_handle* h, int loss, int inner, int chunk) {
+  return ttt_path_name_ex(h, loss, inner, chunk, nullptr);
+}
+
+int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
+                   const ttt_eta* eta, int loss, int inner, int chunk, const ttt_options* opt, void* o,
+                   const ttt_weights_out* W_out, void* workspace, size_t ws_bytes, void* stream) {
   if (!h) return fail(nullptr, TTT_ERR_INVALID, "handle is NULL");
   h->err.clear();
-  int rc = check_request(h, loss, inner, chunk);
+  Opts op;
+  int rc = check_request(h, loss, inner, chunk, opt, &op);
   if (rc) return rc;
   const ttt_config& c = h->cfg;
   if (!q || !k || !v || !o) return fail(h, TTT_ERR_INVALID, "q, k, v and o must be non-NULL");
@@ -292,7 +348,7 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
   Problem pb = make_problem(h, loss, inner);
   if (W0->batch_stride != 0 && W0->batch_stride < (long long)c.H * pb.msz)
     return fail(h, TTT_ERR_INVALID, "W0.batch_stride must be 0 or >= H*in*out (%lld)", (long long)c.H * pb.msz);
-  Plan pl = make_plan(h, loss, inner, chunk);
+  Plan pl = make_plan(h, loss, inner, chunk, op);
   if (!workspace) return fail(h, TTT_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", pl.total);
   if (ws_bytes < pl.total) return fail(h, TTT_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, pl.total);
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(h, TTT_ERR_INVALID, "workspace must be 256-byte aligned");
@@ -304,6 +360,8 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
   float* states = reinterpret_cast<float*>(ws + pl.off_states);
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
   float* gbuf = reinterpret_cast<float*>(ws + pl.off_gbuf);
+  float* mom = reinterpret_cast<float*>(ws + pl.off_mom);
+  float* muon = reinterpret_cast<float*>(ws + pl.off_muon);
   int* flag = reinterpret_cast<int*>(ws + pl.off_flag);
 
   pb.q = q; pb.k = k; pb.v = v; pb.o = o;
@@ -313,8 +371,10 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
 
   const bool log = (c.flags & TTT_FLAG_LOG) || env_log();
   if (log)
-    std::fprintf(stderr, "[ttt] B=%d H=%d N=%d d=%d h=%d %s inner=%d loss=%d chunk=%d nb=%d grad=%s(S=%d) query=%s ws=%zu\n",
-                 c.B, c.H, c.N, c.d, pb.hid, pb.bf16 ? "bf16" : "f32", inner, loss, chunk, pl.nb,
+    std::fprintf(stderr, "[ttt] B=%d H=%d N=%d d=%d h=%d %s inner=%d loss=%d chunk=%d nb=%d epochs=%d mask=0x%x "
+                 "%s rule=%d grad=%s(S=%d) query=%s ws=%zu\n",
+                 c.B, c.H, c.N, c.d, pb.hid, pb.bf16 ? "bf16" : "f32", inner, loss, chunk, pl.nb, op.epochs, op.mask,
+                 op.causal ? "causal" : "write-then-query", op.rule,
                  pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu" : "generic", pl.S_grad,
                  pl.mfma_query ? "mfma" : pl.lact_query ? "mfma_swiglu" : "generic", pl.total);
 
@@ -345,49 +405,91 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
     // read finished (mu, rstd) pairs
     if (!pl.mfma_grad) launch_stats_final(pb, pl.S_stats, stats_part, c.eps, stats, st);
   }
+  if (op.rule != RULE_GD) {     // the momentum starts at zero: a fill kernel (graph-capture safe)
+    launch_fill_zero(mom, (long long)pl.P * pl.wsz, st);
+  }
   mark(1);
 
+  // update batches in order; state b + 1 holds the weights after batch b
+  bool first_step = true;
   for (int b = 0; b < pl.nb; ++b) {
     const int t0 = chunk ? b * chunk : 0;
     const int nt = chunk ? std::min(chunk, c.N - t0) : c.N;
     const WRef cur = b == 0 ? w0 : state_ref(b);
-    if (b == 0) mark(2);
-    if (pl.lact_grad) {
-      launch_lact_grad(pb, cur, t0, nt, pl.S_grad, eta->scale, part, st);
-    } else if (pl.mfma_grad) {
-      // the kernel accumulates eta_n-weighted (V_hat - V) or -eta_n V; the
-      // scalar eta and the MSE constant 2/(n_b d) are applied to its partials
-      const float scale = pb.loss == LOSS_MSE ? eta->scale * 2.0f / ((float)nt * (float)c.d) : eta->scale;
-      launch_mfma_full_grad(pb, cur, t0, nt, scale, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part, st);
-    } else {
-      launch_gen_grad_out(pb, cur, t0, nt, gbuf, st);
-      launch_gen_dW(pb, cur, t0, nt, gbuf, pl.S_grad, part, st);
-    }
-    if (b == 0) mark(3);
+    float* next = states + (long long)b * pl.state_stride;
+    const bool last_batch = b == pl.nb - 1;
     UpdateArgs ua{};
-    ua.cur = cur;
     ua.w0 = w0;
-    ua.part = part;
-    ua.part_mode = pl.mfma_grad ? PART_STREAMK : PART_SPLITS;
-    ua.S = pl.S_grad;
-    ua.part_pair_stride = (long long)pl.P * pl.wsz;
-    if (pl.mfma_grad) mfma_grad_geometry(pb, nt, &ua.sk_G, &ua.sk_J, &ua.sk_tpp);
-    ua.next = states + (long long)b * pl.state_stride;
-    const bool last = b == pl.nb - 1;
-    for (int i = 0; i < 3; ++i) ua.out[i] = (last && W_out && i < nm) ? W_out->w[i] : nullptr;
+    ua.next = next;
+    ua.mask = op.mask;
     ua.renorm = c.renorm;
-    if (b == 0) mark(4);
-    launch_update(pb, ua, st);
-    if (b == 0) mark(5);
+    ua.rule = op.rule;
+    ua.beta = op.beta;
+    ua.mom = mom;
+    ua.part_pair_stride = (long long)pl.P * pl.wsz;
+    if (op.chunk_update && !op.chunk_update[b]) {
+      // read-only batch: W_{b+1} = W_b (an update with no partials)
+      ua.cur = cur;
+      ua.part = part;
+      ua.part_mode = PART_SPLITS;
+      ua.S = 0;
+      ua.rule = RULE_GD;
+      ua.renorm = 0;
+      for (int i = 0; i < 3; ++i) ua.out[i] = (last_batch && W_out && i < nm) ? W_out->w[i] : nullptr;
+      launch_update(pb, ua, st);
+      continue;
+    }
+    for (int e = 0; e < op.epochs; ++e) {
+      // later epochs of a batch read and rewrite state b + 1 in place
+      const WRef src = e == 0 ? cur : state_ref(b + 1);
+      if (first_step) mark(2);
+      if (pl.lact_grad) {
+        launch_lact_grad(pb, src, t0, nt, pl.S_grad, eta->scale, part, st);
+      } else if (pl.mfma_grad) {
+        // the kernel accumulates eta_n-weighted (V_hat - V) or -eta_n V; the
+        // scalar eta and the MSE constant 2/(n_b d) are applied to its partials
+        const float scale = pb.loss == LOSS_MSE ? eta->scale * 2.0f / ((float)nt * (float)c.d) : eta->scale;
+        launch_mfma_full_grad(pb, src, t0, nt, scale, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part, st);
+      } else {
+        launch_gen_grad_out(pb, src, t0, nt, gbuf, st);
+        launch_gen_dW(pb, src, t0, nt, gbuf, pl.S_grad, part, st);
+      }
+      if (first_step) mark(3);
+      ua.cur = src;
+      ua.part = part;
+      ua.part_mode = pl.mfma_grad ? PART_STREAMK : PART_SPLITS;
+      ua.S = pl.S_grad;
+      if (pl.mfma_grad) mfma_grad_geometry(pb, nt, &ua.sk_G, &ua.sk_J, &ua.sk_tpp);
+      const bool last = last_batch && e == op.epochs - 1;
+      for (int i = 0; i < 3; ++i) ua.out[i] = (last && W_out && i < nm) ? W_out->w[i] : nullptr;
+      ua.mom_only = op.rule == RULE_MUON;
+      if (first_step) mark(4);
+      launch_update(pb, ua, st);
+      if (op.rule == RULE_MUON) {
+        // W_{b+1} = W_b - s NS(M) (next already holds W_b), then the re-norm
+        float* mout[3] = {nullptr, nullptr, nullptr};
+        if (!c.renorm)
+          for (int i = 0; i < 3; ++i) mout[i] = ua.out[i];
+        launch_muon(pb, mom, next, mout, op.mask, op.muon_scale, op.ns_steps, muon, st);
+        if (c.renorm) launch_renorm(pb, ua, st);
+      }
+      if (first_step) mark(5);
+      first_step = false;
+    }
   }
 
   mark(6);
+  // causal chunks read the state their chunk starts from; otherwise every
+  // query reads the final state (write-then-query)
+  const float* rstates = op.causal ? states : states + (long long)(pl.nb - 1) * pl.state_stride;
+  const int rchunk = op.causal ? chunk : 0;
+  const int rn = op.causal ? pl.nb : 1;
   if (pl.mfma_query) {
-    launch_mfma_query(pb, w0, states, pl.state_stride, chunk ? pl.nb : 1, chunk, st);
+    launch_mfma_query(pb, w0, rstates, pl.state_stride, rn, rchunk, st);
   } else if (pl.lact_query) {
-    launch_lact_readout(pb, w0, states, pl.state_stride, chunk ? pl.nb : 1, chunk, st);
+    launch_lact_readout(pb, w0, rstates, pl.state_stride, rn, rchunk, st);
   } else {
-    launch_gen_query(pb, w0, states, pl.state_stride, chunk ? pl.nb : 1, chunk, st);
+    launch_gen_query(pb, w0, rstates, pl.state_stride, rn, rchunk, st);
   }
   mark(7);
   hipError_t e = hipGetLastError();
@@ -407,6 +509,12 @@ int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, cons
     if (hflag) return fail(h, TTT_ERR_NONFINITE, "O or the final fast weights contain NaN/Inf");
   }
   return TTT_OK;
+}
+
+int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
+                const ttt_eta* eta, int loss, int inner, int chunk, void* o, const ttt_weights_out* W_out,
+                void* workspace, size_t ws_bytes, void* stream) {
+  return ttt_forward_ex(h, q, k, v, W0, eta, loss, inner, chunk, nullptr, o, W_out, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -55,10 +55,16 @@ struct UpdateArgs {
                                 // (see k_update_streamk)
   int S; long long part_pair_stride;
   int sk_G, sk_J, sk_tpp;       // stream-K geometry of the gradient kernel
-  float* next;                  // [P][nm][msz] fp32
+  float* next;                  // [P][nm][msz] fp32 (may alias cur: every element is read, then written, by one thread)
   float* out[3];                // W_out matrices [B,H,in,out] or null
   int renorm;
+  unsigned mask;                // bit i: matrix i is updated (others: next = cur, momentum untouched)
+  int rule;                     // RULE_*: GD subtracts the partials; MOMENTUM and MUON fold them into mom
+  float beta;                   // momentum coefficient
+  float* mom;                   // [P][nm][msz] momentum (MOMENTUM, MUON) or null
+  int mom_only;                 // MUON: update mom and copy cur to next; the Muon step follows
 };
+enum { RULE_GD = 0, RULE_MOMENTUM = 1, RULE_MUON = 2 };
 enum { PART_SPLITS = 0, PART_STREAMK = 1 };
 
 // Stream-K split of the MFMA gradient kernel.  The (pair, 32-token tile) space
@@ -105,6 +111,8 @@ __host__ __device__ inline long long sk_slot(long long p, long long q, long long
   return q * J + (q == q0 ? p - sk_first_pair(q0, G, C, tpp) : 0);
 }
 void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st);
+// column re-norm of a.next in place (matrices in a.mask), writing a.out
+void launch_renorm(const Problem& pb, const UpdateArgs& a, hipStream_t st);
 
 // ---- MFMA fast paths --------------------------------------------------------
 // GELU-MLP, d = 64, h in {64,128,256}, bf16 tensors: fused forward/backward of
@@ -142,6 +150,16 @@ bool lact_readout_supported(const Problem& pb);
 void launch_lact_readout(const Problem& pb, const WRef& w0, const float* states, long long state_stride,
                          int nchunks, int chunk, hipStream_t st);
 
+// ---- Muon: Newton-Schulz orthogonalisation of the momentum matrices --------
+// For every (pair, updated matrix): X = mom / (||mom||_F + 1e-7) on the wide
+// orientation, ns_steps quintic iterations, then next -= scale * X (back in the
+// [in, out] orientation); W_out is written when out[i] is set.  xa, xb: two
+// [P][nm][m*n] buffers, ga, gb: two [P][nm][m*m] buffers (m = min(in, out),
+// n = max(in, out)).
+size_t muon_scratch_floats(const Problem& pb);
+void launch_muon(const Problem& pb, const float* mom, float* next, float* const* out, unsigned mask, float scale,
+                 int ns_steps, float* scratch, hipStream_t st);
+
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cu_count();
 
@@ -154,6 +172,8 @@ int set_error(ttt_handle* h, int code, const char* fmt, ...);
 
 // ---- finiteness check ------------------------------------------------------
 void launch_zero_flag(int* flag, hipStream_t st);
+// n floats at p set to zero by a fill kernel (no memset node under graph capture)
+void launch_fill_zero(float* p, long long n, hipStream_t st);
 void launch_check_finite(const Problem& pb, float* const* wfinal, long long wcount, int* flag,
                          hipStream_t st);
 

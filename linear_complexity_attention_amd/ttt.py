@@ -36,7 +36,12 @@ TTT_LOSS_MSE, TTT_LOSS_DOT = 0, 1
 TTT_INNER_LINEAR, TTT_INNER_MLP_GELU, TTT_INNER_SWIGLU = 0, 1, 2
 TTT_FLAG_CHECK_FINITE, TTT_FLAG_FORCE_GENERIC, TTT_FLAG_LOG = 0x1, 0x2, 0x4
 
+TTT_RULE_GD, TTT_RULE_MOMENTUM, TTT_RULE_MUON = 0, 1, 2
+TTT_ORDER_CAUSAL, TTT_ORDER_WRITE_THEN_QUERY = 0, 1
+
 LOSSES = {"mse": TTT_LOSS_MSE, "dot": TTT_LOSS_DOT}
+RULES = {"gd": TTT_RULE_GD, "momentum": TTT_RULE_MOMENTUM, "muon": TTT_RULE_MUON}
+ORDERS = {"causal": TTT_ORDER_CAUSAL, "write_then_query": TTT_ORDER_WRITE_THEN_QUERY}
 INNERS = {"linear": TTT_INNER_LINEAR, "mlp_gelu": TTT_INNER_MLP_GELU, "swiglu": TTT_INNER_SWIGLU}
 N_MATRICES = {TTT_INNER_LINEAR: 1, TTT_INNER_MLP_GELU: 2, TTT_INNER_SWIGLU: 3}
 
@@ -59,6 +64,11 @@ class ttt_eta(ctypes.Structure):
     _fields_ = [("scale", c_float), ("per_token", c_void_p)]
 
 
+class ttt_options(ctypes.Structure):
+    _fields_ = [("epochs", c_int), ("update_mask", c_uint), ("order", c_int), ("chunk_update", c_void_p),
+                ("rule", c_int), ("beta", c_float), ("muon_scale", c_float), ("ns_steps", c_int)]
+
+
 _lib.ttt_version.restype = c_int
 _lib.ttt_version.argtypes = []
 _lib.ttt_create.restype = c_int
@@ -69,6 +79,14 @@ _lib.ttt_forward.restype = c_int
 _lib.ttt_forward.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(ttt_weights), POINTER(ttt_eta),
                              c_int, c_int, c_int, c_void_p, POINTER(ttt_weights_out), c_void_p, c_size_t,
                              c_void_p]
+_lib.ttt_forward_ex.restype = c_int
+_lib.ttt_forward_ex.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(ttt_weights), POINTER(ttt_eta),
+                                c_int, c_int, c_int, POINTER(ttt_options), c_void_p, POINTER(ttt_weights_out),
+                                c_void_p, c_size_t, c_void_p]
+_lib.ttt_workspace_bytes_ex.restype = c_int
+_lib.ttt_workspace_bytes_ex.argtypes = [c_void_p, c_int, c_int, c_int, POINTER(ttt_options), POINTER(c_size_t)]
+_lib.ttt_path_name_ex.restype = c_char_p
+_lib.ttt_path_name_ex.argtypes = [c_void_p, c_int, c_int, c_int, POINTER(ttt_options)]
 _lib.ttt_forward_noalloc.restype = c_int
 _lib.ttt_forward_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(ttt_weights),
                                      POINTER(ttt_eta), c_int, c_int, c_int, c_void_p, POINTER(ttt_weights_out),
@@ -85,8 +103,9 @@ _lib.ttt_last_error.argtypes = [c_void_p]
 _lib.ttt_status_string.restype = c_char_p
 _lib.ttt_status_string.argtypes = [c_int]
 
-EXPORTED = ("ttt_version", "ttt_create", "ttt_workspace_bytes", "ttt_forward", "ttt_forward_noalloc",
-            "ttt_path_name", "ttt_set_timing_events", "ttt_destroy", "ttt_last_error", "ttt_status_string")
+EXPORTED = ("ttt_version", "ttt_create", "ttt_workspace_bytes", "ttt_workspace_bytes_ex", "ttt_forward",
+            "ttt_forward_ex", "ttt_forward_noalloc", "ttt_path_name", "ttt_path_name_ex", "ttt_set_timing_events",
+            "ttt_destroy", "ttt_last_error", "ttt_status_string")
 
 
 def matrix_shapes(inner: int, d: int, hidden: int):
@@ -142,6 +161,47 @@ def ttt_workspace_bytes(handle, loss: int, inner: int, chunk: int) -> int:
 def ttt_path_name(handle, loss: int, inner: int, chunk: int):
     r = _lib.ttt_path_name(handle, loss, inner, chunk)
     return r.decode() if r is not None else None
+
+
+def ttt_workspace_bytes_ex(handle, loss: int, inner: int, chunk: int, opt) -> int:
+    n = c_size_t()
+    rc = _lib.ttt_workspace_bytes_ex(handle, loss, inner, chunk, byref(opt) if opt is not None else None, byref(n))
+    if rc != TTT_OK:
+        raise TTTError(rc, ttt_last_error(handle))
+    return n.value
+
+
+def ttt_path_name_ex(handle, loss: int, inner: int, chunk: int, opt):
+    r = _lib.ttt_path_name_ex(handle, loss, inner, chunk, byref(opt) if opt is not None else None)
+    return r.decode() if r is not None else None
+
+
+def ttt_forward_ex(handle, q, k, v, W0: ttt_weights, eta: ttt_eta, loss: int, inner: int, chunk: int, opt, o,
+                   W_out, workspace, ws_bytes: int, stream) -> int:
+    """Raw call with per-call options (a ttt_options or None); returns the
+    status code without raising."""
+    return _lib.ttt_forward_ex(handle, q, k, v, byref(W0), byref(eta), loss, inner, chunk,
+                               byref(opt) if opt is not None else None, o,
+                               byref(W_out) if W_out is not None else None, workspace, ws_bytes, stream)
+
+
+def make_options(*, epochs=1, update_mask=0, order="causal", chunk_update=None, rule="gd", beta=0.0,
+                 muon_scale=1.0, ns_steps=5):
+    """A ttt_options from keyword values; chunk_update (a sequence of 0/1 per
+    chunk) is kept alive on the returned struct."""
+    opt = ttt_options()
+    opt.epochs = int(epochs)
+    opt.update_mask = int(update_mask)
+    opt.order = ORDERS[order] if isinstance(order, str) else int(order)
+    opt.rule = RULES[rule] if isinstance(rule, str) else int(rule)
+    opt.beta = float(beta)
+    opt.muon_scale = float(muon_scale)
+    opt.ns_steps = int(ns_steps)
+    if chunk_update is not None:
+        buf = (ctypes.c_ubyte * len(chunk_update))(*[1 if x else 0 for x in chunk_update])
+        opt._chunk_update_buf = buf
+        opt.chunk_update = ctypes.cast(buf, c_void_p)
+    return opt
 
 
 def ttt_set_timing_events(handle, events) -> None:
@@ -201,14 +261,15 @@ class TTTLayer:
             except Exception:   # interpreter teardown: nothing left to release into
                 pass
 
-    def workspace_bytes(self, loss="mse", inner="mlp_gelu", chunk=0) -> int:
-        return ttt_workspace_bytes(self.handle, LOSSES[loss], INNERS[inner], chunk)
+    def workspace_bytes(self, loss="mse", inner="mlp_gelu", chunk=0, options=None) -> int:
+        return ttt_workspace_bytes_ex(self.handle, LOSSES[loss], INNERS[inner], chunk, options)
 
-    def path_name(self, loss="mse", inner="mlp_gelu", chunk=0):
-        return ttt_path_name(self.handle, LOSSES[loss], INNERS[inner], chunk)
+    def path_name(self, loss="mse", inner="mlp_gelu", chunk=0, options=None):
+        return ttt_path_name_ex(self.handle, LOSSES[loss], INNERS[inner], chunk, options)
 
     def forward(self, q, k, v, W0, *, eta=1.0, eta_tok=None, loss="mse", inner="mlp_gelu", chunk=0,
-                out=None, W_out=None):
+                out=None, W_out=None, options=None):
+        """options: None (the plain layer) or a ttt_options (make_options)."""
         import torch
 
         c = self.cfg
@@ -256,7 +317,12 @@ class TTTLayer:
                         or tuple(w.shape) != (c.B, c.H, fi, fo)):
                     raise ValueError(f"W_out[{i}] must be a contiguous float32 tensor on {q.device} of shape "
                                      f"{(c.B, c.H, fi, fo)}")
-        nbytes = ttt_workspace_bytes(self.handle, li, ii, chunk)
+        nbytes = ttt_workspace_bytes_ex(self.handle, li, ii, chunk, options)
+        if options is not None and options.chunk_update:
+            nb = (c.N + chunk - 1) // chunk if chunk else 1
+            buf = getattr(options, "_chunk_update_buf", None)
+            if buf is None or len(buf) != nb:
+                raise ValueError(f"chunk_update needs {nb} flags (build the options with make_options)")
         if self._ws is None or self._ws.numel() < nbytes or self._ws.device != q.device:
             self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
         wts = ttt_weights()
@@ -270,8 +336,8 @@ class TTTLayer:
             for i, w in enumerate(W_out):
                 wo.w[i] = w.data_ptr() if w is not None else None
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = ttt_forward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), wts, e, li, ii, chunk,
-                         out.data_ptr(), wo, self._ws.data_ptr(), self._ws.numel(), stream)
+        rc = ttt_forward_ex(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), wts, e, li, ii, chunk, options,
+                            out.data_ptr(), wo, self._ws.data_ptr(), self._ws.numel(), stream)
         if rc != TTT_OK:
             raise TTTError(rc, ttt_last_error(self.handle))
         return out

@@ -23,7 +23,7 @@ def device_inputs(w: Workload, *, B=None, H=None, N=None, seed=None, shared_w0=T
     return (tq, tk, tv, tW, tet), exact
 
 
-def run_gpu(w: Workload, dev_in, *, flags=0, eta=None, return_weights=True, chunk=None, eps=1e-5):
+def run_gpu(w: Workload, dev_in, *, flags=0, eta=None, return_weights=True, chunk=None, eps=1e-5, options=None):
     from linear_complexity_attention_amd import ttt
 
     tq, tk, tv, tW, tet = dev_in
@@ -34,17 +34,19 @@ def run_gpu(w: Workload, dev_in, *, flags=0, eta=None, return_weights=True, chun
     if return_weights:
         W_out = [torch.empty((B, H) + tuple(m.shape[-2:]), dtype=torch.float32, device=tq.device) for m in tW]
     O = layer.forward(tq, tk, tv, tW, eta=w.eta if eta is None else eta, eta_tok=tet, loss=w.loss,
-                      inner=w.inner, chunk=w.chunk if chunk is None else chunk, W_out=W_out)
+                      inner=w.inner, chunk=w.chunk if chunk is None else chunk, W_out=W_out, options=options)
     torch.cuda.synchronize()
-    path = layer.path_name(w.loss, w.inner, w.chunk if chunk is None else chunk)
+    path = layer.path_name(w.loss, w.inner, w.chunk if chunk is None else chunk, options)
     return O, W_out, path
 
 
-def run_oracle(w: Workload, exact, *, pairs=None, eta=None, chunk=None, eps=1e-5):
+def run_oracle(w: Workload, exact, *, pairs=None, eta=None, chunk=None, eps=1e-5, okw=None):
     """Oracle on all pairs, or on the listed (b, h) pairs only (each pair is
-    independent, so a slice of the inputs gives that pair's exact result)."""
+    independent, so a slice of the inputs gives that pair's exact result);
+    okw: extra oracle keywords (update variants)."""
     kw = dict(eta_scale=w.eta if eta is None else eta, loss=w.loss, inner=w.inner,
               chunk=w.chunk if chunk is None else chunk, key_norm=w.key_norm, eps=eps, renorm=w.renorm)
+    kw.update(okw or {})
     if pairs is None:
         return orc.oracle_forward(exact["q"], exact["k"], exact["v"], exact["W0"], eta_tok=exact["eta_tok"], **kw)
     Os, Ws = [], []

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert ttt.ttt_version() == 1
+    assert ttt.ttt_version() == 2
     assert ttt.ttt_status_string(0) == "ok"
     assert "workspace" in ttt.ttt_status_string(5)
 
@@ -125,3 +125,15 @@ def test_noalloc_rejects_oversize_request_on_host():
                                        None) == ttt.TTT_ERR_INVALID
     finally:
         ttt.ttt_destroy(h)
+
+
+def test_options_rejected_on_the_host():
+    layer = ttt.TTTLayer(1, 2, 64, 64, 128, key_norm=True)
+    for opts in (dict(update_mask=4), dict(rule=7), dict(order=5), dict(epochs=-1), dict(beta=float("nan"))):
+        with pytest.raises(ttt.TTTError) as ei:
+            layer.workspace_bytes("mse", "mlp_gelu", 0, ttt.make_options(**opts))
+        assert ei.value.status == ttt.TTT_ERR_INVALID, opts
+    with pytest.raises(ttt.TTTError) as ei:       # causal chunks with key norm: would read the future
+        layer.workspace_bytes("mse", "mlp_gelu", 16, ttt.make_options())
+    assert ei.value.status == ttt.TTT_ERR_UNSUPPORTED
+    assert layer.workspace_bytes("mse", "mlp_gelu", 16, ttt.make_options(order="write_then_query")) > 0
