@@ -47,6 +47,9 @@ from scipy.special import erf, expit
 INNER_LINEAR = "linear"
 INNER_MLP = "mlp_gelu"
 INNER_SWIGLU = "swiglu"
+INNER_GLU = "glu"
+INNER_DWCONV = "dwconv"
+INNER_VIT3 = "vit3"
 LOSS_MSE = "mse"
 LOSS_DOT = "dot"
 
@@ -101,10 +104,55 @@ def key_instnorm(K, eps):
 #   swiglu : F(x) = (silu(x W1) * (x W3)) W2, W1, W3 [d, h], W2 [h, d]
 # W is a list: [W] / [W1, W2] / [W1, W2, W3].
 # ---------------------------------------------------------------------------
-def inner_forward(inner, W, X):
+# ViT3 §03 guideline 6 / §04 and its glossary: the simplified gated linear
+# unit FC(x) * SiLU(FC(x)) (two d x d maps, no output projection; reading: no
+# biases, W[0] is the plain branch, W[1] the gated one) and the depthwise
+# convolution, whose kernel is the fast weight: the tokens form a gh x gw
+# raster (token t = i gw + j) and channel c of the output is the k x k
+# cross-correlation of channel c of the input with w[c] (reading: zero padding
+# of (k - 1) / 2 on every side, stride 1, no bias; w stored [d, k*k], tap
+# (a, b) at a k + b).
+def _pad_raster(X, grid, r):
+    gh, gw = grid
+    return np.pad(X.reshape(gh, gw, -1), ((r, r), (r, r), (0, 0)))
+
+
+def dwconv(X, w, grid):
+    """Depthwise k x k cross-correlation of the [N, d] raster X with w [d, k*k]."""
+    gh, gw = grid
+    k = int(round(math.sqrt(w.shape[1])))
+    r = (k - 1) // 2
+    Xp = _pad_raster(X, grid, r)
+    out = np.zeros((gh, gw, X.shape[1]))
+    for a in range(k):
+        for b in range(k):
+            out += Xp[a:a + gh, b:b + gw, :] * w[:, a * k + b]
+    return out.reshape(gh * gw, -1)
+
+
+def dwconv_weight_grad(X, G, grid, k):
+    """dL/dw [d, k*k] of the depthwise convolution given G = dL/dout [N, d]."""
+    gh, gw = grid
+    r = (k - 1) // 2
+    Xp = _pad_raster(X, grid, r)
+    Gr = G.reshape(gh, gw, -1)
+    dw = np.zeros((G.shape[1], k * k))
+    for a in range(k):
+        for b in range(k):
+            dw[:, a * k + b] = np.sum(Gr * Xp[a:a + gh, b:b + gw, :], axis=(0, 1))
+    return dw
+
+
+def inner_forward(inner, W, X, grid=None):
     """Returns (F_W(X), cache) -- cache holds what the hand backward needs."""
     if inner == INNER_LINEAR:
         return X @ W[0], None
+    if inner == INNER_GLU:
+        U = X @ W[0]
+        Z = X @ W[1]
+        return U * silu(Z), (U, Z)
+    if inner == INNER_DWCONV:
+        return dwconv(X, W[0], grid), None
     if inner == INNER_MLP:
         Z = X @ W[0]
         A = gelu(Z)
@@ -117,16 +165,24 @@ def inner_forward(inner, W, X):
     raise ValueError(f"unknown inner model {inner!r}")
 
 
-def inner_backward(inner, W, X, G, cache):
+def inner_backward(inner, W, X, G, cache, grid=None):
     """Hand-derived dL/dW given G = dL/dF_W(X) ([ViT3 §02], step (ii)).
 
     MLP   : dW2 = A^T G ; dZ = (G W2^T) * gelu'(Z) ; dW1 = X^T dZ
     SwiGLU: dW2 = Hh^T G ; dH = G W2^T ; dZ1 = dH * Z3 * silu'(Z1) ;
             dZ3 = dH * silu(Z1) ; dW1 = X^T dZ1 ; dW3 = X^T dZ3
     linear: dW = X^T G
+    GLU   : dU = G * silu(Z) ; dZ = G * U * silu'(Z) ; dW1 = X^T dU ; dW2 = X^T dZ
+    DWConv: dw[c, tap] = sum over tokens of G[., c] times the tap's shifted X[., c]
     """
     if inner == INNER_LINEAR:
         return [X.T @ G]
+    if inner == INNER_GLU:
+        U, Z = cache
+        return [X.T @ (G * silu(Z)), X.T @ (G * U * silu_prime(Z))]
+    if inner == INNER_DWCONV:
+        k = int(round(math.sqrt(W[0].shape[1])))
+        return [dwconv_weight_grad(X, G, grid, k)]
     if inner == INNER_MLP:
         Z, A = cache
         dW2 = A.T @ G
@@ -235,19 +291,29 @@ def apply_rule(W, dW, M, rule, beta, muon_scale, ns_steps, update):
     return W, M
 
 
-def inner_step(inner, loss, W, X, V, eta_n):
+def inner_step(inner, loss, W, X, V, eta_n, grid=None):
     """One gradient step of the inner model on the mini-dataset (X, V).
 
     [ViT3 §02]: V̂ = F_W(X); W <- W - eta * dL(V̂, V)/dW.  Returns (W_new, dW).
     """
-    Vhat, cache = inner_forward(inner, W, X)
+    Vhat, cache = inner_forward(inner, W, X, grid)
     G = loss_grad(loss, Vhat, V, eta_n)
-    dW = inner_backward(inner, W, X, G, cache)
+    dW = inner_backward(inner, W, X, G, cache, grid)
     return [w - g for w, g in zip(W, dW)], dW
 
 
 def n_matrices(inner):
-    return {INNER_LINEAR: 1, INNER_MLP: 2, INNER_SWIGLU: 3}[inner]
+    return {INNER_LINEAR: 1, INNER_MLP: 2, INNER_SWIGLU: 3, INNER_GLU: 2, INNER_DWCONV: 1, INNER_VIT3: 3}[inner]
+
+
+def head_model(inner, h):
+    """ViT3 block [ViT3 §04]: one head uses the depthwise convolution, the other
+    heads the simplified GLU (reading: head 0 is the convolution head).  W0 of
+    "vit3" is [W1, W2, w_conv]; returns (inner model of head h, indices of the
+    matrices it uses)."""
+    if inner != INNER_VIT3:
+        return inner, list(range(n_matrices(inner)))
+    return (INNER_DWCONV, [2]) if h == 0 else (INNER_GLU, [0, 1])
 
 
 def _pair_weights(W0, b, h):
@@ -267,7 +333,7 @@ def oracle_forward(q, k, v, W0, *, eta_scale=1.0, eta_tok=None, loss=LOSS_MSE,
                    inner=INNER_MLP, chunk=0, key_norm=True, eps=1e-5,
                    renorm=False, epochs=1, update_mask=None, order=ORDER_CAUSAL,
                    chunk_update=None, rule=RULE_GD, beta=0.0, muon_scale=1.0,
-                   ns_steps=5):
+                   ns_steps=5, grid=None):
     """TTT-layer forward.  q, k, v: [B, H, N, d]; W0: list of matrices
     ([H, in, out] or [B, H, in, out]); eta_tok: None or [B, H, N].
 
@@ -288,6 +354,9 @@ def oracle_forward(q, k, v, W0, *, eta_scale=1.0, eta_tok=None, loss=LOSS_MSE,
     rule, beta, muon_scale, ns_steps: the update rule (see apply_rule).
     renorm     : after every update, each updated matrix's columns get their
                  W0 norms back [LaCT].
+    grid       : (gh, gw) token raster of the depthwise convolution (inner
+                 "dwconv", and "vit3", whose head 0 is a convolution head and
+                 whose other heads are GLU heads).
     Returns (O [B, H, N, d], W_final list of [B, H, in, out]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -307,9 +376,16 @@ def oracle_forward(q, k, v, W0, *, eta_scale=1.0, eta_tok=None, loss=LOSS_MSE,
     nm = n_matrices(inner)
     if len(W0) != nm:
         raise ValueError(f"{inner} needs {nm} matrices, got {len(W0)}")
-    update = [True] * nm if update_mask is None else [bool(x) for x in update_mask]
-    if len(update) != nm:
+    update_all = [True] * nm if update_mask is None else [bool(x) for x in update_mask]
+    if len(update_all) != nm:
         raise ValueError("update_mask needs one flag per matrix")
+    if inner in (INNER_DWCONV, INNER_VIT3):
+        if grid is None or grid[0] * grid[1] != N:
+            raise ValueError("the convolution needs a token grid with gh * gw == N")
+        if chunk > 0:
+            raise ValueError("the convolution inner model is full batch only")
+        if rule == RULE_MUON or renorm:
+            raise ValueError("Muon and the column re-norm are defined for matrices, not convolution kernels")
     span = chunk if chunk > 0 else N
     nb = (N + span - 1) // span
     if chunk_update is not None and len(chunk_update) != nb:
@@ -318,7 +394,10 @@ def oracle_forward(q, k, v, W0, *, eta_scale=1.0, eta_tok=None, loss=LOSS_MSE,
     W_final = [np.zeros((B, H) + np.asarray(w).shape[-2:]) for w in W0]
     for b in range(B):
         for h in range(H):
-            Wref = _pair_weights(W0, b, h)
+            model, used = head_model(inner, h)
+            allw = _pair_weights(W0, b, h)
+            Wref = [allw[i] for i in used]
+            update = [update_all[i] for i in used]
             W = [w.copy() for w in Wref]
             M = [np.zeros_like(w) for w in Wref]
             Q, K, V = q[b, h], k[b, h], v[b, h]
@@ -329,29 +408,30 @@ def oracle_forward(q, k, v, W0, *, eta_scale=1.0, eta_tok=None, loss=LOSS_MSE,
             for c in range(nb):
                 s, e = c * span, min((c + 1) * span, N)
                 if causal:
-                    O[b, h, s:e] = inner_forward(inner, W, Q[s:e])[0]   # read
+                    O[b, h, s:e] = inner_forward(model, W, Q[s:e])[0]   # read
                 if chunk_update is not None and not chunk_update[c]:
                     continue                                              # read-only chunk
                 for _ in range(epochs):
-                    Vhat, cache = inner_forward(inner, W, Kh[s:e])
+                    Vhat, cache = inner_forward(model, W, Kh[s:e], grid)
                     G = loss_grad(loss, Vhat, V[s:e], eta[s:e])
-                    dW = inner_backward(inner, W, Kh[s:e], G, cache)
+                    dW = inner_backward(model, W, Kh[s:e], G, cache, grid)
                     W, M = apply_rule(W, dW, M, rule, beta, muon_scale, ns_steps, update)
                     if renorm:
                         W = [column_renorm(w, r) if u else w for w, r, u in zip(W, Wref, update)]
             if not causal:
-                O[b, h] = inner_forward(inner, W, Q)[0]                   # write, then query
-            for i in range(nm):
-                W_final[i][b, h] = W[i]
+                O[b, h] = inner_forward(model, W, Q, grid)[0]             # write, then query
+            for i in range(nm):                 # matrices a head does not use stay W0
+                W_final[i][b, h] = W[used.index(i)] if i in used else allw[i]
     return O, W_final
 
 
-def oracle_readout(q, W, inner):
+def oracle_readout(q, W, inner, grid=None):
     """O = F_W(Q) for per-pair weights W ([B, H, in, out] each) -- step (iii)."""
     q = np.asarray(q, dtype=np.float64)
     B, H = q.shape[:2]
     O = np.zeros_like(q)
     for b in range(B):
         for h in range(H):
-            O[b, h] = inner_forward(inner, [np.asarray(w, np.float64)[b, h] for w in W], q[b, h])[0]
+            model, used = head_model(inner, h)
+            O[b, h] = inner_forward(model, [np.asarray(W[i], np.float64)[b, h] for i in used], q[b, h], grid)[0]
     return O

@@ -599,3 +599,168 @@ def test_synthetic_inputs_follow_recipe():
     for m in W0:
         np.testing.assert_allclose(np.sqrt((m.astype(np.float64) ** 2).sum(axis=-2)), 1.0, rtol=1e-5)
     assert et.shape == (1, 4, 64) and float(et.min()) > 0.0
+
+
+# --------------------------------------------------------------------------
+# ViT3's inner models: simplified GLU and the depthwise convolution, and the
+# ViT3 head split (one convolution head, the others GLU heads)
+# --------------------------------------------------------------------------
+def _grid_case(rng, B=1, H=1, gh=5, gw=6, d=4, k=3, shift=0.5):
+    N = gh * gw
+    q = rng.standard_normal((B, H, N, d))
+    kk = rng.standard_normal((B, H, N, d)) + shift
+    v = rng.standard_normal((B, H, N, d))
+    return q, kk, v, (gh, gw), N
+
+
+@pytest.mark.parametrize("loss", [orc.LOSS_MSE, orc.LOSS_DOT])
+def test_glu_and_dwconv_backward_by_finite_differences(loss):
+    rng = np.random.default_rng(40)
+    gh, gw, d, k = 4, 5, 3, 3
+    N = gh * gw
+    X = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    eta = 0.3 + rng.random(N)
+    for inner, W in ((orc.INNER_GLU, [rng.standard_normal((d, d)) * 0.7, rng.standard_normal((d, d)) * 0.7]),
+                     (orc.INNER_DWCONV, [rng.standard_normal((d, k * k)) * 0.5])):
+        def L(Ws):
+            Vh, _ = orc.inner_forward(inner, Ws, X, (gh, gw))
+            if loss == orc.LOSS_MSE:
+                return float(np.sum(eta[:, None] * (Vh - V) ** 2) / V.size)
+            return float(-np.sum(eta[:, None] * Vh * V))
+
+        Vh, cache = orc.inner_forward(inner, W, X, (gh, gw))
+        dW = orc.inner_backward(inner, W, X, orc.loss_grad(loss, Vh, V, eta), cache, (gh, gw))
+        for i, w in enumerate(W):
+            fd = np.zeros_like(w)
+            for idx in np.ndindex(w.shape):
+                wp = [x.copy() for x in W]
+                wm = [x.copy() for x in W]
+                wp[i][idx] += 1e-6
+                wm[i][idx] -= 1e-6
+                fd[idx] = (L(wp) - L(wm)) / 2e-6
+            np.testing.assert_allclose(dW[i], fd, rtol=1e-6, atol=1e-9, err_msg=f"{inner} dW{i}")
+
+
+def _torch_vit3(q, k, v, W0, grid, eta_scale, eta_tok, loss, inner, key_norm, epochs, beta=None):
+    """GLU with F.silu, the depthwise convolution with F.conv2d(groups=d),
+    gradients by autograd; inner "vit3" = head 0 convolution, other heads GLU."""
+    F = torch.nn.functional
+    q, k, v = (torch.tensor(a, dtype=torch.float64) for a in (q, k, v))
+    B, H, N, d = q.shape
+    gh, gw = grid
+    if key_norm:
+        k = F.instance_norm(k.reshape(B * H, N, d).transpose(1, 2), eps=1e-5).transpose(1, 2).reshape(B, H, N, d)
+    eta = torch.full((B, H, N), float(eta_scale), dtype=torch.float64)
+    if eta_tok is not None:
+        eta = eta * torch.tensor(eta_tok, dtype=torch.float64)
+
+    def conv(x, w):                       # x [N, d], w [d, k*k]
+        kk = int(round(math.sqrt(w.shape[1])))
+        img = x.T.reshape(1, d, gh, gw)
+        out = F.conv2d(img, w.reshape(d, 1, kk, kk), padding=(kk - 1) // 2, groups=d)
+        return out.reshape(d, N).T
+
+    def fwd(model, Ws, x):
+        if model == orc.INNER_GLU:
+            return (x @ Ws[0]) * F.silu(x @ Ws[1])
+        return conv(x, Ws[0])
+
+    O = torch.zeros_like(q)
+    for b in range(B):
+        for h in range(H):
+            model, used = orc.head_model(inner, h)
+            Ws = [torch.tensor(np.asarray(W0[i])[h], dtype=torch.float64) for i in used]
+            mom = [torch.zeros_like(w) for w in Ws]
+            for _ in range(epochs):
+                Wg = [w.clone().requires_grad_(True) for w in Ws]
+                Vh = fwd(model, Wg, k[b, h])
+                et = eta[b, h]
+                if loss == orc.LOSS_MSE:
+                    Lv = (et[:, None] * (Vh - v[b, h]) ** 2).mean()
+                else:
+                    Lv = -(et[:, None] * Vh * v[b, h]).sum()
+                grads = torch.autograd.grad(Lv, Wg)
+                if beta is not None:
+                    mom = [beta * m + g for m, g in zip(mom, grads)]
+                    grads = mom
+                Ws = [w - g for w, g in zip(Ws, grads)]
+            O[b, h] = fwd(model, Ws, q[b, h])
+    return O.numpy()
+
+
+@pytest.mark.parametrize("inner,loss,key_norm,epochs,beta", [
+    (orc.INNER_GLU, orc.LOSS_DOT, True, 1, None),
+    (orc.INNER_GLU, orc.LOSS_MSE, False, 2, None),
+    (orc.INNER_DWCONV, orc.LOSS_DOT, True, 1, None),
+    (orc.INNER_DWCONV, orc.LOSS_MSE, False, 3, 0.5),
+    (orc.INNER_VIT3, orc.LOSS_DOT, True, 1, None),
+    (orc.INNER_VIT3, orc.LOSS_MSE, True, 2, None),
+])
+def test_vit3_models_match_autograd_layer(inner, loss, key_norm, epochs, beta):
+    rng = np.random.default_rng(41)
+    B, H, d, k = 2, 3, 5, 3
+    q, kk, v, grid, N = _grid_case(rng, B=B, H=H, d=d, k=k)
+    W0 = {orc.INNER_GLU: [rng.standard_normal((H, d, d)) * 0.4, rng.standard_normal((H, d, d)) * 0.4],
+          orc.INNER_DWCONV: [rng.standard_normal((H, d, k * k)) * 0.3]}
+    W0[orc.INNER_VIT3] = W0[orc.INNER_GLU] + W0[orc.INNER_DWCONV]
+    eta_tok = 0.2 + rng.random((B, H, N))
+    O, _ = orc.oracle_forward(q, kk, v, W0[inner], eta_scale=0.9, eta_tok=eta_tok, loss=loss, inner=inner, chunk=0,
+                              key_norm=key_norm, epochs=epochs, grid=grid,
+                              rule=orc.RULE_GD if beta is None else orc.RULE_MOMENTUM, beta=beta or 0.0)
+    O_ref = _torch_vit3(q, kk, v, W0[inner], grid, 0.9, eta_tok, loss, inner, key_norm, epochs, beta)
+    np.testing.assert_allclose(O, O_ref, rtol=1e-10, atol=1e-12)
+
+
+def test_dwconv_dot_zero_init_closed_form():
+    """Depthwise convolution, dot loss, W0 = 0 (key norm off): the updated
+    kernel of channel c is eta times the cross-correlation of the padded key
+    channel with the value channel, and O is Q cross-correlated with it
+    ('same' mode) -- both through scipy.signal.correlate2d."""
+    from scipy.signal import correlate2d
+
+    rng = np.random.default_rng(42)
+    gh, gw, d, k, eta = 6, 7, 3, 3, 0.7
+    q, kk, v, grid, N = _grid_case(rng, gh=gh, gw=gw, d=d, k=k)
+    O, Wf = orc.oracle_forward(q, kk, v, [np.zeros((1, d, k * k))], eta_scale=eta, loss=orc.LOSS_DOT,
+                               inner=orc.INNER_DWCONV, chunk=0, key_norm=False, grid=grid)
+    Q, K, V = (a[0, 0].reshape(gh, gw, d) for a in (q, kk, v))
+    for c in range(d):
+        w = eta * correlate2d(np.pad(K[:, :, c], 1), V[:, :, c], mode="valid")     # [k, k]
+        np.testing.assert_allclose(Wf[0][0, 0, c].reshape(k, k), w, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(O[0, 0, :, c].reshape(gh, gw), correlate2d(Q[:, :, c], w, mode="same"),
+                                   rtol=1e-11, atol=1e-12)
+
+
+def test_dwconv_1x1_is_channel_scaling_closed_form():
+    """A 1 x 1 depthwise kernel scales every channel: with MSE,
+    w_c* = w_c - eta 2/(N d) sum_t (w_c x_tc - v_tc) x_tc and O = Q w*."""
+    rng = np.random.default_rng(43)
+    q, kk, v, grid, N = _grid_case(rng, gh=4, gw=5, d=3)
+    w0 = rng.standard_normal((1, 3, 1))
+    eta = 1.3
+    O, Wf = orc.oracle_forward(q, kk, v, [w0], eta_scale=eta, loss=orc.LOSS_MSE, inner=orc.INNER_DWCONV, chunk=0,
+                               key_norm=False, grid=grid)
+    X, V = kk[0, 0], v[0, 0]
+    w = w0[0, :, 0] - eta * 2.0 / (N * 3) * np.sum((X * w0[0, :, 0] - V) * X, axis=0)
+    np.testing.assert_allclose(Wf[0][0, 0, :, 0], w, rtol=1e-12)
+    np.testing.assert_allclose(O[0, 0], q[0, 0] * w, rtol=1e-12)
+
+
+def test_vit3_heads_are_the_two_models():
+    """The ViT3 block: head 0 is exactly the convolution layer on that head,
+    the other heads exactly the GLU layer on theirs."""
+    rng = np.random.default_rng(44)
+    B, H, d, k = 2, 3, 4, 3
+    q, kk, v, grid, N = _grid_case(rng, B=B, H=H, d=d)
+    W1, W2 = rng.standard_normal((H, d, d)) * 0.5, rng.standard_normal((H, d, d)) * 0.5
+    Wc = rng.standard_normal((H, d, k * k)) * 0.3
+    args = dict(loss=orc.LOSS_DOT, chunk=0, key_norm=True, grid=grid)
+    O, Wf = orc.oracle_forward(q, kk, v, [W1, W2, Wc], inner=orc.INNER_VIT3, **args)
+    Oc, Wfc = orc.oracle_forward(q[:, :1], kk[:, :1], v[:, :1], [Wc[:1]], inner=orc.INNER_DWCONV, **args)
+    Og, Wfg = orc.oracle_forward(q[:, 1:], kk[:, 1:], v[:, 1:], [W1[1:], W2[1:]], inner=orc.INNER_GLU, **args)
+    np.testing.assert_array_equal(O[:, :1], Oc)
+    np.testing.assert_array_equal(O[:, 1:], Og)
+    np.testing.assert_array_equal(Wf[2][:, :1], Wfc[0])
+    np.testing.assert_array_equal(Wf[0][:, 1:], Wfg[0])
+    np.testing.assert_array_equal(Wf[1][:, 1:], Wfg[1])
