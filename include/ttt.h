@@ -67,9 +67,27 @@ typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_DOT = 1 } ttt_loss;
  *   TTT_INNER_MLP_GELU: F(x) = gelu(x W1) W2           w[0] = W1 [d, h], w[1] = W2 [h, d]
  *   TTT_INNER_SWIGLU  : F(x) = (silu(x W1) * (x W3)) W2
  *                                  w[0] = W1 [d, h], w[1] = W2 [h, d], w[2] = W3 [d, h]
+ *   TTT_INNER_GLU     : F(x) = (x W1) * silu(x W2)     w[0] = W1 [d, d], w[1] = W2 [d, d]
+ *                       (the simplified gated linear unit; hidden is ignored)
+ *   TTT_INNER_DWCONV  : F(x)[t, c] = sum_{a, b} w[c, a k + b] x[t(i + a - r, j + b - r), c]
+ *                       a depthwise k x k cross-correlation over the token
+ *                       raster (token t = i grid_w + j, r = (k - 1) / 2, zero
+ *                       padding); the kernel is the fast weight, w[0] = [d, k*k]
+ *   TTT_INNER_VIT3    : the ViT3 block: head 0 is a DWCONV head, heads 1..H-1
+ *                       are GLU heads; w[0], w[1] = the GLU matrices [H, d, d],
+ *                       w[2] = the convolution kernels [H, d, k*k] (each head
+ *                       reads only the entries of its own model; W_out rows of
+ *                       the other model are not written)
  * gelu is the exact erf form.  (ViT3 page, guideline 4: two-layer MLP of width
- * h = r*d; LaCT page: SwiGLU fast weights with three matrices.) */
-typedef enum { TTT_INNER_LINEAR = 0, TTT_INNER_MLP_GELU = 1, TTT_INNER_SWIGLU = 2 } ttt_inner;
+ * h = r*d; guideline 6, the inner-model table and section 04: simplified GLU,
+ * depthwise convolution, one convolution head per block; LaCT page: SwiGLU
+ * fast weights with three matrices.)  DWCONV and VIT3 are full-batch only
+ * (chunk 0) and take neither TTT_RULE_MUON nor renorm, which are defined for
+ * matrices; VIT3 needs W0.batch_stride == 0. */
+typedef enum {
+  TTT_INNER_LINEAR = 0, TTT_INNER_MLP_GELU = 1, TTT_INNER_SWIGLU = 2,
+  TTT_INNER_GLU = 3, TTT_INNER_DWCONV = 4, TTT_INNER_VIT3 = 5
+} ttt_inner;
 
 /* Flags (ttt_config.flags). */
 #define TTT_FLAG_CHECK_FINITE 0x1u   /* after the call, synchronise the stream and
@@ -98,6 +116,9 @@ typedef struct {
   int renorm;       /* 1: after each update rescale every column of every
                        matrix to the L2 norm that column has in W0 (LaCT page) */
   unsigned flags;   /* TTT_FLAG_* */
+  int grid_h, grid_w; /* DWCONV / VIT3: the N tokens form a grid_h x grid_w
+                         raster (grid_h * grid_w == N); otherwise ignored */
+  int conv_k;       /* DWCONV / VIT3: odd kernel size 1, 3, 5 or 7 */
 } ttt_config;
 
 /* Initial fast weights W0, fp32 device memory.  w[i] points at matrix i of

@@ -1,6 +1,6 @@
 // Generic TTT-layer kernels: fp32 arithmetic on fp32 or bf16 tensors, every
-// inner model (linear, GELU MLP, SwiGLU), both losses, any d <= 128 and
-// h <= 512.  They serve the fp32 configuration (exact erf GELU, fp32 sums) and
+// matrix inner model (linear, GELU MLP, SwiGLU, the simplified GLU of the ViT3
+// page), both losses, any d <= 128 and h <= 512.  They serve the fp32 configuration (exact erf GELU, fp32 sums) and
 // every shape the MFMA kernels do not cover.  Plain LDS-staged loops: the
 // bf16 MFMA kernels are the fast path.
 //
@@ -24,7 +24,7 @@ constexpr int kMaxH = 512;
 
 __device__ __forceinline__ float eta_of(const Problem& pb, int p, int n) {
   float e = pb.eta_scale;
-  if (pb.eta_tok) e *= pb.eta_tok[(size_t)p * pb.N + n];
+  if (pb.eta_tok) e *= pb.eta_tok[(size_t)pb.row(p) * pb.N + n];
   return e;
 }
 
@@ -38,7 +38,7 @@ __device__ __forceinline__ void stage_rows(const Problem& pb, const T* base, int
     const int t = i / d, c = i % d;
     float x = 0.f;
     if (t < nt) {
-      x = to_f32<T>(base[((size_t)p * pb.N + t0 + t) * d + c]);
+      x = to_f32<T>(base[((size_t)pb.row(p) * pb.N + t0 + t) * d + c]);
       if (stats) {
         const float* s = stats + ((size_t)p * d + c) * 2;
         x = (x - s[0]) * s[1];
@@ -49,7 +49,8 @@ __device__ __forceinline__ void stage_rows(const Problem& pb, const T* base, int
 }
 
 // Hidden activations of the inner model for kTok staged rows x:
-//   MLP: act = gelu(x W1);  SwiGLU: act = silu(x W1) * (x W3).
+//   MLP: act = gelu(x W1);  SwiGLU: act = silu(x W1) * (x W3);
+//   GLU: act = (x W1) * silu(x Wg) (Wg passed as W3), which is F itself.
 __device__ __forceinline__ void hidden_fwd(const Problem& pb, const float* W1, const float* W3,
                                            const float* x, float* act) {
   const int d = pb.d, hid = pb.hid;
@@ -59,9 +60,11 @@ __device__ __forceinline__ void hidden_fwd(const Problem& pb, const float* W1, c
     for (int c = 0; c < d; ++c) {
       const float xv = x[t * d + c];
       z1 += xv * W1[(size_t)c * hid + j];
-      if (pb.inner == INNER_SWIGLU) z3 += xv * W3[(size_t)c * hid + j];
+      if (W3) z3 += xv * W3[(size_t)c * hid + j];
     }
-    act[i] = pb.inner == INNER_SWIGLU ? z1 * sigmoid_f(z1) * z3 : gelu_exact(z1);
+    act[i] = pb.inner == INNER_SWIGLU ? z1 * sigmoid_f(z1) * z3
+           : pb.inner == INNER_GLU    ? z1 * z3 * sigmoid_f(z3)
+                                      : gelu_exact(z1);
   }
 }
 
@@ -81,6 +84,10 @@ __device__ __forceinline__ void inner_out(const Problem& pb, const WRef& W, int 
   }
   const float* W1 = W.mat(0, b, h);
   const float* W2 = W.mat(1, b, h);
+  if (pb.inner == INNER_GLU) {            // no output projection: F = act
+    hidden_fwd(pb, W1, W2, x, out);
+    return;
+  }
   const float* W3 = pb.inner == INNER_SWIGLU ? W.mat(2, b, h) : nullptr;
   hidden_fwd(pb, W1, W3, x, act);
   __syncthreads();
@@ -108,7 +115,7 @@ __global__ void __launch_bounds__(kThreads) k_gen_grad_out(Problem pb, WRef W, i
   if (pb.loss == LOSS_DOT) {   // G_n = -eta_n v_n: no forward needed
     for (int i = threadIdx.x; i < cnt * d; i += kThreads) {
       const int t = i / d, c = i % d, n = t0 + tt + t;
-      g[i] = -eta_of(pb, p, n) * to_f32<T>(((const T*)pb.v)[((size_t)p * pb.N + n) * d + c]);
+      g[i] = -eta_of(pb, p, n) * to_f32<T>(((const T*)pb.v)[((size_t)pb.row(p) * pb.N + n) * d + c]);
     }
     return;
   }
@@ -119,7 +126,7 @@ __global__ void __launch_bounds__(kThreads) k_gen_grad_out(Problem pb, WRef W, i
   const float scale = 2.0f / ((float)nt * (float)d);
   for (int i = threadIdx.x; i < cnt * d; i += kThreads) {
     const int t = i / d, c = i % d, n = t0 + tt + t;
-    const float vv = to_f32<T>(((const T*)pb.v)[((size_t)p * pb.N + n) * d + c]);
+    const float vv = to_f32<T>(((const T*)pb.v)[((size_t)pb.row(p) * pb.N + n) * d + c]);
     g[i] = eta_of(pb, p, n) * scale * (vh[i] - vv);
   }
 }
@@ -149,8 +156,10 @@ __global__ void __launch_bounds__(kThreads) k_gen_dW(Problem pb, WRef W, int t0,
 #pragma unroll
   for (int r = 0; r < R; ++r) { acc1[r] = 0.f; acc2[r] = 0.f; acc3[r] = 0.f; }
   const float* W1 = W.mat(0, b, h);
-  const float* W2 = pb.inner == INNER_LINEAR ? nullptr : W.mat(1, b, h);
-  const float* W3 = pb.inner == INNER_SWIGLU ? W.mat(2, b, h) : nullptr;
+  const bool glu = pb.inner == INNER_GLU;
+  // GLU: its gate matrix (matrix 1) takes the place of W3, and there is no W2
+  const float* W2 = pb.inner == INNER_LINEAR || glu ? nullptr : W.mat(1, b, h);
+  const float* W3 = pb.inner == INNER_SWIGLU ? W.mat(2, b, h) : glu ? W.mat(1, b, h) : nullptr;
   const int hid = pb.hid;
   for (int tt = n0; tt < n1; tt += kTok) {
     const int cnt = min(kTok, n1 - tt);
@@ -167,10 +176,14 @@ __global__ void __launch_bounds__(kThreads) k_gen_dW(Problem pb, WRef W, int t0,
         for (int c = 0; c < d; ++c) {
           z1 += xs[t * d + c] * W1[(size_t)c * hid + j];
           if (W3) z3 += xs[t * d + c] * W3[(size_t)c * hid + j];
-          da += gs[t * d + c] * W2[(size_t)j * d + c];
+          if (W2) da += gs[t * d + c] * W2[(size_t)j * d + c];
         }
         const bool live = t < cnt;
-        if (pb.inner == INNER_MLP) {
+        if (glu) {              // F = U * silu(Zg): dU = G silu(Zg), dZg = G U silu'(Zg)
+          const float sg = sigmoid_f(z3), gj = gs[t * d + j];
+          d1[t * kSlice + jj] = live ? gj * z3 * sg : 0.f;
+          d3[t * kSlice + jj] = live ? gj * z1 * sg * (1.f + z3 * (1.f - sg)) : 0.f;
+        } else if (pb.inner == INNER_MLP) {
           aa[t * kSlice + jj] = live ? gelu_exact(z1) : 0.f;
           d1[t * kSlice + jj] = live ? da * gelu_exact_prime(z1) : 0.f;
         } else {
@@ -201,7 +214,7 @@ __global__ void __launch_bounds__(kThreads) k_gen_dW(Problem pb, WRef W, int t0,
         acc3[r] += s3;
       }
       // dW2[j][c] entries: e -> (jj = e / d, c = e % d)
-      if (pb.inner != INNER_LINEAR) {
+      if (W2) {
         const int jj2 = e / d, c2 = e % d;
         if (jj2 < js) {
           float s2 = 0.f;
@@ -219,9 +232,9 @@ __global__ void __launch_bounds__(kThreads) k_gen_dW(Problem pb, WRef W, int t0,
     const int c = e / kSlice, jj = e % kSlice;
     if (c < d && jj < js) {
       base[(size_t)c * outw + j0 + jj] = acc1[r];
-      if (pb.inner == INNER_SWIGLU) base[2 * pb.msz + (size_t)c * outw + j0 + jj] = acc3[r];
+      if (W3) base[(glu ? 1 : 2) * pb.msz + (size_t)c * outw + j0 + jj] = acc3[r];
     }
-    if (pb.inner != INNER_LINEAR) {
+    if (W2) {
       const int jj2 = e / d, c2 = e % d;
       if (jj2 < js) base[pb.msz + (size_t)(j0 + jj2) * d + c2] = acc2[r];
     }
@@ -262,7 +275,7 @@ __global__ void __launch_bounds__(kThreads) k_gen_query(Problem pb, WRef w0, con
   __syncthreads();
   inner_out(pb, W, b, h, xs, act, os);
   __syncthreads();
-  T* o = (T*)pb.o + ((size_t)p * pb.N + tt) * d;
+  T* o = (T*)pb.o + ((size_t)pb.row(p) * pb.N + tt) * d;
   for (int i = threadIdx.x; i < cnt * d; i += kThreads) o[i] = from_f32<T>(os[i]);
 }
 
@@ -325,8 +338,8 @@ void launch_gen_query(const Problem& pb, const WRef& w0, const float* states, lo
     hipLaunchKernelGGL(k_gen_query<float>, grid, dim3(kThreads), 0, st, pb, w0, states, state_stride, chunk);
 }
 
-void launch_check_finite(const Problem& pb, float* const* wfinal, long long wcount, int* flag, hipStream_t st) {
-  const long long n = (long long)pb.B * pb.H * pb.N * pb.d;
+void launch_check_finite(const Problem& pb, long long n, float* const* wfinal, long long wcount, int* flag,
+                         hipStream_t st) {
   hipLaunchKernelGGL(k_check_finite, dim3(1024), dim3(256), 0, st, pb.o, pb.bf16, n, wfinal[0], wfinal[1],
                      wfinal[2], wcount, flag);
 }

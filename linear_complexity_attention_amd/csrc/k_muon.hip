@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(256) k_muon_apply(Problem pb, const float* __r
   const long long msz = pb.msz;
   float* w = next + ((long long)p * pb.nm + i) * msz;
   float* out = i == 0 ? o0 : i == 1 ? o1 : o2;
-  if (out) out += (long long)p * msz;
+  if (out) out += pb.row(p) * msz;
   const bool upd = (mask >> i) & 1u;
   const float* xi = x + ((long long)p * pb.nm + i) * msz;
   const bool tall = rows > cols;

@@ -36,15 +36,17 @@ __device__ __forceinline__ void load8<float>(const float* p, float* x) {
 // key row s (so the variance does not cancel), turned into (count, mean, M2).
 template <typename T>
 __global__ void __launch_bounds__(kThreads) k_stats_partial_v8(const T* __restrict__ k, int N, int d,
-                                                               int S, float* __restrict__ part) {
+                                                               int S, float* __restrict__ part, int H, int Hs,
+                                                               int h0) {
   const int s = blockIdx.x, p = blockIdx.y;
+  const long long prow = (long long)(p / H) * Hs + h0 + p % H;   // the pair's row of k
   const int L = (N + S - 1) / S;
   const int n0 = s * L, n1 = min(N, n0 + L);
   const int groups = d >> 3;
   const int R = kThreads / groups;
   const int cg = threadIdx.x % groups, r = threadIdx.x / groups;
   const bool active = r < R;
-  const T* base = k + (size_t)p * N * d + cg * 8;
+  const T* base = k + (size_t)prow * N * d + cg * 8;
   __shared__ float red[2][kThreads][8];
   float sh[8], s1[8], s2[8];
   load8<T>(base, sh);                       // shift: the pair's first key row
@@ -77,7 +79,7 @@ __global__ void __launch_bounds__(kThreads) k_stats_partial_v8(const T* __restri
     float a1 = 0.f, a2 = 0.f;
     for (int rr = 0; rr < R; ++rr) { a1 += red[0][rr * groups + g][j]; a2 += red[1][rr * groups + g][j]; }
     float shift[8];
-    load8<T>(k + (size_t)p * N * d + g * 8, shift);
+    load8<T>(k + (size_t)prow * N * d + g * 8, shift);
     const float m1 = cnt ? a1 / (float)cnt : 0.f;
     float* o = part + ((size_t)p * S + s) * 3 * d;
     o[c] = (float)cnt;
@@ -89,14 +91,16 @@ __global__ void __launch_bounds__(kThreads) k_stats_partial_v8(const T* __restri
 // any d <= 256: thread = (channel, row lane)
 template <typename T>
 __global__ void __launch_bounds__(kThreads) k_stats_partial_scalar(const T* __restrict__ k, int N, int d,
-                                                                   int S, float* __restrict__ part) {
+                                                                   int S, float* __restrict__ part, int H, int Hs,
+                                                                   int h0) {
   const int s = blockIdx.x, p = blockIdx.y;
+  const long long prow = (long long)(p / H) * Hs + h0 + p % H;
   const int L = (N + S - 1) / S;
   const int n0 = s * L, n1 = min(N, n0 + L);
   const int R = kThreads / d;
   const int c = threadIdx.x % d, r = threadIdx.x / d;
   const bool active = r < R;
-  const T* base = k + (size_t)p * N * d + c;
+  const T* base = k + (size_t)prow * N * d + c;
   __shared__ float red[kThreads];
   __shared__ float mean_s[256];
   float acc = 0.f;
@@ -157,14 +161,14 @@ void launch_stats_partial(const Problem& pb, int S, float* part, hipStream_t st)
   dim3 grid(S, P);
   if (pb.d % 8 == 0 && pb.d <= 128) {
     if (pb.bf16)
-      hipLaunchKernelGGL(k_stats_partial_v8<bf16>, grid, dim3(kThreads), 0, st, (const bf16*)pb.k, pb.N, pb.d, S, part);
+      hipLaunchKernelGGL(k_stats_partial_v8<bf16>, grid, dim3(kThreads), 0, st, (const bf16*)pb.k, pb.N, pb.d, S, part, pb.H, pb.Hs, pb.h0);
     else
-      hipLaunchKernelGGL(k_stats_partial_v8<float>, grid, dim3(kThreads), 0, st, (const float*)pb.k, pb.N, pb.d, S, part);
+      hipLaunchKernelGGL(k_stats_partial_v8<float>, grid, dim3(kThreads), 0, st, (const float*)pb.k, pb.N, pb.d, S, part, pb.H, pb.Hs, pb.h0);
   } else {
     if (pb.bf16)
-      hipLaunchKernelGGL(k_stats_partial_scalar<bf16>, grid, dim3(kThreads), 0, st, (const bf16*)pb.k, pb.N, pb.d, S, part);
+      hipLaunchKernelGGL(k_stats_partial_scalar<bf16>, grid, dim3(kThreads), 0, st, (const bf16*)pb.k, pb.N, pb.d, S, part, pb.H, pb.Hs, pb.h0);
     else
-      hipLaunchKernelGGL(k_stats_partial_scalar<float>, grid, dim3(kThreads), 0, st, (const float*)pb.k, pb.N, pb.d, S, part);
+      hipLaunchKernelGGL(k_stats_partial_scalar<float>, grid, dim3(kThreads), 0, st, (const float*)pb.k, pb.N, pb.d, S, part, pb.H, pb.Hs, pb.h0);
   }
 }
 

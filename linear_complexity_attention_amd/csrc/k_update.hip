@@ -37,6 +37,7 @@ __device__ __forceinline__ long long slot_of(const UpdateArgs& a, int p, long lo
 
 __device__ __forceinline__ void mat_dims(const Problem& pb, int i, int& rows, int& cols) {
   if (pb.inner == INNER_LINEAR) { rows = pb.d; cols = pb.d; return; }
+  if (pb.inner == INNER_DWCONV) { rows = pb.d; cols = pb.ck * pb.ck; return; }   // kernel [d][k*k]
   if (i == 1) { rows = pb.hid; cols = pb.d; }   // W2 [h, d]
   else { rows = pb.d; cols = pb.hid; }          // W1, W3 [d, h]
 }
@@ -87,7 +88,7 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
     if (!a.mom_only) { w.x = wc.x - m.x; w.y = wc.y - m.y; w.z = wc.z - m.z; w.w = wc.w - m.w; }
   }
   *reinterpret_cast<float4*>(a.next + (size_t)p * wsz + e) = w;
-  if (a.out[i]) *reinterpret_cast<float4*>(a.out[i] + (size_t)p * pb.msz + o) = w;
+  if (a.out[i]) *reinterpret_cast<float4*>(a.out[i] + (size_t)pb.row(p) * pb.msz + o) = w;
 }
 
 // Update from the MFMA gradient kernel's stream-K partials, which are stored in
@@ -140,7 +141,7 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
       if (q + u <= q1) { sum.x += d[u].x; sum.y += d[u].y; sum.z += d[u].z; sum.w += d[u].w; }
   }
   float* nxt = a.next + (size_t)p * wsz + (size_t)mat * D * HID;
-  float* out = a.out[mat] ? a.out[mat] + (size_t)p * D * HID : nullptr;
+  float* out = a.out[mat] ? a.out[mat] + (size_t)pb.row(p) * D * HID : nullptr;
   const float s4[4] = {sum.x, sum.y, sum.z, sum.w};
   float* mom = (upd && a.rule != RULE_GD) ? a.mom + (size_t)p * wsz + (size_t)mat * D * HID : nullptr;
 #pragma unroll
@@ -210,7 +211,7 @@ __global__ void __launch_bounds__(kRCols * kRLanes) k_renorm(Problem pb, UpdateA
   // matrices outside the update mask kept W_cur, whose columns already have
   // W0's norms: they are only copied to W_out
   const float scale = ((a.mask >> i) & 1u) ? sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f) : 1.0f;
-  float* out = a.out[i] ? a.out[i] + (size_t)p * pb.msz : nullptr;
+  float* out = a.out[i] ? a.out[i] + (size_t)pb.row(p) * pb.msz : nullptr;
 #pragma unroll
   for (int k = 0; k < RMAX; ++k) {
     const int r = lane + kRLanes * k;
@@ -299,7 +300,7 @@ __global__ void __launch_bounds__(kCols * kLanes) k_update_renorm(Problem pb, Up
   for (int l = 0; l < kLanes; ++l) { sn += red[0][l][threadIdx.x % kCols]; sr += red[1][l][threadIdx.x % kCols]; }
   const float scale = (a.renorm && upd) ? sqrtf(sr) / fmaxf(sqrtf(sn), 1e-12f) : 1.f;
   if (!live) return;
-  float* out = a.out[i] ? a.out[i] + (size_t)p * pb.msz : nullptr;
+  float* out = a.out[i] ? a.out[i] + (size_t)pb.row(p) * pb.msz : nullptr;
   for (int r = lane; r < rows; r += kLanes) {
     const size_t e = (size_t)r * cols + j;
     const float w = nxt[e] * scale;
@@ -348,7 +349,9 @@ void launch_update(const Problem& pb, const UpdateArgs& a_in, hipStream_t st) {
     launch_renorm(pb, a, st);
     return;
   }
-  const int maxcols = pb.inner == INNER_LINEAR ? pb.d : (pb.hid > pb.d ? pb.hid : pb.d);
+  const int maxcols = pb.inner == INNER_LINEAR ? pb.d
+                    : pb.inner == INNER_DWCONV ? pb.ck * pb.ck
+                    : (pb.hid > pb.d ? pb.hid : pb.d);
   dim3 grid((maxcols + kCols - 1) / kCols, pb.nm, P);
   hipLaunchKernelGGL(k_update_renorm, grid, dim3(kCols * kLanes), 0, st, pb, a);
 }

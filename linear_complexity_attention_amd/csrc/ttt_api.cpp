@@ -65,14 +65,52 @@ int fail(ttt_handle* h, int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int n_mats(int inner) { return inner == TTT_INNER_LINEAR ? 1 : inner == TTT_INNER_SWIGLU ? 3 : 2; }
+// matrices the caller passes for a request (ttt_weights.w entries)
+int n_mats(int inner) {
+  switch (inner) {
+    case TTT_INNER_LINEAR: case TTT_INNER_DWCONV: return 1;
+    case TTT_INNER_SWIGLU: case TTT_INNER_VIT3: return 3;
+    default: return 2;   // MLP, GLU
+  }
+}
 
 bool env_log() {
   const char* e = std::getenv("TTT_LOG");
   return e && e[0] == '1';
 }
 
-// Where every buffer of one request lives inside the caller's workspace.
+// One head range of a request and the inner model its heads run: every
+// request is one range, except the ViT3 block, whose head 0 runs the depthwise
+// convolution and whose other heads run the GLU (ViT3 page, section 04).
+// slot[i] is the caller's weight entry that holds matrix i of the model.
+struct Range {
+  int model, h0, hc, nm;
+  int slot[3];
+};
+
+int ranges_of(const ttt_config& c, int inner, Range* r) {
+  switch (inner) {
+    case TTT_INNER_VIT3:
+      r[0] = Range{INNER_DWCONV, 0, 1, 1, {2, 0, 0}};
+      if (c.H == 1) return 1;
+      r[1] = Range{INNER_GLU, 1, c.H - 1, 2, {0, 1, 0}};
+      return 2;
+    case TTT_INNER_LINEAR: r[0] = Range{INNER_LINEAR, 0, c.H, 1, {0, 0, 0}}; return 1;
+    case TTT_INNER_MLP_GELU: r[0] = Range{INNER_MLP, 0, c.H, 2, {0, 1, 0}}; return 1;
+    case TTT_INNER_SWIGLU: r[0] = Range{INNER_SWIGLU, 0, c.H, 3, {0, 1, 2}}; return 1;
+    case TTT_INNER_GLU: r[0] = Range{INNER_GLU, 0, c.H, 2, {0, 1, 0}}; return 1;
+    default: r[0] = Range{INNER_DWCONV, 0, c.H, 1, {0, 0, 0}}; return 1;
+  }
+}
+
+// the request's update mask restricted to a range, in the range's numbering
+unsigned range_mask(unsigned mask, const Range& r) {
+  unsigned m = 0;
+  for (int i = 0; i < r.nm; ++i) m |= ((mask >> r.slot[i]) & 1u) << i;
+  return m;
+}
+
+// Where every buffer of one range lives inside its part of the workspace.
 struct Plan {
   // problem
   int P, nm, hid, nb, chunk, span;   // span: tokens of the longest update batch
@@ -80,6 +118,7 @@ struct Plan {
   // choices
   bool mfma_grad, mfma_query;        // GELU-MLP MFMA kernels
   bool lact_grad, lact_query;        // SwiGLU MFMA kernels
+  bool dwconv;                       // depthwise-convolution kernels
   int S_stats, S_grad;               // S_grad: partial slots of the gradient kernel
   int sk_G, sk_J;                    // stream-K geometry (MFMA gradient kernel)
   // byte offsets
@@ -114,11 +153,12 @@ struct Opts {
   int ns_steps = 5;
 };
 
+bool is_conv(int inner) { return inner == TTT_INNER_DWCONV || inner == TTT_INNER_VIT3; }
+
 int check_request(ttt_handle* h, int loss, int inner, int chunk, const ttt_options* o, Opts* out) {
   const ttt_config& c = h->cfg;
   if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT) return fail(h, TTT_ERR_INVALID, "unknown loss %d", loss);
-  if (inner != TTT_INNER_LINEAR && inner != TTT_INNER_MLP_GELU && inner != TTT_INNER_SWIGLU)
-    return fail(h, TTT_ERR_INVALID, "unknown inner model %d", inner);
+  if (inner < TTT_INNER_LINEAR || inner > TTT_INNER_VIT3) return fail(h, TTT_ERR_INVALID, "unknown inner model %d", inner);
   if (chunk < 0) return fail(h, TTT_ERR_INVALID, "chunk must be >= 0 (got %d)", chunk);
   Opts op;
   const int nm = n_mats(inner);
@@ -150,8 +190,20 @@ int check_request(ttt_handle* h, int loss, int inner, int chunk, const ttt_optio
   if (op.causal && c.key_norm)
     return fail(h, TTT_ERR_UNSUPPORTED,
                 "key_norm with causal chunks: whole-sequence key statistics would read future keys");
-  if (inner != TTT_INNER_LINEAR && (c.hidden < 1 || c.hidden > 512))
+  if ((inner == TTT_INNER_MLP_GELU || inner == TTT_INNER_SWIGLU) && (c.hidden < 1 || c.hidden > 512))
     return fail(h, TTT_ERR_UNSUPPORTED, "hidden must be in 1..512 (got %d)", c.hidden);
+  if (is_conv(inner)) {
+    if ((long long)c.grid_h * c.grid_w != c.N || c.grid_h < 1)
+      return fail(h, TTT_ERR_INVALID, "the convolution needs grid_h * grid_w == N (%d x %d vs %d)", c.grid_h,
+                  c.grid_w, c.N);
+    if (c.conv_k != 1 && c.conv_k != 3 && c.conv_k != 5 && c.conv_k != 7)
+      return fail(h, TTT_ERR_UNSUPPORTED, "conv_k must be 1, 3, 5 or 7 (got %d)", c.conv_k);
+    if (chunk > 0 && chunk < c.N)
+      return fail(h, TTT_ERR_UNSUPPORTED, "the convolution inner model is full batch only (chunk 0)");
+    if (op.rule == RULE_MUON || c.renorm)
+      return fail(h, TTT_ERR_UNSUPPORTED, "Muon and the column re-norm are defined for matrices, not convolution "
+                                          "kernels");
+  }
   const long long nb = chunk ? (c.N + (long long)chunk - 1) / chunk : 1;
   if (nb > 65535) return fail(h, TTT_ERR_UNSUPPORTED, "too many chunks (%lld > 65535)", nb);
   if (nb * op.epochs > (1LL << 20)) return fail(h, TTT_ERR_UNSUPPORTED, "too many updates (%lld)", nb * op.epochs);
@@ -159,24 +211,25 @@ int check_request(ttt_handle* h, int loss, int inner, int chunk, const ttt_optio
   return TTT_OK;
 }
 
-Problem make_problem(const ttt_handle* h, int loss, int inner) {
+Problem make_problem(const ttt_handle* h, int loss, const Range& r) {
   const ttt_config& c = h->cfg;
   Problem pb{};
-  pb.B = c.B; pb.H = c.H; pb.N = c.N; pb.d = c.d;
-  pb.hid = inner == TTT_INNER_LINEAR ? c.d : c.hidden;
-  pb.inner = inner == TTT_INNER_LINEAR ? INNER_LINEAR : inner == TTT_INNER_MLP_GELU ? INNER_MLP : INNER_SWIGLU;
+  pb.B = c.B; pb.H = r.hc; pb.N = c.N; pb.d = c.d;
+  pb.Hs = c.H; pb.h0 = r.h0;
+  pb.inner = r.model;
+  pb.hid = (r.model == INNER_MLP || r.model == INNER_SWIGLU) ? c.hidden : c.d;
   pb.loss = loss == TTT_LOSS_MSE ? LOSS_MSE : LOSS_DOT;
-  pb.nm = n_mats(inner);
+  pb.nm = r.nm;
   pb.bf16 = c.dtype == TTT_BF16;
-  pb.msz = (long long)c.d * pb.hid;
+  pb.gh = c.grid_h; pb.gw = c.grid_w; pb.ck = c.conv_k;
+  pb.msz = r.model == INNER_DWCONV ? (long long)c.d * c.conv_k * c.conv_k : (long long)c.d * pb.hid;
   return pb;
 }
 
-Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk, const Opts& op) {
+Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op) {
   const ttt_config& c = h->cfg;
-  Problem pb = make_problem(h, loss, inner);
   Plan pl{};
-  pl.P = c.B * c.H;
+  pl.P = pb.B * pb.H;
   pl.nm = pb.nm;
   pl.hid = pb.hid;
   pl.chunk = chunk;
@@ -185,25 +238,30 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk, const Opts& 
   pl.msz = pb.msz;
   pl.wsz = pb.msz * pb.nm;
   const bool generic_only = (c.flags & TTT_FLAG_FORCE_GENERIC) != 0;
-  // A chain of several causal updates feeds each step's rounding into the next
-  // (the recurrence amplifies weight perturbations), so bf16 weight operands are
-  // used for a single update only; multi-chunk MLP gradients stay in fp32.
-  pl.mfma_grad = !generic_only && mfma_full_supported(pb) && pl.nb == 1 && op.epochs == 1;
-  pl.mfma_query = !generic_only && mfma_query_supported(pb);
-  pl.lact_grad = !generic_only && !c.key_norm && lact_supported(pb);
-  pl.lact_query = !generic_only && lact_readout_supported(pb);
+  // The MFMA and LaCT kernels address every head of the tensors: a range of
+  // the ViT3 split takes the generic and convolution kernels.  A chain of
+  // several updates feeds each step's rounding into the next (the recurrence
+  // amplifies weight perturbations), so bf16 weight operands are used for a
+  // single update only; multi-step MLP gradients stay in fp32.
+  const bool fast = !generic_only && pb.full_heads();
+  pl.dwconv = pb.inner == INNER_DWCONV;
+  pl.mfma_grad = fast && mfma_full_supported(pb) && pl.nb == 1 && op.epochs == 1;
+  pl.mfma_query = fast && mfma_query_supported(pb);
+  pl.lact_grad = fast && !c.key_norm && lact_supported(pb);
+  pl.lact_query = fast && lact_readout_supported(pb);
   // key-stat slices: at most 4 workgroups per CU in total, so that all of them
   // run in one round (a partial second round would idle most of the chip)
   pl.S_stats = c.key_norm ? stats_splits(pl.P, c.N) : 0;
-  if (pl.lact_grad) {
+  if (pl.dwconv) {
+    pl.S_grad = dwconv_grad_splits(pb);
+  } else if (pl.lact_grad) {
     pl.S_grad = lact_grad_splits(pb, pl.span);
   } else if (pl.mfma_grad) {
     int tpp_unused;
     mfma_grad_geometry(pb, pl.span, &pl.sk_G, &pl.sk_J, &tpp_unused);
     pl.S_grad = pl.sk_G * pl.sk_J;   // partial slots
   } else {
-    const int outw = inner == TTT_INNER_LINEAR ? c.d : pb.hid;
-    pl.S_grad = choose_splits((long long)pl.P * ((outw + 31) / 32), pl.span, 16, 1024);
+    pl.S_grad = choose_splits((long long)pl.P * ((pb.hid + 31) / 32), pl.span, 16, 1024);
   }
   size_t off = 0;
   pl.off_stats_part = off;
@@ -216,7 +274,7 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk, const Opts& 
   pl.off_part = off;
   off = align256(off + sizeof(float) * (size_t)pl.S_grad * (pl.mfma_grad ? 1 : pl.P) * pl.wsz);
   pl.off_gbuf = off;
-  if (!pl.mfma_grad && !pl.lact_grad) off = align256(off + sizeof(float) * (size_t)pl.P * pl.span * c.d);
+  if (!pl.mfma_grad && !pl.lact_grad && !pl.dwconv) off = align256(off + sizeof(float) * (size_t)pl.P * pl.span * c.d);
   pl.off_mom = off;
   if (op.rule != RULE_GD) off = align256(off + sizeof(float) * (size_t)pl.P * pl.wsz);
   pl.off_muon = off;
@@ -225,6 +283,29 @@ Plan make_plan(const ttt_handle* h, int loss, int inner, int chunk, const Opts& 
   off = align256(off + 64);
   pl.total = off;
   return pl;
+}
+
+// every range's problem and plan, and the workspace they need together
+struct Layout {
+  int n;
+  Range r[2];
+  Problem pb[2];
+  Plan pl[2];
+  size_t base[2], total;
+};
+
+Layout make_layout(const ttt_handle* h, int loss, int inner, int chunk, const Opts& op) {
+  Layout L{};
+  L.n = ranges_of(h->cfg, inner, L.r);
+  size_t off = 0;
+  for (int i = 0; i < L.n; ++i) {
+    L.pb[i] = make_problem(h, loss, L.r[i]);
+    L.pl[i] = make_plan(h, L.pb[i], chunk, op);
+    L.base[i] = off;
+    off = align256(off + L.pl[i].total);
+  }
+  L.total = off;
+  return L;
 }
 
 int hip_fail(ttt_handle* h, hipError_t e, const char* what) {
@@ -268,6 +349,8 @@ int ttt_create(const ttt_config* cfg, ttt_handle** out) {
   if (c.B < 1 || c.H < 1 || c.N < 1) return fail(nullptr, TTT_ERR_INVALID, "B, H, N must be >= 1 (got %d, %d, %d)", c.B, c.H, c.N);
   if (c.d < 1 || c.d > 128) return fail(nullptr, TTT_ERR_UNSUPPORTED, "d must be in 1..128 (got %d)", c.d);
   if (c.hidden < 0) return fail(nullptr, TTT_ERR_INVALID, "hidden must be >= 0 (got %d)", c.hidden);
+  if (c.grid_h < 0 || c.grid_w < 0 || c.conv_k < 0)
+    return fail(nullptr, TTT_ERR_INVALID, "grid_h, grid_w and conv_k must be >= 0");
   if (c.dtype != TTT_F32 && c.dtype != TTT_BF16) return fail(nullptr, TTT_ERR_INVALID, "unknown dtype %d", c.dtype);
   if (!(c.eps >= 0.f) || !std::isfinite(c.eps)) return fail(nullptr, TTT_ERR_INVALID, "eps must be finite and >= 0");
   if (c.flags & ~(TTT_FLAG_CHECK_FINITE | TTT_FLAG_FORCE_GENERIC | TTT_FLAG_LOG))
@@ -305,7 +388,7 @@ int ttt_workspace_bytes_ex(const ttt_handle* hc, int loss, int inner, int chunk,
   Opts op;
   int rc = check_request(h, loss, inner, chunk, opt, &op);
   if (rc) return rc;
-  *bytes = make_plan(h, loss, inner, chunk, op).total;
+  *bytes = make_layout(h, loss, inner, chunk, op).total;
   return TTT_OK;
 }
 
@@ -317,7 +400,10 @@ const char* ttt_path_name_ex(const ttt_handle* hc, int loss, int inner, int chun
   ttt_handle* h = const_cast<ttt_handle*>(hc);
   Opts op;
   if (!h || check_request(h, loss, inner, chunk, opt, &op)) return nullptr;
-  Plan pl = make_plan(h, loss, inner, chunk, op);
+  if (inner == TTT_INNER_VIT3) return "dwconv+generic";
+  const Layout L = make_layout(h, loss, inner, chunk, op);
+  const Plan& pl = L.pl[0];
+  if (pl.dwconv) return "dwconv";
   if (pl.mfma_grad && pl.mfma_query) return "mfma";
   if (pl.mfma_query) return "generic_grad+mfma_query";
   if (pl.lact_grad && pl.lact_query) return "mfma_swiglu";
@@ -329,32 +415,31 @@ const char* ttt_path_name(const ttt_handle* h, int loss, int inner, int chunk) {
   return ttt_path_name_ex(h, loss, inner, chunk, nullptr);
 }
 
-int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
-                   const ttt_eta* eta, int loss, int inner, int chunk, const ttt_options* opt, void* o,
-                   const ttt_weights_out* W_out, void* workspace, size_t ws_bytes, void* stream) {
-  if (!h) return fail(nullptr, TTT_ERR_INVALID, "handle is NULL");
-  h->err.clear();
-  Opts op;
-  int rc = check_request(h, loss, inner, chunk, opt, &op);
-  if (rc) return rc;
-  const ttt_config& c = h->cfg;
-  if (!q || !k || !v || !o) return fail(h, TTT_ERR_INVALID, "q, k, v and o must be non-NULL");
-  if (!W0) return fail(h, TTT_ERR_INVALID, "W0 is NULL");
-  if (!eta) return fail(h, TTT_ERR_INVALID, "eta is NULL");
-  if (!std::isfinite(eta->scale)) return fail(h, TTT_ERR_INVALID, "eta scale must be finite");
-  const int nm = n_mats(inner);
-  for (int i = 0; i < nm; ++i)
-    if (!W0->w[i]) return fail(h, TTT_ERR_INVALID, "W0.w[%d] is NULL", i);
-  Problem pb = make_problem(h, loss, inner);
-  if (W0->batch_stride != 0 && W0->batch_stride < (long long)c.H * pb.msz)
-    return fail(h, TTT_ERR_INVALID, "W0.batch_stride must be 0 or >= H*in*out (%lld)", (long long)c.H * pb.msz);
-  Plan pl = make_plan(h, loss, inner, chunk, op);
-  if (!workspace) return fail(h, TTT_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", pl.total);
-  if (ws_bytes < pl.total) return fail(h, TTT_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, pl.total);
-  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(h, TTT_ERR_INVALID, "workspace must be 256-byte aligned");
+}  // extern "C"
 
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
+namespace {
+
+struct Call {
+  const void *q, *k, *v;
+  void* o;
+  const ttt_weights* W0;
+  const ttt_eta* eta;
+  const ttt_weights_out* W_out;
+  int chunk;
+  hipStream_t st;
+};
+
+// Enqueue every kernel of one head range:
+//   key statistics (optional) -> for every update batch b (one in full-batch
+//   mode, ceil(N/C) with chunks) and every epoch: gradient partials at the
+//   current weights, then W_{b+1} = rule(W_b, sum of partials) [+ re-norm]
+//   -> readout of every token at the state its order assigns (causal chunk c:
+//   W_c; otherwise the final state).
+void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, const Opts& op0, char* ws,
+                   const Call& cl, bool timed) {
+  const ttt_config& c = h->cfg;
+  hipStream_t st = cl.st;
+  const int chunk = cl.chunk;
   float* stats_part = reinterpret_cast<float*>(ws + pl.off_stats_part);
   float* stats = reinterpret_cast<float*>(ws + pl.off_stats);
   float* states = reinterpret_cast<float*>(ws + pl.off_states);
@@ -362,52 +447,44 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
   float* gbuf = reinterpret_cast<float*>(ws + pl.off_gbuf);
   float* mom = reinterpret_cast<float*>(ws + pl.off_mom);
   float* muon = reinterpret_cast<float*>(ws + pl.off_muon);
-  int* flag = reinterpret_cast<int*>(ws + pl.off_flag);
+  Opts op = op0;
+  op.mask = range_mask(op0.mask, r);
 
-  pb.q = q; pb.k = k; pb.v = v; pb.o = o;
-  pb.eta_scale = eta->scale;
-  pb.eta_tok = eta->per_token;
+  pb.q = cl.q; pb.k = cl.k; pb.v = cl.v; pb.o = cl.o;
+  pb.eta_scale = cl.eta->scale;
+  pb.eta_tok = cl.eta->per_token;
   pb.stats = c.key_norm ? stats : nullptr;
+  const int nm = r.nm;
 
-  const bool log = (c.flags & TTT_FLAG_LOG) || env_log();
-  if (log)
-    std::fprintf(stderr, "[ttt] B=%d H=%d N=%d d=%d h=%d %s inner=%d loss=%d chunk=%d nb=%d epochs=%d mask=0x%x "
-                 "%s rule=%d grad=%s(S=%d) query=%s ws=%zu\n",
-                 c.B, c.H, c.N, c.d, pb.hid, pb.bf16 ? "bf16" : "f32", inner, loss, chunk, pl.nb, op.epochs, op.mask,
-                 op.causal ? "causal" : "write-then-query", op.rule,
-                 pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu" : "generic", pl.S_grad,
-                 pl.mfma_query ? "mfma" : pl.lact_query ? "mfma_swiglu" : "generic", pl.total);
-
+  // the caller's W0 entries of this range's matrices, from its first head on
   WRef w0{};
-  for (int i = 0; i < 3; ++i) w0.m[i] = i < nm ? W0->w[i] : W0->w[0];
-  w0.sb = W0->batch_stride;
+  for (int i = 0; i < 3; ++i) w0.m[i] = cl.W0->w[r.slot[i < nm ? i : 0]] + (long long)r.h0 * pb.msz;
+  w0.sb = cl.W0->batch_stride;
   w0.sh = pb.msz;
+  float* wout[3] = {nullptr, nullptr, nullptr};
+  if (cl.W_out)
+    for (int i = 0; i < nm; ++i) wout[i] = cl.W_out->w[r.slot[i]];
 
   auto state_ref = [&](int s) -> WRef {   // s >= 1
-    WRef r{};
+    WRef rr{};
     float* base = states + (long long)(s - 1) * pl.state_stride;
-    for (int i = 0; i < 3; ++i) r.m[i] = base + (long long)(i < nm ? i : 0) * pb.msz;
-    r.sb = (long long)c.H * pl.wsz;
-    r.sh = pl.wsz;
-    return r;
+    for (int i = 0; i < 3; ++i) rr.m[i] = base + (long long)(i < nm ? i : 0) * pb.msz;
+    rr.sb = (long long)pb.H * pl.wsz;
+    rr.sh = pl.wsz;
+    return rr;
   };
-
-  // hipGetLastError is per thread and sticky: drop an error some earlier,
-  // unrelated runtime call left behind so that only our launches are judged.
-  (void)hipGetLastError();
   auto mark = [&](int i) {
-    if (h->timing && h->events[i]) (void)hipEventRecord(h->events[i], st);
+    if (timed && h->timing && h->events[i]) (void)hipEventRecord(h->events[i], st);
   };
   mark(0);
   if (c.key_norm) {
     launch_stats_partial(pb, pl.S_stats, stats_part, st);
-    // the MFMA gradient kernel merges the slices itself; the generic kernels
-    // read finished (mu, rstd) pairs
+    // the MFMA gradient kernel merges the slices itself; the generic and
+    // convolution kernels read finished (mu, rstd) pairs
     if (!pl.mfma_grad) launch_stats_final(pb, pl.S_stats, stats_part, c.eps, stats, st);
   }
-  if (op.rule != RULE_GD) {     // the momentum starts at zero: a fill kernel (graph-capture safe)
+  if (op.rule != RULE_GD)      // the momentum starts at zero: a fill kernel (graph-capture safe)
     launch_fill_zero(mom, (long long)pl.P * pl.wsz, st);
-  }
   mark(1);
 
   // update batches in order; state b + 1 holds the weights after batch b
@@ -435,7 +512,7 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
       ua.S = 0;
       ua.rule = RULE_GD;
       ua.renorm = 0;
-      for (int i = 0; i < 3; ++i) ua.out[i] = (last_batch && W_out && i < nm) ? W_out->w[i] : nullptr;
+      for (int i = 0; i < 3; ++i) ua.out[i] = last_batch ? wout[i] : nullptr;
       launch_update(pb, ua, st);
       continue;
     }
@@ -443,12 +520,14 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
       // later epochs of a batch read and rewrite state b + 1 in place
       const WRef src = e == 0 ? cur : state_ref(b + 1);
       if (first_step) mark(2);
-      if (pl.lact_grad) {
-        launch_lact_grad(pb, src, t0, nt, pl.S_grad, eta->scale, part, st);
+      if (pl.dwconv) {
+        launch_dwconv_grad(pb, src, pl.S_grad, part, st);
+      } else if (pl.lact_grad) {
+        launch_lact_grad(pb, src, t0, nt, pl.S_grad, cl.eta->scale, part, st);
       } else if (pl.mfma_grad) {
         // the kernel accumulates eta_n-weighted (V_hat - V) or -eta_n V; the
         // scalar eta and the MSE constant 2/(n_b d) are applied to its partials
-        const float scale = pb.loss == LOSS_MSE ? eta->scale * 2.0f / ((float)nt * (float)c.d) : eta->scale;
+        const float scale = pb.loss == LOSS_MSE ? cl.eta->scale * 2.0f / ((float)nt * (float)c.d) : cl.eta->scale;
         launch_mfma_full_grad(pb, src, t0, nt, scale, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part, st);
       } else {
         launch_gen_grad_out(pb, src, t0, nt, gbuf, st);
@@ -461,7 +540,7 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
       ua.S = pl.S_grad;
       if (pl.mfma_grad) mfma_grad_geometry(pb, nt, &ua.sk_G, &ua.sk_J, &ua.sk_tpp);
       const bool last = last_batch && e == op.epochs - 1;
-      for (int i = 0; i < 3; ++i) ua.out[i] = (last && W_out && i < nm) ? W_out->w[i] : nullptr;
+      for (int i = 0; i < 3; ++i) ua.out[i] = last ? wout[i] : nullptr;
       ua.mom_only = op.rule == RULE_MUON;
       if (first_step) mark(4);
       launch_update(pb, ua, st);
@@ -484,7 +563,9 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
   const float* rstates = op.causal ? states : states + (long long)(pl.nb - 1) * pl.state_stride;
   const int rchunk = op.causal ? chunk : 0;
   const int rn = op.causal ? pl.nb : 1;
-  if (pl.mfma_query) {
+  if (pl.dwconv) {
+    launch_dwconv_query(pb, rstates, st);
+  } else if (pl.mfma_query) {
     launch_mfma_query(pb, w0, rstates, pl.state_stride, rn, rchunk, st);
   } else if (pl.lact_query) {
     launch_lact_readout(pb, w0, rstates, pl.state_stride, rn, rchunk, st);
@@ -492,15 +573,73 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
     launch_gen_query(pb, w0, rstates, pl.state_stride, rn, rchunk, st);
   }
   mark(7);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
+                   const ttt_eta* eta, int loss, int inner, int chunk, const ttt_options* opt, void* o,
+                   const ttt_weights_out* W_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!h) return fail(nullptr, TTT_ERR_INVALID, "handle is NULL");
+  h->err.clear();
+  Opts op;
+  int rc = check_request(h, loss, inner, chunk, opt, &op);
+  if (rc) return rc;
+  const ttt_config& c = h->cfg;
+  if (!q || !k || !v || !o) return fail(h, TTT_ERR_INVALID, "q, k, v and o must be non-NULL");
+  if (!W0) return fail(h, TTT_ERR_INVALID, "W0 is NULL");
+  if (!eta) return fail(h, TTT_ERR_INVALID, "eta is NULL");
+  if (!std::isfinite(eta->scale)) return fail(h, TTT_ERR_INVALID, "eta scale must be finite");
+  const int nm = n_mats(inner);
+  for (int i = 0; i < nm; ++i)
+    if (!W0->w[i]) return fail(h, TTT_ERR_INVALID, "W0.w[%d] is NULL", i);
+  const Layout L = make_layout(h, loss, inner, chunk, op);
+  if (inner == TTT_INNER_VIT3 && W0->batch_stride != 0)
+    return fail(h, TTT_ERR_UNSUPPORTED, "the ViT3 block takes W0 shared over the batch (batch_stride 0)");
+  if (W0->batch_stride != 0 && W0->batch_stride < (long long)c.H * L.pb[0].msz)
+    return fail(h, TTT_ERR_INVALID, "W0.batch_stride must be 0 or >= H*in*out (%lld)", (long long)c.H * L.pb[0].msz);
+  if (!workspace) return fail(h, TTT_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (ws_bytes < L.total) return fail(h, TTT_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(h, TTT_ERR_INVALID, "workspace must be 256-byte aligned");
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const bool log = (c.flags & TTT_FLAG_LOG) || env_log();
+  if (log)
+    for (int i = 0; i < L.n; ++i) {
+      const Plan& pl = L.pl[i];
+      std::fprintf(stderr, "[ttt] B=%d H=%d(%d..%d) N=%d d=%d h=%d %s model=%d loss=%d chunk=%d nb=%d epochs=%d "
+                   "mask=0x%x %s rule=%d grad=%s(S=%d) query=%s ws=%zu\n",
+                   c.B, c.H, L.r[i].h0, L.r[i].h0 + L.r[i].hc - 1, c.N, c.d, pl.hid, c.dtype == TTT_BF16 ? "bf16" : "f32",
+                   L.r[i].model, loss, chunk, pl.nb, op.epochs, range_mask(op.mask, L.r[i]),
+                   op.causal ? "causal" : "write-then-query", op.rule,
+                   pl.dwconv ? "dwconv" : pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu" : "generic", pl.S_grad,
+                   pl.dwconv ? "dwconv" : pl.mfma_query ? "mfma" : pl.lact_query ? "mfma_swiglu" : "generic", L.total);
+    }
+
+  // hipGetLastError is per thread and sticky: drop an error some earlier,
+  // unrelated runtime call left behind so that only our launches are judged.
+  (void)hipGetLastError();
+  const Call cl{q, k, v, o, W0, eta, W_out, chunk, st};
+  for (int i = 0; i < L.n; ++i) enqueue_range(h, L.r[i], L.pb[i], L.pl[i], op, ws + L.base[i], cl, i == 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
 
   if (c.flags & TTT_FLAG_CHECK_FINITE) {
+    int* flag = reinterpret_cast<int*>(ws + L.base[0] + L.pl[0].off_flag);
     launch_zero_flag(flag, st);   // a fill kernel, not a memset node (graph-capture safe)
-    float* wf[3] = {nullptr, nullptr, nullptr};
-    float* last = states + (long long)(pl.nb - 1) * pl.state_stride;
-    wf[0] = last;   // the final state is contiguous: P * wsz floats
-    launch_check_finite(pb, wf, (long long)pl.P * pl.wsz, flag, st);
+    for (int i = 0; i < L.n; ++i) {
+      // O once (every head), then each range's final state (contiguous: P * wsz floats)
+      Problem pb = L.pb[i];
+      pb.o = o;
+      const Plan& pl = L.pl[i];
+      float* wf[3] = {reinterpret_cast<float*>(ws + L.base[i] + pl.off_states) + (long long)(pl.nb - 1) * pl.state_stride,
+                      nullptr, nullptr};
+      const long long n_out = i == 0 ? (long long)c.B * c.H * c.N * c.d : 0;
+      launch_check_finite(pb, n_out, wf, (long long)pl.P * pl.wsz, flag, st);
+    }
     int hflag = 0;
     e = hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, st);
     if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");

@@ -8,20 +8,28 @@ struct ttt_handle;
 
 namespace ttt {
 
-enum { INNER_LINEAR = 0, INNER_MLP = 1, INNER_SWIGLU = 2 };
+enum { INNER_LINEAR = 0, INNER_MLP = 1, INNER_SWIGLU = 2, INNER_GLU = 3, INNER_DWCONV = 4 };
 enum { LOSS_MSE = 0, LOSS_DOT = 1 };
 
 // Everything a kernel of one update batch (the whole sequence in full-batch
 // mode, one chunk in causal mode) needs to know.
+// A problem covers heads [h0, h0 + H) of tensors with Hs heads; its pairs
+// p = b H + h (b < B, h < H) are numbered compactly (weight states, partials
+// and statistics use p), and row(p) gives the pair's row of the [B, Hs, N, d]
+// tensors, of eta_tok and of W_out.
 struct Problem {
-  int B, H, N, d, hid;    // hid: hidden width (d for LINEAR)
+  int B, H, N, d, hid;    // hid: hidden width (d for LINEAR and GLU)
   int inner, loss, nm;    // nm: matrices of the inner model
   int bf16;               // q/k/v/o are bf16 (else fp32)
   const void* q; const void* k; const void* v; void* o;
-  const float* eta_tok;   // [B,H,N] or null
+  const float* eta_tok;   // [B,Hs,N] or null
   float eta_scale;
   const float* stats;     // [P][d][2] (mu, rstd) or null (no key norm)
-  long long msz;          // elements per matrix (d*hid, or d*d)
+  long long msz;          // elements per matrix (d*hid, d*d, or d*k*k)
+  int Hs, h0;             // heads of the tensors, first head of this problem
+  int gh, gw, ck;         // DWCONV: token raster and kernel size
+  __host__ __device__ long long row(long long p) const { return (p / H) * Hs + h0 + p % H; }
+  __host__ __device__ bool full_heads() const { return Hs == H && h0 == 0; }
 };
 
 // ---- key statistics --------------------------------------------------------
@@ -160,6 +168,13 @@ size_t muon_scratch_floats(const Problem& pb);
 void launch_muon(const Problem& pb, const float* mom, float* next, float* const* out, unsigned mask, float scale,
                  int ns_steps, float* scratch, hipStream_t st);
 
+// ---- depthwise-convolution inner model (full batch) --------------------------
+// partial dw over S token splits -> part[S][P][1][d*ck*ck]; readout from the
+// state at `state` (layout [P][d*ck*ck])
+int dwconv_grad_splits(const Problem& pb);
+void launch_dwconv_grad(const Problem& pb, const WRef& W, int S, float* part, hipStream_t st);
+void launch_dwconv_query(const Problem& pb, const float* state, hipStream_t st);
+
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cu_count();
 
@@ -174,7 +189,8 @@ int set_error(ttt_handle* h, int code, const char* fmt, ...);
 void launch_zero_flag(int* flag, hipStream_t st);
 // n floats at p set to zero by a fill kernel (no memset node under graph capture)
 void launch_fill_zero(float* p, long long n, hipStream_t st);
-void launch_check_finite(const Problem& pb, float* const* wfinal, long long wcount, int* flag,
+// n elements of pb.o and wcount elements at each non-null wfinal[i]
+void launch_check_finite(const Problem& pb, long long n, float* const* wfinal, long long wcount, int* flag,
                          hipStream_t st);
 
 }  // namespace ttt

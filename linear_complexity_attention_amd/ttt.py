@@ -33,7 +33,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 TTT_OK, TTT_ERR_INVALID, TTT_ERR_UNSUPPORTED, TTT_ERR_HIP, TTT_ERR_NONFINITE, TTT_ERR_WORKSPACE = range(6)
 TTT_F32, TTT_BF16 = 0, 1
 TTT_LOSS_MSE, TTT_LOSS_DOT = 0, 1
-TTT_INNER_LINEAR, TTT_INNER_MLP_GELU, TTT_INNER_SWIGLU = 0, 1, 2
+TTT_INNER_LINEAR, TTT_INNER_MLP_GELU, TTT_INNER_SWIGLU, TTT_INNER_GLU, TTT_INNER_DWCONV, TTT_INNER_VIT3 = range(6)
 TTT_FLAG_CHECK_FINITE, TTT_FLAG_FORCE_GENERIC, TTT_FLAG_LOG = 0x1, 0x2, 0x4
 
 TTT_RULE_GD, TTT_RULE_MOMENTUM, TTT_RULE_MUON = 0, 1, 2
@@ -42,14 +42,16 @@ TTT_ORDER_CAUSAL, TTT_ORDER_WRITE_THEN_QUERY = 0, 1
 LOSSES = {"mse": TTT_LOSS_MSE, "dot": TTT_LOSS_DOT}
 RULES = {"gd": TTT_RULE_GD, "momentum": TTT_RULE_MOMENTUM, "muon": TTT_RULE_MUON}
 ORDERS = {"causal": TTT_ORDER_CAUSAL, "write_then_query": TTT_ORDER_WRITE_THEN_QUERY}
-INNERS = {"linear": TTT_INNER_LINEAR, "mlp_gelu": TTT_INNER_MLP_GELU, "swiglu": TTT_INNER_SWIGLU}
-N_MATRICES = {TTT_INNER_LINEAR: 1, TTT_INNER_MLP_GELU: 2, TTT_INNER_SWIGLU: 3}
+INNERS = {"linear": TTT_INNER_LINEAR, "mlp_gelu": TTT_INNER_MLP_GELU, "swiglu": TTT_INNER_SWIGLU,
+          "glu": TTT_INNER_GLU, "dwconv": TTT_INNER_DWCONV, "vit3": TTT_INNER_VIT3}
+N_MATRICES = {TTT_INNER_LINEAR: 1, TTT_INNER_MLP_GELU: 2, TTT_INNER_SWIGLU: 3, TTT_INNER_GLU: 2,
+              TTT_INNER_DWCONV: 1, TTT_INNER_VIT3: 3}
 
 
 class ttt_config(ctypes.Structure):
     _fields_ = [("B", c_int), ("H", c_int), ("N", c_int), ("d", c_int), ("hidden", c_int),
                 ("dtype", c_int), ("key_norm", c_int), ("eps", c_float), ("renorm", c_int),
-                ("flags", c_uint)]
+                ("flags", c_uint), ("grid_h", c_int), ("grid_w", c_int), ("conv_k", c_int)]
 
 
 class ttt_weights(ctypes.Structure):
@@ -108,14 +110,21 @@ EXPORTED = ("ttt_version", "ttt_create", "ttt_workspace_bytes", "ttt_workspace_b
             "ttt_destroy", "ttt_last_error", "ttt_status_string")
 
 
-def matrix_shapes(inner: int, d: int, hidden: int):
-    """[in, out] shape of every matrix of the inner model (include/ttt.h)."""
+def matrix_shapes(inner: int, d: int, hidden: int, conv_k: int = 3):
+    """[in, out] shape of every matrix of the inner model (include/ttt.h);
+    a convolution kernel is [d, k*k]."""
     if inner == TTT_INNER_LINEAR:
         return [(d, d)]
     if inner == TTT_INNER_MLP_GELU:
         return [(d, hidden), (hidden, d)]
     if inner == TTT_INNER_SWIGLU:
         return [(d, hidden), (hidden, d), (d, hidden)]
+    if inner == TTT_INNER_GLU:
+        return [(d, d), (d, d)]
+    if inner == TTT_INNER_DWCONV:
+        return [(d, conv_k * conv_k)]
+    if inner == TTT_INNER_VIT3:
+        return [(d, d), (d, d), (d, conv_k * conv_k)]
     raise ValueError(f"unknown inner model {inner}")
 
 
@@ -242,9 +251,12 @@ class TTTLayer:
     """
 
     def __init__(self, B, H, N, d, hidden, *, dtype="bf16", key_norm=True, eps=1e-5, renorm=False,
-                 flags=0):
+                 flags=0, grid=(0, 0), conv_k=0):
+        """grid = (grid_h, grid_w) and conv_k: the token raster and kernel size
+        of the convolution inner models ("dwconv", "vit3")."""
         self.cfg = ttt_config(B, H, N, d, hidden, TTT_BF16 if dtype == "bf16" else TTT_F32,
-                              int(key_norm), float(eps), int(renorm), int(flags))
+                              int(key_norm), float(eps), int(renorm), int(flags), int(grid[0]), int(grid[1]),
+                              int(conv_k))
         self.handle = ttt_create(self.cfg)
         self._ws = None
 
@@ -281,7 +293,7 @@ class TTTLayer:
                                  f"{(c.B, c.H, c.N, c.d)}")
         li, ii = LOSSES[loss], INNERS[inner]
         nm = N_MATRICES[ii]
-        shapes = matrix_shapes(ii, c.d, c.hidden)
+        shapes = matrix_shapes(ii, c.d, c.hidden, c.conv_k)
         if len(W0) != nm:
             raise ValueError(f"{inner} needs {nm} weight matrices")
         lead = None

@@ -38,6 +38,8 @@ class Workload:
     key_shift: float = 0.5        # constant added to every key channel
     unit_columns: bool = False    # W0 columns scaled to unit L2 norm
     seed: int = 0
+    grid: tuple = (0, 0)          # token raster (convolution inner models)
+    conv_k: int = 0               # convolution kernel size
     note: str = field(default="", compare=False)
 
     @property
@@ -59,13 +61,19 @@ WORKLOADS = {
 }
 
 
-def matrix_shapes(inner: str, d: int, hidden: int):
+def matrix_shapes(inner: str, d: int, hidden: int, conv_k: int = 3):
     if inner == "linear":
         return [(d, d)]
     if inner == "mlp_gelu":
         return [(d, hidden), (hidden, d)]
     if inner == "swiglu":
         return [(d, hidden), (hidden, d), (d, hidden)]
+    if inner == "glu":
+        return [(d, d), (d, d)]
+    if inner == "dwconv":
+        return [(d, conv_k * conv_k)]
+    if inner == "vit3":
+        return [(d, d), (d, d), (d, conv_k * conv_k)]
     raise ValueError(inner)
 
 
@@ -75,7 +83,8 @@ def make_inputs(w: Workload, *, B=None, H=None, N=None, seed=None, shared_w0=Tru
     Q, K, V ~ N(0, 1), then ``key_shift`` is added to every key channel (the
     constant key shift the key normalisation must cancel).  W0 ~ N(0, 1/d) for
     every matrix, or Gaussian columns scaled to unit L2 norm when
-    ``unit_columns``.  eta_tok = 0.1 * softplus(z), z ~ N(0, 1) per (b, h, n),
+    ``unit_columns``; a convolution kernel [d, k*k] ~ N(0, 1/k^2) (each output
+    is a sum of k^2 taps).  eta_tok = 0.1 * softplus(z), z ~ N(0, 1) per (b, h, n),
     when ``per_token_eta`` (else None).  With ``shared_w0=False`` W0 gets a
     leading batch axis ([B, H, in, out]).
     """
@@ -91,9 +100,13 @@ def make_inputs(w: Workload, *, B=None, H=None, N=None, seed=None, shared_w0=Tru
         k += np.float32(w.key_shift)
     lead = (H,) if shared_w0 else (B, H)
     W0 = []
-    for (fi, fo) in matrix_shapes(w.inner, w.d, w.hidden):
+    shapes = matrix_shapes(w.inner, w.d, w.hidden, w.conv_k)
+    for i, (fi, fo) in enumerate(shapes):
         m = rng.standard_normal(lead + (fi, fo), dtype=np.float32)
-        if w.unit_columns:
+        conv = (w.inner == "dwconv") or (w.inner == "vit3" and i == 2)
+        if conv:
+            m *= np.float32(1.0 / w.conv_k)
+        elif w.unit_columns:
             m /= np.sqrt((m.astype(np.float64) ** 2).sum(axis=-2, keepdims=True)).astype(np.float32)
         else:
             m *= np.float32(1.0 / np.sqrt(w.d))

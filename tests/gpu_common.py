@@ -29,7 +29,7 @@ def run_gpu(w: Workload, dev_in, *, flags=0, eta=None, return_weights=True, chun
     tq, tk, tv, tW, tet = dev_in
     B, H, N, d = tq.shape
     layer = ttt.TTTLayer(B, H, N, d, w.hidden, dtype=w.dtype, key_norm=w.key_norm, eps=eps,
-                         renorm=w.renorm, flags=flags)
+                         renorm=w.renorm, flags=flags, grid=w.grid, conv_k=w.conv_k)
     W_out = None
     if return_weights:
         W_out = [torch.empty((B, H) + tuple(m.shape[-2:]), dtype=torch.float32, device=tq.device) for m in tW]
@@ -46,6 +46,8 @@ def run_oracle(w: Workload, exact, *, pairs=None, eta=None, chunk=None, eps=1e-5
     okw: extra oracle keywords (update variants)."""
     kw = dict(eta_scale=w.eta if eta is None else eta, loss=w.loss, inner=w.inner,
               chunk=w.chunk if chunk is None else chunk, key_norm=w.key_norm, eps=eps, renorm=w.renorm)
+    if w.conv_k:
+        kw["grid"] = w.grid
     kw.update(okw or {})
     if pairs is None:
         return orc.oracle_forward(exact["q"], exact["k"], exact["v"], exact["W0"], eta_tok=exact["eta_tok"], **kw)

@@ -137,3 +137,29 @@ def test_options_rejected_on_the_host():
         layer.workspace_bytes("mse", "mlp_gelu", 16, ttt.make_options())
     assert ei.value.status == ttt.TTT_ERR_UNSUPPORTED
     assert layer.workspace_bytes("mse", "mlp_gelu", 16, ttt.make_options(order="write_then_query")) > 0
+
+
+def test_convolution_requests_validated_on_host():
+    """The convolution inner models need a raster with grid_h * grid_w == N and
+    an odd kernel size, run full batch only, and take neither Muon nor the
+    column re-norm."""
+    def layer(**kw):
+        args = dict(grid=(10, 10), conv_k=3, key_norm=False)
+        args.update(kw)
+        return ttt.TTTLayer(1, 2, 100, 64, 64, **args)
+
+    assert layer().workspace_bytes("dot", "dwconv", 0) > 0
+    assert layer().path_name("dot", "vit3", 0) == "dwconv+generic"
+    assert layer().path_name("dot", "glu", 0) == "generic"
+    for lay, inner, chunk, opt, code in [
+        (layer(grid=(10, 9)), "dwconv", 0, None, ttt.TTT_ERR_INVALID),
+        (layer(conv_k=4), "dwconv", 0, None, ttt.TTT_ERR_UNSUPPORTED),
+        (layer(conv_k=9), "vit3", 0, None, ttt.TTT_ERR_UNSUPPORTED),
+        (layer(), "dwconv", 50, None, ttt.TTT_ERR_UNSUPPORTED),
+        (layer(renorm=True), "vit3", 0, None, ttt.TTT_ERR_UNSUPPORTED),
+        (layer(), "dwconv", 0, ttt.make_options(rule="muon"), ttt.TTT_ERR_UNSUPPORTED),
+        (layer(), "vit3", 0, ttt.make_options(update_mask=8), ttt.TTT_ERR_INVALID),
+    ]:
+        with pytest.raises(ttt.TTTError) as ei:
+            lay.workspace_bytes("dot", inner, chunk, opt)
+        assert ei.value.status == code, (inner, chunk)
