@@ -435,3 +435,123 @@ def oracle_readout(q, W, inner, grid=None):
             model, used = head_model(inner, h)
             O[b, h] = inner_forward(model, [np.asarray(W[i], np.float64)[b, h] for i in used], q[b, h], grid)[0]
     return O
+
+
+# ---------------------------------------------------------------------------
+# Outer-loop backward [ViT3 §02: the whole inner update is differentiable and
+# trained end to end with the outer network (a gradient of a gradient);
+# §03 guideline 1: the value projection learns through the mixed second
+# derivative of the loss].  Given dO = dS/dO of an outer loss S, the gradients
+# of S with respect to Q, K, V, W0 and the per-token rates eta_n, for the full-
+# batch single gradient step (chunk 0, one epoch, plain gradient descent, no
+# re-norm), for the linear and the GELU-MLP inner models.
+#
+# Steps, per (b, h):
+#   1. forward: K_hat, W* = W0 - g(W0), g = dL/dW at W0 (as oracle_forward)
+#   2. readout backward at W*: U = dS/dW* and dQ (the inner backward with X = Q
+#      and G = dO, plus the input gradient)
+#   3. W* = W0 - g(W0, K_hat, V, eta): with phi = <g, U> = the derivative of L
+#      along U (forward-mode tangent F_dot of the inner model along U, phi =
+#      sum <G, F_dot>), dW0 = U - dphi/dW0, dK_hat = -dphi/dK_hat,
+#      dV = -dphi/dV, deta = -dphi/deta (reverse mode through phi)
+#   4. key-norm backward: dK = rstd (dK_hat - mean_n dK_hat - K_hat mean_n(dK_hat K_hat))
+# Reading: W0 shared over the batch ([H, in, out]) gets the sum over b of its
+# pairs' gradients; deta is the gradient with respect to the effective rate
+# eta_n = eta_scale * eta_tok[n] of each token.
+# ---------------------------------------------------------------------------
+def gelu_second(z):
+    """gelu''(z) = phi(z) (2 - z^2), phi the standard normal density."""
+    return np.exp(-0.5 * z * z) * _INV_SQRT_2PI * (2.0 - z * z)
+
+
+def _readout_backward(inner, W, Q, dO):
+    """dS/dW and dS/dQ of O = F_W(Q) given dO."""
+    if inner == INNER_LINEAR:
+        return [Q.T @ dO], dO @ W[0].T
+    Z = Q @ W[0]
+    A = gelu(Z)
+    dZ = (dO @ W[1].T) * gelu_prime(Z)
+    return [Q.T @ dZ, A.T @ dO], dZ @ W[0].T
+
+
+def _phi_backward(inner, loss, W, U, X, V, eta):
+    """Reverse mode of phi = <dL/dW, U> = sum_n <G_n, F_dot_n> with respect to
+    (W, X, V, eta).  Returns (dW list, dX, dV, deta)."""
+    nb, d = V.shape
+    c = 1.0 / (nb * d)
+    # forward and tangent along U
+    if inner == INNER_LINEAR:
+        F = X @ W[0]
+        Fd = X @ U[0]
+    else:
+        Z = X @ W[0]
+        A = gelu(Z)
+        F = A @ W[1]
+        Zd = X @ U[0]
+        Ad = gelu_prime(Z) * Zd
+        Fd = Ad @ W[1] + A @ U[1]
+    G = loss_grad(loss, F, V, eta)
+    # reverse: phi = <G, Fd>
+    Gb = Fd                                   # d phi / d G
+    if loss == LOSS_MSE:
+        Fb = 2.0 * c * eta[:, None] * Gb      # through G = 2 c eta (F - V)
+        Vb = -Fb
+        etab = 2.0 * c * np.sum(Gb * (F - V), axis=1)
+    else:
+        Fb = np.zeros_like(F)                 # G = -eta V does not depend on F
+        Vb = -eta[:, None] * Gb
+        etab = -np.sum(Gb * V, axis=1)
+    Fdb = G                                   # d phi / d Fd
+    if inner == INNER_LINEAR:
+        Wb = [X.T @ Fb]                       # F = X W
+        Xb = Fdb @ U[0].T + Fb @ W[0].T       # Fd = X U, F = X W
+        return Wb, Xb, Vb, etab
+    Adb = Fdb @ W[1].T                        # Fd = Ad W2 + A U2
+    W2b = Ad.T @ Fdb + A.T @ Fb               # ... and F = A W2
+    Ab = Fdb @ U[1].T + Fb @ W[1].T
+    Zdb = gelu_prime(Z) * Adb                 # Ad = gelu'(Z) Zd
+    Zb = gelu_second(Z) * Zd * Adb + gelu_prime(Z) * Ab
+    Xb = Zdb @ U[0].T + Zb @ W[0].T           # Zd = X U1, Z = X W1
+    W1b = X.T @ Zb
+    return [W1b, W2b], Xb, Vb, etab
+
+
+def key_instnorm_backward(K, dKh, eps):
+    mu = K.mean(axis=0, keepdims=True)
+    rstd = 1.0 / np.sqrt(((K - mu) ** 2).mean(axis=0, keepdims=True) + eps)
+    Kh = (K - mu) * rstd
+    return rstd * (dKh - dKh.mean(axis=0, keepdims=True) - Kh * (dKh * Kh).mean(axis=0, keepdims=True))
+
+
+def oracle_backward(q, k, v, W0, dO, *, eta_scale=1.0, eta_tok=None, loss=LOSS_MSE, inner=INNER_MLP,
+                    key_norm=True, eps=1e-5):
+    """Gradients of S = sum(dO * O) for the full-batch single-step layer.
+    Returns dict(dq, dk, dv [B, H, N, d], dW0 (list, W0's layout), deta [B, H, N])."""
+    if inner not in (INNER_LINEAR, INNER_MLP):
+        raise ValueError("the outer-loop backward covers the linear and GELU-MLP inner models")
+    q, k, v, dO = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dO))
+    B, H, N, d = q.shape
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(q), dv=np.zeros_like(q), deta=np.zeros((B, H, N)),
+               dW0=[np.zeros(np.asarray(w).shape) for w in W0])
+    for b in range(B):
+        for h in range(H):
+            W = _pair_weights(W0, b, h)
+            Q, K, V = q[b, h], k[b, h], v[b, h]
+            eta = np.full(N, float(eta_scale))
+            if eta_tok is not None:
+                eta = eta * np.asarray(eta_tok, dtype=np.float64)[b, h]
+            Kh = key_instnorm(K, eps) if key_norm else K
+            Ws, _ = inner_step(inner, loss, W, Kh, V, eta)                 # 1
+            U, dQ = _readout_backward(inner, Ws, Q, dO[b, h])              # 2
+            Wb, Xb, Vb, etab = _phi_backward(inner, loss, W, U, Kh, V, eta)  # 3
+            dKh = -Xb
+            out["dq"][b, h] = dQ
+            out["dv"][b, h] = -Vb
+            out["deta"][b, h] = -etab
+            out["dk"][b, h] = key_instnorm_backward(K, dKh, eps) if key_norm else dKh   # 4
+            for i, (u, wb) in enumerate(zip(U, Wb)):
+                if np.asarray(W0[i]).ndim == 3:
+                    out["dW0"][i][h] += u - wb
+                else:
+                    out["dW0"][i][b, h] = u - wb
+    return out

@@ -764,3 +764,119 @@ def test_vit3_heads_are_the_two_models():
     np.testing.assert_array_equal(Wf[2][:, :1], Wfc[0])
     np.testing.assert_array_equal(Wf[0][:, 1:], Wfg[0])
     np.testing.assert_array_equal(Wf[1][:, 1:], Wfg[1])
+
+
+# --------------------------------------------------------------------------
+# Outer-loop backward (gradient through the inner update)
+# --------------------------------------------------------------------------
+def _outer_case(rng, inner, B=1, H=2, N=7, d=3, h=4, shared=True):
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d)) + 0.5
+    v = rng.standard_normal((B, H, N, d))
+    dO = rng.standard_normal((B, H, N, d))
+    shapes = [(d, d)] if inner == orc.INNER_LINEAR else [(d, h), (h, d)]
+    lead = (H,) if shared else (B, H)
+    W0 = [rng.standard_normal(lead + s) * 0.6 for s in shapes]
+    eta_tok = 0.5 + rng.random((B, H, N))
+    return q, k, v, dO, W0, eta_tok
+
+
+@pytest.mark.parametrize("inner", [orc.INNER_LINEAR, orc.INNER_MLP])
+@pytest.mark.parametrize("loss", [orc.LOSS_MSE, orc.LOSS_DOT])
+@pytest.mark.parametrize("key_norm", [False, True])
+def test_outer_backward_matches_finite_differences(inner, loss, key_norm):
+    """Brute force: central differences of S = sum(dO * O) with respect to
+    every element of q, k, v, W0 and the per-token rates."""
+    rng = np.random.default_rng(50)
+    q, k, v, dO, W0, et = _outer_case(rng, inner, B=2, H=1, shared=True)
+    scale = 0.7
+
+    def S(q_, k_, v_, W_, et_):
+        O, _ = orc.oracle_forward(q_, k_, v_, W_, eta_scale=scale, eta_tok=et_, loss=loss, inner=inner, chunk=0,
+                                  key_norm=key_norm, eps=1e-5)
+        return float(np.sum(dO * O))
+
+    g = orc.oracle_backward(q, k, v, W0, dO, eta_scale=scale, eta_tok=et, loss=loss, inner=inner,
+                            key_norm=key_norm, eps=1e-5)
+    e = 1e-6
+    for name, pos in (("dq", 0), ("dk", 1), ("dv", 2)):
+        base = [q, k, v]
+        num = np.zeros_like(q)
+        for ix in np.ndindex(q.shape):
+            p_, m_ = [a.copy() for a in base], [a.copy() for a in base]
+            p_[pos][ix] += e
+            m_[pos][ix] -= e
+            num[ix] = (S(*p_, W0, et) - S(*m_, W0, et)) / (2 * e)
+        np.testing.assert_allclose(g[name], num, rtol=1e-5, atol=1e-7, err_msg=name)
+    for i in range(len(W0)):
+        num = np.zeros_like(W0[i])
+        for ix in np.ndindex(W0[i].shape):
+            wp, wm = [w.copy() for w in W0], [w.copy() for w in W0]
+            wp[i][ix] += e
+            wm[i][ix] -= e
+            num[ix] = (S(q, k, v, wp, et) - S(q, k, v, wm, et)) / (2 * e)
+        np.testing.assert_allclose(g["dW0"][i], num, rtol=1e-5, atol=1e-7, err_msg=f"dW0[{i}]")
+    num = np.zeros_like(et)
+    for ix in np.ndindex(et.shape):
+        ep, em = et.copy(), et.copy()
+        ep[ix] += e
+        em[ix] -= e
+        num[ix] = (S(q, k, v, W0, ep) - S(q, k, v, W0, em)) / (2 * e)
+    # deta is the gradient with respect to eta_n = scale * eta_tok[n]
+    np.testing.assert_allclose(g["deta"] * scale, num, rtol=1e-5, atol=1e-7, err_msg="deta")
+
+
+@pytest.mark.parametrize("inner,loss,key_norm,shared", [
+    (orc.INNER_MLP, orc.LOSS_MSE, True, True),
+    (orc.INNER_MLP, orc.LOSS_DOT, False, False),
+    (orc.INNER_LINEAR, orc.LOSS_MSE, True, False),
+    (orc.INNER_LINEAR, orc.LOSS_DOT, True, True),
+])
+def test_outer_backward_matches_autograd(inner, loss, key_norm, shared):
+    """Independent derivation: the layer in torch with F.instance_norm and
+    F.gelu, the inner gradient by autograd with create_graph=True, and the
+    outer gradients by autograd through it."""
+    F = torch.nn.functional
+    rng = np.random.default_rng(51)
+    q, k, v, dO, W0, et = _outer_case(rng, inner, B=2, H=2, N=9, d=4, h=5, shared=shared)
+    scale = 0.8
+    g = orc.oracle_backward(q, k, v, W0, dO, eta_scale=scale, eta_tok=et, loss=loss, inner=inner,
+                            key_norm=key_norm, eps=1e-5)
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    tW = [torch.tensor(w, requires_grad=True) for w in W0]
+    teta = torch.tensor(et * scale, requires_grad=True)          # effective per-token rate
+    B, H, N, d = q.shape
+    kk = tk
+    if key_norm:
+        kk = F.instance_norm(tk.reshape(B * H, N, d).transpose(1, 2), eps=1e-5).transpose(1, 2).reshape(B, H, N, d)
+
+    def fwd(Ws, x):
+        return x @ Ws[0] if inner == orc.INNER_LINEAR else F.gelu(x @ Ws[0]) @ Ws[1]
+
+    S = 0.0
+    for b in range(B):
+        for h in range(H):
+            Ws = [w[h] if shared else w[b, h] for w in tW]
+            Vh = fwd(Ws, kk[b, h])
+            en = teta[b, h][:, None]
+            if loss == orc.LOSS_MSE:
+                Lv = (en * (Vh - tv[b, h]) ** 2).sum() / (N * d)
+            else:
+                Lv = -(en * Vh * tv[b, h]).sum()
+            grads = torch.autograd.grad(Lv, Ws, create_graph=True)
+            Wst = [w - gg for w, gg in zip(Ws, grads)]
+            S = S + (torch.tensor(dO[b, h]) * fwd(Wst, tq[b, h])).sum()
+    S.backward()
+    np.testing.assert_allclose(g["dq"], tq.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(g["dk"], tk.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(g["dv"], tv.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(g["deta"], teta.grad.numpy(), rtol=1e-9, atol=1e-11)
+    for a, t in zip(g["dW0"], tW):
+        np.testing.assert_allclose(a, t.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+def test_gelu_second_derivative_by_finite_difference():
+    z = np.linspace(-6, 6, 1201)
+    e = 1e-6
+    np.testing.assert_allclose(orc.gelu_second(z), (orc.gelu_prime(z + e) - orc.gelu_prime(z - e)) / (2 * e),
+                               rtol=1e-6, atol=1e-8)
