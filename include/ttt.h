@@ -248,6 +248,28 @@ int ttt_workspace_bytes_ex(const ttt_handle* h, int loss, int inner, int chunk, 
 /* Kernel family ttt_forward_ex would use; NULL for an invalid request. */
 const char* ttt_path_name_ex(const ttt_handle* h, int loss, int inner, int chunk, const ttt_options* opt);
 
+/* Outer-loop backward: the gradients of an outer loss S through the layer,
+ * given dO = dS/dO of its output (ViT3 page, section 02: the inner update is
+ * differentiable and trained end to end with the outer network, a gradient of
+ * a gradient; section 03 guideline 1: the value projection learns through the
+ * mixed second derivative of the inner loss).  Full batch (chunk 0), one plain
+ * gradient step, no re-norm; inner TTT_INNER_LINEAR or TTT_INNER_MLP_GELU;
+ * both losses; key norm on or off.  Other requests: TTT_ERR_UNSUPPORTED.
+ *   q, k, v, W0, eta, loss, inner: as for ttt_forward
+ *   dO          [B, H, N, d] in the config's dtype
+ *   dq, dk, dv  [B, H, N, d] fp32 outputs
+ *   dW0         fp32 outputs in W0's layout: [H, in, out] summed over the batch
+ *               when W0.batch_stride == 0, else [B, H, in, out]; NULL entries
+ *               (or a NULL struct) are skipped
+ *   deta        [B, H, N] fp32 output or NULL: the gradient with respect to each
+ *               token's effective rate eta_n = scale * per_token[b, h, n]
+ *   workspace   at least ttt_backward_workspace_bytes bytes, 256-byte aligned
+ * Asynchronous on `stream`, like ttt_forward; arithmetic in fp32. */
+int ttt_backward_workspace_bytes(const ttt_handle* h, int loss, int inner, size_t* bytes);
+int ttt_backward(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
+                 const ttt_eta* eta, int loss, int inner, const void* dO, float* dq, float* dk, float* dv,
+                 const ttt_weights_out* dW0, float* deta, void* workspace, size_t ws_bytes, void* stream);
+
 /* ttt_forward for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Arguments and results are those of ttt_forward, without the workspace: the

@@ -623,7 +623,10 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
   // unrelated runtime call left behind so that only our launches are judged.
   (void)hipGetLastError();
   const Call cl{q, k, v, o, W0, eta, W_out, chunk, st};
-  for (int i = 0; i < L.n; ++i) enqueue_range(h, L.r[i], L.pb[i], L.pl[i], op, ws + L.base[i], cl, i == 0);
+  int timed = 0;                 // the timing hook brackets the range with the most heads
+  for (int i = 1; i < L.n; ++i)
+    if (L.r[i].hc > L.r[timed].hc) timed = i;
+  for (int i = 0; i < L.n; ++i) enqueue_range(h, L.r[i], L.pb[i], L.pl[i], op, ws + L.base[i], cl, i == timed);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
 
@@ -647,6 +650,141 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
     if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");
     if (hflag) return fail(h, TTT_ERR_NONFINITE, "O or the final fast weights contain NaN/Inf");
   }
+  return TTT_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// workspace of the backward: the forward's statistics, W*, the split-N
+// partials and G, then the backward's own buffers
+struct BwdPlan {
+  int P, S, S_stats, S_kn;
+  long long wsz;
+  size_t off_stats_part, off_stats, off_states, off_part, off_gbuf, off_U, off_dpair, off_gG, off_gF, off_knp, total;
+};
+
+int check_backward(ttt_handle* h, int loss, int inner) {
+  const ttt_config& c = h->cfg;
+  if (loss != TTT_LOSS_MSE && loss != TTT_LOSS_DOT) return fail(h, TTT_ERR_INVALID, "unknown loss %d", loss);
+  if (inner < TTT_INNER_LINEAR || inner > TTT_INNER_VIT3) return fail(h, TTT_ERR_INVALID, "unknown inner model %d", inner);
+  if (inner != TTT_INNER_LINEAR && inner != TTT_INNER_MLP_GELU)
+    return fail(h, TTT_ERR_UNSUPPORTED, "the outer-loop backward covers the linear and GELU-MLP inner models");
+  if (inner == TTT_INNER_MLP_GELU && (c.hidden < 1 || c.hidden > 512))
+    return fail(h, TTT_ERR_UNSUPPORTED, "hidden must be in 1..512 (got %d)", c.hidden);
+  if (c.renorm) return fail(h, TTT_ERR_UNSUPPORTED, "the outer-loop backward has no re-norm");
+  return TTT_OK;
+}
+
+BwdPlan make_bwd_plan(const ttt_handle* h, const Problem& pb) {
+  const ttt_config& c = h->cfg;
+  BwdPlan bp{};
+  bp.P = pb.B * pb.H;
+  bp.wsz = pb.msz * pb.nm;
+  bp.S = choose_splits((long long)bp.P * ((pb.hid + 31) / 32), c.N, 16, 1024);
+  bp.S_stats = c.key_norm ? stats_splits(bp.P, c.N) : 0;
+  bp.S_kn = c.key_norm ? bwd_kn_splits(pb) : 0;
+  const size_t f = sizeof(float), tok = (size_t)bp.P * c.N * c.d;
+  size_t off = 0;
+  bp.off_stats_part = off;
+  if (c.key_norm) off = align256(off + f * (size_t)bp.P * bp.S_stats * 3 * c.d);
+  bp.off_stats = off;
+  if (c.key_norm) off = align256(off + f * (size_t)bp.P * c.d * 2);
+  bp.off_states = off;  off = align256(off + f * (size_t)bp.P * bp.wsz);
+  bp.off_part = off;    off = align256(off + f * (size_t)bp.S * bp.P * bp.wsz);
+  bp.off_gbuf = off;    off = align256(off + f * tok);
+  bp.off_U = off;       off = align256(off + f * (size_t)bp.P * bp.wsz);
+  bp.off_dpair = off;   off = align256(off + f * (size_t)bp.P * bp.wsz);
+  bp.off_gG = off;      off = align256(off + f * tok);
+  bp.off_gF = off;      off = align256(off + f * tok);
+  bp.off_knp = off;
+  if (c.key_norm) off = align256(off + f * (size_t)bp.P * bp.S_kn * 2 * c.d);
+  bp.total = off;
+  return bp;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_backward_workspace_bytes(const ttt_handle* hc, int loss, int inner, size_t* bytes) {
+  ttt_handle* h = const_cast<ttt_handle*>(hc);
+  if (!h) return fail(nullptr, TTT_ERR_INVALID, "handle is NULL");
+  if (!bytes) return fail(h, TTT_ERR_INVALID, "bytes is NULL");
+  int rc = check_backward(h, loss, inner);
+  if (rc) return rc;
+  Range r[2];
+  ranges_of(h->cfg, inner, r);
+  *bytes = make_bwd_plan(h, make_problem(h, loss, r[0])).total;
+  return TTT_OK;
+}
+
+int ttt_backward(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
+                 const ttt_eta* eta, int loss, int inner, const void* dO, float* dq, float* dk, float* dv,
+                 const ttt_weights_out* dW0, float* deta, void* workspace, size_t ws_bytes, void* stream) {
+  if (!h) return fail(nullptr, TTT_ERR_INVALID, "handle is NULL");
+  h->err.clear();
+  int rc = check_backward(h, loss, inner);
+  if (rc) return rc;
+  const ttt_config& c = h->cfg;
+  if (!q || !k || !v || !dO || !dq || !dk || !dv)
+    return fail(h, TTT_ERR_INVALID, "q, k, v, dO, dq, dk and dv must be non-NULL");
+  if (!W0) return fail(h, TTT_ERR_INVALID, "W0 is NULL");
+  if (!eta) return fail(h, TTT_ERR_INVALID, "eta is NULL");
+  if (!std::isfinite(eta->scale)) return fail(h, TTT_ERR_INVALID, "eta scale must be finite");
+  const int nm = n_mats(inner);
+  for (int i = 0; i < nm; ++i)
+    if (!W0->w[i]) return fail(h, TTT_ERR_INVALID, "W0.w[%d] is NULL", i);
+  Range r[2];
+  ranges_of(c, inner, r);
+  Problem pb = make_problem(h, loss, r[0]);
+  if (W0->batch_stride != 0 && W0->batch_stride < (long long)c.H * pb.msz)
+    return fail(h, TTT_ERR_INVALID, "W0.batch_stride must be 0 or >= H*in*out (%lld)", (long long)c.H * pb.msz);
+  const BwdPlan bp = make_bwd_plan(h, pb);
+  if (!workspace) return fail(h, TTT_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", bp.total);
+  if (ws_bytes < bp.total) return fail(h, TTT_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, bp.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(h, TTT_ERR_INVALID, "workspace must be 256-byte aligned");
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto buf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  pb.q = q; pb.k = k; pb.v = v; pb.o = nullptr;
+  pb.eta_scale = eta->scale;
+  pb.eta_tok = eta->per_token;
+  pb.stats = c.key_norm ? buf(bp.off_stats) : nullptr;
+  WRef w0{};
+  for (int i = 0; i < 3; ++i) w0.m[i] = W0->w[i < nm ? i : 0];
+  w0.sb = W0->batch_stride;
+  w0.sh = pb.msz;
+  (void)hipGetLastError();
+  // the forward's step: key statistics, G and the split-N gradient at W0, W*
+  if (c.key_norm) {
+    launch_stats_partial(pb, bp.S_stats, buf(bp.off_stats_part), st);
+    launch_stats_final(pb, bp.S_stats, buf(bp.off_stats_part), c.eps, buf(bp.off_stats), st);
+  }
+  launch_gen_grad_out(pb, w0, 0, c.N, buf(bp.off_gbuf), st);
+  launch_gen_dW(pb, w0, 0, c.N, buf(bp.off_gbuf), bp.S, buf(bp.off_part), st);
+  UpdateArgs ua{};
+  ua.cur = w0;
+  ua.w0 = w0;
+  ua.part = buf(bp.off_part);
+  ua.part_mode = PART_SPLITS;
+  ua.S = bp.S;
+  ua.part_pair_stride = (long long)bp.P * bp.wsz;
+  ua.next = buf(bp.off_states);
+  ua.mask = (1u << nm) - 1;
+  ua.rule = RULE_GD;
+  launch_update(pb, ua, st);
+  // the backward
+  float* dw[3] = {nullptr, nullptr, nullptr};
+  if (dW0)
+    for (int i = 0; i < nm; ++i) dw[i] = dW0->w[i];
+  launch_backward(pb, w0, buf(bp.off_states), dO, bp.S, buf(bp.off_part), buf(bp.off_gbuf), buf(bp.off_U),
+                  buf(bp.off_gG), buf(bp.off_gF), buf(bp.off_dpair), buf(bp.off_knp), bp.S_kn, dq, dk, dv, deta, dw,
+                  W0->batch_stride == 0, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
   return TTT_OK;
 }
 

@@ -175,6 +175,18 @@ int dwconv_grad_splits(const Problem& pb);
 void launch_dwconv_grad(const Problem& pb, const WRef& W, int S, float* part, hipStream_t st);
 void launch_dwconv_query(const Problem& pb, const float* state, hipStream_t st);
 
+// ---- outer-loop backward (full batch, one step, linear / GELU MLP) ----------
+// wstar_states: W* of every pair ([P][nm][msz]); S: token splits of the
+// weight reductions (part holds S * P * nm * msz floats); dO32, gG, gF:
+// [P][N][d] fp32; U, dpair: [P][nm][msz]; knp: [P][S_kn][2][d]; dq, dk, dv:
+// fp32 [B,Hs,N,d]; deta fp32 [B,Hs,N] or null; dW0[i] in W0's layout
+// ([H,in,out] summed over the batch when w0_shared, else [B,H,in,out]) or null.
+int bwd_kn_splits(const Problem& pb);
+void launch_backward(const Problem& pb, const WRef& w0, const float* wstar_states, const void* dO, int S,
+                     float* part, float* dO32, float* U, float* gG, float* gF, float* dpair, float* knp, int S_kn,
+                     float* dq, float* dk, float* dv, float* deta, float* const* dW0, int w0_shared,
+                     hipStream_t st);
+
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cu_count();
 

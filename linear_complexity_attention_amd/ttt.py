@@ -89,6 +89,12 @@ _lib.ttt_workspace_bytes_ex.restype = c_int
 _lib.ttt_workspace_bytes_ex.argtypes = [c_void_p, c_int, c_int, c_int, POINTER(ttt_options), POINTER(c_size_t)]
 _lib.ttt_path_name_ex.restype = c_char_p
 _lib.ttt_path_name_ex.argtypes = [c_void_p, c_int, c_int, c_int, POINTER(ttt_options)]
+_lib.ttt_backward_workspace_bytes.restype = c_int
+_lib.ttt_backward_workspace_bytes.argtypes = [c_void_p, c_int, c_int, POINTER(c_size_t)]
+_lib.ttt_backward.restype = c_int
+_lib.ttt_backward.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(ttt_weights), POINTER(ttt_eta), c_int,
+                              c_int, c_void_p, c_void_p, c_void_p, c_void_p, POINTER(ttt_weights_out), c_void_p,
+                              c_void_p, c_size_t, c_void_p]
 _lib.ttt_forward_noalloc.restype = c_int
 _lib.ttt_forward_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, POINTER(ttt_weights),
                                      POINTER(ttt_eta), c_int, c_int, c_int, c_void_p, POINTER(ttt_weights_out),
@@ -107,7 +113,7 @@ _lib.ttt_status_string.argtypes = [c_int]
 
 EXPORTED = ("ttt_version", "ttt_create", "ttt_workspace_bytes", "ttt_workspace_bytes_ex", "ttt_forward",
             "ttt_forward_ex", "ttt_forward_noalloc", "ttt_path_name", "ttt_path_name_ex", "ttt_set_timing_events",
-            "ttt_destroy", "ttt_last_error", "ttt_status_string")
+            "ttt_destroy", "ttt_last_error", "ttt_status_string", "ttt_backward", "ttt_backward_workspace_bytes")
 
 
 def matrix_shapes(inner: int, d: int, hidden: int, conv_k: int = 3):
@@ -192,6 +198,21 @@ def ttt_forward_ex(handle, q, k, v, W0: ttt_weights, eta: ttt_eta, loss: int, in
     return _lib.ttt_forward_ex(handle, q, k, v, byref(W0), byref(eta), loss, inner, chunk,
                                byref(opt) if opt is not None else None, o,
                                byref(W_out) if W_out is not None else None, workspace, ws_bytes, stream)
+
+
+def ttt_backward_workspace_bytes(handle, loss: int, inner: int) -> int:
+    n = c_size_t()
+    rc = _lib.ttt_backward_workspace_bytes(handle, loss, inner, byref(n))
+    if rc != TTT_OK:
+        raise TTTError(rc, ttt_last_error(handle))
+    return n.value
+
+
+def ttt_backward(handle, q, k, v, W0: ttt_weights, eta: ttt_eta, loss: int, inner: int, dO, dq, dk, dv, dW0, deta,
+                 workspace, ws_bytes: int, stream) -> int:
+    """Raw call of the outer-loop backward; returns the status code."""
+    return _lib.ttt_backward(handle, q, k, v, byref(W0), byref(eta), loss, inner, dO, dq, dk, dv,
+                             byref(dW0) if dW0 is not None else None, deta, workspace, ws_bytes, stream)
 
 
 def make_options(*, epochs=1, update_mask=0, order="causal", chunk_update=None, rule="gd", beta=0.0,
@@ -353,6 +374,62 @@ class TTTLayer:
         if rc != TTT_OK:
             raise TTTError(rc, ttt_last_error(self.handle))
         return out
+
+
+def _layer_backward(self, q, k, v, W0, dO, *, eta=1.0, eta_tok=None, loss="mse", inner="mlp_gelu",
+                    want_deta=True):
+    """Outer-loop backward: returns dict(dq, dk, dv, dW0 (list, W0's layout),
+    deta or None), fp32, for the gradient dO of an outer loss with respect to
+    the layer's output."""
+    import torch
+
+    c = self.cfg
+    tdt = torch.bfloat16 if c.dtype == TTT_BF16 else torch.float32
+    shape = (c.B, c.H, c.N, c.d)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dO", dO)):
+        if (not t.is_cuda or t.device != q.device or t.dtype != tdt or not t.is_contiguous()
+                or tuple(t.shape) != shape):
+            raise ValueError(f"{name} must be a contiguous cuda {tdt} tensor on q's device of shape {shape}")
+    li, ii = LOSSES[loss], INNERS[inner]
+    shapes = matrix_shapes(ii, c.d, c.hidden, c.conv_k)
+    if len(W0) != len(shapes):
+        raise ValueError(f"{inner} needs {len(shapes)} weight matrices")
+    lead = None
+    for i, (w, (fi, fo)) in enumerate(zip(W0, shapes)):
+        if (not w.is_cuda or w.device != q.device or w.dtype != torch.float32 or not w.is_contiguous()
+                or tuple(w.shape) not in ((c.H, fi, fo), (c.B, c.H, fi, fo))):
+            raise ValueError(f"W0[{i}] must be a contiguous float32 tensor of shape {(c.H, fi, fo)} or "
+                             f"{(c.B, c.H, fi, fo)}")
+        if lead is None:
+            lead = w.dim()
+        elif w.dim() != lead:
+            raise ValueError("all W0 matrices must share one layout")
+    if eta_tok is not None and (eta_tok.device != q.device or eta_tok.dtype != torch.float32
+                                or not eta_tok.is_contiguous() or tuple(eta_tok.shape) != (c.B, c.H, c.N)):
+        raise ValueError(f"eta_tok must be a contiguous float32 tensor of shape {(c.B, c.H, c.N)}")
+    nbytes = ttt_backward_workspace_bytes(self.handle, li, ii)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (torch.empty(shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    dW = [torch.empty_like(w) for w in W0]
+    deta = torch.empty((c.B, c.H, c.N), dtype=torch.float32, device=q.device) if want_deta else None
+    wts = ttt_weights()
+    for i, w in enumerate(W0):
+        wts.w[i] = w.data_ptr()
+    wts.batch_stride = c.H * shapes[0][0] * shapes[0][1] if lead == 4 else 0
+    wo = ttt_weights_out()
+    for i, w in enumerate(dW):
+        wo.w[i] = w.data_ptr()
+    e = ttt_eta(float(eta), eta_tok.data_ptr() if eta_tok is not None else None)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = ttt_backward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), wts, e, li, ii, dO.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), wo, deta.data_ptr() if deta is not None else None,
+                      ws.data_ptr(), ws.numel(), stream)
+    if rc != TTT_OK:
+        raise TTTError(rc, ttt_last_error(self.handle))
+    return dict(dq=dq, dk=dk, dv=dv, dW0=dW, deta=deta)
+
+
+TTTLayer.backward = _layer_backward
 
 
 def forward(q, k, v, W0, *, hidden=None, eta=1.0, eta_tok=None, loss="mse", inner="mlp_gelu", chunk=0,

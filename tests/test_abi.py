@@ -163,3 +163,32 @@ def test_convolution_requests_validated_on_host():
         with pytest.raises(ttt.TTTError) as ei:
             lay.workspace_bytes("dot", inner, chunk, opt)
         assert ei.value.status == code, (inner, chunk)
+
+
+def test_backward_requests_validated_on_host():
+    h = ttt.ttt_create(_cfg())
+    try:
+        assert ttt.ttt_backward_workspace_bytes(h, ttt.TTT_LOSS_MSE, ttt.TTT_INNER_MLP_GELU) > 0
+        assert ttt.ttt_backward_workspace_bytes(h, ttt.TTT_LOSS_DOT, ttt.TTT_INNER_LINEAR) > 0
+        for inner in (ttt.TTT_INNER_SWIGLU, ttt.TTT_INNER_GLU):
+            with pytest.raises(ttt.TTTError) as ei:
+                ttt.ttt_backward_workspace_bytes(h, ttt.TTT_LOSS_DOT, inner)
+            assert ei.value.status == ttt.TTT_ERR_UNSUPPORTED
+        fake = 1 << 20
+        W = ttt.ttt_weights()
+        W.w[0] = W.w[1] = fake
+        rc = ttt.ttt_backward(h, fake, fake, fake, W, ttt.ttt_eta(1.0, None), 0, 1, None, fake, fake, fake, None,
+                              None, fake, 1 << 30, None)
+        assert rc == ttt.TTT_ERR_INVALID and "dO" in ttt.ttt_last_error(h)
+        rc = ttt.ttt_backward(h, fake, fake, fake, W, ttt.ttt_eta(1.0, None), 0, 1, fake, fake, fake, fake, None,
+                              None, fake, 16, None)
+        assert rc == ttt.TTT_ERR_WORKSPACE
+    finally:
+        ttt.ttt_destroy(h)
+    h = ttt.ttt_create(_cfg(renorm=1))
+    try:
+        with pytest.raises(ttt.TTTError) as ei:
+            ttt.ttt_backward_workspace_bytes(h, ttt.TTT_LOSS_MSE, ttt.TTT_INNER_MLP_GELU)
+        assert ei.value.status == ttt.TTT_ERR_UNSUPPORTED
+    finally:
+        ttt.ttt_destroy(h)
