@@ -179,23 +179,30 @@ def percentile(xs, q):
 
 
 def measure_mfma_peak(torch, blib):
-    """bf16 MFMA throughput of a chip-filling micro-benchmark (TFLOP/s)."""
-    blocks, iters = 8 * 256, 10000
+    """bf16 MFMA throughput of a chip-filling micro-benchmark (TFLOP/s) and the
+    shader clock (MHz) one of its blocks saw."""
+    blocks, iters = 8 * 256, 5000
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
+    args = lambda it: (blocks, it, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clk.data_ptr()),
+                       ctypes.c_void_p(stream))
     for _ in range(2):
-        blib.bench_mfma_peak_launch(blocks, 500, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream))
+        blib.bench_mfma_peak_launch(*args(500))
     torch.cuda.synchronize()
-    best = None
+    best, mhz = None, None
     for _ in range(3):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        blib.bench_mfma_peak_launch(blocks, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream))
+        blib.bench_mfma_peak_launch(*args(iters))
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b)
-        best = ms if best is None else min(best, ms)
-    return blib.bench_mfma_peak_flops(blocks, iters) / (best * 1e-3) / 1e12
+        if best is None or ms < best:
+            best = ms
+            c, r = clk.cpu().tolist()
+            mhz = c * 100.0 / r if r else None
+    return blib.bench_mfma_peak_flops(blocks, iters) / (best * 1e-3) / 1e12, mhz
 
 
 def main():
@@ -329,8 +336,9 @@ def main():
             extras["shader_clock_mhz"] = {"median": percentile(mhz, 0.5), "min": mhz[0], "max": mhz[-1],
                                           "how": "s_memtime / s_memrealtime (100 MHz) of a probe wave "
                                                  "enqueued after each of 30 steps"}
-            peak = measure_mfma_peak(torch, blib)
+            peak, peak_mhz = measure_mfma_peak(torch, blib)
             extras["mfma_bf16_microbench_tflops"] = peak
+            extras["mfma_microbench_clock_mhz"] = peak_mhz
         else:
             extras["note"] = "libttt_bench.so not built: no clock probe or MFMA micro-benchmark"
 

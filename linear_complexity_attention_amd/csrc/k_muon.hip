@@ -18,7 +18,6 @@ namespace ttt {
 namespace {
 
 constexpr float kNsA = 3.4445f, kNsB = -4.7750f, kNsC = 2.0315f;
-constexpr int kT = 32;            // output tile and k-step of the batched GEMM
 
 __device__ __forceinline__ void mat_shape(const Problem& pb, int i, int& rows, int& cols) {
   if (pb.inner == INNER_LINEAR) { rows = pb.d; cols = pb.d; return; }
@@ -37,31 +36,74 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// X0 = M / (||M||_F + 1e-7) in the wide orientation.  grid = (nm, P)
+// sum of squares of slice s (kNormSlice elements) of every (pair, matrix):
+// part[(p nm + i) nsl + s].  grid = (nsl, nm, P)
+constexpr int kNormSlice = 4096;
+__global__ void __launch_bounds__(256) k_ns_norm(Problem pb, const float* __restrict__ mom, unsigned mask, int nsl,
+                                                 float* __restrict__ part) {
+  const int s = blockIdx.x, i = blockIdx.y, p = blockIdx.z;
+  if (!((mask >> i) & 1u)) return;
+  const long long msz = pb.msz;
+  const float* m = mom + ((long long)p * pb.nm + i) * msz;
+  __shared__ float red[4];
+  float ss = 0.f;
+  const long long e1 = min(msz, (long long)(s + 1) * kNormSlice);
+  for (long long e = (long long)s * kNormSlice + threadIdx.x; e < e1; e += blockDim.x) ss += m[e] * m[e];
+  const float t = block_sum(ss, red);
+  if (threadIdx.x == 0) part[((long long)p * pb.nm + i) * nsl + s] = t;
+}
+
+__device__ __forceinline__ float inv_norm(const float* part, int nsl) {
+  float t = 0.f;
+  for (int k = 0; k < nsl; ++k) t += part[k];
+  return 1.0f / (sqrtf(t) + 1e-7f);
+}
+
+// X0 = M / (||M||_F + 1e-7) in the wide orientation, through 32 x 32 LDS
+// tiles so that both the read of M and the (transposed) write of X are
+// row-wise.  grid = (tiles of M, nm, P)
 __global__ void __launch_bounds__(256) k_ns_init(Problem pb, const float* __restrict__ mom, unsigned mask,
-                                                 float* __restrict__ x) {
-  const int i = blockIdx.x, p = blockIdx.y;
+                                                 const float* __restrict__ npart, int nsl, float* __restrict__ x) {
+  const int i = blockIdx.y, p = blockIdx.z;
   if (!((mask >> i) & 1u)) return;
   int rows, cols;
   mat_shape(pb, i, rows, cols);
+  const int tcols = (cols + 31) / 32;
+  const int tr = blockIdx.x / tcols, tc = blockIdx.x % tcols;
+  if (tr * 32 >= rows) return;
   const long long msz = pb.msz;
   const float* m = mom + ((long long)p * pb.nm + i) * msz;
   float* xo = x + ((long long)p * pb.nm + i) * msz;
-  __shared__ float red[4];
-  float ss = 0.f;
-  for (long long e = threadIdx.x; e < msz; e += blockDim.x) ss += m[e] * m[e];
-  const float inv = 1.0f / (sqrtf(block_sum(ss, red)) + 1e-7f);
-  const bool tall = rows > cols;
-  for (long long e = threadIdx.x; e < msz; e += blockDim.x) {
-    const int r = (int)(e / cols), c = (int)(e % cols);
-    xo[tall ? (long long)c * rows + r : e] = m[e] * inv;
+  const float inv = inv_norm(npart + ((long long)p * pb.nm + i) * nsl, nsl);
+  __shared__ float tile[32][33];
+  const int lx = threadIdx.x % 32, ly = threadIdx.x / 32;      // 32 x 8
+  for (int yy = ly; yy < 32; yy += 8) {
+    const int r = tr * 32 + yy, c = tc * 32 + lx;
+    tile[yy][lx] = (r < rows && c < cols) ? m[(long long)r * cols + c] * inv : 0.f;
+  }
+  __syncthreads();
+  if (rows > cols) {            // tall: X[c][r] = M[r][c], written along r
+    for (int yy = ly; yy < 32; yy += 8) {
+      const int c = tc * 32 + yy, r = tr * 32 + lx;
+      if (c < cols && r < rows) xo[(long long)c * rows + r] = tile[lx][yy];
+    }
+  } else {
+    for (int yy = ly; yy < 32; yy += 8) {
+      const int r = tr * 32 + yy, c = tc * 32 + lx;
+      if (r < rows && c < cols) xo[(long long)r * cols + c] = tile[yy][lx];
+    }
   }
 }
 
 // C = alpha * A op(B) + beta * D for every (pair, matrix) in the mask:
 // A [M][K], op(B) = B [K][Nc] or (transB) B^T with B [Nc][K], C, D [M][Nc];
 // all row-major, contiguous, batch entry z = p * nm + i at z * stride.
-// grid = (ceil(Nc / 32), ceil(M / 32), nm * P), 256 threads, 2 x 2 outputs each.
+// 32 x 32 output tiles (so a launch has P * nm * (M/32) * (Nc/32) workgroups)
+// and up to 256 of K staged in LDS at once ([k][row] and [k][col], 72 KB): the
+// workgroup pays one global round trip per 256 of K instead of one per
+// k-step.  Each thread computes a 2 x 2 block from float2 LDS reads.
+// grid = (ceil(Nc / 32), ceil(M / 32), nm * P), 256 threads.
+constexpr int kBT = 32, kBK = 256, kBP = kBT + 4;
 __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int Nc, int K, float alpha,
                                                const float* __restrict__ A, long long sA,
                                                const float* __restrict__ B, long long sB, int transB, float beta,
@@ -69,32 +111,74 @@ __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int
                                                long long sC) {
   const int z = blockIdx.z, i = z % nm;
   if (!((mask >> i) & 1u)) return;
-  const int r0 = blockIdx.y * kT, c0 = blockIdx.x * kT;
+  const int r0 = blockIdx.y * kBT, c0 = blockIdx.x * kBT;
   A += z * sA; B += z * sB; C += z * sC;
   if (D) D += z * sD;
-  __shared__ float As[kT][kT + 1];
-  __shared__ float Bs[kT][kT + 1];   // Bs[k][j]
+  __shared__ __attribute__((aligned(16))) float As[kBK][kBP];   // [k][row]
+  __shared__ __attribute__((aligned(16))) float Bs[kBK][kBP];   // [k][col]
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  for (int k0 = 0; k0 < K; k0 += kT) {
-    for (int t = threadIdx.x; t < kT * kT; t += 256) {
-      const int rr = t / kT, cc = t % kT;
-      // A tile: row r0 + rr, column k0 + cc (coalesced along k)
-      As[rr][cc] = (r0 + rr < M && k0 + cc < K) ? A[(long long)(r0 + rr) * K + k0 + cc] : 0.f;
-      if (transB)   // B [Nc][K]: row c0 + rr, column k0 + cc -> Bs[k][j]
-        Bs[cc][rr] = (c0 + rr < Nc && k0 + cc < K) ? B[(long long)(c0 + rr) * K + k0 + cc] : 0.f;
-      else          // B [K][Nc]: row k0 + rr, column c0 + cc
-        Bs[rr][cc] = (k0 + rr < K && c0 + cc < Nc) ? B[(long long)(k0 + rr) * Nc + c0 + cc] : 0.f;
+  float acc[2][2] = {};
+  // float4 loads need 16-byte aligned rows and batch entries
+  const bool vec = K % 4 == 0 && Nc % 4 == 0 && sA % 4 == 0 && sB % 4 == 0;
+  for (int k0 = 0; k0 < K; k0 += kBK) {
+    const int kc = min(kBK, K - k0);
+    if (vec && kc % 4 == 0) {
+      // float4 loads, all of a thread's loads in flight before the LDS stores:
+      // A (and B^T) rows along k into [k][row], B [K][Nc] rows into [k][col]
+      constexpr int NV = kBT * kBK / 4 / 256;      // float4 per thread and operand (8)
+      const int k4 = kc / 4;
+      float4 av[NV], bv[NV];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int f = threadIdx.x + 256 * u;
+        av[u] = float4{0.f, 0.f, 0.f, 0.f};
+        bv[u] = float4{0.f, 0.f, 0.f, 0.f};
+        if (f < kBT * k4) {
+          const int rr = f / k4, kk = 4 * (f % k4);
+          if (r0 + rr < M) av[u] = *reinterpret_cast<const float4*>(A + (long long)(r0 + rr) * K + k0 + kk);
+          if (transB) {
+            if (c0 + rr < Nc) bv[u] = *reinterpret_cast<const float4*>(B + (long long)(c0 + rr) * K + k0 + kk);
+          } else {
+            const int kr = f / (kBT / 4), cc = 4 * (f % (kBT / 4));
+            if (c0 + cc < Nc) bv[u] = *reinterpret_cast<const float4*>(B + (long long)(k0 + kr) * Nc + c0 + cc);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int f = threadIdx.x + 256 * u;
+        if (f < kBT * k4) {
+          const int rr = f / k4, kk = 4 * (f % k4);
+          As[kk][rr] = av[u].x; As[kk + 1][rr] = av[u].y; As[kk + 2][rr] = av[u].z; As[kk + 3][rr] = av[u].w;
+          if (transB) {
+            Bs[kk][rr] = bv[u].x; Bs[kk + 1][rr] = bv[u].y; Bs[kk + 2][rr] = bv[u].z; Bs[kk + 3][rr] = bv[u].w;
+          } else {
+            const int kr = f / (kBT / 4), cc = 4 * (f % (kBT / 4));
+            *reinterpret_cast<float4*>(&Bs[kr][cc]) = bv[u];
+          }
+        }
+      }
+    } else {
+      for (int t = threadIdx.x; t < kBT * kc; t += 256) {
+        const int rr = t / kc, kk = t % kc;
+        As[kk][rr] = (r0 + rr < M) ? A[(long long)(r0 + rr) * K + k0 + kk] : 0.f;
+        if (transB) Bs[kk][rr] = (c0 + rr < Nc) ? B[(long long)(c0 + rr) * K + k0 + kk] : 0.f;
+      }
+      if (!transB)
+        for (int t = threadIdx.x; t < kBT * kc; t += 256) {
+          const int kr = t / kBT, cc = t % kBT;
+          Bs[kr][cc] = (c0 + cc < Nc) ? B[(long long)(k0 + kr) * Nc + c0 + cc] : 0.f;
+        }
     }
     __syncthreads();
 #pragma unroll 8
-    for (int kk = 0; kk < kT; ++kk) {
-      const float a0 = As[2 * ty][kk], a1 = As[2 * ty + 1][kk];
-      const float b0 = Bs[kk][2 * tx], b1 = Bs[kk][2 * tx + 1];
-      acc[0][0] = fmaf(a0, b0, acc[0][0]);
-      acc[0][1] = fmaf(a0, b1, acc[0][1]);
-      acc[1][0] = fmaf(a1, b0, acc[1][0]);
-      acc[1][1] = fmaf(a1, b1, acc[1][1]);
+    for (int kk = 0; kk < kc; ++kk) {
+      const float2 a = *reinterpret_cast<const float2*>(&As[kk][2 * ty]);
+      const float2 b = *reinterpret_cast<const float2*>(&Bs[kk][2 * tx]);
+      acc[0][0] = fmaf(a.x, b.x, acc[0][0]);
+      acc[0][1] = fmaf(a.x, b.y, acc[0][1]);
+      acc[1][0] = fmaf(a.y, b.x, acc[1][0]);
+      acc[1][1] = fmaf(a.y, b.y, acc[1][1]);
     }
     __syncthreads();
   }
@@ -110,37 +194,60 @@ __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int
     }
 }
 
-// next -= scale * X (back in the [in, out] orientation), W_out if requested.
-// grid = (nm, P)
+// next -= scale * X (back in the [in, out] orientation), W_out if requested;
+// 32 x 32 LDS tiles as in k_ns_init.  grid = (tiles of W, nm, P)
 __global__ void __launch_bounds__(256) k_muon_apply(Problem pb, const float* __restrict__ x, unsigned mask,
                                                     float scale, float* __restrict__ next, float* o0, float* o1,
                                                     float* o2) {
-  const int i = blockIdx.x, p = blockIdx.y;
+  const int i = blockIdx.y, p = blockIdx.z;
   int rows, cols;
   mat_shape(pb, i, rows, cols);
+  const int tcols = (cols + 31) / 32;
+  const int tr = blockIdx.x / tcols, tc = blockIdx.x % tcols;
+  if (tr * 32 >= rows) return;
   const long long msz = pb.msz;
   float* w = next + ((long long)p * pb.nm + i) * msz;
   float* out = i == 0 ? o0 : i == 1 ? o1 : o2;
   if (out) out += pb.row(p) * msz;
   const bool upd = (mask >> i) & 1u;
   const float* xi = x + ((long long)p * pb.nm + i) * msz;
-  const bool tall = rows > cols;
-  for (long long e = threadIdx.x; e < msz; e += blockDim.x) {
-    float v = w[e];
-    if (upd) {
-      const int r = (int)(e / cols), c = (int)(e % cols);
-      v -= scale * xi[tall ? (long long)c * rows + r : e];
-      w[e] = v;
+  __shared__ float tile[32][33];   // the X values of this tile of W, [row][col] of W
+  const int lx = threadIdx.x % 32, ly = threadIdx.x / 32;
+  if (upd) {
+    if (rows > cols) {            // X [cols][rows]: read along r
+      for (int yy = ly; yy < 32; yy += 8) {
+        const int c = tc * 32 + yy, r = tr * 32 + lx;
+        tile[lx][yy] = (c < cols && r < rows) ? xi[(long long)c * rows + r] : 0.f;
+      }
+    } else {
+      for (int yy = ly; yy < 32; yy += 8) {
+        const int r = tr * 32 + yy, c = tc * 32 + lx;
+        tile[yy][lx] = (r < rows && c < cols) ? xi[(long long)r * cols + c] : 0.f;
+      }
     }
-    if (out) out[e] = v;
+  }
+  __syncthreads();
+  for (int yy = ly; yy < 32; yy += 8) {
+    const int r = tr * 32 + yy, c = tc * 32 + lx;
+    if (r < rows && c < cols) {
+      const long long e = (long long)r * cols + c;
+      float v = w[e];
+      if (upd) {
+        v -= scale * tile[yy][lx];
+        w[e] = v;
+      }
+      if (out) out[e] = v;
+    }
   }
 }
 
 }  // namespace
 
+static int norm_slices(const Problem& pb) { return (int)((pb.msz + kNormSlice - 1) / kNormSlice); }
+
 size_t muon_scratch_floats(const Problem& pb) {
   const long long m = pb.inner == INNER_LINEAR ? pb.d : (pb.d < pb.hid ? pb.d : pb.hid);
-  return (size_t)pb.B * pb.H * pb.nm * (2 * pb.msz + 2 * m * m);
+  return (size_t)pb.B * pb.H * pb.nm * (2 * pb.msz + 2 * m * m + norm_slices(pb));
 }
 
 void launch_muon(const Problem& pb, const float* mom, float* next, float* const* out, unsigned mask, float scale,
@@ -153,9 +260,15 @@ void launch_muon(const Problem& pb, const float* mom, float* next, float* const*
   float* xb = xa + (size_t)P * nm * sx;
   float* ga = xb + (size_t)P * nm * sx;
   float* gb = ga + (size_t)P * nm * sg;
-  hipLaunchKernelGGL(k_ns_init, dim3(nm, P), dim3(256), 0, st, pb, mom, mask, xa);
+  float* npart = gb + (size_t)P * nm * sg;
+  const int nsl = norm_slices(pb);
+  // tiles of the largest [in, out] matrix of the model (every matrix is d x h or h x d)
+  const int side_r = pb.inner == INNER_LINEAR ? pb.d : (pb.d > pb.hid ? pb.d : pb.hid);
+  const unsigned wtiles = (unsigned)(((side_r + 31) / 32) * ((side_r + 31) / 32));
+  hipLaunchKernelGGL(k_ns_norm, dim3(nsl, nm, P), dim3(256), 0, st, pb, mom, mask, nsl, npart);
+  hipLaunchKernelGGL(k_ns_init, dim3(wtiles, nm, P), dim3(256), 0, st, pb, mom, mask, (const float*)npart, nsl, xa);
   const unsigned zb = (unsigned)(nm * P);
-  const dim3 gmm((m + kT - 1) / kT, (m + kT - 1) / kT, zb), gmn((n + kT - 1) / kT, (m + kT - 1) / kT, zb);
+  const dim3 gmm((m + kBT - 1) / kBT, (m + kBT - 1) / kBT, zb), gmn((n + kBT - 1) / kBT, (m + kBT - 1) / kBT, zb);
   for (int s = 0; s < ns_steps; ++s) {
     // A = X X^T
     hipLaunchKernelGGL(k_bgemm, gmm, dim3(256), 0, st, nm, mask, m, m, n, 1.0f, xa, sx, xa, sx, 1, 0.0f,
@@ -168,7 +281,8 @@ void launch_muon(const Problem& pb, const float* mom, float* next, float* const*
                        (const float*)xa, sx, xb, sx);
     float* t = xa; xa = xb; xb = t;
   }
-  hipLaunchKernelGGL(k_muon_apply, dim3(nm, P), dim3(256), 0, st, pb, xa, mask, scale, next, out[0], out[1], out[2]);
+  hipLaunchKernelGGL(k_muon_apply, dim3(wtiles, nm, P), dim3(256), 0, st, pb, xa, mask, scale, next, out[0], out[1],
+                     out[2]);
 }
 
 }  // namespace ttt

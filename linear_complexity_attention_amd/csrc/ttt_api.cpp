@@ -119,6 +119,7 @@ struct Plan {
   bool mfma_grad, mfma_query;        // GELU-MLP MFMA kernels
   bool lact_grad, lact_query;        // SwiGLU MFMA kernels
   bool dwconv;                       // depthwise-convolution kernels
+  bool glu_grad, glu_query;          // GLU MFMA kernels
   int S_stats, S_grad;               // S_grad: partial slots of the gradient kernel
   int sk_G, sk_J;                    // stream-K geometry (MFMA gradient kernel)
   // byte offsets
@@ -249,11 +250,18 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
   pl.mfma_query = fast && mfma_query_supported(pb);
   pl.lact_grad = fast && !c.key_norm && lact_supported(pb);
   pl.lact_query = fast && lact_readout_supported(pb);
+  // the GLU kernels address pairs through Problem::row, so they also serve a
+  // head range of the ViT3 split; their readout reads one state (full batch
+  // or write-then-query)
+  pl.glu_grad = !generic_only && glu_supported(pb) && pl.nb == 1 && op.epochs == 1;
+  pl.glu_query = !generic_only && glu_supported(pb) && !op.causal;
   // key-stat slices: at most 4 workgroups per CU in total, so that all of them
   // run in one round (a partial second round would idle most of the chip)
   pl.S_stats = c.key_norm ? stats_splits(pl.P, c.N) : 0;
   if (pl.dwconv) {
     pl.S_grad = dwconv_grad_splits(pb);
+  } else if (pl.glu_grad) {
+    pl.S_grad = glu_grad_splits(pb, pl.span);
   } else if (pl.lact_grad) {
     pl.S_grad = lact_grad_splits(pb, pl.span);
   } else if (pl.mfma_grad) {
@@ -274,7 +282,8 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
   pl.off_part = off;
   off = align256(off + sizeof(float) * (size_t)pl.S_grad * (pl.mfma_grad ? 1 : pl.P) * pl.wsz);
   pl.off_gbuf = off;
-  if (!pl.mfma_grad && !pl.lact_grad && !pl.dwconv) off = align256(off + sizeof(float) * (size_t)pl.P * pl.span * c.d);
+  if (!pl.mfma_grad && !pl.lact_grad && !pl.dwconv && !pl.glu_grad)
+    off = align256(off + sizeof(float) * (size_t)pl.P * pl.span * c.d);
   pl.off_mom = off;
   if (op.rule != RULE_GD) off = align256(off + sizeof(float) * (size_t)pl.P * pl.wsz);
   pl.off_muon = off;
@@ -400,10 +409,13 @@ const char* ttt_path_name_ex(const ttt_handle* hc, int loss, int inner, int chun
   ttt_handle* h = const_cast<ttt_handle*>(hc);
   Opts op;
   if (!h || check_request(h, loss, inner, chunk, opt, &op)) return nullptr;
-  if (inner == TTT_INNER_VIT3) return "dwconv+generic";
   const Layout L = make_layout(h, loss, inner, chunk, op);
+  if (inner == TTT_INNER_VIT3)
+    return L.n > 1 && L.pl[1].glu_grad && L.pl[1].glu_query ? "dwconv+mfma_glu" : "dwconv+generic";
   const Plan& pl = L.pl[0];
   if (pl.dwconv) return "dwconv";
+  if (pl.glu_grad && pl.glu_query) return "mfma_glu";
+  if (pl.glu_query) return "generic_grad+mfma_glu_query";
   if (pl.mfma_grad && pl.mfma_query) return "mfma";
   if (pl.mfma_query) return "generic_grad+mfma_query";
   if (pl.lact_grad && pl.lact_query) return "mfma_swiglu";
@@ -522,6 +534,8 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
       if (first_step) mark(2);
       if (pl.dwconv) {
         launch_dwconv_grad(pb, src, pl.S_grad, part, st);
+      } else if (pl.glu_grad) {
+        launch_glu_grad(pb, src, t0, nt, pl.S_grad, part, st);
       } else if (pl.lact_grad) {
         launch_lact_grad(pb, src, t0, nt, pl.S_grad, cl.eta->scale, part, st);
       } else if (pl.mfma_grad) {
@@ -565,6 +579,8 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
   const int rn = op.causal ? pl.nb : 1;
   if (pl.dwconv) {
     launch_dwconv_query(pb, rstates, st);
+  } else if (pl.glu_query) {
+    launch_glu_query(pb, rstates, st);
   } else if (pl.mfma_query) {
     launch_mfma_query(pb, w0, rstates, pl.state_stride, rn, rchunk, st);
   } else if (pl.lact_query) {
@@ -615,8 +631,12 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
                    c.B, c.H, L.r[i].h0, L.r[i].h0 + L.r[i].hc - 1, c.N, c.d, pl.hid, c.dtype == TTT_BF16 ? "bf16" : "f32",
                    L.r[i].model, loss, chunk, pl.nb, op.epochs, range_mask(op.mask, L.r[i]),
                    op.causal ? "causal" : "write-then-query", op.rule,
-                   pl.dwconv ? "dwconv" : pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu" : "generic", pl.S_grad,
-                   pl.dwconv ? "dwconv" : pl.mfma_query ? "mfma" : pl.lact_query ? "mfma_swiglu" : "generic", L.total);
+                   pl.dwconv ? "dwconv" : pl.glu_grad ? "mfma_glu" : pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu"
+                                                                                                          : "generic",
+                   pl.S_grad,
+                   pl.dwconv ? "dwconv" : pl.glu_query ? "mfma_glu" : pl.mfma_query ? "mfma" : pl.lact_query ? "mfma_swiglu"
+                                                                                                             : "generic",
+                   L.total);
     }
 
   // hipGetLastError is per thread and sticky: drop an error some earlier,

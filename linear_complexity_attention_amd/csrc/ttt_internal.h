@@ -168,6 +168,14 @@ size_t muon_scratch_floats(const Problem& pb);
 void launch_muon(const Problem& pb, const float* mom, float* next, float* const* out, unsigned mask, float scale,
                  int ns_steps, float* scratch, hipStream_t st);
 
+// ---- simplified GLU on bf16 MFMA (d = 64, bf16 tensors) ----------------------
+// partials part[S][P][2][d*d] of the update batch [t0, t0 + nt); readout from
+// the state (layout [P][2][d*d]); head ranges via Problem::row
+bool glu_supported(const Problem& pb);
+int glu_grad_splits(const Problem& pb, int nt);
+void launch_glu_grad(const Problem& pb, const WRef& W, int t0, int nt, int S, float* part, hipStream_t st);
+void launch_glu_query(const Problem& pb, const float* state, hipStream_t st);
+
 // ---- depthwise-convolution inner model (full batch) --------------------------
 // partial dw over S token splits -> part[S][P][1][d*ck*ck]; readout from the
 // state at `state` (layout [P][d*ck*ck])

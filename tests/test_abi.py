@@ -149,8 +149,10 @@ def test_convolution_requests_validated_on_host():
         return ttt.TTTLayer(1, 2, 100, 64, 64, **args)
 
     assert layer().workspace_bytes("dot", "dwconv", 0) > 0
-    assert layer().path_name("dot", "vit3", 0) == "dwconv+generic"
-    assert layer().path_name("dot", "glu", 0) == "generic"
+    assert layer().path_name("dot", "vit3", 0) == "dwconv+mfma_glu"
+    assert layer().path_name("dot", "glu", 0) == "mfma_glu"
+    assert layer(dtype="f32").path_name("dot", "glu", 0) == "generic"
+    assert layer(flags=ttt.TTT_FLAG_FORCE_GENERIC).path_name("dot", "vit3", 0) == "dwconv+generic"
     for lay, inner, chunk, opt, code in [
         (layer(grid=(10, 9)), "dwconv", 0, None, ttt.TTT_ERR_INVALID),
         (layer(conv_k=4), "dwconv", 0, None, ttt.TTT_ERR_UNSUPPORTED),

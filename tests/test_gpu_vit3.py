@@ -13,13 +13,13 @@ from tests.gpu_common import TOL, device_inputs, rel_err, run_gpu, run_oracle
 pytestmark = pytest.mark.gpu
 
 
-def _check(w, *, opts=None, okw=None, path=None):
+def _check(w, *, opts=None, okw=None, path=None, flags=0):
     from linear_complexity_attention_amd import ttt
     from oracle import ttt_oracle as orc
 
     options = ttt.make_options(**opts) if opts else None
     dev_in, exact = device_inputs(w)
-    O, W_out, got = run_gpu(w, dev_in, options=options)
+    O, W_out, got = run_gpu(w, dev_in, options=options, flags=flags)
     O_ref, W_ref = run_oracle(w, exact, okw=okw)
     tol = TOL[w.dtype]
     tag = f"{w.name} {w.inner} {w.dtype} {w.loss} kn={w.key_norm} grid={w.grid} k={w.conv_k} path={got}"
@@ -42,7 +42,18 @@ def _check(w, *, opts=None, okw=None, path=None):
 def test_glu(dtype, loss, key_norm, d):
     w = Workload("glu", B=2, H=3, N=333, d=d, hidden=d, dtype=dtype, inner="glu", loss=loss, key_norm=key_norm,
                  per_token_eta=loss == "dot", eta=1.0 if loss == "mse" else 0.01, seed=601 + d)
-    _check(w, path="generic")
+    # bf16 at d = 64 takes the MFMA GLU kernels, everything else the generic ones
+    _check(w, path="mfma_glu" if dtype == "bf16" and d == 64 else "generic")
+
+
+@pytest.mark.parametrize("loss", ["dot", "mse"])
+def test_glu_generic_forced_and_mfma_ragged(loss):
+    """The generic GLU kernels on bf16 tensors (forced), and the MFMA ones on a
+    ragged token count that leaves a partial last tile in several splits."""
+    w = Workload("glu2", B=3, H=2, N=1001, d=64, hidden=64, inner="glu", loss=loss, key_norm=True,
+                 per_token_eta=True, eta=1.0 if loss == "mse" else 0.003, seed=650)
+    _check(w, path="generic", flags=0x2)
+    _check(w, path="mfma_glu")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -66,7 +77,7 @@ def test_dwconv(dtype, k, grid, d, loss, key_norm):
 def test_vit3_block(dtype, H, loss):
     w = Workload("vit3", B=2, H=H, N=196, d=64, hidden=64, dtype=dtype, inner="vit3", loss=loss, key_norm=True,
                  eta=1.0 / 196 if loss == "dot" else 1.0, grid=(14, 14), conv_k=3, seed=800 + H)
-    _check(w, path="dwconv+generic")
+    _check(w, path="dwconv+mfma_glu" if dtype == "bf16" and H > 1 else "dwconv+generic")
 
 
 def test_dwconv_with_epochs_and_momentum():
