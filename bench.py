@@ -274,7 +274,8 @@ def main():
     timed_events = mode == "forward"
     ev_grad = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)] if timed_events else []
-    nburst = max(1, args.steps // args.burst)
+    burst = max(1, min(args.burst, args.steps))
+    nburst = args.steps // burst
     ev_burst = [torch.cuda.Event(enable_timing=True) for _ in range(nburst + 1)]
     for a, b in ev_grad:
         a.record(stream)
@@ -287,13 +288,13 @@ def main():
             a, b = ev_grad[i]
             ttt.ttt_set_timing_events(layer.handle, [None, None, a.cuda_event, b.cuda_event, None, None, None, None])
         step()
-        if (i + 1) % args.burst == 0 and (i + 1) // args.burst <= nburst:
-            ev_burst[(i + 1) // args.burst].record(stream)
+        if (i + 1) % burst == 0 and (i + 1) // burst <= nburst:
+            ev_burst[(i + 1) // burst].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ttt.ttt_set_timing_events(layer.handle, None)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    per_step = [ev_burst[j].elapsed_time(ev_burst[j + 1]) / args.burst for j in range(nburst)]
+    per_step = [ev_burst[j].elapsed_time(ev_burst[j + 1]) / burst for j in range(nburst)]
     grad_ms = sum(a.elapsed_time(b) for a, b in ev_grad) / len(ev_grad) if ev_grad else None
 
     # Per-family breakdown, outside the timed region: all four families timed
@@ -395,7 +396,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.N, "heads": w.H, "head_dim": w.d, "hidden": w.hidden,
                    "path": path},
         "step_ms": {"median": percentile(per_step, 0.5), "p10": percentile(per_step, 0.1),
-                    "p90": percentile(per_step, 0.9), "bursts": nburst, "steps_per_burst": args.burst},
+                    "p90": percentile(per_step, 0.9), "bursts": nburst, "steps_per_burst": burst},
         "layer_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
         "frac_of_bf16_peak": layer_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "kernel_ms": kern_ms,
