@@ -228,7 +228,13 @@ int ttt_workspace_bytes(const ttt_handle* h, int loss, int inner, int chunk, siz
  *   W_out     optional final weights; workspace/ws_bytes: device scratch of at
  *             least ttt_workspace_bytes(...) bytes, 256-byte aligned.
  * q/k/v/o/W0 must not alias o or the workspace.  Returns TTT_OK once the work
- * is enqueued (or, with TTT_FLAG_CHECK_FINITE, once it has finished). */
+ * is enqueued (or, with TTT_FLAG_CHECK_FINITE, once it has finished).
+ * Range of the fast path: the GELU-MLP MFMA kernels (bf16 tensors, d = 64)
+ * carry the activations, the loss gradient and dZ in f16.  If |V - F(K)|, |V|
+ * or a pre-activation exceeds about 4e4, those values overflow and O and the
+ * final weights can hold Inf or NaN while the call still returns TTT_OK.
+ * Set TTT_FLAG_CHECK_FINITE to have such a result reported as
+ * TTT_ERR_NONFINITE, or TTT_FLAG_FORCE_GENERIC to compute it in fp32. */
 int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v,
                 const ttt_weights* W0, const ttt_eta* eta, int loss, int inner, int chunk,
                 void* o, const ttt_weights_out* W_out, void* workspace, size_t ws_bytes,
