@@ -49,7 +49,7 @@ VARIANTS = {
     "c5_lact_video_mask": ("c5_lact_swiglu", dict(chunk_update=[1, 0] * 8), "forward", "mfma"),
     "c3_first_layer_only": ("c3_hires_r4", dict(update_mask=1), "forward", "mfma"),
     "c3_epochs3": ("c3_hires_r4", dict(epochs=3), "forward", "alu"),
-    "vit3_hires": ("vit3_hires", None, "forward", "alu"),
+    "vit3_hires": ("vit3_hires", None, "forward", "mfma"),
     "c3_outer_backward": ("c3_hires_r4", None, "backward", "alu"),
 }
 
@@ -365,7 +365,7 @@ def main():
         grad_flops = P * gemm_flops(w, first_tokens)[0]
         if w.inner == "vit3":
             grad_flops = w.B * (w.H - 1) * gemm_flops(w, first_tokens)[0]
-            kname = "GLU gradient kernels (11 of 12 heads; generic fp32)"
+            kname = f"GLU gradient (k_glu_grad, MFMA bf16), heads 1..{w.H - 1} of the block"
         if bound == "hbm":
             nbytes = P * first_tokens * w.d * 2 * (2 if w.dtype == "bf16" else 4)   # K and V once
             achieved = nbytes / (grad_ms * 1e-3) / 1e9

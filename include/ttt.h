@@ -30,7 +30,8 @@
  *   - A handle holds host state only.  One handle must not be used by two
  *     threads at the same time; calls on one handle are ordered by the caller.
  *   - Dense row-major layouts, no padding between rows:
- *       q, k, v, o     [B, H, N, d]       dtype of the config (fp32 or bf16)
+ *       q, k, v, o     [B, H, N, d]       dtype of the config (fp32 or bf16),
+ *                                         16-byte aligned (TTT_ERR_INVALID if not)
  *       weights        [in, out] per matrix, fp32 (see ttt_weights)
  *       per-token eta  [B, H, N]          fp32
  */
@@ -264,6 +265,7 @@ const char* ttt_path_name_ex(const ttt_handle* h, int loss, int inner, int chunk
  *   q, k, v, W0, eta, loss, inner: as for ttt_forward
  *   dO          [B, H, N, d] in the config's dtype
  *   dq, dk, dv  [B, H, N, d] fp32 outputs
+ *               (q, k, v, dO, dq, dk, dv 16-byte aligned, else TTT_ERR_INVALID)
  *   dW0         fp32 outputs in W0's layout: [H, in, out] summed over the batch
  *               when W0.batch_stride == 0, else [B, H, in, out]; NULL entries
  *               (or a NULL struct) are skipped

@@ -22,8 +22,10 @@ namespace ttt {
 
 namespace {
 
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
 constexpr int D = 64;
-constexpr int TT = 32;               // tokens per tile
+constexpr int TT = 64;               // tokens per tile
 constexpr int NW = 4;                // waves: 16 hidden units each
 constexpr int LX = D + 8;            // [token][channel] row stride (bf16)
 constexpr int LT = TT + 8;           // [channel|unit][token] row stride (bf16)
@@ -43,8 +45,28 @@ __device__ __forceinline__ void load_wfrag(const float* W, int jb, int r, int g,
     for (int e = 0; e < 8; ++e) f[ks][e] = (bf16)W[(32 * ks + 8 * g + e) * D + 16 * jb + r];
 }
 
-// partial dW1, dW2 of token split blockIdx.x of pair blockIdx.y
-__global__ void __launch_bounds__(NW * 64) k_glu_grad(Problem pb, WRef W, int t0, int nt, int S,
+// Staging map: thread t moves channels 8 (t % 8) .. + 7 of the adjacent tile
+// tokens 2 (t / 8) and 2 (t / 8) + 1 (two 16-byte loads per tensor; a wave's
+// loads cover whole 128-byte token rows).
+//
+// X^T is kept in LDS as [channel][token] rows whose 8-token groups are
+// permuted per row: group G of channel c sits at group G ^ swz(c),
+// swz(c) = (c / 8) & 6.  Then both the packed two-token stores of the staging
+// map and the 16-byte MFMA operand reads (16 channels, one group) fall on 64
+// distinct LDS banks.
+__device__ __forceinline__ int xt_col(int c, int t) { return ((((t >> 3) ^ ((c >> 3) & 6))) << 3) | (t & 7); }
+
+struct TileRegs {
+  bf16x8 x[2], v[2];
+  float e;
+};
+
+// partial dW1, dW2 of token split blockIdx.x of pair blockIdx.y (tiles
+// [s T / S, (s + 1) T / S) of the T tiles).  The K, V and eta of the next two
+// tiles are loaded into registers while the current tile is computed, so each
+// workgroup keeps two tiles (32 KiB) of loads in flight.  Three workgroups
+// per CU (LDS); the register budget is held to three waves per SIMD to match.
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) k_glu_grad(Problem pb, WRef W, int t0, int nt, int S,
                                                       float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) bf16 Xs[TT * LX];     // [token][channel]
   __shared__ __attribute__((aligned(16))) bf16 Xt[D * LT];      // [channel][token]
@@ -65,41 +87,63 @@ __global__ void __launch_bounds__(NW * 64) k_glu_grad(Problem pb, WRef W, int t0
   bf16x8 w1f[2], w2f[2];
   load_wfrag(W.mat(0, b, h), w, r, g, w1f);
   load_wfrag(W.mat(1, b, h), w, r, g, w2f);
-  // staging: thread -> (token st, channels 8 sc8 .. 8 sc8 + 7)
-  const int st = tid >> 3, sc = (tid & 7) * 8;
-  float mu[8], rs[8];
+  const int st = 2 * (tid >> 3), sc = (tid & 7) * 8;
+  // key statistics (mean, rstd), channel c at [c % 8][c / 8] so that the
+  // eight channel groups of a wave read eight consecutive entries
+  __shared__ float2 nrm[D];
+  if (tid < D)
+    nrm[(tid & 7) * 8 + (tid >> 3)] =
+        pb.stats ? reinterpret_cast<const float2*>(pb.stats)[(size_t)p * D + tid] : float2{0.f, 1.f};
+  auto fetch = [&](int kt, TileRegs& t) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    mu[e] = pb.stats ? pb.stats[((size_t)p * D + sc + e) * 2] : 0.f;
-    rs[e] = pb.stats ? pb.stats[((size_t)p * D + sc + e) * 2 + 1] : 1.f;
-  }
+    for (int q = 0; q < 2; ++q) {
+      const int n = kt * TT + st + q;
+      if (n < nt) {
+        t.x[q] = *reinterpret_cast<const bf16x8*>(kp + (long long)n * D + sc);
+        t.v[q] = *reinterpret_cast<const bf16x8*>(vp + (long long)n * D + sc);
+      } else {
+        t.x[q] = bf16x8{};
+        t.v[q] = bf16x8{};
+      }
+    }
+    const int n = kt * TT + tid;
+    t.e = tid < TT && n < nt ? pb.eta_scale * (ep ? ep[n] : 1.f) : 0.f;
+  };
   f32x4 a1[4], a2[4];   // dW1, dW2 blocks [channel block cb][unit block w]
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) { a1[cb] = f32x4{0, 0, 0, 0}; a2[cb] = f32x4{0, 0, 0, 0}; }
   const int tiles = (nt + TT - 1) / TT;
-  const int per = (tiles + S - 1) / S;
-  const int k0 = s * per, k1 = min(tiles, k0 + per);
-  for (int kt = k0; kt < k1; ++kt) {
-    const int n = kt * TT + st;
-    bf16x8 xv = {}, vv = {};
-    if (n < nt) {
-      xv = *reinterpret_cast<const bf16x8*>(kp + (long long)n * D + sc);
-      vv = *reinterpret_cast<const bf16x8*>(vp + (long long)n * D + sc);
-      if (pb.stats) {
+  const int k0 = (int)((long long)s * tiles / S), k1 = (int)((long long)(s + 1) * tiles / S);
+  // one tile: its registers -> LDS, refill them with tile kt + 2, compute
+  auto step = [&](int kt, TileRegs& cur) {
+    __syncthreads();                                   // the previous tile's LDS reads are done
+    bf16x8 xv[2] = {cur.x[0], cur.x[1]};
+    if (pb.stats) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] = (bf16)(((float)xv[e] - mu[e]) * rs[e]);
+      for (int e = 0; e < 8; ++e) {
+        const float2 m = nrm[e * 8 + (sc >> 3)];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) xv[q][e] = (bf16)(((float)xv[q][e] - m.x) * m.y);
       }
     }
-    __syncthreads();                                   // the previous tile's reads are done
-    *reinterpret_cast<bf16x8*>(&Xs[st * LX + sc]) = xv;
-    *reinterpret_cast<bf16x8*>(&Vs[st * LX + sc]) = vv;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) Xt[(sc + e) * LT + st] = xv[e];
-    if (tid < TT) es[tid] = kt * TT + tid < nt ? pb.eta_scale * (ep ? ep[kt * TT + tid] : 1.f) : 0.f;
+    for (int q = 0; q < 2; ++q) {
+      *reinterpret_cast<bf16x8*>(&Xs[(st + q) * LX + sc]) = xv[q];
+      *reinterpret_cast<bf16x8*>(&Vs[(st + q) * LX + sc]) = cur.v[q];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bf16x2 pr;
+      pr[0] = xv[0][e];
+      pr[1] = xv[1][e];
+      *reinterpret_cast<bf16x2*>(&Xt[(sc + e) * LT + xt_col(sc + e, st)]) = pr;
+    }
+    if (tid < TT) es[tid] = cur.e;
+    if (kt + 2 < k1) fetch(kt + 2, cur);
     __syncthreads();
-    // U, Z of (16 tokens x this wave's 16 units), two token blocks
+    // U, Z of (16 tokens x this wave's 16 units), four token blocks
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int tb = 0; tb < TT / 16; ++tb) {
       f32x4 u = {0, 0, 0, 0}, z = {0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -122,15 +166,27 @@ __global__ void __launch_bounds__(NW * 64) k_glu_grad(Problem pb, WRef W, int t0
       *reinterpret_cast<bf16x4*>(&dZs[(16 * w + r) * LT + 16 * tb + 4 * g]) = dz;
     }
     __syncthreads();
-    // dW1 += X^T dU, dW2 += X^T dZ for (channel block cb, unit block w), k = 32 tokens
-    const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&dUs[(16 * w + r) * LT + 8 * g]);
-    const bf16x8 bz = *reinterpret_cast<const bf16x8*>(&dZs[(16 * w + r) * LT + 8 * g]);
+    // dW1 += X^T dU, dW2 += X^T dZ for (channel block cb, unit block w), 32 tokens per product
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&Xt[(16 * cb + r) * LT + 8 * g]);
-      a1[cb] = mfma16(xa, bu, a1[cb]);
-      a2[cb] = mfma16(xa, bz, a2[cb]);
+    for (int kk = 0; kk < TT / 32; ++kk) {
+      const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&dUs[(16 * w + r) * LT + 32 * kk + 8 * g]);
+      const bf16x8 bz = *reinterpret_cast<const bf16x8*>(&dZs[(16 * w + r) * LT + 32 * kk + 8 * g]);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int c = 16 * cb + r;
+        const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&Xt[c * LT + xt_col(c, 32 * kk + 8 * g)]);
+        a1[cb] = mfma16(xa, bu, a1[cb]);
+        a2[cb] = mfma16(xa, bz, a2[cb]);
+      }
     }
+  };
+  // two tiles of loads in flight: ra and rb alternate
+  TileRegs ra, rb;
+  if (k0 < k1) fetch(k0, ra);
+  if (k0 + 1 < k1) fetch(k0 + 1, rb);
+  for (int kt = k0; kt < k1; kt += 2) {
+    step(kt, ra);
+    if (kt + 1 < k1) step(kt + 1, rb);
   }
   // lane holds dW[c = 16 cb + 4 g + i][j = 16 w + r]
   float* o = part + ((long long)s * pb.B * pb.H + p) * 2 * D * D;
@@ -144,13 +200,15 @@ __global__ void __launch_bounds__(NW * 64) k_glu_grad(Problem pb, WRef W, int t0
     }
 }
 
-// O = (Q W1*) * silu(Q W2*) for 128 tokens of pair blockIdx.y from the
-// state (layout [P][2][d*d]); O is staged in LDS for row-wise stores
-constexpr int kQTiles = 4;
-__global__ void __launch_bounds__(NW * 64) k_glu_query(Problem pb, const float* __restrict__ state) {
+// O = (Q W1*) * silu(Q W2*) for tiles [s T / S, (s + 1) T / S) of pair
+// blockIdx.y from the state (layout [P][2][d*d]).  Q of the next two tiles
+// is loaded while the current one is computed; O is staged in LDS for
+// row-wise 16-byte stores.  Registers are held to eight waves per SIMD, so
+// eight workgroups fit a CU (LDS 18 KiB each) and the grid is one round.
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(8, 8))) k_glu_query(Problem pb, const float* __restrict__ state, int S) {
   __shared__ __attribute__((aligned(16))) bf16 Qs[TT * LX];
   __shared__ __attribute__((aligned(16))) bf16 Os[TT * LX];
-  const int p = blockIdx.y;
+  const int s = blockIdx.x, p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const long long prow = pb.row(p);
@@ -161,26 +219,51 @@ __global__ void __launch_bounds__(NW * 64) k_glu_query(Problem pb, const float* 
   load_wfrag(Ws, w, r, g, w1f);
   load_wfrag(Ws + D * D, w, r, g, w2f);
   const int st = tid >> 3, sc = (tid & 7) * 8;
-  for (int kt = blockIdx.x * kQTiles; kt < min((pb.N + TT - 1) / TT, (blockIdx.x + 1) * kQTiles); ++kt) {
-    const int n = kt * TT + st;
-    const bf16x8 qv = n < pb.N ? *reinterpret_cast<const bf16x8*>(qp + (long long)n * D + sc) : bf16x8{};
-    __syncthreads();
-    *reinterpret_cast<bf16x8*>(&Qs[st * LX + sc]) = qv;
+  struct QRegs { bf16x8 q[2]; };
+  auto fetch = [&](int kt, QRegs& t) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int n = kt * TT + st + 32 * q;
+      t.q[q] = n < pb.N ? *reinterpret_cast<const bf16x8*>(qp + (long long)n * D + sc) : bf16x8{};
+    }
+  };
+  const int tiles = (pb.N + TT - 1) / TT;
+  const int k0 = (int)((long long)s * tiles / S), k1 = (int)((long long)(s + 1) * tiles / S);
+  auto step = [&](int kt, QRegs& cur) {
+    __syncthreads();                                   // Qs and Os of the previous tile are consumed
+#pragma unroll
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<bf16x8*>(&Qs[(st + 32 * q) * LX + sc]) = cur.q[q];
+    if (kt + 2 < k1) fetch(kt + 2, cur);
     __syncthreads();
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int tb = 0; tb < TT / 16; ++tb) {
       f32x4 u = {0, 0, 0, 0}, z = {0, 0, 0, 0};
+      // U^T = W1^T Q^T: the lane holds units 16 w + 4 g .. + 3 of token 16 tb + r
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[(16 * tb + r) * LX + 32 * ks + 8 * g]);
-        u = mfma16(qa, w1f[ks], u);
-        z = mfma16(qa, w2f[ks], z);
+        u = mfma16(w1f[ks], qa, u);
+        z = mfma16(w2f[ks], qa, z);
       }
+      bf16x4 ov;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Os[(16 * tb + 4 * g + i) * LX + 16 * w + r] = (bf16)(u[i] * z[i] * sigm(z[i]));
+      for (int i = 0; i < 4; ++i) ov[i] = (bf16)(u[i] * z[i] * sigm(z[i]));
+      *reinterpret_cast<bf16x4*>(&Os[(16 * tb + r) * LX + 16 * w + 4 * g]) = ov;
     }
     __syncthreads();
-    if (n < pb.N) *reinterpret_cast<bf16x8*>(op + (long long)n * D + sc) = *reinterpret_cast<const bf16x8*>(&Os[st * LX + sc]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int n = kt * TT + st + 32 * q;
+      if (n < pb.N)
+        *reinterpret_cast<bf16x8*>(op + (long long)n * D + sc) = *reinterpret_cast<const bf16x8*>(&Os[(st + 32 * q) * LX + sc]);
+    }
+  };
+  QRegs ra, rb;
+  if (k0 < k1) fetch(k0, ra);
+  if (k0 + 1 < k1) fetch(k0 + 1, rb);
+  for (int kt = k0; kt < k1; kt += 2) {
+    step(kt, ra);
+    if (kt + 1 < k1) step(kt + 1, rb);
   }
 }
 
@@ -188,11 +271,14 @@ __global__ void __launch_bounds__(NW * 64) k_glu_query(Problem pb, const float* 
 
 bool glu_supported(const Problem& pb) { return pb.bf16 && pb.inner == INNER_GLU && pb.d == D; }
 
+// token splits per pair: one round of workgroups over the chip (the LDS of
+// the gradient kernel, about 46 KiB, fits three per CU), at least two tiles
+// per split so that the prefetch overlaps
 int glu_grad_splits(const Problem& pb, int nt) {
   const long long P = (long long)pb.B * pb.H;
-  long long s = (4LL * device_cu_count() + P - 1) / P;
+  long long s = 3LL * device_cu_count() / P;
   const long long tiles = (nt + TT - 1) / TT;
-  const long long maxs = (tiles + 3) / 4;         // at least 4 tiles per split
+  const long long maxs = (tiles + 1) / 2;
   if (s > maxs) s = maxs;
   if (s < 1) s = 1;
   return (int)s;
@@ -202,10 +288,15 @@ void launch_glu_grad(const Problem& pb, const WRef& W, int t0, int nt, int S, fl
   hipLaunchKernelGGL(k_glu_grad, dim3(S, pb.B * pb.H), dim3(NW * 64), 0, st, pb, W, t0, nt, S, part);
 }
 
+// one round of readout workgroups over the chip (eight per CU), each over a
+// balanced range of at least two tiles of its pair
 void launch_glu_query(const Problem& pb, const float* state, hipStream_t st) {
-  const int tiles = (pb.N + TT - 1) / TT;
-  hipLaunchKernelGGL(k_glu_query, dim3((tiles + kQTiles - 1) / kQTiles, pb.B * pb.H), dim3(NW * 64), 0, st, pb,
-                     state);
+  const long long P = (long long)pb.B * pb.H;
+  const long long tiles = (pb.N + TT - 1) / TT;
+  long long S = 8LL * device_cu_count() / P;
+  if (S > (tiles + 1) / 2) S = (tiles + 1) / 2;
+  if (S < 1) S = 1;
+  hipLaunchKernelGGL(k_glu_query, dim3((unsigned)S, (unsigned)P), dim3(NW * 64), 0, st, pb, state, (int)S);
 }
 
 }  // namespace ttt

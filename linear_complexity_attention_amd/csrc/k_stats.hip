@@ -132,26 +132,39 @@ __global__ void __launch_bounds__(kThreads) k_stats_partial_scalar(const T* __re
   }
 }
 
-// Chan et al.'s pairwise combination, applied slice by slice in a fixed order.
-__global__ void k_stats_final(const float* __restrict__ part, int P, int S, int d, float eps,
-                              float* __restrict__ stats) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= P * d) return;
-  const int p = i / d, c = i % d;
+// Chan et al.'s pairwise combination of (count, mean, M2) statistics, in
+// double precision: (n, mean, m2) absorbs (nb, mb, m2b); empty parts are skipped.
+__device__ __forceinline__ void chan_d(double& n, double& mean, double& m2, double nb, double mb, double m2b) {
+  if (nb == 0.0) return;
+  const double nt = n + nb, delta = mb - mean;
+  mean += delta * nb / nt;
+  m2 += m2b + delta * delta * n * nb / nt;
+  n = nt;
+}
+
+// One wave per (pair, channel): lane l merges slices l, l + 64, ... in order,
+// then the 64 lane results are merged by a fixed butterfly (xor 32, 16, ..., 1),
+// so the result is the same on every run.  stats[p][c] = (mean, rstd).
+__global__ void __launch_bounds__(256) k_stats_final(const float* __restrict__ part, int P, int S, int d, float eps,
+                                                     float* __restrict__ stats) {
+  const int wv = (blockIdx.x * blockDim.x + threadIdx.x) >> 6, lane = threadIdx.x & 63;
+  if (wv >= P * d) return;
+  const int p = wv / d, c = wv % d;
   double n = 0.0, mean = 0.0, m2 = 0.0;
-  for (int s = 0; s < S; ++s) {
+  for (int s = lane; s < S; s += 64) {
     const float* o = part + ((size_t)p * S + s) * 3 * d;
-    const double nb = o[c];
-    if (nb == 0.0) continue;
-    const double mb = o[d + c], m2b = o[2 * d + c];
-    const double nt = n + nb, delta = mb - mean;
-    mean += delta * nb / nt;
-    m2 += m2b + delta * delta * n * nb / nt;
-    n = nt;
+    chan_d(n, mean, m2, o[c], o[d + c], o[2 * d + c]);
   }
-  const double var = n > 0.0 ? m2 / n : 0.0;
-  stats[(size_t)i * 2] = (float)mean;
-  stats[(size_t)i * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double nb = __shfl_xor(n, off), mb = __shfl_xor(mean, off), m2b = __shfl_xor(m2, off);
+    chan_d(n, mean, m2, nb, mb, m2b);
+  }
+  if (lane == 0) {
+    const double var = n > 0.0 ? m2 / n : 0.0;
+    stats[(size_t)wv * 2] = (float)mean;
+    stats[(size_t)wv * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
+  }
 }
 
 }  // namespace
@@ -175,7 +188,7 @@ void launch_stats_partial(const Problem& pb, int S, float* part, hipStream_t st)
 void launch_stats_final(const Problem& pb, int S, const float* part, float eps, float* stats, hipStream_t st) {
   const int P = pb.B * pb.H;
   const int n = P * pb.d;
-  hipLaunchKernelGGL(k_stats_final, dim3((n + 255) / 256), dim3(256), 0, st, part, P, S, pb.d, eps, stats);
+  hipLaunchKernelGGL(k_stats_final, dim3((n + 3) / 4), dim3(256), 0, st, part, P, S, pb.d, eps, stats);
 }
 
 }  // namespace ttt

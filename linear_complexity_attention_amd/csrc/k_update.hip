@@ -42,50 +42,59 @@ __device__ __forceinline__ void mat_dims(const Problem& pb, int i, int& rows, in
   else { rows = pb.d; cols = pb.hid; }          // W1, W3 [d, h]
 }
 
-// No re-norm: every element is independent.  grid = (chunks of 1024 elements
-// of one pair's [nm][msz] block, P); each thread updates 4 consecutive floats.
+// No re-norm: every element is independent.  grid = (blocks of 64 float4s of
+// one pair's [nm][msz] block, P), 256 threads: lane l owns float4 64 x + l;
+// wave w sums the splits [w S / 4, (w + 1) S / 4) in split order with eight
+// loads in flight, and wave 0 adds the four wave sums in wave order and
+// applies the rule.
 __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
   const int p = blockIdx.y;
   const int b = p / pb.H, h = p % pb.H;
   const long long wsz = (long long)pb.nm * pb.msz;
-  const long long e = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= wsz) return;
-  const int i = (int)(e / pb.msz);
-  const long long o = e - (long long)i * pb.msz;           // offset inside matrix i (msz % 4 == 0)
-  const float4 wc = *reinterpret_cast<const float4*>(a.cur.mat(i, b, h) + o);
-  float4 w = wc;
-  const bool upd = (a.mask >> i) & 1u;
-  const bool gd = a.rule == RULE_GD;
-  // gradient descent subtracts the partials one by one; the momentum rules sum
-  // them first (same order) and fold the sum into M
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long long e = ((long long)blockIdx.x * 64 + lane) * 4;
+  const bool in = e < wsz;
+  const int i = in ? (int)(e / pb.msz) : 0;
+  const bool upd = in && ((a.mask >> i) & 1u);
   float4 g = {0.f, 0.f, 0.f, 0.f};
-  auto take = [&](const float4& d) {
-    if (gd) { w.x -= d.x; w.y -= d.y; w.z -= d.z; w.w -= d.w; }
-    else { g.x += d.x; g.y += d.y; g.z += d.z; g.w += d.w; }
-  };
-  if (!upd) {
-  } else if (a.part_mode == PART_SPLITS) {    // four splits' loads in flight, taken in split order
-    const float* pp = a.part + (size_t)p * wsz;
-    for (int s = 0; s < a.S; s += 4) {
-      float4 d[4];
+  auto take = [&](const float4& d) { g.x += d.x; g.y += d.y; g.z += d.z; g.w += d.w; };
+  if (upd && a.part_mode == PART_SPLITS) {
+    const float* pp = a.part + (size_t)p * wsz + e;
+    const int s0 = (int)((long long)wv * a.S / 4), s1 = (int)((long long)(wv + 1) * a.S / 4);
+    for (int s = s0; s < s1; s += 8) {
+      float4 d[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (s + u < a.S) d[u] = *reinterpret_cast<const float4*>(pp + (s + u) * a.part_pair_stride + e);
+      for (int u = 0; u < 8; ++u)
+        if (s + u < s1) d[u] = *reinterpret_cast<const float4*>(pp + (s + u) * a.part_pair_stride);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (s + u < a.S) take(d[u]);
+      for (int u = 0; u < 8; ++u)
+        if (s + u < s1) take(d[u]);
     }
-  } else {
+  } else if (upd && wv == 0) {
     long long q0, q1, C;
     sk_range(a, pb.B * pb.H, p, q0, q1, C);
     for (long long q = q0; q <= q1; ++q) take(*reinterpret_cast<const float4*>(a.part + slot_of(a, p, q, q0, C) * wsz + e));
   }
-  if (upd && !gd) {
-    float4* mp = reinterpret_cast<float4*>(a.mom + (size_t)p * wsz + e);
-    float4 m = *mp;
-    m.x = a.beta * m.x + g.x; m.y = a.beta * m.y + g.y; m.z = a.beta * m.z + g.z; m.w = a.beta * m.w + g.w;
-    *mp = m;
-    if (!a.mom_only) { w.x = wc.x - m.x; w.y = wc.y - m.y; w.z = wc.z - m.z; w.w = wc.w - m.w; }
+  __shared__ float4 red[4][64];
+  red[wv][lane] = g;
+  __syncthreads();
+  if (wv != 0 || !in) return;
+#pragma unroll
+  for (int q = 1; q < 4; ++q) { const float4 d = red[q][lane]; g.x += d.x; g.y += d.y; g.z += d.z; g.w += d.w; }
+  const long long o = e - (long long)i * pb.msz;           // offset inside matrix i (msz % 4 == 0)
+  const float4 wc = *reinterpret_cast<const float4*>(a.cur.mat(i, b, h) + o);
+  float4 w = wc;
+  if (upd) {
+    if (a.rule == RULE_GD) {
+      w.x = wc.x - g.x; w.y = wc.y - g.y; w.z = wc.z - g.z; w.w = wc.w - g.w;
+    } else {
+      // the momentum rules fold the summed partials into M (Muon leaves the step to its kernels)
+      float4* mp = reinterpret_cast<float4*>(a.mom + (size_t)p * wsz + e);
+      float4 m = *mp;
+      m.x = a.beta * m.x + g.x; m.y = a.beta * m.y + g.y; m.z = a.beta * m.z + g.z; m.w = a.beta * m.w + g.w;
+      *mp = m;
+      if (!a.mom_only) { w.x = wc.x - m.x; w.y = wc.y - m.y; w.z = wc.z - m.z; w.w = wc.w - m.w; }
+    }
   }
   *reinterpret_cast<float4*>(a.next + (size_t)p * wsz + e) = w;
   if (a.out[i]) *reinterpret_cast<float4*>(a.out[i] + (size_t)pb.row(p) * pb.msz + o) = w;
@@ -338,7 +347,7 @@ void launch_update(const Problem& pb, const UpdateArgs& a_in, hipStream_t st) {
                                           (!a.out[i] || reinterpret_cast<uintptr_t>(a.out[i]) % 16 == 0);
   if (aligned) {
     const long long wsz = (long long)pb.nm * pb.msz;
-    dim3 grid((unsigned)((wsz / 4 + 255) / 256), P);
+    dim3 grid((unsigned)((wsz / 4 + 63) / 64), P);
     if (!a.renorm) {
       hipLaunchKernelGGL(k_update_flat, grid, dim3(256), 0, st, pb, a);
       return;

@@ -65,6 +65,9 @@ int fail(ttt_handle* h, int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// token tensors are read and written with 16-byte vector accesses
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 // matrices the caller passes for a request (ttt_weights.w entries)
 int n_mats(int inner) {
   switch (inner) {
@@ -605,6 +608,8 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
   if (rc) return rc;
   const ttt_config& c = h->cfg;
   if (!q || !k || !v || !o) return fail(h, TTT_ERR_INVALID, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(h, TTT_ERR_INVALID, "q, k, v and o must be 16-byte aligned");
   if (!W0) return fail(h, TTT_ERR_INVALID, "W0 is NULL");
   if (!eta) return fail(h, TTT_ERR_INVALID, "eta is NULL");
   if (!std::isfinite(eta->scale)) return fail(h, TTT_ERR_INVALID, "eta scale must be finite");
@@ -750,6 +755,9 @@ int ttt_backward(ttt_handle* h, const void* q, const void* k, const void* v, con
   const ttt_config& c = h->cfg;
   if (!q || !k || !v || !dO || !dq || !dk || !dv)
     return fail(h, TTT_ERR_INVALID, "q, k, v, dO, dq, dk and dv must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return fail(h, TTT_ERR_INVALID, "q, k, v, dO, dq, dk and dv must be 16-byte aligned");
   if (!W0) return fail(h, TTT_ERR_INVALID, "W0 is NULL");
   if (!eta) return fail(h, TTT_ERR_INVALID, "eta is NULL");
   if (!std::isfinite(eta->scale)) return fail(h, TTT_ERR_INVALID, "eta scale must be finite");

@@ -105,6 +105,13 @@ def test_forward_rejects_before_enqueue():
         rc = ttt.ttt_forward(h, fake, fake, fake, W, e, ttt.TTT_LOSS_MSE, ttt.TTT_INNER_MLP_GELU, 0, fake,
                              None, fake, 1 << 30, None)
         assert rc == ttt.TTT_ERR_INVALID and "batch_stride" in ttt.ttt_last_error(h)
+        W.batch_stride = 0
+        for bad in range(4):   # q, k, v or o off a 16-byte boundary
+            ptrs = [fake] * 4
+            ptrs[bad] = fake + 2
+            rc = ttt.ttt_forward(h, ptrs[0], ptrs[1], ptrs[2], W, e, ttt.TTT_LOSS_MSE, ttt.TTT_INNER_MLP_GELU, 0,
+                                 ptrs[3], None, fake, 1 << 30, None)
+            assert rc == ttt.TTT_ERR_INVALID and "16-byte" in ttt.ttt_last_error(h)
     finally:
         ttt.ttt_destroy(h)
 
@@ -185,6 +192,9 @@ def test_backward_requests_validated_on_host():
         rc = ttt.ttt_backward(h, fake, fake, fake, W, ttt.ttt_eta(1.0, None), 0, 1, fake, fake, fake, fake, None,
                               None, fake, 16, None)
         assert rc == ttt.TTT_ERR_WORKSPACE
+        rc = ttt.ttt_backward(h, fake, fake, fake, W, ttt.ttt_eta(1.0, None), 0, 1, fake + 4, fake, fake, fake,
+                              None, None, fake, 1 << 30, None)
+        assert rc == ttt.TTT_ERR_INVALID and "16-byte" in ttt.ttt_last_error(h)
     finally:
         ttt.ttt_destroy(h)
     h = ttt.ttt_create(_cfg(renorm=1))

@@ -63,8 +63,16 @@ def test_glu_generic_forced_and_mfma_ragged(loss):
     (1, (9, 11), 64, "mse", True),
     (5, (12, 10), 128, "dot", False),
     (7, (11, 9), 48, "mse", True),
+    (3, (10, 21), 128, "mse", True),
+    (7, (20, 19), 64, "dot", True),
+    (3, (17, 9), 32, "dot", False),
+    (5, (1, 37), 16, "mse", True),
+    (3, (190, 190), 64, "dot", True),
 ])
 def test_dwconv(dtype, k, grid, d, loss, key_norm):
+    """The LDS-tiled kernels take d in {8, ..., 128} whose window fits 64 KiB
+    (8 x 8 tiles, ragged edges, one tile row, more tiles than workgroups at
+    190 x 190); d = 48 and k = 5 at d = 128 take the direct kernels."""
     N = grid[0] * grid[1]
     w = Workload("dw", B=2, H=2, N=N, d=d, hidden=d, dtype=dtype, inner="dwconv", loss=loss, key_norm=key_norm,
                  per_token_eta=loss == "dot", eta=1.0 if loss == "mse" else 0.01, grid=grid, conv_k=k,
