@@ -802,17 +802,22 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
     const f16* w2s = w2b[BUF];
 
     const int units = (n1 - n0 + 15) >> 4;
-    const int a_ = n0 + 16 * (w * units / QW);
-    const int b_ = min(n1, n0 + 16 * ((w + 1) * units / QW));
+    // the wave's share (wave-uniform: kept in scalar registers, so the loop
+    // below branches on scalars, not on exec masks)
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int a_ = __builtin_amdgcn_readfirstlane(n0 + 16 * (wu * units / QW));
+    const int b_ = __builtin_amdgcn_readfirstlane(min(n1, n0 + 16 * ((wu + 1) * units / QW)));
     const bf16* qp = (const bf16*)pb.q + (long long)p * N * D;
     bf16* op = (bf16*)pb.o + (long long)p * N * D;
+    // rows past the wave's share read the share's last row (their O rows are
+    // not stored), so the loads need no branch
     auto load_q = [&](int pos, bf16x8 (&q)[QTB][2]) {
 #pragma unroll
       for (int tb = 0; tb < QTB; ++tb)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int n = pos + 16 * tb + r;
-          q[tb][ks] = n < b_ ? ld8(qp + (long long)n * D + 32 * ks + 8 * g) : bf16x8{};
+          const int n = min(pos + 16 * tb + r, b_ - 1);
+          q[tb][ks] = ld8(qp + (long long)n * D + 32 * ks + 8 * g);
         }
     };
     // one pass over NTB 16-token blocks starting at pos
@@ -866,38 +871,34 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
           for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = mfma16(a, ab[tb], o[cb][tb]);
         }
       }
+      // a row past the share holds the share's last row (its Q was clamped),
+      // so storing it there rewrites identical values: no branch
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        const int n = pos + 16 * tb + r;
-        if (n < b_) {
+        const int n = min(pos + 16 * tb + r, b_ - 1);
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = pack4(o[cb][tb]);
-        }
+        for (int cb = 0; cb < 4; ++cb)
+          *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = pack4(o[cb][tb]);
       }
     };
-    bf16x8 qc[QTB][2];
+    // Q of the next piece is loaded while the current one is computed; the two
+    // register sets alternate and every piece is a full pass, so the loop has
+    // no branch that leaves a load unconsumed (which would make the compiler
+    // wait for every outstanding load and store before the next prefetch)
+    constexpr int STEP = 16 * QTB;
+    bf16x8 qa[QTB][2], qb[QTB][2];
     int pos = a_;
-    if (pos < b_) load_q(pos, qc);
+    if (pos < b_) load_q(pos, qa);
+    // the prefetch is issued unconditionally (past the share it re-reads the
+    // share's last row), so every path through the loop has the same loads
     while (pos < b_) {
-      const int rem = b_ - pos;
-      const int take = rem > 16 * (QTB - 1) ? 16 * QTB : (rem > 16 ? 32 : 16);
-      const int nxt = pos + take;
-      bf16x8 qn[QTB][2];
-      if (nxt < b_) load_q(nxt, qn);     // prefetch the next piece
-      if constexpr (QTB == 4) {
-        if (take == 64) pass(std::integral_constant<int, 4>{}, pos, qc);
-        else if (take == 32) pass(std::integral_constant<int, 2>{}, pos, qc);
-        else pass(std::integral_constant<int, 1>{}, pos, qc);
-      } else {
-        if (take == 32) pass(std::integral_constant<int, 2>{}, pos, qc);
-        else pass(std::integral_constant<int, 1>{}, pos, qc);
-      }
-#pragma unroll
-      for (int tb = 0; tb < QTB; ++tb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) qc[tb][ks] = qn[tb][ks];
-      pos = nxt;
+      load_q(pos + STEP, qb);
+      pass(std::integral_constant<int, QTB>{}, pos, qa);
+      pos += STEP;
+      if (pos >= b_) break;
+      load_q(pos + STEP, qa);
+      pass(std::integral_constant<int, QTB>{}, pos, qb);
+      pos += STEP;
     }
     };
     if (buf == 0) segment(std::integral_constant<int, 0>{});

@@ -94,20 +94,19 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3,
   if (tid < D)
     nrm[(tid & 7) * 8 + (tid >> 3)] =
         pb.stats ? reinterpret_cast<const float2*>(pb.stats)[(size_t)p * D + tid] : float2{0.f, 1.f};
+  // Rows past the batch load the batch's last row (every load is issued on
+  // every path, so the compiler's waits stay exact); their eta is 0, which
+  // zeroes their dU and dZ and so their share of dW.
   auto fetch = [&](int kt, TileRegs& t) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int n = kt * TT + st + q;
-      if (n < nt) {
-        t.x[q] = *reinterpret_cast<const bf16x8*>(kp + (long long)n * D + sc);
-        t.v[q] = *reinterpret_cast<const bf16x8*>(vp + (long long)n * D + sc);
-      } else {
-        t.x[q] = bf16x8{};
-        t.v[q] = bf16x8{};
-      }
+      const int n = min(kt * TT + st + q, nt - 1);
+      t.x[q] = *reinterpret_cast<const bf16x8*>(kp + (long long)n * D + sc);
+      t.v[q] = *reinterpret_cast<const bf16x8*>(vp + (long long)n * D + sc);
     }
-    const int n = kt * TT + tid;
-    t.e = tid < TT && n < nt ? pb.eta_scale * (ep ? ep[n] : 1.f) : 0.f;
+    const int n = kt * TT + (tid & (TT - 1));
+    const float e = pb.eta_scale * (ep ? ep[min(n, nt - 1)] : 1.f);
+    t.e = n < nt ? e : 0.f;
   };
   f32x4 a1[4], a2[4];   // dW1, dW2 blocks [channel block cb][unit block w]
 #pragma unroll
