@@ -485,12 +485,18 @@ void launch_backward(const Problem& pb, const WRef& w0, const float* wstar_state
     hipLaunchKernelGGL(k_bwd_key_tok<float>, tiles, dim3(kThreads), 0, st, pb, w0, U, dv, deta, dk, gG, gF);
     hipLaunchKernelGGL(k_bwd_wbar<float>, wgrid, dim3(kThreads), 0, st, pb, w0, U, gG, gF, S, part);
   }
-  // dW0 of each pair = U - dphi/dW0, then the caller's layout
+  // dW0 of each pair = U - dphi/dW0, then the caller's layout and the key norm
   hipLaunchKernelGGL(k_sum_splits, dim3(nblk), dim3(kThreads), 0, st, part, S, pw, -1.0f, (const float*)U, dpair);
+  launch_bwd_tail(pb, dpair, w0_shared, dW0, dk, S_kn, knp, st);
+}
+
+void launch_bwd_tail(const Problem& pb, const float* dpair, int w0_shared, float* const* dW0, float* dk, int S_kn,
+                     float* knp, hipStream_t st) {
+  const int P = pb.B * pb.H;
   const long long nout = (w0_shared ? (long long)pb.H : (long long)P) * pb.msz;
   hipLaunchKernelGGL(k_bwd_dw0, dim3((unsigned)((nout + kThreads - 1) / kThreads), pb.nm), dim3(kThreads), 0, st, pb,
                      dpair, w0_shared, dW0[0], pb.nm > 1 ? dW0[1] : nullptr);
-  // key norm
+  // key norm: dK from dK_hat in place
   if (pb.stats) {
     const dim3 g1(S_kn, P);
     const dim3 g2((unsigned)std::min<long long>(((long long)pb.N * pb.d + kThreads - 1) / kThreads, 256), P);

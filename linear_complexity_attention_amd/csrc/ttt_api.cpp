@@ -687,7 +687,14 @@ namespace {
 struct BwdPlan {
   int P, S, S_stats, S_kn;
   long long wsz;
-  size_t off_stats_part, off_stats, off_states, off_part, off_gbuf, off_U, off_dpair, off_gG, off_gF, off_knp, total;
+  size_t off_stats_part, off_stats, off_knp;
+  // generic-kernel path
+  size_t off_states, off_part, off_gbuf, off_U, off_dpair, off_gG, off_gF;
+  // fp32-MFMA path (GELU MLP, d and h multiples of 16): region offsets in the
+  // order of BwdMfmaBufs
+  bool mfma_shape;
+  size_t off_m[18];
+  size_t total;
 };
 
 int check_backward(ttt_handle* h, int loss, int inner) {
@@ -716,6 +723,11 @@ BwdPlan make_bwd_plan(const ttt_handle* h, const Problem& pb) {
   if (c.key_norm) off = align256(off + f * (size_t)bp.P * bp.S_stats * 3 * c.d);
   bp.off_stats = off;
   if (c.key_norm) off = align256(off + f * (size_t)bp.P * c.d * 2);
+  bp.off_knp = off;
+  if (c.key_norm) off = align256(off + f * (size_t)bp.P * bp.S_kn * 2 * c.d);
+  const size_t body = off;
+  // the workspace holds either path (which one runs also depends on the
+  // alignment of W0, known only at the call)
   bp.off_states = off;  off = align256(off + f * (size_t)bp.P * bp.wsz);
   bp.off_part = off;    off = align256(off + f * (size_t)bp.S * bp.P * bp.wsz);
   bp.off_gbuf = off;    off = align256(off + f * tok);
@@ -723,9 +735,22 @@ BwdPlan make_bwd_plan(const ttt_handle* h, const Problem& pb) {
   bp.off_dpair = off;   off = align256(off + f * (size_t)bp.P * bp.wsz);
   bp.off_gG = off;      off = align256(off + f * tok);
   bp.off_gF = off;      off = align256(off + f * tok);
-  bp.off_knp = off;
-  if (c.key_norm) off = align256(off + f * (size_t)bp.P * bp.S_kn * 2 * c.d);
-  bp.total = off;
+  size_t total = off;
+  bp.mfma_shape = pb.inner == INNER_MLP && c.d % 16 == 0 && pb.hid % 16 == 0;
+  if (bp.mfma_shape) {
+    BwdMfmaSizes sz;
+    bwd_mfma_sizes(pb, &sz);
+    const long long n[18] = {sz.tok_d, sz.tok_d, sz.tok_d, sz.tok_d, sz.tok_d, sz.tok_d,          // X Q dO G F Fd
+                             sz.tok_h, sz.tok_h, sz.tok_h, sz.tok_h, sz.tok_h, sz.tok_h, sz.tok_h,  // Z A dA dZ Zd Ad Ab
+                             sz.KS * sz.wsz, sz.wsz, sz.wsz, sz.wsz, 0};                            // part dW Ws U
+    off = body;
+    for (int i = 0; i < 18; ++i) {
+      bp.off_m[i] = off;
+      off = align256(off + f * (size_t)n[i]);
+    }
+    if (off > total) total = off;
+  }
+  bp.total = total;
   return bp;
 }
 
@@ -791,26 +816,39 @@ int ttt_backward(ttt_handle* h, const void* q, const void* k, const void* v, con
     launch_stats_partial(pb, bp.S_stats, buf(bp.off_stats_part), st);
     launch_stats_final(pb, bp.S_stats, buf(bp.off_stats_part), c.eps, buf(bp.off_stats), st);
   }
-  launch_gen_grad_out(pb, w0, 0, c.N, buf(bp.off_gbuf), st);
-  launch_gen_dW(pb, w0, 0, c.N, buf(bp.off_gbuf), bp.S, buf(bp.off_part), st);
-  UpdateArgs ua{};
-  ua.cur = w0;
-  ua.w0 = w0;
-  ua.part = buf(bp.off_part);
-  ua.part_mode = PART_SPLITS;
-  ua.S = bp.S;
-  ua.part_pair_stride = (long long)bp.P * bp.wsz;
-  ua.next = buf(bp.off_states);
-  ua.mask = (1u << nm) - 1;
-  ua.rule = RULE_GD;
-  launch_update(pb, ua, st);
+  // the fp32-MFMA path recomputes the step itself from whole-pair products
+  const bool use_mfma = bp.mfma_shape && bwd_mfma_supported(pb, w0);
+  if (!use_mfma) {
+    launch_gen_grad_out(pb, w0, 0, c.N, buf(bp.off_gbuf), st);
+    launch_gen_dW(pb, w0, 0, c.N, buf(bp.off_gbuf), bp.S, buf(bp.off_part), st);
+    UpdateArgs ua{};
+    ua.cur = w0;
+    ua.w0 = w0;
+    ua.part = buf(bp.off_part);
+    ua.part_mode = PART_SPLITS;
+    ua.S = bp.S;
+    ua.part_pair_stride = (long long)bp.P * bp.wsz;
+    ua.next = buf(bp.off_states);
+    ua.mask = (1u << nm) - 1;
+    ua.rule = RULE_GD;
+    launch_update(pb, ua, st);
+  }
   // the backward
   float* dw[3] = {nullptr, nullptr, nullptr};
   if (dW0)
     for (int i = 0; i < nm; ++i) dw[i] = dW0->w[i];
-  launch_backward(pb, w0, buf(bp.off_states), dO, bp.S, buf(bp.off_part), buf(bp.off_gbuf), buf(bp.off_U),
-                  buf(bp.off_gG), buf(bp.off_gF), buf(bp.off_dpair), buf(bp.off_knp), bp.S_kn, dq, dk, dv, deta, dw,
-                  W0->batch_stride == 0, st);
+  if (use_mfma) {
+    BwdMfmaBufs bb;
+    float** slot[17] = {&bb.X, &bb.Q, &bb.dO, &bb.G, &bb.F, &bb.Fd, &bb.Z, &bb.A, &bb.dA, &bb.dZ,
+                        &bb.Zd, &bb.Ad, &bb.Ab, &bb.part, &bb.dW, &bb.Ws, &bb.U};
+    for (int i = 0; i < 17; ++i) *slot[i] = buf(bp.off_m[i]);
+    bb.knp = buf(bp.off_knp);
+    launch_backward_mfma(pb, w0, dO, bb, dq, dk, dv, deta, dw, W0->batch_stride == 0, bp.S_kn, st);
+  } else {
+    launch_backward(pb, w0, buf(bp.off_states), dO, bp.S, buf(bp.off_part), buf(bp.off_gbuf), buf(bp.off_U),
+                    buf(bp.off_gG), buf(bp.off_gF), buf(bp.off_dpair), buf(bp.off_knp), bp.S_kn, dq, dk, dv, deta,
+                    dw, W0->batch_stride == 0, st);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
   return TTT_OK;

@@ -190,6 +190,27 @@ void launch_dwconv_query(const Problem& pb, const float* state, hipStream_t st);
 // fp32 [B,Hs,N,d]; deta fp32 [B,Hs,N] or null; dW0[i] in W0's layout
 // ([H,in,out] summed over the batch when w0_shared, else [B,H,in,out]) or null.
 int bwd_kn_splits(const Problem& pb);
+// dW0 in the caller's layout from the per-pair [P][nm][msz] gradient (summed
+// over the batch for a shared W0), then the key-norm backward of dk in place
+void launch_bwd_tail(const Problem& pb, const float* dpair, int w0_shared, float* const* dW0, float* dk, int S_kn,
+                     float* knp, hipStream_t st);
+// the fp32-MFMA backward of the GELU MLP (d, h multiples of 16, W0 16-byte aligned)
+struct BwdMfmaSizes {
+  long long tok_d, tok_h, wsz;   // floats of a [P][N][d], a [P][N][h] and a [P][2][d h] buffer
+  int KS;                        // token slices of the reductions over N
+};
+struct BwdMfmaBufs {
+  float *X, *Q, *dO, *G, *F, *Fd;             // [P][N][d]
+  float *Z, *A, *dA, *dZ, *Zd, *Ad, *Ab;      // [P][N][h]
+  float *part;                                // [KS][P][2][d h]
+  float *dW, *Ws, *U;                         // [P][2][d h]
+  float *knp;                                 // key-norm partials
+};
+bool bwd_mfma_supported(const Problem& pb, const WRef& w0);
+void bwd_mfma_sizes(const Problem& pb, BwdMfmaSizes* s);
+void launch_backward_mfma(const Problem& pb, const WRef& w0, const void* dO, const BwdMfmaBufs& bb, float* dq,
+                          float* dk, float* dv, float* deta, float* const* dW0, int w0_shared, int S_kn,
+                          hipStream_t st);
 void launch_backward(const Problem& pb, const WRef& w0, const float* wstar_states, const void* dO, int S,
                      float* part, float* dO32, float* U, float* gG, float* gF, float* dpair, float* knp, int S_kn,
                      float* dq, float* dk, float* dv, float* deta, float* const* dW0, int w0_shared,
