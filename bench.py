@@ -30,7 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
-PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector (published)
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32, vector and dense matrix (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 METRIC = "TTT-layer tokens/sec on 1 MI355X (N=6084, r=4) + % of bf16 MFMA peak"
 

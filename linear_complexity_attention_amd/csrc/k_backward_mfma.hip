@@ -62,10 +62,27 @@ struct OutOp {
   long long sb, sh, cstride;
   int ld;
 };
+// Elementwise epilogues on the product v (= alpha A B, plus C when
+// accumulating); z, zd, da and out2 share C's layout:
+//   EPI_STORE  C = v
+//   EPI_GELU   C = v, out2 = gelu(v)
+//   EPI_GP     C = v, out2 = v gelu'(z)   (out2 == C: only the product is kept)
+//   EPI_ZBAR   C = gelu''(z) zd da + gelu'(z) v
+enum { EPI_STORE = 0, EPI_GELU = 1, EPI_GP = 2, EPI_ZBAR = 3 };
+struct Epi {
+  const float *z, *zd, *da;
+  float* out2;
+};
 
-template <bool TA, bool TB>
+// LDS tile element (k, x) of a [BK][64] tile: rows of 80 floats, the column
+// XOR-ed with 16 (k / 4), so that the transposing scalar stores (four k rows
+// per thread) and the fragment reads (four k rows x 16 columns per wave) both
+// fall on 64 distinct banks; four consecutive columns stay consecutive.
+__device__ __forceinline__ int sw(int k, int x) { return k * LS + (x ^ ((k >> 2) << 4)); }
+
+template <bool TA, bool TB, int EPI>
 __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int KS, Op A, Op B, OutOp C,
-                                                 float alpha, int accumulate) {
+                                                 float alpha, int accumulate, Epi ep) {
   __shared__ __attribute__((aligned(16))) float As[2][BK * LS];   // [k][m]
   __shared__ __attribute__((aligned(16))) float Bs[2][BK * LS];   // [k][n]
   const int p = blockIdx.z / KS, ks = blockIdx.z % KS;
@@ -100,21 +117,21 @@ __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int
   auto store = [&](int buf) {
     if (!TA) {
       const int m = tid >> 2, k = 4 * (tid & 3);
-      As[buf][(k + 0) * LS + m] = ra.x;
-      As[buf][(k + 1) * LS + m] = ra.y;
-      As[buf][(k + 2) * LS + m] = ra.z;
-      As[buf][(k + 3) * LS + m] = ra.w;
+      As[buf][sw(k + 0, m)] = ra.x;
+      As[buf][sw(k + 1, m)] = ra.y;
+      As[buf][sw(k + 2, m)] = ra.z;
+      As[buf][sw(k + 3, m)] = ra.w;
     } else {
-      *reinterpret_cast<float4*>(&As[buf][(tid >> 4) * LS + 4 * (tid & 15)]) = ra;
+      *reinterpret_cast<float4*>(&As[buf][sw(tid >> 4, 4 * (tid & 15))]) = ra;
     }
     if (!TB) {
-      *reinterpret_cast<float4*>(&Bs[buf][(tid >> 4) * LS + 4 * (tid & 15)]) = rb;
+      *reinterpret_cast<float4*>(&Bs[buf][sw(tid >> 4, 4 * (tid & 15))]) = rb;
     } else {
       const int n = tid >> 2, k = 4 * (tid & 3);
-      Bs[buf][(k + 0) * LS + n] = rb.x;
-      Bs[buf][(k + 1) * LS + n] = rb.y;
-      Bs[buf][(k + 2) * LS + n] = rb.z;
-      Bs[buf][(k + 3) * LS + n] = rb.w;
+      Bs[buf][sw(k + 0, n)] = rb.x;
+      Bs[buf][sw(k + 1, n)] = rb.y;
+      Bs[buf][sw(k + 2, n)] = rb.z;
+      Bs[buf][sw(k + 3, n)] = rb.w;
     }
   };
   // wave (wm, wn) owns the 32 x 32 block at (32 wm, 32 wn): 2 x 2 MFMA tiles.
@@ -125,7 +142,7 @@ __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int fr = (lane >> 4) * LS + (lane & 15);
+  const int kk = lane >> 4, col = lane & 15;
   if (kt0 < kt1) {
     load(kt0 * BK);
     store(0);
@@ -137,9 +154,9 @@ __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int
       for (int s = 0; s < BK / 4; ++s) {
         float fa[2], fb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = As[buf][4 * s * LS + fr + 32 * wm + 16 * i];
+        for (int i = 0; i < 2; ++i) fa[i] = As[buf][sw(4 * s + kk, 32 * wm + 16 * i + col)];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = Bs[buf][4 * s * LS + fr + 32 * wn + 16 * j];
+        for (int j = 0; j < 2; ++j) fb[j] = Bs[buf][sw(4 * s + kk, 32 * wn + 16 * j + col)];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -158,8 +175,23 @@ __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + 32 * wm + 16 * i + 4 * (lane >> 4) + e;
         if (m < M && n < N) {
-          float* o = c + (long long)m * C.ld + n;
-          *o = accumulate ? *o + alpha * acc[i][j][e] : alpha * acc[i][j][e];
+          const long long oi = (long long)m * C.ld + n;
+          float* o = c + oi;
+          const float v = accumulate ? *o + alpha * acc[i][j][e] : alpha * acc[i][j][e];
+          if constexpr (EPI == EPI_STORE) {
+            *o = v;
+          } else if constexpr (EPI == EPI_GELU) {
+            *o = v;
+            (ep.out2 + (o - C.p))[0] = gelu_exact(v);
+          } else if constexpr (EPI == EPI_GP) {
+            const float gp = gelu_exact_prime((ep.z + (o - C.p))[0]);
+            if (ep.out2 != C.p) *o = v;
+            (ep.out2 + (o - C.p))[0] = v * gp;
+          } else {
+            const long long q = o - C.p;
+            const float zz = ep.z[q];
+            *o = gelu_second_f(zz) * ep.zd[q] * ep.da[q] + gelu_exact_prime(zz) * v;
+          }
         }
       }
     }
@@ -184,27 +216,6 @@ __global__ void __launch_bounds__(kT) k_rows_f32(Problem pb, const T* __restrict
       x = (x - stats[((size_t)p * d + ch) * 2]) * stats[((size_t)p * d + ch) * 2 + 1];
     }
     o[i] = x;
-  }
-}
-
-// out = gelu(z)
-__global__ void __launch_bounds__(kT) k_gelu(long long n, const float* __restrict__ z, float* __restrict__ out) {
-  for (long long i = blockIdx.x * (long long)kT + threadIdx.x; i < n; i += (long long)gridDim.x * kT)
-    out[i] = gelu_exact(z[i]);
-}
-
-// x *= gelu'(z)
-__global__ void __launch_bounds__(kT) k_mul_gelu_prime(long long n, const float* __restrict__ z, float* __restrict__ x) {
-  for (long long i = blockIdx.x * (long long)kT + threadIdx.x; i < n; i += (long long)gridDim.x * kT)
-    x[i] *= gelu_exact_prime(z[i]);
-}
-
-// Z_bar = gelu''(Z) Z_dot A_dot_bar + gelu'(Z) A_bar, in place of A_bar
-__global__ void __launch_bounds__(kT) k_zbar(long long n, const float* __restrict__ z, const float* __restrict__ zd,
-                                             const float* __restrict__ adb, float* __restrict__ ab) {
-  for (long long i = blockIdx.x * (long long)kT + threadIdx.x; i < n; i += (long long)gridDim.x * kT) {
-    const float zz = z[i];
-    ab[i] = gelu_second_f(zz) * zd[i] * adb[i] + gelu_exact_prime(zz) * ab[i];
   }
 }
 
@@ -309,11 +320,12 @@ void bwd_mfma_sizes(const Problem& pb, BwdMfmaSizes* s) {
 
 namespace {
 
-template <bool TA, bool TB>
+template <bool TA, bool TB, int EPI = EPI_STORE>
 void gemm(int P, int H, int M, int N, int K, int KS, const Op& A, const Op& B, const OutOp& C, bool acc,
-          hipStream_t st, float alpha = 1.0f) {
+          hipStream_t st, float alpha = 1.0f, const Epi& ep = Epi{}) {
   const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, P * KS);
-  hipLaunchKernelGGL((k_gemm_f32<TA, TB>), grid, dim3(kT), 0, st, H, M, N, K, KS, A, B, C, alpha, acc ? 1 : 0);
+  hipLaunchKernelGGL((k_gemm_f32<TA, TB, EPI>), grid, dim3(kT), 0, st, H, M, N, K, KS, A, B, C, alpha, acc ? 1 : 0,
+                     ep);
 }
 
 // pair-major [P][rows][ld] buffer as an operand
@@ -342,7 +354,6 @@ void launch_backward_mfma(const Problem& pb, const WRef& w0, const void* dO, con
   auto so1 = [&](float* base, long long cs) { return OutOp{base, wpp * H, wpp, cs, h}; };
   auto so2 = [&](float* base, long long cs) { return OutOp{base + msz, wpp * H, wpp, cs, d}; };
   const long long cs = (long long)P * wpp;                     // K-slice stride of the weight partials
-  const unsigned ewd = ew_blocks(sz.tok_d), ewh = ew_blocks(sz.tok_h);
 
   // token rows as fp32: X = K_hat, Q, dO
   if (pb.bf16) {
@@ -357,17 +368,16 @@ void launch_backward_mfma(const Problem& pb, const WRef& w0, const void* dO, con
   const Op X = pm(bb.X, nd, H, d), Q = pm(bb.Q, nd, H, d), dOp = pm(bb.dO, nd, H, d);
 
   // ---- the step at W0: Z, A, F, G, dA, dZ, dW, W*
-  gemm<false, false>(P, H, N, h, d, 1, X, W1, pmo(bb.Z, nh, H, h), false, st);
-  hipLaunchKernelGGL(k_gelu, dim3(ewh), dim3(kT), 0, st, sz.tok_h, bb.Z, bb.A);
+  gemm<false, false, EPI_GELU>(P, H, N, h, d, 1, X, W1, pmo(bb.Z, nh, H, h), false, st, 1.0f,
+                               Epi{nullptr, nullptr, nullptr, bb.A});                               // Z, A
   if (mse) gemm<false, false>(P, H, N, d, h, 1, pm(bb.A, nh, H, h), W2, pmo(bb.F, nd, H, d), false, st);
   if (pb.bf16) hipLaunchKernelGGL(k_loss_grad<bf16>, rows, dim3(kT), 0, st, pb, bb.F, bb.G);
   else hipLaunchKernelGGL(k_loss_grad<float>, rows, dim3(kT), 0, st, pb, bb.F, bb.G);
   const Op G = pm(bb.G, nd, H, d);
   // dW2 = A^T G, dA = G W2^T, dZ = gelu'(Z) dA, dW1 = X^T dZ (slices of N, summed in order)
   gemm<true, false>(P, H, h, d, N, KS, pm(bb.A, nh, H, h), G, so2(bb.part, cs), false, st);
-  gemm<false, true>(P, H, N, h, d, 1, G, W2, pmo(bb.dA, nh, H, h), false, st);
-  hipMemcpyAsync(bb.dZ, bb.dA, sizeof(float) * sz.tok_h, hipMemcpyDeviceToDevice, st);
-  hipLaunchKernelGGL(k_mul_gelu_prime, dim3(ewh), dim3(kT), 0, st, sz.tok_h, bb.Z, bb.dZ);
+  gemm<false, true, EPI_GP>(P, H, N, h, d, 1, G, W2, pmo(bb.dA, nh, H, h), false, st, 1.0f,
+                            Epi{bb.Z, nullptr, nullptr, bb.dZ});                                    // dA, dZ
   gemm<true, false>(P, H, d, h, N, KS, X, pm(bb.dZ, nh, H, h), so1(bb.part, cs), false, st);
   hipLaunchKernelGGL(k_sum_slices, dim3(ew_blocks(cs)), dim3(kT), 0, st, bb.part, KS, cs, 1.0f,
                      (const float*)nullptr, bb.dW);
@@ -375,11 +385,11 @@ void launch_backward_mfma(const Problem& pb, const WRef& w0, const void* dO, con
                      w0, bb.dW, bb.Ws);
 
   // ---- the readout backward at W*: U = dS/dW*, dQ
-  gemm<false, false>(P, H, N, h, d, 1, Q, st1(bb.Ws), pmo(bb.Zd, nh, H, h), false, st);      // Zq (in Zd)
-  hipLaunchKernelGGL(k_gelu, dim3(ewh), dim3(kT), 0, st, sz.tok_h, bb.Zd, bb.Ad);           // Aq (in Ad)
+  gemm<false, false, EPI_GELU>(P, H, N, h, d, 1, Q, st1(bb.Ws), pmo(bb.Zd, nh, H, h), false, st, 1.0f,
+                               Epi{nullptr, nullptr, nullptr, bb.Ad});                              // Zq, Aq (in Zd, Ad)
   gemm<true, false>(P, H, h, d, N, KS, pm(bb.Ad, nh, H, h), dOp, so2(bb.part, cs), false, st);  // U2 slices
-  gemm<false, true>(P, H, N, h, d, 1, dOp, st2(bb.Ws), pmo(bb.Ab, nh, H, h), false, st);     // dO W2*^T (in Ab)
-  hipLaunchKernelGGL(k_mul_gelu_prime, dim3(ewh), dim3(kT), 0, st, sz.tok_h, bb.Zd, bb.Ab);  // dZq
+  gemm<false, true, EPI_GP>(P, H, N, h, d, 1, dOp, st2(bb.Ws), pmo(bb.Ab, nh, H, h), false, st, 1.0f,
+                            Epi{bb.Zd, nullptr, nullptr, bb.Ab});                                  // dZq (in Ab)
   gemm<true, false>(P, H, d, h, N, KS, Q, pm(bb.Ab, nh, H, h), so1(bb.part, cs), false, st);    // U1 slices
   hipLaunchKernelGGL(k_sum_slices, dim3(ew_blocks(cs)), dim3(kT), 0, st, bb.part, KS, cs, 1.0f,
                      (const float*)nullptr, bb.U);
@@ -390,18 +400,21 @@ void launch_backward_mfma(const Problem& pb, const WRef& w0, const void* dO, con
   }
 
   // ---- through the step: tangent along U, phi's per-token and weight terms
-  gemm<false, false>(P, H, N, h, d, 1, X, st1(bb.U), pmo(bb.Zd, nh, H, h), false, st);       // Z_dot
-  hipMemcpyAsync(bb.Ad, bb.Zd, sizeof(float) * sz.tok_h, hipMemcpyDeviceToDevice, st);
-  hipLaunchKernelGGL(k_mul_gelu_prime, dim3(ewh), dim3(kT), 0, st, sz.tok_h, bb.Z, bb.Ad);   // A_dot
+  gemm<false, false, EPI_GP>(P, H, N, h, d, 1, X, st1(bb.U), pmo(bb.Zd, nh, H, h), false, st, 1.0f,
+                             Epi{bb.Z, nullptr, nullptr, bb.Ad});                                  // Z_dot, A_dot
   gemm<false, false>(P, H, N, d, h, 1, pm(bb.Ad, nh, H, h), W2, pmo(bb.Fd, nd, H, d), false, st);
   gemm<false, false>(P, H, N, d, h, 1, pm(bb.A, nh, H, h), st2(bb.U), pmo(bb.Fd, nd, H, d), true, st);  // F_dot
   if (pb.bf16) hipLaunchKernelGGL(k_phi_tok<bf16>, dim3((N + 3) / 4, P), dim3(kT), 0, st, pb, bb.F, bb.Fd, dv, deta);
   else hipLaunchKernelGGL(k_phi_tok<float>, dim3((N + 3) / 4, P), dim3(kT), 0, st, pb, bb.F, bb.Fd, dv, deta);
   const Op Fb = pm(bb.Fd, nd, H, d);    // F_bar (MSE)
   // A_bar = G U2^T + F_bar W2^T, then Z_bar in its place
-  gemm<false, true>(P, H, N, h, d, 1, G, st2(bb.U), pmo(bb.Ab, nh, H, h), false, st);
-  if (mse) gemm<false, true>(P, H, N, h, d, 1, Fb, W2, pmo(bb.Ab, nh, H, h), true, st);
-  hipLaunchKernelGGL(k_zbar, dim3(ewh), dim3(kT), 0, st, sz.tok_h, bb.Z, bb.Zd, bb.dA, bb.Ab);
+  const Epi zbar{bb.Z, bb.Zd, bb.dA, nullptr};
+  if (mse) {
+    gemm<false, true>(P, H, N, h, d, 1, G, st2(bb.U), pmo(bb.Ab, nh, H, h), false, st);
+    gemm<false, true, EPI_ZBAR>(P, H, N, h, d, 1, Fb, W2, pmo(bb.Ab, nh, H, h), true, st, 1.0f, zbar);
+  } else {
+    gemm<false, true, EPI_ZBAR>(P, H, N, h, d, 1, G, st2(bb.U), pmo(bb.Ab, nh, H, h), false, st, 1.0f, zbar);
+  }
   // dK_hat = -(Z_dot_bar U1^T + Z_bar W1^T), at the pair's rows of dk
   {
     const OutOp dko{dk + (long long)pb.h0 * nd, (long long)pb.Hs * nd, nd, 0, d};
