@@ -48,7 +48,7 @@ VARIANTS = {
     "c5_lact_muon": ("c5_lact_swiglu", dict(rule="muon", beta=0.9, muon_scale=0.02), "forward", "mfma"),
     "c5_lact_video_mask": ("c5_lact_swiglu", dict(chunk_update=[1, 0] * 8), "forward", "mfma"),
     "c3_first_layer_only": ("c3_hires_r4", dict(update_mask=1), "forward", "mfma"),
-    "c3_epochs3": ("c3_hires_r4", dict(epochs=3), "forward", "alu"),
+    "c3_epochs3": ("c3_hires_r4", dict(epochs=3), "forward", "mfma"),
     "vit3_hires": ("vit3_hires", None, "forward", "mfma"),
     "c3_outer_backward": ("c3_hires_r4", None, "backward", "mfma"),
 }
@@ -205,6 +205,34 @@ def measure_mfma_peak(torch, blib):
     return blib.bench_mfma_peak_flops(blocks, iters) / (best * 1e-3) / 1e12, mhz
 
 
+def measure_overlap(torch):
+    """Times of the overlap probe: 16 MFMAs (16x16x32 bf16) and/or NV packed
+    f16 FMAs per wave and iteration, one or two waves per SIMD, no memory."""
+    blib = ctypes.CDLL(os.path.join(ROOT, "linear_complexity_attention_amd", "libttt_bench.so"))
+    blib.bench_overlap_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 20000
+    sink = torch.empty(cu * 512, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    names = ["1 wave/SIMD: 16 MFMA", "1 wave/SIMD: 64 VALU", "1 wave/SIMD: 16 MFMA + 32 VALU in one wave",
+             "1 wave/SIMD: 16 MFMA + 64 VALU in one wave", "2 waves/SIMD: 16 MFMA each",
+             "2 waves/SIMD: one 16 MFMA, the other 64 VALU", "2 waves/SIMD: 16 MFMA + 64 VALU in each"]
+    out = {"iterations": iters, "cus": cu, "ms": {}}
+    for i, name in enumerate(names):
+        blib.bench_overlap_launch(i, cu, 200, ctypes.c_void_p(sink.data_ptr()), stream)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            blib.bench_overlap_launch(i, cu, iters, ctypes.c_void_p(sink.data_ptr()), stream)
+            b.record()
+            torch.cuda.synchronize()
+            best = a.elapsed_time(b) if best is None else min(best, a.elapsed_time(b))
+        out["ms"][name] = round(best, 3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,16 +243,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the clock probe and the MFMA micro-benchmark")
+    ap.add_argument("--mfma-valu-overlap", action="store_true",
+                    help="only run the MFMA / packed-f16 VALU overlap micro-benchmark and print its times")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (fp32 read + write) five times; its "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "runs on one GPU only; --gpus must be 1 (sharding over (batch, head) "
+                                   "pairs across GPUs is not built)"}))
         sys.exit(2)
 
     import torch
+
+    if args.mfma_valu_overlap:
+        print(json.dumps(measure_overlap(torch)))
+        return
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -362,6 +396,9 @@ def main():
     else:
         kname = {"mfma": "fused forward/backward (k_mfma_grad)", "mfma_swiglu": "SwiGLU forward/backward "
                  "(k_lact_grad), first chunk"}.get(path, "gradient kernels of the first update batch")
+        fp32_mfma = path.startswith("mfma_f32")
+        if fp32_mfma:
+            kname = "fp32 matrix-core step (k_gemm_f32 products + passes), first update batch"
         grad_flops = P * gemm_flops(w, first_tokens)[0]
         if w.inner == "vit3":
             grad_flops = w.B * (w.H - 1) * gemm_flops(w, first_tokens)[0]
@@ -372,7 +409,7 @@ def main():
             roof.update(kernel=kname, achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s", frac=achieved / PEAK_HBM_GBS,
                         traffic=stored_traffic("grad", args.workload), algorithmic_bytes_per_launch=nbytes)
         else:
-            peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_FP32_TFLOPS
+            peak = PEAK_BF16_TFLOPS if bound == "mfma" and not fp32_mfma else PEAK_FP32_TFLOPS
             achieved = grad_flops / (grad_ms * 1e-3) / 1e12
             roof.update(kernel=kname, achieved=achieved, peak=peak, unit="TFLOP/s", frac=achieved / peak,
                         traffic=stored_traffic("grad", args.workload), algorithmic_flops_per_launch=grad_flops)

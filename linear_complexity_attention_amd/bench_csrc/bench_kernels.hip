@@ -6,7 +6,13 @@
 //    chains per wave; 16x16x32 needs 16 chains to come within 15 % of it);
 //  - a shader-clock probe: one wave reads the shader cycle counter
 //    (s_memtime) and the constant 100 MHz counter (s_memrealtime) around a
-//    busy loop; their ratio is the shader clock at that moment.
+//    busy loop; their ratio is the shader clock at that moment;
+//  - an MFMA / VALU overlap probe: per iteration a wave issues 16
+//    v_mfma_f32_16x16x32_bf16 on 16 independent accumulators and/or NV
+//    packed-f16 FMAs on 8 independent chains, either in the same wave or split
+//    over two waves of a SIMD (even waves MFMA, odd waves VALU); no memory
+//    traffic.  Comparing the times shows how much VALU work hides under the
+//    matrix cores.
 #include <hip/hip_runtime.h>
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -58,7 +64,69 @@ __global__ void k_clock_probe(int spins, unsigned long long* __restrict__ out) {
   }
 }
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// MODE 0: MFMA only; 1: VALU only; 2: both in each wave; 3: even waves MFMA,
+// odd waves VALU.  NV packed FMAs per iteration.
+template <int MODE, int NV>
+__global__ void __launch_bounds__(512) k_overlap(int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(1e-3f * (lane + i));
+    b[i] = (__bf16)(2e-3f * (lane - i));
+  }
+  f32x4v c[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) c[j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  h2v x[8];
+  const h2v m = h2v{(_Float16)0.999f, (_Float16)0.999f}, add = h2v{(_Float16)0.001f, (_Float16)0.001f};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = h2v{(_Float16)(0.01f * j), (_Float16)(0.02f * lane)};
+  const bool do_m = MODE == 0 || MODE == 2 || (MODE == 3 && (wv & 1) == 0);
+  const bool do_v = MODE == 1 || MODE == 2 || (MODE == 3 && (wv & 1) == 1);
+  for (int it = 0; it < iters; ++it) {
+    if (do_m) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[j], 0, 0, 0);
+    }
+    if (do_v) {
+#pragma unroll
+      for (int u = 0; u < NV / 8; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = __builtin_elementwise_fma(x[j], m, add);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += (float)x[j][0] + (float)x[j][1];
+  if (s == 12345.f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;   // keeps the chains alive
+}
+
 extern "C" {
+
+// One overlap-probe launch: case 0..6 = (waves per SIMD, mode, NV)
+//   0: 1, MFMA only          1: 1, VALU only (NV 64)     2: 1, both (NV 32)
+//   3: 1, both (NV 64)       4: 2, MFMA only             5: 2, split MFMA | VALU (NV 64)
+//   6: 2, both (NV 64)
+// blocks = CUs; threads = 256 per wave per SIMD.  sink: blocks * 512 floats.
+int bench_overlap_launch(int which, int blocks, int iters, float* sink, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  switch (which) {
+    case 0: hipLaunchKernelGGL((k_overlap<0, 64>), dim3(blocks), dim3(256), 0, st, iters, sink); break;
+    case 1: hipLaunchKernelGGL((k_overlap<1, 64>), dim3(blocks), dim3(256), 0, st, iters, sink); break;
+    case 2: hipLaunchKernelGGL((k_overlap<2, 32>), dim3(blocks), dim3(256), 0, st, iters, sink); break;
+    case 3: hipLaunchKernelGGL((k_overlap<2, 64>), dim3(blocks), dim3(256), 0, st, iters, sink); break;
+    case 4: hipLaunchKernelGGL((k_overlap<0, 64>), dim3(blocks), dim3(512), 0, st, iters, sink); break;
+    case 5: hipLaunchKernelGGL((k_overlap<3, 64>), dim3(blocks), dim3(512), 0, st, iters, sink); break;
+    default: hipLaunchKernelGGL((k_overlap<2, 64>), dim3(blocks), dim3(512), 0, st, iters, sink); break;
+  }
+  return (int)hipGetLastError();
+}
 
 // flops of one k_mfma_peak launch: blocks * 4 waves * iters * chains * 32*32*16*2
 double bench_mfma_peak_flops(int blocks, int iters) {

@@ -1,10 +1,15 @@
-// Outer-loop backward of the TTT layer on the fp32 matrix cores (GELU MLP,
-// d and h multiples of 16): the same gradient of a gradient as the token-tile
-// kernels of k_backward.hip (ViT3 summary page, section 02: the inner update
-// is differentiable and trained end to end; section 03 guideline 1: the value
-// projection learns through the loss's mixed second derivative), restated as
-// batched products over whole pairs plus elementwise passes, so that every
-// product runs on v_mfma_f32_16x16x4f32 (exact fp32 products, fp32 sums).
+// GELU-MLP products on the fp32 matrix cores (d and h multiples of 16):
+// batched products over whole pairs plus elementwise passes, every product on
+// v_mfma_f32_16x16x4f32 (exact fp32 products, fp32 sums), for the two fp32
+// paths of the layer:
+//  - one inner step on a token range at the fp32 weights (ViT3 summary page,
+//    section 02, steps (i)-(ii)), for the multi-step requests (epochs, chunks,
+//    section 03 guideline 2) that cannot use the bf16 fused kernel: its
+//    token-sliced partials feed the ordinary update kernels;
+//  - the outer-loop backward, the same gradient of a gradient as the token-tile
+//    kernels of k_backward.hip (section 02: the inner update is differentiable
+//    and trained end to end; section 03 guideline 1: the value projection
+//    learns through the loss's mixed second derivative).
 //
 // Per pair, with X = K_hat, Z = X W1, A = gelu(Z), F = A W2 and the loss
 // gradient G (MSE: 2/(N d) eta (F - V); dot: -eta V):
@@ -200,14 +205,14 @@ __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int
 // ---------------------------------------------------------------------------
 // elementwise passes over [P][N][x] buffers (pair-major)
 
-// token rows of a [B, Hs, N, d] tensor -> fp32 [P][N][d]; keys normalised
-// with the statistics when given
+// token rows t0 .. t0 + nt of a [B, Hs, N, d] tensor -> fp32 [P][nt][d];
+// keys normalised with the statistics when given
 template <typename T>
 __global__ void __launch_bounds__(kT) k_rows_f32(Problem pb, const T* __restrict__ src, const float* __restrict__ stats,
-                                                 float* __restrict__ dst) {
+                                                 int t0, int nt, float* __restrict__ dst) {
   const int p = blockIdx.y, d = pb.d;
-  const long long n = (long long)pb.N * d;
-  const T* s = src + pb.row(p) * n;
+  const long long n = (long long)nt * d;
+  const T* s = src + pb.row(p) * (long long)pb.N * d + (long long)t0 * d;
   float* o = dst + (long long)p * n;
   for (long long i = blockIdx.x * (long long)kT + threadIdx.x; i < n; i += (long long)gridDim.x * kT) {
     float x = to_f32<T>(s[i]);
@@ -219,16 +224,18 @@ __global__ void __launch_bounds__(kT) k_rows_f32(Problem pb, const T* __restrict
   }
 }
 
-// the loss gradient at W0: G = 2/(N d) eta (F - V) [MSE], -eta V [dot]
+// the loss gradient of tokens t0 .. t0 + nt: G = 2/(nt d) eta (F - V) [MSE],
+// -eta V [dot] -> [P][nt][d]
 template <typename T>
-__global__ void __launch_bounds__(kT) k_loss_grad(Problem pb, const float* __restrict__ F, float* __restrict__ G) {
+__global__ void __launch_bounds__(kT) k_loss_grad(Problem pb, int t0, int nt, const float* __restrict__ F,
+                                                  float* __restrict__ G) {
   const int p = blockIdx.y, d = pb.d, N = pb.N;
-  const long long n = (long long)N * d, prow = pb.row(p);
-  const T* v = (const T*)pb.v + prow * n;
-  const float c2 = 2.0f / ((float)N * (float)d);
+  const long long n = (long long)nt * d, prow = pb.row(p);
+  const T* v = (const T*)pb.v + (prow * N + t0) * d;
+  const float c2 = 2.0f / ((float)nt * (float)d);
   const bool mse = pb.loss == LOSS_MSE;
   for (long long i = blockIdx.x * (long long)kT + threadIdx.x; i < n; i += (long long)gridDim.x * kT) {
-    const int t = (int)(i / d);
+    const int t = t0 + (int)(i / d);
     const float e = pb.eta_scale * (pb.eta_tok ? pb.eta_tok[prow * N + t] : 1.f);
     const float vv = to_f32<T>(v[i]);
     G[(long long)p * n + i] = mse ? e * c2 * (F[(long long)p * n + i] - vv) : -e * vv;
@@ -336,6 +343,51 @@ OutOp pmo(float* p, long long per_pair, int H, int ld, long long cstride = 0) {
 
 }  // namespace
 
+bool step_mfma_shape(const Problem& pb) { return pb.inner == INNER_MLP && pb.d % 16 == 0 && pb.hid % 16 == 0; }
+
+bool step_mfma_aligned(const WRef& W) {
+  for (int i = 0; i < 2; ++i)
+    if (reinterpret_cast<uintptr_t>(W.m[i]) % 16 != 0) return false;
+  return W.sb % 4 == 0 && W.sh % 4 == 0;
+}
+
+int step_mfma_splits(const Problem& pb, int nt) {
+  const long long P = (long long)pb.B * pb.H;
+  return red_slices(P * ((pb.d + BM - 1) / BM) * ((pb.hid + BN - 1) / BN), nt);
+}
+
+// One inner step on tokens [t0, t0 + nt) of every pair at the weights W:
+//   X = K_hat rows, Z = X W1 and A = gelu(Z), F = A W2 (MSE), G, dW2 = A^T G,
+//   dA = G W2^T and dZ = gelu'(Z) dA, dW1 = X^T dZ
+// The weight gradients go to part as KS token slices [KS][P][2][d h] (the
+// layout of the token-split partials the update kernels sum); dA is kept only
+// when sb.dA is given (else dZ overwrites it in place).
+void launch_step_mfma(const Problem& pb, const WRef& W, int t0, int nt, const StepMfmaBufs& sb, float* part, int KS,
+                      hipStream_t st) {
+  const int P = pb.B * pb.H, H = pb.H, d = pb.d, h = pb.hid;
+  const long long nd = (long long)nt * d, nh = (long long)nt * h, msz = pb.msz, wpp = 2 * msz;
+  const long long cs = (long long)P * wpp;
+  const dim3 rows(64, P);
+  const Op W1{W.m[0], W.sb, W.sh, h}, W2{W.m[1], W.sb, W.sh, d};
+  if (pb.bf16)
+    hipLaunchKernelGGL(k_rows_f32<bf16>, rows, dim3(kT), 0, st, pb, (const bf16*)pb.k, pb.stats, t0, nt, sb.X);
+  else
+    hipLaunchKernelGGL(k_rows_f32<float>, rows, dim3(kT), 0, st, pb, (const float*)pb.k, pb.stats, t0, nt, sb.X);
+  const Op X = pm(sb.X, nd, H, d);
+  gemm<false, false, EPI_GELU>(P, H, nt, h, d, 1, X, W1, pmo(sb.Z, nh, H, h), false, st, 1.0f,
+                               Epi{nullptr, nullptr, nullptr, sb.A});                               // Z, A
+  if (pb.loss == LOSS_MSE) gemm<false, false>(P, H, nt, d, h, 1, pm(sb.A, nh, H, h), W2, pmo(sb.F, nd, H, d), false, st);
+  if (pb.bf16) hipLaunchKernelGGL(k_loss_grad<bf16>, rows, dim3(kT), 0, st, pb, t0, nt, sb.F, sb.G);
+  else hipLaunchKernelGGL(k_loss_grad<float>, rows, dim3(kT), 0, st, pb, t0, nt, sb.F, sb.G);
+  const Op G = pm(sb.G, nd, H, d);
+  const OutOp o1{part, wpp * H, wpp, cs, h}, o2{part + msz, wpp * H, wpp, cs, d};
+  gemm<true, false>(P, H, h, d, nt, KS, pm(sb.A, nh, H, h), G, o2, false, st);                      // dW2 slices
+  float* dA = sb.dA ? sb.dA : sb.dZ;
+  gemm<false, true, EPI_GP>(P, H, nt, h, d, 1, G, W2, pmo(dA, nh, H, h), false, st, 1.0f,
+                            Epi{sb.Z, nullptr, nullptr, sb.dZ});                                    // dA, dZ
+  gemm<true, false>(P, H, d, h, nt, KS, X, pm(sb.dZ, nh, H, h), o1, false, st);                     // dW1 slices
+}
+
 void launch_backward_mfma(const Problem& pb, const WRef& w0, const void* dO, const BwdMfmaBufs& bb, float* dq,
                           float* dk, float* dv, float* deta, float* const* dW0, int w0_shared, int S_kn,
                           hipStream_t st) {
@@ -355,30 +407,21 @@ void launch_backward_mfma(const Problem& pb, const WRef& w0, const void* dO, con
   auto so2 = [&](float* base, long long cs) { return OutOp{base + msz, wpp * H, wpp, cs, d}; };
   const long long cs = (long long)P * wpp;                     // K-slice stride of the weight partials
 
-  // token rows as fp32: X = K_hat, Q, dO
+  // token rows as fp32: Q, dO (X = K_hat comes with the step)
   if (pb.bf16) {
-    hipLaunchKernelGGL(k_rows_f32<bf16>, rows, dim3(kT), 0, st, pb, (const bf16*)pb.k, pb.stats, bb.X);
-    hipLaunchKernelGGL(k_rows_f32<bf16>, rows, dim3(kT), 0, st, pb, (const bf16*)pb.q, (const float*)nullptr, bb.Q);
-    hipLaunchKernelGGL(k_rows_f32<bf16>, rows, dim3(kT), 0, st, pb, (const bf16*)dO, (const float*)nullptr, bb.dO);
+    hipLaunchKernelGGL(k_rows_f32<bf16>, rows, dim3(kT), 0, st, pb, (const bf16*)pb.q, (const float*)nullptr, 0, N, bb.Q);
+    hipLaunchKernelGGL(k_rows_f32<bf16>, rows, dim3(kT), 0, st, pb, (const bf16*)dO, (const float*)nullptr, 0, N, bb.dO);
   } else {
-    hipLaunchKernelGGL(k_rows_f32<float>, rows, dim3(kT), 0, st, pb, (const float*)pb.k, pb.stats, bb.X);
-    hipLaunchKernelGGL(k_rows_f32<float>, rows, dim3(kT), 0, st, pb, (const float*)pb.q, (const float*)nullptr, bb.Q);
-    hipLaunchKernelGGL(k_rows_f32<float>, rows, dim3(kT), 0, st, pb, (const float*)dO, (const float*)nullptr, bb.dO);
+    hipLaunchKernelGGL(k_rows_f32<float>, rows, dim3(kT), 0, st, pb, (const float*)pb.q, (const float*)nullptr, 0, N,
+                       bb.Q);
+    hipLaunchKernelGGL(k_rows_f32<float>, rows, dim3(kT), 0, st, pb, (const float*)dO, (const float*)nullptr, 0, N,
+                       bb.dO);
   }
   const Op X = pm(bb.X, nd, H, d), Q = pm(bb.Q, nd, H, d), dOp = pm(bb.dO, nd, H, d);
 
-  // ---- the step at W0: Z, A, F, G, dA, dZ, dW, W*
-  gemm<false, false, EPI_GELU>(P, H, N, h, d, 1, X, W1, pmo(bb.Z, nh, H, h), false, st, 1.0f,
-                               Epi{nullptr, nullptr, nullptr, bb.A});                               // Z, A
-  if (mse) gemm<false, false>(P, H, N, d, h, 1, pm(bb.A, nh, H, h), W2, pmo(bb.F, nd, H, d), false, st);
-  if (pb.bf16) hipLaunchKernelGGL(k_loss_grad<bf16>, rows, dim3(kT), 0, st, pb, bb.F, bb.G);
-  else hipLaunchKernelGGL(k_loss_grad<float>, rows, dim3(kT), 0, st, pb, bb.F, bb.G);
+  // ---- the step at W0 (Z, A, F, G, dA, dZ kept for the terms of phi), W*
+  launch_step_mfma(pb, w0, 0, N, StepMfmaBufs{bb.X, bb.Z, bb.A, bb.dA, bb.dZ, bb.F, bb.G}, bb.part, KS, st);
   const Op G = pm(bb.G, nd, H, d);
-  // dW2 = A^T G, dA = G W2^T, dZ = gelu'(Z) dA, dW1 = X^T dZ (slices of N, summed in order)
-  gemm<true, false>(P, H, h, d, N, KS, pm(bb.A, nh, H, h), G, so2(bb.part, cs), false, st);
-  gemm<false, true, EPI_GP>(P, H, N, h, d, 1, G, W2, pmo(bb.dA, nh, H, h), false, st, 1.0f,
-                            Epi{bb.Z, nullptr, nullptr, bb.dZ});                                    // dA, dZ
-  gemm<true, false>(P, H, d, h, N, KS, X, pm(bb.dZ, nh, H, h), so1(bb.part, cs), false, st);
   hipLaunchKernelGGL(k_sum_slices, dim3(ew_blocks(cs)), dim3(kT), 0, st, bb.part, KS, cs, 1.0f,
                      (const float*)nullptr, bb.dW);
   hipLaunchKernelGGL(k_wstar, dim3((unsigned)std::min<long long>((msz + kT - 1) / kT, 64), P, 2), dim3(kT), 0, st, pb,

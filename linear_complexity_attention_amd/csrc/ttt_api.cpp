@@ -123,10 +123,13 @@ struct Plan {
   bool lact_grad, lact_query;        // SwiGLU MFMA kernels
   bool dwconv;                       // depthwise-convolution kernels
   bool glu_grad, glu_query;          // GLU MFMA kernels
+  bool step_mfma;                    // fp32 GELU-MLP step on the matrix cores (else k_gen_*)
   int S_stats, S_grad;               // S_grad: partial slots of the gradient kernel
+  int S_step;                        // token slices of the fp32 matrix-core step
   int sk_G, sk_J;                    // stream-K geometry (MFMA gradient kernel)
   // byte offsets
   size_t off_stats_part, off_stats, off_states, off_part, off_gbuf, off_mom, off_muon, off_flag, total;
+  size_t off_step[6];                // X, Z, A, dZ, F, G of the fp32 matrix-core step
   long long state_stride;            // floats between consecutive states
 };
 
@@ -274,6 +277,11 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
   } else {
     pl.S_grad = choose_splits((long long)pl.P * ((pb.hid + 31) / 32), pl.span, 16, 1024);
   }
+  // the GELU MLP off the fused bf16 kernel (several steps, fp32 tensors):
+  // the fp32 matrix-core step, or the generic kernels when the weights are not
+  // 16-byte aligned (known only at the call, so both get workspace)
+  pl.step_mfma = !generic_only && !pl.mfma_grad && step_mfma_shape(pb);
+  pl.S_step = pl.step_mfma ? step_mfma_splits(pb, pl.span) : 0;
   size_t off = 0;
   pl.off_stats_part = off;
   if (c.key_norm) off = align256(off + sizeof(float) * (size_t)pl.P * pl.S_stats * 3 * c.d);
@@ -283,7 +291,15 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
   pl.state_stride = (long long)pl.P * pl.wsz;
   off = align256(off + sizeof(float) * (size_t)pl.nb * pl.state_stride);
   pl.off_part = off;
-  off = align256(off + sizeof(float) * (size_t)pl.S_grad * (pl.mfma_grad ? 1 : pl.P) * pl.wsz);
+  off = align256(off + sizeof(float) * (size_t)std::max(pl.S_grad, pl.S_step) * (pl.mfma_grad ? 1 : pl.P) * pl.wsz);
+  if (pl.step_mfma) {
+    const size_t td = sizeof(float) * (size_t)pl.P * pl.span * c.d, th = sizeof(float) * (size_t)pl.P * pl.span * pb.hid;
+    const size_t sz[6] = {td, th, th, th, td, td};
+    for (int i = 0; i < 6; ++i) {
+      pl.off_step[i] = off;
+      off = align256(off + sz[i]);
+    }
+  }
   pl.off_gbuf = off;
   if (!pl.mfma_grad && !pl.lact_grad && !pl.dwconv && !pl.glu_grad)
     off = align256(off + sizeof(float) * (size_t)pl.P * pl.span * c.d);
@@ -420,6 +436,7 @@ const char* ttt_path_name_ex(const ttt_handle* hc, int loss, int inner, int chun
   if (pl.glu_grad && pl.glu_query) return "mfma_glu";
   if (pl.glu_query) return "generic_grad+mfma_glu_query";
   if (pl.mfma_grad && pl.mfma_query) return "mfma";
+  if (pl.step_mfma) return pl.mfma_query ? "mfma_f32_grad+mfma_query" : "mfma_f32_grad";
   if (pl.mfma_query) return "generic_grad+mfma_query";
   if (pl.lact_grad && pl.lact_query) return "mfma_swiglu";
   if (pl.lact_query) return "generic_grad+mfma_swiglu_query";
@@ -535,6 +552,7 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
       // later epochs of a batch read and rewrite state b + 1 in place
       const WRef src = e == 0 ? cur : state_ref(b + 1);
       if (first_step) mark(2);
+      int S_used = pl.S_grad;
       if (pl.dwconv) {
         launch_dwconv_grad(pb, src, pl.S_grad, part, st);
       } else if (pl.glu_grad) {
@@ -546,6 +564,11 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
         // scalar eta and the MSE constant 2/(n_b d) are applied to its partials
         const float scale = pb.loss == LOSS_MSE ? cl.eta->scale * 2.0f / ((float)nt * (float)c.d) : cl.eta->scale;
         launch_mfma_full_grad(pb, src, t0, nt, scale, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part, st);
+      } else if (pl.step_mfma && step_mfma_aligned(src)) {
+        auto sbuf = [&](int i) { return reinterpret_cast<float*>(ws + pl.off_step[i]); };
+        launch_step_mfma(pb, src, t0, nt, StepMfmaBufs{sbuf(0), sbuf(1), sbuf(2), nullptr, sbuf(3), sbuf(4), sbuf(5)},
+                         part, pl.S_step, st);
+        S_used = pl.S_step;
       } else {
         launch_gen_grad_out(pb, src, t0, nt, gbuf, st);
         launch_gen_dW(pb, src, t0, nt, gbuf, pl.S_grad, part, st);
@@ -554,7 +577,7 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
       ua.cur = src;
       ua.part = part;
       ua.part_mode = pl.mfma_grad ? PART_STREAMK : PART_SPLITS;
-      ua.S = pl.S_grad;
+      ua.S = S_used;
       if (pl.mfma_grad) mfma_grad_geometry(pb, nt, &ua.sk_G, &ua.sk_J, &ua.sk_tpp);
       const bool last = last_batch && e == op.epochs - 1;
       for (int i = 0; i < 3; ++i) ua.out[i] = last ? wout[i] : nullptr;
@@ -637,7 +660,7 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
                    L.r[i].model, loss, chunk, pl.nb, op.epochs, range_mask(op.mask, L.r[i]),
                    op.causal ? "causal" : "write-then-query", op.rule,
                    pl.dwconv ? "dwconv" : pl.glu_grad ? "mfma_glu" : pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu"
-                                                                                                          : "generic",
+                                                                       : pl.step_mfma ? "mfma_f32" : "generic",
                    pl.S_grad,
                    pl.dwconv ? "dwconv" : pl.glu_query ? "mfma_glu" : pl.mfma_query ? "mfma" : pl.lact_query ? "mfma_swiglu"
                                                                                                              : "generic",

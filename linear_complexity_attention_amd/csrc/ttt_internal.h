@@ -206,6 +206,17 @@ struct BwdMfmaBufs {
   float *dW, *Ws, *U;                         // [P][2][d h]
   float *knp;                                 // key-norm partials
 };
+// one fp32 inner step of the GELU MLP on tokens [t0, t0 + nt) on the same
+// matrix-core products: X [P][nt][d], Z, A, dZ [P][nt][h], F, G [P][nt][d];
+// dA optional ([P][nt][h], else dZ overwrites it)
+struct StepMfmaBufs {
+  float *X, *Z, *A, *dA, *dZ, *F, *G;
+};
+bool step_mfma_shape(const Problem& pb);
+bool step_mfma_aligned(const WRef& W);
+int step_mfma_splits(const Problem& pb, int nt);
+void launch_step_mfma(const Problem& pb, const WRef& W, int t0, int nt, const StepMfmaBufs& sb, float* part, int KS,
+                      hipStream_t st);
 bool bwd_mfma_supported(const Problem& pb, const WRef& w0);
 void bwd_mfma_sizes(const Problem& pb, BwdMfmaSizes* s);
 void launch_backward_mfma(const Problem& pb, const WRef& w0, const void* dO, const BwdMfmaBufs& bb, float* dq,

@@ -177,11 +177,13 @@ def test_shapes_mlp_mse(d, hidden, N):
 
 
 # the remaining kernel instances and the largest widths: SwiGLU at (d, h) =
-# (64, 256) and (128, 128) (the LaCT kernels' other two shapes), the generic
-# path at h = 512 (the widest supported) and the linear model at d = 128
+# (64, 256) and (128, 128) (the LaCT kernels' other two shapes), the GELU MLP
+# at h = 512 (the widest supported: the fp32 matrix-core step, and the generic
+# kernels when forced) and the linear model at d = 128
 @pytest.mark.parametrize("inner,loss,d,hidden,chunk,renorm,path", [
     ("swiglu", "dot", 64, 256, 100, True, "mfma_swiglu"),
     ("swiglu", "dot", 128, 128, 128, True, "mfma_swiglu"),
+    ("mlp_gelu", "mse", 64, 512, 0, False, "mfma_f32_grad"),
     ("mlp_gelu", "mse", 64, 512, 0, False, "generic"),
     ("linear", "mse", 128, 128, 0, False, "generic"),
 ])
@@ -190,7 +192,9 @@ def test_shapes_other_kernels(inner, loss, d, hidden, chunk, renorm, path):
                  key_norm=(chunk == 0), renorm=renorm, per_token_eta=(loss == "dot"), unit_columns=renorm,
                  seed=11 + d + hidden, eta=0.3 if loss == "dot" else 1.0)
     dev_in, exact = device_inputs(w)
-    _, _, got = _check_pairs(w, dev_in, exact, [(0, 0), (0, 1)], tag=f"{inner} d={d} h={hidden} chunk={chunk}")
+    flags = GENERIC if (inner == "mlp_gelu" and path == "generic") else 0
+    _, _, got = _check_pairs(w, dev_in, exact, [(0, 0), (0, 1)], flags=flags,
+                             tag=f"{inner} d={d} h={hidden} chunk={chunk} {path}")
     assert got == path
 
 
