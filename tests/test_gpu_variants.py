@@ -54,6 +54,16 @@ def _swiglu(dtype="bf16", **kw):
 
 
 # several epochs [ViT3 guideline 2]
+def test_epochs_c3_full_size():
+    """c3 (B=8, H=12, N=6084, d=64, h=256) with three epochs, in the
+    benchmark's configuration: the fp32 matrix-core step at full size, every
+    pair."""
+    from synth_inputs import WORKLOADS
+
+    _check(WORKLOADS["c3_hires_r4"], dict(epochs=3), dict(epochs=3), path="mfma_f32_grad+mfma_query")
+
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_epochs_full_batch(dtype):
     _check(_mlp(dtype), dict(epochs=3), dict(epochs=3))

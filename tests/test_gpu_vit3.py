@@ -92,3 +92,13 @@ def test_dwconv_with_epochs_and_momentum():
     w = Workload("dwe", B=1, H=2, N=150, d=64, hidden=64, inner="dwconv", loss="mse", key_norm=True,
                  grid=(10, 15), conv_k=3, seed=810)
     _check(w, opts=dict(epochs=3, rule="momentum", beta=0.5), okw=dict(epochs=3, rule="momentum", beta=0.5))
+
+
+def test_vit3_block_full_size():
+    """The ViT3 block at 1248^2 in the benchmark's configuration (B=8, H=12,
+    N=6084 on a 78 x 78 raster, d=64, 3 x 3 convolution head, dot loss,
+    eta = 1/N), every pair: the LDS-tiled convolution with a hundred tiles
+    per pair, the GLU kernels' full token splits and the statistics merge."""
+    w = Workload("vit3_hires", B=8, H=12, N=6084, d=64, hidden=64, inner="vit3", loss="dot", key_norm=True,
+                 eta=1.0 / 6084, grid=(78, 78), conv_k=3, seed=1006)
+    _check(w, path="dwconv+mfma_glu")
