@@ -961,10 +961,12 @@ void launch_mfma_query(const Problem& pb, const WRef& w0, const float* states, l
                        int chunk, hipStream_t st) {
   (void)nchunks;
   const int span = chunk ? (chunk < pb.N ? chunk : pb.N) : pb.N;
-  // one workgroup per CU, fewer when there are not 512 tokens for each
+  // one workgroup per CU, fewer when there are not 128 tokens for each (with
+  // many short pairs every CU is worth using: a workgroup's time is mostly
+  // the staging of the weights of the pairs it touches, one per segment)
   const long long T = (long long)pb.B * pb.H * pb.N;
   long long G = device_cu_count();
-  if (G > (T + 511) / 512) G = (T + 511) / 512;
+  if (G > (T + 127) / 128) G = (T + 127) / 128;
   if (G < 1) G = 1;
   switch (pb.hid) {
     case 64: hipLaunchKernelGGL((k_mfma_query<64>), dim3((unsigned)G), dim3(kQW<64> * 64), 0, st, pb, w0, states, state_stride, chunk, span); break;
