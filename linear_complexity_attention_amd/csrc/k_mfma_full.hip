@@ -882,20 +882,30 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
       }
     };
     // Q of the next piece is loaded while the current one is computed; the two
-    // register sets alternate and every piece is a full pass, so the loop has
-    // no branch that leaves a load unconsumed (which would make the compiler
-    // wait for every outstanding load and store before the next prefetch)
+    // register sets alternate and every piece inside the loop is a full pass,
+    // so no path back to the loop head leaves a load unconsumed (that would
+    // make the compiler wait for every outstanding load and store before each
+    // prefetch).  The share's last piece, when shorter than a pass, takes the
+    // shortest pass that covers it (16 or 32 tokens; the share of the last wave
+    // of a segment may end inside a 16-token unit) and leaves the loop; all
+    // these branches are on wave-uniform scalars.
     constexpr int STEP = 16 * QTB;
     bf16x8 qa[QTB][2], qb[QTB][2];
+    auto tail = [&](int pos, const bf16x8 (&q)[QTB][2]) {
+      const int rem = b_ - pos;
+      if (rem <= 16) pass(std::integral_constant<int, 1>{}, pos, q);
+      else if (QTB == 2 || rem <= 32) pass(std::integral_constant<int, 2>{}, pos, q);
+      else pass(std::integral_constant<int, QTB>{}, pos, q);   // rows past the share are clamped
+    };
     int pos = a_;
     if (pos < b_) load_q(pos, qa);
-    // the prefetch is issued unconditionally (past the share it re-reads the
-    // share's last row), so every path through the loop has the same loads
     while (pos < b_) {
-      load_q(pos + STEP, qb);
+      if (b_ - pos < STEP) { tail(pos, qa); break; }
+      load_q(pos + STEP, qb);          // past the share it re-reads the share's last row
       pass(std::integral_constant<int, QTB>{}, pos, qa);
       pos += STEP;
       if (pos >= b_) break;
+      if (b_ - pos < STEP) { tail(pos, qb); break; }
       load_q(pos + STEP, qa);
       pass(std::integral_constant<int, QTB>{}, pos, qb);
       pos += STEP;
