@@ -272,10 +272,10 @@ __device__ __forceinline__ void chan_merge(float& cn, float& mean, float& m2, fl
 // The gelu' polynomial runs on the consumers: the producers' GELU arithmetic
 // is the critical path, the consumers have slack.
 // Buffers: K tiles x4, V tiles x3, A' x3, w x3, G' x2.
-template <int HID, int LOSS, bool KNORM, int NW>
+template <int HID, int LOSS, bool KNORM, int NW, bool DIRECT>
 __global__ void __launch_bounds__(128 * NW, kGradBlocksPerCU<HID> * NW / 2)   // threads, waves per SIMD
 k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float* __restrict__ spart, int S_stats,
-            float eps, float* __restrict__ part) {
+            float eps, float* __restrict__ part, GradDirect dw) {
   typedef typename std::conditional<KNORM, f16, bf16>::type KT;
   typedef typename Vec<KT>::v8 k8;
   constexpr int NTH = 128 * NW;        // threads
@@ -676,8 +676,8 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       // instruction writes 1 KB contiguously.  With G' the negated gradient,
       // acc2 holds A'^T G' = -sqrt(2) A^T G and acc1 holds K_hat^T dZ' =
       // K_hat^T dZ / sqrt(2).
-      f32x4* out = reinterpret_cast<f32x4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
       const float scale1 = scale * kSqrt2, scale2 = -scale * kRSqrt2;
+      f32x4* out = reinterpret_cast<f32x4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -686,6 +686,46 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) out[D * HID / 4 + ((q * NHB + hb) * 4 + cb) * 64 + lane] = scale2 * acc2[hb][cb];
+    }
+    if constexpr (DIRECT) {
+      // direct mode (the segment is the whole pair): after the barrier every
+      // thread of the workgroup takes float4s of the pair's partial, which
+      // this workgroup just wrote (L2-resident), and applies W* = W - dW to
+      // the 4 weights each maps to (partial layout above), in the natural
+      // layouts W1 [c][h] and W2 [h][c]
+      __syncthreads();
+      const float4* pin = reinterpret_cast<const float4*>(part + (long long)blockIdx.x * J * (2LL * D * HID));
+      const float* Wm[2] = {W1, W.mat(1, bb, hh_)};
+      float* nx = dw.next + (long long)p * 2 * D * HID;
+      constexpr int HALF = D * HID / 4;
+      for (int jj = tid; jj < 2 * HALF; jj += NTH) {
+        const int mat = jj >= HALF ? 1 : 0;
+        const int jl = jj - mat * HALF, l = jl & 63, blk = jl >> 6, gg = l >> 4, rr = l & 15;
+        int base, step;
+        if (mat == 0) {
+          const int hb = blk % NHB, cb = (blk / NHB) & 3, qq = blk / (4 * NHB);
+          base = (16 * cb + 4 * gg) * HID + qq * HP + 16 * hb + rr;
+          step = HID;
+        } else {
+          const int cb = blk & 3, hb = (blk >> 2) % NHB, qq = blk / (4 * NHB);
+          base = (qq * HP + 16 * hb + 4 * gg) * D + 16 * cb + rr;
+          step = D;
+        }
+        const float4 d = pin[jj];
+        const float* wc = Wm[mat];
+        const float dv[4] = {d.x, d.y, d.z, d.w};
+        float wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[i] = wc[base + i * step];
+        float* nm = nx + mat * D * HID;
+        float* om = dw.out[mat] ? dw.out[mat] + pb.row(p) * D * HID : nullptr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = wv[i] - dv[i];
+          nm[base + i * step] = x;
+          if (om) om[base + i * step] = x;
+        }
+      }
     }
     x = seg_end;
   }
@@ -917,26 +957,32 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
   }
 }
 
-template <int HID>
-void launch_grad_h(const Problem& pb, const WRef& W, int t0, int nt, int G, int J, float scale,
-                   const float* spart, int S_stats, float eps, float* part, hipStream_t st) {
+template <int HID, bool DIRECT>
+void launch_grad_hd(const Problem& pb, const WRef& W, int t0, int nt, int G, int J, float scale,
+                    const float* spart, int S_stats, float eps, float* part, const GradDirect& dw, hipStream_t st) {
   constexpr int NW = kGradWaves<HID>;
   const dim3 grid(G), block(128 * NW);
   if (pb.loss == LOSS_MSE) {
     if (spart)
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, true, NW>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
-                         S_stats, eps, part);
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, true, NW, DIRECT>), grid, block, 0, st, pb, W, t0, nt, J, scale,
+                         spart, S_stats, eps, part, dw);
     else
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, false, NW>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
-                         S_stats, eps, part);
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_MSE, false, NW, DIRECT>), grid, block, 0, st, pb, W, t0, nt, J, scale,
+                         spart, S_stats, eps, part, dw);
   } else {
     if (spart)
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, true, NW>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
-                         S_stats, eps, part);
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, true, NW, DIRECT>), grid, block, 0, st, pb, W, t0, nt, J, scale,
+                         spart, S_stats, eps, part, dw);
     else
-      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, false, NW>), grid, block, 0, st, pb, W, t0, nt, J, scale, spart,
-                         S_stats, eps, part);
+      hipLaunchKernelGGL((k_mfma_grad<HID, LOSS_DOT, false, NW, DIRECT>), grid, block, 0, st, pb, W, t0, nt, J, scale,
+                         spart, S_stats, eps, part, dw);
   }
+}
+template <int HID>
+void launch_grad_h(const Problem& pb, const WRef& W, int t0, int nt, int G, int J, float scale,
+                   const float* spart, int S_stats, float eps, float* part, const GradDirect& dw, hipStream_t st) {
+  if (dw.next) launch_grad_hd<HID, true>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, dw, st);
+  else launch_grad_hd<HID, false>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, dw, st);
 }
 
 }  // namespace
@@ -956,14 +1002,33 @@ void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_pe
   sk_geometry(P, tpp, (long long)device_cu_count() * (pb.hid == 64 ? kGradBlocksPerCU<64> : 1), G, J);
 }
 
+// one pair per workgroup in a single round that fills at least half the
+// slots (measured on the ViT-S shape, 384 pairs of 196 tokens: at width 64,
+// one round of 384 of 512 slots, 49 -> 43 us per step; at width 256 the two
+// rounds of 384 over 256 slots only matched the stream-K split)
+bool mfma_grad_direct_fits(const Problem& pb) {
+  const long long slots = (long long)device_cu_count() * (pb.hid == 64 ? kGradBlocksPerCU<64> : 1);
+  const long long P = (long long)pb.B * pb.H;
+  return 2 * P >= slots && P <= slots;
+}
+
 void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, float scale, const float* spart,
-                           int S_stats, float eps, float* part, hipStream_t st) {
+                           int S_stats, float eps, float* part, const GradDirect* direct, hipStream_t st) {
   int G, J, tpp;
-  mfma_grad_geometry(pb, nt, &G, &J, &tpp);
+  GradDirect dw{nullptr, {nullptr, nullptr}};
+  if (direct) {
+    // G = pairs: on the stream-K cost line every workgroup's range is then
+    // exactly one pair's tiles
+    dw = *direct;
+    G = pb.B * pb.H;
+    J = 1;
+  } else {
+    mfma_grad_geometry(pb, nt, &G, &J, &tpp);
+  }
   switch (pb.hid) {
-    case 64: launch_grad_h<64>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
-    case 128: launch_grad_h<128>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
-    default: launch_grad_h<256>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, st); break;
+    case 64: launch_grad_h<64>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, dw, st); break;
+    case 128: launch_grad_h<128>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, dw, st); break;
+    default: launch_grad_h<256>(pb, W, t0, nt, G, J, scale, spart, S_stats, eps, part, dw, st); break;
   }
 }
 

@@ -124,6 +124,7 @@ struct Plan {
   bool dwconv;                       // depthwise-convolution kernels
   bool glu_grad, glu_query;          // GLU MFMA kernels
   bool step_mfma;                    // fp32 GELU-MLP step on the matrix cores (else k_gen_*)
+  bool mfma_direct;                  // MFMA gradient kernel with one workgroup per pair, writing W* itself
   int S_stats, S_grad;               // S_grad: partial slots of the gradient kernel
   int S_step;                        // token slices of the fp32 matrix-core step
   int sk_G, sk_J;                    // stream-K geometry (MFMA gradient kernel)
@@ -253,6 +254,11 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
   const bool fast = !generic_only && pb.full_heads();
   pl.dwconv = pb.inner == INNER_DWCONV;
   pl.mfma_grad = fast && mfma_full_supported(pb) && pl.nb == 1 && op.epochs == 1;
+  // a plain gradient step of every matrix with many pairs: the gradient
+  // kernel takes whole pairs and applies the step itself (no partials, no
+  // update kernel)
+  pl.mfma_direct = pl.mfma_grad && op.rule == RULE_GD && !c.renorm && (op.mask & 3u) == 3u &&
+                   mfma_grad_direct_fits(pb);
   pl.mfma_query = fast && mfma_query_supported(pb);
   pl.lact_grad = fast && !c.key_norm && lact_supported(pb);
   pl.lact_query = fast && lact_readout_supported(pb);
@@ -274,6 +280,7 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
     int tpp_unused;
     mfma_grad_geometry(pb, pl.span, &pl.sk_G, &pl.sk_J, &tpp_unused);
     pl.S_grad = pl.sk_G * pl.sk_J;   // partial slots
+    if (pl.mfma_direct && pl.S_grad < pl.P) pl.S_grad = pl.P;   // direct mode: one slot per pair
   } else {
     pl.S_grad = choose_splits((long long)pl.P * ((pb.hid + 31) / 32), pl.span, 16, 1024);
   }
@@ -563,7 +570,9 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
         // the kernel accumulates eta_n-weighted (V_hat - V) or -eta_n V; the
         // scalar eta and the MSE constant 2/(n_b d) are applied to its partials
         const float scale = pb.loss == LOSS_MSE ? cl.eta->scale * 2.0f / ((float)nt * (float)c.d) : cl.eta->scale;
-        launch_mfma_full_grad(pb, src, t0, nt, scale, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part, st);
+        const GradDirect gd{next, {wout[0], wout[1]}};
+        launch_mfma_full_grad(pb, src, t0, nt, scale, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part,
+                              pl.mfma_direct ? &gd : nullptr, st);
       } else if (pl.step_mfma && step_mfma_aligned(src)) {
         auto sbuf = [&](int i) { return reinterpret_cast<float*>(ws + pl.off_step[i]); };
         launch_step_mfma(pb, src, t0, nt, StepMfmaBufs{sbuf(0), sbuf(1), sbuf(2), nullptr, sbuf(3), sbuf(4), sbuf(5)},
@@ -574,6 +583,11 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
         launch_gen_dW(pb, src, t0, nt, gbuf, pl.S_grad, part, st);
       }
       if (first_step) mark(3);
+      if (pl.mfma_direct) {           // the gradient kernel has written W* (and W_out)
+        if (first_step) { mark(4); mark(5); }
+        first_step = false;
+        continue;
+      }
       ua.cur = src;
       ua.part = part;
       ua.part_mode = pl.mfma_grad ? PART_STREAMK : PART_SPLITS;
@@ -659,7 +673,8 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
                    c.B, c.H, L.r[i].h0, L.r[i].h0 + L.r[i].hc - 1, c.N, c.d, pl.hid, c.dtype == TTT_BF16 ? "bf16" : "f32",
                    L.r[i].model, loss, chunk, pl.nb, op.epochs, range_mask(op.mask, L.r[i]),
                    op.causal ? "causal" : "write-then-query", op.rule,
-                   pl.dwconv ? "dwconv" : pl.glu_grad ? "mfma_glu" : pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu"
+                   pl.dwconv ? "dwconv" : pl.glu_grad ? "mfma_glu" : pl.mfma_direct ? "mfma_direct"
+                   : pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu"
                                                                        : pl.step_mfma ? "mfma_f32" : "generic",
                    pl.S_grad,
                    pl.dwconv ? "dwconv" : pl.glu_query ? "mfma_glu" : pl.mfma_query ? "mfma" : pl.lact_query ? "mfma_swiglu"

@@ -137,8 +137,18 @@ bool mfma_full_supported(const Problem& pb);
 // (at three waves per SIMD the consumers spill registers).
 constexpr int mfma_grad_waves(int /*hid*/) { return 4; }
 void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_per_pair);
+// Direct mode: one workgroup per pair (grid = pairs), so each workgroup holds
+// its pair's whole gradient and applies the plain gradient step itself,
+// W* = W - dW, to `next` (the [P][2][d*hid] fp32 state, natural layouts) and,
+// when given, to the caller's W_out matrices (rows pb.row(p)); no partials.
+// It is taken when the pairs fill between half and all of the workgroup slots
+// in one round (many short pairs: the split-N partials and the update kernel
+// would outweigh the work).  The workgroup stores its partial like a stream-K
+// slot and, after a barrier, all its threads apply the step from it.
+struct GradDirect { float* next; float* out[2]; };
+bool mfma_grad_direct_fits(const Problem& pb);
 void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, float scale, const float* spart,
-                           int S_stats, float eps, float* part, hipStream_t st);
+                           int S_stats, float eps, float* part, const GradDirect* direct, hipStream_t st);
 // readout O = F_W(Q) on bf16 MFMA from fp32 states: full batch reads state 1,
 // causal chunk c reads state c (state 0 = w0, state s >= 1 at
 // states + (s-1)*state_stride, layout [P][nm][msz]).

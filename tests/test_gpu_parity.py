@@ -14,6 +14,7 @@ from tests.gpu_common import TOL, device_inputs, rel_err, run_gpu, run_oracle
 pytestmark = pytest.mark.gpu
 
 GENERIC = 0x2   # TTT_FLAG_FORCE_GENERIC
+LOG = 0x4       # TTT_FLAG_LOG
 
 
 def _w0_pair(exact, b, h):
@@ -166,6 +167,24 @@ def test_mfma_mlp_instances(hidden, loss, key_norm):
     dev_in, exact = device_inputs(w)
     _, _, path = _check_pairs(w, dev_in, exact, None, tag=f"h={hidden} {loss} kn={key_norm}")
     assert path == "mfma"
+
+
+# the direct mode of the same kernel (one workgroup per pair, which applies the
+# gradient step itself): as many pairs as CUs, ragged N, every instance;
+# sampled pairs (first, last and scattered), O and dW
+@pytest.mark.parametrize("hidden", [64, 128, 256])
+@pytest.mark.parametrize("loss", ["mse", "dot"])
+@pytest.mark.parametrize("key_norm", [False, True])
+def test_mfma_direct_instances(hidden, loss, key_norm, capfd):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    w = Workload("direct", B=cus // 8, H=8, N=77, d=64, hidden=hidden, loss=loss, key_norm=key_norm,
+                 per_token_eta=(loss == "dot"), seed=700 + hidden + 2 * key_norm,
+                 eta=1.0 if loss == "mse" else 0.05)
+    dev_in, exact = device_inputs(w)
+    pairs = [(0, 0), (1, 3), (w.B // 2, 5), (w.B - 1, 7)]
+    _, _, path = _check_pairs(w, dev_in, exact, pairs, flags=LOG, tag=f"direct h={hidden} {loss} kn={key_norm}")
+    assert path == "mfma"
+    assert "grad=mfma_direct" in capfd.readouterr().err
 
 
 @pytest.mark.parametrize("d,hidden,N", [(32, 32, 256), (64, 64, 130), (64, 256, 517), (128, 256, 300),
