@@ -687,21 +687,23 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) out[D * HID / 4 + ((q * NHB + hb) * 4 + cb) * 64 + lane] = scale2 * acc2[hb][cb];
     }
-    if constexpr (DIRECT) {
-      // direct mode (the segment is the whole pair): after the barrier every
-      // thread of the workgroup takes float4s of the pair's partial, which
-      // this workgroup just wrote (L2-resident), and applies W* = W - dW to
-      // the 4 weights each maps to (partial layout above), in the natural
+    if (DIRECT && tile0 == 0 && n == tpp) {
+      // direct step (this segment is the whole pair): after the barrier
+      // every thread of the workgroup takes float4s of the pair's partial,
+      // which this workgroup just wrote (L2-resident), and applies W* = W - dW
+      // to the 4 weights each maps to (partial layout above), in the natural
       // layouts W1 [c][h] and W2 [h][c]
       __syncthreads();
-      const float4* pin = reinterpret_cast<const float4*>(part + (long long)blockIdx.x * J * (2LL * D * HID));
+      const float4* pin =
+          reinterpret_cast<const float4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
       const float* Wm[2] = {W1, W.mat(1, bb, hh_)};
       float* nx = dw.next + (long long)p * 2 * D * HID;
       constexpr int HALF = D * HID / 4;
-      for (int jj = tid; jj < 2 * HALF; jj += NTH) {
-        const int mat = jj >= HALF ? 1 : 0;
+      // float4 jj of the partial -> element offset of its i = 0 weight in
+      // matrix jj / HALF and the stride over i
+      auto map = [&](int jj, int& mat, int& base, int& step) {
+        mat = jj >= HALF ? 1 : 0;
         const int jl = jj - mat * HALF, l = jl & 63, blk = jl >> 6, gg = l >> 4, rr = l & 15;
-        int base, step;
         if (mat == 0) {
           const int hb = blk % NHB, cb = (blk / NHB) & 3, qq = blk / (4 * NHB);
           base = (16 * cb + 4 * gg) * HID + qq * HP + 16 * hb + rr;
@@ -711,19 +713,40 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           base = (qq * HP + 16 * hb + 4 * gg) * D + 16 * cb + rr;
           step = D;
         }
-        const float4 d = pin[jj];
-        const float* wc = Wm[mat];
-        const float dv[4] = {d.x, d.y, d.z, d.w};
-        float wv[4];
+      };
+      // eight float4s per thread at a time, every load of the batch issued
+      // before its stores (the stores may alias the loads in the compiler's
+      // view, so a plain loop would wait for each iteration's loads)
+      // the thread index passes through an empty asm statement, so that the
+      // compiler cannot hoist the (segment-invariant) index arithmetic below
+      // to the kernel entry and keep it in registers through the main loops
+      int tid_o = tid;
+      asm volatile("" : "+v"(tid_o));
+      constexpr int PER = 2 * HALF / NTH, UB = PER < 8 ? PER : 8;
+      static_assert(2 * HALF % (NTH * UB) == 0, "the partial splits evenly into batches");
+      for (int j0 = 0; j0 < PER; j0 += UB) {
+        float4 dv[UB];
+        float wv[UB][4];
+        int mat[UB], base[UB], step[UB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wv[i] = wc[base + i * step];
-        float* nm = nx + mat * D * HID;
-        float* om = dw.out[mat] ? dw.out[mat] + pb.row(p) * D * HID : nullptr;
+        for (int u = 0; u < UB; ++u) {
+          const int jj = tid_o + NTH * (j0 + u);
+          map(jj, mat[u], base[u], step[u]);
+          dv[u] = pin[jj];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = wv[i] - dv[i];
-          nm[base + i * step] = x;
-          if (om) om[base + i * step] = x;
+          for (int i = 0; i < 4; ++i) wv[u][i] = Wm[mat[u]][base[u] + i * step[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+          float* nm = nx + mat[u] * D * HID;
+          float* om = dw.out[mat[u]] ? dw.out[mat[u]] + pb.row(p) * D * HID : nullptr;
+          const float d4[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = wv[u][i] - d4[i];
+            nm[base[u] + i * step[u]] = x;
+            if (om) om[base[u] + i * step[u]] = x;
+          }
         }
       }
     }
@@ -1012,14 +1035,28 @@ bool mfma_grad_direct_fits(const Problem& pb) {
   return 2 * P >= slots && P <= slots;
 }
 
+long long mfma_grad_split_pairs(const Problem& pb, int nt) {
+  int G, J, tpp;
+  mfma_grad_geometry(pb, nt, &G, &J, &tpp);
+  const long long P = (long long)pb.B * pb.H, C = P * (tpp + kSkAlpha);
+  long long split = 0;
+  for (long long p = 0; p < P; ++p) {
+    long long q0, q1;
+    sk_pair_groups(p, tpp, G, C, &q0, &q1);
+    split += q0 != q1;
+  }
+  return split;
+}
+
 void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, float scale, const float* spart,
-                           int S_stats, float eps, float* part, const GradDirect* direct, hipStream_t st) {
+                           int S_stats, float eps, float* part, const GradDirect* direct, bool one_round,
+                           hipStream_t st) {
   int G, J, tpp;
   GradDirect dw{nullptr, {nullptr, nullptr}};
-  if (direct) {
+  if (direct) dw = *direct;
+  if (one_round) {
     // G = pairs: on the stream-K cost line every workgroup's range is then
     // exactly one pair's tiles
-    dw = *direct;
     G = pb.B * pb.H;
     J = 1;
   } else {

@@ -137,6 +137,7 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
   const bool upd = (a.mask >> mat) & 1u;
   long long q0, q1, C;
   sk_range(a, pb.B * pb.H, p, q0, q1, C);
+  if (a.sk_direct && q0 == q1) return;   // one workgroup held the whole pair and wrote its step
   if (!upd) q1 = q0 - 1;          // a matrix outside the mask keeps W_cur
   // the pair's slots, four loads in flight at a time, added in workgroup order
   float4 sum = {0.f, 0.f, 0.f, 0.f};

@@ -124,7 +124,9 @@ struct Plan {
   bool dwconv;                       // depthwise-convolution kernels
   bool glu_grad, glu_query;          // GLU MFMA kernels
   bool step_mfma;                    // fp32 GELU-MLP step on the matrix cores (else k_gen_*)
-  bool mfma_direct;                  // MFMA gradient kernel with one workgroup per pair, writing W* itself
+  bool mfma_direct;                  // the MFMA gradient kernel applies the step to every whole pair
+  bool mfma_one_round;               // ... with one workgroup per pair
+  bool mfma_split;                   // ... and some pair is split (the update kernel finishes those)
   int S_stats, S_grad;               // S_grad: partial slots of the gradient kernel
   int S_step;                        // token slices of the fp32 matrix-core step
   int sk_G, sk_J;                    // stream-K geometry (MFMA gradient kernel)
@@ -257,8 +259,12 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
   // a plain gradient step of every matrix with many pairs: the gradient
   // kernel takes whole pairs and applies the step itself (no partials, no
   // update kernel)
-  pl.mfma_direct = pl.mfma_grad && op.rule == RULE_GD && !c.renorm && (op.mask & 3u) == 3u &&
-                   mfma_grad_direct_fits(pb);
+  if (pl.mfma_grad && op.rule == RULE_GD && !c.renorm && (op.mask & 3u) == 3u) {
+    pl.mfma_one_round = mfma_grad_direct_fits(pb);
+    const long long split = pl.mfma_one_round ? 0 : mfma_grad_split_pairs(pb, pl.span);
+    pl.mfma_direct = split < pl.P;     // some pair is whole
+    pl.mfma_split = split > 0;
+  }
   pl.mfma_query = fast && mfma_query_supported(pb);
   pl.lact_grad = fast && !c.key_norm && lact_supported(pb);
   pl.lact_query = fast && lact_readout_supported(pb);
@@ -280,7 +286,7 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
     int tpp_unused;
     mfma_grad_geometry(pb, pl.span, &pl.sk_G, &pl.sk_J, &tpp_unused);
     pl.S_grad = pl.sk_G * pl.sk_J;   // partial slots
-    if (pl.mfma_direct && pl.S_grad < pl.P) pl.S_grad = pl.P;   // direct mode: one slot per pair
+    if (pl.mfma_one_round && pl.S_grad < pl.P) pl.S_grad = pl.P;   // one slot per pair
   } else {
     pl.S_grad = choose_splits((long long)pl.P * ((pb.hid + 31) / 32), pl.span, 16, 1024);
   }
@@ -572,7 +578,7 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
         const float scale = pb.loss == LOSS_MSE ? cl.eta->scale * 2.0f / ((float)nt * (float)c.d) : cl.eta->scale;
         const GradDirect gd{next, {wout[0], wout[1]}};
         launch_mfma_full_grad(pb, src, t0, nt, scale, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part,
-                              pl.mfma_direct ? &gd : nullptr, st);
+                              pl.mfma_direct ? &gd : nullptr, pl.mfma_one_round, st);
       } else if (pl.step_mfma && step_mfma_aligned(src)) {
         auto sbuf = [&](int i) { return reinterpret_cast<float*>(ws + pl.off_step[i]); };
         launch_step_mfma(pb, src, t0, nt, StepMfmaBufs{sbuf(0), sbuf(1), sbuf(2), nullptr, sbuf(3), sbuf(4), sbuf(5)},
@@ -583,7 +589,7 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
         launch_gen_dW(pb, src, t0, nt, gbuf, pl.S_grad, part, st);
       }
       if (first_step) mark(3);
-      if (pl.mfma_direct) {           // the gradient kernel has written W* (and W_out)
+      if (pl.mfma_direct && !pl.mfma_split) {   // the gradient kernel has written W* (and W_out)
         if (first_step) { mark(4); mark(5); }
         first_step = false;
         continue;
@@ -593,6 +599,7 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
       ua.part_mode = pl.mfma_grad ? PART_STREAMK : PART_SPLITS;
       ua.S = S_used;
       if (pl.mfma_grad) mfma_grad_geometry(pb, nt, &ua.sk_G, &ua.sk_J, &ua.sk_tpp);
+      ua.sk_direct = pl.mfma_direct;
       const bool last = last_batch && e == op.epochs - 1;
       for (int i = 0; i < 3; ++i) ua.out[i] = last ? wout[i] : nullptr;
       ua.mom_only = op.rule == RULE_MUON;

@@ -63,6 +63,7 @@ struct UpdateArgs {
                                 // (see k_update_streamk)
   int S; long long part_pair_stride;
   int sk_G, sk_J, sk_tpp;       // stream-K geometry of the gradient kernel
+  int sk_direct;                // the gradient kernel applied the step to every whole pair: skip those
   float* next;                  // [P][nm][msz] fp32 (may alias cur: every element is read, then written, by one thread)
   float* out[3];                // W_out matrices [B,H,in,out] or null
   int renorm;
@@ -137,18 +138,23 @@ bool mfma_full_supported(const Problem& pb);
 // (at three waves per SIMD the consumers spill registers).
 constexpr int mfma_grad_waves(int /*hid*/) { return 4; }
 void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_per_pair);
-// Direct mode: one workgroup per pair (grid = pairs), so each workgroup holds
-// its pair's whole gradient and applies the plain gradient step itself,
-// W* = W - dW, to `next` (the [P][2][d*hid] fp32 state, natural layouts) and,
-// when given, to the caller's W_out matrices (rows pb.row(p)); no partials.
-// It is taken when the pairs fill between half and all of the workgroup slots
-// in one round (many short pairs: the split-N partials and the update kernel
-// would outweigh the work).  The workgroup stores its partial like a stream-K
-// slot and, after a barrier, all its threads apply the step from it.
+// Direct step: a workgroup whose range holds a whole pair applies the plain
+// gradient step to it itself, W* = W - dW, writing `next` (the [P][2][d*hid]
+// fp32 state, natural layouts) and, when given, the caller's W_out matrices
+// (rows pb.row(p)); it stores the pair's partial like any slot and, after a
+// barrier, all its threads apply the step from it.  The update kernel then
+// skips those pairs (UpdateArgs::sk_direct), and is not launched when no pair
+// is split.  With one_round the grid is one workgroup per pair, every pair
+// is whole; it is taken when the pairs fill between half and all of the
+// workgroup slots in one round (many short pairs: the split-N partials and
+// the update kernel would outweigh the work).
 struct GradDirect { float* next; float* out[2]; };
 bool mfma_grad_direct_fits(const Problem& pb);
+// pairs of the stream-K split whose tiles more than one workgroup holds
+long long mfma_grad_split_pairs(const Problem& pb, int nt);
 void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, float scale, const float* spart,
-                           int S_stats, float eps, float* part, const GradDirect* direct, hipStream_t st);
+                           int S_stats, float eps, float* part, const GradDirect* direct, bool one_round,
+                           hipStream_t st);
 // readout O = F_W(Q) on bf16 MFMA from fp32 states: full batch reads state 1,
 // causal chunk c reads state c (state 0 = w0, state s >= 1 at
 // states + (s-1)*state_stride, layout [P][nm][msz]).

@@ -187,6 +187,23 @@ def test_mfma_direct_instances(hidden, loss, key_norm, capfd):
     assert "grad=mfma_direct" in capfd.readouterr().err
 
 
+# the direct step inside the stream-K split: more pairs than slots, short
+# pairs, so some workgroups hold whole pairs (stepped by the gradient kernel)
+# and others split pairs (finished by the update kernel); every 7th pair
+@pytest.mark.parametrize("hidden,loss,key_norm", [(64, "mse", True), (256, "mse", True), (128, "dot", False)])
+def test_mfma_direct_mixed(hidden, loss, key_norm, capfd):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pairs_per_slot = 2.5 if hidden == 64 else 1.25
+    w = Workload("direct_mixed", B=int(cus * pairs_per_slot) // 8, H=8, N=100, d=64, hidden=hidden, loss=loss,
+                 key_norm=key_norm, per_token_eta=(loss == "dot"), seed=730 + hidden,
+                 eta=1.0 if loss == "mse" else 0.05)
+    dev_in, exact = device_inputs(w)
+    pairs = [divmod(i, w.H) for i in range(0, w.B * w.H, 7)]
+    _, _, path = _check_pairs(w, dev_in, exact, pairs, flags=LOG, tag=f"direct mixed h={hidden} {loss}")
+    assert path == "mfma"
+    assert "grad=mfma_direct" in capfd.readouterr().err
+
+
 @pytest.mark.parametrize("d,hidden,N", [(32, 32, 256), (64, 64, 130), (64, 256, 517), (128, 256, 300),
                                         (16, 48, 77), (64, 192, 250)])
 def test_shapes_mlp_mse(d, hidden, N):
