@@ -786,6 +786,12 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
   constexpr int L2 = 80;                 // [h][c] row stride
   __shared__ __attribute__((aligned(16))) bf16 w1b[2][D * L1];
   __shared__ __attribute__((aligned(16))) f16 w2b[2][HID * L2];
+  // per-wave staging of a 16-token output block (16 rows of 128 bytes, the
+  // 16-byte chunks of row t XOR-permuted by t & 7), so that each output store
+  // writes 8 whole rows (1 KB) instead of 32 bytes of 16 rows; at width 256
+  // the weight buffers leave no room for it
+  constexpr bool kStageO = HID <= 128;
+  __shared__ __attribute__((aligned(16))) bf16 ob[kStageO ? QW : 1][kStageO ? 16 * D : 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int N = pb.N;
@@ -938,10 +944,29 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
       // so storing it there rewrites identical values: no branch
 #pragma unroll
       for (int tb = 0; tb < NTB; ++tb) {
-        const int n = min(pos + 16 * tb + r, b_ - 1);
+        if constexpr (kStageO) {
+          // lane (g, r) holds channels 16 cb + 4 g .. + 3 of token r; through
+          // the wave's LDS block, lane l then takes channels 8 (l & 7) .. + 7
+          // of token (l >> 3) + 8 k (the wave's own LDS operations are done
+          // in order: no barrier)
+          bf16* sb = ob[w];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = pack4(o[cb][tb]);
+          for (int cb = 0; cb < 4; ++cb)
+            *reinterpret_cast<bf16x4*>(sb + r * D + (((2 * cb + (g >> 1)) ^ (r & 7)) << 3) + 4 * (g & 1)) =
+                pack4(o[cb][tb]);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int t = (lane >> 3) + 8 * k, c = lane & 7;
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(sb + t * D + ((c ^ (t & 7)) << 3));
+            const int n = min(pos + 16 * tb + t, b_ - 1);
+            *reinterpret_cast<bf16x8*>(op + (long long)n * D + 8 * c) = v;
+          }
+        } else {
+          const int n = min(pos + 16 * tb + r, b_ - 1);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = pack4(o[cb][tb]);
+        }
       }
     };
     // Q of the next piece is loaded while the current one is computed; the two
