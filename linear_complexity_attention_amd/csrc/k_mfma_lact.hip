@@ -227,6 +227,10 @@ k_lact_readout(Problem pb, WRef w0, const float* __restrict__ states, long long 
   __shared__ __attribute__((aligned(16))) bf16 w1s[D * L1];
   __shared__ __attribute__((aligned(16))) bf16 w3s[D * L1];
   __shared__ __attribute__((aligned(16))) bf16 w2s[HH * L2];
+  // per-wave staging of a 16-token output block (16 rows of D bf16, the
+  // 16-byte chunks of row t XOR-permuted by t & 7), so that each output store
+  // writes whole rows (1 KB contiguous) instead of 32 bytes of 16 rows
+  __shared__ __attribute__((aligned(16))) bf16 ob[RW][16 * D];
   // XCD-aware work mapping: workgroups are dealt to the 8 XCDs round-robin, so
   // the work index L gives consecutive L (the groups of one (pair, chunk),
   // which read the same weight state) to workgroups of one XCD and its L2
@@ -336,17 +340,27 @@ k_lact_readout(Problem pb, WRef w0, const float* __restrict__ states, long long 
       }
     }
   }
+  // lane (g, r) holds channels 16 cb + 4 g .. + 3 of token r; through the
+  // wave's LDS block, lane l then takes the 16-byte chunk l % (D / 8) of token
+  // l / (D / 8) + k 64 / (D / 8) (the wave's own LDS operations are done in
+  // order: no barrier)
+  constexpr int ROWC = D / 8, RPI = 64 / ROWC;
+  bf16* sb = ob[w];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    const int n = base + 16 * tb + r;
-    if (n < n1) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        bf16x4 v;
+    for (int cb = 0; cb < NCB; ++cb) {
+      bf16x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = (bf16)o[cb][tb][i];
-        *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = v;
-      }
+      for (int i = 0; i < 4; ++i) v[i] = (bf16)o[cb][tb][i];
+      *reinterpret_cast<bf16x4*>(sb + r * D + (((2 * cb + (g >> 1)) ^ (r & 7)) << 3) + 4 * (g & 1)) = v;
+    }
+#pragma unroll
+    for (int k = 0; k < 16 / RPI; ++k) {
+      const int t = lane / ROWC + RPI * k, c = lane % ROWC;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(sb + t * D + ((c ^ (t & 7)) << 3));
+      const int n = base + 16 * tb + t;
+      if (n < n1) *reinterpret_cast<bf16x8*>(op + (long long)n * D + 8 * c) = v;
     }
   }
 }
