@@ -8,6 +8,11 @@
 //     writes is below G*J and is written once, each workgroup touches at most
 //     J pairs, and the update kernel reads back exactly the slots that were
 //     written for each pair, from workgroups q0..q1.  Integer work: bit-exact.
+//     For the direct gradient step: a pair is held whole by one workgroup
+//     (the kernel's own test: a segment from the pair's first to its last
+//     tile) exactly when its first and last workgroups coincide (q0 == q1,
+//     the test the update kernel and the host use to skip it), and with one
+//     workgroup per pair (G = P) workgroup q's range is exactly pair q.
 //  2. The C ABI's host-side validation and workspace planning: bad configs and
 //     bad forward arguments are rejected with the right status before anything
 //     is enqueued, workspace sizes are 256-byte multiples, path names resolve.
@@ -49,6 +54,7 @@ static void check_streamk(long long P, int tpp, long long target) {
   const long long C = P * (tpp + kSkAlpha);
   std::vector<int> covered((size_t)(P * tpp), 0);
   std::vector<long long> slot_pair((size_t)G * J, -1);   // pair whose partial a slot holds
+  std::vector<char> whole((size_t)P, 0);                 // some workgroup holds the pair entirely
   long long prev_end = 0;
   for (long long q = 0; q < G; ++q) {
     // as the gradient kernel: its tile range and segments
@@ -70,6 +76,7 @@ static void check_streamk(long long P, int tpp, long long target) {
       CHECK(slot_pair[(size_t)slot] == -1, "slot %lld written twice", slot);
       slot_pair[(size_t)slot] = p;
       for (long long t = x; t < seg_end; ++t) covered[(size_t)t]++;
+      if (x == p * tpp && seg_end == (p + 1) * tpp) whole[(size_t)p] = 1;
       ++pairs;
       x = seg_end;
     }
@@ -85,6 +92,8 @@ static void check_streamk(long long P, int tpp, long long target) {
     long long q0, q1;
     sk_pair_groups(p, tpp, G, C, &q0, &q1);
     CHECK(0 <= q0 && q0 <= q1 && q1 < G, "pair %lld groups [%lld, %lld]", p, q0, q1);
+    CHECK((q0 == q1) == (whole[(size_t)p] != 0), "pair %lld: q0 %lld q1 %lld but held whole: %d (P=%lld tpp=%d G=%d)",
+          p, q0, q1, (int)whole[(size_t)p], P, tpp, G);
     for (long long q = q0; q <= q1; ++q) {
       const long long s = sk_slot(p, q, q0, G, C, tpp, J);
       CHECK(s >= 0 && s < (long long)G * J, "pair %lld q %lld slot %lld out of range", p, q, s);
@@ -100,7 +109,21 @@ static void check_streamk(long long P, int tpp, long long target) {
   g_tiles += P * tpp;
 }
 
+// one workgroup per pair (the direct step's one-round grid, G = P, J = 1)
+static void check_one_round(long long P, int tpp) {
+  using namespace ttt;
+  const long long G = P, C = P * (tpp + kSkAlpha);
+  for (long long q = 0; q < G; ++q) {
+    const long long begin = sk_tile_at(q * C / G, tpp), end = sk_tile_at((q + 1) * C / G, tpp);
+    CHECK(begin == q * tpp && end == (q + 1) * tpp, "one round: q=%lld range [%lld, %lld) (P=%lld tpp=%d)", q, begin,
+          end, P, tpp);
+    CHECK(sk_first_pair(q, G, C, tpp) == q, "one round: q=%lld first pair %lld", q, sk_first_pair(q, G, C, tpp));
+  }
+}
+
 static void streamk_sweep() {
+  for (long long P = 1; P <= 1100; P += (P < 40 ? 1 : 37))
+    for (int tpp = 1; tpp <= 600; tpp += (tpp < 12 ? 1 : tpp / 3)) { check_one_round(P, tpp); if (g_fail) return; }
   // the benchmarked shapes (ViT-S 384 pairs x 7 tiles, 1248^2 96 x 191, DiT
   // 48 x 512) at one and two workgroups per CU, then a dense sweep
   const long long targets[] = {1, 2, 3, 7, 64, 255, 256, 512, 1024};
