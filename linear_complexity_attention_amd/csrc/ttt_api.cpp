@@ -28,6 +28,12 @@ struct ttt_handle {
   std::string err;
   hipEvent_t events[8] = {};
   bool timing = false;
+  // second stream for the independent head ranges of one request (the ViT3
+  // block), with its fork and join events; created on first use on device
+  // side_dev, default priority
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  int side_dev = -1;
 };
 
 namespace ttt {
@@ -415,6 +421,12 @@ int ttt_set_timing_events(ttt_handle* h, void* const* events, int n_events) {
 }
 
 int ttt_destroy(ttt_handle* h) {
+  if (h && h->side) {
+    // pending work on the side stream finishes before its resources go
+    (void)hipEventDestroy(h->ev_fork);
+    (void)hipEventDestroy(h->ev_join);
+    (void)hipStreamDestroy(h->side);
+  }
   delete h;
   return TTT_OK;
 }
@@ -642,9 +654,33 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
 
 extern "C" {
 
-int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
-                   const ttt_eta* eta, int loss, int inner, int chunk, const ttt_options* opt, void* o,
-                   const ttt_weights_out* W_out, void* workspace, size_t ws_bytes, void* stream) {
+// the handle's second stream on the current device, created here when
+// may_create (never from the no-alloc entry point); null: run serially
+static hipStream_t side_stream(ttt_handle* h, bool may_create) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  if (h->side) return h->side_dev == dev ? h->side : nullptr;
+  if (!may_create) return nullptr;
+  hipStream_t s = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+    if (a) (void)hipEventDestroy(a);
+    (void)hipStreamDestroy(s);
+    return nullptr;
+  }
+  h->side = s;
+  h->ev_fork = a;
+  h->ev_join = b;
+  h->side_dev = dev;
+  return s;
+}
+
+static int forward_impl(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
+                        const ttt_eta* eta, int loss, int inner, int chunk, const ttt_options* opt, void* o,
+                        const ttt_weights_out* W_out, void* workspace, size_t ws_bytes, void* stream,
+                        bool may_create) {
   if (!h) return fail(nullptr, TTT_ERR_INVALID, "handle is NULL");
   h->err.clear();
   Opts op;
@@ -689,14 +725,29 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
                    L.total);
     }
 
+  // the head ranges of a request are independent (disjoint heads of O, their
+  // own workspace regions): the smaller ones run on the handle's second
+  // stream, forked from and joined back to the caller's
+  hipStream_t side = L.n > 1 ? side_stream(h, may_create) : nullptr;
   // hipGetLastError is per thread and sticky: drop an error some earlier,
   // unrelated runtime call left behind so that only our launches are judged.
   (void)hipGetLastError();
   const Call cl{q, k, v, o, W0, eta, W_out, chunk, st};
+  Call cl_side = cl;
+  cl_side.st = side;
   int timed = 0;                 // the timing hook brackets the range with the most heads
   for (int i = 1; i < L.n; ++i)
     if (L.r[i].hc > L.r[timed].hc) timed = i;
-  for (int i = 0; i < L.n; ++i) enqueue_range(h, L.r[i], L.pb[i], L.pl[i], op, ws + L.base[i], cl, i == timed);
+  if (side) {
+    (void)hipEventRecord(h->ev_fork, st);
+    (void)hipStreamWaitEvent(side, h->ev_fork, 0);
+  }
+  for (int i = 0; i < L.n; ++i)
+    enqueue_range(h, L.r[i], L.pb[i], L.pl[i], op, ws + L.base[i], side && i != timed ? cl_side : cl, i == timed);
+  if (side) {
+    (void)hipEventRecord(h->ev_join, side);
+    (void)hipStreamWaitEvent(st, h->ev_join, 0);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
 
@@ -723,7 +774,21 @@ int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, c
   return TTT_OK;
 }
 
+int ttt_forward_ex(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
+                   const ttt_eta* eta, int loss, int inner, int chunk, const ttt_options* opt, void* o,
+                   const ttt_weights_out* W_out, void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(h, q, k, v, W0, eta, loss, inner, chunk, opt, o, W_out, workspace, ws_bytes, stream, true);
+}
+
 }  // extern "C"
+
+namespace ttt {
+int forward_no_create(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
+                      const ttt_eta* eta, int loss, int inner, int chunk, void* o, const ttt_weights_out* W_out,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(h, q, k, v, W0, eta, loss, inner, chunk, nullptr, o, W_out, workspace, ws_bytes, stream, false);
+}
+}  // namespace ttt
 
 namespace {
 

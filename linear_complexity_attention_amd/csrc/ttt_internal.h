@@ -3,8 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include "common.h"
-
-struct ttt_handle;
+#include "ttt.h"
 
 namespace ttt {
 
@@ -252,6 +251,12 @@ constexpr size_t kNoallocScratchBytes = size_t(192) << 20;
 // record a printf-style message as the handle's last error (h == NULL: the
 // thread's create error) and return code
 int set_error(ttt_handle* h, int code, const char* fmt, ...);
+// ttt_forward that creates no stream or event: the head ranges of a request
+// use the handle's second stream only if an earlier ttt_forward created it,
+// and otherwise run one after another on the caller's stream
+int forward_no_create(ttt_handle* h, const void* q, const void* k, const void* v, const ttt_weights* W0,
+                      const ttt_eta* eta, int loss, int inner, int chunk, void* o, const ttt_weights_out* W_out,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 // ---- finiteness check ------------------------------------------------------
 void launch_zero_flag(int* flag, hipStream_t st);

@@ -9,7 +9,9 @@
 // symbol): on the first call on a device, with that device current, its device
 // address is looked up once with hipGetSymbolAddress and kept per device; every
 // later call on that device passes that address as the workspace of
-// ttt_forward.  No call here allocates or frees memory.
+// ttt_forward.  No call here allocates or frees memory, and none creates a
+// stream or an event (a request with several head ranges uses the handle's
+// second stream only if an earlier ttt_forward created it).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -56,7 +58,8 @@ extern "C" int ttt_forward_noalloc(ttt_handle* h, const void* q, const void* k, 
     }
     ws = g_scratch[dev];
   }
-  return ttt_forward(h, q, k, v, W0, eta, loss, inner, chunk, o, W_out, ws, ttt::kNoallocScratchBytes, stream);
+  return ttt::forward_no_create(h, q, k, v, W0, eta, loss, inner, chunk, o, W_out, ws, ttt::kNoallocScratchBytes,
+                                stream);
 }
 
 static_assert(ttt::kNoallocScratchBytes == TTT_NOALLOC_SCRATCH_BYTES, "header and library disagree on the size");

@@ -187,6 +187,19 @@ def test_mfma_direct_instances(hidden, loss, key_norm, capfd):
     assert "grad=mfma_direct" in capfd.readouterr().err
 
 
+def test_mfma_direct_without_w_out():
+    """The direct step with no W_out requested (as the benchmark calls it):
+    O of sampled pairs against the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    w = Workload("direct_o", B=cus // 8, H=8, N=77, d=64, hidden=256, seed=760)
+    dev_in, exact = device_inputs(w)
+    O, _, path = run_gpu(w, dev_in, return_weights=False)
+    pairs = [(0, 0), (w.B // 2, 3), (w.B - 1, 7)]
+    O_ref, _ = run_oracle(w, exact, pairs=pairs)
+    for i, (b, h) in enumerate(pairs):
+        assert rel_err(O[b, h].float().cpu().numpy(), O_ref[i]) <= 1e-2, (b, h, path)
+
+
 # the direct step inside the stream-K split: more pairs than slots, short
 # pairs, so some workgroups hold whole pairs (stepped by the gradient kernel)
 # and others split pairs (finished by the update kernel); every 7th pair
