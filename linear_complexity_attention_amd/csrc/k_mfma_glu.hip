@@ -66,7 +66,35 @@ struct TileRegs {
 // tiles are loaded into registers while the current tile is computed, so each
 // workgroup keeps two tiles (32 KiB) of loads in flight.  Three workgroups
 // per CU (LDS); the register budget is held to three waves per SIMD to match.
+// (mean, rstd) of one channel from the key-statistics slices of its pair, sp =
+// [S][3][d] (count, mean, M2): Chan et al.'s pairwise combination in double
+// precision, slices in order (loads of eight slices in flight)
+__device__ float2 merge_key_slices(const float* __restrict__ sp, int S, int d, int c, float eps) {
+  double n = 0.0, mean = 0.0, m2 = 0.0;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float a[8], b[8], e[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* o = sp + (size_t)min(s0 + u, S - 1) * 3 * d + c;
+      a[u] = o[0];
+      b[u] = o[d];
+      e[u] = o[2 * d];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u >= S || a[u] == 0.f) continue;
+      const double nb = a[u], nt = n + nb, delta = (double)b[u] - mean;
+      mean += delta * nb / nt;
+      m2 += (double)e[u] + delta * delta * n * nb / nt;
+      n = nt;
+    }
+  }
+  const double var = n > 0.0 ? m2 / n : 0.0;
+  return float2{(float)mean, (float)(1.0 / sqrt(var + (double)eps))};
+}
+
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) k_glu_grad(Problem pb, WRef W, int t0, int nt, int S,
+                                                      const float* __restrict__ spart, int S_stats, float eps,
                                                       float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) bf16 Xs[TT * LX];     // [token][channel]
   __shared__ __attribute__((aligned(16))) bf16 Xt[D * LT];      // [channel][token]
@@ -88,12 +116,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3,
   load_wfrag(W.mat(0, b, h), w, r, g, w1f);
   load_wfrag(W.mat(1, b, h), w, r, g, w2f);
   const int st = 2 * (tid >> 3), sc = (tid & 7) * 8;
-  // key statistics (mean, rstd), channel c at [c % 8][c / 8] so that the
-  // eight channel groups of a wave read eight consecutive entries
+  // key statistics (mean, rstd), merged here from the pair's slices (or read
+  // finished), channel c at [c % 8][c / 8] so that the eight channel groups of
+  // a wave read eight consecutive entries
   __shared__ float2 nrm[D];
   if (tid < D)
     nrm[(tid & 7) * 8 + (tid >> 3)] =
-        pb.stats ? reinterpret_cast<const float2*>(pb.stats)[(size_t)p * D + tid] : float2{0.f, 1.f};
+        spart ? merge_key_slices(spart + (size_t)p * S_stats * 3 * D, S_stats, D, tid, eps)
+              : pb.stats ? reinterpret_cast<const float2*>(pb.stats)[(size_t)p * D + tid] : float2{0.f, 1.f};
   // Rows past the batch load the batch's last row (every load is issued on
   // every path, so the compiler's waits stay exact); their eta is 0, which
   // zeroes their dU and dZ and so their share of dW.
@@ -283,8 +313,10 @@ int glu_grad_splits(const Problem& pb, int nt) {
   return (int)s;
 }
 
-void launch_glu_grad(const Problem& pb, const WRef& W, int t0, int nt, int S, float* part, hipStream_t st) {
-  hipLaunchKernelGGL(k_glu_grad, dim3(S, pb.B * pb.H), dim3(NW * 64), 0, st, pb, W, t0, nt, S, part);
+void launch_glu_grad(const Problem& pb, const WRef& W, int t0, int nt, int S, const float* spart, int S_stats,
+                     float eps, float* part, hipStream_t st) {
+  hipLaunchKernelGGL(k_glu_grad, dim3(S, pb.B * pb.H), dim3(NW * 64), 0, st, pb, W, t0, nt, S, spart, S_stats, eps,
+                     part);
 }
 
 // one round of readout workgroups over the chip (eight per CU), each over a

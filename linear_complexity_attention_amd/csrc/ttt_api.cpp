@@ -536,9 +536,9 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
   mark(0);
   if (c.key_norm) {
     launch_stats_partial(pb, pl.S_stats, stats_part, st);
-    // the MFMA gradient kernel merges the slices itself; the generic and
-    // convolution kernels read finished (mu, rstd) pairs
-    if (!pl.mfma_grad) launch_stats_final(pb, pl.S_stats, stats_part, c.eps, stats, st);
+    // the MFMA and GLU gradient kernels merge the slices themselves; the
+    // generic and convolution kernels read finished (mu, rstd) pairs
+    if (!pl.mfma_grad && !pl.glu_grad) launch_stats_final(pb, pl.S_stats, stats_part, c.eps, stats, st);
   }
   if (op.rule != RULE_GD)      // the momentum starts at zero: a fill kernel (graph-capture safe)
     launch_fill_zero(mom, (long long)pl.P * pl.wsz, st);
@@ -581,7 +581,7 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
       if (pl.dwconv) {
         launch_dwconv_grad(pb, src, pl.S_grad, part, st);
       } else if (pl.glu_grad) {
-        launch_glu_grad(pb, src, t0, nt, pl.S_grad, part, st);
+        launch_glu_grad(pb, src, t0, nt, pl.S_grad, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part, st);
       } else if (pl.lact_grad) {
         launch_lact_grad(pb, src, t0, nt, pl.S_grad, cl.eta->scale, part, st);
       } else if (pl.mfma_grad) {

@@ -188,7 +188,10 @@ void launch_muon(const Problem& pb, const float* mom, float* next, float* const*
 // the state (layout [P][2][d*d]); head ranges via Problem::row
 bool glu_supported(const Problem& pb);
 int glu_grad_splits(const Problem& pb, int nt);
-void launch_glu_grad(const Problem& pb, const WRef& W, int t0, int nt, int S, float* part, hipStream_t st);
+// spart: the key-statistics slices (S_stats per pair), merged by the kernel
+// itself; null: pb.stats (finished statistics) or no key norm
+void launch_glu_grad(const Problem& pb, const WRef& W, int t0, int nt, int S, const float* spart, int S_stats,
+                     float eps, float* part, hipStream_t st);
 void launch_glu_query(const Problem& pb, const float* state, hipStream_t st);
 
 // ---- depthwise-convolution inner model (full batch) --------------------------

@@ -19,7 +19,8 @@ def _raw_call(layer, w, dev_in, noalloc):
     tq, tk, tv, tW, tet = dev_in
     li, ii = ttt.LOSSES[w.loss], ttt.INNERS[w.inner]
     out = torch.empty_like(tq)
-    W_out = [torch.empty((w.B, w.H) + tuple(m.shape[-2:]), dtype=torch.float32, device=tq.device) for m in tW]
+    # zero-filled: a ViT3 request writes each matrix only for the heads of its range
+    W_out = [torch.zeros((w.B, w.H) + tuple(m.shape[-2:]), dtype=torch.float32, device=tq.device) for m in tW]
     wts = ttt.ttt_weights()
     for i, m in enumerate(tW):
         wts.w[i] = m.data_ptr()
@@ -65,6 +66,30 @@ def test_noalloc_matches_forward_twice_second_smaller():
             assert torch.equal(a, b), f"{w.name}: final weights differ from ttt_forward"
         assert torch.isfinite(O.float()).all()
     assert sizes[1] < sizes[0]
+
+
+def test_vit3_block_serial_and_concurrent_ranges_agree():
+    """The ViT3 block's two head ranges run one after another through the
+    no-alloc entry point on a fresh handle (it creates no stream), then on
+    the handle's second stream through ttt_forward (which creates it), then
+    on that stream through the no-alloc entry point again: O and the final
+    weights are bit-identical every time."""
+    from linear_complexity_attention_amd import ttt
+
+    w = Workload("na_vit3", B=4, H=6, N=400, d=64, hidden=64, inner="vit3", loss="dot", key_norm=True,
+                 eta=1.0 / 400, grid=(20, 20), conv_k=3, seed=63)
+    print(f"no-alloc case {w.name}: B={w.B} H={w.H} N={w.N} grid={w.grid}", flush=True)
+    dev_in, _ = device_inputs(w)
+    layer = ttt.TTTLayer(w.B, w.H, w.N, w.d, w.hidden, dtype=w.dtype, key_norm=w.key_norm, renorm=w.renorm,
+                         grid=w.grid, conv_k=w.conv_k)
+    runs = [_raw_call(layer, w, dev_in, noalloc=True), _raw_call(layer, w, dev_in, noalloc=False),
+            _raw_call(layer, w, dev_in, noalloc=True)]
+    O_ref, W_ref = runs[0]
+    assert torch.isfinite(O_ref.float()).all()
+    for O, W in runs[1:]:
+        assert torch.equal(O, O_ref)
+        for a, b in zip(W, W_ref):
+            assert torch.equal(a, b)
 
 
 def test_noalloc_rejects_oversize_request():
