@@ -730,7 +730,7 @@ static int forward_impl(ttt_handle* h, const void* q, const void* k, const void*
   // stream, forked from and joined back to the caller's
   hipStream_t side = L.n > 1 ? side_stream(h, may_create) : nullptr;
   // hipGetLastError is per thread and sticky: drop an error some earlier,
-  // unrelated runtime call left behind so that only our launches are judged.
+  // unrelated runtime call left behind so that only our launches are checked.
   (void)hipGetLastError();
   const Call cl{q, k, v, o, W0, eta, W_out, chunk, st};
   Call cl_side = cl;
