@@ -200,6 +200,17 @@ def test_mfma_direct_without_w_out():
         assert rel_err(O[b, h].float().cpu().numpy(), O_ref[i]) <= 1e-2, (b, h, path)
 
 
+def test_mfma_direct_batch_specific_w0():
+    """The direct step with a W0 per (batch, head) (the step's W is read
+    through the batch stride): O and dW of sampled pairs."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    w = Workload("direct_bw0", B=cus // 8, H=8, N=100, d=64, hidden=64, seed=770)
+    dev_in, exact = device_inputs(w, shared_w0=False)
+    pairs = [(0, 1), (w.B // 3, 6), (w.B - 1, 0)]
+    _, _, path = _check_pairs(w, dev_in, exact, pairs, flags=LOG, tag="direct per-batch W0")
+    assert path == "mfma"
+
+
 # the direct step inside the stream-K split: more pairs than slots, short
 # pairs, so some workgroups hold whole pairs (stepped by the gradient kernel)
 # and others split pairs (finished by the update kernel); every 7th pair
