@@ -394,12 +394,16 @@ def main():
                     peak=PEAK_FP32_TFLOPS, unit="TFLOP/s", frac=achieved / PEAK_FP32_TFLOPS, traffic=None,
                     algorithmic_flops_per_launch=layer_flops)
     else:
-        kname = {"mfma": "fused forward/backward (k_mfma_grad)", "mfma_swiglu": "SwiGLU forward/backward "
-                 "(k_lact_grad), first chunk"}.get(path, "gradient kernels of the first update batch")
+        kname = {"mfma": "fused forward/backward (k_mfma_grad)",
+                 "mfma_fused": "fused forward/backward, gradient step and readout (k_mfma_grad, whole pairs)",
+                 "mfma_swiglu": "SwiGLU forward/backward (k_lact_grad), first chunk"}.get(
+                     path, "gradient kernels of the first update batch")
         fp32_mfma = path.startswith("mfma_f32")
         if fp32_mfma:
             kname = "fp32 matrix-core step (k_gemm_f32 products + passes), first update batch"
         grad_flops = P * gemm_flops(w, first_tokens)[0]
+        if path == "mfma_fused":          # the same kernel also computes the readout
+            grad_flops += P * f_q
         if w.inner == "vit3":
             grad_flops = w.B * (w.H - 1) * gemm_flops(w, first_tokens)[0]
             kname = f"GLU gradient (k_glu_grad, MFMA bf16), heads 1..{w.H - 1} of the block"

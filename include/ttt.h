@@ -298,8 +298,14 @@ int ttt_forward_noalloc(ttt_handle* h, const void* q, const void* k, const void*
                         const ttt_weights* W0, const ttt_eta* eta, int loss, int inner, int chunk,
                         void* o, const ttt_weights_out* W_out, void* stream);
 
-/* Name of the kernel family ttt_forward would use for this request, e.g.
- * "mfma_full_mlp" or "generic"; NULL for an invalid request.  Host-only. */
+/* Name of the kernel family ttt_forward would use for this request; NULL for
+ * an invalid request.  Host-only.  Names: "mfma" (GELU-MLP bf16 MFMA gradient
+ * and readout kernels), "mfma_fused" (the same gradient kernel, every pair held
+ * whole by one workgroup, which also applies the step and reads the pair out),
+ * "mfma_swiglu" (LaCT SwiGLU kernels), "mfma_glu", "dwconv", "dwconv+mfma_glu"
+ * and "dwconv+generic" (ViT3 block), "mfma_f32_grad" and
+ * "mfma_f32_grad+mfma_query" (fp32 matrix-core step), "generic_grad+..." and
+ * "generic". */
 const char* ttt_path_name(const ttt_handle* h, int loss, int inner, int chunk);
 
 /* Measurement hook: with n_events == 8 and events[] holding hipEvent_t

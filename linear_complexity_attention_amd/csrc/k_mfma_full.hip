@@ -232,6 +232,137 @@ __device__ __forceinline__ int tswz(int row) { return ((row >> 3) & 1) * 4 + ((r
 __device__ __forceinline__ int tok_col(int t) { return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3); }
 
 
+// One wave's share [a_, b_) of a pair's tokens (wave-uniform bounds, a_ < b_
+// or empty): O = gelu(Q W1*) W2* with the weights staged in LDS as the readout
+// stages them (w1s: W1 [c][h] bf16 scaled by sqrt(2)/c, rows of HID + 16;
+// w2s: W2 [h][c] f16 scaled by c/sqrt(2), rows of 80) and, with STAGE_O, the
+// wave's 2 KB output staging block sb; QTB 16-token blocks per full pass.
+template <int HID, int QTB, bool STAGE_O>
+__device__ __forceinline__ void readout_share(const bf16* w1s, const f16* w2s, bf16* sb, const bf16* qp, bf16* op,
+                                              int a_, int b_, int lane) {
+  constexpr int L1 = HID + 16, L2 = 80;
+  const int r = lane & 15, g = lane >> 4;
+  // rows past the wave's share read the share's last row (their O rows are
+  // not stored), so the loads need no branch
+  auto load_q = [&](int pos, bf16x8 (&q)[QTB][2]) {
+#pragma unroll
+    for (int tb = 0; tb < QTB; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int n = min(pos + 16 * tb + r, b_ - 1);
+        q[tb][ks] = ld8(qp + (long long)n * D + 32 * ks + 8 * g);
+      }
+  };
+  // one pass over NTB 16-token blocks starting at pos
+  auto pass = [&](auto ntb_c, int pos, const bf16x8 (&q)[QTB][2]) {
+    constexpr int NTB = decltype(ntb_c)::value;
+    f32x4 o[4][NTB];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int hc = 0; hc < HID / 32; ++hc) {
+      f32x4 z[2][NTB];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) z[u][tb] = f32x4{0, 0, 0, 0};
+      // issue priority while this wave has MFMAs to issue, so that the MFMA
+      // pipe is fed ahead of the other waves' GELU arithmetic (measured: 2 %)
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          // W1^T operand: W1[c = 32 ks + 8 g + j][h = 32 hc + 16 u + r]
+          const bf16x4 lo = ld_tr(&w1s[(32 * ks + 8 * g + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
+          const bf16x4 hi = ld_tr(&w1s[(32 * ks + 8 * g + 4 + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
+          const bf16x8 a = cat44(lo, hi);
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb) z[u][tb] = mfma16(a, q[tb][ks], z[u][tb]);
+        }
+      // activation operand: hidden k-slots j < 4 -> u = 0, i = j; j >= 4 -> u = 1, i = j - 4
+      __builtin_amdgcn_s_setprio(0);
+      f16x8 ab[NTB];
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) {
+        const float zz[8] = {z[0][tb][0], z[0][tb][1], z[0][tb][2], z[0][tb][3],
+                             z[1][tb][0], z[1][tb][1], z[1][tb][2], z[1][tb][3]};
+        h2 x[4];
+        gelu_chains_oc<GeluFit4, 4>(zz, x);
+        ab[tb] = f16x8{x[0].x, x[0].y, x[1].x, x[1].y, x[2].x, x[2].y, x[3].x, x[3].y};
+      }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        // W2^T operand: W2[h = 32 hc + tau(g, j)][c = 16 cb + r]
+        const f16x4 lo = ld_trt(&w2s[(32 * hc + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
+        const f16x4 hi = ld_trt(&w2s[(32 * hc + 16 + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
+        const f16x8 a = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = mfma16(a, ab[tb], o[cb][tb]);
+      }
+    }
+    // a row past the share holds the share's last row (its Q was clamped),
+    // so storing it there rewrites identical values: no branch
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      if constexpr (STAGE_O) {
+        // lane (g, r) holds channels 16 cb + 4 g .. + 3 of token r; through
+        // the wave's LDS block, lane l then takes channels 8 (l & 7) .. + 7
+        // of token (l >> 3) + 8 k (the wave's own LDS operations are done
+        // in order: no barrier)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          *reinterpret_cast<bf16x4*>(sb + r * D + (((2 * cb + (g >> 1)) ^ (r & 7)) << 3) + 4 * (g & 1)) =
+              pack4(o[cb][tb]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int t = (lane >> 3) + 8 * k, c = lane & 7;
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(sb + t * D + ((c ^ (t & 7)) << 3));
+          const int n = min(pos + 16 * tb + t, b_ - 1);
+          *reinterpret_cast<bf16x8*>(op + (long long)n * D + 8 * c) = v;
+        }
+      } else {
+        const int n = min(pos + 16 * tb + r, b_ - 1);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = pack4(o[cb][tb]);
+      }
+    }
+  };
+  // Q of the next piece is loaded while the current one is computed; the two
+  // register sets alternate and every piece inside the loop is a full pass,
+  // so no path back to the loop head leaves a load unconsumed (that would
+  // make the compiler wait for every outstanding load and store before each
+  // prefetch).  The share's last piece, when shorter than a pass, takes the
+  // shortest pass that covers it (16 or 32 tokens; the share of the last wave
+  // of a segment may end inside a 16-token unit) and leaves the loop; all
+  // these branches are on wave-uniform scalars.
+  constexpr int STEP = 16 * QTB;
+  bf16x8 qa[QTB][2], qb[QTB][2];
+  auto tail = [&](int pos, const bf16x8 (&q)[QTB][2]) {
+    const int rem = b_ - pos;
+    if (rem <= 16) pass(std::integral_constant<int, 1>{}, pos, q);
+    else if (QTB == 2 || rem <= 32) pass(std::integral_constant<int, 2>{}, pos, q);
+    else pass(std::integral_constant<int, QTB>{}, pos, q);   // rows past the share are clamped
+  };
+  int pos = a_;
+  if (pos < b_) load_q(pos, qa);
+  while (pos < b_) {
+    if (b_ - pos < STEP) { tail(pos, qa); break; }
+    load_q(pos + STEP, qb);          // past the share it re-reads the share's last row
+    pass(std::integral_constant<int, QTB>{}, pos, qa);
+    pos += STEP;
+    if (pos >= b_) break;
+    if (b_ - pos < STEP) { tail(pos, qb); break; }
+    load_q(pos + STEP, qa);
+    pass(std::integral_constant<int, QTB>{}, pos, qb);
+    pos += STEP;
+  }
+}
+
 // producer (and consumer) waves of the gradient kernel for hidden width HID
 template <int HID> constexpr int kGradWaves = mfma_grad_waves(HID);
 // workgroups per CU: at width 64 the kernel fits twice (both its LDS and, under
@@ -698,6 +829,14 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           reinterpret_cast<const float4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
       const float* Wm[2] = {W1, W.mat(1, bb, hh_)};
       float* nx = dw.next + (long long)p * 2 * D * HID;
+      // with the fused readout, W* goes to LDS in the readout's layouts (over
+      // the A' and w buffers) instead of to the state
+      const bool rq = dw.readout != 0;
+      constexpr int QL1 = HID + 16, QL2 = 80;
+      bf16* w1q = reinterpret_cast<bf16*>(&At[0][0]);
+      f16* w2q = reinterpret_cast<f16*>(&Gp[0][0]);
+      static_assert(D * QL1 * sizeof(bf16) <= sizeof(At) && HID * QL2 * sizeof(f16) <= sizeof(Gp),
+                    "the readout's weight copies fit the A' and w buffers");
       constexpr int HALF = D * HID / 4;
       // float4 jj of the partial -> element offset of its i = 0 weight in
       // matrix jj / HALF and the stride over i
@@ -743,11 +882,37 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           const float d4[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            const int e = base[u] + i * step[u];
             const float x = wv[u][i] - d4[i];
-            nm[base[u] + i * step[u]] = x;
-            if (om) om[base[u] + i * step[u]] = x;
+            if (rq) {
+              if (mat[u] == 0) w1q[(e / HID) * QL1 + e % HID] = (bf16)(x * kZScaleQ);
+              else w2q[(e / D) * QL2 + e % D] = (f16)(x * kW2ScaleQ);
+            } else {
+              nm[e] = x;
+            }
+            if (om) om[e] = x;
           }
         }
+      }
+      if (rq) {
+        // fused readout of the whole pair, O = F_W*(Q), its tokens split over
+        // all 2 NW waves in 16-token units (the readout kernel's pass loop);
+        // the output staging blocks go over the key tiles
+        __syncthreads();
+        static_assert(2 * NW * 16 * D * sizeof(bf16) <= sizeof(Kr), "output staging fits the key tiles");
+        const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int units = (pb.N + 15) >> 4;
+        const int a_ = __builtin_amdgcn_readfirstlane(16 * (wq * units / (2 * NW)));
+        const int b_ = __builtin_amdgcn_readfirstlane(min(pb.N, 16 * ((wq + 1) * units / (2 * NW))));
+        const bf16* qp = (const bf16*)pb.q + (long long)p * pb.N * D;
+        bf16* op = (bf16*)pb.o + (long long)p * pb.N * D;
+        bf16* sb = reinterpret_cast<bf16*>(&Kr[0][0]) + wq * 16 * D;
+        // the lane index passes through an empty asm statement so that the
+        // readout's per-lane offsets are not hoisted into the main loops
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
+        readout_share<HID, (HID == 64 ? 1 : 2), (HID <= 128)>(w1q, w2q, sb, qp, op, a_, b_, lane_o);
+        __syncthreads();                      // LDS is the next segment's
       }
     }
     x = seg_end;
@@ -878,126 +1043,7 @@ k_mfma_query(Problem pb, WRef w0, const float* __restrict__ states, long long st
     const int b_ = __builtin_amdgcn_readfirstlane(min(n1, n0 + 16 * ((wu + 1) * units / QW)));
     const bf16* qp = (const bf16*)pb.q + (long long)p * N * D;
     bf16* op = (bf16*)pb.o + (long long)p * N * D;
-    // rows past the wave's share read the share's last row (their O rows are
-    // not stored), so the loads need no branch
-    auto load_q = [&](int pos, bf16x8 (&q)[QTB][2]) {
-#pragma unroll
-      for (int tb = 0; tb < QTB; ++tb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int n = min(pos + 16 * tb + r, b_ - 1);
-          q[tb][ks] = ld8(qp + (long long)n * D + 32 * ks + 8 * g);
-        }
-    };
-    // one pass over NTB 16-token blocks starting at pos
-    auto pass = [&](auto ntb_c, int pos, const bf16x8 (&q)[QTB][2]) {
-      constexpr int NTB = decltype(ntb_c)::value;
-      f32x4 o[4][NTB];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int hc = 0; hc < HID / 32; ++hc) {
-        f32x4 z[2][NTB];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int tb = 0; tb < NTB; ++tb) z[u][tb] = f32x4{0, 0, 0, 0};
-        // issue priority while this wave has MFMAs to issue, so that the MFMA
-        // pipe is fed ahead of the other waves' GELU arithmetic (measured: 2 %)
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            // W1^T operand: W1[c = 32 ks + 8 g + j][h = 32 hc + 16 u + r]
-            const bf16x4 lo = ld_tr(&w1s[(32 * ks + 8 * g + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
-            const bf16x4 hi = ld_tr(&w1s[(32 * ks + 8 * g + 4 + (r >> 2)) * L1 + 32 * hc + 16 * u + 4 * (r & 3)]);
-            const bf16x8 a = cat44(lo, hi);
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) z[u][tb] = mfma16(a, q[tb][ks], z[u][tb]);
-          }
-        // activation operand: hidden k-slots j < 4 -> u = 0, i = j; j >= 4 -> u = 1, i = j - 4
-        __builtin_amdgcn_s_setprio(0);
-        f16x8 ab[NTB];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          const float zz[8] = {z[0][tb][0], z[0][tb][1], z[0][tb][2], z[0][tb][3],
-                               z[1][tb][0], z[1][tb][1], z[1][tb][2], z[1][tb][3]};
-          h2 x[4];
-          gelu_chains_oc<GeluFit4, 4>(zz, x);
-          ab[tb] = f16x8{x[0].x, x[0].y, x[1].x, x[1].y, x[2].x, x[2].y, x[3].x, x[3].y};
-        }
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          // W2^T operand: W2[h = 32 hc + tau(g, j)][c = 16 cb + r]
-          const f16x4 lo = ld_trt(&w2s[(32 * hc + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
-          const f16x4 hi = ld_trt(&w2s[(32 * hc + 16 + 4 * g + (r >> 2)) * L2 + 16 * cb + 4 * (r & 3)]);
-          const f16x8 a = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-          for (int tb = 0; tb < NTB; ++tb) o[cb][tb] = mfma16(a, ab[tb], o[cb][tb]);
-        }
-      }
-      // a row past the share holds the share's last row (its Q was clamped),
-      // so storing it there rewrites identical values: no branch
-#pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) {
-        if constexpr (kStageO) {
-          // lane (g, r) holds channels 16 cb + 4 g .. + 3 of token r; through
-          // the wave's LDS block, lane l then takes channels 8 (l & 7) .. + 7
-          // of token (l >> 3) + 8 k (the wave's own LDS operations are done
-          // in order: no barrier)
-          bf16* sb = ob[w];
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            *reinterpret_cast<bf16x4*>(sb + r * D + (((2 * cb + (g >> 1)) ^ (r & 7)) << 3) + 4 * (g & 1)) =
-                pack4(o[cb][tb]);
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int t = (lane >> 3) + 8 * k, c = lane & 7;
-            const bf16x8 v = *reinterpret_cast<const bf16x8*>(sb + t * D + ((c ^ (t & 7)) << 3));
-            const int n = min(pos + 16 * tb + t, b_ - 1);
-            *reinterpret_cast<bf16x8*>(op + (long long)n * D + 8 * c) = v;
-          }
-        } else {
-          const int n = min(pos + 16 * tb + r, b_ - 1);
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            *reinterpret_cast<bf16x4*>(op + (long long)n * D + 16 * cb + 4 * g) = pack4(o[cb][tb]);
-        }
-      }
-    };
-    // Q of the next piece is loaded while the current one is computed; the two
-    // register sets alternate and every piece inside the loop is a full pass,
-    // so no path back to the loop head leaves a load unconsumed (that would
-    // make the compiler wait for every outstanding load and store before each
-    // prefetch).  The share's last piece, when shorter than a pass, takes the
-    // shortest pass that covers it (16 or 32 tokens; the share of the last wave
-    // of a segment may end inside a 16-token unit) and leaves the loop; all
-    // these branches are on wave-uniform scalars.
-    constexpr int STEP = 16 * QTB;
-    bf16x8 qa[QTB][2], qb[QTB][2];
-    auto tail = [&](int pos, const bf16x8 (&q)[QTB][2]) {
-      const int rem = b_ - pos;
-      if (rem <= 16) pass(std::integral_constant<int, 1>{}, pos, q);
-      else if (QTB == 2 || rem <= 32) pass(std::integral_constant<int, 2>{}, pos, q);
-      else pass(std::integral_constant<int, QTB>{}, pos, q);   // rows past the share are clamped
-    };
-    int pos = a_;
-    if (pos < b_) load_q(pos, qa);
-    while (pos < b_) {
-      if (b_ - pos < STEP) { tail(pos, qa); break; }
-      load_q(pos + STEP, qb);          // past the share it re-reads the share's last row
-      pass(std::integral_constant<int, QTB>{}, pos, qa);
-      pos += STEP;
-      if (pos >= b_) break;
-      if (b_ - pos < STEP) { tail(pos, qb); break; }
-      load_q(pos + STEP, qa);
-      pass(std::integral_constant<int, QTB>{}, pos, qb);
-      pos += STEP;
-    }
+    readout_share<HID, QTB, kStageO>(w1s, w2s, kStageO ? ob[w] : nullptr, qp, op, a_, b_, lane);
     };
     if (buf == 0) segment(std::integral_constant<int, 0>{});
     else segment(std::integral_constant<int, 1>{});
@@ -1077,7 +1123,7 @@ void launch_mfma_full_grad(const Problem& pb, const WRef& W, int t0, int nt, flo
                            int S_stats, float eps, float* part, const GradDirect* direct, bool one_round,
                            hipStream_t st) {
   int G, J, tpp;
-  GradDirect dw{nullptr, {nullptr, nullptr}};
+  GradDirect dw{nullptr, {nullptr, nullptr}, 0};
   if (direct) dw = *direct;
   if (one_round) {
     // G = pairs: on the stream-K cost line every workgroup's range is then

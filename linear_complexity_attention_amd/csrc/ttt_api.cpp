@@ -133,6 +133,7 @@ struct Plan {
   bool mfma_direct;                  // the MFMA gradient kernel applies the step to every whole pair
   bool mfma_one_round;               // ... with one workgroup per pair
   bool mfma_split;                   // ... and some pair is split (the update kernel finishes those)
+  bool mfma_fused_q;                 // ... no pair is split: the gradient kernel also reads every pair out
   int S_stats, S_grad;               // S_grad: partial slots of the gradient kernel
   int S_step;                        // token slices of the fp32 matrix-core step
   int sk_G, sk_J;                    // stream-K geometry (MFMA gradient kernel)
@@ -262,6 +263,7 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
   const bool fast = !generic_only && pb.full_heads();
   pl.dwconv = pb.inner == INNER_DWCONV;
   pl.mfma_grad = fast && mfma_full_supported(pb) && pl.nb == 1 && op.epochs == 1;
+  pl.mfma_query = fast && mfma_query_supported(pb);
   // a plain gradient step of every matrix with many pairs: the gradient
   // kernel takes whole pairs and applies the step itself (no partials, no
   // update kernel)
@@ -270,8 +272,9 @@ Plan make_plan(const ttt_handle* h, const Problem& pb, int chunk, const Opts& op
     const long long split = pl.mfma_one_round ? 0 : mfma_grad_split_pairs(pb, pl.span);
     pl.mfma_direct = split < pl.P;     // some pair is whole
     pl.mfma_split = split > 0;
+    // the finite check reads the final state, which the fused readout does not write
+    pl.mfma_fused_q = pl.mfma_direct && !pl.mfma_split && pl.mfma_query && !(c.flags & TTT_FLAG_CHECK_FINITE);
   }
-  pl.mfma_query = fast && mfma_query_supported(pb);
   pl.lact_grad = fast && !c.key_norm && lact_supported(pb);
   pl.lact_query = fast && lact_readout_supported(pb);
   // the GLU kernels address pairs through Problem::row, so they also serve a
@@ -460,6 +463,7 @@ const char* ttt_path_name_ex(const ttt_handle* hc, int loss, int inner, int chun
   if (pl.dwconv) return "dwconv";
   if (pl.glu_grad && pl.glu_query) return "mfma_glu";
   if (pl.glu_query) return "generic_grad+mfma_glu_query";
+  if (pl.mfma_fused_q) return "mfma_fused";   // the gradient kernel also reads every pair out
   if (pl.mfma_grad && pl.mfma_query) return "mfma";
   if (pl.step_mfma) return pl.mfma_query ? "mfma_f32_grad+mfma_query" : "mfma_f32_grad";
   if (pl.mfma_query) return "generic_grad+mfma_query";
@@ -588,7 +592,7 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
         // the kernel accumulates eta_n-weighted (V_hat - V) or -eta_n V; the
         // scalar eta and the MSE constant 2/(n_b d) are applied to its partials
         const float scale = pb.loss == LOSS_MSE ? cl.eta->scale * 2.0f / ((float)nt * (float)c.d) : cl.eta->scale;
-        const GradDirect gd{next, {wout[0], wout[1]}};
+        const GradDirect gd{next, {wout[0], wout[1]}, pl.mfma_fused_q ? 1 : 0};
         launch_mfma_full_grad(pb, src, t0, nt, scale, c.key_norm ? stats_part : nullptr, pl.S_stats, c.eps, part,
                               pl.mfma_direct ? &gd : nullptr, pl.mfma_one_round, st);
       } else if (pl.step_mfma && step_mfma_aligned(src)) {
@@ -636,7 +640,9 @@ void enqueue_range(ttt_handle* h, const Range& r, Problem pb, const Plan& pl, co
   const float* rstates = op.causal ? states : states + (long long)(pl.nb - 1) * pl.state_stride;
   const int rchunk = op.causal ? chunk : 0;
   const int rn = op.causal ? pl.nb : 1;
-  if (pl.dwconv) {
+  if (pl.mfma_fused_q) {
+    // the gradient kernel has read every pair out
+  } else if (pl.dwconv) {
     launch_dwconv_query(pb, rstates, st);
   } else if (pl.glu_query) {
     launch_glu_query(pb, rstates, st);
@@ -716,7 +722,8 @@ static int forward_impl(ttt_handle* h, const void* q, const void* k, const void*
                    c.B, c.H, L.r[i].h0, L.r[i].h0 + L.r[i].hc - 1, c.N, c.d, pl.hid, c.dtype == TTT_BF16 ? "bf16" : "f32",
                    L.r[i].model, loss, chunk, pl.nb, op.epochs, range_mask(op.mask, L.r[i]),
                    op.causal ? "causal" : "write-then-query", op.rule,
-                   pl.dwconv ? "dwconv" : pl.glu_grad ? "mfma_glu" : pl.mfma_direct ? "mfma_direct"
+                   pl.dwconv ? "dwconv" : pl.glu_grad ? "mfma_glu" : pl.mfma_fused_q ? "mfma_direct+readout"
+                   : pl.mfma_direct ? "mfma_direct"
                    : pl.mfma_grad ? "mfma" : pl.lact_grad ? "mfma_swiglu"
                                                                        : pl.step_mfma ? "mfma_f32" : "generic",
                    pl.S_grad,

@@ -183,7 +183,7 @@ def test_mfma_direct_instances(hidden, loss, key_norm, capfd):
     dev_in, exact = device_inputs(w)
     pairs = [(0, 0), (1, 3), (w.B // 2, 5), (w.B - 1, 7)]
     _, _, path = _check_pairs(w, dev_in, exact, pairs, flags=LOG, tag=f"direct h={hidden} {loss} kn={key_norm}")
-    assert path == "mfma"
+    assert path == "mfma_fused"
     assert "grad=mfma_direct" in capfd.readouterr().err
 
 
@@ -194,6 +194,7 @@ def test_mfma_direct_without_w_out():
     w = Workload("direct_o", B=cus // 8, H=8, N=77, d=64, hidden=256, seed=760)
     dev_in, exact = device_inputs(w)
     O, _, path = run_gpu(w, dev_in, return_weights=False)
+    assert path == "mfma_fused"
     pairs = [(0, 0), (w.B // 2, 3), (w.B - 1, 7)]
     O_ref, _ = run_oracle(w, exact, pairs=pairs)
     for i, (b, h) in enumerate(pairs):
@@ -208,7 +209,7 @@ def test_mfma_direct_batch_specific_w0():
     dev_in, exact = device_inputs(w, shared_w0=False)
     pairs = [(0, 1), (w.B // 3, 6), (w.B - 1, 0)]
     _, _, path = _check_pairs(w, dev_in, exact, pairs, flags=LOG, tag="direct per-batch W0")
-    assert path == "mfma"
+    assert path == "mfma_fused"
 
 
 # the direct step inside the stream-K split: more pairs than slots, short
@@ -285,7 +286,7 @@ def test_single_token_tiny_eps_padding_rows():
     w = Workload("n1eps", B=1, H=3, N=1, d=64, hidden=256, seed=48)
     dev_in, exact = device_inputs(w)
     O, W_out, path = run_gpu(w, dev_in, eps=1e-10)
-    assert path == "mfma"
+    assert path == "mfma_fused"      # three one-tile pairs: each workgroup holds one whole
     for m, w0 in zip(W_out, dev_in[3]):
         torch.testing.assert_close(m, w0[None].expand_as(m), rtol=0, atol=1e-7)
     assert torch.isfinite(O.float()).all()
