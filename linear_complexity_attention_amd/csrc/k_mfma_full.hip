@@ -808,15 +808,70 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       // acc2 holds A'^T G' = -sqrt(2) A^T G and acc1 holds K_hat^T dZ' =
       // K_hat^T dZ / sqrt(2).
       const float scale1 = scale * kSqrt2, scale2 = -scale * kRSqrt2;
-      f32x4* out = reinterpret_cast<f32x4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
+      if (DIRECT && dw.readout && tile0 == 0 && n == tpp) {
+        // fused readout of a whole pair: W* = W - dW straight from the
+        // accumulators into the readout's LDS copies (over the A' and w
+        // buffers, free once every wave has passed the loop's last barrier),
+        // and to W_out; one row block at a time, the lane index opaque so that
+        // none of this index arithmetic is hoisted into the main loop (the
+        // step without the fused readout goes through the partial instead:
+        // the extra global stores here spill registers in the main loop)
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
+        const int rr = lane_o & 15, gg = lane_o >> 4;
+        constexpr int QL1 = HID + 16, QL2 = 80;
+        bf16* w1q = reinterpret_cast<bf16*>(&At[0][0]);
+        f16* w2q = reinterpret_cast<f16*>(&Gp[0][0]);
+        const float* W2c = W.mat(1, bb, hh_);
+        float* o1 = dw.out[0] ? dw.out[0] + pb.row(p) * D * HID : nullptr;
+        float* o2 = dw.out[1] ? dw.out[1] + pb.row(p) * D * HID : nullptr;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb) {
+          float v[NHB][4];
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) out[((q * 4 + cb) * NHB + hb) * 64 + lane] = scale1 * acc1[cb][hb];
+          for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
+            for (int i = 0; i < 4; ++i) v[hb][i] = W1[(16 * cb + 4 * gg + i) * HID + h0 + 16 * hb + rr];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) out[D * HID / 4 + ((q * NHB + hb) * 4 + cb) * 64 + lane] = scale2 * acc2[hb][cb];
+          for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int c = 16 * cb + 4 * gg + i, hh = h0 + 16 * hb + rr;
+              const float x = v[hb][i] - scale1 * acc1[cb][hb][i];
+              w1q[c * QL1 + hh] = (bf16)(x * kZScaleQ);
+              if (o1) o1[c * HID + hh] = x;
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          float v[4][4];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[cb][i] = W2c[(h0 + 16 * hb + 4 * gg + i) * D + 16 * cb + rr];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int hh = h0 + 16 * hb + 4 * gg + i, c = 16 * cb + rr;
+              const float x = v[cb][i] - scale2 * acc2[hb][cb][i];
+              w2q[hh * QL2 + c] = (f16)(x * kW2ScaleQ);
+              if (o2) o2[hh * D + c] = x;
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        f32x4* out = reinterpret_cast<f32x4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) out[((q * 4 + cb) * NHB + hb) * 64 + lane] = scale1 * acc1[cb][hb];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) out[D * HID / 4 + ((q * NHB + hb) * 4 + cb) * 64 + lane] = scale2 * acc2[hb][cb];
+      }
     }
     if (DIRECT && tile0 == 0 && n == tpp) {
       // direct step (this segment is the whole pair): after the barrier
@@ -825,18 +880,16 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       // to the 4 weights each maps to (partial layout above), in the natural
       // layouts W1 [c][h] and W2 [h][c]
       __syncthreads();
+      // with the fused readout the consumers have already put W* into LDS in
+      // the readout's layouts (over the A' and w buffers)
+      constexpr int QL1 = HID + 16, QL2 = 80;
+      static_assert(D * QL1 * sizeof(bf16) <= sizeof(At) && HID * QL2 * sizeof(f16) <= sizeof(Gp),
+                    "the readout's weight copies fit the A' and w buffers");
+      if (!dw.readout) {
       const float4* pin =
           reinterpret_cast<const float4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
       const float* Wm[2] = {W1, W.mat(1, bb, hh_)};
       float* nx = dw.next + (long long)p * 2 * D * HID;
-      // with the fused readout, W* goes to LDS in the readout's layouts (over
-      // the A' and w buffers) instead of to the state
-      const bool rq = dw.readout != 0;
-      constexpr int QL1 = HID + 16, QL2 = 80;
-      bf16* w1q = reinterpret_cast<bf16*>(&At[0][0]);
-      f16* w2q = reinterpret_cast<f16*>(&Gp[0][0]);
-      static_assert(D * QL1 * sizeof(bf16) <= sizeof(At) && HID * QL2 * sizeof(f16) <= sizeof(Gp),
-                    "the readout's weight copies fit the A' and w buffers");
       constexpr int HALF = D * HID / 4;
       // float4 jj of the partial -> element offset of its i = 0 weight in
       // matrix jj / HALF and the stride over i
@@ -884,21 +937,15 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
           for (int i = 0; i < 4; ++i) {
             const int e = base[u] + i * step[u];
             const float x = wv[u][i] - d4[i];
-            if (rq) {
-              if (mat[u] == 0) w1q[(e / HID) * QL1 + e % HID] = (bf16)(x * kZScaleQ);
-              else w2q[(e / D) * QL2 + e % D] = (f16)(x * kW2ScaleQ);
-            } else {
-              nm[e] = x;
-            }
+            nm[e] = x;
             if (om) om[e] = x;
           }
         }
       }
-      if (rq) {
+      } else {
         // fused readout of the whole pair, O = F_W*(Q), its tokens split over
         // all 2 NW waves in 16-token units (the readout kernel's pass loop);
         // the output staging blocks go over the key tiles
-        __syncthreads();
         static_assert(2 * NW * 16 * D * sizeof(bf16) <= sizeof(Kr), "output staging fits the key tiles");
         const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int units = (pb.N + 15) >> 4;
@@ -911,7 +958,9 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
         // readout's per-lane offsets are not hoisted into the main loops
         int lane_o = lane;
         asm volatile("" : "+v"(lane_o));
-        readout_share<HID, (HID == 64 ? 1 : 2), (HID <= 128)>(w1q, w2q, sb, qp, op, a_, b_, lane_o);
+        readout_share<HID, (HID == 64 ? 1 : 2), (HID <= 128)>(reinterpret_cast<const bf16*>(&At[0][0]),
+                                                             reinterpret_cast<const f16*>(&Gp[0][0]), sb, qp, op,
+                                                             a_, b_, lane_o);
         __syncthreads();                      // LDS is the next segment's
       }
     }

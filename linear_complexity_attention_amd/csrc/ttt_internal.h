@@ -147,9 +147,10 @@ void mfma_grad_geometry(const Problem& pb, int nt, int* G, int* J, int* tiles_pe
 // is whole; it is taken when the pairs fill between half and all of the
 // workgroup slots in one round (many short pairs: the split-N partials and
 // the update kernel would outweigh the work).
-// With readout set (every pair whole), the workgroup then reads out its pair
-// itself: W* is staged in LDS instead of written to next, and O = F_W*(Q) of
-// the pair's tokens is computed there (no readout kernel).
+// With readout set (every pair whole), the workgroup reads out its pair
+// itself instead: its consumer waves put W* from their accumulators into LDS
+// (and W_out), no partial and no state is written, and after a barrier all
+// its waves compute O = F_W*(Q) of the pair's tokens (no readout kernel).
 struct GradDirect { float* next; float* out[2]; int readout; };
 bool mfma_grad_direct_fits(const Problem& pb);
 // pairs of the stream-K split whose tiles more than one workgroup holds
