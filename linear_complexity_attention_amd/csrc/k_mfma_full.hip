@@ -874,78 +874,77 @@ k_mfma_grad(Problem pb, WRef W, int t0, int nt, int J, float scale, const float*
       }
     }
     if (DIRECT && tile0 == 0 && n == tpp) {
-      // direct step (this segment is the whole pair): after the barrier
-      // every thread of the workgroup takes float4s of the pair's partial,
-      // which this workgroup just wrote (L2-resident), and applies W* = W - dW
-      // to the 4 weights each maps to (partial layout above), in the natural
-      // layouts W1 [c][h] and W2 [h][c]
+      // this segment is the whole pair
       __syncthreads();
-      // with the fused readout the consumers have already put W* into LDS in
-      // the readout's layouts (over the A' and w buffers)
       constexpr int QL1 = HID + 16, QL2 = 80;
       static_assert(D * QL1 * sizeof(bf16) <= sizeof(At) && HID * QL2 * sizeof(f16) <= sizeof(Gp),
                     "the readout's weight copies fit the A' and w buffers");
       if (!dw.readout) {
-      const float4* pin =
-          reinterpret_cast<const float4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
-      const float* Wm[2] = {W1, W.mat(1, bb, hh_)};
-      float* nx = dw.next + (long long)p * 2 * D * HID;
-      constexpr int HALF = D * HID / 4;
-      // float4 jj of the partial -> element offset of its i = 0 weight in
-      // matrix jj / HALF and the stride over i
-      auto map = [&](int jj, int& mat, int& base, int& step) {
-        mat = jj >= HALF ? 1 : 0;
-        const int jl = jj - mat * HALF, l = jl & 63, blk = jl >> 6, gg = l >> 4, rr = l & 15;
-        if (mat == 0) {
-          const int hb = blk % NHB, cb = (blk / NHB) & 3, qq = blk / (4 * NHB);
-          base = (16 * cb + 4 * gg) * HID + qq * HP + 16 * hb + rr;
-          step = HID;
-        } else {
-          const int cb = blk & 3, hb = (blk >> 2) % NHB, qq = blk / (4 * NHB);
-          base = (qq * HP + 16 * hb + 4 * gg) * D + 16 * cb + rr;
-          step = D;
-        }
-      };
-      // eight float4s per thread at a time, every load of the batch issued
-      // before its stores (the stores may alias the loads in the compiler's
-      // view, so a plain loop would wait for each iteration's loads)
-      // the thread index passes through an empty asm statement, so that the
-      // compiler cannot hoist the (segment-invariant) index arithmetic below
-      // to the kernel entry and keep it in registers through the main loops
-      int tid_o = tid;
-      asm volatile("" : "+v"(tid_o));
-      constexpr int PER = 2 * HALF / NTH, UB = PER < 8 ? PER : 8;
-      static_assert(2 * HALF % (NTH * UB) == 0, "the partial splits evenly into batches");
-      for (int j0 = 0; j0 < PER; j0 += UB) {
-        float4 dv[UB];
-        float wv[UB][4];
-        int mat[UB], base[UB], step[UB];
+        // direct step: every thread of the workgroup takes float4s of the
+        // pair's partial, which this workgroup just wrote (L2-resident), and
+        // applies W* = W - dW to the 4 weights each maps to (partial layout
+        // above), in the natural layouts W1 [c][h] and W2 [h][c]
+        const float4* pin =
+            reinterpret_cast<const float4*>(part + ((long long)blockIdx.x * J + (p - p_first)) * (2LL * D * HID));
+        const float* Wm[2] = {W1, W.mat(1, bb, hh_)};
+        float* nx = dw.next + (long long)p * 2 * D * HID;
+        constexpr int HALF = D * HID / 4;
+        // float4 jj of the partial -> element offset of its i = 0 weight in
+        // matrix jj / HALF and the stride over i
+        auto map = [&](int jj, int& mat, int& base, int& step) {
+          mat = jj >= HALF ? 1 : 0;
+          const int jl = jj - mat * HALF, l = jl & 63, blk = jl >> 6, gg = l >> 4, rr = l & 15;
+          if (mat == 0) {
+            const int hb = blk % NHB, cb = (blk / NHB) & 3, qq = blk / (4 * NHB);
+            base = (16 * cb + 4 * gg) * HID + qq * HP + 16 * hb + rr;
+            step = HID;
+          } else {
+            const int cb = blk & 3, hb = (blk >> 2) % NHB, qq = blk / (4 * NHB);
+            base = (qq * HP + 16 * hb + 4 * gg) * D + 16 * cb + rr;
+            step = D;
+          }
+        };
+        // eight float4s per thread at a time, every load of the batch issued
+        // before its stores (the stores may alias the loads in the compiler's
+        // view, so a plain loop would wait for each iteration's loads)
+        // the thread index passes through an empty asm statement, so that the
+        // compiler cannot hoist the (segment-invariant) index arithmetic below
+        // to the kernel entry and keep it in registers through the main loops
+        int tid_o = tid;
+        asm volatile("" : "+v"(tid_o));
+        constexpr int PER = 2 * HALF / NTH, UB = PER < 8 ? PER : 8;
+        static_assert(2 * HALF % (NTH * UB) == 0, "the partial splits evenly into batches");
+        for (int j0 = 0; j0 < PER; j0 += UB) {
+          float4 dv[UB];
+          float wv[UB][4];
+          int mat[UB], base[UB], step[UB];
 #pragma unroll
-        for (int u = 0; u < UB; ++u) {
-          const int jj = tid_o + NTH * (j0 + u);
-          map(jj, mat[u], base[u], step[u]);
-          dv[u] = pin[jj];
+          for (int u = 0; u < UB; ++u) {
+            const int jj = tid_o + NTH * (j0 + u);
+            map(jj, mat[u], base[u], step[u]);
+            dv[u] = pin[jj];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) wv[u][i] = Wm[mat[u]][base[u] + i * step[u]];
-        }
+            for (int i = 0; i < 4; ++i) wv[u][i] = Wm[mat[u]][base[u] + i * step[u]];
+          }
 #pragma unroll
-        for (int u = 0; u < UB; ++u) {
-          float* nm = nx + mat[u] * D * HID;
-          float* om = dw.out[mat[u]] ? dw.out[mat[u]] + pb.row(p) * D * HID : nullptr;
-          const float d4[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
+          for (int u = 0; u < UB; ++u) {
+            float* nm = nx + mat[u] * D * HID;
+            float* om = dw.out[mat[u]] ? dw.out[mat[u]] + pb.row(p) * D * HID : nullptr;
+            const float d4[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = base[u] + i * step[u];
-            const float x = wv[u][i] - d4[i];
-            nm[e] = x;
-            if (om) om[e] = x;
+            for (int i = 0; i < 4; ++i) {
+              const int e = base[u] + i * step[u];
+              const float x = wv[u][i] - d4[i];
+              nm[e] = x;
+              if (om) om[e] = x;
+            }
           }
         }
-      }
       } else {
-        // fused readout of the whole pair, O = F_W*(Q), its tokens split over
-        // all 2 NW waves in 16-token units (the readout kernel's pass loop);
-        // the output staging blocks go over the key tiles
+        // fused readout: the consumers have put W* into LDS in the readout's
+        // layouts (over the A' and w buffers); O = F_W*(Q) of the pair's
+        // tokens, split over all 2 NW waves in 16-token units (the readout
+        // kernel's pass loop); the output staging blocks go over the key tiles
         static_assert(2 * NW * 16 * D * sizeof(bf16) <= sizeof(Kr), "output staging fits the key tiles");
         const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int units = (pb.N + 15) >> 4;
