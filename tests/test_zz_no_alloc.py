@@ -92,6 +92,26 @@ def test_vit3_block_serial_and_concurrent_ranges_agree():
             assert torch.equal(a, b)
 
 
+def test_noalloc_fused_gradient_and_readout():
+    """A request on the fused path (every pair held whole by one gradient
+    workgroup, which also reads it out) through both entry points: O and the
+    final weights bit-identical."""
+    from linear_complexity_attention_amd import ttt
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    w = Workload("na_fused", B=cus // 8, H=8, N=196, d=64, hidden=256, seed=64)
+    print(f"no-alloc case {w.name}: B={w.B} H={w.H} N={w.N} h={w.hidden}", flush=True)
+    dev_in, _ = device_inputs(w)
+    layer = ttt.TTTLayer(w.B, w.H, w.N, w.d, w.hidden, dtype=w.dtype, key_norm=w.key_norm, renorm=w.renorm)
+    assert layer.path_name(w.loss, w.inner, w.chunk) == "mfma_fused"
+    O_ref, W_ref = _raw_call(layer, w, dev_in, noalloc=False)
+    O, W = _raw_call(layer, w, dev_in, noalloc=True)
+    assert torch.isfinite(O_ref.float()).all()
+    assert torch.equal(O, O_ref)
+    for a, b in zip(W, W_ref):
+        assert torch.equal(a, b)
+
+
 def test_noalloc_rejects_oversize_request():
     from linear_complexity_attention_amd import ttt
 
