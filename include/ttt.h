@@ -235,7 +235,13 @@ int ttt_workspace_bytes(const ttt_handle* h, int loss, int inner, int chunk, siz
  * or a pre-activation exceeds about 4e4, those values overflow and O and the
  * final weights can hold Inf or NaN while the call still returns TTT_OK.
  * Set TTT_FLAG_CHECK_FINITE to have such a result reported as
- * TTT_ERR_NONFINITE, or TTT_FLAG_FORCE_GENERIC to compute it in fp32. */
+ * TTT_ERR_NONFINITE, or TTT_FLAG_FORCE_GENERIC to compute it in fp32.
+ * Streams: the ViT3 block's head ranges (TTT_INNER_VIT3) are independent and
+ * run concurrently, the smaller one on a second stream of the handle (default
+ * priority), forked from `stream` by an event and joined back to it before the
+ * call returns; that stream and its two events are created on the first such
+ * request and released by ttt_destroy.  Every other request runs on `stream`
+ * alone. */
 int ttt_forward(ttt_handle* h, const void* q, const void* k, const void* v,
                 const ttt_weights* W0, const ttt_eta* eta, int loss, int inner, int chunk,
                 void* o, const ttt_weights_out* W_out, void* workspace, size_t ws_bytes,
