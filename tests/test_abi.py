@@ -146,6 +146,27 @@ def test_options_rejected_on_the_host():
     assert layer.workspace_bytes("mse", "mlp_gelu", 16, ttt.make_options(order="write_then_query")) > 0
 
 
+def test_gelu_mlp_gradient_forms_chosen_on_host():
+    """Which form of the GELU-MLP gradient step a request takes (a host-side
+    plan; without a GPU the compute-unit count is taken as 256, the MI355X's):
+    the ViT-S shapes hold every pair whole in one workgroup, which then also
+    reads it out ("mfma_fused"); longer pairs are split over workgroups and
+    reduced by the update kernel ("mfma"), and so is every request the fused
+    step does not cover (re-norm, momentum, first layer only, finite check)."""
+    def layer(B, H, N, h, **kw):
+        return ttt.TTTLayer(B, H, N, 64, h, **kw)
+
+    assert layer(64, 6, 196, 256).path_name() == "mfma_fused"     # stream-K ranges of whole pairs
+    assert layer(64, 6, 196, 64).path_name() == "mfma_fused"      # one workgroup per pair
+    assert layer(64, 6, 196, 64).path_name("dot") == "mfma_fused"
+    assert layer(8, 12, 6084, 256).path_name() == "mfma"
+    assert layer(2, 24, 16384, 64).path_name() == "mfma"
+    assert layer(64, 6, 196, 256, renorm=True).path_name() == "mfma"
+    assert layer(64, 6, 196, 256, flags=ttt.TTT_FLAG_CHECK_FINITE).path_name() == "mfma"
+    assert layer(64, 6, 196, 256).path_name(options=ttt.make_options(rule="momentum", beta=0.9)) == "mfma"
+    assert layer(64, 6, 196, 256).path_name(options=ttt.make_options(update_mask=1)) == "mfma"
+
+
 def test_convolution_requests_validated_on_host():
     """The convolution inner models need a raster with grid_h * grid_w == N and
     an odd kernel size, run full batch only, and take neither Muon nor the
