@@ -76,7 +76,9 @@ __device__ __forceinline__ void load8<float>(const float* p, float* x) {
 // window) as (x - mu) * rs per channel; window positions outside the raster
 // hold 0, the convolution's zero padding.  Thread t owns channels
 // 8 (t % (d / 8)) .. + 7, whose mu / rs it holds.  All loads are issued
-// before the first is used.
+// before the first is used: a position outside the raster reads the pair's
+// first row and is zeroed afterwards, so that no load sits under a branch
+// of its own (each would be waited for before the next is issued).
 template <typename T, int K, int U>
 __device__ __forceinline__ void stage_tile(const T* __restrict__ src, int gh, int gw, int d, int ti0, int tj0,
                                            const float* mu, const float* rs, float* __restrict__ tile) {
@@ -91,21 +93,14 @@ __device__ __forceinline__ void stage_tile(const T* __restrict__ src, int gh, in
     const int pos = e / groups, cg = e % groups;
     const int ii = ti0 + pos / SP - R, jj = tj0 + pos % SP - R;
     in[it] = e < total && ii >= 0 && ii < gh && jj >= 0 && jj < gw;
-    if (in[it]) {
-      load8<T>(src + ((long long)ii * gw + jj) * d + cg * 8, x[it]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[it][i] = 0.f;
-    }
+    load8<T>(src + (in[it] ? ((long long)ii * gw + jj) * d + cg * 8 : 0LL), x[it]);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int e = threadIdx.x + it * kWaves * 64;
     if (e >= total) break;
-    if (in[it]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[it][i] = (x[it][i] - mu[i]) * rs[i];
-    }
+    for (int i = 0; i < 8; ++i) x[it][i] = in[it] ? (x[it][i] - mu[i]) * rs[i] : 0.f;
     float4* dst = reinterpret_cast<float4*>(tile + (size_t)e * 8);   // pos * d + cg * 8 == 8 e
     dst[0] = make_float4(x[it][0], x[it][1], x[it][2], x[it][3]);
     dst[1] = make_float4(x[it][4], x[it][5], x[it][6], x[it][7]);
@@ -132,11 +127,16 @@ __global__ void __launch_bounds__(kWaves * 64) k_dw_grad_tile(Problem pb, WRef W
   const bool mse = pb.loss == LOSS_MSE;
   const int cg = threadIdx.x % (d >> 3);
   float smu[8], srs[8];
+  if (pb.stats) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = cg * 8 + i;
-    smu[i] = pb.stats ? pb.stats[((size_t)p * d + c) * 2] : 0.f;
-    srs[i] = pb.stats ? pb.stats[((size_t)p * d + c) * 2 + 1] : 1.f;
+    for (int i = 0; i < 8; ++i) {
+      const int c = cg * 8 + i;
+      smu[i] = pb.stats[((size_t)p * d + c) * 2];
+      srs[i] = pb.stats[((size_t)p * d + c) * 2 + 1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { smu[i] = 0.f; srs[i] = 1.f; }
   }
   float acc[U][KK], wr[U][KK];
 #pragma unroll
@@ -163,12 +163,15 @@ __global__ void __launch_bounds__(kWaves * 64) k_dw_grad_tile(Problem pb, WRef W
         const int e = threadIdx.x + it * kWaves * 64, tt = e / groups;
         const int i = ti0 + tt / kTile, j = tj0 + tt % kTile;
         const bool ok = e < kTileTok * groups && i < gh && j < gw;
-        const T* src = vp + ((long long)i * gw + j) * d + (e % groups) * 8;
+        // outside the raster: read the pair's first row, zeroed below
+        const T* src = vp + (ok ? ((long long)i * gw + j) * d + (e % groups) * 8 : 0LL);
         if constexpr (sizeof(T) == 2) {
-          vb[it] = ok ? *reinterpret_cast<const bf16x8*>(src) : bf16x8{};
+          vb[it] = *reinterpret_cast<const bf16x8*>(src);
+          if (!ok) vb[it] = bf16x8{};
         } else {
-          vf[it][0] = ok ? reinterpret_cast<const float4*>(src)[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-          vf[it][1] = ok ? reinterpret_cast<const float4*>(src)[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+          vf[it][0] = reinterpret_cast<const float4*>(src)[0];
+          vf[it][1] = reinterpret_cast<const float4*>(src)[1];
+          if (!ok) vf[it][0] = vf[it][1] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
       float ev = 0.f;

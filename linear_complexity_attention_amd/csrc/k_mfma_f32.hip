@@ -101,22 +101,30 @@ __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int
   // this slice's k range, in whole BK tiles
   const int nkt = (K + BK - 1) / BK;
   const int kt0 = (int)((long long)ks * nkt / KS), kt1 = (int)((long long)(ks + 1) * nkt / KS);
-  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 ra, rb;
+  // An out-of-range element is read at the operand's first element and masked
+  // after the load.  Written as a conditional load, it was compiled into a
+  // select between the global address and a private one holding the zero, as
+  // four flat loads, which the LDS waits of the MFMA loop count as well: the
+  // next tile's loads then stalled every fragment read.
+  auto ld4 = [](const float* base, long long off, bool ok) {
+    const float4 v = *reinterpret_cast<const float4*>(base + (ok ? off : 0));
+    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
   auto load = [&](int k0) {
     if (!TA) {   // A[m][k]: thread -> row m, four k
       const int m = m0 + (tid >> 2), k = k0 + 4 * (tid & 3);
-      ra = m < M && k < K ? *reinterpret_cast<const float4*>(a + (long long)m * A.ld + k) : zero;
+      ra = ld4(a, (long long)m * A.ld + k, m < M && k < K);
     } else {     // stored [k][m]: thread -> row k, four m
       const int k = k0 + (tid >> 4), m = m0 + 4 * (tid & 15);
-      ra = k < K && m < M ? *reinterpret_cast<const float4*>(a + (long long)k * A.ld + m) : zero;
+      ra = ld4(a, (long long)k * A.ld + m, k < K && m < M);
     }
     if (!TB) {   // B[k][n]: thread -> row k, four n
       const int k = k0 + (tid >> 4), n = n0 + 4 * (tid & 15);
-      rb = k < K && n < N ? *reinterpret_cast<const float4*>(b + (long long)k * B.ld + n) : zero;
+      rb = ld4(b, (long long)k * B.ld + n, k < K && n < N);
     } else {     // stored [n][k]: thread -> row n, four k
       const int n = n0 + (tid >> 2), k = k0 + 4 * (tid & 3);
-      rb = n < N && k < K ? *reinterpret_cast<const float4*>(b + (long long)n * B.ld + k) : zero;
+      rb = ld4(b, (long long)n * B.ld + k, n < N && k < K);
     }
   };
   auto store = [&](int buf) {
@@ -171,35 +179,55 @@ __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int
       __syncthreads();
     }
   }
+  // Epilogue.  The inputs of all 16 elements (C when accumulating, and the
+  // epilogue's operands) are loaded first, unconditionally, at the tile's
+  // first element when out of range, so that their loads are in flight
+  // together; then the in-range elements are computed and stored.
+  const long long tb = (c - C.p) + (long long)m0 * C.ld + n0;   // the tile's first element
+  constexpr int NIN = EPI == EPI_ZBAR ? 3 : (EPI == EPI_GP ? 1 : 0);
+  int off[2][2][4];
+  float prev[2][2][4], in[NIN > 0 ? NIN : 1][2][2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + 32 * wn + 16 * j + (lane & 15);
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + 32 * wm + 16 * i + 4 * (lane >> 4) + e;
-        if (m < M && n < N) {
-          const long long oi = (long long)m * C.ld + n;
-          float* o = c + oi;
-          const float v = accumulate ? *o + alpha * acc[i][j][e] : alpha * acc[i][j][e];
-          if constexpr (EPI == EPI_STORE) {
-            *o = v;
-          } else if constexpr (EPI == EPI_GELU) {
-            *o = v;
-            (ep.out2 + (o - C.p))[0] = gelu_exact(v);
-          } else if constexpr (EPI == EPI_GP) {
-            const float gp = gelu_exact_prime((ep.z + (o - C.p))[0]);
-            if (ep.out2 != C.p) *o = v;
-            (ep.out2 + (o - C.p))[0] = v * gp;
-          } else {
-            const long long q = o - C.p;
-            const float zz = ep.z[q];
-            *o = gelu_second_f(zz) * ep.zd[q] * ep.da[q] + gelu_exact_prime(zz) * v;
-          }
+        const int nn = 32 * wn + 16 * j + (lane & 15);
+        const int mm = 32 * wm + 16 * i + 4 * (lane >> 4) + e;
+        const bool ok = m0 + mm < M && n0 + nn < N;
+        off[i][j][e] = ok ? mm * C.ld + nn : -1;
+        const long long q = tb + (ok ? mm * C.ld + nn : 0);
+        prev[i][j][e] = accumulate ? C.p[q] : 0.f;
+        if constexpr (NIN >= 1) in[0][i][j][e] = ep.z[q];
+        if constexpr (NIN >= 3) {
+          in[1][i][j][e] = ep.zd[q];
+          in[2][i][j][e] = ep.da[q];
         }
       }
-    }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (off[i][j][e] < 0) continue;
+        const long long q = tb + off[i][j][e];
+        const float v = accumulate ? prev[i][j][e] + alpha * acc[i][j][e] : alpha * acc[i][j][e];
+        if constexpr (EPI == EPI_STORE) {
+          C.p[q] = v;
+        } else if constexpr (EPI == EPI_GELU) {
+          C.p[q] = v;
+          ep.out2[q] = gelu_exact(v);
+        } else if constexpr (EPI == EPI_GP) {
+          const float gp = gelu_exact_prime(in[0][i][j][e]);
+          if (ep.out2 != C.p) C.p[q] = v;
+          ep.out2[q] = v * gp;
+        } else {
+          const float zz = in[0][i][j][e];
+          C.p[q] = gelu_second_f(zz) * in[1][i][j][e] * in[2][i][j][e] + gelu_exact_prime(zz) * v;
+        }
+      }
 }
 
 // ---------------------------------------------------------------------------

@@ -127,22 +127,32 @@ __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int
       // A (and B^T) rows along k into [k][row], B [K][Nc] rows into [k][col]
       constexpr int NV = kBT * kBK / 4 / 256;      // float4 per thread and operand (8)
       const int k4 = kc / 4;
+      // out-of-range elements are read at the batch entry's first element and
+      // masked after the load, so that no load waits under a branch of its own
       float4 av[NV], bv[NV];
+      bool aok[NV], bok[NV];
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
         const int f = threadIdx.x + 256 * u;
-        av[u] = float4{0.f, 0.f, 0.f, 0.f};
-        bv[u] = float4{0.f, 0.f, 0.f, 0.f};
-        if (f < kBT * k4) {
-          const int rr = f / k4, kk = 4 * (f % k4);
-          if (r0 + rr < M) av[u] = *reinterpret_cast<const float4*>(A + (long long)(r0 + rr) * K + k0 + kk);
-          if (transB) {
-            if (c0 + rr < Nc) bv[u] = *reinterpret_cast<const float4*>(B + (long long)(c0 + rr) * K + k0 + kk);
-          } else {
-            const int kr = f / (kBT / 4), cc = 4 * (f % (kBT / 4));
-            if (c0 + cc < Nc) bv[u] = *reinterpret_cast<const float4*>(B + (long long)(k0 + kr) * Nc + c0 + cc);
-          }
+        const bool fin = f < kBT * k4;
+        const int rr = fin ? f / k4 : 0, kk = fin ? 4 * (f % k4) : 0;
+        aok[u] = fin && r0 + rr < M;
+        av[u] = *reinterpret_cast<const float4*>(A + (aok[u] ? (long long)(r0 + rr) * K + k0 + kk : 0LL));
+        long long bo;
+        if (transB) {
+          bok[u] = fin && c0 + rr < Nc;
+          bo = (long long)(c0 + rr) * K + k0 + kk;
+        } else {
+          const int kr = f / (kBT / 4), cc = 4 * (f % (kBT / 4));
+          bok[u] = fin && c0 + cc < Nc;
+          bo = (long long)(k0 + kr) * Nc + c0 + cc;
         }
+        bv[u] = *reinterpret_cast<const float4*>(B + (bok[u] ? bo : 0LL));
+      }
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        if (!aok[u]) av[u] = float4{0.f, 0.f, 0.f, 0.f};
+        if (!bok[u]) bv[u] = float4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
@@ -182,15 +192,28 @@ __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int
     }
     __syncthreads();
   }
+  // D's four values are loaded together (at the entry's first element when
+  // out of range) before the stores
+  float dv[2][2] = {};
+  if (D) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const int r = r0 + 2 * ty + u, c = c0 + 2 * tx + v;
+        dv[u][v] = D[r < M && c < Nc ? (long long)r * Nc + c : 0LL];
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) dv[u][v] *= beta;
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       const int r = r0 + 2 * ty + u, c = c0 + 2 * tx + v;
-      if (r < M && c < Nc) {
-        const long long e = (long long)r * Nc + c;
-        C[e] = alpha * acc[u][v] + (D ? beta * D[e] : 0.f);
-      }
+      if (r < M && c < Nc) C[(long long)r * Nc + c] = alpha * acc[u][v] + dv[u][v];
     }
 }
 

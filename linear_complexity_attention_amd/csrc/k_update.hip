@@ -187,19 +187,26 @@ __global__ void __launch_bounds__(kRCols * kRLanes) k_renorm(Problem pb, UpdateA
   float* nxt = a.next + ((size_t)p * pb.nm + i) * pb.msz;
   constexpr int kWaves = kRCols * kRLanes / 64;   // each wave holds 4 row lanes of every column
   __shared__ float red[2][kWaves][kRCols];
-  float v[RMAX];
-  float nn = 0.f, nr = 0.f;
+  // the register block's loads are issued together: row and column are
+  // clamped into the matrix and the out-of-range values are masked after the
+  // loads, so no load sits under its own branch (a wait after each of them)
+  const int jc = live ? j : cols - 1;
+  float v[RMAX], v0[RMAX];
 #pragma unroll
   for (int k = 0; k < RMAX; ++k) {
     const int r = lane + kRLanes * k;
-    v[k] = 0.f;
-    if (live && r < rows) {
-      const size_t e = (size_t)r * cols + j;
-      v[k] = nxt[e];
-      const float w0v = w0[e];
-      nn += v[k] * v[k];
-      nr += w0v * w0v;
-    }
+    const size_t e = (size_t)(r < rows ? r : rows - 1) * cols + jc;
+    v[k] = nxt[e];
+    v0[k] = w0[e];
+  }
+  float nn = 0.f, nr = 0.f;
+#pragma unroll
+  for (int k = 0; k < RMAX; ++k) {
+    const bool in = live && lane + kRLanes * k < rows;
+    v[k] = in ? v[k] : 0.f;
+    const float w0v = in ? v0[k] : 0.f;
+    nn += v[k] * v[k];
+    nr += w0v * w0v;
   }
   if (live)                                  // rows beyond the register block: read twice
     for (int r = lane + kRLanes * RMAX; r < rows; r += kRLanes) {
