@@ -99,9 +99,13 @@ __global__ void __launch_bounds__(256) k_ns_init(Problem pb, const float* __rest
 // A [M][K], op(B) = B [K][Nc] or (transB) B^T with B [Nc][K], C, D [M][Nc];
 // all row-major, contiguous, batch entry z = p * nm + i at z * stride.
 // 32 x 32 output tiles (so a launch has P * nm * (M/32) * (Nc/32) workgroups)
-// and up to 256 of K staged in LDS at once ([k][row] and [k][col], 72 KB): the
-// workgroup pays one global round trip per 256 of K instead of one per
-// k-step.  Each thread computes a 2 x 2 block from float2 LDS reads.
+// and up to 256 of K staged in LDS at once (A and B^T as [row][k], B as
+// [k][col], 70 KB), each operand in its stored orientation so that the LDS
+// stores are 16 bytes; the workgroup pays one global round trip per 256 of K
+// instead of one per k-step.  Wave w computes the 16 x 16 block (16 (w / 2), 16 (w % 2)) on
+// v_mfma_f32_16x16x4f32 (fp32 operands and sums): lane l supplies
+// A[16 (w / 2) + l % 16][4 s + l / 16] and B[4 s + l / 16][16 (w % 2) + l % 16]
+// and holds the result rows 4 (l / 16) + e, column l % 16.
 // grid = (ceil(Nc / 32), ceil(M / 32), nm * P), 256 threads.
 constexpr int kBT = 32, kBK = 256, kBP = kBT + 4;
 __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int Nc, int K, float alpha,
@@ -114,17 +118,23 @@ __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int
   const int r0 = blockIdx.y * kBT, c0 = blockIdx.x * kBT;
   A += z * sA; B += z * sB; C += z * sC;
   if (D) D += z * sD;
-  __shared__ __attribute__((aligned(16))) float As[kBK][kBP];   // [k][row]
-  __shared__ __attribute__((aligned(16))) float Bs[kBK][kBP];   // [k][col]
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  float acc[2][2] = {};
+  // [row][k] rows of kBK + 4 floats: the fragment reads (16 rows x 4 k per
+  // wave) fall on 64 distinct banks
+  constexpr int LA = kBK + 4, NB = kBK * kBP > kBT * LA ? kBK * kBP : kBT * LA;
+  __shared__ __attribute__((aligned(16))) float smem[kBT * LA + NB];
+  float(*As)[LA] = reinterpret_cast<float(*)[LA]>(smem);                 // A [row][k]
+  float(*Bt)[LA] = reinterpret_cast<float(*)[LA]>(smem + kBT * LA);      // B^T [col][k] (transB)
+  float(*Bs)[kBP] = reinterpret_cast<float(*)[kBP]>(smem + kBT * LA);    // B [k][col]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wi = w >> 1, wj = w & 1;
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   // float4 loads need 16-byte aligned rows and batch entries
   const bool vec = K % 4 == 0 && Nc % 4 == 0 && sA % 4 == 0 && sB % 4 == 0;
   for (int k0 = 0; k0 < K; k0 += kBK) {
     const int kc = min(kBK, K - k0);
     if (vec && kc % 4 == 0) {
       // float4 loads, all of a thread's loads in flight before the LDS stores:
-      // A (and B^T) rows along k into [k][row], B [K][Nc] rows into [k][col]
+      // A (and B^T) rows along k into [row][k], B [K][Nc] rows into [k][col]
       constexpr int NV = kBT * kBK / 4 / 256;      // float4 per thread and operand (8)
       const int k4 = kc / 4;
       // out-of-range elements are read at the batch entry's first element and
@@ -159,9 +169,9 @@ __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int
         const int f = threadIdx.x + 256 * u;
         if (f < kBT * k4) {
           const int rr = f / k4, kk = 4 * (f % k4);
-          As[kk][rr] = av[u].x; As[kk + 1][rr] = av[u].y; As[kk + 2][rr] = av[u].z; As[kk + 3][rr] = av[u].w;
+          *reinterpret_cast<float4*>(&As[rr][kk]) = av[u];
           if (transB) {
-            Bs[kk][rr] = bv[u].x; Bs[kk + 1][rr] = bv[u].y; Bs[kk + 2][rr] = bv[u].z; Bs[kk + 3][rr] = bv[u].w;
+            *reinterpret_cast<float4*>(&Bt[rr][kk]) = bv[u];
           } else {
             const int kr = f / (kBT / 4), cc = 4 * (f % (kBT / 4));
             *reinterpret_cast<float4*>(&Bs[kr][cc]) = bv[u];
@@ -171,8 +181,8 @@ __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int
     } else {
       for (int t = threadIdx.x; t < kBT * kc; t += 256) {
         const int rr = t / kc, kk = t % kc;
-        As[kk][rr] = (r0 + rr < M) ? A[(long long)(r0 + rr) * K + k0 + kk] : 0.f;
-        if (transB) Bs[kk][rr] = (c0 + rr < Nc) ? B[(long long)(c0 + rr) * K + k0 + kk] : 0.f;
+        As[rr][kk] = (r0 + rr < M) ? A[(long long)(r0 + rr) * K + k0 + kk] : 0.f;
+        if (transB) Bt[rr][kk] = (c0 + rr < Nc) ? B[(long long)(c0 + rr) * K + k0 + kk] : 0.f;
       }
       if (!transB)
         for (int t = threadIdx.x; t < kBT * kc; t += 256) {
@@ -180,41 +190,49 @@ __global__ void __launch_bounds__(256) k_bgemm(int nm, unsigned mask, int M, int
           Bs[kr][cc] = (c0 + cc < Nc) ? B[(long long)(k0 + kr) * Nc + c0 + cc] : 0.f;
         }
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kc; ++kk) {
-      const float2 a = *reinterpret_cast<const float2*>(&As[kk][2 * ty]);
-      const float2 b = *reinterpret_cast<const float2*>(&Bs[kk][2 * tx]);
-      acc[0][0] = fmaf(a.x, b.x, acc[0][0]);
-      acc[0][1] = fmaf(a.x, b.y, acc[0][1]);
-      acc[1][0] = fmaf(a.y, b.x, acc[1][0]);
-      acc[1][1] = fmaf(a.y, b.y, acc[1][1]);
+    // k rows up to the next multiple of 4 are zero (the MFMA takes 4 of k)
+    const int kc4 = (kc + 3) & ~3;
+    for (int t = threadIdx.x; t < (kc4 - kc) * kBT; t += 256) {
+      const int kk = kc + t / kBT, x = t % kBT;
+      As[x][kk] = 0.f;
+      if (transB) Bt[x][kk] = 0.f;
+      else Bs[kk][x] = 0.f;
     }
+    __syncthreads();
+    // eight k-steps' fragments are read before their MFMAs, which alternate
+    // between two accumulators
+    const int kq = lane >> 4, ca = 16 * wi + (lane & 15), cb = 16 * wj + (lane & 15);
+    auto bfrag = [&](int k) { return transB ? Bt[cb][k] : Bs[k][cb]; };
+    int s4 = 0;
+    for (; s4 + 32 <= kc4; s4 += 32) {
+      float a[8], b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { a[u] = As[ca][s4 + 4 * u + kq]; b[u] = bfrag(s4 + 4 * u + kq); }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], acc[u & 1], 0, 0, 0);
+    }
+    for (; s4 < kc4; s4 += 4)
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(As[ca][s4 + kq], bfrag(s4 + kq), acc[0], 0, 0, 0);
     __syncthreads();
   }
   // D's four values are loaded together (at the entry's first element when
   // out of range) before the stores
-  float dv[2][2] = {};
+  float dv[4] = {0.f, 0.f, 0.f, 0.f};
+  const int c = c0 + 16 * wj + (lane & 15);
   if (D) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + 16 * wi + 4 * (lane >> 4) + e;
+      dv[e] = D[r < M && c < Nc ? (long long)r * Nc + c : 0LL];
+    }
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const int r = r0 + 2 * ty + u, c = c0 + 2 * tx + v;
-        dv[u][v] = D[r < M && c < Nc ? (long long)r * Nc + c : 0LL];
-      }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int v = 0; v < 2; ++v) dv[u][v] *= beta;
+    for (int e = 0; e < 4; ++e) dv[e] *= beta;
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int r = r0 + 2 * ty + u, c = c0 + 2 * tx + v;
-      if (r < M && c < Nc) C[(long long)r * Nc + c] = alpha * acc[u][v] + dv[u][v];
-    }
+  for (int e = 0; e < 4; ++e) {
+    const int r = r0 + 16 * wi + 4 * (lane >> 4) + e;
+    if (r < M && c < Nc) C[(long long)r * Nc + c] = alpha * (acc[0][e] + acc[1][e]) + dv[e];
+  }
 }
 
 // next -= scale * X (back in the [in, out] orientation), W_out if requested;
