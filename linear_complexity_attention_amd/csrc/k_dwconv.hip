@@ -309,21 +309,32 @@ __global__ void __launch_bounds__(kWaves * 64) k_dw_grad(Problem pb, WRef W, int
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int L = (N + S - 1) / S, n0 = s * L, n1 = min(N, n0 + L);
   const bool mse = pb.loss == LOSS_MSE;
+  // Lanes past d repeat channel d - 1 (their sums are never written), and
+  // neighbours outside the raster are read at the nearest raster position
+  // and zeroed, so that no load sits under a branch of its own (each would
+  // be waited for before the next is issued).
   float acc[2][KK], wr[2][KK], mu[2] = {0.f, 0.f}, rs[2] = {1.f, 1.f};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int c = lane + 64 * u;
+    const int c = min(lane + 64 * u, d - 1);
 #pragma unroll
-    for (int t = 0; t < KK; ++t) { acc[u][t] = 0.f; wr[u][t] = (mse && c < d) ? w[c * KK + t] : 0.f; }
-    if (pb.stats && c < d) { mu[u] = pb.stats[((size_t)p * d + c) * 2]; rs[u] = pb.stats[((size_t)p * d + c) * 2 + 1]; }
+    for (int t = 0; t < KK; ++t) acc[u][t] = 0.f;
+    if (mse) {
+#pragma unroll
+      for (int t = 0; t < KK; ++t) wr[u][t] = w[c * KK + t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < KK; ++t) wr[u][t] = 0.f;
+    }
+    if (pb.stats) { mu[u] = pb.stats[((size_t)p * d + c) * 2]; rs[u] = pb.stats[((size_t)p * d + c) * 2 + 1]; }
   }
   for (int n = n0 + wv; n < n1; n += kWaves) {
     const int i = n / gw, j = n % gw;
     const float et = pb.eta_scale * (ep ? ep[n] : 1.f);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int c = lane + 64 * u;
-      if (c >= d) continue;
+      if (64 * u >= d) break;
+      const int c = min(lane + 64 * u, d - 1);
       float nb[KK];
 #pragma unroll
       for (int a = 0; a < K; ++a)
@@ -331,7 +342,9 @@ __global__ void __launch_bounds__(kWaves * 64) k_dw_grad(Problem pb, WRef W, int
         for (int bb = 0; bb < K; ++bb) {
           const int ii = i + a - R, jj = j + bb - R;
           const bool in = ii >= 0 && ii < gh && jj >= 0 && jj < gw;
-          nb[a * K + bb] = in ? (ldf(kp + ((long long)ii * gw + jj) * d + c) - mu[u]) * rs[u] : 0.f;
+          const int iic = min(max(ii, 0), gh - 1), jjc = min(max(jj, 0), gw - 1);
+          const float x = ldf(kp + ((long long)iic * gw + jjc) * d + c);
+          nb[a * K + bb] = in ? (x - mu[u]) * rs[u] : 0.f;
         }
       const float vv = ldf(vp + (long long)n * d + c);
       float g;
@@ -376,28 +389,39 @@ __global__ void __launch_bounds__(kWaves * 64) k_dw_query(Problem pb, const floa
   T* op = (T*)pb.o + prow * N * d;
   const float* w = state + (long long)p * pb.msz;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // lanes past d repeat channel d - 1 and store nothing; neighbours outside
+  // the raster are read at the nearest raster position and left out of the
+  // sum, so that the loads of a token are all in flight together
   float wr[2][KK];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int t = 0; t < KK; ++t) wr[u][t] = lane + 64 * u < d ? w[(lane + 64 * u) * KK + t] : 0.f;
+    for (int t = 0; t < KK; ++t) wr[u][t] = w[min(lane + 64 * u, d - 1) * KK + t];
   const int n0 = blockIdx.x * kQTok, n1 = min(N, n0 + kQTok);
   for (int n = n0 + wv; n < n1; n += kWaves) {
     const int i = n / gw, j = n % gw;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int c = lane + 64 * u;
-      if (c >= d) continue;
+      if (64 * u >= d) break;
+      const int c = min(lane + 64 * u, d - 1);
+      float x[KK];
+#pragma unroll
+      for (int a = 0; a < K; ++a)
+#pragma unroll
+        for (int bb = 0; bb < K; ++bb) {
+          const int iic = min(max(i + a - R, 0), gh - 1), jjc = min(max(j + bb - R, 0), gw - 1);
+          x[a * K + bb] = ldf(qp + ((long long)iic * gw + jjc) * d + c);
+        }
       float f = 0.f;
 #pragma unroll
       for (int a = 0; a < K; ++a)
 #pragma unroll
         for (int bb = 0; bb < K; ++bb) {
           const int ii = i + a - R, jj = j + bb - R;
-          if (ii >= 0 && ii < gh && jj >= 0 && jj < gw)
-            f = fmaf(wr[u][a * K + bb], ldf(qp + ((long long)ii * gw + jj) * d + c), f);
+          const bool in = ii >= 0 && ii < gh && jj >= 0 && jj < gw;
+          f = in ? fmaf(wr[u][a * K + bb], x[a * K + bb], f) : f;
         }
-      op[(long long)n * d + c] = from_f32<T>(f);
+      if (lane + 64 * u < d) op[(long long)n * d + c] = from_f32<T>(f);
     }
   }
 }
