@@ -32,6 +32,8 @@
 // so one kernel takes all pairs at once (grid z = pair) in 64 x 64 output
 // tiles; the reductions over the tokens split K and add the slices in order.
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 
 #include "ttt_internal.h"
 
@@ -89,7 +91,7 @@ constexpr int CS = BM + 4;   // row stride (floats) of the output tile staged in
 
 template <bool TA, bool TB, int EPI>
 __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int KS, Op A, Op B, OutOp C,
-                                                 float alpha, int accumulate, int vec, Epi ep) {
+                                                 float alpha, int accumulate, Epi ep) {
   // operand tiles; after the main loop the output tile [BM][CS] reuses them
   __shared__ __attribute__((aligned(16))) float smem[4 * BK * LS];
   static_assert(BM * CS <= 4 * BK * LS, "output tile exceeds the operand tiles");
@@ -184,125 +186,75 @@ __global__ void __launch_bounds__(kT) k_gemm_f32(int H, int M, int N, int K, int
       __syncthreads();
     }
   }
+  // Epilogue through LDS: the accumulators go to the [64][CS] output tile,
+  // then thread t takes columns 4 (t % 16) .. + 3 of rows t / 16 + 16 k, so
+  // that every load and store of C and of the epilogue operands is 16 bytes
+  // and a wave covers 4 whole tile rows (stores straight from the MFMA layout
+  // write 64-byte pieces of rows).  The inputs of the 4 rows are loaded
+  // before any is used, at the tile's first element when out of range.
+  // Requires 16-byte aligned rows of C and of the epilogue operands and N a
+  // multiple of 4 (checked by the launcher).
   const long long tb = (c - C.p) + (long long)m0 * C.ld + n0;   // the tile's first element
   constexpr int NIN = EPI == EPI_ZBAR ? 3 : (EPI == EPI_GP ? 1 : 0);
-  if (vec) {
-    // Epilogue through LDS (C and the epilogue operands 16-byte aligned, N a
-    // multiple of 4): the accumulators go to the [64][CS] output tile, then
-    // thread t takes columns 4 (t % 16) .. + 3 of rows t / 16 + 16 k, so that
-    // every load and store is 16 bytes and a wave covers 4 whole tile rows
-    // (direct stores from the MFMA layout write 64-byte pieces of rows).
-    // The inputs of the 4 rows are loaded before any is used, at the tile's
-    // first element when out of range.
-    __syncthreads();   // every wave has read its last fragments
+  __syncthreads();   // every wave has read its last fragments
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          smem[(32 * wm + 16 * i + 4 * (lane >> 4) + e) * CS + 32 * wn + 16 * j + (lane & 15)] = acc[i][j][e];
-    __syncthreads();
-    const int nn = 4 * (tid & 15), rr = tid >> 4;
-    const bool colok = n0 + nn < N;
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 pv[4], x0[4], x1[4], x2[4];
-    int offv[4];
+      for (int e = 0; e < 4; ++e)
+        smem[(32 * wm + 16 * i + 4 * (lane >> 4) + e) * CS + 32 * wn + 16 * j + (lane & 15)] = acc[i][j][e];
+  __syncthreads();
+  const int nn = 4 * (tid & 15), rr = tid >> 4;
+  const bool colok = n0 + nn < N;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 pv[4], x0[4], x1[4], x2[4];
+  int offv[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int mm = rr + 16 * k;
-      const bool ok = colok && m0 + mm < M;
-      offv[k] = ok ? mm * C.ld + nn : -1;
-      const long long q = tb + (ok ? mm * C.ld + nn : 0);
-      pv[k] = accumulate ? *reinterpret_cast<const float4*>(C.p + q) : z4;
-      if constexpr (NIN >= 1) x0[k] = *reinterpret_cast<const float4*>(ep.z + q);
-      if constexpr (NIN >= 3) {
-        x1[k] = *reinterpret_cast<const float4*>(ep.zd + q);
-        x2[k] = *reinterpret_cast<const float4*>(ep.da + q);
-      }
+  for (int k = 0; k < 4; ++k) {
+    const int mm = rr + 16 * k;
+    const bool ok = colok && m0 + mm < M;
+    offv[k] = ok ? mm * C.ld + nn : -1;
+    const long long q = tb + (ok ? mm * C.ld + nn : 0);
+    pv[k] = accumulate ? *reinterpret_cast<const float4*>(C.p + q) : z4;
+    if constexpr (NIN >= 1) x0[k] = *reinterpret_cast<const float4*>(ep.z + q);
+    if constexpr (NIN >= 3) {
+      x1[k] = *reinterpret_cast<const float4*>(ep.zd + q);
+      x2[k] = *reinterpret_cast<const float4*>(ep.da + q);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (offv[k] < 0) continue;
-      const long long q = tb + offv[k];
-      const float4 a4 = *reinterpret_cast<const float4*>(&smem[(rr + 16 * k) * CS + nn]);
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-      const float pp[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
-      float v[4], o2[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = accumulate ? pp[u] + alpha * av[u] : alpha * av[u];
-      if constexpr (EPI == EPI_STORE) {
-        *reinterpret_cast<float4*>(C.p + q) = make_float4(v[0], v[1], v[2], v[3]);
-      } else if constexpr (EPI == EPI_GELU) {
-        *reinterpret_cast<float4*>(C.p + q) = make_float4(v[0], v[1], v[2], v[3]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) o2[u] = gelu_exact(v[u]);
-        *reinterpret_cast<float4*>(ep.out2 + q) = make_float4(o2[0], o2[1], o2[2], o2[3]);
-      } else if constexpr (EPI == EPI_GP) {
-        const float zz[4] = {x0[k].x, x0[k].y, x0[k].z, x0[k].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) o2[u] = v[u] * gelu_exact_prime(zz[u]);
-        if (ep.out2 != C.p) *reinterpret_cast<float4*>(C.p + q) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(ep.out2 + q) = make_float4(o2[0], o2[1], o2[2], o2[3]);
-      } else {
-        const float zz[4] = {x0[k].x, x0[k].y, x0[k].z, x0[k].w};
-        const float zd[4] = {x1[k].x, x1[k].y, x1[k].z, x1[k].w};
-        const float da[4] = {x2[k].x, x2[k].y, x2[k].z, x2[k].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) o2[u] = gelu_second_f(zz[u]) * zd[u] * da[u] + gelu_exact_prime(zz[u]) * v[u];
-        *reinterpret_cast<float4*>(C.p + q) = make_float4(o2[0], o2[1], o2[2], o2[3]);
-      }
-    }
-    return;
   }
-  // Epilogue straight from the MFMA layout.  The inputs of all 16 elements
-  // (C when accumulating, and the epilogue's operands) are loaded first,
-  // unconditionally, at the tile's first element when out of range, so that
-  // their loads are in flight together; then the in-range elements are
-  // computed and stored.
-  int off[2][2][4];
-  float prev[2][2][4], in[NIN > 0 ? NIN : 1][2][2][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int k = 0; k < 4; ++k) {
+    if (offv[k] < 0) continue;
+    const long long q = tb + offv[k];
+    const float4 a4 = *reinterpret_cast<const float4*>(&smem[(rr + 16 * k) * CS + nn]);
+    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+    const float pp[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
+    float v[4], o2[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int u = 0; u < 4; ++u) v[u] = accumulate ? pp[u] + alpha * av[u] : alpha * av[u];
+    if constexpr (EPI == EPI_STORE) {
+      *reinterpret_cast<float4*>(C.p + q) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (EPI == EPI_GELU) {
+      *reinterpret_cast<float4*>(C.p + q) = make_float4(v[0], v[1], v[2], v[3]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int nn = 32 * wn + 16 * j + (lane & 15);
-        const int mm = 32 * wm + 16 * i + 4 * (lane >> 4) + e;
-        const bool ok = m0 + mm < M && n0 + nn < N;
-        off[i][j][e] = ok ? mm * C.ld + nn : -1;
-        const long long q = tb + (ok ? mm * C.ld + nn : 0);
-        prev[i][j][e] = accumulate ? C.p[q] : 0.f;
-        if constexpr (NIN >= 1) in[0][i][j][e] = ep.z[q];
-        if constexpr (NIN >= 3) {
-          in[1][i][j][e] = ep.zd[q];
-          in[2][i][j][e] = ep.da[q];
-        }
-      }
+      for (int u = 0; u < 4; ++u) o2[u] = gelu_exact(v[u]);
+      *reinterpret_cast<float4*>(ep.out2 + q) = make_float4(o2[0], o2[1], o2[2], o2[3]);
+    } else if constexpr (EPI == EPI_GP) {
+      const float zz[4] = {x0[k].x, x0[k].y, x0[k].z, x0[k].w};
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int u = 0; u < 4; ++u) o2[u] = v[u] * gelu_exact_prime(zz[u]);
+      if (ep.out2 != C.p) *reinterpret_cast<float4*>(C.p + q) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(ep.out2 + q) = make_float4(o2[0], o2[1], o2[2], o2[3]);
+    } else {
+      const float zz[4] = {x0[k].x, x0[k].y, x0[k].z, x0[k].w};
+      const float zd[4] = {x1[k].x, x1[k].y, x1[k].z, x1[k].w};
+      const float da[4] = {x2[k].x, x2[k].y, x2[k].z, x2[k].w};
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (off[i][j][e] < 0) continue;
-        const long long q = tb + off[i][j][e];
-        const float v = accumulate ? prev[i][j][e] + alpha * acc[i][j][e] : alpha * acc[i][j][e];
-        if constexpr (EPI == EPI_STORE) {
-          C.p[q] = v;
-        } else if constexpr (EPI == EPI_GELU) {
-          C.p[q] = v;
-          ep.out2[q] = gelu_exact(v);
-        } else if constexpr (EPI == EPI_GP) {
-          const float gp = gelu_exact_prime(in[0][i][j][e]);
-          if (ep.out2 != C.p) C.p[q] = v;
-          ep.out2[q] = v * gp;
-        } else {
-          const float zz = in[0][i][j][e];
-          C.p[q] = gelu_second_f(zz) * in[1][i][j][e] * in[2][i][j][e] + gelu_exact_prime(zz) * v;
-        }
-      }
+      for (int u = 0; u < 4; ++u) o2[u] = gelu_second_f(zz[u]) * zd[u] * da[u] + gelu_exact_prime(zz[u]) * v[u];
+      *reinterpret_cast<float4*>(C.p + q) = make_float4(o2[0], o2[1], o2[2], o2[3]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -434,15 +386,23 @@ template <bool TA, bool TB, int EPI = EPI_STORE>
 void gemm(int P, int H, int M, int N, int K, int KS, const Op& A, const Op& B, const OutOp& C, bool acc,
           hipStream_t st, float alpha = 1.0f, const Epi& ep = Epi{}) {
   const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, P * KS);
-  // the staged epilogue's 16-byte accesses: every row of C (and of the
-  // epilogue operands, which share C's layout) starts 16-byte aligned, and
-  // N is a multiple of 4
+  // The epilogue's 16-byte accesses need every row of C (and of the epilogue
+  // operands, which share C's layout) 16-byte aligned and N a multiple of 4.
+  // Every call meets this: C is workspace (256-byte aligned) or the
+  // caller's dq / dk (16-byte aligned, checked at the boundary), and the row
+  // lengths and strides are multiples of d or h, which this path requires to
+  // be multiples of 16.  A call that broke it would be a bug here, not a
+  // caller's error, so it stops the process rather than fault the GPU.
   auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   const bool vec = N % 4 == 0 && C.ld % 4 == 0 && C.sb % 4 == 0 && C.sh % 4 == 0 && C.cstride % 4 == 0 &&
                    al16(C.p) && (!ep.z || al16(ep.z)) && (!ep.zd || al16(ep.zd)) && (!ep.da || al16(ep.da)) &&
                    (!ep.out2 || al16(ep.out2));
+  if (!vec) {
+    std::fprintf(stderr, "ttt: fp32 product with an unaligned output (internal error)\n");
+    std::abort();
+  }
   hipLaunchKernelGGL((k_gemm_f32<TA, TB, EPI>), grid, dim3(kT), 0, st, H, M, N, K, KS, A, B, C, alpha, acc ? 1 : 0,
-                     vec ? 1 : 0, ep);
+                     ep);
 }
 
 // pair-major [P][rows][ld] buffer as an operand
