@@ -106,40 +106,62 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
 //   dW1 part: float4 ((qq*4 + cb)*NHB + hb)*64 + l  ->  dW1[16cb + 4g + i][qq*HP + 16hb + r]
 //   dW2 part: float4 ((qq*NHB + hb)*4 + cb)*64 + l  ->  dW2[qq*HP + 16hb + 4g + i][16cb + r]
 // with l = 16g + r, i = 0..3.  Thread = one float4 of the partial: it sums that
-// float4 over the pair's slots (coalesced) and updates the 4 weights it maps to.
+// float4 over the pair's slots (coalesced reads, slots in workgroup order).
+// The 256 float4s of a workgroup (four consecutive 64-float4 blocks of one
+// matrix) cover a block of whole matrix rows segments: W1 rows 16 cb0 ..
+// + 64/NHB, columns qq HP .. + HP; W2 16 whole rows.  The sums go through an
+// LDS copy of that block, so that W_cur, the momentum, the next state and
+// W_out are read and written as float4s along the rows (a direct store of the
+// register order writes 64-byte pieces of 4 rows per instruction).  The
+// arithmetic, and so the result, is that of the element-wise update.
 // grid = (D*HID/2 / 256, P).
 template <int HID, int HP>
 __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a) {
   constexpr int D = 64, NHB = HP / 16, HALF = D * HID / 4;   // float4s per matrix
+  static_assert(HALF % 256 == 0, "a workgroup's float4s lie in one matrix");
+  constexpr int LD0 = HP + 4, LD1 = D + 4;                  // LDS row strides (floats) of the W1 / W2 blocks
+  constexpr int TILE = (64 / NHB) * LD0 > 16 * LD1 ? (64 / NHB) * LD0 : 16 * LD1;
+  __shared__ __attribute__((aligned(16))) float tile[TILE];
   const int p = blockIdx.y;
   const int b = p / pb.H, h = p % pb.H;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= 2 * HALF) return;
-  const int mat = j >= HALF ? 1 : 0;
-  const int jj = j - mat * HALF;
+  const int mat = (int)blockIdx.x * 256 >= HALF ? 1 : 0;     // uniform
+  const int jj = (int)blockIdx.x * 256 + (int)threadIdx.x - mat * HALF;
   const int l = jj & 63, blk = jj >> 6, g = l >> 4, r = l & 15;
-  int base, step;                 // element offset of i = 0 inside the matrix, stride over i
+  const int blk0 = ((int)blockIdx.x * 256 - mat * HALF) >> 6, dl = blk - blk0;   // blk0 % 4 == 0
+  // the block: rows [row0, row0 + R) x columns [col0, col0 + CB) of a matrix with row stride RS
+  int row0, col0, CB, RS, lrw, lcw;                          // lrw + i, lcw: this thread's sums in the block
   if (mat == 0) {
-    const int hb = blk % NHB, cb = (blk / NHB) & 3, qq = blk / (4 * NHB);
-    base = (16 * cb + 4 * g) * HID + qq * HP + 16 * hb + r;
-    step = HID;
+    const int u0 = blk0 / NHB;                               // qq * 4 + cb0
+    row0 = 16 * (u0 & 3); col0 = (u0 >> 2) * HP; CB = HP; RS = HID;
+    lrw = 16 * (dl / NHB) + 4 * g; lcw = 16 * (dl % NHB) + r;
   } else {
-    const int cb = blk & 3, hb = (blk >> 2) % NHB, qq = blk / (4 * NHB);
-    base = (qq * HP + 16 * hb + 4 * g) * D + 16 * cb + r;
-    step = D;
+    row0 = 16 * (blk0 >> 2); col0 = 0; CB = D; RS = D;
+    lrw = 4 * g; lcw = 16 * dl + r;
   }
-  const long long wsz = 2LL * D * HID;
-  // W_cur's four values first, so that their loads overlap the partials'
+  const int LD = mat == 0 ? LD0 : LD1;
+  // this thread's float4 of the block in row order
+  const int lr = (int)threadIdx.x / (CB / 4), lc = 4 * ((int)threadIdx.x % (CB / 4));
+  const int e = (row0 + lr) * RS + col0 + lc;
   const float* cur = a.cur.mat(mat, b, h);
-  float c4[4];
+  float* out = a.out[mat] ? a.out[mat] + (size_t)pb.row(p) * D * HID : nullptr;
+  // W_cur first, so that its load overlaps the partials'
+  const bool v4 = ((reinterpret_cast<uintptr_t>(cur) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;   // uniform
+  float wc[4];
+  if (v4) {
+    const float4 t = *reinterpret_cast<const float4*>(cur + e);
+    wc[0] = t.x; wc[1] = t.y; wc[2] = t.z; wc[3] = t.w;
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) c4[i] = cur[base + i * step];
+    for (int i = 0; i < 4; ++i) wc[i] = cur[e + i];
+  }
   const bool upd = (a.mask >> mat) & 1u;
   long long q0, q1, C;
   sk_range(a, pb.B * pb.H, p, q0, q1, C);
-  if (a.sk_direct && q0 == q1) return;   // one workgroup held the whole pair and wrote its step
+  if (a.sk_direct && q0 == q1) return;   // one workgroup held the whole pair and wrote its step (uniform)
   if (!upd) q1 = q0 - 1;          // a matrix outside the mask keeps W_cur
   // the pair's slots, four loads in flight at a time, added in workgroup order
+  const long long wsz = 2LL * D * HID;
+  const int j = mat * HALF + jj;
   float4 sum = {0.f, 0.f, 0.f, 0.f};
   for (long long q = q0; q <= q1; q += 4) {
     float4 d[4];
@@ -150,21 +172,34 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
     for (int u = 0; u < 4; ++u)
       if (q + u <= q1) { sum.x += d[u].x; sum.y += d[u].y; sum.z += d[u].z; sum.w += d[u].w; }
   }
+  tile[(lrw + 0) * LD + lcw] = sum.x;
+  tile[(lrw + 1) * LD + lcw] = sum.y;
+  tile[(lrw + 2) * LD + lcw] = sum.z;
+  tile[(lrw + 3) * LD + lcw] = sum.w;
+  __syncthreads();
+  const float4 s = *reinterpret_cast<const float4*>(&tile[lr * LD + lc]);
+  const float s4[4] = {s.x, s.y, s.z, s.w};
   float* nxt = a.next + (size_t)p * wsz + (size_t)mat * D * HID;
-  float* out = a.out[mat] ? a.out[mat] + (size_t)pb.row(p) * D * HID : nullptr;
-  const float s4[4] = {sum.x, sum.y, sum.z, sum.w};
   float* mom = (upd && a.rule != RULE_GD) ? a.mom + (size_t)p * wsz + (size_t)mat * D * HID : nullptr;
+  float w[4];
+  if (mom) {
+    const float4 t = *reinterpret_cast<const float4*>(mom + e);
+    const float m4[4] = {a.beta * t.x + s4[0], a.beta * t.y + s4[1], a.beta * t.z + s4[2], a.beta * t.w + s4[3]};
+    *reinterpret_cast<float4*>(mom + e) = float4{m4[0], m4[1], m4[2], m4[3]};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = base + i * step;
-    float w = c4[i] - s4[i];
-    if (mom) {
-      const float m = a.beta * mom[e] + s4[i];
-      mom[e] = m;
-      w = a.mom_only ? c4[i] : c4[i] - m;
+    for (int i = 0; i < 4; ++i) w[i] = a.mom_only ? wc[i] : wc[i] - m4[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = wc[i] - s4[i];
+  }
+  *reinterpret_cast<float4*>(nxt + e) = float4{w[0], w[1], w[2], w[3]};
+  if (out) {
+    if (v4) {
+      *reinterpret_cast<float4*>(out + e) = float4{w[0], w[1], w[2], w[3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[e + i] = w[i];
     }
-    nxt[e] = w;
-    if (out) out[e] = w;
   }
 }
 
