@@ -6,20 +6,23 @@ leg of ``bench.py`` use it.  It shares no code with the HIP library.
 
 It is a plain, slow, direct transcription of what the pages define, in NumPy
 float64 (matmul is the only library primitive used for the algebra; ``erf`` comes
-from SciPy).  Pages cited (full addresses in the design doc):
+from SciPy).  Pages cited:
 
-* [ViT3]  ViT³ paper summary (podcasttoinsight), §02 "method essence" -- the
+* [ViT3]  ViT³ paper summary (app.podcasttoinsight.top, papers/vit3-test-time-
+  training-vision), §02 "method essence" -- the
   inner-loop update equation (forward on keys, one gradient step with rate eta,
   readout on queries); §03 guideline 1 (losses MSE / dot product), guideline 2
   (single epoch, full batch B = N), guideline 3 (eta = 1.0), guideline 4 (two-layer
   MLP widened to r*d), glossary entry "linear attention" (W = K^T V).
-* [LaCT]  "Test-Time Training Done Right" analysis (iplexlaw blog), sections
+* [LaCT]  "Test-Time Training Done Right" analysis (www.iplexlaw.co.kr, blog/lact-
+  large-chunk-test-time-training), sections
   "Fast weights as memory of the current context" (large chunks), "Nonlinear
   memory complements local attention" (SwiGLU fast weights with three matrices,
   negative dot-product loss, chunk gradients summed with per-token learning
   rates, L2 normalisation after the update), "Order of operations excludes
   leaking the future" (read-then-update per chunk; write-then-query for sets).
-* [TvS]   "Test-Time Training vs Sleep" compare page, section "Side one"
+* [TvS]   "Test-Time Training vs Sleep" compare page (researchpapers.dev, en/
+  compare/test-time-training-vs-sleep), section "Side one"
   (key instance normalisation removes the constant key shift; NaN without it).
 
 The update variants follow the same pages:
@@ -33,9 +36,9 @@ The update variants follow the same pages:
   chunks read) [LaCT "Order of operations..."].
 
 Every pinned property of this file is exercised by ``tests/test_oracle.py``.
-Readings of points the pages leave open (MSE reduction constant, norm axis,
-epsilon, activation, re-norm axis, ...) are listed in the design doc; each function
-names the reading it implements.
+Points the pages leave open (MSE reduction constant, norm axis, epsilon,
+activation, re-norm axis, ...) are readings, not page facts; each function
+states the reading it implements.
 """
 from __future__ import annotations
 
