@@ -93,6 +93,7 @@ __device__ float2 merge_key_slices(const float* __restrict__ sp, int S, int d, i
   return float2{(float)mean, (float)(1.0 / sqrt(var + (double)eps))};
 }
 
+template <int LOSS>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) k_glu_grad(Problem pb, WRef W, int t0, int nt, int S,
                                                       const float* __restrict__ spart, int S_stats, float eps,
                                                       float* __restrict__ part) {
@@ -110,7 +111,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3,
   const bf16* kp = (const bf16*)pb.k + (prow * pb.N + t0) * D;
   const bf16* vp = (const bf16*)pb.v + (prow * pb.N + t0) * D;
   const float* ep = pb.eta_tok ? pb.eta_tok + prow * pb.N + t0 : nullptr;
-  const bool mse = pb.loss == LOSS_MSE;
+  constexpr bool mse = LOSS == LOSS_MSE;     // the loss is a template parameter: no select between both forms
   const float cm = 2.0f / ((float)nt * (float)D);
   bf16x8 w1f[2], w2f[2];
   load_wfrag(W.mat(0, b, h), w, r, g, w1f);
@@ -315,8 +316,12 @@ int glu_grad_splits(const Problem& pb, int nt) {
 
 void launch_glu_grad(const Problem& pb, const WRef& W, int t0, int nt, int S, const float* spart, int S_stats,
                      float eps, float* part, hipStream_t st) {
-  hipLaunchKernelGGL(k_glu_grad, dim3(S, pb.B * pb.H), dim3(NW * 64), 0, st, pb, W, t0, nt, S, spart, S_stats, eps,
-                     part);
+  if (pb.loss == LOSS_MSE)
+    hipLaunchKernelGGL(k_glu_grad<LOSS_MSE>, dim3(S, pb.B * pb.H), dim3(NW * 64), 0, st, pb, W, t0, nt, S, spart,
+                       S_stats, eps, part);
+  else
+    hipLaunchKernelGGL(k_glu_grad<LOSS_DOT>, dim3(S, pb.B * pb.H), dim3(NW * 64), 0, st, pb, W, t0, nt, S, spart,
+                       S_stats, eps, part);
 }
 
 // one round of readout workgroups over the chip (eight per CU), each over a
