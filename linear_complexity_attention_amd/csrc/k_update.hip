@@ -101,47 +101,35 @@ __global__ void __launch_bounds__(256) k_update_flat(Problem pb, UpdateArgs a) {
 }
 
 // Update from the MFMA gradient kernel's stream-K partials, which are stored in
-// its register order (d = 64, GELU MLP, hidden width HID split over its waves
-// in slices of HP units, NHB = HP/16 blocks of 16):
-//   dW1 part: float4 ((qq*4 + cb)*NHB + hb)*64 + l  ->  dW1[16cb + 4g + i][qq*HP + 16hb + r]
-//   dW2 part: float4 ((qq*NHB + hb)*4 + cb)*64 + l  ->  dW2[qq*HP + 16hb + 4g + i][16cb + r]
-// with l = 16g + r, i = 0..3.  Thread = one float4 of the partial: it sums that
-// float4 over the pair's slots (coalesced reads, slots in workgroup order).
-// The 256 float4s of a workgroup (four consecutive 64-float4 blocks of one
-// matrix) cover a block of whole matrix rows segments: W1 rows 16 cb0 ..
-// + 64/NHB, columns qq HP .. + HP; W2 16 whole rows.  The sums go through an
-// LDS copy of that block, so that W_cur, the momentum, the next state and
-// W_out are read and written as float4s along the rows (a direct store of the
-// register order writes 64-byte pieces of 4 rows per instruction).  The
-// arithmetic, and so the result, is that of the element-wise update.
+// its register order (sk_part_elem: float4 j holds four consecutive rows of
+// one column).  Thread = one float4 of the partial: it sums that float4 over
+// the pair's slots (coalesced reads, slots in workgroup order).  The 256
+// float4s of a workgroup cover a block of whole matrix row segments
+// (sk_update_block: W1 rows 16 cb0 .. + 64/NHB, columns qq HP .. + HP; W2 16
+// whole rows).  The sums go through an LDS copy of that block, so that W_cur,
+// the momentum, the next state and W_out are read and written as float4s
+// along the rows (a direct store of the register order writes 64-byte pieces
+// of 4 rows per instruction).  The arithmetic, and so the result, is that of
+// the element-wise update.  Both index maps are pinned on the host.
 // grid = (D*HID/2 / 256, P).
 template <int HID, int HP>
 __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a) {
   constexpr int D = 64, NHB = HP / 16, HALF = D * HID / 4;   // float4s per matrix
-  static_assert(HALF % 256 == 0, "a workgroup's float4s lie in one matrix");
+  static_assert(HALF % 256 == 0 && HP == HID / 4, "a workgroup's float4s lie in one matrix");
   constexpr int LD0 = HP + 4, LD1 = D + 4;                  // LDS row strides (floats) of the W1 / W2 blocks
   constexpr int TILE = (64 / NHB) * LD0 > 16 * LD1 ? (64 / NHB) * LD0 : 16 * LD1;
   __shared__ __attribute__((aligned(16))) float tile[TILE];
   const int p = blockIdx.y;
   const int b = p / pb.H, h = p % pb.H;
-  const int mat = (int)blockIdx.x * 256 >= HALF ? 1 : 0;     // uniform
-  const int jj = (int)blockIdx.x * 256 + (int)threadIdx.x - mat * HALF;
-  const int l = jj & 63, blk = jj >> 6, g = l >> 4, r = l & 15;
-  const int blk0 = ((int)blockIdx.x * 256 - mat * HALF) >> 6, dl = blk - blk0;   // blk0 % 4 == 0
-  // the block: rows [row0, row0 + R) x columns [col0, col0 + CB) of a matrix with row stride RS
-  int row0, col0, CB, RS, lrw, lcw;                          // lrw + i, lcw: this thread's sums in the block
-  if (mat == 0) {
-    const int u0 = blk0 / NHB;                               // qq * 4 + cb0
-    row0 = 16 * (u0 & 3); col0 = (u0 >> 2) * HP; CB = HP; RS = HID;
-    lrw = 16 * (dl / NHB) + 4 * g; lcw = 16 * (dl % NHB) + r;
-  } else {
-    row0 = 16 * (blk0 >> 2); col0 = 0; CB = D; RS = D;
-    lrw = 4 * g; lcw = 16 * dl + r;
-  }
+  const int j = (int)blockIdx.x * 256 + (int)threadIdx.x;   // float4 of the partial
+  const SkBlock blk = sk_update_block(HID, (int)blockIdx.x); // uniform
+  const SkElem el = sk_part_elem(HID, j);
+  const int mat = blk.mat;
+  const int lrw = el.row - blk.row0, lcw = el.col - blk.col0;   // this thread's sums: rows lrw + 0..3, column lcw
   const int LD = mat == 0 ? LD0 : LD1;
   // this thread's float4 of the block in row order
-  const int lr = (int)threadIdx.x / (CB / 4), lc = 4 * ((int)threadIdx.x % (CB / 4));
-  const int e = (row0 + lr) * RS + col0 + lc;
+  const int lr = (int)threadIdx.x / (blk.cols / 4), lc = 4 * ((int)threadIdx.x % (blk.cols / 4));
+  const int e = (blk.row0 + lr) * blk.rs + blk.col0 + lc;
   const float* cur = a.cur.mat(mat, b, h);
   float* out = a.out[mat] ? a.out[mat] + (size_t)pb.row(p) * D * HID : nullptr;
   // W_cur first, so that its load overlaps the partials'
@@ -161,7 +149,6 @@ __global__ void __launch_bounds__(256) k_update_streamk(Problem pb, UpdateArgs a
   if (!upd) q1 = q0 - 1;          // a matrix outside the mask keeps W_cur
   // the pair's slots, four loads in flight at a time, added in workgroup order
   const long long wsz = 2LL * D * HID;
-  const int j = mat * HALF + jj;
   float4 sum = {0.f, 0.f, 0.f, 0.f};
   for (long long q = q0; q <= q1; q += 4) {
     float4 d[4];

@@ -118,6 +118,40 @@ __host__ __device__ inline long long sk_slot(long long p, long long q, long long
                                              int J) {
   return q * J + (q == q0 ? p - sk_first_pair(q0, G, C, tpp) : 0);
 }
+// Register order of the MFMA gradient kernel's stream-K partials (d = 64,
+// GELU MLP, hidden width hid split over its 4 waves in slices of HP = hid/4
+// units, NHB = HP/16 blocks of 16 units).  Float4 j of a pair's partial
+// (j < 32 hid) holds elements (row + i, col), i = 0..3, of matrix mat:
+//   dW1 part, j < 16 hid:  float4 ((qq*4 + cb)*NHB + hb)*64 + l -> dW1[16cb + 4g + i][qq*HP + 16hb + r]
+//   dW2 part:              float4 ((qq*NHB + hb)*4 + cb)*64 + l -> dW2[qq*HP + 16hb + 4g + i][16cb + r]
+// with l = 16g + r.
+struct SkElem { int mat, row, col; };
+__host__ __device__ inline SkElem sk_part_elem(int hid, int j) {
+  const int hp = hid / 4, nhb = hp / 16, half = 16 * hid;
+  const int mat = j >= half ? 1 : 0, jj = j - mat * half;
+  const int l = jj & 63, blk = jj >> 6, g = l >> 4, r = l & 15;
+  if (mat == 0) {
+    const int hb = blk % nhb, cb = (blk / nhb) & 3, qq = blk / (4 * nhb);
+    return SkElem{0, 16 * cb + 4 * g, qq * hp + 16 * hb + r};
+  }
+  const int cb = blk & 3, hb = (blk >> 2) % nhb, qq = blk / (4 * nhb);
+  return SkElem{1, qq * hp + 16 * hb + 4 * g, 16 * cb + r};
+}
+// The stream-K update kernel's workgroup x takes partial float4s [256x, 256x +
+// 256), four consecutive 64-float4 blocks of one matrix, which hold the
+// matrix block rows [row0, row0 + rows) x columns [col0, col0 + cols) (W1:
+// 64/NHB rows of HP columns; W2: 16 whole rows); rs is the matrix row stride.
+struct SkBlock { int mat, row0, col0, rows, cols, rs; };
+__host__ __device__ inline SkBlock sk_update_block(int hid, int x) {
+  const int hp = hid / 4, nhb = hp / 16, half = 16 * hid;
+  const int mat = 256 * x >= half ? 1 : 0;
+  const int blk0 = (256 * x - mat * half) >> 6;
+  if (mat == 0) {
+    const int u0 = blk0 / nhb;                     // qq * 4 + first cb
+    return SkBlock{0, 16 * (u0 & 3), (u0 >> 2) * hp, 64 / nhb, hp, hid};
+  }
+  return SkBlock{1, 16 * (blk0 >> 2), 0, 16, 64, 64};
+}
 void launch_update(const Problem& pb, const UpdateArgs& a, hipStream_t st);
 // column re-norm of a.next in place (matrices in a.mask), writing a.out
 void launch_renorm(const Problem& pb, const UpdateArgs& a, hipStream_t st);

@@ -13,6 +13,12 @@
 //     tile) exactly when its first and last workgroups coincide (q0 == q1,
 //     the test the update kernel and the host use to skip it), and with one
 //     workgroup per pair (G = P) workgroup q's range is exactly pair q.
+//     The stream-K update kernel's index maps (sk_part_elem: the gradient
+//     kernel's register order of a partial; sk_update_block: the matrix block
+//     a 256-float4 workgroup covers), for every hidden width: each float4's
+//     four elements lie in its workgroup's block, land on distinct slots of
+//     the block's LDS copy, the row-order read-back covers the block exactly,
+//     and the partial covers every element of both matrices exactly once.
 //  2. The C ABI's host-side validation and workspace planning: bad configs and
 //     bad forward arguments are rejected with the right status before anything
 //     is enqueued, workspace sizes are 256-byte multiples, path names resolve.
@@ -135,6 +141,48 @@ static void streamk_sweep() {
       for (long long t : targets) { check_streamk(P, tpp, t); if (g_fail) return; }
 }
 
+// the stream-K update's block map, mirroring k_update_streamk: the LDS copy of
+// a block has rows of cols + 4 floats; thread t reads float4 (t / (cols/4),
+// 4 (t % (cols/4))) of it
+static void check_update_blocks() {
+  const int D = 64;
+  for (int hid : {64, 128, 256}) {
+    const int nf4 = D * hid / 2;                      // float4s of a pair's partial (both matrices)
+    std::vector<int> seen(2 * D * hid, 0);
+    for (int x = 0; x < nf4 / 256; ++x) {
+      const ttt::SkBlock bk = ttt::sk_update_block(hid, x);
+      CHECK(bk.rows * bk.cols == 1024, "hid %d x %d: block %d x %d", hid, x, bk.rows, bk.cols);
+      CHECK(bk.cols % 4 == 0 && bk.col0 % 4 == 0 && bk.rs % 4 == 0, "hid %d x %d: float4 alignment", hid, x);
+      const int ld = bk.cols + 4;
+      std::vector<int> slot(bk.rows * ld, -1);       // LDS slot -> matrix element
+      for (int t = 0; t < 256; ++t) {
+        const int j = 256 * x + t;
+        const ttt::SkElem el = ttt::sk_part_elem(hid, j);
+        CHECK(el.mat == bk.mat, "hid %d j %d: matrix %d, block matrix %d", hid, j, el.mat, bk.mat);
+        const int lr = el.row - bk.row0, lc = el.col - bk.col0;
+        CHECK(lr >= 0 && lr + 3 < bk.rows && lc >= 0 && lc < bk.cols, "hid %d j %d: (%d, %d) outside the block", hid,
+              j, el.row, el.col);
+        for (int i = 0; i < 4; ++i) {
+          const int s_ = (lr + i) * ld + lc;
+          CHECK(slot[s_] == -1, "hid %d j %d: LDS slot %d written twice", hid, j, s_);
+          const int e = (el.row + i) * bk.rs + el.col;
+          slot[s_] = e;
+          const int g = bk.mat * D * hid + e;
+          CHECK(e >= 0 && e < D * hid && seen[g] == 0, "hid %d j %d: element %d out of range or repeated", hid, j, e);
+          seen[g] = 1;
+        }
+      }
+      for (int t = 0; t < 256; ++t) {                 // row-order read-back
+        const int lr = t / (bk.cols / 4), lc = 4 * (t % (bk.cols / 4));
+        const int e = (bk.row0 + lr) * bk.rs + bk.col0 + lc;
+        for (int i = 0; i < 4; ++i)
+          CHECK(slot[lr * ld + lc + i] == e + i, "hid %d x %d t %d: read-back of slot %d", hid, x, t, lr * ld + lc + i);
+      }
+    }
+    for (int g = 0; g < 2 * D * hid; ++g) CHECK(seen[g] == 1, "hid %d: element %d of the pair not covered", hid, g);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 2. ABI host-side validation
 static ttt_config cfg(int B = 2, int H = 3, int N = 100, int d = 64, int hidden = 256) {
@@ -244,6 +292,8 @@ static void abi_checks() {
 int main() {
   streamk_sweep();
   if (!g_fail) std::printf("stream-K: %lld shapes, %lld tiles checked\n", g_configs, g_tiles);
+  if (!g_fail) check_update_blocks();
+  if (!g_fail) std::printf("stream-K update blocks checked\n");
   if (!g_fail) abi_checks();
   if (!g_fail) std::printf("ABI host checks passed\n");
   return g_fail;

@@ -3,7 +3,9 @@ UndefinedBehaviorSanitizer on the host code (tests/native/host_checks.cpp):
 
 * the stream-K split of the MFMA gradient kernel and the slot arithmetic of
   its update kernel, exhaustively over many shapes (bit-exact cover of every
-  (pair, tile), slots below G*J written once and read back by the right pair);
+  (pair, tile), slots below G*J written once and read back by the right pair),
+  and the update kernel's map from the partials' register order to row-wise
+  matrix blocks (every element once, distinct LDS slots, exact read-back);
 * the C ABI's host-side validation and workspace planning.
 
 The checker links the sanitized ttt_api.cpp with the library's own device
@@ -57,5 +59,6 @@ def test_streamk_cover_and_abi_under_sanitizers(checker):
                HIP_VISIBLE_DEVICES="")
     r = subprocess.run([checker], capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+    assert "stream-K update blocks checked" in r.stdout
     assert "ABI host checks passed" in r.stdout
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr
